@@ -1,0 +1,223 @@
+// CPU oracle for sparse convolution over coordinate/feature sparse tensors.
+//
+// TEST INFRASTRUCTURE ONLY.  This file is the slow, obviously-correct
+// reference that the GPU library is checked against.  Only the test suite,
+// the smoke check and the benchmark's CPU-baseline leg load it; the product
+// path never does.  It shares no code, header, table or constant with the GPU
+// library.
+//
+// What it computes (torch-lattice "Migrating from TorchSparse" page, sections
+// "Sparse tensor expectations", "Convolution mapping" and "Backend and
+// configuration differences"):
+//   * a sparse tensor is integer coordinate rows (batch, x, y[, z]) with one
+//     dense feature row per coordinate row; the batch id lives in column 0;
+//   * SubmConv3d keeps the input coordinate set as the output set;
+//   * a strided Conv3d creates a downsampled output set;
+//   * every dataflow must give the same result for a fixed relation
+//     (input row, output row, kernel offset) and weight tensor.
+//
+// Readings taken where the pages are silent (all of them are also listed in
+// the design notes):
+//   * key = the full coordinate tuple; a repeated coordinate keeps the
+//     lowest row and raises the DUP flag;
+//   * batch must lie in [0, 65534] and every spatial value in
+//     [-32768, 32767]; a row outside is not inserted and raises RANGE;
+//   * kernel offsets delta_d in {-r, ..., K-1-r} with r = (K-1)/2, enumerated
+//     with the first spatial axis slowest; no cross-batch neighbours;
+//   * submanifold: output row j reads input q_j + delta;
+//     strided: outputs are unique(floor(c/s)) in first-occurrence order and
+//     output j reads input s*q_j + delta;
+//   * cross-correlation (no kernel flip), W laid out [offset][cin][cout];
+//   * all arithmetic in fp64.
+//
+// Parity pins: tests/test_oracle_*.py check every function here against dense
+// convolution (torch CPU, fp64), brute-force searches, closed forms and the
+// page's two-voxel example.
+#include <array>
+#include <cstdint>
+#include <cstring>
+#include <unordered_map>
+#include <vector>
+
+namespace {
+
+using Key = std::array<int64_t, 4>;
+
+struct KeyHash {
+  size_t operator()(const Key& k) const {
+    size_t h = 1469598103934665603ull;
+    for (int64_t v : k) {
+      h ^= static_cast<size_t>(v) + 0x9e3779b97f4a7c15ull + (h << 6) + (h >> 2);
+    }
+    return h;
+  }
+};
+
+using Map = std::unordered_map<Key, int64_t, KeyHash>;
+
+const uint32_t FLAG_DUP = 1u, FLAG_RANGE = 2u;
+
+bool in_range(const int32_t* row, int ndim) {
+  if (row[0] < 0 || row[0] > 65534) return false;
+  for (int d = 1; d <= ndim; ++d)
+    if (row[d] < -32768 || row[d] > 32767) return false;
+  return true;
+}
+
+Key key_of(const int32_t* row, int ndim) {
+  Key k{0, 0, 0, 0};
+  for (int d = 0; d <= ndim; ++d) k[d] = row[d];
+  return k;
+}
+
+// Insert rows in index order; first insertion of a coordinate wins.
+Map build_map(const int32_t* coords, int64_t n, int ndim, uint32_t* flags) {
+  Map m;
+  m.reserve(static_cast<size_t>(n) * 2 + 1);
+  for (int64_t i = 0; i < n; ++i) {
+    const int32_t* row = coords + i * (ndim + 1);
+    if (!in_range(row, ndim)) {
+      if (flags) *flags |= FLAG_RANGE;
+      continue;
+    }
+    auto ins = m.emplace(key_of(row, ndim), i);
+    if (!ins.second && flags) *flags |= FLAG_DUP;
+  }
+  return m;
+}
+
+int64_t lookup(const Map& m, const Key& k) {
+  auto it = m.find(k);
+  return it == m.end() ? -1 : it->second;
+}
+
+int64_t floor_div(int64_t a, int64_t b) {
+  int64_t q = a / b;
+  if ((a % b != 0) && ((a < 0) != (b < 0))) --q;
+  return q;
+}
+
+// Offset o -> spatial displacement, first spatial axis slowest.
+void offset_delta(int o, int ndim, int ksize, int64_t* delta) {
+  const int r = (ksize - 1) / 2;
+  for (int d = ndim - 1; d >= 0; --d) {
+    delta[d] = (o % ksize) - r;
+    o /= ksize;
+  }
+}
+
+int ipow(int b, int e) {
+  int v = 1;
+  for (int i = 0; i < e; ++i) v *= b;
+  return v;
+}
+
+}  // namespace
+
+extern "C" {
+
+// Key -> row lookup of every query row (batch, spatial...) after inserting
+// `coords` in row order.  rows[i] = owning input row or -1.  Returns 0.
+int64_t oracle_hash_query(const int32_t* coords, int64_t n, int ndim, const int32_t* q, int64_t m,
+                          int32_t* rows, uint32_t* flags) {
+  uint32_t f = 0;
+  Map map = build_map(coords, n, ndim, &f);
+  for (int64_t i = 0; i < m; ++i) {
+    const int32_t* row = q + i * (ndim + 1);
+    rows[i] = static_cast<int32_t>(lookup(map, key_of(row, ndim)));
+  }
+  if (flags) *flags = f;
+  return 0;
+}
+
+// Downsampled output coordinates of a stride-s convolution: for each input
+// row in order, (b, floor(x/s), ...) appended when first seen.  Rows outside
+// the coordinate range take no part.  Returns the number of output rows.
+int64_t oracle_strided_support(const int32_t* coords, int64_t n, int ndim, int stride,
+                               int32_t* out_coords) {
+  Map seen;
+  int64_t n_out = 0;
+  for (int64_t i = 0; i < n; ++i) {
+    const int32_t* row = coords + i * (ndim + 1);
+    if (!in_range(row, ndim)) continue;
+    Key k{0, 0, 0, 0};
+    k[0] = row[0];
+    for (int d = 1; d <= ndim; ++d) k[d] = floor_div(row[d], stride);
+    if (seen.emplace(k, n_out).second) {
+      for (int d = 0; d <= ndim; ++d) out_coords[n_out * (ndim + 1) + d] = static_cast<int32_t>(k[d]);
+      ++n_out;
+    }
+  }
+  return n_out;
+}
+
+// Kernel map: for every output row j (in order) and offset o (in order), the
+// input row i at s*q_j + delta_o (s = 1: q_j + delta_o) if it exists.  Writes
+// up to `cap` triples (in, out, offset) and returns how many exist.
+int64_t oracle_kmap(const int32_t* in_coords, int64_t n_in, const int32_t* out_coords, int64_t n_out,
+                    int ndim, int ksize, int stride, int32_t* t_in, int32_t* t_out, int32_t* t_off,
+                    int64_t cap) {
+  Map map = build_map(in_coords, n_in, ndim, nullptr);
+  const int kvol = ipow(ksize, ndim);
+  int64_t count = 0;
+  int64_t delta[3];
+  for (int64_t j = 0; j < n_out; ++j) {
+    const int32_t* q = out_coords + j * (ndim + 1);
+    for (int o = 0; o < kvol; ++o) {
+      offset_delta(o, ndim, ksize, delta);
+      Key p{0, 0, 0, 0};
+      p[0] = q[0];
+      for (int d = 0; d < ndim; ++d) p[d + 1] = static_cast<int64_t>(stride) * q[d + 1] + delta[d];
+      const int64_t i = lookup(map, p);
+      if (i < 0) continue;
+      if (count < cap) {
+        t_in[count] = static_cast<int32_t>(i);
+        t_out[count] = static_cast<int32_t>(j);
+        t_off[count] = o;
+      }
+      ++count;
+    }
+  }
+  return count;
+}
+
+// y[j][co] = sum over triples (i, j, o) and ci of x[i][ci] * w[o][ci][co].
+void oracle_conv_fwd(const int32_t* t_in, const int32_t* t_out, const int32_t* t_off, int64_t n_pairs,
+                     const double* x, int cin, const double* w, int cout, double* y, int64_t n_out) {
+  std::memset(y, 0, sizeof(double) * static_cast<size_t>(n_out) * cout);
+  for (int64_t p = 0; p < n_pairs; ++p) {
+    const double* xi = x + static_cast<int64_t>(t_in[p]) * cin;
+    const double* wo = w + static_cast<int64_t>(t_off[p]) * cin * cout;
+    double* yj = y + static_cast<int64_t>(t_out[p]) * cout;
+    for (int ci = 0; ci < cin; ++ci)
+      for (int co = 0; co < cout; ++co) yj[co] += xi[ci] * wo[ci * cout + co];
+  }
+}
+
+// dx[i][ci] = sum over triples (i, j, o) and co of dy[j][co] * w[o][ci][co].
+void oracle_conv_dgrad(const int32_t* t_in, const int32_t* t_out, const int32_t* t_off, int64_t n_pairs,
+                       const double* dy, int cout, const double* w, int cin, double* dx, int64_t n_in) {
+  std::memset(dx, 0, sizeof(double) * static_cast<size_t>(n_in) * cin);
+  for (int64_t p = 0; p < n_pairs; ++p) {
+    const double* g = dy + static_cast<int64_t>(t_out[p]) * cout;
+    const double* wo = w + static_cast<int64_t>(t_off[p]) * cin * cout;
+    double* d = dx + static_cast<int64_t>(t_in[p]) * cin;
+    for (int ci = 0; ci < cin; ++ci)
+      for (int co = 0; co < cout; ++co) d[ci] += g[co] * wo[ci * cout + co];
+  }
+}
+
+// dw[o][ci][co] = sum over triples (i, j, o) of x[i][ci] * dy[j][co].
+void oracle_conv_wgrad(const int32_t* t_in, const int32_t* t_out, const int32_t* t_off, int64_t n_pairs,
+                       const double* x, int cin, const double* dy, int cout, double* dw, int kvol) {
+  std::memset(dw, 0, sizeof(double) * static_cast<size_t>(kvol) * cin * cout);
+  for (int64_t p = 0; p < n_pairs; ++p) {
+    const double* xi = x + static_cast<int64_t>(t_in[p]) * cin;
+    const double* g = dy + static_cast<int64_t>(t_out[p]) * cout;
+    double* d = dw + static_cast<int64_t>(t_off[p]) * cin * cout;
+    for (int ci = 0; ci < cin; ++ci)
+      for (int co = 0; co < cout; ++co) d[ci * cout + co] += xi[ci] * g[co];
+  }
+}
+
+}  // extern "C"
