@@ -1,0 +1,255 @@
+/*
+ * ts.h -- C ABI of the MI355X (gfx950) sparse-convolution library.
+ *
+ * The library computes sparse convolution over coordinate/feature sparse
+ * tensors as the torch-lattice page "Migrating from TorchSparse" states the
+ * problem (section "Sparse tensor expectations"): coordinates are int32 rows
+ * (batch, x, y, z) -- or (batch, x, y) in 2-D -- with the batch id inside
+ * each row, and feature row i of a dense (N, C) matrix belongs to coordinate
+ * row i.  Section "Convolution mapping" fixes the support rules: a
+ * submanifold convolution keeps the input coordinate set, a strided
+ * convolution creates a downsampled one.  Section "Backend and configuration
+ * differences" fixes that the dataflow (implicit GEMM, gather-scatter) is a
+ * performance choice that must not change the result beyond floating-point
+ * rounding, and names the hash-table reserve ratio.
+ *
+ * Conventions shared by every entry point
+ * ----------------------------------------
+ * - Memory: the caller allocates every device buffer; the library never
+ *   allocates device memory.  Size queries (ts_hash_capacity,
+ *   ts_hash_table_bytes, ts_kmap_bytes, ts_conv_workspace_bytes) say how
+ *   much.  All pointers named "device" must be device memory of the current
+ *   HIP device; feature matrices are row-major and contiguous.
+ * - Streams: every call is asynchronous and ordered on `stream`; there is no
+ *   host synchronisation inside the library.  Counts that only the device
+ *   knows (the number of strided output rows) are written to device int64
+ *   scalars.
+ * - Errors: problems visible on the host (null pointers, negative sizes,
+ *   unsupported shapes or dtypes, short buffers) return a status before any
+ *   launch.  A failed launch returns TS_ERR_HIP.  Problems only the device
+ *   sees are ORed into a caller-zeroed uint32 flag word (TS_FLAG_*): the call
+ *   still returns TS_OK, and the caller reads the word after synchronising.
+ *   Nothing aborts and no exception crosses the ABI.
+ * - Coordinates: batch in [0, 65534], spatial values in [-32768, 32767].
+ *   A row outside that range is left out of the hash table (it neither finds
+ *   nor is found) and raises TS_FLAG_RANGE.  A repeated coordinate keeps its
+ *   lowest row and raises TS_FLAG_DUP.
+ * - Kernel offsets: offset o of a kernel of size K in D dims is the
+ *   displacement delta with delta_d in {-r, ..., K-1-r}, r = (K-1)/2, the
+ *   first spatial axis varying slowest:  o = sum_d (delta_d + r) K^(D-1-d).
+ *   Weights are [K^D][Cin][Cout]; the convolution is a cross-correlation:
+ *     submanifold:  y[j] = sum_o x[row(q_j + delta_o)] . W[o]
+ *     strided (s):  y[j] = sum_o x[row(s q_j + delta_o)] . W[o]
+ *   with absent rows contributing nothing.  K^D <= 64.
+ */
+#ifndef TS_H_
+#define TS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum ts_status {
+  TS_OK = 0,
+  TS_ERR_INVALID_ARG = 1, /* null pointer, negative size, bad shape, short buffer */
+  TS_ERR_UNSUPPORTED = 2, /* valid request this library does not implement      */
+  TS_ERR_HIP = 3          /* a HIP launch or runtime call failed                 */
+} ts_status;
+
+typedef enum ts_dtype { TS_F32 = 0, TS_F16 = 1, TS_BF16 = 2 } ts_dtype;
+
+typedef enum ts_dataflow {
+  TS_DATAFLOW_AUTO = 0,          /* per-shape choice                                   */
+  TS_DATAFLOW_IMPLICIT_GEMM = 1, /* output-stationary tiles, MFMA for fp16/bf16        */
+  TS_DATAFLOW_GATHER_SCATTER = 2 /* per offset: gather, multiply, add into the outputs */
+} ts_dataflow;
+
+/* device-detected conditions, ORed into the caller's flag word */
+#define TS_FLAG_DUP 1u   /* a coordinate appeared twice; its lowest row owns it */
+#define TS_FLAG_RANGE 2u /* a coordinate was outside the packable range         */
+#define TS_FLAG_FULL 4u  /* the hash table had no free slot left                */
+
+/* kernel-map build options (bit set) */
+#define TS_KMAP_PAIRS 1u   /* also build per-offset (in, out) pair lists            */
+#define TS_KMAP_BWD 2u     /* strided: also build the transposed relation (dgrad)   */
+#define TS_KMAP_NATURAL 4u /* keep destination rows in index order inside tiles    */
+
+#define TS_TILE 16     /* destination rows per tile */
+#define TS_MAX_KVOL 64 /* largest supported K^D     */
+
+/* Human-readable name of a status code (static string). */
+const char* ts_status_string(ts_status s);
+
+/* Library version string and the GPU architecture it was built for. */
+const char* ts_version(void);
+
+/* ------------------------------------------------------------------------
+ * Coordinate hash (the "hashing" and "coordinate query" kernels of the
+ * torch-lattice page, section "What remains familiar"; table size set by the
+ * reserve ratio of section "Backend and configuration differences").
+ *
+ * The table is an open-addressing map from a packed 64-bit coordinate key to
+ * a row index, in one caller buffer of ts_hash_table_bytes(cap) bytes
+ * (8-byte aligned).  Its slot layout is internal and may differ between runs;
+ * only the lookup function is defined.
+ * ---------------------------------------------------------------------- */
+
+/* Capacity for n keys at reserve ratio rsv (>= 1): the smallest power of two
+ * >= max(64, ceil(rsv * n)).  Returns -1 for n < 0 or rsv < 1. */
+int64_t ts_hash_capacity(int64_t n, double rsv_ratio);
+
+/* Bytes of a table of `cap` slots (12 per slot). */
+size_t ts_hash_table_bytes(int64_t cap);
+
+/* Build the table of `n` coordinate rows coords[n][ndim+1] (device int32):
+ * key(coords[i]) -> i, the lowest row winning for repeated keys.  `table`
+ * (device, ts_hash_table_bytes(cap) bytes) is overwritten; cap must be a
+ * power of two >= n.  err_flags (device uint32, may be NULL) receives
+ * TS_FLAG_DUP / TS_FLAG_RANGE / TS_FLAG_FULL. */
+ts_status ts_hash_build(const int32_t* coords, int64_t n, int ndim, void* table, int64_t cap,
+                        uint32_t* err_flags, hipStream_t stream);
+
+/* rows[k] = row owning coordinate q[k] (device int32 [m][ndim+1]) or -1. */
+ts_status ts_hash_query(const void* table, int64_t cap, int ndim, const int32_t* q, int64_t m,
+                        int32_t* rows, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Downsampled support of a strided convolution (page section "Convolution
+ * mapping": a strided forward convolution creates a downsampled support).
+ *
+ * Output coordinates are unique((b, floor(x/s), floor(y/s)[, floor(z/s)]))
+ * over the input rows (floor toward -inf), ordered by first occurrence in
+ * input row order.  out_coords (device int32, capacity n_in rows) receives
+ * them, *n_out (device int64) their count, and out_table (device,
+ * ts_hash_table_bytes(out_cap), out_cap a power of two >= n_in) maps each
+ * output coordinate to its output row -- it serves as the input table of a
+ * following layer.  `scratch` (device) needs ts_support_scratch_bytes(n_in).
+ * ---------------------------------------------------------------------- */
+size_t ts_support_scratch_bytes(int64_t n_in);
+ts_status ts_strided_support(const int32_t* in_coords, int64_t n_in, int ndim, int stride,
+                             int32_t* out_coords, int64_t* n_out, void* out_table, int64_t out_cap,
+                             void* scratch, size_t scratch_bytes, uint32_t* err_flags,
+                             hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Kernel map (the "kernel-map construction" of the page's section "Sparse
+ * tensor expectations"): for every output row j and offset o, the input row
+ * i at q_j + delta_o (stride 1) or s q_j + delta_o (stride s), as a tiled
+ * relation:
+ *
+ *   destination rows are grouped in tiles of TS_TILE; tile t has an offset
+ *   bit mask tile_mask[t] (bit o set when any of its rows has a neighbour at
+ *   offset o); for the k-th set bit o of tile_mask[t] (ascending),
+ *   pool[(t*kvol + k)*TS_TILE + r] is the source row of slot r at offset o,
+ *   or -1; tile_rows[t*TS_TILE + r] is the destination row in slot r, or -1.
+ *   row_mask[d] is the offset mask of destination row d.
+ *
+ * Which destination rows share a tile is a performance choice (rows with
+ * similar masks are grouped unless TS_KMAP_NATURAL is set); the relation
+ * itself -- the set of (in, out, offset) triples -- is fixed.
+ * ---------------------------------------------------------------------- */
+typedef struct ts_rel {
+  int64_t n_dest_cap;    /* destination rows, upper bound (host)               */
+  int64_t n_tiles;       /* ceil(n_dest_cap / TS_TILE)                         */
+  const int64_t* n_dest; /* device int64: destination row count                */
+  uint64_t* tile_mask;   /* device [n_tiles]                                   */
+  int32_t* tile_rows;    /* device [n_tiles * TS_TILE]                         */
+  int32_t* pool;         /* device [n_tiles * kvol * TS_TILE]                  */
+  uint64_t* row_mask;    /* device [n_dest_cap]                                */
+} ts_rel;
+
+typedef struct ts_kmap {
+  int32_t ndim, ksize, stride, kvol;
+  uint32_t flags;      /* TS_KMAP_* bits actually built                            */
+  int32_t mirror_bwd;  /* 1: the transposed relation is fwd with offset kvol-1-o  */
+  int64_t n_in;        /* input rows                                               */
+  int64_t n_out_cap;   /* output rows, upper bound                                 */
+  int64_t* n_out;      /* device int64: output rows                                */
+  ts_rel fwd;          /* destination = output rows, source = input rows           */
+  ts_rel bwd;          /* strided with TS_KMAP_BWD: destination = input rows       */
+  int64_t pair_cap;    /* capacity of the pair lists                               */
+  int64_t* pair_start; /* device [kvol+1]: offset o owns pairs [start[o], start[o+1]) */
+  int32_t* pair_in;    /* device [pair_cap] input row of each pair, output-row order */
+  int32_t* pair_out;   /* device [pair_cap] output row of each pair                  */
+  void* scratch;       /* device scratch inside the map buffer                     */
+  size_t scratch_bytes;
+} ts_kmap;
+
+/* Bytes of the map buffer for the given shape and TS_KMAP_* flags. */
+size_t ts_kmap_bytes(int64_t n_in, int64_t n_out_cap, int ndim, int ksize, int stride, uint32_t flags);
+
+/* Build the kernel map into `buf` (device, ts_kmap_bytes(...) bytes) and fill
+ * the host struct *map with pointers into it.
+ *   stride == 1 (submanifold): ksize odd; the outputs are the inputs, so
+ *     out_coords / n_out / out_table may be NULL and n_out_cap = n_in.
+ *   stride > 1: out_coords (device, n_out_cap rows), n_out (device int64)
+ *     and, with TS_KMAP_BWD, out_table (out_cap slots) describe the output
+ *     support, normally from ts_strided_support.
+ * in_table / in_cap is the ts_hash_build table of the inputs. */
+ts_status ts_kmap_build(const int32_t* in_coords, int64_t n_in, const void* in_table, int64_t in_cap,
+                        const int32_t* out_coords, int64_t n_out_cap, const int64_t* n_out,
+                        const void* out_table, int64_t out_cap, int ndim, int ksize, int stride,
+                        uint32_t flags, void* buf, size_t buf_bytes, ts_kmap* map, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Convolution (forward, dgrad, wgrad) over a built map.  Features are
+ * fp32 / fp16 / bf16 with fp32 accumulation; the output type is fp32 or the
+ * input type (round to nearest even).  Every output row is written exactly
+ * once (rows without neighbours get zeros); there are no atomics, so results
+ * are bitwise repeatable.
+ * ---------------------------------------------------------------------- */
+#define TS_OP_FWD 0
+#define TS_OP_DGRAD 1
+#define TS_OP_WGRAD 2
+
+/* Workspace bytes for an op on this map (0 is a valid answer). */
+size_t ts_conv_workspace_bytes(const ts_kmap* map, int cin, int cout, int op, ts_dtype in_dtype,
+                               ts_dataflow dataflow);
+
+/* y[n_out][cout] = sparse conv of x[n_in][cin] with w[kvol][cin][cout] over
+ * map->fwd (any stride). */
+ts_status ts_conv_fwd(const ts_kmap* map, const void* x, int cin, const void* w, int cout, void* y,
+                      ts_dtype in_dtype, ts_dtype out_dtype, ts_dataflow dataflow, void* ws,
+                      size_t ws_bytes, hipStream_t stream);
+
+/* Submanifold SubmConv3d / SubmConv2d forward: ts_conv_fwd on a stride-1 map
+ * (output rows = input rows). */
+ts_status ts_subm_conv_fwd(const ts_kmap* map, const void* x, int cin, const void* w, int cout, void* y,
+                           ts_dtype in_dtype, ts_dtype out_dtype, ts_dataflow dataflow, void* ws,
+                           size_t ws_bytes, hipStream_t stream);
+
+/* Strided Conv3d / Conv2d forward, support generation included: runs
+ * ts_strided_support, ts_kmap_build (kmap_flags) and ts_conv_fwd in order.
+ * `map_buf` holds ts_kmap_bytes(n_in, n_in, ndim, ksize, stride, kmap_flags)
+ * + ts_support_scratch_bytes(n_in) bytes; *map is filled for the backward
+ * pass.  y has capacity n_in rows; rows >= *n_out are not written. */
+ts_status ts_conv_fwd_strided(const int32_t* in_coords, int64_t n_in, int ndim, const void* in_table,
+                              int64_t in_cap, int ksize, int stride, uint32_t kmap_flags,
+                              int32_t* out_coords, int64_t* n_out, void* out_table, int64_t out_cap,
+                              uint32_t* err_flags, void* map_buf, size_t map_bytes, ts_kmap* map,
+                              const void* x, int cin, const void* w, int cout, void* y,
+                              ts_dtype in_dtype, ts_dtype out_dtype, ts_dataflow dataflow, void* ws,
+                              size_t ws_bytes, hipStream_t stream);
+
+/* dx[n_in][cin] = sum over triples (i, j, o) of dy[j] . W[o]^T.  Strided
+ * maps need TS_KMAP_BWD (implicit GEMM) or TS_KMAP_PAIRS (gather-scatter). */
+ts_status ts_conv_bwd_dgrad(const ts_kmap* map, const void* dy, int cout, const void* w, int cin, void* dx,
+                            ts_dtype in_dtype, ts_dtype out_dtype, ts_dataflow dataflow, void* ws,
+                            size_t ws_bytes, hipStream_t stream);
+
+/* dw[kvol][cin][cout] (device fp32, overwritten) = sum over triples (i, j, o)
+ * of x[i]^T dy[j].  Needs TS_KMAP_PAIRS.  The per-offset reduction is split
+ * over chunks of pairs and summed in a fixed order (deterministic). */
+ts_status ts_conv_bwd_wgrad(const ts_kmap* map, const void* x, int cin, const void* dy, int cout,
+                            ts_dtype in_dtype, float* dw, void* ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TS_H_ */

@@ -22,6 +22,9 @@
 //     lowest row and raises the DUP flag;
 //   * batch must lie in [0, 65534] and every spatial value in
 //     [-32768, 32767]; a row outside is not inserted and raises RANGE;
+//   * a row that is out of range, or repeats the coordinate of a lower row,
+//     takes no part in the convolution: it is never found as a neighbour
+//     and, as a submanifold output row, it has no neighbours (zero output);
 //   * kernel offsets delta_d in {-r, ..., K-1-r} with r = (K-1)/2, enumerated
 //     with the first spatial axis slowest; no cross-batch neighbours;
 //   * submanifold: output row j reads input q_j + delta;
@@ -163,6 +166,10 @@ int64_t oracle_kmap(const int32_t* in_coords, int64_t n_in, const int32_t* out_c
   int64_t delta[3];
   for (int64_t j = 0; j < n_out; ++j) {
     const int32_t* q = out_coords + j * (ndim + 1);
+    if (!in_range(q, ndim)) continue;
+    // submanifold outputs are the input rows: only the owner of a coordinate
+    // takes part
+    if (stride == 1 && lookup(map, key_of(q, ndim)) != j) continue;
     for (int o = 0; o < kvol; ++o) {
       offset_delta(o, ndim, ksize, delta);
       Key p{0, 0, 0, 0};

@@ -80,6 +80,23 @@ def test_hash_query_vs_linear_scan():
     del rng
 
 
+def test_duplicate_and_range_rows_take_no_part():
+    """A repeated or out-of-range row is never a neighbour and, as a
+    submanifold output, has no neighbours; the relation stays symmetric."""
+    c = synth.random_coords(5, 200, 3, 1, 6)
+    bad = np.array([[0, 40000, 1, 1], [0, -40000, 0, 0]], np.int32)
+    c2 = np.concatenate([c, c[[3, 10]], bad], axis=0)
+    n = len(c)
+    t_in, t_out, t_off = oracle.kmap(c2, c2, 3, 1)
+    assert t_in.max() < n and t_out.max() < n
+    assert canon((t_in, t_out, t_off)).tolist() == canon(oracle.kmap(c, c, 3, 1)).tolist()
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal((len(c2), 2))
+    w = rng.standard_normal((27, 2, 2))
+    y = oracle.conv_fwd((t_in, t_out, t_off), x, w, len(c2))
+    assert np.all(y[n:] == 0)
+
+
 def test_hash_range_rows_not_inserted():
     c = np.array([[0, 0, 0, 0], [0, 40000, 0, 0], [70000, 1, 1, 1], [0, -32768, 32767, 5]], np.int32)
     rows, flags = oracle.hash_query(c, c)
