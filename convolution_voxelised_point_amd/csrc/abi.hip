@@ -1,0 +1,388 @@
+// C entry points: host-side validation, buffer layout and kernel dispatch.
+// Every check that the host can make happens here, before any launch.
+#include <string.h>
+
+#include "common.h"
+#include "launch.h"
+
+using namespace ts;
+
+namespace {
+
+#define TS_TRY(expr)                                  \
+  do {                                                \
+    hipError_t e_ = (expr);                           \
+    if (e_ != hipSuccess) return TS_ERR_HIP;          \
+  } while (0)
+
+bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+bool dtype_ok(int d) { return d == TS_F32 || d == TS_F16 || d == TS_BF16; }
+int ipow(int b, int e) {
+  int v = 1;
+  for (int i = 0; i < e; ++i) v *= b;
+  return v;
+}
+bool shape_ok(int ndim, int ksize, int stride) {
+  if (ndim != 2 && ndim != 3) return false;
+  if (ksize < 1 || ksize > 64 || stride < 1 || stride > 65535) return false;
+  return ipow(ksize, ndim) <= TS_MAX_KVOL;
+}
+
+constexpr int64_t kMaxRows = (int64_t{1} << 31) - 1;
+constexpr int kMaxChannels = 1 << 16;
+
+// Layout of the kernel-map buffer: every region starts on a 256-byte boundary.
+struct Carver {
+  char* base;
+  size_t off = 0;
+  template <typename T>
+  T* take(size_t count) {
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off = align_up(off + count * sizeof(T), 256);
+    return p;
+  }
+};
+
+int64_t pair_capacity(int64_t n_in, int64_t n_out_cap, int ndim, int ksize, int stride) {
+  const int kvol = ipow(ksize, ndim);
+  const int per_axis = (ksize + stride - 1) / stride;
+  const int64_t a = n_out_cap * kvol;
+  const int64_t b = n_in * ipow(per_axis, ndim);
+  return a < b ? a : b;
+}
+
+void carve_rel(Carver& c, ts_rel* r, int64_t n_dest_cap, int kvol) {
+  r->n_dest_cap = n_dest_cap;
+  r->n_tiles = ceil_div<int64_t>(n_dest_cap, kTile);
+  r->tile_mask = c.take<uint64_t>(static_cast<size_t>(r->n_tiles));
+  r->tile_rows = c.take<int32_t>(static_cast<size_t>(r->n_tiles) * kTile);
+  r->pool = c.take<int32_t>(static_cast<size_t>(r->n_tiles) * kvol * kTile);
+  r->row_mask = c.take<uint64_t>(static_cast<size_t>(n_dest_cap));
+  r->n_dest = nullptr;
+}
+
+// Lays out a map; with base == NULL only the size is computed.
+size_t layout_kmap(char* base, ts_kmap* m, int64_t n_in, int64_t n_out_cap, int ndim, int ksize, int stride,
+                   uint32_t flags) {
+  Carver c{base};
+  memset(m, 0, sizeof(*m));
+  m->ndim = ndim;
+  m->ksize = ksize;
+  m->stride = stride;
+  m->kvol = ipow(ksize, ndim);
+  m->flags = flags;
+  m->mirror_bwd = stride == 1 ? 1 : 0;
+  m->n_in = n_in;
+  m->n_out_cap = n_out_cap;
+  m->n_out = c.take<int64_t>(1);
+  carve_rel(c, &m->fwd, n_out_cap, m->kvol);
+  if (stride > 1 && (flags & TS_KMAP_BWD)) carve_rel(c, &m->bwd, n_in, m->kvol);
+  size_t scratch = rel_scratch_bytes(n_out_cap, m->kvol);
+  if (flags & TS_KMAP_PAIRS) {
+    m->pair_cap = pair_capacity(n_in, n_out_cap, ndim, ksize, stride);
+    m->pair_start = c.take<int64_t>(static_cast<size_t>(m->kvol) + 1);
+    m->pair_in = c.take<int32_t>(static_cast<size_t>(m->pair_cap));
+    m->pair_out = c.take<int32_t>(static_cast<size_t>(m->pair_cap));
+    const size_t ps = pairs_scratch_bytes(n_out_cap, m->kvol);
+    if (ps > scratch) scratch = ps;
+  }
+  if (stride > 1 && (flags & TS_KMAP_BWD)) {
+    const size_t rs = rel_scratch_bytes(n_in, m->kvol);
+    if (rs > scratch) scratch = rs;
+  }
+  m->scratch_bytes = scratch;
+  m->scratch = c.take<char>(scratch);
+  return c.off;
+}
+
+ts_status check_conv(const ts_kmap* map, int cin, int cout, ts_dtype in, ts_dtype out) {
+  if (!map || map->kvol < 1 || map->kvol > TS_MAX_KVOL || !map->fwd.tile_mask) return TS_ERR_INVALID_ARG;
+  if (cin < 1 || cout < 1 || cin > kMaxChannels || cout > kMaxChannels) return TS_ERR_INVALID_ARG;
+  if (!dtype_ok(in) || !dtype_ok(out)) return TS_ERR_INVALID_ARG;
+  if (out != TS_F32 && out != in) return TS_ERR_UNSUPPORTED;
+  return TS_OK;
+}
+
+bool use_igemm(ts_dataflow df, int c_src, int c_dst, ts_dtype in) {
+  return (df == TS_DATAFLOW_AUTO || df == TS_DATAFLOW_IMPLICIT_GEMM) && igemm_supported(c_src, c_dst, in);
+}
+
+size_t conv_ws(const ts_kmap* map, int c_src, int c_dst, ts_dtype in, ts_dtype out, ts_dataflow df, int64_t n_dest) {
+  if (df == TS_DATAFLOW_GATHER_SCATTER) return gs_workspace_bytes(n_dest, c_dst, out);
+  if (use_igemm(df, c_src, c_dst, in)) return igemm_workspace_bytes(map->kvol, c_src, c_dst);
+  return 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ts_status_string(ts_status s) {
+  switch (s) {
+    case TS_OK: return "ok";
+    case TS_ERR_INVALID_ARG: return "invalid argument";
+    case TS_ERR_UNSUPPORTED: return "unsupported";
+    case TS_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* ts_version(void) { return "ts 0.1.0 (gfx950)"; }
+
+int64_t ts_hash_capacity(int64_t n, double rsv_ratio) {
+  if (n < 0 || !(rsv_ratio >= 1.0)) return -1;
+  double want = rsv_ratio * static_cast<double>(n);
+  int64_t cap = 64;
+  while (static_cast<double>(cap) < want) cap <<= 1;
+  return cap;
+}
+
+size_t ts_hash_table_bytes(int64_t cap) { return cap > 0 ? static_cast<size_t>(cap) * 12 : 0; }
+
+ts_status ts_hash_build(const int32_t* coords, int64_t n, int ndim, void* table, int64_t cap, uint32_t* err_flags,
+                        hipStream_t stream) {
+  if (n < 0 || n > kMaxRows || (n > 0 && !coords) || !table) return TS_ERR_INVALID_ARG;
+  if ((ndim != 2 && ndim != 3) || !is_pow2(cap) || cap < n || cap > kMaxRows) return TS_ERR_INVALID_ARG;
+  TS_TRY(launch_hash_build(coords, n, ndim, table, cap, err_flags, stream));
+  return TS_OK;
+}
+
+ts_status ts_hash_query(const void* table, int64_t cap, int ndim, const int32_t* q, int64_t m, int32_t* rows,
+                        hipStream_t stream) {
+  if (!table || m < 0 || m > kMaxRows || (m > 0 && (!q || !rows))) return TS_ERR_INVALID_ARG;
+  if ((ndim != 2 && ndim != 3) || !is_pow2(cap) || cap > kMaxRows) return TS_ERR_INVALID_ARG;
+  TS_TRY(launch_hash_query(table, cap, ndim, q, m, rows, stream));
+  return TS_OK;
+}
+
+size_t ts_support_scratch_bytes(int64_t n_in) { return n_in < 0 ? 0 : support_scratch_bytes(n_in); }
+
+ts_status ts_strided_support(const int32_t* in_coords, int64_t n_in, int ndim, int stride, int32_t* out_coords,
+                             int64_t* n_out, void* out_table, int64_t out_cap, void* scratch, size_t scratch_bytes,
+                             uint32_t* err_flags, hipStream_t stream) {
+  if (n_in < 0 || n_in > kMaxRows || (n_in > 0 && (!in_coords || !out_coords)) || !n_out || !out_table)
+    return TS_ERR_INVALID_ARG;
+  if ((ndim != 2 && ndim != 3) || stride < 1 || stride > 65535) return TS_ERR_INVALID_ARG;
+  if (!is_pow2(out_cap) || out_cap < n_in || out_cap > kMaxRows) return TS_ERR_INVALID_ARG;
+  if (!scratch || scratch_bytes < support_scratch_bytes(n_in)) return TS_ERR_INVALID_ARG;
+  TS_TRY(launch_strided_support(in_coords, n_in, ndim, stride, out_coords, n_out, out_table, out_cap, scratch,
+                                err_flags, stream));
+  return TS_OK;
+}
+
+size_t ts_kmap_bytes(int64_t n_in, int64_t n_out_cap, int ndim, int ksize, int stride, uint32_t flags) {
+  if (n_in < 0 || n_out_cap < 0 || !shape_ok(ndim, ksize, stride)) return 0;
+  ts_kmap tmp;
+  return layout_kmap(nullptr, &tmp, n_in, n_out_cap, ndim, ksize, stride, flags);
+}
+
+ts_status ts_kmap_build(const int32_t* in_coords, int64_t n_in, const void* in_table, int64_t in_cap,
+                        const int32_t* out_coords, int64_t n_out_cap, const int64_t* n_out, const void* out_table,
+                        int64_t out_cap, int ndim, int ksize, int stride, uint32_t flags, void* buf,
+                        size_t buf_bytes, ts_kmap* map, hipStream_t stream) {
+  if (!map || !buf || !in_table) return TS_ERR_INVALID_ARG;
+  if (!shape_ok(ndim, ksize, stride)) {
+    if ((ndim == 2 || ndim == 3) && ksize >= 1 && stride >= 1) return TS_ERR_UNSUPPORTED;
+    return TS_ERR_INVALID_ARG;
+  }
+  if (n_in < 0 || n_in > kMaxRows || (n_in > 0 && !in_coords) || !is_pow2(in_cap) || in_cap > kMaxRows)
+    return TS_ERR_INVALID_ARG;
+  if (flags & ~(TS_KMAP_PAIRS | TS_KMAP_BWD | TS_KMAP_NATURAL)) return TS_ERR_INVALID_ARG;
+  const int kvol = ipow(ksize, ndim);
+  if (stride == 1) {
+    if (ksize % 2 == 0) return TS_ERR_UNSUPPORTED;  // submanifold needs a centred kernel
+    out_coords = in_coords;
+    n_out_cap = n_in;
+  } else {
+    if (n_out_cap < 0 || n_out_cap > kMaxRows || (n_out_cap > 0 && !out_coords) || !n_out) return TS_ERR_INVALID_ARG;
+    if ((flags & TS_KMAP_BWD) && (!out_table || !is_pow2(out_cap) || out_cap > kMaxRows)) return TS_ERR_INVALID_ARG;
+  }
+  if (n_out_cap * kvol > kMaxRows || n_in * kvol > kMaxRows) return TS_ERR_UNSUPPORTED;
+  ts_kmap m;
+  const size_t need = layout_kmap(static_cast<char*>(buf), &m, n_in, n_out_cap, ndim, ksize, stride, flags);
+  if (buf_bytes < need) return TS_ERR_INVALID_ARG;
+  const bool natural = (flags & TS_KMAP_NATURAL) != 0;
+
+  RelBuild f;
+  f.mode = stride == 1 ? kModeSubm : kModeDown;
+  f.dest_coords = out_coords;
+  f.n_dest_cap = n_out_cap;
+  f.ndim = ndim;
+  f.ksize = ksize;
+  f.stride = stride;
+  f.kvol = kvol;
+  f.src_table = in_table;
+  f.src_cap = in_cap;
+  f.own_table = nullptr;
+  f.own_cap = 0;
+  if (stride == 1) {
+    TS_TRY(fill_i64(m.n_out, 1, n_in, stream));
+    f.n_dest = nullptr;
+  } else {
+    m.n_out = const_cast<int64_t*>(n_out);
+    f.n_dest = n_out;
+  }
+  m.fwd.n_dest = m.n_out;
+  TS_TRY(launch_rel_build(f, m.fwd, natural, m.scratch, stream));
+
+  if (stride > 1 && (flags & TS_KMAP_BWD)) {
+    RelBuild b = f;
+    b.mode = kModeUp;
+    b.dest_coords = in_coords;
+    b.n_dest_cap = n_in;
+    b.n_dest = nullptr;
+    b.src_table = out_table;
+    b.src_cap = out_cap;
+    b.own_table = in_table;
+    b.own_cap = in_cap;
+    TS_TRY(launch_rel_build(b, m.bwd, natural, m.scratch, stream));
+  }
+  if (flags & TS_KMAP_PAIRS) TS_TRY(launch_pairs_build(f, m.fwd, m.pair_start, m.pair_in, m.pair_out, m.scratch, stream));
+  *map = m;
+  return TS_OK;
+}
+
+size_t ts_conv_workspace_bytes(const ts_kmap* map, int cin, int cout, int op, ts_dtype in_dtype,
+                               ts_dataflow dataflow) {
+  if (!map || cin < 1 || cout < 1) return 0;
+  switch (op) {
+    case TS_OP_FWD: return conv_ws(map, cin, cout, in_dtype, TS_BF16, dataflow, map->n_out_cap);
+    case TS_OP_DGRAD: return conv_ws(map, cout, cin, in_dtype, TS_BF16, dataflow, map->n_in);
+    case TS_OP_WGRAD: return wgrad_workspace_bytes(map, cin, cout);
+  }
+  return 0;
+}
+
+ts_status ts_conv_fwd(const ts_kmap* map, const void* x, int cin, const void* w, int cout, void* y,
+                      ts_dtype in_dtype, ts_dtype out_dtype, ts_dataflow dataflow, void* ws, size_t ws_bytes,
+                      hipStream_t stream) {
+  ts_status st = check_conv(map, cin, cout, in_dtype, out_dtype);
+  if (st != TS_OK) return st;
+  if (dataflow < TS_DATAFLOW_AUTO || dataflow > TS_DATAFLOW_GATHER_SCATTER) return TS_ERR_INVALID_ARG;
+  if (!w || (map->n_in > 0 && !x) || (map->n_out_cap > 0 && !y)) return TS_ERR_INVALID_ARG;
+  const size_t need = conv_ws(map, cin, cout, in_dtype, out_dtype, dataflow, map->n_out_cap);
+  if (need > 0 && (!ws || ws_bytes < need)) return TS_ERR_INVALID_ARG;
+  ConvArgs a;
+  a.rel = &map->fwd;
+  a.kvol = map->kvol;
+  a.src = x;
+  a.c_src = cin;
+  a.dst = y;
+  a.c_dst = cout;
+  a.w = w;
+  a.w_cin = cin;
+  a.w_cout = cout;
+  a.transpose = false;
+  a.mirror = false;
+  a.in_dtype = in_dtype;
+  a.out_dtype = out_dtype;
+  if (dataflow == TS_DATAFLOW_GATHER_SCATTER) {
+    if (!(map->flags & TS_KMAP_PAIRS)) return TS_ERR_INVALID_ARG;
+    TS_TRY(launch_gather_scatter(map, a, false, map->n_out_cap, ws, stream));
+  } else if (use_igemm(dataflow, cin, cout, in_dtype)) {
+    TS_TRY(launch_igemm(a, ws, stream));
+  } else {
+    TS_TRY(launch_direct(a, stream));
+  }
+  return TS_OK;
+}
+
+ts_status ts_subm_conv_fwd(const ts_kmap* map, const void* x, int cin, const void* w, int cout, void* y,
+                           ts_dtype in_dtype, ts_dtype out_dtype, ts_dataflow dataflow, void* ws, size_t ws_bytes,
+                           hipStream_t stream) {
+  if (!map || map->stride != 1) return TS_ERR_INVALID_ARG;
+  return ts_conv_fwd(map, x, cin, w, cout, y, in_dtype, out_dtype, dataflow, ws, ws_bytes, stream);
+}
+
+ts_status ts_conv_fwd_strided(const int32_t* in_coords, int64_t n_in, int ndim, const void* in_table, int64_t in_cap,
+                              int ksize, int stride, uint32_t kmap_flags, int32_t* out_coords, int64_t* n_out,
+                              void* out_table, int64_t out_cap, uint32_t* err_flags, void* map_buf, size_t map_bytes,
+                              ts_kmap* map, const void* x, int cin, const void* w, int cout, void* y,
+                              ts_dtype in_dtype, ts_dtype out_dtype, ts_dataflow dataflow, void* ws, size_t ws_bytes,
+                              hipStream_t stream) {
+  if (stride < 2 || !map_buf || !map) return TS_ERR_INVALID_ARG;
+  if (!shape_ok(ndim, ksize, stride)) return TS_ERR_INVALID_ARG;
+  if (n_in < 0 || n_in > kMaxRows) return TS_ERR_INVALID_ARG;
+  const size_t kb = ts_kmap_bytes(n_in, n_in, ndim, ksize, stride, kmap_flags);
+  const size_t sb = support_scratch_bytes(n_in);
+  if (kb == 0 || map_bytes < kb + sb) return TS_ERR_INVALID_ARG;
+  // validate the convolution arguments before launching anything
+  {
+    const int kvol = ipow(ksize, ndim);
+    if (cin < 1 || cout < 1 || cin > kMaxChannels || cout > kMaxChannels || !w) return TS_ERR_INVALID_ARG;
+    if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return TS_ERR_INVALID_ARG;
+    if (out_dtype != TS_F32 && out_dtype != in_dtype) return TS_ERR_UNSUPPORTED;
+    if (n_in > 0 && (!x || !y)) return TS_ERR_INVALID_ARG;
+    if (dataflow == TS_DATAFLOW_GATHER_SCATTER && !(kmap_flags & TS_KMAP_PAIRS)) return TS_ERR_INVALID_ARG;
+    ts_kmap probe;
+    layout_kmap(nullptr, &probe, n_in, n_in, ndim, ksize, stride, kmap_flags);
+    const size_t need = conv_ws(&probe, cin, cout, in_dtype, out_dtype, dataflow, n_in);
+    if (need > 0 && (!ws || ws_bytes < need)) return TS_ERR_INVALID_ARG;
+    (void)kvol;
+  }
+  void* scratch = static_cast<char*>(map_buf) + kb;
+  ts_status st = ts_strided_support(in_coords, n_in, ndim, stride, out_coords, n_out, out_table, out_cap, scratch, sb,
+                                    err_flags, stream);
+  if (st != TS_OK) return st;
+  st = ts_kmap_build(in_coords, n_in, in_table, in_cap, out_coords, n_in, n_out, out_table, out_cap, ndim, ksize,
+                     stride, kmap_flags, map_buf, kb, map, stream);
+  if (st != TS_OK) return st;
+  return ts_conv_fwd(map, x, cin, w, cout, y, in_dtype, out_dtype, dataflow, ws, ws_bytes, stream);
+}
+
+ts_status ts_conv_bwd_dgrad(const ts_kmap* map, const void* dy, int cout, const void* w, int cin, void* dx,
+                            ts_dtype in_dtype, ts_dtype out_dtype, ts_dataflow dataflow, void* ws, size_t ws_bytes,
+                            hipStream_t stream) {
+  ts_status st = check_conv(map, cin, cout, in_dtype, out_dtype);
+  if (st != TS_OK) return st;
+  if (dataflow < TS_DATAFLOW_AUTO || dataflow > TS_DATAFLOW_GATHER_SCATTER) return TS_ERR_INVALID_ARG;
+  if (!w || (map->n_out_cap > 0 && !dy) || (map->n_in > 0 && !dx)) return TS_ERR_INVALID_ARG;
+  const size_t need = conv_ws(map, cout, cin, in_dtype, out_dtype, dataflow, map->n_in);
+  if (need > 0 && (!ws || ws_bytes < need)) return TS_ERR_INVALID_ARG;
+  ConvArgs a;
+  a.kvol = map->kvol;
+  a.src = dy;
+  a.c_src = cout;
+  a.dst = dx;
+  a.c_dst = cin;
+  a.w = w;
+  a.w_cin = cin;
+  a.w_cout = cout;
+  a.transpose = true;
+  a.in_dtype = in_dtype;
+  a.out_dtype = out_dtype;
+  if (dataflow == TS_DATAFLOW_GATHER_SCATTER) {
+    if (!(map->flags & TS_KMAP_PAIRS)) return TS_ERR_INVALID_ARG;
+    a.rel = &map->fwd;
+    a.mirror = false;
+    TS_TRY(launch_gather_scatter(map, a, true, map->n_in, ws, stream));
+    return TS_OK;
+  }
+  if (map->mirror_bwd) {
+    a.rel = &map->fwd;
+    a.mirror = true;
+  } else {
+    if (!(map->flags & TS_KMAP_BWD) || !map->bwd.tile_mask) return TS_ERR_INVALID_ARG;
+    a.rel = &map->bwd;
+    a.mirror = false;
+  }
+  if (use_igemm(dataflow, cout, cin, in_dtype)) {
+    TS_TRY(launch_igemm(a, ws, stream));
+  } else {
+    TS_TRY(launch_direct(a, stream));
+  }
+  return TS_OK;
+}
+
+ts_status ts_conv_bwd_wgrad(const ts_kmap* map, const void* x, int cin, const void* dy, int cout, ts_dtype in_dtype,
+                            float* dw, void* ws, size_t ws_bytes, hipStream_t stream) {
+  ts_status st = check_conv(map, cin, cout, in_dtype, TS_F32);
+  if (st != TS_OK) return st;
+  if (!(map->flags & TS_KMAP_PAIRS) || !dw || (map->n_in > 0 && !x) || (map->n_out_cap > 0 && !dy))
+    return TS_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < wgrad_workspace_bytes(map, cin, cout)) return TS_ERR_INVALID_ARG;
+  TS_TRY(launch_wgrad(map, x, cin, dy, cout, in_dtype, dw, ws, stream));
+  return TS_OK;
+}
+
+}  // extern "C"

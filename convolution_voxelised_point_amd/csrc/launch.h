@@ -1,0 +1,86 @@
+// Host-side launchers of the library's kernels (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "ts.h"
+
+namespace ts {
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// small fill kernels (graph-capturable replacements for memset); scan.hip
+hipError_t fill_i64(int64_t* p, int64_t n, int64_t v, hipStream_t s);
+hipError_t fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
+hipError_t fill_f32(float* p, int64_t n, float v, hipStream_t s);
+
+// scan.hip
+size_t scan_tmp_bytes(int64_t n);
+// out[i] = sum_{k<i} in[k] (in and out may alias); *total (device, may be
+// NULL) = sum of all.  `tmp` holds scan_tmp_bytes(n) bytes.
+hipError_t scan_exclusive_i32(const int32_t* in, int32_t* out, int64_t n, int64_t* total, void* tmp,
+                              hipStream_t s);
+
+// hash.hip
+hipError_t launch_hash_build(const int32_t* coords, int64_t n, int ndim, void* table, int64_t cap, uint32_t* flags,
+                             hipStream_t s);
+hipError_t launch_hash_query(const void* table, int64_t cap, int ndim, const int32_t* q, int64_t m, int32_t* rows,
+                             hipStream_t s);
+size_t support_scratch_bytes(int64_t n);
+hipError_t launch_strided_support(const int32_t* coords, int64_t n, int ndim, int stride, int32_t* out_coords,
+                                  int64_t* n_out, void* out_table, int64_t out_cap, void* scratch, uint32_t* flags,
+                                  hipStream_t s);
+
+// kmap.hip
+enum RelMode { kModeSubm = 0, kModeDown = 1, kModeUp = 2 };
+
+struct RelBuild {
+  int mode;
+  const int32_t* dest_coords;  // [n_dest_cap][ndim+1]
+  int64_t n_dest_cap;
+  const int64_t* n_dest;       // device count (may be NULL: = n_dest_cap)
+  int ndim, ksize, stride, kvol;
+  const void* src_table;       // table probed for neighbours
+  int64_t src_cap;
+  const void* own_table;       // kModeUp: input table for the ownership test
+  int64_t own_cap;
+};
+
+size_t rel_scratch_bytes(int64_t n_dest_cap, int kvol);
+hipError_t launch_rel_build(const RelBuild& b, const ts_rel& rel, bool natural, void* scratch, hipStream_t s);
+size_t pairs_scratch_bytes(int64_t n_dest_cap, int kvol);
+hipError_t launch_pairs_build(const RelBuild& b, const ts_rel& rel, int64_t* pair_start, int32_t* pair_in,
+                              int32_t* pair_out, void* scratch, hipStream_t s);
+
+// conv.hip
+struct ConvArgs {
+  const ts_rel* rel;  // relation walked (destination tiles)
+  int kvol;
+  const void* src;    // source features [n_src][c_src]
+  int c_src;
+  void* dst;          // destination features [n_dest][c_dst]
+  int c_dst;
+  const void* w;      // weights [kvol][cin][cout] of the layer
+  int w_cin, w_cout;
+  bool transpose;     // dgrad: contract over the layer's cout
+  bool mirror;        // dgrad of a submanifold map: use W[kvol-1-o]
+  ts_dtype in_dtype, out_dtype;
+};
+
+size_t igemm_workspace_bytes(int kvol, int c_src, int c_dst);
+bool igemm_supported(int c_src, int c_dst, ts_dtype in_dtype);
+hipError_t launch_igemm(const ConvArgs& a, void* ws, hipStream_t s);
+hipError_t launch_direct(const ConvArgs& a, hipStream_t s);
+
+size_t gs_workspace_bytes(int64_t n_dest_cap, int c_dst, ts_dtype out_dtype);
+hipError_t launch_gather_scatter(const ts_kmap* map, const ConvArgs& a, bool backward, int64_t n_dest_cap,
+                                 void* ws, hipStream_t s);
+
+// wgrad.hip
+size_t wgrad_workspace_bytes(const ts_kmap* map, int cin, int cout);
+hipError_t launch_wgrad(const ts_kmap* map, const void* x, int cin, const void* dy, int cout, ts_dtype dt, float* dw,
+                        void* ws, hipStream_t s);
+
+}  // namespace ts

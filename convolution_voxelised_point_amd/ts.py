@@ -1,0 +1,355 @@
+"""ctypes binding of ``libts.so`` (the C ABI declared in ``include/ts.h``).
+
+Argument marshalling only: every step of the sparse-convolution path runs in
+the library's HIP kernels.  PyTorch supplies device memory and the current
+HIP stream.  Importing this module loads the in-tree ``libts.so`` and fails
+loudly when it is missing -- there is no CPU fallback.
+
+The ``ts_*`` functions mirror the C entry points one to one.  The small
+classes below (``HashTable``, ``Kmap``) allocate the buffers the size queries
+ask for and keep them alive next to the C structs that point into them.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libts.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m convolution_voxelised_point_amd.build`")
+_lib = ctypes.CDLL(LIB_PATH)
+
+TS_OK, TS_ERR_INVALID_ARG, TS_ERR_UNSUPPORTED, TS_ERR_HIP = 0, 1, 2, 3
+TS_F32, TS_F16, TS_BF16 = 0, 1, 2
+TS_DATAFLOW_AUTO, TS_DATAFLOW_IMPLICIT_GEMM, TS_DATAFLOW_GATHER_SCATTER = 0, 1, 2
+TS_FLAG_DUP, TS_FLAG_RANGE, TS_FLAG_FULL = 1, 2, 4
+TS_KMAP_PAIRS, TS_KMAP_BWD, TS_KMAP_NATURAL = 1, 2, 4
+TS_OP_FWD, TS_OP_DGRAD, TS_OP_WGRAD = 0, 1, 2
+TS_TILE, TS_MAX_KVOL = 16, 64
+
+_DT = {torch.float32: TS_F32, torch.float16: TS_F16, torch.bfloat16: TS_BF16}
+
+_vp, _i64, _i32, _u32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_uint32, ctypes.c_size_t
+
+
+class TsRel(ctypes.Structure):
+    _fields_ = [("n_dest_cap", _i64), ("n_tiles", _i64), ("n_dest", _vp), ("tile_mask", _vp),
+                ("tile_rows", _vp), ("pool", _vp), ("row_mask", _vp)]
+
+
+class TsKmap(ctypes.Structure):
+    _fields_ = [("ndim", ctypes.c_int32), ("ksize", ctypes.c_int32), ("stride", ctypes.c_int32),
+                ("kvol", ctypes.c_int32), ("flags", ctypes.c_uint32), ("mirror_bwd", ctypes.c_int32),
+                ("n_in", _i64), ("n_out_cap", _i64), ("n_out", _vp), ("fwd", TsRel), ("bwd", TsRel),
+                ("pair_cap", _i64), ("pair_start", _vp), ("pair_in", _vp), ("pair_out", _vp),
+                ("scratch", _vp), ("scratch_bytes", _sz)]
+
+
+def _sig(name, res, args):
+    f = getattr(_lib, name)
+    f.restype = res
+    f.argtypes = args
+    return f
+
+
+_P = ctypes.POINTER(TsKmap)
+_lib_status_string = _sig("ts_status_string", ctypes.c_char_p, [_i32])
+_lib_version = _sig("ts_version", ctypes.c_char_p, [])
+_lib_hash_capacity = _sig("ts_hash_capacity", _i64, [_i64, ctypes.c_double])
+_lib_hash_table_bytes = _sig("ts_hash_table_bytes", _sz, [_i64])
+_lib_hash_build = _sig("ts_hash_build", _i32, [_vp, _i64, _i32, _vp, _i64, _vp, _vp])
+_lib_hash_query = _sig("ts_hash_query", _i32, [_vp, _i64, _i32, _vp, _i64, _vp, _vp])
+_lib_support_scratch_bytes = _sig("ts_support_scratch_bytes", _sz, [_i64])
+_lib_strided_support = _sig("ts_strided_support", _i32, [_vp, _i64, _i32, _i32, _vp, _vp, _vp, _i64, _vp, _sz, _vp, _vp])
+_lib_kmap_bytes = _sig("ts_kmap_bytes", _sz, [_i64, _i64, _i32, _i32, _i32, _u32])
+_lib_kmap_build = _sig("ts_kmap_build", _i32, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _i64, _i32, _i32, _i32, _u32,
+                                               _vp, _sz, _P, _vp])
+_lib_conv_workspace_bytes = _sig("ts_conv_workspace_bytes", _sz, [_P, _i32, _i32, _i32, _i32, _i32])
+_lib_conv_fwd = _sig("ts_conv_fwd", _i32, [_P, _vp, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _vp, _sz, _vp])
+_lib_subm_conv_fwd = _sig("ts_subm_conv_fwd", _i32, [_P, _vp, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _vp, _sz, _vp])
+_lib_conv_fwd_strided = _sig("ts_conv_fwd_strided", _i32,
+                             [_vp, _i64, _i32, _vp, _i64, _i32, _i32, _u32, _vp, _vp, _vp, _i64, _vp, _vp, _sz, _P,
+                              _vp, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _vp, _sz, _vp])
+_lib_conv_bwd_dgrad = _sig("ts_conv_bwd_dgrad", _i32, [_P, _vp, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _vp, _sz, _vp])
+_lib_conv_bwd_wgrad = _sig("ts_conv_bwd_wgrad", _i32, [_P, _vp, _i32, _vp, _i32, _i32, _vp, _vp, _sz, _vp])
+
+EXPORTED = ["ts_status_string", "ts_version", "ts_hash_capacity", "ts_hash_table_bytes", "ts_hash_build",
+            "ts_hash_query", "ts_support_scratch_bytes", "ts_strided_support", "ts_kmap_bytes", "ts_kmap_build",
+            "ts_conv_workspace_bytes", "ts_conv_fwd", "ts_subm_conv_fwd", "ts_conv_fwd_strided",
+            "ts_conv_bwd_dgrad", "ts_conv_bwd_wgrad"]
+
+
+class TsError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {ts_status_string(status)} ({status})")
+        self.status = status
+
+
+def _check(st: int, what: str) -> None:
+    if st != TS_OK:
+        raise TsError(st, what)
+
+
+def _p(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    assert t.is_cuda and t.is_contiguous(), "device tensors must be contiguous CUDA/HIP tensors"
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dt(t: torch.Tensor) -> int:
+    return _DT[t.dtype]
+
+
+# ---------------------------------------------------------------- 1:1 wrappers
+def ts_status_string(st: int) -> str:
+    return _lib_status_string(st).decode()
+
+
+def ts_version() -> str:
+    return _lib_version().decode()
+
+
+def ts_hash_capacity(n: int, rsv_ratio: float = 2.0) -> int:
+    return int(_lib_hash_capacity(n, rsv_ratio))
+
+
+def ts_hash_table_bytes(cap: int) -> int:
+    return int(_lib_hash_table_bytes(cap))
+
+
+def ts_hash_build(coords: torch.Tensor, table: torch.Tensor, cap: int, err_flags: Optional[torch.Tensor] = None,
+                  stream=None) -> None:
+    ndim = coords.shape[1] - 1
+    _check(_lib_hash_build(_p(coords), coords.shape[0], ndim, _p(table), cap, _p(err_flags), _stream(stream)),
+           "ts_hash_build")
+
+
+def ts_hash_query(table: torch.Tensor, cap: int, q: torch.Tensor, rows: torch.Tensor, stream=None) -> None:
+    _check(_lib_hash_query(_p(table), cap, q.shape[1] - 1, _p(q), q.shape[0], _p(rows), _stream(stream)),
+           "ts_hash_query")
+
+
+def ts_support_scratch_bytes(n_in: int) -> int:
+    return int(_lib_support_scratch_bytes(n_in))
+
+
+def ts_strided_support(in_coords, stride, out_coords, n_out, out_table, out_cap, scratch, err_flags=None,
+                       stream=None) -> None:
+    _check(_lib_strided_support(_p(in_coords), in_coords.shape[0], in_coords.shape[1] - 1, stride, _p(out_coords),
+                                _p(n_out), _p(out_table), out_cap, _p(scratch), scratch.numel(), _p(err_flags),
+                                _stream(stream)), "ts_strided_support")
+
+
+def ts_kmap_bytes(n_in: int, n_out_cap: int, ndim: int, ksize: int, stride: int, flags: int) -> int:
+    return int(_lib_kmap_bytes(n_in, n_out_cap, ndim, ksize, stride, flags))
+
+
+def ts_kmap_build(in_coords, in_table, in_cap, out_coords, n_out_cap, n_out, out_table, out_cap, ndim, ksize, stride,
+                  flags, buf, kmap: TsKmap, stream=None) -> None:
+    _check(_lib_kmap_build(_p(in_coords), in_coords.shape[0], _p(in_table), in_cap, _p(out_coords), n_out_cap,
+                           _p(n_out), _p(out_table), out_cap, ndim, ksize, stride, flags, _p(buf), buf.numel(),
+                           ctypes.byref(kmap), _stream(stream)), "ts_kmap_build")
+
+
+def ts_conv_workspace_bytes(kmap: TsKmap, cin: int, cout: int, op: int, in_dtype: int, dataflow: int) -> int:
+    return int(_lib_conv_workspace_bytes(ctypes.byref(kmap), cin, cout, op, in_dtype, dataflow))
+
+
+def ts_conv_fwd(kmap, x, w, y, dataflow=TS_DATAFLOW_AUTO, ws=None, stream=None, subm=False) -> None:
+    f = _lib_subm_conv_fwd if subm else _lib_conv_fwd
+    _check(f(ctypes.byref(kmap), _p(x), x.shape[1], _p(w), w.shape[2], _p(y), _dt(x), _dt(y), dataflow, _p(ws),
+             0 if ws is None else ws.numel(), _stream(stream)), "ts_subm_conv_fwd" if subm else "ts_conv_fwd")
+
+
+def ts_subm_conv_fwd(kmap, x, w, y, dataflow=TS_DATAFLOW_AUTO, ws=None, stream=None) -> None:
+    ts_conv_fwd(kmap, x, w, y, dataflow, ws, stream, subm=True)
+
+
+def ts_conv_fwd_strided(in_coords, in_table, in_cap, ksize, stride, kmap_flags, out_coords, n_out, out_table, out_cap,
+                        err_flags, map_buf, kmap, x, w, y, dataflow=TS_DATAFLOW_AUTO, ws=None, stream=None) -> None:
+    _check(_lib_conv_fwd_strided(_p(in_coords), in_coords.shape[0], in_coords.shape[1] - 1, _p(in_table), in_cap,
+                                 ksize, stride, kmap_flags, _p(out_coords), _p(n_out), _p(out_table), out_cap,
+                                 _p(err_flags), _p(map_buf), map_buf.numel(), ctypes.byref(kmap), _p(x), x.shape[1],
+                                 _p(w), w.shape[2], _p(y), _dt(x), _dt(y), dataflow, _p(ws),
+                                 0 if ws is None else ws.numel(), _stream(stream)), "ts_conv_fwd_strided")
+
+
+def ts_conv_bwd_dgrad(kmap, dy, w, dx, dataflow=TS_DATAFLOW_AUTO, ws=None, stream=None) -> None:
+    _check(_lib_conv_bwd_dgrad(ctypes.byref(kmap), _p(dy), dy.shape[1], _p(w), dx.shape[1], _p(dx), _dt(dy), _dt(dx),
+                               dataflow, _p(ws), 0 if ws is None else ws.numel(), _stream(stream)),
+           "ts_conv_bwd_dgrad")
+
+
+def ts_conv_bwd_wgrad(kmap, x, dy, dw, ws, stream=None) -> None:
+    _check(_lib_conv_bwd_wgrad(ctypes.byref(kmap), _p(x), x.shape[1], _p(dy), dy.shape[1], _dt(x), _p(dw), _p(ws),
+                               ws.numel(), _stream(stream)), "ts_conv_bwd_wgrad")
+
+
+# ---------------------------------------------------------------- owners of buffers
+def _bytes(n: int, device) -> torch.Tensor:
+    return torch.empty(max(int(n), 1), dtype=torch.uint8, device=device)
+
+
+class HashTable:
+    """A coordinate table sized by the reserve ratio."""
+
+    def __init__(self, coords: torch.Tensor, rsv_ratio: float = 2.0, err_flags: Optional[torch.Tensor] = None,
+                 build: bool = True, stream=None):
+        self.ndim = coords.shape[1] - 1
+        self.cap = ts_hash_capacity(coords.shape[0], rsv_ratio)
+        self.buf = _bytes(ts_hash_table_bytes(self.cap), coords.device)
+        if build:
+            ts_hash_build(coords, self.buf, self.cap, err_flags, stream)
+
+    def query(self, q: torch.Tensor, stream=None) -> torch.Tensor:
+        rows = torch.empty(q.shape[0], dtype=torch.int32, device=q.device)
+        ts_hash_query(self.buf, self.cap, q, rows, stream)
+        return rows
+
+
+class Kmap:
+    """A built kernel map: the C struct plus the buffers it points into."""
+
+    def __init__(self, struct: TsKmap, buf: torch.Tensor, keep=()):
+        self.s = struct
+        self.buf = buf
+        self.keep = keep
+
+    @property
+    def kvol(self) -> int:
+        return self.s.kvol
+
+    def n_out(self) -> int:
+        """Output row count (reads a device scalar: synchronises)."""
+        base = self.buf.data_ptr()
+        if self.s.n_out >= base and self.s.n_out < base + self.buf.numel():
+            return int(self._view(self.s.n_out, torch.int64, 1)[0])
+        for t in self.keep:
+            if isinstance(t, torch.Tensor) and t.data_ptr() == self.s.n_out:
+                return int(t[0])
+        raise RuntimeError("n_out pointer not owned")
+
+    def _view(self, ptr: int, dtype, count: int) -> torch.Tensor:
+        off = ptr - self.buf.data_ptr()
+        itemsize = torch.tensor([], dtype=dtype).element_size()
+        assert 0 <= off and off + count * itemsize <= self.buf.numel()
+        return self.buf[off:off + count * itemsize].view(dtype)
+
+    def rel_arrays(self, which: str = "fwd") -> dict:
+        r = getattr(self.s, which)
+        nt, kv = r.n_tiles, self.s.kvol
+        return {
+            "tile_mask": self._view(r.tile_mask, torch.int64, nt),
+            "tile_rows": self._view(r.tile_rows, torch.int32, nt * TS_TILE),
+            "pool": self._view(r.pool, torch.int32, nt * kv * TS_TILE),
+            "row_mask": self._view(r.row_mask, torch.int64, r.n_dest_cap),
+        }
+
+    def pairs(self):
+        """(pair_start[kvol+1], pair_in[P], pair_out[P]) on the host."""
+        ps = self._view(self.s.pair_start, torch.int64, self.s.kvol + 1).cpu().numpy()
+        P = int(ps[-1])
+        pin = self._view(self.s.pair_in, torch.int32, max(P, 0)).cpu().numpy()
+        pout = self._view(self.s.pair_out, torch.int32, max(P, 0)).cpu().numpy()
+        return ps, pin, pout
+
+
+def decode_rel(arrs: dict, kvol: int, transposed: bool = False) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Host decode of a tiled relation into (in, out, offset) triples.
+
+    Used by tests; ``transposed`` marks a relation whose destinations are
+    input rows."""
+    tm = arrs["tile_mask"].cpu().numpy().view(np.uint64)
+    rows = arrs["tile_rows"].cpu().numpy().reshape(-1, TS_TILE)
+    pool = arrs["pool"].cpu().numpy().reshape(-1, kvol, TS_TILE)
+    ti, to, tf = [], [], []
+    for t in range(tm.shape[0]):
+        m = int(tm[t])
+        k = 0
+        o = 0
+        while m:
+            if m & 1:
+                src = pool[t, k]
+                dst = rows[t]
+                ok = (src >= 0) & (dst >= 0)
+                ti.append(src[ok]); to.append(dst[ok]); tf.append(np.full(int(ok.sum()), o, np.int32))
+                k += 1
+            m >>= 1
+            o += 1
+    cat = (lambda a: np.concatenate(a).astype(np.int32) if a else np.zeros(0, np.int32))
+    a, b, c = cat(ti), cat(to), cat(tf)
+    return (b, a, c) if transposed else (a, b, c)
+
+
+def build_kmap(coords: torch.Tensor, table: HashTable, ksize: int, stride: int = 1, flags: int = 0,
+               out_coords: Optional[torch.Tensor] = None, n_out: Optional[torch.Tensor] = None,
+               out_table: Optional[HashTable] = None, stream=None) -> Kmap:
+    """Allocate and build a kernel map (submanifold when stride == 1)."""
+    ndim = coords.shape[1] - 1
+    n_in = coords.shape[0]
+    n_out_cap = n_in if stride == 1 else out_coords.shape[0]
+    nbytes = ts_kmap_bytes(n_in, n_out_cap, ndim, ksize, stride, flags)
+    if nbytes == 0:
+        raise TsError(TS_ERR_INVALID_ARG, "ts_kmap_bytes")
+    buf = _bytes(nbytes, coords.device)
+    km = TsKmap()
+    ts_kmap_build(coords, table.buf, table.cap, out_coords, n_out_cap, n_out,
+                  None if out_table is None else out_table.buf, 0 if out_table is None else out_table.cap,
+                  ndim, ksize, stride, flags, buf, km, stream)
+    return Kmap(km, buf, keep=(coords, table, out_coords, n_out, out_table))
+
+
+def strided_support(coords: torch.Tensor, stride: int, rsv_ratio: float = 2.0, err_flags=None, stream=None):
+    """(out_coords [capacity n_in], n_out device scalar, out table)."""
+    n = coords.shape[0]
+    out = torch.zeros_like(coords)
+    n_out = torch.zeros(1, dtype=torch.int64, device=coords.device)
+    table = HashTable(coords, rsv_ratio, build=False)
+    scratch = _bytes(ts_support_scratch_bytes(n), coords.device)
+    ts_strided_support(coords, stride, out, n_out, table.buf, table.cap, scratch, err_flags, stream)
+    return out, n_out, table
+
+
+def workspace(kmap: Kmap, cin: int, cout: int, op: int, dtype: torch.dtype, dataflow: int = TS_DATAFLOW_AUTO):
+    n = ts_conv_workspace_bytes(kmap.s, cin, cout, op, _DT[dtype], dataflow)
+    return _bytes(n, kmap.buf.device) if n > 0 else None
+
+
+def conv_fwd(kmap: Kmap, x: torch.Tensor, w: torch.Tensor, out_dtype=None, dataflow=TS_DATAFLOW_AUTO, ws=None,
+             stream=None) -> torch.Tensor:
+    out_dtype = out_dtype or x.dtype
+    y = torch.empty((kmap.s.n_out_cap, w.shape[2]), dtype=out_dtype, device=x.device)
+    if ws is None:
+        ws = workspace(kmap, w.shape[1], w.shape[2], TS_OP_FWD, x.dtype, dataflow)
+    ts_conv_fwd(kmap.s, x, w, y, dataflow, ws, stream, subm=kmap.s.stride == 1)
+    return y
+
+
+def conv_dgrad(kmap: Kmap, dy: torch.Tensor, w: torch.Tensor, out_dtype=None, dataflow=TS_DATAFLOW_AUTO, ws=None,
+               stream=None) -> torch.Tensor:
+    out_dtype = out_dtype or dy.dtype
+    dx = torch.empty((kmap.s.n_in, w.shape[1]), dtype=out_dtype, device=dy.device)
+    if ws is None:
+        ws = workspace(kmap, w.shape[1], w.shape[2], TS_OP_DGRAD, dy.dtype, dataflow)
+    ts_conv_bwd_dgrad(kmap.s, dy, w, dx, dataflow, ws, stream)
+    return dx
+
+
+def conv_wgrad(kmap: Kmap, x: torch.Tensor, dy: torch.Tensor, ws=None, stream=None) -> torch.Tensor:
+    dw = torch.empty((kmap.kvol, x.shape[1], dy.shape[1]), dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = workspace(kmap, x.shape[1], dy.shape[1], TS_OP_WGRAD, x.dtype)
+    ts_conv_bwd_wgrad(kmap.s, x, dy, dw, ws, stream)
+    return dw

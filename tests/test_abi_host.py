@@ -1,0 +1,156 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function ``include/ts.h`` declares, answers size queries, and rejects
+bad arguments before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ts.h")
+LIB = os.path.join(ROOT, "convolution_voxelised_point_amd", "libts.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libts.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ts_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def ts():
+    from convolution_voxelised_point_amd import ts as mod
+    return mod
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(LIB)
+    names = declared_functions()
+    assert len(names) >= 16
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_binding_lists_all_declared(ts):
+    assert sorted(ts.EXPORTED) == declared_functions()
+
+
+def test_version_and_status(ts):
+    assert "gfx950" in ts.ts_version()
+    assert ts.ts_status_string(0) == "ok"
+    assert ts.ts_status_string(1) == "invalid argument"
+    assert ts.ts_status_string(3) == "HIP error"
+
+
+def test_hash_capacity(ts):
+    assert ts.ts_hash_capacity(0, 2.0) == 64
+    assert ts.ts_hash_capacity(100, 2.0) == 256
+    assert ts.ts_hash_capacity(102835, 2.0) == 262144
+    assert ts.ts_hash_capacity(1000, 1.0) == 1024
+    assert ts.ts_hash_capacity(1025, 1.0) == 2048
+    assert ts.ts_hash_capacity(10, 0.5) == -1
+    assert ts.ts_hash_capacity(-1, 2.0) == -1
+    assert ts.ts_hash_table_bytes(1024) == 12 * 1024
+
+
+def test_kmap_bytes(ts):
+    b = ts.ts_kmap_bytes(1000, 1000, 3, 3, 1, 0)
+    assert b > 1000 * 27 * 4
+    assert ts.ts_kmap_bytes(1000, 1000, 3, 3, 1, ts.TS_KMAP_PAIRS) > b
+    assert ts.ts_kmap_bytes(1000, 800, 3, 2, 2, ts.TS_KMAP_BWD) > ts.ts_kmap_bytes(1000, 800, 3, 2, 2, 0)
+    assert ts.ts_kmap_bytes(10, 10, 4, 3, 1, 0) == 0   # ndim 4
+    assert ts.ts_kmap_bytes(10, 10, 3, 5, 1, 0) == 0   # 125 offsets > 64
+    assert ts.ts_kmap_bytes(-1, 10, 3, 3, 1, 0) == 0
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
+
+
+def test_hash_build_rejects(ts):
+    L = ts._lib_hash_build
+    assert L(None, 10, 3, FAKE, 64, None, None) == ts.TS_ERR_INVALID_ARG          # null coords
+    assert L(FAKE, 10, 3, None, 64, None, None) == ts.TS_ERR_INVALID_ARG          # null table
+    assert L(FAKE, -1, 3, FAKE, 64, None, None) == ts.TS_ERR_INVALID_ARG          # n < 0
+    assert L(FAKE, 10, 4, FAKE, 64, None, None) == ts.TS_ERR_INVALID_ARG          # ndim
+    assert L(FAKE, 10, 3, FAKE, 48, None, None) == ts.TS_ERR_INVALID_ARG          # cap not a power of 2
+    assert L(FAKE, 100, 3, FAKE, 64, None, None) == ts.TS_ERR_INVALID_ARG         # cap < n
+
+
+def test_hash_query_rejects(ts):
+    L = ts._lib_hash_query
+    assert L(None, 64, 3, FAKE, 5, FAKE, None) == ts.TS_ERR_INVALID_ARG
+    assert L(FAKE, 64, 3, None, 5, FAKE, None) == ts.TS_ERR_INVALID_ARG
+    assert L(FAKE, 63, 3, FAKE, 5, FAKE, None) == ts.TS_ERR_INVALID_ARG
+    assert L(FAKE, 64, 1, FAKE, 5, FAKE, None) == ts.TS_ERR_INVALID_ARG
+
+
+def test_kmap_build_rejects(ts):
+    L = ts._lib_kmap_build
+    km = ts.TsKmap()
+    ref = ctypes.byref(km)
+    need = ts.ts_kmap_bytes(100, 100, 3, 3, 1, 0)
+    args = dict(in_coords=FAKE, n_in=100, in_table=FAKE, in_cap=256, out_coords=None, n_out_cap=0, n_out=None,
+                out_table=None, out_cap=0, ndim=3, ksize=3, stride=1, flags=0, buf=FAKE, buf_bytes=need)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return L(a["in_coords"], a["n_in"], a["in_table"], a["in_cap"], a["out_coords"], a["n_out_cap"], a["n_out"],
+                 a["out_table"], a["out_cap"], a["ndim"], a["ksize"], a["stride"], a["flags"], a["buf"],
+                 a["buf_bytes"], ref, None)
+
+    assert call(buf_bytes=need - 1) == ts.TS_ERR_INVALID_ARG       # short buffer
+    assert call(ksize=2) == ts.TS_ERR_UNSUPPORTED                  # even submanifold kernel
+    assert call(ksize=5) == ts.TS_ERR_UNSUPPORTED                  # 125 offsets
+    assert call(ndim=1) == ts.TS_ERR_INVALID_ARG
+    assert call(stride=0) == ts.TS_ERR_INVALID_ARG
+    assert call(in_table=None) == ts.TS_ERR_INVALID_ARG
+    assert call(in_cap=100) == ts.TS_ERR_INVALID_ARG
+    assert call(flags=64) == ts.TS_ERR_INVALID_ARG
+    # strided maps need the output count and coordinates
+    sneed = ts.ts_kmap_bytes(100, 100, 3, 2, 2, ts.TS_KMAP_BWD)
+    assert call(stride=2, ksize=2, n_out_cap=100, buf_bytes=sneed) == ts.TS_ERR_INVALID_ARG
+    assert call(stride=2, ksize=2, n_out_cap=100, out_coords=FAKE, n_out=FAKE, flags=ts.TS_KMAP_BWD,
+                buf_bytes=sneed) == ts.TS_ERR_INVALID_ARG          # BWD without an output table
+
+
+def test_conv_rejects(ts):
+    km = ts.TsKmap()
+    ref = ctypes.byref(km)
+    # an unbuilt map
+    assert ts._lib_conv_fwd(ref, FAKE, 16, FAKE, 16, FAKE, 1, 1, 0, None, 0, None) == ts.TS_ERR_INVALID_ARG
+    # a map that looks built
+    km.kvol = 27
+    km.stride = 1
+    km.n_in = km.n_out_cap = 100
+    km.fwd.tile_mask = 0x2000
+    km.fwd.n_tiles = 7
+    assert ts._lib_conv_fwd(ref, FAKE, 0, FAKE, 16, FAKE, 1, 1, 0, None, 0, None) == ts.TS_ERR_INVALID_ARG   # cin 0
+    assert ts._lib_conv_fwd(ref, FAKE, 16, FAKE, 16, FAKE, 7, 1, 0, None, 0, None) == ts.TS_ERR_INVALID_ARG  # dtype
+    assert ts._lib_conv_fwd(ref, FAKE, 16, FAKE, 16, FAKE, 1, 2, 0, None, 0, None) == ts.TS_ERR_UNSUPPORTED  # f16->bf16
+    assert ts._lib_conv_fwd(ref, FAKE, 64, FAKE, 64, FAKE, 1, 1, 0, None, 0, None) == ts.TS_ERR_INVALID_ARG  # no ws
+    assert ts._lib_conv_fwd(ref, FAKE, 64, FAKE, 64, FAKE, 1, 1, 2, FAKE, 1 << 30, None) == ts.TS_ERR_INVALID_ARG  # GS w/o pairs
+    assert ts._lib_conv_fwd(ref, FAKE, 16, None, 16, FAKE, 1, 1, 0, None, 0, None) == ts.TS_ERR_INVALID_ARG  # null w
+    assert ts._lib_conv_fwd(ref, FAKE, 16, FAKE, 16, FAKE, 1, 1, 9, None, 0, None) == ts.TS_ERR_INVALID_ARG  # dataflow
+    # wgrad needs the pair lists
+    assert ts._lib_conv_bwd_wgrad(ref, FAKE, 16, FAKE, 16, 1, FAKE, FAKE, 1 << 30, None) == ts.TS_ERR_INVALID_ARG
+    # dgrad of a strided map needs the transposed relation
+    km.stride = 2
+    km.mirror_bwd = 0
+    assert ts._lib_conv_bwd_dgrad(ref, FAKE, 16, FAKE, 16, FAKE, 1, 1, 0, None, 0, None) == ts.TS_ERR_INVALID_ARG
+    km.stride = 1
+    assert ts._lib_subm_conv_fwd(ref, FAKE, 16, FAKE, 16, FAKE, 9, 1, 0, None, 0, None) == ts.TS_ERR_INVALID_ARG
+
+
+def test_workspace_sizes(ts):
+    km = ts.TsKmap()
+    km.kvol = 27
+    km.n_in = km.n_out_cap = 1000
+    km.pair_cap = 27000
+    ref = ctypes.byref(km)
+    assert ts._lib_conv_workspace_bytes(ref, 64, 64, ts.TS_OP_FWD, ts.TS_F16, 0) >= 27 * 64 * 64 * 2
+    assert ts._lib_conv_workspace_bytes(ref, 16, 16, ts.TS_OP_FWD, ts.TS_F32, 0) == 0
+    assert ts._lib_conv_workspace_bytes(ref, 64, 64, ts.TS_OP_FWD, ts.TS_F16, 2) >= 1000 * 64 * 4
+    assert ts._lib_conv_workspace_bytes(ref, 64, 64, ts.TS_OP_WGRAD, ts.TS_F16, 0) >= 27 * 64 * 64 * 4

@@ -1,0 +1,143 @@
+"""GPU parity of the contraction -- forward, dgrad, wgrad -- against the fp64
+CPU oracle run on the same (already rounded) inputs, for both dataflows, plus
+bitwise repeatability and the degenerate shapes."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from convolution_voxelised_point_amd import synth
+from helpers import assert_feature_close, dev
+
+pytestmark = pytest.mark.gpu
+
+DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+def make_problem(coords, ksize, stride, cin, cout, dtype, seed):
+    """Device tensors, the GPU map and the oracle's triples for one layer."""
+    from convolution_voxelised_point_amd import ts
+    ndim = coords.shape[1] - 1
+    kvol = ksize ** ndim
+    cd = dev(coords)
+    tab = ts.HashTable(cd, 2.0)
+    flags = ts.TS_KMAP_PAIRS | ts.TS_KMAP_BWD
+    if stride == 1:
+        km = ts.build_kmap(cd, tab, ksize, 1, ts.TS_KMAP_PAIRS)
+        oc = coords
+    else:
+        out, n_out, otab = ts.strided_support(cd, stride)
+        km = ts.build_kmap(cd, tab, ksize, stride, flags, out_coords=out, n_out=n_out, out_table=otab)
+        oc = oracle.strided_support(coords, stride)
+        assert km.n_out() == oc.shape[0]
+    tr = oracle.kmap(coords, oc, ksize, stride)
+    x = synth.normal(seed, (coords.shape[0], cin), 1.0, dtype)
+    w = synth.weight(seed + 1, kvol, cin, cout, dtype)
+    dy = synth.normal(seed + 2, (oc.shape[0], cout), 1.0, dtype)
+    return km, tr, oc, x, w, dy
+
+
+CONV_CASES = [
+    # name, coords, ksize, stride, cin, cout, dtype
+    ("tiny_f32_16", synth.make("tiny").coords, 3, 1, 16, 16, "f32"),
+    ("lidar_f16_64", synth.make("lidar", scale=0.04).coords, 3, 1, 64, 64, "f16"),
+    ("lidar_bf16_128", synth.make("lidar", scale=0.03).coords, 3, 1, 128, 128, "bf16"),
+    ("fuzz_f16_32x16", synth.random_coords(11, 1500, 3, 2, 14, lo=-7), 3, 1, 32, 16, "f16"),
+    ("fuzz_bf16_96x48", synth.random_coords(12, 900, 3, 3, 12, lo=-6), 3, 1, 96, 48, "bf16"),
+    ("fuzz_f16_odd", synth.random_coords(13, 700, 3, 2, 10), 3, 1, 3, 5, "f16"),
+    ("pixels_f16_1x8", synth.make("pixels", scale=0.03).coords, 3, 1, 1, 8, "f16"),
+    ("pixels_f16_8x8", synth.make("pixels", scale=0.03).coords, 3, 1, 8, 8, "f16"),
+    ("pixels_f32_k5", synth.random_coords(14, 800, 2, 2, 40), 5, 1, 4, 6, "f32"),
+    ("down_f16_64x128", synth.make("down", scale=0.03).coords, 2, 2, 64, 128, "f16"),
+    ("down_bf16_k3s2", synth.random_coords(15, 1500, 3, 2, 24, lo=-12), 3, 2, 32, 32, "bf16"),
+    ("down_f32_2d", synth.random_coords(16, 900, 2, 2, 50), 2, 2, 7, 9, "f32"),
+]
+CONV_IDS = [c[0] for c in CONV_CASES]
+
+
+@pytest.mark.parametrize("case", CONV_CASES, ids=CONV_IDS)
+def test_forward(ts, case):
+    name, c, k, s, cin, cout, dt = case
+    km, tr, oc, x, w, _ = make_problem(c, k, s, cin, cout, dt, 500)
+    ref = oracle.conv_fwd(tr, x, w, oc.shape[0])
+    xd, wd = dev(x), dev(w)
+    for out_dtype in (torch.float32, DT[dt]):
+        for df in (ts.TS_DATAFLOW_AUTO, ts.TS_DATAFLOW_GATHER_SCATTER):
+            y = ts.conv_fwd(km, xd, wd, out_dtype=out_dtype, dataflow=df)
+            assert_feature_close(y[:oc.shape[0]], ref, DT[dt], f"{name} fwd out={out_dtype} df={df}")
+
+
+@pytest.mark.parametrize("case", CONV_CASES, ids=CONV_IDS)
+def test_dgrad(ts, case):
+    name, c, k, s, cin, cout, dt = case
+    km, tr, oc, x, w, dy = make_problem(c, k, s, cin, cout, dt, 600)
+    ref = oracle.conv_dgrad(tr, dy, w, c.shape[0])
+    dyd = torch.zeros((c.shape[0] if s == 1 else km.s.n_out_cap, cout), dtype=DT[dt], device="cuda")
+    dyd[:oc.shape[0]] = dev(dy)
+    wd = dev(w)
+    for out_dtype in (torch.float32, DT[dt]):
+        for df in (ts.TS_DATAFLOW_AUTO, ts.TS_DATAFLOW_GATHER_SCATTER):
+            dx = ts.conv_dgrad(km, dyd, wd, out_dtype=out_dtype, dataflow=df)
+            assert_feature_close(dx, ref, DT[dt], f"{name} dgrad out={out_dtype} df={df}")
+
+
+@pytest.mark.parametrize("case", CONV_CASES, ids=CONV_IDS)
+def test_wgrad(ts, case):
+    name, c, k, s, cin, cout, dt = case
+    km, tr, oc, x, w, dy = make_problem(c, k, s, cin, cout, dt, 700)
+    ref = oracle.conv_wgrad(tr, x, dy, w.shape[0])
+    dyd = torch.zeros((km.s.n_out_cap, cout), dtype=DT[dt], device="cuda")
+    dyd[:oc.shape[0]] = dev(dy)
+    dw = ts.conv_wgrad(km, dev(x), dyd)
+    assert_feature_close(dw, ref, DT[dt], f"{name} wgrad")
+
+
+def test_bitwise_repeatable(ts):
+    c = synth.make("lidar", scale=0.05).coords
+    km, tr, oc, x, w, dy = make_problem(c, 3, 1, 64, 64, "f16", 800)
+    xd, wd, dyd = dev(x), dev(w), dev(dy)
+    for _ in range(2):
+        a = [ts.conv_fwd(km, xd, wd), ts.conv_dgrad(km, dyd, wd), ts.conv_wgrad(km, xd, dyd)]
+        b = [ts.conv_fwd(km, xd, wd), ts.conv_dgrad(km, dyd, wd), ts.conv_wgrad(km, xd, dyd)]
+        for u, v in zip(a, b):
+            assert torch.equal(u, v)
+    # a rebuilt map gives the same outputs too
+    km2, *_ = make_problem(c, 3, 1, 64, 64, "f16", 800)
+    assert torch.equal(ts.conv_fwd(km, xd, wd), ts.conv_fwd(km2, xd, wd))
+
+
+def test_dataflows_agree(ts):
+    """Implicit GEMM and gather-scatter give the same result for a fixed
+    relation and weight tensor, within floating-point tolerance."""
+    c = synth.make("lidar", scale=0.05).coords
+    km, tr, oc, x, w, dy = make_problem(c, 3, 1, 64, 64, "f16", 900)
+    xd, wd = dev(x), dev(w)
+    a = ts.conv_fwd(km, xd, wd, out_dtype=torch.float32, dataflow=ts.TS_DATAFLOW_IMPLICIT_GEMM)
+    b = ts.conv_fwd(km, xd, wd, out_dtype=torch.float32, dataflow=ts.TS_DATAFLOW_GATHER_SCATTER)
+    assert_feature_close(a, b.double().cpu().numpy(), torch.float16, "igemm vs gather-scatter")
+
+
+@pytest.mark.parametrize("n", [0, 1, 15, 16, 17])
+def test_degenerate_sizes(ts, n):
+    c = synth.random_coords(40 + n, 4 * n, 3, 1, 6) if n else np.zeros((0, 4), np.int32)
+    c = c[:n]
+    assert c.shape[0] == n
+    km, tr, oc, x, w, dy = make_problem(c, 3, 1, 64, 64, "f16", 1000)
+    xd, wd, dyd = dev(x), dev(w), dev(dy)
+    y = ts.conv_fwd(km, xd, wd, out_dtype=torch.float32)
+    assert_feature_close(y, oracle.conv_fwd(tr, x, w, n), torch.float16, "fwd")
+    dx = ts.conv_dgrad(km, dyd, wd, out_dtype=torch.float32)
+    assert_feature_close(dx, oracle.conv_dgrad(tr, dy, w, n), torch.float16, "dgrad")
+    dw = ts.conv_wgrad(km, xd, dyd)
+    assert_feature_close(dw, oracle.conv_wgrad(tr, x, dy, 27), torch.float16, "wgrad")
+
+
+def test_isolated_rows_get_zero(ts):
+    """Rows with no neighbour but themselves get x W_centre; repeated rows get 0."""
+    c = np.array([[0, 0, 0, 0], [0, 10, 10, 10], [1, 0, 0, 0], [0, 10, 10, 10]], np.int32)
+    km, tr, oc, x, w, dy = make_problem(c, 3, 1, 32, 16, "f16", 1100)
+    y = ts.conv_fwd(km, dev(x), dev(w), out_dtype=torch.float32).cpu().double().numpy()
+    xc, wc = x.double().numpy(), w.double().numpy()
+    for i in range(3):
+        np.testing.assert_allclose(y[i], xc[i] @ wc[13], rtol=1e-5, atol=1e-5)
+    assert np.all(y[3] == 0)
