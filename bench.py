@@ -1,0 +1,372 @@
+"""Benchmark of the sparse-convolution hot path on one MI355X.
+
+A step is one pass of the whole path over the LiDAR-like ring-scan scene
+(~103k voxels, one batch): coordinate hash build, kernel-map build and the
+SubmConv3d k=3, 64 -> 64 channel fp16 forward (fp32 accumulation).  The
+printed JSON line reports map-valid TFLOP/s of that step (2 * pairs * Cin *
+Cout per step time), the per-stage times taken with HIP events on the launch
+stream, the roofline position of the dominant kernel, and the CPU oracle
+timed on this host.  The other workloads (strided 64 -> 128 downsampling,
+the 2-D pixel tracks, the bf16 128-channel training step) are measured the
+same way and reported under "secondary".
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+                       [--only lidar] [--copy-calib MB]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from convolution_voxelised_point_amd import synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+MFMA_F16_PEAK_TFLOPS = 2500.0  # dense fp16/bf16 MFMA
+
+
+def popcount_sum(masks: torch.Tensor, kvol: int) -> int:
+    """Number of (in, out, offset) pairs = set bits over the row masks."""
+    m = masks.to(torch.int64)
+    total = 0
+    for o in range(kvol):
+        total += int(((m >> o) & 1).sum().item())
+    return total
+
+
+class Timer:
+    """HIP events on the current stream around named stages of a step."""
+
+    def __init__(self, names):
+        self.names = names
+        self.acc = {n: 0.0 for n in names}
+        self.count = 0
+        self.pending = []
+
+    def step(self, fns):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)]
+        ev[0].record()
+        for i, f in enumerate(fns):
+            f()
+            ev[i + 1].record()
+        self.pending.append(ev)
+
+    def collect(self):
+        for ev in self.pending:
+            for i, n in enumerate(self.names):
+                self.acc[n] += ev[i].elapsed_time(ev[i + 1]) * 1e3  # us
+            self.count += 1
+        self.pending = []
+
+    def mean_us(self):
+        return {n: self.acc[n] / max(self.count, 1) for n in self.names}
+
+
+def run_steps(fns, names, steps, warmup):
+    for _ in range(warmup):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    timer = Timer(names)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        timer.step(fns)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    timer.collect()
+    return (t1 - t0) * 1e3 / steps, timer.mean_us()
+
+
+# ---------------------------------------------------------------- workloads
+def lidar_setup(ts, w):
+    dev = torch.device("cuda")
+    coords = torch.from_numpy(w.coords).to(dev)
+    x = w.x.to(dev)
+    wt = w.w.to(dev)
+    n = coords.shape[0]
+    flags = torch.zeros(1, dtype=torch.int32, device=dev)
+    table = ts.HashTable(coords, 2.0, build=False)
+    kbytes = ts.ts_kmap_bytes(n, n, 3, 3, 1, 0)
+    kbuf = torch.empty(kbytes, dtype=torch.uint8, device=dev)
+    km = ts.TsKmap()
+    y = torch.empty((n, w.cout), dtype=torch.float16, device=dev)
+
+    def hash_build():
+        ts.ts_hash_build(coords, table.buf, table.cap, flags)
+
+    def kmap_build():
+        ts.ts_kmap_build(coords, table.buf, table.cap, None, n, None, None, 0, 3, 3, 1, 0, kbuf, km)
+
+    hash_build()
+    kmap_build()
+    wsb = ts.ts_conv_workspace_bytes(km, w.cin, w.cout, ts.TS_OP_FWD, ts.TS_F16, ts.TS_DATAFLOW_AUTO)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+
+    def conv():
+        ts.ts_subm_conv_fwd(km, x, wt, y, ts.TS_DATAFLOW_AUTO, ws)
+
+    torch.cuda.synchronize()
+    kmap = ts.Kmap(km, kbuf, keep=(coords, table))
+    P = popcount_sum(kmap.rel_arrays("fwd")["row_mask"][:n], 27)
+    return dict(fns=[hash_build, kmap_build, conv], names=["hash", "kmap", "conv"], P=P, n=n, cap=table.cap,
+                flags=flags, y=y)
+
+
+def measure_lidar(ts, steps, warmup):
+    w = synth.make("lidar")
+    s = lidar_setup(ts, w)
+    ms, st = run_steps(s["fns"], s["names"], steps, warmup)
+    n, P, cap = s["n"], s["P"], s["cap"]
+    cin, cout, kvol, e = w.cin, w.cout, 27, 2
+    flop = 2.0 * P * cin * cout
+    conv_bytes = n * cin * e + kvol * cin * cout * e + P * 4 + n * 4 + n * cout * e
+    kmap_bytes = n * 16 + cap * 12 + P * 8 + n * 8
+    hash_bytes = n * 16 + cap * 12
+    conv_s = st["conv"] * 1e-6
+    res = {
+        "n": n, "pairs": P, "flop_per_step": flop,
+        "ms_per_step": ms,
+        "stages_us": {k: round(v, 3) for k, v in st.items()},
+        "fwd_tflops": flop / conv_s / 1e12,
+        "fwd_mfma_frac": flop / conv_s / 1e12 / MFMA_F16_PEAK_TFLOPS,
+        "fwd_alg_bytes": conv_bytes,
+        "fwd_gbs": conv_bytes / conv_s / 1e9,
+        "kmap_mvox_s": n / (st["kmap"] * 1e-6) / 1e6,
+        "kmap_with_hash_mvox_s": n / ((st["kmap"] + st["hash"]) * 1e-6) / 1e6,
+        "kmap_alg_bytes": kmap_bytes,
+        "kmap_gbs": kmap_bytes / (st["kmap"] * 1e-6) / 1e9,
+        "hash_gbs": hash_bytes / (st["hash"] * 1e-6) / 1e9,
+        "err_flags": int(s["flags"].item()),
+    }
+    return w, res
+
+
+def measure_down(ts, steps, warmup):
+    """Strided Conv3d k=2 s=2, 64 -> 128, fp16, two scenes (support included)."""
+    w = synth.make("down")
+    dev = torch.device("cuda")
+    coords = torch.from_numpy(w.coords).to(dev)
+    x, wt = w.x.to(dev), w.w.to(dev)
+    n = coords.shape[0]
+    table = ts.HashTable(coords, 2.0, build=False)
+    out_table = ts.HashTable(coords, 2.0, build=False)
+    out = torch.empty_like(coords)
+    n_out = torch.zeros(1, dtype=torch.int64, device=dev)
+    flags = torch.zeros(1, dtype=torch.int32, device=dev)
+    mbytes = ts.ts_kmap_bytes(n, n, 3, 2, 2, 0) + ts.ts_support_scratch_bytes(n)
+    mbuf = torch.empty(mbytes, dtype=torch.uint8, device=dev)
+    km = ts.TsKmap()
+    y = torch.empty((n, w.cout), dtype=torch.float16, device=dev)
+    wsb = 2 * 8 * w.cin * w.cout + 4096
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+
+    def hash_build():
+        ts.ts_hash_build(coords, table.buf, table.cap, flags)
+
+    def conv():
+        ts.ts_conv_fwd_strided(coords, table.buf, table.cap, 2, 2, 0, out, n_out, out_table.buf, out_table.cap, flags,
+                               mbuf, km, x, wt, y, ts.TS_DATAFLOW_AUTO, ws)
+
+    ms, st = run_steps([hash_build, conv], ["hash", "support_kmap_conv"], steps, warmup)
+    kmap = ts.Kmap(km, mbuf[:ts.ts_kmap_bytes(n, n, 3, 2, 2, 0)], keep=(n_out,))
+    n_o = int(n_out.item())
+    P = popcount_sum(kmap.rel_arrays("fwd")["row_mask"][:n_o], 8)
+    flop = 2.0 * P * w.cin * w.cout
+    return {"workload": "down", "n_in": n, "n_out": n_o, "pairs": P, "ms_per_step": ms,
+            "stages_us": {k: round(v, 3) for k, v in st.items()},
+            "tflops_step": flop / (ms * 1e-3) / 1e12}
+
+
+def measure_pixels(ts, steps, warmup):
+    """2-D tracks: hash + kmap, then layers 1 -> 8 and 8 -> 8 (fp16)."""
+    w = synth.make("pixels")
+    dev = torch.device("cuda")
+    coords = torch.from_numpy(w.coords).to(dev)
+    x = w.x.to(dev)
+    w1, w2 = w.w.to(dev), w.extra["w2"].to(dev)
+    n = coords.shape[0]
+    table = ts.HashTable(coords, 2.0, build=False)
+    kbuf = torch.empty(ts.ts_kmap_bytes(n, n, 2, 3, 1, ts.TS_KMAP_PAIRS), dtype=torch.uint8, device=dev)
+    km = ts.TsKmap()
+    y1 = torch.empty((n, 8), dtype=torch.float16, device=dev)
+    y2 = torch.empty((n, 8), dtype=torch.float16, device=dev)
+    ws = torch.empty(n * 8 * 4 + 4096, dtype=torch.uint8, device=dev)
+
+    def hash_build():
+        ts.ts_hash_build(coords, table.buf, table.cap, None)
+
+    def kmap_build():
+        ts.ts_kmap_build(coords, table.buf, table.cap, None, n, None, None, 0, 2, 3, 1, ts.TS_KMAP_PAIRS, kbuf, km)
+
+    def layers():
+        ts.ts_subm_conv_fwd(km, x, w1, y1, ts.TS_DATAFLOW_AUTO, ws)
+        ts.ts_subm_conv_fwd(km, y1, w2, y2, ts.TS_DATAFLOW_AUTO, ws)
+
+    def layers_gs():
+        ts.ts_subm_conv_fwd(km, x, w1, y1, ts.TS_DATAFLOW_GATHER_SCATTER, ws)
+        ts.ts_subm_conv_fwd(km, y1, w2, y2, ts.TS_DATAFLOW_GATHER_SCATTER, ws)
+
+    ms, st = run_steps([hash_build, kmap_build, layers], ["hash", "kmap", "layers"], steps, warmup)
+    _, st_gs = run_steps([hash_build, kmap_build, layers_gs], ["hash", "kmap", "layers"], steps, warmup)
+    kmap = ts.Kmap(km, kbuf)
+    P = popcount_sum(kmap.rel_arrays("fwd")["row_mask"][:n], 9)
+    alg = (n * 1 * 2 + n * 8 * 2 + 9 * 8 * 2 + P * 4 + n * 4) + (n * 8 * 2 * 2 + 9 * 64 * 2 + P * 4 + n * 4)
+    return {"workload": "pixels", "n": n, "pairs": P, "ms_per_step": ms,
+            "stages_us": {k: round(v, 3) for k, v in st.items()},
+            "layers_gather_scatter_us": round(st_gs["layers"], 3),
+            "layers_gbs": alg / (st["layers"] * 1e-6) / 1e9}
+
+
+def measure_train(ts, steps, warmup):
+    """bf16 128 -> 128 training step: hash, kmap (+pairs), fwd, dgrad, wgrad."""
+    w = synth.make("train")
+    dev = torch.device("cuda")
+    coords = torch.from_numpy(w.coords).to(dev)
+    x, wt, dy = w.x.to(dev), w.w.to(dev), w.dy.to(dev)
+    n = coords.shape[0]
+    table = ts.HashTable(coords, 2.0, build=False)
+    flags_k = ts.TS_KMAP_PAIRS
+    kbuf = torch.empty(ts.ts_kmap_bytes(n, n, 3, 3, 1, flags_k), dtype=torch.uint8, device=dev)
+    km = ts.TsKmap()
+    y = torch.empty((n, 128), dtype=torch.bfloat16, device=dev)
+    dx = torch.empty((n, 128), dtype=torch.bfloat16, device=dev)
+    dw = torch.empty((27, 128, 128), dtype=torch.float32, device=dev)
+
+    def hash_build():
+        ts.ts_hash_build(coords, table.buf, table.cap, None)
+
+    def kmap_build():
+        ts.ts_kmap_build(coords, table.buf, table.cap, None, n, None, None, 0, 3, 3, 1, flags_k, kbuf, km)
+
+    hash_build()
+    kmap_build()
+    torch.cuda.synchronize()
+    ws_f = torch.empty(max(ts.ts_conv_workspace_bytes(km, 128, 128, ts.TS_OP_FWD, ts.TS_BF16, 0), 1), dtype=torch.uint8, device=dev)
+    ws_w = torch.empty(max(ts.ts_conv_workspace_bytes(km, 128, 128, ts.TS_OP_WGRAD, ts.TS_BF16, 0), 1), dtype=torch.uint8, device=dev)
+
+    def fwd():
+        ts.ts_subm_conv_fwd(km, x, wt, y, ts.TS_DATAFLOW_AUTO, ws_f)
+
+    def dgrad():
+        ts.ts_conv_bwd_dgrad(km, dy, wt, dx, ts.TS_DATAFLOW_AUTO, ws_f)
+
+    def wgrad():
+        ts.ts_conv_bwd_wgrad(km, x, dy, dw, ws_w)
+
+    ms, st = run_steps([hash_build, kmap_build, fwd, dgrad, wgrad], ["hash", "kmap", "fwd", "dgrad", "wgrad"],
+                       steps, warmup)
+    kmap = ts.Kmap(km, kbuf)
+    P = popcount_sum(kmap.rel_arrays("fwd")["row_mask"][:n], 27)
+    flop = 2.0 * P * 128 * 128
+    return {"workload": "train", "n": n, "pairs": P, "ms_per_step": ms,
+            "stages_us": {k: round(v, 3) for k, v in st.items()},
+            "fwd_tflops": flop / (st["fwd"] * 1e-6) / 1e12,
+            "dgrad_tflops": flop / (st["dgrad"] * 1e-6) / 1e12,
+            "wgrad_tflops": flop / (st["wgrad"] * 1e-6) / 1e12,
+            "step_tflops": 3 * flop / (ms * 1e-3) / 1e12}
+
+
+# ---------------------------------------------------------------- CPU oracle
+def cpu_baseline(w, P):
+    """The oracle (hash, kernel map, forward; fp64, one thread) on the full
+    LiDAR workload, one pass."""
+    import oracle
+    oracle.lib()
+    t0 = time.perf_counter()
+    tr = oracle.kmap(w.coords, w.coords, 3, 1)
+    t1 = time.perf_counter()
+    oracle.conv_fwd(tr, w.x, w.w, w.coords.shape[0])
+    t2 = time.perf_counter()
+    assert len(tr[0]) == P, (len(tr[0]), P)
+    flop = 2.0 * P * w.cin * w.cout
+    return {"value": flop / (t2 - t0) / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"full ring-scan scene ({w.coords.shape[0]} voxels, {P} pairs): one pass of hash + kernel "
+                      f"map ({t1 - t0:.2f} s) and fp64 forward ({t2 - t1:.2f} s), single thread",
+            "seconds": t2 - t0}
+
+
+def copy_calibration(mb: int, steps: int):
+    """A plain device copy of known size, for scaling rocprofv3 byte counters."""
+    n = mb * (1 << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(steps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_each_way": n * 4, "launches": steps}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--only", default=None, help="measure one workload (lidar, down, pixels, train)")
+    ap.add_argument("--copy-calib", type=int, default=0, help="run only a plain copy of this many MiB")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this library has no multi-GPU path (see the sharding notes); "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calib:
+        copy_calibration(args.copy_calib, args.steps)
+        return
+    from convolution_voxelised_point_amd import ts
+
+    torch.cuda.synchronize()
+    if args.only and args.only != "lidar":
+        fn = {"down": measure_down, "pixels": measure_pixels, "train": measure_train}[args.only]
+        print(json.dumps(fn(ts, args.steps, args.warmup)))
+        return
+    w, r = measure_lidar(ts, args.steps, args.warmup)
+    secondary = []
+    if args.only is None:
+        for fn in (measure_down, measure_pixels, measure_train):
+            secondary.append(fn(ts, args.steps, args.warmup))
+    value = r["flop_per_step"] / (r["ms_per_step"] * 1e-3) / 1e12
+    conv_s = r["stages_us"]["conv"] * 1e-6
+    line = {
+        "metric": "map-valid TFLOP/s + % MFMA peak, SubmConv3d k3 C64 fp16; kmap Mvox/s",
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "ring-scan SubmConv3d k3 C64->64 fp16 (hash + kernel map + forward)",
+                   "voxels": r["n"], "pairs": r["pairs"], "batch": 1, "kernel": 3, "stride": 1},
+        "fwd_tflops": r["fwd_tflops"],
+        "fwd_mfma_frac": r["fwd_mfma_frac"],
+        "kmap_mvox_s": r["kmap_mvox_s"],
+        "kmap_with_hash_mvox_s": r["kmap_with_hash_mvox_s"],
+        "kmap_hbm_frac": r["kmap_gbs"] / HBM_PEAK_GBS,
+        "stages_us": r["stages_us"],
+        "roofline": {"bound": "hbm", "kernel": "implicit-GEMM forward (k_igemm)",
+                     "achieved": r["fwd_alg_bytes"] / conv_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": r["fwd_alg_bytes"] / conv_s / 1e9 / HBM_PEAK_GBS, "traffic": None,
+                     "alg_bytes_per_launch": r["fwd_alg_bytes"]},
+        "secondary": secondary,
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(w, r["pairs"])
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()
