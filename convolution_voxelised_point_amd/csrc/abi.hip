@@ -29,6 +29,7 @@ bool shape_ok(int ndim, int ksize, int stride) {
 }
 
 constexpr int64_t kMaxRows = (int64_t{1} << 31) - 1;
+constexpr int64_t kMaxCap = int64_t{1} << 25;  // block slots (cell indices stay int32)
 constexpr int kMaxChannels = 1 << 16;
 
 // Layout of the kernel-map buffer: every region starts on a 256-byte boundary.
@@ -137,12 +138,15 @@ int64_t ts_hash_capacity(int64_t n, double rsv_ratio) {
   return cap;
 }
 
-size_t ts_hash_table_bytes(int64_t cap) { return cap > 0 ? static_cast<size_t>(cap) * 12 : 0; }
+size_t ts_hash_table_bytes(int64_t cap) {
+  return cap > 0 ? table_keys_bytes(cap) + static_cast<size_t>(cap) * kCells * sizeof(int32_t) : 0;
+}
 
 ts_status ts_hash_build(const int32_t* coords, int64_t n, int ndim, void* table, int64_t cap, uint32_t* err_flags,
                         hipStream_t stream) {
   if (n < 0 || n > kMaxRows || (n > 0 && !coords) || !table) return TS_ERR_INVALID_ARG;
-  if ((ndim != 2 && ndim != 3) || !is_pow2(cap) || cap < n || cap > kMaxRows) return TS_ERR_INVALID_ARG;
+  if ((ndim != 2 && ndim != 3) || !is_pow2(cap) || cap < n) return TS_ERR_INVALID_ARG;
+  if (cap > kMaxCap) return TS_ERR_UNSUPPORTED;
   TS_TRY(launch_hash_build(coords, n, ndim, table, cap, err_flags, stream));
   return TS_OK;
 }
@@ -150,7 +154,7 @@ ts_status ts_hash_build(const int32_t* coords, int64_t n, int ndim, void* table,
 ts_status ts_hash_query(const void* table, int64_t cap, int ndim, const int32_t* q, int64_t m, int32_t* rows,
                         hipStream_t stream) {
   if (!table || m < 0 || m > kMaxRows || (m > 0 && (!q || !rows))) return TS_ERR_INVALID_ARG;
-  if ((ndim != 2 && ndim != 3) || !is_pow2(cap) || cap > kMaxRows) return TS_ERR_INVALID_ARG;
+  if ((ndim != 2 && ndim != 3) || !is_pow2(cap) || cap > kMaxCap) return TS_ERR_INVALID_ARG;
   TS_TRY(launch_hash_query(table, cap, ndim, q, m, rows, stream));
   return TS_OK;
 }
@@ -163,7 +167,8 @@ ts_status ts_strided_support(const int32_t* in_coords, int64_t n_in, int ndim, i
   if (n_in < 0 || n_in > kMaxRows || (n_in > 0 && (!in_coords || !out_coords)) || !n_out || !out_table)
     return TS_ERR_INVALID_ARG;
   if ((ndim != 2 && ndim != 3) || stride < 1 || stride > 65535) return TS_ERR_INVALID_ARG;
-  if (!is_pow2(out_cap) || out_cap < n_in || out_cap > kMaxRows) return TS_ERR_INVALID_ARG;
+  if (!is_pow2(out_cap) || out_cap < n_in) return TS_ERR_INVALID_ARG;
+  if (out_cap > kMaxCap) return TS_ERR_UNSUPPORTED;
   if (!scratch || scratch_bytes < support_scratch_bytes(n_in)) return TS_ERR_INVALID_ARG;
   TS_TRY(launch_strided_support(in_coords, n_in, ndim, stride, out_coords, n_out, out_table, out_cap, scratch,
                                 err_flags, stream));
@@ -185,7 +190,7 @@ ts_status ts_kmap_build(const int32_t* in_coords, int64_t n_in, const void* in_t
     if ((ndim == 2 || ndim == 3) && ksize >= 1 && stride >= 1) return TS_ERR_UNSUPPORTED;
     return TS_ERR_INVALID_ARG;
   }
-  if (n_in < 0 || n_in > kMaxRows || (n_in > 0 && !in_coords) || !is_pow2(in_cap) || in_cap > kMaxRows)
+  if (n_in < 0 || n_in > kMaxRows || (n_in > 0 && !in_coords) || !is_pow2(in_cap) || in_cap > kMaxCap)
     return TS_ERR_INVALID_ARG;
   if (flags & ~(TS_KMAP_PAIRS | TS_KMAP_BWD | TS_KMAP_NATURAL)) return TS_ERR_INVALID_ARG;
   const int kvol = ipow(ksize, ndim);
@@ -195,7 +200,7 @@ ts_status ts_kmap_build(const int32_t* in_coords, int64_t n_in, const void* in_t
     n_out_cap = n_in;
   } else {
     if (n_out_cap < 0 || n_out_cap > kMaxRows || (n_out_cap > 0 && !out_coords) || !n_out) return TS_ERR_INVALID_ARG;
-    if ((flags & TS_KMAP_BWD) && (!out_table || !is_pow2(out_cap) || out_cap > kMaxRows)) return TS_ERR_INVALID_ARG;
+    if ((flags & TS_KMAP_BWD) && (!out_table || !is_pow2(out_cap) || out_cap > kMaxCap)) return TS_ERR_INVALID_ARG;
   }
   if (n_out_cap * kvol > kMaxRows || n_in * kvol > kMaxRows) return TS_ERR_UNSUPPORTED;
   ts_kmap m;
@@ -215,15 +220,16 @@ ts_status ts_kmap_build(const int32_t* in_coords, int64_t n_in, const void* in_t
   f.src_cap = in_cap;
   f.own_table = nullptr;
   f.own_cap = 0;
+  int64_t* n_out_fill = nullptr;
   if (stride == 1) {
-    TS_TRY(fill_i64(m.n_out, 1, n_in, stream));
+    n_out_fill = m.n_out;  // written by the map kernel: outputs = inputs
     f.n_dest = nullptr;
   } else {
     m.n_out = const_cast<int64_t*>(n_out);
     f.n_dest = n_out;
   }
   m.fwd.n_dest = m.n_out;
-  TS_TRY(launch_rel_build(f, m.fwd, natural, m.scratch, stream));
+  TS_TRY(launch_rel_build(f, m.fwd, natural, n_out_fill, stream));
 
   if (stride > 1 && (flags & TS_KMAP_BWD)) {
     RelBuild b = f;
@@ -235,7 +241,7 @@ ts_status ts_kmap_build(const int32_t* in_coords, int64_t n_in, const void* in_t
     b.src_cap = out_cap;
     b.own_table = in_table;
     b.own_cap = in_cap;
-    TS_TRY(launch_rel_build(b, m.bwd, natural, m.scratch, stream));
+    TS_TRY(launch_rel_build(b, m.bwd, natural, nullptr, stream));
   }
   if (flags & TS_KMAP_PAIRS) TS_TRY(launch_pairs_build(f, m.fwd, m.pair_start, m.pair_in, m.pair_out, m.scratch, stream));
   *map = m;

@@ -32,18 +32,32 @@ inline Offsets make_offsets(int ndim, int ksize) {
   return o;
 }
 
-// Open-addressing table view: keys[cap] (u64) followed by vals[cap] (i32).
+// Two-level coordinate table.  Voxels are grouped in blocks (4x4x4 in 3-D,
+// 8x8 in 2-D, 64 cells either way).  An open-addressing table (linear
+// probing) maps a block key to a block slot; each slot owns a dense array of
+// 64 cells holding the row of each voxel of the block (kNoRow when absent).
+// The neighbourhood of a voxel then needs a few block lookups and direct
+// cell loads instead of one hashed probe per neighbour.
+//   buffer: keys [cap] u64 | (256-byte aligned) cells [cap][64] int32
+constexpr int kCells = 64;
+constexpr int32_t kNoRow = 0x7fffffff;
+
 struct Table {
   uint64_t* keys;
-  int32_t* vals;
+  int32_t* cells;
   uint64_t mask;  // cap - 1
+  int nd;         // 2 or 3
 };
 
-inline Table table_view(const void* base, int64_t cap) {
+inline size_t table_keys_bytes(int64_t cap) { return (static_cast<size_t>(cap) * 8 + 255) / 256 * 256; }
+
+inline Table table_view(const void* base, int64_t cap, int ndim) {
   Table t;
-  t.keys = reinterpret_cast<uint64_t*>(const_cast<void*>(base));
-  t.vals = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(const_cast<void*>(base)) + cap * 8);
+  char* p = reinterpret_cast<char*>(const_cast<void*>(base));
+  t.keys = reinterpret_cast<uint64_t*>(p);
+  t.cells = reinterpret_cast<int32_t*>(p + table_keys_bytes(cap));
   t.mask = static_cast<uint64_t>(cap - 1);
+  t.nd = ndim;
   return t;
 }
 
@@ -82,16 +96,38 @@ __device__ __forceinline__ uint64_t hash64(uint64_t k) {
   return k;
 }
 
-// Lookup: linear probing from hash(key); returns the row or -1.
-__device__ __forceinline__ int32_t table_find(const Table& t, uint64_t key) {
-  uint64_t slot = hash64(key) & t.mask;
+// Key layout: [batch:16][f0:16][f1:16][f2:16] with f = value + 2^15 (a
+// 2-D key keeps f2 = 2^15).  Block key: the fields divided by the block side
+// (4 in 3-D, 8 in 2-D; 2-D keeps f2).  Cell: the remainders, row-major.
+__device__ __forceinline__ uint64_t block_key(uint64_t key, int nd) {
+  const uint64_t b = key >> 48, f0 = (key >> 32) & 0xffff, f1 = (key >> 16) & 0xffff, f2 = key & 0xffff;
+  if (nd == 3) return (b << 48) | ((f0 >> 2) << 32) | ((f1 >> 2) << 16) | (f2 >> 2);
+  return (b << 48) | ((f0 >> 3) << 32) | ((f1 >> 3) << 16) | f2;
+}
+__device__ __forceinline__ int cell_of(uint64_t key, int nd) {
+  const uint32_t f0 = (key >> 32) & 0xffff, f1 = (key >> 16) & 0xffff, f2 = key & 0xffff;
+  if (nd == 3) return static_cast<int>(((f0 & 3) << 4) | ((f1 & 3) << 2) | (f2 & 3));
+  return static_cast<int>(((f0 & 7) << 3) | (f1 & 7));
+}
+
+// Slot of a block key or -1 (linear probing from its hash).
+__device__ __forceinline__ int64_t block_find(const Table& t, uint64_t bkey) {
+  uint64_t slot = hash64(bkey) & t.mask;
   for (uint64_t probe = 0; probe <= t.mask; ++probe) {
     const uint64_t k = t.keys[slot];
-    if (k == key) return t.vals[slot];
+    if (k == bkey) return static_cast<int64_t>(slot);
     if (k == kEmptyKey) return -1;
     slot = (slot + 1) & t.mask;
   }
   return -1;
+}
+
+// Lookup of a voxel key: its row or -1.
+__device__ __forceinline__ int32_t table_find(const Table& t, uint64_t key) {
+  const int64_t s = block_find(t, block_key(key, t.nd));
+  if (s < 0) return -1;
+  const int32_t r = t.cells[s * kCells + cell_of(key, t.nd)];
+  return r == kNoRow ? -1 : r;
 }
 
 __device__ __forceinline__ int64_t floor_div(int64_t a, int64_t b) {

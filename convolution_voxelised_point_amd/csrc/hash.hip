@@ -3,133 +3,156 @@
 // lists hashing and coordinate query among the library's kernels (section
 // "What remains familiar") and says a strided convolution creates a
 // downsampled support (section "Convolution mapping").
+//
+// Build, in three launches:
+//   1. clear the block keys;
+//   2. each voxel claims the slot of its block (CAS on the block key, linear
+//      probing); the lane that claims a slot resets the block's 64 cells;
+//   3. each voxel finds its block and atomicMin's its row into its cell, so a
+//      repeated coordinate keeps the lowest row (and raises TS_FLAG_DUP).
+// Cells are written only after every claim has reset its cells (a kernel
+// boundary apart), so no reset can overwrite a row.
 #include "common.h"
 #include "launch.h"
 
 namespace ts {
 
-// Fill every slot with the empty key and the "no row" value.  A plain fill
-// kernel (not a memset node) so the call can be captured in a graph.
-__global__ __launch_bounds__(256) void k_table_clear(uint64_t* __restrict__ keys, int32_t* __restrict__ vals,
-                                                     int64_t cap) {
+__global__ __launch_bounds__(256) void k_table_clear(uint64_t* __restrict__ keys, int64_t cap) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i < cap) {
-    keys[i] = kEmptyKey;
-    vals[i] = 0x7fffffff;
-  }
+  if (i < cap) keys[i] = kEmptyKey;
 }
 
-// Insert `key` -> `row`: claim the first empty slot of the probe sequence or
-// join the slot already holding the key; the row value is the minimum over
-// all inserters (lowest row wins).  Returns the slot or -1 when full.
-__device__ __forceinline__ int64_t table_insert(const Table& t, uint64_t key, int32_t row, uint32_t* flags) {
-  uint64_t slot = hash64(key) & t.mask;
+// Slot of block `bkey`, claiming an empty one; the claimer resets the cells.
+// Returns -1 when the table is full.
+__device__ __forceinline__ int64_t block_claim(const Table& t, uint64_t bkey, uint32_t* flags) {
+  uint64_t slot = hash64(bkey) & t.mask;
   for (uint64_t probe = 0; probe <= t.mask; ++probe) {
-    uint64_t k = t.keys[slot];
+    const uint64_t k = atomicCAS(reinterpret_cast<unsigned long long*>(t.keys + slot), kEmptyKey, bkey);
     if (k == kEmptyKey) {
-      k = atomicCAS(reinterpret_cast<unsigned long long*>(t.keys + slot), kEmptyKey, key);
-      if (k == kEmptyKey) {
-        atomicMin(t.vals + slot, row);
-        return static_cast<int64_t>(slot);
-      }
-    }
-    if (k == key) {
-      atomicMin(t.vals + slot, row);
-      if (flags) atomicOr(flags, TS_FLAG_DUP);
+      uint4* c = reinterpret_cast<uint4*>(t.cells + slot * kCells);
+      const uint4 none = make_uint4(kNoRow, kNoRow, kNoRow, kNoRow);
+#pragma unroll
+      for (int i = 0; i < kCells / 4; ++i) c[i] = none;
       return static_cast<int64_t>(slot);
     }
+    if (k == bkey) return static_cast<int64_t>(slot);
     slot = (slot + 1) & t.mask;
   }
   if (flags) atomicOr(flags, TS_FLAG_FULL);
   return -1;
 }
 
-__global__ __launch_bounds__(256) void k_hash_insert(const int32_t* __restrict__ coords, int64_t n, int ndim,
-                                                     Table t, uint32_t* flags) {
+__global__ __launch_bounds__(256) void k_hash_claim(const int32_t* __restrict__ coords, int64_t n, Table t,
+                                                    uint32_t* flags) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i >= n) return;
   uint64_t key;
-  if (!row_key(coords, i, ndim, &key)) {
+  if (!row_key(coords, i, t.nd, &key)) {
     if (flags) atomicOr(flags, TS_FLAG_RANGE);
     return;
   }
-  table_insert(t, key, static_cast<int32_t>(i), flags);
+  block_claim(t, block_key(key, t.nd), flags);
 }
 
-__global__ __launch_bounds__(256) void k_hash_query(Table t, int ndim, const int32_t* __restrict__ q, int64_t m,
+__global__ __launch_bounds__(256) void k_hash_cells(const int32_t* __restrict__ coords, int64_t n, Table t,
+                                                    uint32_t* flags) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  uint64_t key;
+  if (!row_key(coords, i, t.nd, &key)) return;
+  const int64_t s = block_find(t, block_key(key, t.nd));
+  if (s < 0) return;  // only when the table was full
+  const int32_t old = atomicMin(t.cells + s * kCells + cell_of(key, t.nd), static_cast<int32_t>(i));
+  if (old != kNoRow && flags) atomicOr(flags, TS_FLAG_DUP);
+}
+
+__global__ __launch_bounds__(256) void k_hash_query(Table t, const int32_t* __restrict__ q, int64_t m,
                                                     int32_t* __restrict__ rows) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i >= m) return;
   uint64_t key;
-  rows[i] = row_key(q, i, ndim, &key) ? table_find(t, key) : -1;
+  rows[i] = row_key(q, i, t.nd, &key) ? table_find(t, key) : -1;
 }
 
 hipError_t launch_hash_build(const int32_t* coords, int64_t n, int ndim, void* table, int64_t cap, uint32_t* flags,
                              hipStream_t s) {
-  Table t = table_view(table, cap);
-  k_table_clear<<<static_cast<unsigned>(ceil_div<int64_t>(cap, 256)), 256, 0, s>>>(t.keys, t.vals, cap);
-  if (n > 0)
-    k_hash_insert<<<static_cast<unsigned>(ceil_div<int64_t>(n, 256)), 256, 0, s>>>(coords, n, ndim, t, flags);
+  Table t = table_view(table, cap, ndim);
+  k_table_clear<<<static_cast<unsigned>(ceil_div<int64_t>(cap, 256)), 256, 0, s>>>(t.keys, cap);
+  if (n > 0) {
+    const unsigned g = static_cast<unsigned>(ceil_div<int64_t>(n, 256));
+    k_hash_claim<<<g, 256, 0, s>>>(coords, n, t, flags);
+    k_hash_cells<<<g, 256, 0, s>>>(coords, n, t, flags);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_hash_query(const void* table, int64_t cap, int ndim, const int32_t* q, int64_t m, int32_t* rows,
                              hipStream_t s) {
   if (m == 0) return hipSuccess;
-  Table t = table_view(table, cap);
-  k_hash_query<<<static_cast<unsigned>(ceil_div<int64_t>(m, 256)), 256, 0, s>>>(t, ndim, q, m, rows);
+  Table t = table_view(table, cap, ndim);
+  k_hash_query<<<static_cast<unsigned>(ceil_div<int64_t>(m, 256)), 256, 0, s>>>(t, q, m, rows);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
 // Strided support: unique(floor(c / s)) per batch, in first-occurrence order.
-//   1. every in-range input inserts its downsampled key, the table value
-//      keeping the lowest input row (= the first occurrence);
-//   2. an input is "first" when the slot's value is its own row;
-//   3. an exclusive scan over the first-flags numbers the outputs;
-//   4. each first input writes its output coordinate and stores its output
-//      row into the slot, so the table then maps coordinate -> output row.
+//   1. every in-range input claims the block of its downsampled key;
+//   2. it atomicMin's its row into the key's cell (the cell keeps the lowest
+//      input row = the first occurrence) and remembers the cell;
+//   3. an input is "first" when its cell holds its own row;
+//   4. an exclusive scan over the first-flags numbers the outputs;
+//   5. each first input writes its output coordinate and stores its output
+//      row into the cell, so the table then maps coordinate -> output row.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ bool down_key(const int32_t* coords, int64_t i, int ndim, int stride, int64_t* b,
-                                         int64_t* s, uint64_t* key) {
+__device__ __forceinline__ bool down_key(const int32_t* coords, int64_t i, int ndim, int stride, uint64_t* key) {
   const int32_t* c = coords + i * (ndim + 1);
   int64_t full[3] = {0, 0, 0};
   for (int d = 0; d < ndim; ++d) full[d] = c[1 + d];
-  *b = c[0];
   uint64_t k0;
-  if (!make_key(ndim, *b, full, &k0)) return false;  // the input row itself must be valid
-  s[0] = s[1] = s[2] = 0;
-  for (int d = 0; d < ndim; ++d) s[d] = floor_div(full[d], stride);
-  return make_key(ndim, *b, s, key);
+  if (!make_key(ndim, c[0], full, &k0)) return false;  // the input row itself must be valid
+  int64_t q[3] = {0, 0, 0};
+  for (int d = 0; d < ndim; ++d) q[d] = floor_div(full[d], stride);
+  return make_key(ndim, c[0], q, key);
 }
 
-__global__ __launch_bounds__(256) void k_down_insert(const int32_t* __restrict__ coords, int64_t n, int ndim,
-                                                     int stride, Table t, int32_t* __restrict__ slot_of,
-                                                     uint32_t* flags) {
+__global__ __launch_bounds__(256) void k_down_claim(const int32_t* __restrict__ coords, int64_t n, int stride,
+                                                    Table t, uint32_t* flags) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i >= n) return;
-  int64_t b, s[3];
   uint64_t key;
-  int64_t slot = -1;
-  if (down_key(coords, i, ndim, stride, &b, s, &key)) {
-    slot = table_insert(t, key, static_cast<int32_t>(i), nullptr);
-    if (slot < 0 && flags) atomicOr(flags, TS_FLAG_FULL);
+  if (down_key(coords, i, t.nd, stride, &key)) {
+    block_claim(t, block_key(key, t.nd), flags);
   } else if (flags) {
     atomicOr(flags, TS_FLAG_RANGE);
   }
-  slot_of[i] = static_cast<int32_t>(slot);
 }
 
-__global__ __launch_bounds__(256) void k_down_flag(const int32_t* __restrict__ slot_of, int64_t n, Table t,
+__global__ __launch_bounds__(256) void k_down_cells(const int32_t* __restrict__ coords, int64_t n, int stride,
+                                                    Table t, int32_t* __restrict__ cell_at) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  uint64_t key;
+  int32_t at = -1;
+  if (down_key(coords, i, t.nd, stride, &key)) {
+    const int64_t s = block_find(t, block_key(key, t.nd));
+    if (s >= 0) {
+      at = static_cast<int32_t>(s * kCells + cell_of(key, t.nd));
+      atomicMin(t.cells + at, static_cast<int32_t>(i));
+    }
+  }
+  cell_at[i] = at;
+}
+
+__global__ __launch_bounds__(256) void k_down_flag(const int32_t* __restrict__ cell_at, int64_t n, Table t,
                                                    int32_t* __restrict__ first) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i >= n) return;
-  const int32_t slot = slot_of[i];
-  first[i] = (slot >= 0 && t.vals[slot] == static_cast<int32_t>(i)) ? 1 : 0;
+  const int32_t at = cell_at[i];
+  first[i] = (at >= 0 && t.cells[at] == static_cast<int32_t>(i)) ? 1 : 0;
 }
 
 __global__ __launch_bounds__(256) void k_down_emit(const int32_t* __restrict__ coords, int64_t n, int ndim,
-                                                   int stride, const int32_t* __restrict__ slot_of,
+                                                   int stride, const int32_t* __restrict__ cell_at,
                                                    const int32_t* __restrict__ first,
                                                    const int32_t* __restrict__ index, Table t,
                                                    int32_t* __restrict__ out_coords) {
@@ -140,7 +163,7 @@ __global__ __launch_bounds__(256) void k_down_emit(const int32_t* __restrict__ c
   int32_t* o = out_coords + static_cast<int64_t>(j) * (ndim + 1);
   o[0] = c[0];
   for (int d = 0; d < ndim; ++d) o[1 + d] = static_cast<int32_t>(floor_div(c[1 + d], stride));
-  t.vals[slot_of[i]] = j;
+  t.cells[cell_at[i]] = j;
 }
 
 size_t support_scratch_bytes(int64_t n) {
@@ -151,23 +174,22 @@ size_t support_scratch_bytes(int64_t n) {
 hipError_t launch_strided_support(const int32_t* coords, int64_t n, int ndim, int stride, int32_t* out_coords,
                                   int64_t* n_out, void* out_table, int64_t out_cap, void* scratch,
                                   uint32_t* flags, hipStream_t s) {
-  Table t = table_view(out_table, out_cap);
+  Table t = table_view(out_table, out_cap, ndim);
   const size_t a = align_up(static_cast<size_t>(n) * 4, 256);
   char* p = static_cast<char*>(scratch);
-  int32_t* slot_of = reinterpret_cast<int32_t*>(p);
+  int32_t* cell_at = reinterpret_cast<int32_t*>(p);
   int32_t* first = reinterpret_cast<int32_t*>(p + a);
   int32_t* index = reinterpret_cast<int32_t*>(p + 2 * a);
   void* tmp = p + 3 * a;
-  k_table_clear<<<static_cast<unsigned>(ceil_div<int64_t>(out_cap, 256)), 256, 0, s>>>(t.keys, t.vals, out_cap);
-  if (n == 0) {
-    return fill_i64(n_out, 1, 0, s);
-  }
+  k_table_clear<<<static_cast<unsigned>(ceil_div<int64_t>(out_cap, 256)), 256, 0, s>>>(t.keys, out_cap);
+  if (n == 0) return fill_i64(n_out, 1, 0, s);
   const unsigned g = static_cast<unsigned>(ceil_div<int64_t>(n, 256));
-  k_down_insert<<<g, 256, 0, s>>>(coords, n, ndim, stride, t, slot_of, flags);
-  k_down_flag<<<g, 256, 0, s>>>(slot_of, n, t, first);
+  k_down_claim<<<g, 256, 0, s>>>(coords, n, stride, t, flags);
+  k_down_cells<<<g, 256, 0, s>>>(coords, n, stride, t, cell_at);
+  k_down_flag<<<g, 256, 0, s>>>(cell_at, n, t, first);
   hipError_t e = scan_exclusive_i32(first, index, n, n_out, tmp, s);
   if (e != hipSuccess) return e;
-  k_down_emit<<<g, 256, 0, s>>>(coords, n, ndim, stride, slot_of, first, index, t, out_coords);
+  k_down_emit<<<g, 256, 0, s>>>(coords, n, ndim, stride, cell_at, first, index, t, out_coords);
   return hipGetLastError();
 }
 

@@ -4,18 +4,31 @@
 // source row at the displaced coordinate, stored as a tiled relation with
 // per-tile offset masks so that the contraction skips empty offsets.
 //
-// Three relations share one kernel, differing only in how the probed
+// Three relations share the code, differing only in how the probed
 // coordinate is formed from the destination coordinate c and offset delta:
 //   submanifold  (dest = outputs = inputs):  c + delta       in the input table
 //   downsampling (dest = strided outputs):   s*c + delta     in the input table
 //   transposed   (dest = inputs):            (c - delta)/s   in the output table,
 //                                            only when s divides c - delta
+//
+// Probing: a lane owns one destination row and issues the first-slot loads
+// of all its offsets before examining any of them (one memory round trip
+// for the common case instead of one per offset); collisions continue
+// linearly from the loaded slot.
+//
+// Tiles: rows are either kept in index order (spatially local) or, by
+// default, sorted by offset mask inside windows of 4096 rows so that the 16
+// rows of a tile share most offsets and the contraction pads less.  The sort
+// is stable (ties keep row order), so the map is deterministic.
 #include "common.h"
 #include "launch.h"
 
 namespace ts {
 
 namespace {
+
+constexpr int kSortWindow = 4096;  // rows sorted together
+constexpr int kSortThreads = 1024;
 
 struct RelK {
   const int32_t* dc;
@@ -38,6 +51,176 @@ __device__ __forceinline__ int64_t dest_count(const int64_t* n_dest, int64_t cap
   return n < cap ? n : cap;
 }
 
+// Compile-time kernel geometry: offsets as packed key displacements.  A key
+// is [batch:16][axis0+2^15:16][axis1+2^15:16][axis2+2^15:16] (2-D keys keep
+// the last field at 2^15), so displacing a coordinate by delta adds
+// delta0*2^32 + delta1*2^16 + delta2 to its key as long as no field leaves
+// [0, 65535] -- which each probe checks per axis.
+template <int ND, int K>
+struct Geo {
+  static constexpr int KV = ND == 3 ? K * K * K : K * K;
+  static constexpr int R = (K - 1) / 2;
+  int8_t d[KV][3];
+  int64_t packed[KV];
+  constexpr Geo() : d{}, packed{} {
+    for (int o = 0; o < KV; ++o) {
+      int rem = o;
+      for (int ax = ND - 1; ax >= 0; --ax) {
+        d[o][ax] = static_cast<int8_t>(rem % K - R);
+        rem /= K;
+      }
+      packed[o] = d[o][0] * (int64_t{1} << 32) + d[o][1] * (int64_t{1} << 16) + (ND == 3 ? d[o][2] : 0);
+    }
+  }
+};
+
+// Biased fields (value + 2^15) of a coordinate, as int64; false when the
+// batch or a field is out of range.
+template <int ND>
+__device__ __forceinline__ bool fields_of(int64_t b, const int64_t* v, int64_t* f) {
+  if (b < 0 || b > 65534) return false;
+  bool ok = true;
+#pragma unroll
+  for (int ax = 0; ax < 3; ++ax) {
+    f[ax] = ax < ND ? v[ax] + 32768 : 32768;
+    ok = ok && f[ax] >= 0 && f[ax] <= 65535;
+  }
+  return ok;
+}
+
+__device__ __forceinline__ uint64_t key_of_fields(int64_t b, const int64_t* f) {
+  return (static_cast<uint64_t>(b) << 48) | (static_cast<uint64_t>(f[0]) << 32) | (static_cast<uint64_t>(f[1]) << 16) |
+         static_cast<uint64_t>(f[2]);
+}
+
+// Key probed at offset o from the base fields f (already scaled by the
+// stride for the downsampling relation); false when a field leaves range.
+template <int ND, int K>
+__device__ __forceinline__ bool offset_key(const Geo<ND, K>& g, uint64_t base, const int64_t* f, int o,
+                                           uint64_t* key) {
+  bool ok = true;
+#pragma unroll
+  for (int ax = 0; ax < ND; ++ax) {
+    const int64_t v = f[ax] + g.d[o][ax];
+    ok = ok && v >= 0 && v <= 65535;
+  }
+  *key = base + static_cast<uint64_t>(g.packed[o]);
+  return ok;
+}
+
+// All offsets of one row against the two-level table.  The displaced
+// coordinates of a kernel of size K span at most two blocks per axis, i.e. at
+// most 2^ND "corner" blocks:
+//   phase 1: the slots of the needed corner blocks, looked up together in
+//            rounds (every round issues the loads of all unresolved corners);
+//   phase 2: one cell load per wanted offset, all issued before any is used.
+// No load sits under a branch (invalid ones read cell 0 and are masked), so
+// a row costs two memory round trips plus rare collision rounds.
+template <int ND, int K>
+__device__ __forceinline__ void probe_fields(const Table& t, uint64_t base, const int64_t* f, uint64_t want,
+                                             int32_t (&nb)[Geo<ND, K>::KV]) {
+  constexpr Geo<ND, K> g;
+  constexpr int KV = Geo<ND, K>::KV;
+  constexpr int LB = ND == 3 ? 2 : 3;  // log2 of the block side
+  constexpr int NC = 1 << ND;
+  constexpr int DMIN = -Geo<ND, K>::R, DMAX = K - 1 - Geo<ND, K>::R;
+  const uint64_t b = base >> 48;
+  int64_t lo[3] = {0, 0, 0}, hi[3] = {0, 0, 0};
+  bool live = want != 0;
+#pragma unroll
+  for (int ax = 0; ax < ND; ++ax) {
+    const int64_t vmin = f[ax] + DMIN, vmax = f[ax] + DMAX;
+    live = live && vmax >= 0 && vmin <= 65535;
+    lo[ax] = (vmin < 0 ? 0 : vmin) >> LB;
+    hi[ax] = (vmax > 65535 ? 65535 : vmax) >> LB;
+  }
+  // corner block of each wanted offset, and the corners needed
+  uint32_t need = 0;
+  uint8_t corner[KV];
+#pragma unroll
+  for (int o = 0; o < KV; ++o) {
+    int c = 0;
+#pragma unroll
+    for (int ax = 0; ax < ND; ++ax) c |= (((f[ax] + g.d[o][ax]) >> LB) != lo[ax] ? 1 : 0) << ax;
+    corner[o] = static_cast<uint8_t>(c);
+    if (live && ((want >> o) & 1)) need |= 1u << c;
+  }
+  // phase 1: corner block slots
+  uint64_t bk[NC];
+  uint32_t slot[NC];
+  int32_t found[NC];
+  uint32_t pend = need;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const uint64_t b0 = (c & 1) ? hi[0] : lo[0];
+    const uint64_t b1 = (c & 2) ? hi[1] : lo[1];
+    const uint64_t b2 = ND == 3 ? static_cast<uint64_t>((c & 4) ? hi[2] : lo[2]) : static_cast<uint64_t>(f[2]);
+    bk[c] = (b << 48) | (b0 << 32) | (b1 << 16) | b2;
+    slot[c] = static_cast<uint32_t>(hash64(bk[c]) & t.mask);
+    found[c] = -1;
+  }
+  for (uint64_t round = 0; round <= t.mask && __ballot(pend != 0); ++round) {
+    uint64_t k[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) k[c] = t.keys[((pend >> c) & 1) ? slot[c] : 0];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      if (!((pend >> c) & 1)) continue;
+      if (k[c] == bk[c]) {
+        found[c] = static_cast<int32_t>(slot[c]);
+        pend &= ~(1u << c);
+      } else if (k[c] == kEmptyKey) {
+        pend &= ~(1u << c);
+      } else {
+        slot[c] = static_cast<uint32_t>((slot[c] + 1) & t.mask);
+      }
+    }
+  }
+  // phase 2: cells
+  int32_t r[KV];
+  bool ok[KV];
+#pragma unroll
+  for (int o = 0; o < KV; ++o) {
+    int32_t sl = found[0];
+#pragma unroll
+    for (int c = 1; c < NC; ++c) sl = corner[o] == c ? found[c] : sl;
+    bool valid = live && ((want >> o) & 1) && sl >= 0;
+    int cell = 0;
+#pragma unroll
+    for (int ax = 0; ax < ND; ++ax) {
+      const int64_t v = f[ax] + g.d[o][ax];
+      valid = valid && v >= 0 && v <= 65535;
+      cell = ND == 3 ? (cell << 2) | static_cast<int>(v & 3) : (cell << 3) | static_cast<int>(v & 7);
+    }
+    ok[o] = valid;
+    r[o] = t.cells[valid ? static_cast<int64_t>(sl) * kCells + cell : 0];
+  }
+#pragma unroll
+  for (int o = 0; o < KV; ++o) nb[o] = (ok[o] && r[o] != kNoRow) ? r[o] : -1;
+}
+
+// Base fields of destination `row` for the submanifold (c) and downsampling
+// (s*c) relations; false when the row takes no part.
+template <int MODE, int ND>
+__device__ __forceinline__ bool dest_fields(const RelK& a, int64_t row, uint64_t* base, int64_t* f) {
+  const int32_t* c = a.dc + row * (ND + 1);
+  int64_t v[3] = {0, 0, 0};
+#pragma unroll
+  for (int ax = 0; ax < ND; ++ax) v[ax] = c[1 + ax];
+  int64_t f0[3];
+  if (!fields_of<ND>(c[0], v, f0)) return false;  // the row's own coordinate must be valid
+  if (MODE == kModeDown) {
+#pragma unroll
+    for (int ax = 0; ax < ND; ++ax) v[ax] *= a.stride;
+  }
+  // scaled fields may leave range; offset_key checks every probe
+#pragma unroll
+  for (int ax = 0; ax < 3; ++ax) f[ax] = ax < ND ? v[ax] + 32768 : 32768;
+  *base = (static_cast<uint64_t>(c[0]) << 48) + (static_cast<uint64_t>(f[0]) << 32) +
+          (static_cast<uint64_t>(f[1]) << 16) + static_cast<uint64_t>(f[2]);
+  return true;
+}
+
 // Destination coordinate of `row`; false when the row takes no part.
 template <int MODE>
 __device__ __forceinline__ bool dest_load(const RelK& a, int64_t row, int64_t* b, int64_t* s) {
@@ -51,8 +234,10 @@ __device__ __forceinline__ bool dest_load(const RelK& a, int64_t row, int64_t* b
   return true;
 }
 
+// Key probed for offset o; false when no source row can exist there.
 template <int MODE>
-__device__ __forceinline__ int32_t probe(const RelK& a, const int8_t* offs, int64_t b, const int64_t* s, int o) {
+__device__ __forceinline__ bool probe_key(const RelK& a, const int8_t* offs, int64_t b, const int64_t* s, int o,
+                                          uint64_t* key) {
   int64_t p[3] = {0, 0, 0};
   for (int d = 0; d < a.ndim; ++d) {
     const int64_t dd = offs[o * 3 + d];
@@ -62,12 +247,17 @@ __device__ __forceinline__ int32_t probe(const RelK& a, const int8_t* offs, int6
       p[d] = static_cast<int64_t>(a.stride) * s[d] + dd;
     } else {
       const int64_t t = s[d] - dd;
-      if (t % a.stride != 0) return -1;
+      if (t % a.stride != 0) return false;
       p[d] = t / a.stride;
     }
   }
+  return make_key(a.ndim, b, p, key);
+}
+
+template <int MODE>
+__device__ __forceinline__ int32_t probe(const RelK& a, const int8_t* offs, int64_t b, const int64_t* s, int o) {
   uint64_t key;
-  if (!make_key(a.ndim, b, p, &key)) return -1;
+  if (!probe_key<MODE>(a, offs, b, s, o, &key)) return -1;
   return table_find(a.src, key);
 }
 
@@ -81,44 +271,206 @@ __device__ __forceinline__ uint64_t group16_or(uint64_t v) {
   return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
-// One 16-lane group per tile of destination rows in index order: probe every
-// offset, keep the neighbours in LDS, then write the row masks, the tile mask
-// and the tile's neighbour blocks for the offsets present in the tile.
-template <int MODE>
-__global__ __launch_bounds__(256) void k_rel_natural(RelK a) {
-  extern __shared__ int32_t nbr_lds[];  // [256][kvol]
-  __shared__ int8_t offs[TS_MAX_KVOL * 3];
+__device__ __forceinline__ void load_offsets(const RelK& a, int8_t* offs) {
   const int8_t* src_offs = &a.offs.d[0][0];
   for (int i = threadIdx.x; i < a.kvol * 3; i += blockDim.x) offs[i] = src_offs[i];
   __syncthreads();
+}
 
+// Writes one tile's mask and neighbour blocks from each lane's neighbours.
+template <int KV>
+__device__ __forceinline__ void write_tile(const RelK& a, int64_t t, int r, uint64_t mask, const int32_t (&nb)[KV]) {
+  const uint64_t tmask = group16_or(mask);
+  if (r == 0) a.tile_mask[t] = tmask;
+  int k = 0;
+#pragma unroll
+  for (int o = 0; o < KV; ++o) {
+    if ((tmask >> o) & 1) {
+      a.pool[(t * a.kvol + k) * kTile + r] = ((mask >> o) & 1) ? nb[o] : -1;
+      ++k;
+    }
+  }
+}
+
+// Pass 1: one lane per destination row in index order.  Writes row masks;
+// with `natural` it also writes the tiles (rows stay in index order).
+template <int MODE, int ND, int K>
+__global__ __launch_bounds__(256) void k_rel_probe(RelK a, int natural, int64_t* n_out_fill) {
+  constexpr int KV = Geo<ND, K>::KV;
   const int64_t t = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / kTile;
   const int r = threadIdx.x & (kTile - 1);
+  if (n_out_fill && blockIdx.x == 0 && threadIdx.x == 0) *n_out_fill = a.n_dest_cap;
   if (t >= a.n_tiles) return;  // whole 16-lane groups leave together
   const int64_t n_dest = dest_count(a.n_dest, a.n_dest_cap);
   const int64_t row = t * kTile + r;
+  uint64_t base = 0;
+  int64_t f[3] = {0, 0, 0};
+  const bool valid = row < n_dest && dest_fields<MODE, ND>(a, row, &base, f);
+  int32_t nb[KV];
+  probe_fields<ND, K>(a.src, base, f, valid ? ~0ull : 0ull, nb);
+  uint64_t mask = 0;
+#pragma unroll
+  for (int o = 0; o < KV; ++o)
+    if (nb[o] >= 0) mask |= 1ull << o;
+  // a submanifold output takes part only when it owns its coordinate
+  if (MODE == kModeSubm && nb[(KV - 1) / 2] != static_cast<int32_t>(row)) mask = 0;
+  if (row < a.n_dest_cap) a.row_mask[row] = mask;
+  if (natural) {
+    a.tile_rows[t * kTile + r] = row < n_dest ? static_cast<int32_t>(row) : -1;
+    write_tile<KV>(a, t, r, mask, nb);
+  }
+}
 
+// Pass 3 (sorted tiles): one lane per tile slot; re-probes only the offsets
+// the row has.
+template <int MODE, int ND, int K>
+__global__ __launch_bounds__(256) void k_rel_tiles(RelK a) {
+  constexpr int KV = Geo<ND, K>::KV;
+  const int64_t t = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / kTile;
+  const int r = threadIdx.x & (kTile - 1);
+  if (t >= a.n_tiles) return;
+  const int32_t row = a.tile_rows[t * kTile + r];
+  uint64_t mask = 0, base = 0;
+  int64_t f[3] = {0, 0, 0};
+  if (row >= 0) {
+    mask = a.row_mask[row];
+    if (mask) dest_fields<MODE, ND>(a, row, &base, f);
+  }
+  int32_t nb[KV];
+  probe_fields<ND, K>(a.src, base, f, mask, nb);
+  write_tile<KV>(a, t, r, mask, nb);
+}
+
+// Runtime-kvol versions (neighbours kept in LDS), for kernel sizes without a
+// compile-time instance.
+template <int MODE>
+__global__ __launch_bounds__(256) void k_rel_probe_any(RelK a, int natural) {
+  extern __shared__ int32_t nbr_lds[];  // [256][kvol]
+  __shared__ int8_t offs[TS_MAX_KVOL * 3];
+  load_offsets(a, offs);
+  const int64_t t = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / kTile;
+  const int r = threadIdx.x & (kTile - 1);
+  if (t >= a.n_tiles) return;
+  const int64_t n_dest = dest_count(a.n_dest, a.n_dest_cap);
+  const int64_t row = t * kTile + r;
   int64_t b, s[3];
   const bool valid = row < n_dest && dest_load<MODE>(a, row, &b, s);
   int32_t* my = nbr_lds + threadIdx.x * a.kvol;
   uint64_t mask = 0;
-  if (valid) {
-    for (int o = 0; o < a.kvol; ++o) {
-      const int32_t n = probe<MODE>(a, offs, b, s, o);
-      my[o] = n;
-      if (n >= 0) mask |= 1ull << o;
-    }
-    // a submanifold output takes part only when it owns its coordinate
-    if (MODE == kModeSubm && my[a.centre] != static_cast<int32_t>(row)) mask = 0;
+  for (int o = 0; o < a.kvol; ++o) {
+    const int32_t n = valid ? probe<MODE>(a, offs, b, s, o) : -1;
+    my[o] = n;
+    if (n >= 0) mask |= 1ull << o;
   }
+  if (MODE == kModeSubm && valid && my[a.centre] != static_cast<int32_t>(row)) mask = 0;
   if (row < a.n_dest_cap) a.row_mask[row] = mask;
+  if (!natural) return;
   const uint64_t tmask = group16_or(mask);
   if (r == 0) a.tile_mask[t] = tmask;
   a.tile_rows[t * kTile + r] = row < n_dest ? static_cast<int32_t>(row) : -1;
   int k = 0;
-  for (uint64_t m = tmask; m; m &= m - 1, ++k) {
-    const int o = __builtin_ctzll(m);
+  for (uint64_t mm = tmask; mm; mm &= mm - 1, ++k) {
+    const int o = __builtin_ctzll(mm);
     a.pool[(t * a.kvol + k) * kTile + r] = ((mask >> o) & 1) ? my[o] : -1;
+  }
+}
+
+template <int MODE>
+__global__ __launch_bounds__(256) void k_rel_tiles_any(RelK a) {
+  __shared__ int8_t offs[TS_MAX_KVOL * 3];
+  load_offsets(a, offs);
+  const int64_t t = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / kTile;
+  const int r = threadIdx.x & (kTile - 1);
+  if (t >= a.n_tiles) return;
+  const int32_t row = a.tile_rows[t * kTile + r];
+  uint64_t mask = 0;
+  int64_t b = 0, s[3] = {0, 0, 0};
+  if (row >= 0) {
+    mask = a.row_mask[row];
+    if (mask) dest_load<MODE>(a, row, &b, s);
+  }
+  const uint64_t tmask = group16_or(mask);
+  if (r == 0) a.tile_mask[t] = tmask;
+  int k = 0;
+  for (uint64_t mm = tmask; mm; mm &= mm - 1, ++k) {
+    const int o = __builtin_ctzll(mm);
+    a.pool[(t * a.kvol + k) * kTile + r] = ((mask >> o) & 1) ? probe<MODE>(a, offs, b, s, o) : -1;
+  }
+}
+
+// Pass 2: stable sort of each window's rows by offset mask.  1024 threads,
+// 4 rows each; one split pass per mask bit (zeros before ones, order kept),
+// a block-wide prefix sum giving every row its new place.
+__device__ __forceinline__ int block_excl_1024(int v, int* wsum, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kSortThreads / 64; ++w) {
+    const int sv = wsum[w];
+    before += w < wave ? sv : 0;
+    tot += sv;
+  }
+  __syncthreads();
+  *total = tot;
+  return before + x - v;
+}
+
+__global__ __launch_bounds__(kSortThreads) void k_rel_sort(const uint64_t* __restrict__ row_mask, int64_t n_dest_cap,
+                                                           const int64_t* n_dest_p, int nbits, int64_t n_slots,
+                                                           int32_t* __restrict__ tile_rows) {
+  __shared__ uint2 buf[kSortWindow];
+  __shared__ int wsum[kSortThreads / 64];
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * kSortWindow;
+  const int64_t n_dest = dest_count(n_dest_p, n_dest_cap);
+  uint32_t key[4];
+  int32_t row[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t r = base + threadIdx.x * 4 + i;
+    const bool ok = r < n_dest;
+    const uint64_t m = ok ? row_mask[r] : 0;
+    key[i] = ok ? static_cast<uint32_t>(m ^ (m >> 32)) : 0xffffffffu;
+    row[i] = ok ? static_cast<int32_t>(r) : -1;
+  }
+  for (int bit = 0; bit < nbits; ++bit) {
+    int f[4], c = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[i] = (key[i] >> bit) & 1;
+      c += f[i];
+    }
+    int ones;
+    int before = block_excl_1024(c, wsum, &ones);
+    if (ones == 0 || ones == kSortWindow) continue;  // block-uniform
+    const int zeros = kSortWindow - ones;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = threadIdx.x * 4 + i;
+      const int dest = f[i] ? zeros + before : e - before;
+      before += f[i];
+      buf[dest] = make_uint2(key[i], static_cast<uint32_t>(row[i]));
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint2 v = buf[threadIdx.x * 4 + i];
+      key[i] = v.x;
+      row[i] = static_cast<int32_t>(v.y);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t slot = base + threadIdx.x * 4 + i;
+    if (slot < n_slots) tile_rows[slot] = row[i];
   }
 }
 
@@ -191,8 +543,8 @@ RelK make_relk(const RelBuild& bld, const ts_rel& rel) {
   a.kvol = bld.kvol;
   a.centre = (bld.kvol - 1) / 2;
   a.offs = make_offsets(bld.ndim, bld.ksize);
-  a.src = table_view(bld.src_table, bld.src_cap);
-  a.own = bld.own_table ? table_view(bld.own_table, bld.own_cap) : a.src;
+  a.src = table_view(bld.src_table, bld.src_cap, bld.ndim);
+  a.own = bld.own_table ? table_view(bld.own_table, bld.own_cap, bld.ndim) : a.src;
   a.n_tiles = rel.n_tiles;
   a.tile_mask = rel.tile_mask;
   a.tile_rows = rel.tile_rows;
@@ -201,25 +553,57 @@ RelK make_relk(const RelBuild& bld, const ts_rel& rel) {
   return a;
 }
 
-}  // namespace
-
-size_t rel_scratch_bytes(int64_t n_dest_cap, int kvol) {
-  (void)n_dest_cap;
-  (void)kvol;
-  return 0;
+void launch_sort(const RelK& a, hipStream_t s) {
+  const int64_t slots = a.n_tiles * kTile;
+  const int nbits = a.kvol < 32 ? a.kvol : 32;
+  k_rel_sort<<<static_cast<unsigned>(ceil_div<int64_t>(slots, kSortWindow)), kSortThreads, 0, s>>>(
+      a.row_mask, a.n_dest_cap, a.n_dest, nbits, slots, a.tile_rows);
 }
 
-hipError_t launch_rel_build(const RelBuild& bld, const ts_rel& rel, bool natural, void* scratch, hipStream_t s) {
-  (void)natural;
-  (void)scratch;
-  if (rel.n_tiles == 0) return hipSuccess;
+template <int MODE, int ND, int K>
+void launch_rel_geo(const RelK& a, bool natural, unsigned grid, int64_t* n_out_fill, hipStream_t s) {
+  k_rel_probe<MODE, ND, K><<<grid, 256, 0, s>>>(a, natural ? 1 : 0, n_out_fill);
+  if (!natural) {
+    launch_sort(a, s);
+    k_rel_tiles<MODE, ND, K><<<grid, 256, 0, s>>>(a);
+  }
+}
+
+template <int MODE>
+void launch_rel_any(const RelK& a, bool natural, unsigned grid, int64_t* n_out_fill, hipStream_t s) {
+  const size_t lds = static_cast<size_t>(256) * a.kvol * sizeof(int32_t);
+  if (n_out_fill) (void)fill_i64(n_out_fill, 1, a.n_dest_cap, s);
+  k_rel_probe_any<MODE><<<grid, 256, lds, s>>>(a, natural ? 1 : 0);
+  if (!natural) {
+    launch_sort(a, s);
+    k_rel_tiles_any<MODE><<<grid, 256, 0, s>>>(a);
+  }
+}
+
+template <int MODE>
+void launch_rel_mode(const RelK& a, int ksize, bool natural, unsigned grid, int64_t* n_out_fill, hipStream_t s) {
+  if (a.ndim == 3 && ksize == 3) return launch_rel_geo<MODE, 3, 3>(a, natural, grid, n_out_fill, s);
+  if (a.ndim == 3 && ksize == 2) return launch_rel_geo<MODE, 3, 2>(a, natural, grid, n_out_fill, s);
+  if (a.ndim == 3 && ksize == 1) return launch_rel_geo<MODE, 3, 1>(a, natural, grid, n_out_fill, s);
+  if (a.ndim == 2 && ksize == 3) return launch_rel_geo<MODE, 2, 3>(a, natural, grid, n_out_fill, s);
+  if (a.ndim == 2 && ksize == 2) return launch_rel_geo<MODE, 2, 2>(a, natural, grid, n_out_fill, s);
+  if (a.ndim == 2 && ksize == 5) return launch_rel_geo<MODE, 2, 5>(a, natural, grid, n_out_fill, s);
+  return launch_rel_any<MODE>(a, natural, grid, n_out_fill, s);
+}
+
+}  // namespace
+
+size_t rel_scratch_bytes(int64_t, int) { return 0; }
+
+hipError_t launch_rel_build(const RelBuild& bld, const ts_rel& rel, bool natural, int64_t* n_out_fill,
+                            hipStream_t s) {
+  if (rel.n_tiles == 0) return n_out_fill ? fill_i64(n_out_fill, 1, bld.n_dest_cap, s) : hipSuccess;
   RelK a = make_relk(bld, rel);
   const unsigned grid = static_cast<unsigned>(ceil_div<int64_t>(rel.n_tiles * kTile, 256));
-  const size_t lds = static_cast<size_t>(256) * bld.kvol * sizeof(int32_t);
   switch (bld.mode) {
-    case kModeSubm: k_rel_natural<kModeSubm><<<grid, 256, lds, s>>>(a); break;
-    case kModeDown: k_rel_natural<kModeDown><<<grid, 256, lds, s>>>(a); break;
-    default: k_rel_natural<kModeUp><<<grid, 256, lds, s>>>(a); break;
+    case kModeSubm: launch_rel_mode<kModeSubm>(a, bld.ksize, natural, grid, n_out_fill, s); break;
+    case kModeDown: launch_rel_mode<kModeDown>(a, bld.ksize, natural, grid, n_out_fill, s); break;
+    default: launch_rel_any<kModeUp>(a, natural, grid, n_out_fill, s); break;
   }
   return hipGetLastError();
 }

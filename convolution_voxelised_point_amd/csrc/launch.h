@@ -49,7 +49,8 @@ struct RelBuild {
 };
 
 size_t rel_scratch_bytes(int64_t n_dest_cap, int kvol);
-hipError_t launch_rel_build(const RelBuild& b, const ts_rel& rel, bool natural, void* scratch, hipStream_t s);
+// n_out_fill (device, may be NULL): receives n_dest_cap (the submanifold output count)
+hipError_t launch_rel_build(const RelBuild& b, const ts_rel& rel, bool natural, int64_t* n_out_fill, hipStream_t s);
 size_t pairs_scratch_bytes(int64_t n_dest_cap, int kvol);
 hipError_t launch_pairs_build(const RelBuild& b, const ts_rel& rel, int64_t* pair_start, int32_t* pair_in,
                               int32_t* pair_out, void* scratch, hipStream_t s);

@@ -93,17 +93,20 @@ const char* ts_version(void);
  * torch-lattice page, section "What remains familiar"; table size set by the
  * reserve ratio of section "Backend and configuration differences").
  *
- * The table is an open-addressing map from a packed 64-bit coordinate key to
- * a row index, in one caller buffer of ts_hash_table_bytes(cap) bytes
- * (8-byte aligned).  Its slot layout is internal and may differ between runs;
- * only the lookup function is defined.
+ * The table maps a coordinate to a row index.  Internally voxels are grouped
+ * in blocks (4x4x4 in 3-D, 8x8 in 2-D): an open-addressing table of `cap`
+ * block slots, each owning the rows of its block's 64 cells, in one caller
+ * buffer of ts_hash_table_bytes(cap) bytes (256-byte aligned).  The slot
+ * layout is internal and may differ between runs; only the lookup function is
+ * defined.  `cap` bounds the number of distinct blocks, so cap >= n always
+ * suffices; cap <= 2^25 (larger tables return TS_ERR_UNSUPPORTED).
  * ---------------------------------------------------------------------- */
 
 /* Capacity for n keys at reserve ratio rsv (>= 1): the smallest power of two
  * >= max(64, ceil(rsv * n)).  Returns -1 for n < 0 or rsv < 1. */
 int64_t ts_hash_capacity(int64_t n, double rsv_ratio);
 
-/* Bytes of a table of `cap` slots (12 per slot). */
+/* Bytes of a table of `cap` block slots (8 + 256 per slot). */
 size_t ts_hash_table_bytes(int64_t cap);
 
 /* Build the table of `n` coordinate rows coords[n][ndim+1] (device int32):

@@ -53,7 +53,7 @@ def test_hash_capacity(ts):
     assert ts.ts_hash_capacity(1025, 1.0) == 2048
     assert ts.ts_hash_capacity(10, 0.5) == -1
     assert ts.ts_hash_capacity(-1, 2.0) == -1
-    assert ts.ts_hash_table_bytes(1024) == 12 * 1024
+    assert ts.ts_hash_table_bytes(1024) == 8 * 1024 + 256 * 1024
 
 
 def test_kmap_bytes(ts):
@@ -130,7 +130,8 @@ def test_conv_rejects(ts):
     assert ts._lib_conv_fwd(ref, FAKE, 0, FAKE, 16, FAKE, 1, 1, 0, None, 0, None) == ts.TS_ERR_INVALID_ARG   # cin 0
     assert ts._lib_conv_fwd(ref, FAKE, 16, FAKE, 16, FAKE, 7, 1, 0, None, 0, None) == ts.TS_ERR_INVALID_ARG  # dtype
     assert ts._lib_conv_fwd(ref, FAKE, 16, FAKE, 16, FAKE, 1, 2, 0, None, 0, None) == ts.TS_ERR_UNSUPPORTED  # f16->bf16
-    assert ts._lib_conv_fwd(ref, FAKE, 64, FAKE, 64, FAKE, 1, 1, 0, None, 0, None) == ts.TS_ERR_INVALID_ARG  # no ws
+    assert ts._lib_conv_fwd(ref, None, 64, FAKE, 64, FAKE, 1, 1, 0, None, 0, None) == ts.TS_ERR_INVALID_ARG  # null x
+    assert ts._lib_conv_fwd(ref, FAKE, 64, FAKE, 64, None, 1, 1, 0, None, 0, None) == ts.TS_ERR_INVALID_ARG  # null y
     assert ts._lib_conv_fwd(ref, FAKE, 64, FAKE, 64, FAKE, 1, 1, 2, FAKE, 1 << 30, None) == ts.TS_ERR_INVALID_ARG  # GS w/o pairs
     assert ts._lib_conv_fwd(ref, FAKE, 16, None, 16, FAKE, 1, 1, 0, None, 0, None) == ts.TS_ERR_INVALID_ARG  # null w
     assert ts._lib_conv_fwd(ref, FAKE, 16, FAKE, 16, FAKE, 1, 1, 9, None, 0, None) == ts.TS_ERR_INVALID_ARG  # dataflow
@@ -150,7 +151,7 @@ def test_workspace_sizes(ts):
     km.n_in = km.n_out_cap = 1000
     km.pair_cap = 27000
     ref = ctypes.byref(km)
-    assert ts._lib_conv_workspace_bytes(ref, 64, 64, ts.TS_OP_FWD, ts.TS_F16, 0) >= 27 * 64 * 64 * 2
+    assert ts._lib_conv_workspace_bytes(ref, 64, 64, ts.TS_OP_FWD, ts.TS_F16, 0) == 0   # implicit GEMM: none
     assert ts._lib_conv_workspace_bytes(ref, 16, 16, ts.TS_OP_FWD, ts.TS_F32, 0) == 0
     assert ts._lib_conv_workspace_bytes(ref, 64, 64, ts.TS_OP_FWD, ts.TS_F16, 2) >= 1000 * 64 * 4
     assert ts._lib_conv_workspace_bytes(ref, 64, 64, ts.TS_OP_WGRAD, ts.TS_F16, 0) >= 27 * 64 * 64 * 4
