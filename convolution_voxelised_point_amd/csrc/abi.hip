@@ -104,13 +104,13 @@ ts_status check_conv(const ts_kmap* map, int cin, int cout, ts_dtype in, ts_dtyp
   return TS_OK;
 }
 
-bool use_igemm(ts_dataflow df, int c_src, int c_dst, ts_dtype in) {
-  return (df == TS_DATAFLOW_AUTO || df == TS_DATAFLOW_IMPLICIT_GEMM) && igemm_supported(c_src, c_dst, in);
+bool use_igemm(ts_dataflow df, int kvol, int c_src, int c_dst, ts_dtype in) {
+  return (df == TS_DATAFLOW_AUTO || df == TS_DATAFLOW_IMPLICIT_GEMM) && igemm_supported(kvol, c_src, c_dst, in);
 }
 
 size_t conv_ws(const ts_kmap* map, int c_src, int c_dst, ts_dtype in, ts_dtype out, ts_dataflow df, int64_t n_dest) {
   if (df == TS_DATAFLOW_GATHER_SCATTER) return gs_workspace_bytes(n_dest, c_dst, out);
-  if (use_igemm(df, c_src, c_dst, in)) return igemm_workspace_bytes(map->kvol, c_src, c_dst);
+  if (use_igemm(df, map->kvol, c_src, c_dst, in)) return igemm_workspace_bytes(map->kvol, c_src, c_dst);
   return 0;
 }
 
@@ -285,7 +285,7 @@ ts_status ts_conv_fwd(const ts_kmap* map, const void* x, int cin, const void* w,
   if (dataflow == TS_DATAFLOW_GATHER_SCATTER) {
     if (!(map->flags & TS_KMAP_PAIRS)) return TS_ERR_INVALID_ARG;
     TS_TRY(launch_gather_scatter(map, a, false, map->n_out_cap, ws, stream));
-  } else if (use_igemm(dataflow, cin, cout, in_dtype)) {
+  } else if (use_igemm(dataflow, map->kvol, cin, cout, in_dtype)) {
     TS_TRY(launch_igemm(a, ws, stream));
   } else {
     TS_TRY(launch_direct(a, stream));
@@ -372,7 +372,7 @@ ts_status ts_conv_bwd_dgrad(const ts_kmap* map, const void* dy, int cout, const 
     a.rel = &map->bwd;
     a.mirror = false;
   }
-  if (use_igemm(dataflow, cout, cin, in_dtype)) {
+  if (use_igemm(dataflow, map->kvol, cout, cin, in_dtype)) {
     TS_TRY(launch_igemm(a, ws, stream));
   } else {
     TS_TRY(launch_direct(a, stream));

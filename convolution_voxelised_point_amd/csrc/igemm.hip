@@ -9,20 +9,28 @@
 // with memory access) for its speed; the relation is the kernel map of the
 // torch-lattice page "Migrating from TorchSparse".
 //
+// First a small kernel packs the weights into MFMA fragment order (16-byte
+// chunks, fragment (o, mb, kb) = 64 consecutive chunks), so every later copy
+// of a slice is a straight coalesced 16-byte copy.
+//
 // Work split.  A block of 4 waves owns 4*G tiles of 16 destination rows (each
-// wave G tiles, all output channels of one 128-channel column).  The block
-// walks the union of its tiles' offset masks in ascending order; per offset:
-//   * the weight slice is copied from global memory into LDS once per block,
-//     already in MFMA fragment order (the forward transposes on the way);
+// wave G tiles, the output channels of one block column).  The block walks
+// the union of its tiles' offset masks in ascending order.  Per offset:
+//   * the packed weight slice is copied into LDS once per block;
 //   * each wave gathers, for each of its tiles that has the offset, the 16
 //     source rows straight into B fragments (16 bytes per lane);
 //   * v_mfma_f32_16x16x32 with D = A . X^T, so a lane ends holding 4
 //     consecutive output channels of one row.
-// Software pipeline: while offset i is multiplied, the gathers and weight
-// slice of offset i+1 and the pool indices and weight loads of offset i+2 are
-// in flight; the LDS weight buffer is double-buffered, one barrier per offset.  Every output
-// row is written once, no atomics.  Blocks are numbered so that each XCD
-// walks a contiguous range of tiles (its L2 keeps the gathered rows).
+// Latency: a tile's pool rows (the source row of each slot at each of its
+// offsets) are loaded once, up front, into registers and picked per offset
+// with a lane shuffle, so no load address waits on another load inside the
+// loop.  Gathers and weight loads run two offsets ahead (three register sets
+// of gathers, two LDS weight buffers, one barrier per offset); each step first
+// stores the weights loaded one step earlier into the free LDS buffer, then
+// issues the next weight loads before its gathers, so that the in-order load
+// counter never forces a gather to land early.  Every output
+// row is written once, no atomics.  Blocks are numbered so that each XCD walks
+// a contiguous range of tiles (its L2 keeps the gathered rows).
 #include <stdlib.h>
 
 #include "common.h"
@@ -35,6 +43,7 @@ namespace {
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));  // one 16-byte chunk
 
 template <typename T>
 struct Mfma;
@@ -53,6 +62,11 @@ struct Mfma<__bf16> {
   }
 };
 
+// Pool rows held per tile and lane: lane (col, q) keeps slots k = q + 4j,
+// j < kPoolRegs, so tiles of up to 4 * kPoolRegs offsets are supported.
+constexpr int kPoolRegs = 7;
+constexpr int kMaxIgemmKvol = 4 * kPoolRegs;
+
 struct IgK {
   const uint64_t* tile_mask;
   const int32_t* tile_rows;
@@ -61,9 +75,8 @@ struct IgK {
   int kvol;
   const void* src;
   int c_src;
-  const void* w;
-  int trans;   // dgrad layout
-  int mirror;  // dgrad of a submanifold map
+  const u32x4* wp;  // packed fragments [kvol][mbt][c_src/32][64]
+  int mbt;          // fragments of 16 output channels in the packed weights
   void* dst;
   int c_dst;
   int out_dtype;
@@ -71,6 +84,39 @@ struct IgK {
   int64_t nb8;   // ceil(nblk / 8)
   int xcd_map;   // number blocks so that each XCD walks a contiguous range
 };
+
+// Packed chunk i = ((o * mbt + mb) * kbn + kb) * 64 + lane holds A_o[n][k..k+7]
+// with n = mb*16 + lane%16, k = kb*32 + (lane/16)*8; zero for n >= c_dst.
+template <typename T>
+__global__ __launch_bounds__(256) void k_wpack(const T* __restrict__ w, int kvol, int c_src, int c_dst, int mbt,
+                                               int trans, int mirror, u32x4* __restrict__ out) {
+  const int kbn = c_src / 32;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= static_cast<int64_t>(kvol) * mbt * kbn * 64) return;
+  const int lane = static_cast<int>(i & 63);
+  int64_t r = i >> 6;
+  const int kb = static_cast<int>(r % kbn);
+  r /= kbn;
+  const int mb = static_cast<int>(r % mbt);
+  const int o = static_cast<int>(r / mbt);
+  const int n = mb * 16 + (lane & 15);
+  const int k0 = kb * 32 + (lane >> 4) * 8;
+  const int64_t slice = static_cast<int64_t>(c_src) * c_dst;
+  u32x4 v = {0u, 0u, 0u, 0u};
+  if (n < c_dst) {
+    if (trans) {
+      const int os = mirror ? kvol - 1 - o : o;
+      v = *reinterpret_cast<const u32x4*>(w + os * slice + static_cast<int64_t>(n) * c_src + k0);
+    } else {
+      unsigned short e[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) e[j] = __builtin_bit_cast(unsigned short, w[o * slice + static_cast<int64_t>(k0 + j) * c_dst + n]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = static_cast<unsigned>(e[2 * j]) | (static_cast<unsigned>(e[2 * j + 1]) << 16);
+    }
+  }
+  out[i] = v;
+}
 
 __device__ __forceinline__ int next_bit(uint64_t u, int o) {
   if (o < 0 || o >= 63) return -1;
@@ -81,10 +127,10 @@ __device__ __forceinline__ int next_bit(uint64_t u, int o) {
 template <typename T, int MB, int KB, int G>
 __global__ __launch_bounds__(256) void k_igemm(IgK a) {
   typedef typename Mfma<T>::frag Frag;
-  constexpr int FR = MB * KB;                      // fragments per offset
+  constexpr int FR = MB * KB;                      // fragments per offset and block column
   constexpr int CHUNKS = FR * 64;                  // 16-byte chunks per weight slice
   constexpr int CH = (CHUNKS + 255) / 256;         // per thread
-  __shared__ uint4 wl[2][FR * 64];
+  __shared__ u32x4 wl[2][CHUNKS];
   __shared__ uint64_t wunion[4];
 
   const int lane = threadIdx.x & 63;
@@ -96,13 +142,23 @@ __global__ __launch_bounds__(256) void k_igemm(IgK a) {
   if (lb >= a.nblk) return;                        // whole block, before any barrier
   const int mb0 = blockIdx.y * MB;
   const int64_t t0 = (lb * 4 + wave) * G;
+  const int kvol = a.kvol;
 
+  // masks and pool rows (first loads of the kernel)
   uint64_t m[G];
+  int32_t pr[G][kPoolRegs];
   uint64_t u = 0;
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    m[g] = (t0 + g < a.n_tiles) ? a.tile_mask[t0 + g] : 0ull;
+    const bool live = t0 + g < a.n_tiles;
+    const int64_t tile = live ? t0 + g : 0;
+    m[g] = live ? a.tile_mask[tile] : 0ull;
     u |= m[g];
+#pragma unroll
+    for (int j = 0; j < kPoolRegs; ++j) {
+      const int k = kq + 4 * j;
+      pr[g][j] = a.pool[(tile * kvol + (k < kvol ? k : 0)) * kTile + col];
+    }
   }
   if (lane == 0) wunion[wave] = u;
   __syncthreads();
@@ -115,110 +171,77 @@ __global__ __launch_bounds__(256) void k_igemm(IgK a) {
     for (int mb = 0; mb < MB; ++mb) acc[g][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const T* src = static_cast<const T*>(a.src);
-  const T* w = static_cast<const T*>(a.w);
   const int c_src = a.c_src, c_dst = a.c_dst;
-  const int64_t slice = static_cast<int64_t>(c_src) * c_dst;
 
-  // ---- helpers.  No load is issued under a branch: every load reads a valid
-  // address (row or tile 0 when there is nothing to fetch), and masking is
-  // applied only where the value is consumed, so the compiler can count
-  // outstanding loads exactly and the prefetches really overlap the multiplies.
-  auto pool_idx = [&](int o, int32_t* nb) {
+  // Source row of slot `col` of tile g at offset o (meaningful when the tile
+  // has the offset): the k-th pool row, k = rank of o among the tile's bits,
+  // sits in register k/4 of lane col + 16*(k%4).
+  auto pool_row = [&](int g, int o) -> int32_t {
+    const int k = __popcll(m[g] & ((1ull << o) - 1));
+    const int j = k >> 2;
+    int32_t v = pr[g][0];
+#pragma unroll
+    for (int jj = 1; jj < kPoolRegs; ++jj) v = (j == jj) ? pr[g][jj] : v;
+    return __shfl(v, col + 16 * (k & 3), 64);
+  };
+  // Gathers of offset o, branch-free (row 0 when there is nothing to fetch);
+  // ok[g] marks a present row, and consumers zero the others.
+  auto gather = [&](int o, Frag (&x)[G][KB], bool (&ok)[G]) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const bool has = (m[g] >> o) & 1;
-      const int k = __popcll(m[g] & ((1ull << o) - 1));
-      const int64_t tile = has ? t0 + g : 0;
-      nb[g] = a.pool[(tile * a.kvol + (has ? k : 0)) * kTile + col];  // meaningful only when `has`
+      const int32_t nb = pool_row(g, o);
+      ok[g] = ((m[g] >> o) & 1) && nb >= 0;
+      const T* row = src + static_cast<int64_t>(ok[g] ? nb : 0) * c_src + kq * 8;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) x[g][kb] = __builtin_bit_cast(Frag, *reinterpret_cast<const u32x4*>(row + kb * 32));
     }
   };
-  // gathers of offset o; ok[g] = row present (consumers zero the others)
-  auto gather = [&](int o, const int32_t* nb, Frag (*x)[KB], bool* ok) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      ok[g] = ((m[g] >> o) & 1) && nb[g] >= 0;
-      const T* row = src + static_cast<int64_t>(ok[g] ? nb[g] : 0) * c_src + kq * 8;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) x[g][kb] = __builtin_bit_cast(Frag, *reinterpret_cast<const uint4*>(row + kb * 32));
-    }
-  };
-  // global -> registers: this thread's chunks of the weight slice of offset o.
-  // Chunks past c_dst read a clamped address: they land in fragment rows of
-  // output channels that are never written out.
-  auto wload = [&](int o, uint4* r) {
-    const int os = (a.trans && a.mirror) ? a.kvol - 1 - o : o;
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int i0 = threadIdx.x + c * 256;
-      const int i = i0 < CHUNKS ? i0 : 0;
-      int64_t off;
-      if (a.trans) {
-        // A[n][k] = W[o'][n][k]; chunk = (n, 8 consecutive k)
-        const int n = mb0 * 16 + i / (KB * 4);
-        const int k = (i % (KB * 4)) * 8;
-        off = os * slice + static_cast<int64_t>(n < c_dst ? n : 0) * c_src + k;
-      } else {
-        // A[n][k] = W[o][k][n]; chunk = (k, 8 consecutive n)
-        const int k = i / (MB * 2);
-        const int n = mb0 * 16 + (i % (MB * 2)) * 8;
-        off = os * slice + static_cast<int64_t>(k) * c_dst + (n < c_dst ? n : 0);
-      }
-      r[c] = *reinterpret_cast<const uint4*>(w + off);
-    }
-  };
-  // registers -> LDS in fragment order: slot (mb, kb, lane) holds A[n][k..k+7]
-  // with n = mb*16 + lane%16, k = kb*32 + (lane/16)*8
-  auto wstore = [&](const uint4* r, uint4* buf) {
+  // This thread's chunks of the packed slice of offset o.  Chunks of
+  // fragments past the packed column count read the slice start: they land in
+  // fragment rows of output channels that are never written out.
+  auto wload = [&](int o, u32x4 (&r)[CH]) {
+    const int64_t base = (static_cast<int64_t>(o) * a.mbt + mb0) * KB * 64;
+    const int64_t lim = (static_cast<int64_t>(o) * a.mbt + a.mbt) * KB * 64;
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       const int i = threadIdx.x + c * 256;
-      if (i >= CHUNKS) continue;
-      if (a.trans) {
-        const int nl = i / (KB * 4);
-        const int k = (i % (KB * 4)) * 8;
-        const int slot = ((nl >> 4) * KB + (k >> 5)) * 64 + (nl & 15) + 16 * ((k & 31) >> 3);
-        buf[slot] = r[c];
-      } else {
-        const int k = i / (MB * 2);
-        const int nl = (i % (MB * 2)) * 8;
-        const T* v = reinterpret_cast<const T*>(&r[c]);
-        T* b = reinterpret_cast<T*>(buf);
-        const int base = ((nl >> 4) * KB + (k >> 5)) * 64 + 16 * ((k & 31) >> 3);
+      const int64_t idx = base + (i < CHUNKS ? i : 0);
+      r[c] = a.wp[idx < lim ? idx : base];
+    }
+  };
+  auto wstore = [&](const u32x4 (&r)[CH], u32x4* buf) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) b[(base + ((nl + e) & 15)) * 8 + (k & 7)] = v[e];
-      }
+    for (int c = 0; c < CH; ++c) {
+      const int i = threadIdx.x + c * 256;
+      if ((c + 1) * 256 <= CHUNKS || i < CHUNKS) buf[i] = r[c];
     }
   };
 
   if (U) {
-    // Pipeline over the union of offsets, unrolled by two with ping-pong
-    // register sets (A/B) so nothing is copied between iterations.  Entering
-    // a step for offset oc: LDS buffer `buf` holds W(oc); xcur = gathers of
-    // oc (issued one step earlier); nbnxt = pool indices of o1; wnxt = W(o1)
-    // loads (issued one step earlier).  Each load thus has a whole step of
-    // multiplies and barrier to land.  Past the last offset the prefetches
-    // repeat a valid offset (harmless loads, no branches).
-    int oc = __builtin_ctzll(U);
-    int o1 = next_bit(U, oc);
+    // Offsets u_0 < u_1 < ... of U.  Entering step i: LDS buffer i%2 holds
+    // W(u_i); the weight registers hold W(u_{i+1}); gather set i%3 holds
+    // X(u_i) (issued at step i-2) and set (i+1)%3 holds X(u_{i+1}).  Past the
+    // last offset the prefetches repeat a valid offset (harmless loads).
+    int o0 = __builtin_ctzll(U);
+    int o1 = next_bit(U, o0);
     int o2 = o1 >= 0 ? next_bit(U, o1) : -1;
-    Frag xA[G][KB], xB[G][KB];
-    bool okA[G], okB[G];
-    int32_t nbA[G], nbB[G];
-    uint4 wA[CH], wB[CH];
-    wload(oc, wA);
-    pool_idx(oc, nbA);
-    gather(oc, nbA, xA, okA);
-    pool_idx(o1 >= 0 ? o1 : oc, nbB);
-    wstore(wA, wl[0]);
-    wload(o1 >= 0 ? o1 : oc, wB);
+    Frag x0[G][KB], x1[G][KB], x2[G][KB];
+    bool k0[G], k1[G], k2[G];
+    u32x4 wr[CH];
+    wload(o0, wr);
+    gather(o0, x0, k0);
+    gather(o1 >= 0 ? o1 : o0, x1, k1);
+    wstore(wr, wl[0]);
+    wload(o1 >= 0 ? o1 : o0, wr);
     __syncthreads();
-    int buf = 0;
-    auto step = [&](Frag (&xcur)[G][KB], bool (&okcur)[G], Frag (&xnxt)[G][KB], bool (&oknxt)[G],
-                    int32_t (&nbcur)[G], int32_t (&nbnxt)[G], uint4 (&wcur)[CH], uint4 (&wnxt)[CH]) -> bool {
-      const int okeep = o1 >= 0 ? o1 : oc;
-      gather(okeep, nbnxt, xnxt, oknxt);          // X(o1)
-      pool_idx(o2 >= 0 ? o2 : okeep, nbcur);      // pool(o2)
-      const uint4* lw = wl[buf];
+
+    auto step = [&](Frag (&xc)[G][KB], bool (&kc)[G], Frag (&xf)[G][KB], bool (&kf)[G], u32x4 (&w)[CH],
+                    int b) -> bool {
+      const int okeep = o2 >= 0 ? o2 : (o1 >= 0 ? o1 : o0);
+      wstore(w, wl[b ^ 1]);                       // W(u_{i+1}), loaded one step ago
+      wload(okeep, w);                            // W(u_{i+2}), before the gathers
+      gather(okeep, xf, kf);                      // X(u_{i+2})
+      const u32x4* lw = wl[b];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         Frag af[MB];
@@ -226,23 +249,21 @@ __global__ __launch_bounds__(256) void k_igemm(IgK a) {
         for (int mb = 0; mb < MB; ++mb) af[mb] = __builtin_bit_cast(Frag, lw[(mb * KB + kb) * 64 + lane]);
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-          if (!((m[g] >> oc) & 1)) continue;  // wave-uniform
-          const Frag bx = okcur[g] ? xcur[g][kb] : Frag{};
+          if (!((m[g] >> o0) & 1)) continue;  // wave-uniform
+          const Frag bx = kc[g] ? xc[g][kb] : Frag{};
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb) acc[g][mb] = Mfma<T>::run(af[mb], bx, acc[g][mb]);
         }
       }
       if (o1 < 0) return false;
-      wstore(wnxt, wl[buf ^ 1]);                  // W(o1), loaded one step ago
-      wload(o2 >= 0 ? o2 : okeep, wcur);          // W(o2)
       __syncthreads();
-      buf ^= 1;
-      oc = o1;
+      o0 = o1;
       o1 = o2;
       o2 = o2 >= 0 ? next_bit(U, o2) : -1;
       return true;
     };
-    while (step(xA, okA, xB, okB, nbA, nbB, wA, wB) && step(xB, okB, xA, okA, nbB, nbA, wB, wA)) {
+    while (step(x0, k0, x2, k2, wr, 0) && step(x1, k1, x0, k0, wr, 1) && step(x2, k2, x1, k1, wr, 0) &&
+           step(x0, k0, x2, k2, wr, 1) && step(x1, k1, x0, k0, wr, 0) && step(x2, k2, x1, k1, wr, 1)) {
     }
   }
 
@@ -275,15 +296,17 @@ __global__ __launch_bounds__(256) void k_igemm(IgK a) {
   }
 }
 
-// Tiles per wave.  Default: 4 for up to 64 output channels, 2 above; the
+// Tiles per wave.  Default 1: more blocks in flight and a smaller offset
+// union per block beat sharing a weight slice across more tiles; the
 // environment variable TS_IGEMM_G (1, 2 or 4) overrides it for tuning.
 static int tiles_per_wave(int mb) {
   static const int forced = [] {
     const char* e = getenv("TS_IGEMM_G");
     return e ? atoi(e) : 0;
   }();
+  (void)mb;
   if (forced == 1 || forced == 2 || forced == 4) return forced;
-  return mb <= 4 ? 4 : 2;
+  return 1;
 }
 
 // Workgroups are dealt to the 8 XCDs round-robin; numbering blocks so that
@@ -349,13 +372,16 @@ hipError_t launch_t(const IgK& k, hipStream_t s) {
 
 }  // namespace
 
-bool igemm_supported(int c_src, int c_dst, ts_dtype in_dtype) {
-  return in_dtype != TS_F32 && c_src % 32 == 0 && c_dst % 16 == 0 && c_src > 0 && c_src <= 128 && c_dst > 0;
+bool igemm_supported(int kvol, int c_src, int c_dst, ts_dtype in_dtype) {
+  return in_dtype != TS_F32 && kvol >= 1 && kvol <= kMaxIgemmKvol && c_src % 32 == 0 && c_dst % 16 == 0 &&
+         c_src > 0 && c_src <= 128 && c_dst > 0;
 }
 
-size_t igemm_workspace_bytes(int, int, int) { return 0; }
+size_t igemm_workspace_bytes(int kvol, int c_src, int c_dst) {
+  return static_cast<size_t>(kvol) * ceil_div(c_dst, 16) * (c_src / 32) * 64 * 16;
+}
 
-hipError_t launch_igemm(const ConvArgs& a, void*, hipStream_t s) {
+hipError_t launch_igemm(const ConvArgs& a, void* ws, hipStream_t s) {
   const ts_rel& rel = *a.rel;
   if (rel.n_tiles == 0) return hipSuccess;
   IgK k;
@@ -366,15 +392,23 @@ hipError_t launch_igemm(const ConvArgs& a, void*, hipStream_t s) {
   k.kvol = a.kvol;
   k.src = a.src;
   k.c_src = a.c_src;
-  k.w = a.w;
-  k.trans = a.transpose ? 1 : 0;
-  k.mirror = a.mirror ? 1 : 0;
+  k.wp = static_cast<const u32x4*>(ws);
+  k.mbt = ceil_div(a.c_dst, 16);
   k.dst = a.dst;
   k.c_dst = a.c_dst;
   k.out_dtype = a.out_dtype;
   k.nblk = 0;
   k.nb8 = 0;
-  return a.in_dtype == TS_F16 ? launch_t<_Float16>(k, s) : launch_t<__bf16>(k, s);
+  const int64_t chunks = static_cast<int64_t>(a.kvol) * k.mbt * (a.c_src / 32) * 64;
+  const unsigned pg = static_cast<unsigned>(ceil_div<int64_t>(chunks, 256));
+  if (a.in_dtype == TS_F16) {
+    k_wpack<_Float16><<<pg, 256, 0, s>>>(static_cast<const _Float16*>(a.w), a.kvol, a.c_src, a.c_dst, k.mbt,
+                                         a.transpose ? 1 : 0, a.mirror ? 1 : 0, static_cast<u32x4*>(ws));
+    return launch_t<_Float16>(k, s);
+  }
+  k_wpack<__bf16><<<pg, 256, 0, s>>>(static_cast<const __bf16*>(a.w), a.kvol, a.c_src, a.c_dst, k.mbt,
+                                     a.transpose ? 1 : 0, a.mirror ? 1 : 0, static_cast<u32x4*>(ws));
+  return launch_t<__bf16>(k, s);
 }
 
 }  // namespace ts

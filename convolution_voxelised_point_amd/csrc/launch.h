@@ -71,7 +71,7 @@ struct ConvArgs {
 };
 
 size_t igemm_workspace_bytes(int kvol, int c_src, int c_dst);
-bool igemm_supported(int c_src, int c_dst, ts_dtype in_dtype);
+bool igemm_supported(int kvol, int c_src, int c_dst, ts_dtype in_dtype);
 hipError_t launch_igemm(const ConvArgs& a, void* ws, hipStream_t s);
 hipError_t launch_direct(const ConvArgs& a, hipStream_t s);
 

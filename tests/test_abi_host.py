@@ -151,7 +151,9 @@ def test_workspace_sizes(ts):
     km.n_in = km.n_out_cap = 1000
     km.pair_cap = 27000
     ref = ctypes.byref(km)
-    assert ts._lib_conv_workspace_bytes(ref, 64, 64, ts.TS_OP_FWD, ts.TS_F16, 0) == 0   # implicit GEMM: none
+    # implicit GEMM: the weights packed in MFMA fragment order (kvol * Cout * Cin fp16/bf16)
+    assert ts._lib_conv_workspace_bytes(ref, 64, 64, ts.TS_OP_FWD, ts.TS_F16, 0) == 27 * 64 * 64 * 2
+    assert ts._lib_conv_workspace_bytes(ref, 48, 128, ts.TS_OP_DGRAD, ts.TS_BF16, 0) == 27 * 48 * 128 * 2
     assert ts._lib_conv_workspace_bytes(ref, 16, 16, ts.TS_OP_FWD, ts.TS_F32, 0) == 0
     assert ts._lib_conv_workspace_bytes(ref, 64, 64, ts.TS_OP_FWD, ts.TS_F16, 2) >= 1000 * 64 * 4
     assert ts._lib_conv_workspace_bytes(ref, 64, 64, ts.TS_OP_WGRAD, ts.TS_F16, 0) >= 27 * 64 * 64 * 4
