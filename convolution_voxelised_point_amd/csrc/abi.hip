@@ -57,7 +57,7 @@ void carve_rel(Carver& c, ts_rel* r, int64_t n_dest_cap, int kvol) {
   r->n_tiles = ceil_div<int64_t>(n_dest_cap, kTile);
   r->tile_mask = c.take<uint64_t>(static_cast<size_t>(r->n_tiles));
   r->tile_rows = c.take<int32_t>(static_cast<size_t>(r->n_tiles) * kTile);
-  r->pool = c.take<int32_t>(static_cast<size_t>(r->n_tiles) * kvol * kTile);
+  r->nbr = c.take<int32_t>(static_cast<size_t>(n_dest_cap) * kvol);
   r->row_mask = c.take<uint64_t>(static_cast<size_t>(n_dest_cap));
   r->n_dest = nullptr;
 }

@@ -33,7 +33,7 @@ __device__ __forceinline__ T from_f32(float v) {
 struct DirectK {
   const uint64_t* tile_mask;
   const int32_t* tile_rows;
-  const int32_t* pool;
+  const int32_t* nbr;  // [rows][kvol]
   int64_t n_tiles;
   int kvol;
   const void* src;
@@ -57,10 +57,10 @@ __global__ __launch_bounds__(256) void k_direct(DirectK a) {
   const T* src = static_cast<const T*>(a.src);
   const T* w = static_cast<const T*>(a.w);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  int k = 0;
-  for (uint64_t mm = tm; mm; mm &= mm - 1, ++k) {
+  const int32_t row = a.tile_rows[t * kTile + r];
+  for (uint64_t mm = row >= 0 ? tm : 0ull; mm; mm &= mm - 1) {
     const int o = __builtin_ctzll(mm);
-    const int32_t nb = a.pool[(t * a.kvol + k) * kTile + r];
+    const int32_t nb = a.nbr[static_cast<int64_t>(row) * a.kvol + o];
     if (nb < 0) continue;
     const int os = a.mirror ? a.kvol - 1 - o : o;
     const T* wo = w + static_cast<int64_t>(os) * a.w_cin * a.w_cout;
@@ -77,7 +77,6 @@ __global__ __launch_bounds__(256) void k_direct(DirectK a) {
       }
     }
   }
-  const int32_t row = a.tile_rows[t * kTile + r];
   if (row < 0) return;
   OT* out = static_cast<OT*>(a.dst) + static_cast<int64_t>(row) * a.c_dst;
 #pragma unroll
@@ -161,7 +160,7 @@ hipError_t launch_direct(const ConvArgs& a, hipStream_t s) {
   DirectK k;
   k.tile_mask = rel.tile_mask;
   k.tile_rows = rel.tile_rows;
-  k.pool = rel.pool;
+  k.nbr = rel.nbr;
   k.n_tiles = rel.n_tiles;
   k.kvol = a.kvol;
   k.src = a.src;

@@ -21,10 +21,10 @@
 //     source rows straight into B fragments (16 bytes per lane);
 //   * v_mfma_f32_16x16x32 with D = A . X^T, so a lane ends holding 4
 //     consecutive output channels of one row.
-// Latency: a tile's pool rows (the source row of each slot at each of its
-// offsets) are loaded once, up front, into registers and picked per offset
-// with a lane shuffle, so no load address waits on another load inside the
-// loop.  Gathers and weight loads run two offsets ahead (three register sets
+// Latency: the neighbour rows of a tile's 16 rows (the source row of each
+// slot at each offset) are loaded once, up front, into registers and picked
+// per offset with a lane shuffle, so no load address waits on another load
+// inside the loop.  Gathers and weight loads run two offsets ahead (three register sets
 // of gathers, two LDS weight buffers, one barrier per offset); each step first
 // stores the weights loaded one step earlier into the free LDS buffer, then
 // issues the next weight loads before its gathers, so that the in-order load
@@ -62,15 +62,16 @@ struct Mfma<__bf16> {
   }
 };
 
-// Pool rows held per tile and lane: lane (col, q) keeps slots k = q + 4j,
-// j < kPoolRegs, so tiles of up to 4 * kPoolRegs offsets are supported.
-constexpr int kPoolRegs = 7;
-constexpr int kMaxIgemmKvol = 4 * kPoolRegs;
+// Neighbours held per tile and lane: lane (col, q) keeps offsets o = q*kNbRegs
+// + j, j < kNbRegs, of the row in slot col, so kernels of up to 4 * kNbRegs
+// offsets are supported.
+constexpr int kNbRegs = 7;
+constexpr int kMaxIgemmKvol = 4 * kNbRegs;
 
 struct IgK {
   const uint64_t* tile_mask;
   const int32_t* tile_rows;
-  const int32_t* pool;
+  const int32_t* nbr;  // [rows][kvol]
   int64_t n_tiles;
   int kvol;
   const void* src;
@@ -144,9 +145,9 @@ __global__ __launch_bounds__(256) void k_igemm(IgK a) {
   const int64_t t0 = (lb * 4 + wave) * G;
   const int kvol = a.kvol;
 
-  // masks and pool rows (first loads of the kernel)
+  // masks, destination rows and their neighbours (first loads of the kernel)
   uint64_t m[G];
-  int32_t pr[G][kPoolRegs];
+  int32_t pr[G][kNbRegs];
   uint64_t u = 0;
 #pragma unroll
   for (int g = 0; g < G; ++g) {
@@ -154,10 +155,13 @@ __global__ __launch_bounds__(256) void k_igemm(IgK a) {
     const int64_t tile = live ? t0 + g : 0;
     m[g] = live ? a.tile_mask[tile] : 0ull;
     u |= m[g];
+    const int32_t drow = a.tile_rows[tile * kTile + col];
+    const int32_t* nrow = a.nbr + static_cast<int64_t>(drow >= 0 ? drow : 0) * kvol;
 #pragma unroll
-    for (int j = 0; j < kPoolRegs; ++j) {
-      const int k = kq + 4 * j;
-      pr[g][j] = a.pool[(tile * kvol + (k < kvol ? k : 0)) * kTile + col];
+    for (int j = 0; j < kNbRegs; ++j) {
+      const int o = kq * kNbRegs + j;
+      const int32_t v = nrow[o < kvol ? o : 0];
+      pr[g][j] = drow >= 0 ? v : -1;
     }
   }
   if (lane == 0) wunion[wave] = u;
@@ -173,16 +177,14 @@ __global__ __launch_bounds__(256) void k_igemm(IgK a) {
   const T* src = static_cast<const T*>(a.src);
   const int c_src = a.c_src, c_dst = a.c_dst;
 
-  // Source row of slot `col` of tile g at offset o (meaningful when the tile
-  // has the offset): the k-th pool row, k = rank of o among the tile's bits,
-  // sits in register k/4 of lane col + 16*(k%4).
+  // Source row of slot `col` of tile g at offset o: register o % kNbRegs of
+  // lane col + 16 * (o / kNbRegs).
   auto pool_row = [&](int g, int o) -> int32_t {
-    const int k = __popcll(m[g] & ((1ull << o) - 1));
-    const int j = k >> 2;
+    const int q = o / kNbRegs, j = o - q * kNbRegs;
     int32_t v = pr[g][0];
 #pragma unroll
-    for (int jj = 1; jj < kPoolRegs; ++jj) v = (j == jj) ? pr[g][jj] : v;
-    return __shfl(v, col + 16 * (k & 3), 64);
+    for (int jj = 1; jj < kNbRegs; ++jj) v = (j == jj) ? pr[g][jj] : v;
+    return __shfl(v, col + 16 * q, 64);
   };
   // Gathers of offset o, branch-free (row 0 when there is nothing to fetch);
   // ok[g] marks a present row, and consumers zero the others.
@@ -387,7 +389,7 @@ hipError_t launch_igemm(const ConvArgs& a, void* ws, hipStream_t s) {
   IgK k;
   k.tile_mask = rel.tile_mask;
   k.tile_rows = rel.tile_rows;
-  k.pool = rel.pool;
+  k.nbr = rel.nbr;
   k.n_tiles = rel.n_tiles;
   k.kvol = a.kvol;
   k.src = a.src;

@@ -1,8 +1,9 @@
 // Kernel-map construction (the "kernel-map construction" that the
 // torch-lattice page "Migrating from TorchSparse" names in section "Sparse
 // tensor expectations"): for each destination row and kernel offset, the
-// source row at the displaced coordinate, stored as a tiled relation with
-// per-tile offset masks so that the contraction skips empty offsets.
+// source row at the displaced coordinate (a row-major [rows][kvol] table),
+// plus per-row and per-tile offset masks so that the contraction skips empty
+// offsets.
 //
 // Three relations share the code, differing only in how the probed
 // coordinate is formed from the destination coordinate c and offset delta:
@@ -11,10 +12,9 @@
 //   transposed   (dest = inputs):            (c - delta)/s   in the output table,
 //                                            only when s divides c - delta
 //
-// Probing: a lane owns one destination row and issues the first-slot loads
-// of all its offsets before examining any of them (one memory round trip
-// for the common case instead of one per offset); collisions continue
-// linearly from the loaded slot.
+// Probing: a lane owns one destination row; the coordinate table is a grid
+// of voxel blocks, so all offsets of a row resolve through at most 2^D block
+// lookups (issued together) and then one cell load per offset.
 //
 // Tiles: rows are either kept in index order (spatially local) or, by
 // default, sorted by offset mask inside windows of 4096 rows so that the 16
@@ -41,7 +41,7 @@ struct RelK {
   int64_t n_tiles;
   uint64_t* tile_mask;
   int32_t* tile_rows;
-  int32_t* pool;
+  int32_t* nbr;
   uint64_t* row_mask;
 };
 
@@ -277,23 +277,9 @@ __device__ __forceinline__ void load_offsets(const RelK& a, int8_t* offs) {
   __syncthreads();
 }
 
-// Writes one tile's mask and neighbour blocks from each lane's neighbours.
-template <int KV>
-__device__ __forceinline__ void write_tile(const RelK& a, int64_t t, int r, uint64_t mask, const int32_t (&nb)[KV]) {
-  const uint64_t tmask = group16_or(mask);
-  if (r == 0) a.tile_mask[t] = tmask;
-  int k = 0;
-#pragma unroll
-  for (int o = 0; o < KV; ++o) {
-    if ((tmask >> o) & 1) {
-      a.pool[(t * a.kvol + k) * kTile + r] = ((mask >> o) & 1) ? nb[o] : -1;
-      ++k;
-    }
-  }
-}
-
-// Pass 1: one lane per destination row in index order.  Writes row masks;
-// with `natural` it also writes the tiles (rows stay in index order).
+// Pass 1: one lane per destination row in index order.  Writes the row's
+// neighbours and mask; with `natural` it also writes the tiles (rows stay in
+// index order).
 template <int MODE, int ND, int K>
 __global__ __launch_bounds__(256) void k_rel_probe(RelK a, int natural, int64_t* n_out_fill) {
   constexpr int KV = Geo<ND, K>::KV;
@@ -314,31 +300,17 @@ __global__ __launch_bounds__(256) void k_rel_probe(RelK a, int natural, int64_t*
     if (nb[o] >= 0) mask |= 1ull << o;
   // a submanifold output takes part only when it owns its coordinate
   if (MODE == kModeSubm && nb[(KV - 1) / 2] != static_cast<int32_t>(row)) mask = 0;
-  if (row < a.n_dest_cap) a.row_mask[row] = mask;
+  if (row < a.n_dest_cap) {
+    a.row_mask[row] = mask;
+    int32_t* out = a.nbr + row * KV;
+#pragma unroll
+    for (int o = 0; o < KV; ++o) out[o] = ((mask >> o) & 1) ? nb[o] : -1;
+  }
   if (natural) {
+    const uint64_t tmask = group16_or(mask);
+    if (r == 0) a.tile_mask[t] = tmask;
     a.tile_rows[t * kTile + r] = row < n_dest ? static_cast<int32_t>(row) : -1;
-    write_tile<KV>(a, t, r, mask, nb);
   }
-}
-
-// Pass 3 (sorted tiles): one lane per tile slot; re-probes only the offsets
-// the row has.
-template <int MODE, int ND, int K>
-__global__ __launch_bounds__(256) void k_rel_tiles(RelK a) {
-  constexpr int KV = Geo<ND, K>::KV;
-  const int64_t t = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / kTile;
-  const int r = threadIdx.x & (kTile - 1);
-  if (t >= a.n_tiles) return;
-  const int32_t row = a.tile_rows[t * kTile + r];
-  uint64_t mask = 0, base = 0;
-  int64_t f[3] = {0, 0, 0};
-  if (row >= 0) {
-    mask = a.row_mask[row];
-    if (mask) dest_fields<MODE, ND>(a, row, &base, f);
-  }
-  int32_t nb[KV];
-  probe_fields<ND, K>(a.src, base, f, mask, nb);
-  write_tile<KV>(a, t, r, mask, nb);
 }
 
 // Runtime-kvol versions (neighbours kept in LDS), for kernel sizes without a
@@ -363,39 +335,14 @@ __global__ __launch_bounds__(256) void k_rel_probe_any(RelK a, int natural) {
     if (n >= 0) mask |= 1ull << o;
   }
   if (MODE == kModeSubm && valid && my[a.centre] != static_cast<int32_t>(row)) mask = 0;
-  if (row < a.n_dest_cap) a.row_mask[row] = mask;
+  if (row < a.n_dest_cap) {
+    a.row_mask[row] = mask;
+    for (int o = 0; o < a.kvol; ++o) a.nbr[row * a.kvol + o] = ((mask >> o) & 1) ? my[o] : -1;
+  }
   if (!natural) return;
   const uint64_t tmask = group16_or(mask);
   if (r == 0) a.tile_mask[t] = tmask;
   a.tile_rows[t * kTile + r] = row < n_dest ? static_cast<int32_t>(row) : -1;
-  int k = 0;
-  for (uint64_t mm = tmask; mm; mm &= mm - 1, ++k) {
-    const int o = __builtin_ctzll(mm);
-    a.pool[(t * a.kvol + k) * kTile + r] = ((mask >> o) & 1) ? my[o] : -1;
-  }
-}
-
-template <int MODE>
-__global__ __launch_bounds__(256) void k_rel_tiles_any(RelK a) {
-  __shared__ int8_t offs[TS_MAX_KVOL * 3];
-  load_offsets(a, offs);
-  const int64_t t = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / kTile;
-  const int r = threadIdx.x & (kTile - 1);
-  if (t >= a.n_tiles) return;
-  const int32_t row = a.tile_rows[t * kTile + r];
-  uint64_t mask = 0;
-  int64_t b = 0, s[3] = {0, 0, 0};
-  if (row >= 0) {
-    mask = a.row_mask[row];
-    if (mask) dest_load<MODE>(a, row, &b, s);
-  }
-  const uint64_t tmask = group16_or(mask);
-  if (r == 0) a.tile_mask[t] = tmask;
-  int k = 0;
-  for (uint64_t mm = tmask; mm; mm &= mm - 1, ++k) {
-    const int o = __builtin_ctzll(mm);
-    a.pool[(t * a.kvol + k) * kTile + r] = ((mask >> o) & 1) ? probe<MODE>(a, offs, b, s, o) : -1;
-  }
 }
 
 // Pass 2: stable sort of each window's rows by offset mask.  1024 threads,
@@ -425,7 +372,8 @@ __device__ __forceinline__ int block_excl_1024(int v, int* wsum, int* total) {
 
 __global__ __launch_bounds__(kSortThreads) void k_rel_sort(const uint64_t* __restrict__ row_mask, int64_t n_dest_cap,
                                                            const int64_t* n_dest_p, int nbits, int64_t n_slots,
-                                                           int32_t* __restrict__ tile_rows) {
+                                                           int32_t* __restrict__ tile_rows,
+                                                           uint64_t* __restrict__ tile_mask) {
   __shared__ uint2 buf[kSortWindow];
   __shared__ int wsum[kSortThreads / 64];
   const int64_t base = static_cast<int64_t>(blockIdx.x) * kSortWindow;
@@ -467,11 +415,19 @@ __global__ __launch_bounds__(kSortThreads) void k_rel_sort(const uint64_t* __res
     }
     __syncthreads();
   }
+  // a tile = 16 consecutive slots = 4 consecutive threads
+  uint64_t tm = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int64_t slot = base + threadIdx.x * 4 + i;
     if (slot < n_slots) tile_rows[slot] = row[i];
+    tm |= row[i] >= 0 ? row_mask[row[i]] : 0ull;
   }
+  const uint32_t lo = static_cast<uint32_t>(tm), hi = static_cast<uint32_t>(tm >> 32);
+  const uint32_t lo2 = lo | __shfl_xor(lo, 1, 64), hi2 = hi | __shfl_xor(hi, 1, 64);
+  const uint32_t lo4 = lo2 | __shfl_xor(lo2, 2, 64), hi4 = hi2 | __shfl_xor(hi2, 2, 64);
+  const int64_t slot0 = base + threadIdx.x * 4;
+  if ((threadIdx.x & 3) == 0 && slot0 < n_slots) tile_mask[slot0 / kTile] = (static_cast<uint64_t>(hi4) << 32) | lo4;
 }
 
 // Per-offset pair lists, destination rows in index order.  Blocks of 256
@@ -503,13 +459,9 @@ __global__ void k_pairs_start(const int32_t* __restrict__ base, int kvol, int64_
   if (o == kvol) pair_start[kvol] = *total;
 }
 
-template <int MODE>
 __global__ __launch_bounds__(256) void k_pairs_fill(RelK a, int64_t nblk, const int32_t* __restrict__ base,
                                                     int32_t* __restrict__ pair_in, int32_t* __restrict__ pair_out) {
   __shared__ int wave_cnt[4][TS_MAX_KVOL];
-  __shared__ int8_t offs[TS_MAX_KVOL * 3];
-  const int8_t* src_offs = &a.offs.d[0][0];
-  for (int i = threadIdx.x; i < a.kvol * 3; i += blockDim.x) offs[i] = src_offs[i];
   const int64_t n_dest = dest_count(a.n_dest, a.n_dest_cap);
   const int64_t row = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   const uint64_t mask = row < n_dest ? a.row_mask[row] : 0;
@@ -520,8 +472,6 @@ __global__ __launch_bounds__(256) void k_pairs_fill(RelK a, int64_t nblk, const 
     if (lane == 0) wave_cnt[wave][o] = __popcll(bal);
   }
   __syncthreads();
-  int64_t b = 0, s[3] = {0, 0, 0};
-  if (mask) dest_load<MODE>(a, row, &b, s);
   for (int o = 0; o < a.kvol; ++o) {
     const bool has = (mask >> o) & 1;
     const uint64_t bal = __ballot(has);  // every lane takes part
@@ -529,7 +479,7 @@ __global__ __launch_bounds__(256) void k_pairs_fill(RelK a, int64_t nblk, const 
     int pos = base[o * nblk + blockIdx.x] + __popcll(bal & below);
     for (int w = 0; w < wave; ++w) pos += wave_cnt[w][o];
     pair_out[pos] = static_cast<int32_t>(row);
-    pair_in[pos] = probe<MODE>(a, offs, b, s, o);
+    pair_in[pos] = a.nbr[row * a.kvol + o];
   }
 }
 
@@ -548,7 +498,7 @@ RelK make_relk(const RelBuild& bld, const ts_rel& rel) {
   a.n_tiles = rel.n_tiles;
   a.tile_mask = rel.tile_mask;
   a.tile_rows = rel.tile_rows;
-  a.pool = rel.pool;
+  a.nbr = rel.nbr;
   a.row_mask = rel.row_mask;
   return a;
 }
@@ -557,16 +507,13 @@ void launch_sort(const RelK& a, hipStream_t s) {
   const int64_t slots = a.n_tiles * kTile;
   const int nbits = a.kvol < 32 ? a.kvol : 32;
   k_rel_sort<<<static_cast<unsigned>(ceil_div<int64_t>(slots, kSortWindow)), kSortThreads, 0, s>>>(
-      a.row_mask, a.n_dest_cap, a.n_dest, nbits, slots, a.tile_rows);
+      a.row_mask, a.n_dest_cap, a.n_dest, nbits, slots, a.tile_rows, a.tile_mask);
 }
 
 template <int MODE, int ND, int K>
 void launch_rel_geo(const RelK& a, bool natural, unsigned grid, int64_t* n_out_fill, hipStream_t s) {
   k_rel_probe<MODE, ND, K><<<grid, 256, 0, s>>>(a, natural ? 1 : 0, n_out_fill);
-  if (!natural) {
-    launch_sort(a, s);
-    k_rel_tiles<MODE, ND, K><<<grid, 256, 0, s>>>(a);
-  }
+  if (!natural) launch_sort(a, s);
 }
 
 template <int MODE>
@@ -574,10 +521,7 @@ void launch_rel_any(const RelK& a, bool natural, unsigned grid, int64_t* n_out_f
   const size_t lds = static_cast<size_t>(256) * a.kvol * sizeof(int32_t);
   if (n_out_fill) (void)fill_i64(n_out_fill, 1, a.n_dest_cap, s);
   k_rel_probe_any<MODE><<<grid, 256, lds, s>>>(a, natural ? 1 : 0);
-  if (!natural) {
-    launch_sort(a, s);
-    k_rel_tiles_any<MODE><<<grid, 256, 0, s>>>(a);
-  }
+  if (!natural) launch_sort(a, s);
 }
 
 template <int MODE>
@@ -627,11 +571,7 @@ hipError_t launch_pairs_build(const RelBuild& bld, const ts_rel& rel, int64_t* p
   if (e != hipSuccess) return e;
   k_pairs_start<<<1, 128, 0, s>>>(cnt, bld.kvol, nblk, pair_start + bld.kvol, pair_start);
   RelK a = make_relk(bld, rel);
-  switch (bld.mode) {
-    case kModeSubm: k_pairs_fill<kModeSubm><<<static_cast<unsigned>(nblk), 256, 0, s>>>(a, nblk, cnt, pair_in, pair_out); break;
-    case kModeDown: k_pairs_fill<kModeDown><<<static_cast<unsigned>(nblk), 256, 0, s>>>(a, nblk, cnt, pair_in, pair_out); break;
-    default: k_pairs_fill<kModeUp><<<static_cast<unsigned>(nblk), 256, 0, s>>>(a, nblk, cnt, pair_in, pair_out); break;
-  }
+  k_pairs_fill<<<static_cast<unsigned>(nblk), 256, 0, s>>>(a, nblk, cnt, pair_in, pair_out);
   return hipGetLastError();
 }
 

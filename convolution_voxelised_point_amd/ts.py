@@ -40,7 +40,7 @@ _vp, _i64, _i32, _u32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctyp
 
 class TsRel(ctypes.Structure):
     _fields_ = [("n_dest_cap", _i64), ("n_tiles", _i64), ("n_dest", _vp), ("tile_mask", _vp),
-                ("tile_rows", _vp), ("pool", _vp), ("row_mask", _vp)]
+                ("tile_rows", _vp), ("nbr", _vp), ("row_mask", _vp)]
 
 
 class TsKmap(ctypes.Structure):
@@ -253,7 +253,7 @@ class Kmap:
         return {
             "tile_mask": self._view(r.tile_mask, torch.int64, nt),
             "tile_rows": self._view(r.tile_rows, torch.int32, nt * TS_TILE),
-            "pool": self._view(r.pool, torch.int32, nt * kv * TS_TILE),
+            "nbr": self._view(r.nbr, torch.int32, r.n_dest_cap * kv),
             "row_mask": self._view(r.row_mask, torch.int64, r.n_dest_cap),
         }
 
@@ -267,29 +267,19 @@ class Kmap:
 
 
 def decode_rel(arrs: dict, kvol: int, transposed: bool = False) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
-    """Host decode of a tiled relation into (in, out, offset) triples.
+    """Host decode of a relation into (in, out, offset) triples, walking the
+    tiles (so every destination row must sit in exactly one tile slot).
 
     Used by tests; ``transposed`` marks a relation whose destinations are
     input rows."""
-    tm = arrs["tile_mask"].cpu().numpy().view(np.uint64)
-    rows = arrs["tile_rows"].cpu().numpy().reshape(-1, TS_TILE)
-    pool = arrs["pool"].cpu().numpy().reshape(-1, kvol, TS_TILE)
-    ti, to, tf = [], [], []
-    for t in range(tm.shape[0]):
-        m = int(tm[t])
-        k = 0
-        o = 0
-        while m:
-            if m & 1:
-                src = pool[t, k]
-                dst = rows[t]
-                ok = (src >= 0) & (dst >= 0)
-                ti.append(src[ok]); to.append(dst[ok]); tf.append(np.full(int(ok.sum()), o, np.int32))
-                k += 1
-            m >>= 1
-            o += 1
-    cat = (lambda a: np.concatenate(a).astype(np.int32) if a else np.zeros(0, np.int32))
-    a, b, c = cat(ti), cat(to), cat(tf)
+    rows = arrs["tile_rows"].cpu().numpy()
+    rows = rows[rows >= 0].astype(np.int64)
+    nbr = arrs["nbr"].cpu().numpy().reshape(-1, kvol)
+    sub = nbr[rows]
+    d, o = np.nonzero(sub >= 0)
+    a = sub[d, o].astype(np.int32)
+    b = rows[d].astype(np.int32)
+    c = o.astype(np.int32)
     return (b, a, c) if transposed else (a, b, c)
 
 

@@ -142,15 +142,15 @@ ts_status ts_strided_support(const int32_t* in_coords, int64_t n_in, int ndim, i
 /* ------------------------------------------------------------------------
  * Kernel map (the "kernel-map construction" of the page's section "Sparse
  * tensor expectations"): for every output row j and offset o, the input row
- * i at q_j + delta_o (stride 1) or s q_j + delta_o (stride s), as a tiled
- * relation:
+ * i at q_j + delta_o (stride 1) or s q_j + delta_o (stride s), as a relation
+ * between destination rows and source rows:
  *
- *   destination rows are grouped in tiles of TS_TILE; tile t has an offset
- *   bit mask tile_mask[t] (bit o set when any of its rows has a neighbour at
- *   offset o); for the k-th set bit o of tile_mask[t] (ascending),
- *   pool[(t*kvol + k)*TS_TILE + r] is the source row of slot r at offset o,
- *   or -1; tile_rows[t*TS_TILE + r] is the destination row in slot r, or -1.
- *   row_mask[d] is the offset mask of destination row d.
+ *   nbr[d*kvol + o] is the source row of destination row d at offset o, or
+ *   -1; row_mask[d] has bit o set exactly when nbr[d*kvol + o] >= 0.
+ *   Destination rows are grouped in tiles of TS_TILE: tile_rows[t*TS_TILE + r]
+ *   is the destination row in slot r of tile t (-1 for padding; every row
+ *   appears once), and tile_mask[t] is the OR of its rows' masks, so the
+ *   contraction of a tile skips every offset none of its rows uses.
  *
  * Which destination rows share a tile is a performance choice (rows with
  * similar masks are grouped unless TS_KMAP_NATURAL is set); the relation
@@ -162,7 +162,7 @@ typedef struct ts_rel {
   const int64_t* n_dest; /* device int64: destination row count                */
   uint64_t* tile_mask;   /* device [n_tiles]                                   */
   int32_t* tile_rows;    /* device [n_tiles * TS_TILE]                         */
-  int32_t* pool;         /* device [n_tiles * kvol * TS_TILE]                  */
+  int32_t* nbr;          /* device [n_dest_cap * kvol]                         */
   uint64_t* row_mask;    /* device [n_dest_cap]                                */
 } ts_rel;
 
