@@ -104,13 +104,14 @@ ts_status check_conv(const ts_kmap* map, int cin, int cout, ts_dtype in, ts_dtyp
   return TS_OK;
 }
 
-bool use_igemm(ts_dataflow df, int kvol, int c_src, int c_dst, ts_dtype in) {
-  return (df == TS_DATAFLOW_AUTO || df == TS_DATAFLOW_IMPLICIT_GEMM) && igemm_supported(kvol, c_src, c_dst, in);
+bool use_igemm(ts_dataflow df, int kvol, int64_t n_src, int c_src, int c_dst, ts_dtype in) {
+  return (df == TS_DATAFLOW_AUTO || df == TS_DATAFLOW_IMPLICIT_GEMM) && igemm_supported(kvol, n_src, c_src, c_dst, in);
 }
 
-size_t conv_ws(const ts_kmap* map, int c_src, int c_dst, ts_dtype in, ts_dtype out, ts_dataflow df, int64_t n_dest) {
+size_t conv_ws(const ts_kmap* map, int c_src, int c_dst, ts_dtype in, ts_dtype out, ts_dataflow df, int64_t n_dest,
+               int64_t n_src) {
   if (df == TS_DATAFLOW_GATHER_SCATTER) return gs_workspace_bytes(n_dest, c_dst, out);
-  if (use_igemm(df, map->kvol, c_src, c_dst, in)) return igemm_workspace_bytes(map->kvol, c_src, c_dst);
+  if (use_igemm(df, map->kvol, n_src, c_src, c_dst, in)) return igemm_workspace_bytes(map->kvol, c_src, c_dst);
   return 0;
 }
 
@@ -252,8 +253,8 @@ size_t ts_conv_workspace_bytes(const ts_kmap* map, int cin, int cout, int op, ts
                                ts_dataflow dataflow) {
   if (!map || cin < 1 || cout < 1) return 0;
   switch (op) {
-    case TS_OP_FWD: return conv_ws(map, cin, cout, in_dtype, TS_BF16, dataflow, map->n_out_cap);
-    case TS_OP_DGRAD: return conv_ws(map, cout, cin, in_dtype, TS_BF16, dataflow, map->n_in);
+    case TS_OP_FWD: return conv_ws(map, cin, cout, in_dtype, TS_BF16, dataflow, map->n_out_cap, map->n_in);
+    case TS_OP_DGRAD: return conv_ws(map, cout, cin, in_dtype, TS_BF16, dataflow, map->n_in, map->n_out_cap);
     case TS_OP_WGRAD: return wgrad_workspace_bytes(map, cin, cout);
   }
   return 0;
@@ -266,12 +267,13 @@ ts_status ts_conv_fwd(const ts_kmap* map, const void* x, int cin, const void* w,
   if (st != TS_OK) return st;
   if (dataflow < TS_DATAFLOW_AUTO || dataflow > TS_DATAFLOW_GATHER_SCATTER) return TS_ERR_INVALID_ARG;
   if (!w || (map->n_in > 0 && !x) || (map->n_out_cap > 0 && !y)) return TS_ERR_INVALID_ARG;
-  const size_t need = conv_ws(map, cin, cout, in_dtype, out_dtype, dataflow, map->n_out_cap);
+  const size_t need = conv_ws(map, cin, cout, in_dtype, out_dtype, dataflow, map->n_out_cap, map->n_in);
   if (need > 0 && (!ws || ws_bytes < need)) return TS_ERR_INVALID_ARG;
   ConvArgs a;
   a.rel = &map->fwd;
   a.kvol = map->kvol;
   a.src = x;
+  a.n_src = map->n_in;
   a.c_src = cin;
   a.dst = y;
   a.c_dst = cout;
@@ -285,7 +287,7 @@ ts_status ts_conv_fwd(const ts_kmap* map, const void* x, int cin, const void* w,
   if (dataflow == TS_DATAFLOW_GATHER_SCATTER) {
     if (!(map->flags & TS_KMAP_PAIRS)) return TS_ERR_INVALID_ARG;
     TS_TRY(launch_gather_scatter(map, a, false, map->n_out_cap, ws, stream));
-  } else if (use_igemm(dataflow, map->kvol, cin, cout, in_dtype)) {
+  } else if (use_igemm(dataflow, map->kvol, map->n_in, cin, cout, in_dtype)) {
     TS_TRY(launch_igemm(a, ws, stream));
   } else {
     TS_TRY(launch_direct(a, stream));
@@ -322,7 +324,7 @@ ts_status ts_conv_fwd_strided(const int32_t* in_coords, int64_t n_in, int ndim, 
     if (dataflow == TS_DATAFLOW_GATHER_SCATTER && !(kmap_flags & TS_KMAP_PAIRS)) return TS_ERR_INVALID_ARG;
     ts_kmap probe;
     layout_kmap(nullptr, &probe, n_in, n_in, ndim, ksize, stride, kmap_flags);
-    const size_t need = conv_ws(&probe, cin, cout, in_dtype, out_dtype, dataflow, n_in);
+    const size_t need = conv_ws(&probe, cin, cout, in_dtype, out_dtype, dataflow, n_in, n_in);
     if (need > 0 && (!ws || ws_bytes < need)) return TS_ERR_INVALID_ARG;
     (void)kvol;
   }
@@ -343,11 +345,12 @@ ts_status ts_conv_bwd_dgrad(const ts_kmap* map, const void* dy, int cout, const 
   if (st != TS_OK) return st;
   if (dataflow < TS_DATAFLOW_AUTO || dataflow > TS_DATAFLOW_GATHER_SCATTER) return TS_ERR_INVALID_ARG;
   if (!w || (map->n_out_cap > 0 && !dy) || (map->n_in > 0 && !dx)) return TS_ERR_INVALID_ARG;
-  const size_t need = conv_ws(map, cout, cin, in_dtype, out_dtype, dataflow, map->n_in);
+  const size_t need = conv_ws(map, cout, cin, in_dtype, out_dtype, dataflow, map->n_in, map->n_out_cap);
   if (need > 0 && (!ws || ws_bytes < need)) return TS_ERR_INVALID_ARG;
   ConvArgs a;
   a.kvol = map->kvol;
   a.src = dy;
+  a.n_src = map->n_out_cap;
   a.c_src = cout;
   a.dst = dx;
   a.c_dst = cin;
@@ -372,7 +375,7 @@ ts_status ts_conv_bwd_dgrad(const ts_kmap* map, const void* dy, int cout, const 
     a.rel = &map->bwd;
     a.mirror = false;
   }
-  if (use_igemm(dataflow, map->kvol, cout, cin, in_dtype)) {
+  if (use_igemm(dataflow, map->kvol, map->n_out_cap, cout, cin, in_dtype)) {
     TS_TRY(launch_igemm(a, ws, stream));
   } else {
     TS_TRY(launch_direct(a, stream));

@@ -24,11 +24,11 @@
 // Latency: the neighbour rows of a tile's 16 rows (the source row of each
 // slot at each offset) are loaded once, up front, into registers and picked
 // per offset with a lane shuffle, so no load address waits on another load
-// inside the loop.  Gathers and weight loads run two offsets ahead (three register sets
-// of gathers, two LDS weight buffers, one barrier per offset); each step first
-// stores the weights loaded one step earlier into the free LDS buffer, then
-// issues the next weight loads before its gathers, so that the in-order load
-// counter never forces a gather to land early.  Every output
+// inside the loop.  Gathers and weight loads run D offsets ahead (D+1
+// register sets of each, two LDS weight buffers, one barrier per offset), so
+// the in-order load counter never forces a load to land early.  Gathers are
+// buffer loads: an absent row reads out of range and returns zeros without a
+// memory access.  Every output
 // row is written once, no atomics.  Blocks are numbered so that each XCD walks
 // a contiguous range of tiles (its L2 keeps the gathered rows).
 #include <stdlib.h>
@@ -75,6 +75,7 @@ struct IgK {
   int64_t n_tiles;
   int kvol;
   const void* src;
+  uint32_t src_bytes;  // < 2^31: a buffer offset of 2^31 is out of range
   int c_src;
   const u32x4* wp;  // packed fragments [kvol][mbt][c_src/32][64]
   int mbt;          // fragments of 16 output channels in the packed weights
@@ -119,13 +120,50 @@ __global__ __launch_bounds__(256) void k_wpack(const T* __restrict__ w, int kvol
   out[i] = v;
 }
 
+// Stores 4 consecutive output channels (fp32 accumulators) in the output type.
+__device__ __forceinline__ void store4(void* dst, int out_dtype, int64_t off, f32x4 v) {
+  if (out_dtype == TS_F32) {
+    *reinterpret_cast<f32x4*>(static_cast<float*>(dst) + off) = v;
+  } else if (out_dtype == TS_F16) {
+    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+    h4 h = {static_cast<_Float16>(v[0]), static_cast<_Float16>(v[1]), static_cast<_Float16>(v[2]),
+            static_cast<_Float16>(v[3])};
+    *reinterpret_cast<h4*>(static_cast<_Float16*>(dst) + off) = h;
+  } else {
+    typedef __bf16 b4 __attribute__((ext_vector_type(4)));
+    b4 h = {static_cast<__bf16>(v[0]), static_cast<__bf16>(v[1]), static_cast<__bf16>(v[2]),
+            static_cast<__bf16>(v[3])};
+    *reinterpret_cast<b4*>(static_cast<__bf16*>(dst) + off) = h;
+  }
+}
+
 __device__ __forceinline__ int next_bit(uint64_t u, int o) {
   if (o < 0 || o >= 63) return -1;
   const uint64_t rest = u & ~((2ull << o) - 1);
   return rest ? __builtin_ctzll(rest) : -1;
 }
 
-template <typename T, int MB, int KB, int G>
+// Compile-time step index, so that register sets picked by step stay static.
+template <int I>
+struct Ic {
+  static constexpr int v = I;
+};
+template <int I, int N>
+struct Seq {
+  template <typename F>
+  __device__ __forceinline__ static bool go(F& f) {
+    return f(Ic<I>{}) && Seq<I + 1, N>::go(f);
+  }
+};
+template <int N>
+struct Seq<N, N> {
+  template <typename F>
+  __device__ __forceinline__ static bool go(F&) {
+    return true;
+  }
+};
+
+template <typename T, int MB, int KB, int G, int D>
 __global__ __launch_bounds__(256) void k_igemm(IgK a) {
   typedef typename Mfma<T>::frag Frag;
   constexpr int FR = MB * KB;                      // fragments per offset and block column
@@ -186,16 +224,21 @@ __global__ __launch_bounds__(256) void k_igemm(IgK a) {
     for (int jj = 1; jj < kNbRegs; ++jj) v = (j == jj) ? pr[g][jj] : v;
     return __shfl(v, col + 16 * q, 64);
   };
-  // Gathers of offset o, branch-free (row 0 when there is nothing to fetch);
-  // ok[g] marks a present row, and consumers zero the others.
-  auto gather = [&](int o, Frag (&x)[G][KB], bool (&ok)[G]) {
+  // Gathers of offset o as buffer loads over the source matrix: a row that is
+  // absent (or a tile without the offset) gets an out-of-range offset, which
+  // returns zeros without touching memory, so no select is needed at use and
+  // no cache access is spent on it.
+  const __amdgpu_buffer_rsrc_t xr =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(src), 0, static_cast<int>(a.src_bytes), 0x00020000);
+  auto gather = [&](int o, Frag (&x)[G][KB]) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const int32_t nb = pool_row(g, o);
-      ok[g] = ((m[g] >> o) & 1) && nb >= 0;
-      const T* row = src + static_cast<int64_t>(ok[g] ? nb : 0) * c_src + kq * 8;
+      const bool ok = ((m[g] >> o) & 1) && nb >= 0;
+      const uint32_t off = ok ? static_cast<uint32_t>(nb * c_src + kq * 8) * 2u : 0x80000000u;
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) x[g][kb] = __builtin_bit_cast(Frag, *reinterpret_cast<const u32x4*>(row + kb * 32));
+      for (int kb = 0; kb < KB; ++kb)
+        x[g][kb] = __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(xr, static_cast<int>(off + kb * 64), 0, 0));
     }
   };
   // This thread's chunks of the packed slice of offset o.  Chunks of
@@ -220,29 +263,36 @@ __global__ __launch_bounds__(256) void k_igemm(IgK a) {
   };
 
   if (U) {
-    // Offsets u_0 < u_1 < ... of U.  Entering step i: LDS buffer i%2 holds
-    // W(u_i); the weight registers hold W(u_{i+1}); gather set i%3 holds
-    // X(u_i) (issued at step i-2) and set (i+1)%3 holds X(u_{i+1}).  Past the
-    // last offset the prefetches repeat a valid offset (harmless loads).
-    int o0 = __builtin_ctzll(U);
-    int o1 = next_bit(U, o0);
-    int o2 = o1 >= 0 ? next_bit(U, o1) : -1;
-    Frag x0[G][KB], x1[G][KB], x2[G][KB];
-    bool k0[G], k1[G], k2[G];
-    u32x4 wr[CH];
-    wload(o0, wr);
-    gather(o0, x0, k0);
-    gather(o1 >= 0 ? o1 : o0, x1, k1);
-    wstore(wr, wl[0]);
-    wload(o1 >= 0 ? o1 : o0, wr);
+    // Offsets u_0 < u_1 < ... of U; R = D + 1 register sets of gathers and of
+    // weights.  Step i: store W(u_{i+1}) (loaded at step i+1-D) into LDS
+    // buffer (i+1)%2, load W(u_{i+D}) and gather X(u_{i+D}) into set
+    // (i+D)%R, multiply X(u_i) (set i%R) by W(u_i) (buffer i%2), barrier.
+    // Past the last offset the prefetches repeat a valid offset (harmless
+    // loads).  Loads of one step are thus always D steps ahead of their use
+    // and never forced early by the in-order load counter.
+    constexpr int R = D + 1;
+    Frag xs[R][G][KB];
+    u32x4 wr[R][CH];
+    int oc = __builtin_ctzll(U);  // u_i
+    int onx = oc;                 // u_{i+D} (repeats the last offset past the end)
+    int last = 63 - __builtin_clzll(U);
+    int ow = oc;                  // u_{i+1}
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      wload(onx, wr[j]);
+      gather(onx, xs[j]);
+      if (j + 1 < D) onx = onx < last ? next_bit(U, onx) : onx;
+    }
+    wstore(wr[0], wl[0]);
     __syncthreads();
-
-    auto step = [&](Frag (&xc)[G][KB], bool (&kc)[G], Frag (&xf)[G][KB], bool (&kf)[G], u32x4 (&w)[CH],
-                    int b) -> bool {
-      const int okeep = o2 >= 0 ? o2 : (o1 >= 0 ? o1 : o0);
-      wstore(w, wl[b ^ 1]);                       // W(u_{i+1}), loaded one step ago
-      wload(okeep, w);                            // W(u_{i+2}), before the gathers
-      gather(okeep, xf, kf);                      // X(u_{i+2})
+    ow = oc < last ? next_bit(U, oc) : oc;
+    auto step = [&](auto ic) -> bool {
+      constexpr int i = decltype(ic)::v;
+      constexpr int cur = i % R, nxt = (i + 1) % R, fill = (i + D) % R, b = i % 2;
+      wstore(wr[nxt], wl[b ^ 1]);                 // W(u_{i+1})
+      onx = onx < last ? next_bit(U, onx) : onx;  // u_{i+D}
+      wload(onx, wr[fill]);
+      gather(onx, xs[fill]);
       const u32x4* lw = wl[b];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
@@ -251,21 +301,18 @@ __global__ __launch_bounds__(256) void k_igemm(IgK a) {
         for (int mb = 0; mb < MB; ++mb) af[mb] = __builtin_bit_cast(Frag, lw[(mb * KB + kb) * 64 + lane]);
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-          if (!((m[g] >> o0) & 1)) continue;  // wave-uniform
-          const Frag bx = kc[g] ? xc[g][kb] : Frag{};
+          if (!((m[g] >> oc) & 1)) continue;  // wave-uniform
 #pragma unroll
-          for (int mb = 0; mb < MB; ++mb) acc[g][mb] = Mfma<T>::run(af[mb], bx, acc[g][mb]);
+          for (int mb = 0; mb < MB; ++mb) acc[g][mb] = Mfma<T>::run(af[mb], xs[cur][g][kb], acc[g][mb]);
         }
       }
-      if (o1 < 0) return false;
+      if (oc == last) return false;
       __syncthreads();
-      o0 = o1;
-      o1 = o2;
-      o2 = o2 >= 0 ? next_bit(U, o2) : -1;
+      oc = ow;
+      ow = ow < last ? next_bit(U, ow) : ow;
       return true;
     };
-    while (step(x0, k0, x2, k2, wr, 0) && step(x1, k1, x0, k0, wr, 1) && step(x2, k2, x1, k1, wr, 0) &&
-           step(x0, k0, x2, k2, wr, 1) && step(x1, k1, x0, k0, wr, 0) && step(x2, k2, x1, k1, wr, 1)) {
+    while (Seq<0, 2 * R>::go(step)) {
     }
   }
 
@@ -300,14 +347,14 @@ __global__ __launch_bounds__(256) void k_igemm(IgK a) {
 
 // Tiles per wave.  Default 1: more blocks in flight and a smaller offset
 // union per block beat sharing a weight slice across more tiles; the
-// environment variable TS_IGEMM_G (1, 2 or 4) overrides it for tuning.
+// environment variable TS_IGEMM_G (1 or 2) overrides it for tuning.
 static int tiles_per_wave(int mb) {
   static const int forced = [] {
     const char* e = getenv("TS_IGEMM_G");
     return e ? atoi(e) : 0;
   }();
   (void)mb;
-  if (forced == 1 || forced == 2 || forced == 4) return forced;
+  if (forced == 1 || forced == 2) return forced;
   return 1;
 }
 
@@ -322,22 +369,35 @@ static int xcd_map_on() {
   return on;
 }
 
+// Prefetch depth in offsets: TS_IGEMM_D (2, 3 or 4) overrides the default 2.
+static int prefetch_depth() {
+  static const int d = [] {
+    const char* e = getenv("TS_IGEMM_D");
+    const int v = e ? atoi(e) : 0;
+    return (v >= 2 && v <= 4) ? v : 2;
+  }();
+  return d;
+}
+
 template <typename T, int MB, int KB, int G>
 hipError_t launch_g(IgK k, hipStream_t s) {
   k.nblk = ceil_div<int64_t>(k.n_tiles, 4 * G);
   k.nb8 = ceil_div<int64_t>(k.nblk, 8);
   k.xcd_map = xcd_map_on();
   dim3 grid(static_cast<unsigned>(k.xcd_map ? k.nb8 * 8 : k.nblk), static_cast<unsigned>(ceil_div(k.c_dst / 16, MB)));
-  k_igemm<T, MB, KB, G><<<grid, 256, 0, s>>>(k);
+  switch (prefetch_depth()) {
+    case 2: k_igemm<T, MB, KB, G, 2><<<grid, 256, 0, s>>>(k); break;
+    case 4: k_igemm<T, MB, KB, G, 4><<<grid, 256, 0, s>>>(k); break;
+    default: k_igemm<T, MB, KB, G, 3><<<grid, 256, 0, s>>>(k); break;
+  }
   return hipGetLastError();
 }
 
 template <typename T, int MB, int KB>
 hipError_t launch_mb_kb(const IgK& k, hipStream_t s) {
   switch (tiles_per_wave(MB)) {
-    case 1: return launch_g<T, MB, KB, 1>(k, s);
     case 2: return launch_g<T, MB, KB, 2>(k, s);
-    default: return launch_g<T, MB, KB, 4>(k, s);
+    default: return launch_g<T, MB, KB, 1>(k, s);
   }
 }
 
@@ -374,9 +434,10 @@ hipError_t launch_t(const IgK& k, hipStream_t s) {
 
 }  // namespace
 
-bool igemm_supported(int kvol, int c_src, int c_dst, ts_dtype in_dtype) {
+bool igemm_supported(int kvol, int64_t n_src, int c_src, int c_dst, ts_dtype in_dtype) {
+  const int64_t bytes = n_src * c_src * 2;
   return in_dtype != TS_F32 && kvol >= 1 && kvol <= kMaxIgemmKvol && c_src % 32 == 0 && c_dst % 16 == 0 &&
-         c_src > 0 && c_src <= 128 && c_dst > 0;
+         c_src > 0 && c_src <= 128 && c_dst > 0 && bytes < (int64_t{1} << 31);
 }
 
 size_t igemm_workspace_bytes(int kvol, int c_src, int c_dst) {
@@ -393,6 +454,7 @@ hipError_t launch_igemm(const ConvArgs& a, void* ws, hipStream_t s) {
   k.n_tiles = rel.n_tiles;
   k.kvol = a.kvol;
   k.src = a.src;
+  k.src_bytes = static_cast<uint32_t>(a.n_src * a.c_src * 2);
   k.c_src = a.c_src;
   k.wp = static_cast<const u32x4*>(ws);
   k.mbt = ceil_div(a.c_dst, 16);

@@ -345,29 +345,25 @@ __global__ __launch_bounds__(256) void k_rel_probe_any(RelK a, int natural) {
   a.tile_rows[t * kTile + r] = row < n_dest ? static_cast<int32_t>(row) : -1;
 }
 
-// Pass 2: stable sort of each window's rows by offset mask.  1024 threads,
-// 4 rows each; one split pass per mask bit (zeros before ones, order kept),
-// a block-wide prefix sum giving every row its new place.
-__device__ __forceinline__ int block_excl_1024(int v, int* wsum, int* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int x = v;
+// Pass 2: stable sort of each window's rows by offset mask: an LSD radix
+// sort with 4-bit digits in LDS.  1024 threads; thread t holds window
+// elements t, t+1024, t+2048, t+3072 (element order = row order).  Per pass:
+//   * inside a wave, a row's rank among the rows of its item and digit comes
+//     from four ballots (one per digit bit) and a lane-mask popcount;
+//   * the (digit, item, wave) counts, laid out digit-major, are
+//     exclusive-scanned once across the block, which yields every row's
+//     destination directly;
+// ties keep their order, so the map is deterministic.
+constexpr int kDigits = 16;
+constexpr int kItems = kSortWindow / kSortThreads;  // 4
+constexpr int kSortWaves = kSortThreads / 64;       // 16
+
+// Lanes whose digit equals d, from the four per-bit ballots.
+__device__ __forceinline__ uint64_t digit_lanes(const uint64_t (&bal)[4], uint32_t d) {
+  uint64_t m = ~0ull;
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) wsum[wave] = x;
-  __syncthreads();
-  int before = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < kSortThreads / 64; ++w) {
-    const int sv = wsum[w];
-    before += w < wave ? sv : 0;
-    tot += sv;
-  }
-  __syncthreads();
-  *total = tot;
-  return before + x - v;
+  for (int b = 0; b < 4; ++b) m &= ((d >> b) & 1) ? bal[b] : ~bal[b];
+  return m;
 }
 
 __global__ __launch_bounds__(kSortThreads) void k_rel_sort(const uint64_t* __restrict__ row_mask, int64_t n_dest_cap,
@@ -375,59 +371,72 @@ __global__ __launch_bounds__(kSortThreads) void k_rel_sort(const uint64_t* __res
                                                            int32_t* __restrict__ tile_rows,
                                                            uint64_t* __restrict__ tile_mask) {
   __shared__ uint2 buf[kSortWindow];
-  __shared__ int wsum[kSortThreads / 64];
+  __shared__ int hist[kDigits * kItems * kSortWaves];  // [digit][item][wave] -> exclusive start
+  __shared__ int wsum[kSortWaves];
   const int64_t base = static_cast<int64_t>(blockIdx.x) * kSortWindow;
   const int64_t n_dest = dest_count(n_dest_p, n_dest_cap);
-  uint32_t key[4];
-  int32_t row[4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint64_t lt = (1ull << lane) - 1;
+  uint32_t key[kItems];
+  int32_t row[kItems];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t r = base + threadIdx.x * 4 + i;
+  for (int i = 0; i < kItems; ++i) {
+    const int64_t r = base + i * kSortThreads + threadIdx.x;
     const bool ok = r < n_dest;
     const uint64_t m = ok ? row_mask[r] : 0;
     key[i] = ok ? static_cast<uint32_t>(m ^ (m >> 32)) : 0xffffffffu;
     row[i] = ok ? static_cast<int32_t>(r) : -1;
   }
-  for (int bit = 0; bit < nbits; ++bit) {
-    int f[4], c = 0;
+  for (int sh = 0; sh < nbits; sh += 4) {
+    int rank[kItems];
+    uint32_t d[kItems];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f[i] = (key[i] >> bit) & 1;
-      c += f[i];
+    for (int i = 0; i < kItems; ++i) {
+      d[i] = (key[i] >> sh) & (kDigits - 1);
+      uint64_t bal[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) bal[b] = __ballot((d[i] >> b) & 1);
+      rank[i] = __popcll(digit_lanes(bal, d[i]) & lt);
+      if (lane < kDigits) hist[(lane * kItems + i) * kSortWaves + wave] = __popcll(digit_lanes(bal, lane));
     }
-    int ones;
-    int before = block_excl_1024(c, wsum, &ones);
-    if (ones == 0 || ones == kSortWindow) continue;  // block-uniform
-    const int zeros = kSortWindow - ones;
+    __syncthreads();
+    // block-wide exclusive scan of the 1024 counts (one per thread)
+    const int v = hist[threadIdx.x];
+    int x = v;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = threadIdx.x * 4 + i;
-      const int dest = f[i] ? zeros + before : e - before;
-      before += f[i];
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o, 64);
+      x += lane >= o ? y : 0;
+    }
+    if (lane == 63) wsum[wave] = x;
+    __syncthreads();
+    int before = 0;
+#pragma unroll
+    for (int w = 0; w < kSortWaves; ++w) before += w < wave ? wsum[w] : 0;
+    hist[threadIdx.x] = before + x - v;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kItems; ++i) {
+      const int dest = hist[(d[i] * kItems + i) * kSortWaves + wave] + rank[i];
       buf[dest] = make_uint2(key[i], static_cast<uint32_t>(row[i]));
     }
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint2 v = buf[threadIdx.x * 4 + i];
-      key[i] = v.x;
-      row[i] = static_cast<int32_t>(v.y);
+    for (int i = 0; i < kItems; ++i) {
+      const uint2 e = buf[i * kSortThreads + threadIdx.x];
+      key[i] = e.x;
+      row[i] = static_cast<int32_t>(e.y);
     }
-    __syncthreads();
+    __syncthreads();  // reads of buf and hist done before the next pass writes them
   }
-  // a tile = 16 consecutive slots = 4 consecutive threads
-  uint64_t tm = 0;
+  // a tile = 16 consecutive slots = 16 consecutive lanes of one item
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t slot = base + threadIdx.x * 4 + i;
+  for (int i = 0; i < kItems; ++i) {
+    const int64_t slot = base + i * kSortThreads + threadIdx.x;
     if (slot < n_slots) tile_rows[slot] = row[i];
-    tm |= row[i] >= 0 ? row_mask[row[i]] : 0ull;
+    const uint64_t tm = group16_or(row[i] >= 0 ? row_mask[row[i]] : 0ull);
+    if ((lane & 15) == 0 && slot < n_slots) tile_mask[slot / kTile] = tm;
   }
-  const uint32_t lo = static_cast<uint32_t>(tm), hi = static_cast<uint32_t>(tm >> 32);
-  const uint32_t lo2 = lo | __shfl_xor(lo, 1, 64), hi2 = hi | __shfl_xor(hi, 1, 64);
-  const uint32_t lo4 = lo2 | __shfl_xor(lo2, 2, 64), hi4 = hi2 | __shfl_xor(hi2, 2, 64);
-  const int64_t slot0 = base + threadIdx.x * 4;
-  if ((threadIdx.x & 3) == 0 && slot0 < n_slots) tile_mask[slot0 / kTile] = (static_cast<uint64_t>(hi4) << 32) | lo4;
 }
 
 // Per-offset pair lists, destination rows in index order.  Blocks of 256

@@ -60,6 +60,7 @@ struct ConvArgs {
   const ts_rel* rel;  // relation walked (destination tiles)
   int kvol;
   const void* src;    // source features [n_src][c_src]
+  int64_t n_src;
   int c_src;
   void* dst;          // destination features [n_dest][c_dst]
   int c_dst;
@@ -71,7 +72,7 @@ struct ConvArgs {
 };
 
 size_t igemm_workspace_bytes(int kvol, int c_src, int c_dst);
-bool igemm_supported(int kvol, int c_src, int c_dst, ts_dtype in_dtype);
+bool igemm_supported(int kvol, int64_t n_src, int c_src, int c_dst, ts_dtype in_dtype);
 hipError_t launch_igemm(const ConvArgs& a, void* ws, hipStream_t s);
 hipError_t launch_direct(const ConvArgs& a, hipStream_t s);
 

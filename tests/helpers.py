@@ -45,3 +45,16 @@ def dev(a, dtype=None) -> torch.Tensor:
     if dtype is not None:
         t = t.to(dtype)
     return t.contiguous().cuda()
+
+
+def check_window_sorted(slots, rm, window=4096):
+    """Inside each window of slots, rows are ordered by (folded) offset mask,
+    ties in row order, and every window holds exactly its own rows."""
+    for w0 in range(0, len(slots), window):
+        rows = slots[w0:w0 + window]
+        rows = rows[rows >= 0]
+        np.testing.assert_array_equal(np.sort(rows), np.arange(w0, w0 + len(rows)))
+        m = rm[rows]
+        key = (m ^ (m >> np.uint64(32))) & np.uint64(0xffffffff)
+        order = np.lexsort((rows, key))
+        np.testing.assert_array_equal(order, np.arange(len(rows)))

@@ -10,7 +10,7 @@ import torch
 import bench
 import oracle
 from convolution_voxelised_point_amd import synth
-from helpers import assert_feature_close, canon
+from helpers import assert_feature_close, canon, check_window_sorted
 
 pytestmark = pytest.mark.gpu
 
@@ -61,6 +61,8 @@ def test_full_lidar_subm_f16(ts):
     check_hash(ts, s, w.coords, 11)
     tr = oracle.kmap(w.coords, w.coords, 3, 1)
     check_triples(s.kmap, tr, 27, "lidar")
+    rel = s.kmap.rel_arrays("fwd")
+    check_window_sorted(rel["tile_rows"].cpu().numpy(), rel["row_mask"].cpu().numpy().view(np.uint64)[:w.n])
     rows = sample_rows(w.n, 12)
     ref = oracle.conv_fwd(restrict(tr, rows, 1), w.x, w.w, w.n)[rows]
     assert_feature_close(s.y[torch.from_numpy(rows).cuda()], ref, torch.float16, "lidar fwd (fp16 out)")

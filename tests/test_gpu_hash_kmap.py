@@ -9,7 +9,7 @@ import torch
 
 import oracle
 from convolution_voxelised_point_amd import synth
-from helpers import canon, dev
+from helpers import check_window_sorted, canon, dev
 
 pytestmark = pytest.mark.gpu
 
@@ -121,6 +121,11 @@ def test_subm_kmap(ts, case, natural):
     np.testing.assert_array_equal(canon(got), canon(ref))
     rm = check_rel_structure(km, "fwd", c.shape[0], kvol)
     np.testing.assert_array_equal(rm, row_masks_from_triples(ref, c.shape[0], kvol))
+    slots = km.rel_arrays("fwd")["tile_rows"].cpu().numpy()
+    if natural:
+        np.testing.assert_array_equal(slots[:c.shape[0]], np.arange(c.shape[0]))
+    else:
+        check_window_sorted(slots, rm)
     # per-offset pair lists: same triples, output rows ascending within an offset
     ps, pin, pout = km.pairs()
     off = np.repeat(np.arange(kvol), np.diff(ps))
