@@ -3,10 +3,11 @@
 A step is one pass of the whole path over the LiDAR-like ring-scan scene
 (~103k voxels, one batch): coordinate hash build, kernel-map build and the
 SubmConv3d k=3, 64 -> 64 channel fp16 forward (fp32 accumulation).  The
-printed JSON line reports map-valid TFLOP/s of that step (2 * pairs * Cin *
-Cout per step time), the per-stage times taken with HIP events on the launch
-stream, the roofline position of the dominant kernel, and the CPU oracle
-timed on this host.  The other workloads (strided 64 -> 128 downsampling,
+step's launches are captured once in a HIP graph and replayed; the printed
+JSON line reports map-valid TFLOP/s of that step (2 * pairs * Cin * Cout per
+replay time), the per-stage times of eager launches taken with HIP events on
+the launch stream, the roofline position of the dominant kernel, and the CPU
+oracle timed on this host.  The other workloads (strided 64 -> 128 downsampling,
 the 2-D pixel tracks, the bf16 128-channel training step) are measured the
 same way and reported under "secondary".
 
@@ -77,6 +78,8 @@ class Timer:
 
 
 def run_steps(fns, names, steps, warmup):
+    """Eager launches with HIP events between the stages of every step:
+    (wall ms per step, mean us per stage)."""
     for _ in range(warmup):
         for f in fns:
             f()
@@ -89,6 +92,41 @@ def run_steps(fns, names, steps, warmup):
     t1 = time.perf_counter()
     timer.collect()
     return (t1 - t0) * 1e3 / steps, timer.mean_us()
+
+
+def capture(fns):
+    """The launches of one step captured in a HIP graph (the library never
+    synchronises or allocates, so a step replays without host work)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for f in fns:
+            f()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    return g
+
+
+def run_graph(g, steps, warmup):
+    """Replays of a captured step, bracketed by synchronisation: ms per step
+    (wall clock around the K replays, and HIP events on the replay stream)."""
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    return (t1 - t0) * 1e3 / steps, e0.elapsed_time(e1) / steps
 
 
 class Step:
@@ -254,7 +292,8 @@ def setup_train(ts, w) -> Step:
 def measure_lidar(ts, steps, warmup):
     w = synth.make("lidar")
     s = setup_subm(ts, w)
-    ms, st = run_steps(s.fns, s.names, steps, warmup)
+    ms_eager, st = run_steps(s.fns, s.names, steps, warmup)
+    ms, ms_events = run_graph(capture(s.fns), steps, warmup)
     n, cap = s.n, s.table.cap
     P = popcount_sum(s.kmap.rel_arrays("fwd")["row_mask"][:n], 27)
     cin, cout, kvol, e = w.cin, w.cout, 27, 2
@@ -265,7 +304,7 @@ def measure_lidar(ts, steps, warmup):
     conv_s = st["conv"] * 1e-6
     res = {
         "n": n, "pairs": P, "flop_per_step": flop,
-        "ms_per_step": ms,
+        "ms_per_step": ms, "ms_per_step_events": ms_events, "ms_per_step_eager": ms_eager,
         "stages_us": {k: round(v, 3) for k, v in st.items()},
         "fwd_tflops": flop / conv_s / 1e12,
         "fwd_mfma_frac": flop / conv_s / 1e12 / MFMA_F16_PEAK_TFLOPS,
@@ -284,11 +323,13 @@ def measure_lidar(ts, steps, warmup):
 def measure_down(ts, steps, warmup):
     w = synth.make("down")
     s = setup_down(ts, w)
-    ms, st = run_steps(s.fns, s.names, steps, warmup)
+    ms_eager, st = run_steps(s.fns, s.names, steps, warmup)
+    ms, _ = run_graph(capture(s.fns), steps, warmup)
     n_o = int(s.n_out.item())
     P = popcount_sum(s.kmap.rel_arrays("fwd")["row_mask"][:n_o], 8)
     flop = 2.0 * P * w.cin * w.cout
     return {"workload": "down", "n_in": s.n, "n_out": n_o, "pairs": P, "ms_per_step": ms,
+            "ms_per_step_eager": ms_eager,
             "stages_us": {k: round(v, 3) for k, v in st.items()},
             "tflops_step": flop / (ms * 1e-3) / 1e12}
 
@@ -296,13 +337,14 @@ def measure_down(ts, steps, warmup):
 def measure_pixels(ts, steps, warmup):
     w = synth.make("pixels")
     s = setup_pixels(ts, w)
-    ms, st = run_steps(s.fns, s.names, steps, warmup)
+    ms_eager, st = run_steps(s.fns, s.names, steps, warmup)
+    ms, _ = run_graph(capture(s.fns), steps, warmup)
     g = setup_pixels(ts, w, ts.TS_DATAFLOW_GATHER_SCATTER)
     _, st_gs = run_steps(g.fns, g.names, steps, warmup)
     n = s.n
     P = popcount_sum(s.kmap.rel_arrays("fwd")["row_mask"][:n], 9)
     alg = (n * 1 * 2 + n * 8 * 2 + 9 * 8 * 2 + P * 4 + n * 4) + (n * 8 * 2 * 2 + 9 * 64 * 2 + P * 4 + n * 4)
-    return {"workload": "pixels", "n": n, "pairs": P, "ms_per_step": ms,
+    return {"workload": "pixels", "n": n, "pairs": P, "ms_per_step": ms, "ms_per_step_eager": ms_eager,
             "stages_us": {k: round(v, 3) for k, v in st.items()},
             "layers_gather_scatter_us": round(st_gs["layers"], 3),
             "layers_gbs": alg / (st["layers"] * 1e-6) / 1e9}
@@ -311,10 +353,11 @@ def measure_pixels(ts, steps, warmup):
 def measure_train(ts, steps, warmup):
     w = synth.make("train")
     s = setup_train(ts, w)
-    ms, st = run_steps(s.fns, s.names, steps, warmup)
+    ms_eager, st = run_steps(s.fns, s.names, steps, warmup)
+    ms, _ = run_graph(capture(s.fns), steps, warmup)
     P = popcount_sum(s.kmap.rel_arrays("fwd")["row_mask"][:s.n], 27)
     flop = 2.0 * P * 128 * 128
-    return {"workload": "train", "n": s.n, "pairs": P, "ms_per_step": ms,
+    return {"workload": "train", "n": s.n, "pairs": P, "ms_per_step": ms, "ms_per_step_eager": ms_eager,
             "stages_us": {k: round(v, 3) for k, v in st.items()},
             "fwd_tflops": flop / (st["fwd"] * 1e-6) / 1e12,
             "dgrad_tflops": flop / (st["dgrad"] * 1e-6) / 1e12,
@@ -406,6 +449,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": r["ms_per_step"],
+        "ms_per_step_events": r["ms_per_step_events"],
+        "ms_per_step_eager": r["ms_per_step_eager"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
