@@ -46,33 +46,71 @@ struct DirectK {
 };
 
 // 256 threads = 16 tiles x 16 rows; each thread owns 8 destination channels
-// (grid.y walks the 8-channel chunks).
-template <typename T, typename OT>
+// (grid.y walks the 8-channel chunks).  With STAGE, the block first converts
+// the 8-channel weight slice of every offset to fp32 in LDS ([o][ci][8]), so
+// the inner loop reads weights as LDS broadcasts instead of global loads.
+constexpr int kDirectLdsFloats = 12288;  // 48 KiB
+
+template <typename T, typename OT, bool STAGE>
 __global__ __launch_bounds__(256) void k_direct(DirectK a) {
+  extern __shared__ __attribute__((aligned(16))) float wsh[];  // STAGE: kvol * c_src * 8 floats
   const int64_t t = static_cast<int64_t>(blockIdx.x) * 16 + (threadIdx.x >> 4);
   const int r = threadIdx.x & 15;
-  if (t >= a.n_tiles) return;
   const int c0 = blockIdx.y * 8;
-  const uint64_t tm = a.tile_mask[t];
   const T* src = static_cast<const T*>(a.src);
   const T* w = static_cast<const T*>(a.w);
+  const int c_src = a.c_src, kvol = a.kvol;
+  if (STAGE) {
+    const int total = kvol * c_src * 8;
+    for (int i = threadIdx.x; i < total; i += 256) {
+      const int e = i & 7;
+      const int ci = (i >> 3) % c_src;
+      const int o = (i >> 3) / c_src;
+      const int os = a.mirror ? kvol - 1 - o : o;
+      const int c = c0 + e;
+      const T* wo = w + static_cast<int64_t>(os) * a.w_cin * a.w_cout;
+      float v = 0.f;
+      if (c < a.c_dst) v = to_f32(a.transpose ? wo[static_cast<int64_t>(c) * a.w_cout + ci] : wo[static_cast<int64_t>(ci) * a.w_cout + c]);
+      wsh[i] = v;
+    }
+    __syncthreads();
+  }
+  if (t >= a.n_tiles) return;
+  const uint64_t tm = a.tile_mask[t];
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   const int32_t row = a.tile_rows[t * kTile + r];
   for (uint64_t mm = row >= 0 ? tm : 0ull; mm; mm &= mm - 1) {
     const int o = __builtin_ctzll(mm);
-    const int32_t nb = a.nbr[static_cast<int64_t>(row) * a.kvol + o];
+    const int32_t nb = a.nbr[static_cast<int64_t>(row) * kvol + o];
     if (nb < 0) continue;
-    const int os = a.mirror ? a.kvol - 1 - o : o;
-    const T* wo = w + static_cast<int64_t>(os) * a.w_cin * a.w_cout;
-    const T* xs = src + static_cast<int64_t>(nb) * a.c_src;
-    for (int ci = 0; ci < a.c_src; ++ci) {
-      const float xv = to_f32(xs[ci]);
+    const T* xs = src + static_cast<int64_t>(nb) * c_src;
+    if (STAGE) {
+      const float* wo = wsh + o * c_src * 8;
+      for (int ci = 0; ci < c_src; ++ci) {
+        const float xv = to_f32(xs[ci]);
+        const float4 w0 = *reinterpret_cast<const float4*>(wo + ci * 8);
+        const float4 w1 = *reinterpret_cast<const float4*>(wo + ci * 8 + 4);
+        acc[0] = fmaf(xv, w0.x, acc[0]);
+        acc[1] = fmaf(xv, w0.y, acc[1]);
+        acc[2] = fmaf(xv, w0.z, acc[2]);
+        acc[3] = fmaf(xv, w0.w, acc[3]);
+        acc[4] = fmaf(xv, w1.x, acc[4]);
+        acc[5] = fmaf(xv, w1.y, acc[5]);
+        acc[6] = fmaf(xv, w1.z, acc[6]);
+        acc[7] = fmaf(xv, w1.w, acc[7]);
+      }
+    } else {
+      const int os = a.mirror ? kvol - 1 - o : o;
+      const T* wo = w + static_cast<int64_t>(os) * a.w_cin * a.w_cout;
+      for (int ci = 0; ci < c_src; ++ci) {
+        const float xv = to_f32(xs[ci]);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int c = c0 + e;
-        if (c < a.c_dst) {
-          const T wv = a.transpose ? wo[static_cast<int64_t>(c) * a.w_cout + ci] : wo[static_cast<int64_t>(ci) * a.w_cout + c];
-          acc[e] = fmaf(xv, to_f32(wv), acc[e]);
+        for (int e = 0; e < 8; ++e) {
+          const int c = c0 + e;
+          if (c < a.c_dst) {
+            const T wv = a.transpose ? wo[static_cast<int64_t>(c) * a.w_cout + ci] : wo[static_cast<int64_t>(ci) * a.w_cout + c];
+            acc[e] = fmaf(xv, to_f32(wv), acc[e]);
+          }
         }
       }
     }
@@ -86,20 +124,32 @@ __global__ __launch_bounds__(256) void k_direct(DirectK a) {
 
 // ---------------------------------------------------------------- gather-scatter
 // One launch per offset o: thread = (pair, 8-channel chunk).  acc (fp32
-// [n_dest][c_dst]) += src[src_row] . W[o] at dst_row.
-template <typename T>
+// [n_dest][c_dst]) += src[src_row] . W[o] at dst_row.  With STAGE the offset's
+// weights are first converted to fp32 in LDS ([ci][c_dst]) and read from
+// there (broadcasts), instead of once per multiply from global memory.
+template <typename T, bool STAGE>
 __global__ __launch_bounds__(256) void k_gs_offset(const int64_t* __restrict__ pair_start, int o,
                                                    const int32_t* __restrict__ src_rows,
                                                    const int32_t* __restrict__ dst_rows, const T* __restrict__ src,
                                                    int c_src, const T* __restrict__ w, int w_cin, int w_cout,
                                                    bool transpose, float* __restrict__ acc, int c_dst) {
+  extern __shared__ __attribute__((aligned(16))) float wsh[];  // STAGE: c_src * c_dst floats
   const int nchunk = (c_dst + 7) / 8;
+  const T* wo = w + static_cast<int64_t>(o) * w_cin * w_cout;
+  // blocks past this offset's pairs leave before staging (block-uniform)
+  if (pair_start[o] + static_cast<int64_t>(blockIdx.x) * blockDim.x / nchunk >= pair_start[o + 1]) return;
+  if (STAGE) {
+    for (int i = threadIdx.x; i < c_src * c_dst; i += blockDim.x) {
+      const int ci = i / c_dst, c = i % c_dst;
+      wsh[i] = to_f32(transpose ? wo[static_cast<int64_t>(c) * w_cout + ci] : wo[static_cast<int64_t>(ci) * w_cout + c]);
+    }
+    __syncthreads();
+  }
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   const int64_t p = pair_start[o] + i / nchunk;
   if (p >= pair_start[o + 1]) return;
   const int c0 = static_cast<int>(i % nchunk) * 8;
   const T* xs = src + static_cast<int64_t>(src_rows[p]) * c_src;
-  const T* wo = w + static_cast<int64_t>(o) * w_cin * w_cout;
   float sum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int ci = 0; ci < c_src; ++ci) {
     const float xv = to_f32(xs[ci]);
@@ -107,8 +157,10 @@ __global__ __launch_bounds__(256) void k_gs_offset(const int64_t* __restrict__ p
     for (int e = 0; e < 8; ++e) {
       const int c = c0 + e;
       if (c < c_dst) {
-        const T wv = transpose ? wo[static_cast<int64_t>(c) * w_cout + ci] : wo[static_cast<int64_t>(ci) * w_cout + c];
-        sum[e] = fmaf(xv, to_f32(wv), sum[e]);
+        const float wv = STAGE ? wsh[ci * c_dst + c]
+                               : to_f32(transpose ? wo[static_cast<int64_t>(c) * w_cout + ci]
+                                                  : wo[static_cast<int64_t>(ci) * w_cout + c]);
+        sum[e] = fmaf(xv, wv, sum[e]);
       }
     }
   }
@@ -130,7 +182,11 @@ __global__ __launch_bounds__(256) void k_cast_rows(const float* __restrict__ acc
 template <typename T, typename OT>
 hipError_t direct_launch(const DirectK& k, hipStream_t s) {
   dim3 grid(static_cast<unsigned>(ceil_div<int64_t>(k.n_tiles, 16)), static_cast<unsigned>(ceil_div(k.c_dst, 8)));
-  k_direct<T, OT><<<grid, 256, 0, s>>>(k);
+  const int64_t floats = static_cast<int64_t>(k.kvol) * k.c_src * 8;
+  if (floats <= kDirectLdsFloats)
+    k_direct<T, OT, true><<<grid, 256, static_cast<size_t>(floats) * sizeof(float), s>>>(k);
+  else
+    k_direct<T, OT, false><<<grid, 256, 0, s>>>(k);
   return hipGetLastError();
 }
 
@@ -194,9 +250,17 @@ static hipError_t gs_offsets(const ts_kmap* map, const ConvArgs& a, bool backwar
   const unsigned grid = static_cast<unsigned>(ceil_div<int64_t>(threads, 256));
   const int32_t* src_rows = backward ? map->pair_out : map->pair_in;
   const int32_t* dst_rows = backward ? map->pair_in : map->pair_out;
+  const size_t lds = static_cast<size_t>(a.c_src) * a.c_dst * sizeof(float);
+  const bool stage = lds <= 48 * 1024;
   for (int o = 0; o < a.kvol; ++o) {
-    k_gs_offset<T><<<grid, 256, 0, s>>>(map->pair_start, o, src_rows, dst_rows, static_cast<const T*>(a.src), a.c_src,
-                                        static_cast<const T*>(a.w), a.w_cin, a.w_cout, a.transpose, acc, a.c_dst);
+    if (stage)
+      k_gs_offset<T, true><<<grid, 256, lds, s>>>(map->pair_start, o, src_rows, dst_rows, static_cast<const T*>(a.src),
+                                                  a.c_src, static_cast<const T*>(a.w), a.w_cin, a.w_cout, a.transpose,
+                                                  acc, a.c_dst);
+    else
+      k_gs_offset<T, false><<<grid, 256, 0, s>>>(map->pair_start, o, src_rows, dst_rows, static_cast<const T*>(a.src),
+                                                 a.c_src, static_cast<const T*>(a.w), a.w_cin, a.w_cout, a.transpose,
+                                                 acc, a.c_dst);
   }
   return hipGetLastError();
 }

@@ -294,16 +294,21 @@ __global__ __launch_bounds__(256) void k_igemm(IgK a) {
       wload(onx, wr[fill]);
       gather(onx, xs[fill]);
       const u32x4* lw = wl[b];
+      uint64_t mine = 0;
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        Frag af[MB];
+      for (int g = 0; g < G; ++g) mine |= m[g];
+      if ((mine >> oc) & 1) {  // wave-uniform: no fragment reads for a wave without the offset
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) af[mb] = __builtin_bit_cast(Frag, lw[(mb * KB + kb) * 64 + lane]);
+        for (int kb = 0; kb < KB; ++kb) {
+          Frag af[MB];
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-          if (!((m[g] >> oc) & 1)) continue;  // wave-uniform
+          for (int mb = 0; mb < MB; ++mb) af[mb] = __builtin_bit_cast(Frag, lw[(mb * KB + kb) * 64 + lane]);
 #pragma unroll
-          for (int mb = 0; mb < MB; ++mb) acc[g][mb] = Mfma<T>::run(af[mb], xs[cur][g][kb], acc[g][mb]);
+          for (int g = 0; g < G; ++g) {
+            if (!((m[g] >> oc) & 1)) continue;  // wave-uniform
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) acc[g][mb] = Mfma<T>::run(af[mb], xs[cur][g][kb], acc[g][mb]);
+          }
         }
       }
       if (oc == last) return false;

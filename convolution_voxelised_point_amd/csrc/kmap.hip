@@ -20,6 +20,8 @@
 // default, sorted by offset mask inside windows of 4096 rows so that the 16
 // rows of a tile share most offsets and the contraction pads less.  The sort
 // is stable (ties keep row order), so the map is deterministic.
+#include <stdlib.h>
+
 #include "common.h"
 #include "launch.h"
 
@@ -27,8 +29,7 @@ namespace ts {
 
 namespace {
 
-constexpr int kSortWindow = 4096;  // rows sorted together
-constexpr int kSortThreads = 1024;
+constexpr int kSortItems = 4;  // rows per sorting thread
 
 struct RelK {
   const int32_t* dc;
@@ -355,8 +356,6 @@ __global__ __launch_bounds__(256) void k_rel_probe_any(RelK a, int natural) {
 //     destination directly;
 // ties keep their order, so the map is deterministic.
 constexpr int kDigits = 16;
-constexpr int kItems = kSortWindow / kSortThreads;  // 4
-constexpr int kSortWaves = kSortThreads / 64;       // 16
 
 // Lanes whose digit equals d, from the four per-bit ballots.
 __device__ __forceinline__ uint64_t digit_lanes(const uint64_t (&bal)[4], uint32_t d) {
@@ -366,10 +365,14 @@ __device__ __forceinline__ uint64_t digit_lanes(const uint64_t (&bal)[4], uint32
   return m;
 }
 
+template <int kSortThreads>
 __global__ __launch_bounds__(kSortThreads) void k_rel_sort(const uint64_t* __restrict__ row_mask, int64_t n_dest_cap,
                                                            const int64_t* n_dest_p, int nbits, int64_t n_slots,
                                                            int32_t* __restrict__ tile_rows,
                                                            uint64_t* __restrict__ tile_mask) {
+  constexpr int kItems = kSortItems;
+  constexpr int kSortWindow = kSortThreads * kItems;
+  constexpr int kSortWaves = kSortThreads / 64;
   __shared__ uint2 buf[kSortWindow];
   __shared__ int hist[kDigits * kItems * kSortWaves];  // [digit][item][wave] -> exclusive start
   __shared__ int wsum[kSortWaves];
@@ -512,11 +515,33 @@ RelK make_relk(const RelBuild& bld, const ts_rel& rel) {
   return a;
 }
 
+// Rows sorted together: kSortItems * threads.  TS_SORT_THREADS (256, 512 or
+// 1024) overrides the default for tuning.
+static int sort_threads() {
+  static const int v = [] {
+    const char* e = getenv("TS_SORT_THREADS");
+    const int t = e ? atoi(e) : 0;
+    return (t == 256 || t == 512 || t == 1024) ? t : 1024;
+  }();
+  return v;
+}
+
 void launch_sort(const RelK& a, hipStream_t s) {
   const int64_t slots = a.n_tiles * kTile;
   const int nbits = a.kvol < 32 ? a.kvol : 32;
-  k_rel_sort<<<static_cast<unsigned>(ceil_div<int64_t>(slots, kSortWindow)), kSortThreads, 0, s>>>(
-      a.row_mask, a.n_dest_cap, a.n_dest, nbits, slots, a.tile_rows, a.tile_mask);
+  const int th = sort_threads();
+  const unsigned grid = static_cast<unsigned>(ceil_div<int64_t>(slots, static_cast<int64_t>(th) * kSortItems));
+  switch (th) {
+    case 256:
+      k_rel_sort<256><<<grid, 256, 0, s>>>(a.row_mask, a.n_dest_cap, a.n_dest, nbits, slots, a.tile_rows, a.tile_mask);
+      break;
+    case 512:
+      k_rel_sort<512><<<grid, 512, 0, s>>>(a.row_mask, a.n_dest_cap, a.n_dest, nbits, slots, a.tile_rows, a.tile_mask);
+      break;
+    default:
+      k_rel_sort<1024><<<grid, 1024, 0, s>>>(a.row_mask, a.n_dest_cap, a.n_dest, nbits, slots, a.tile_rows, a.tile_mask);
+      break;
+  }
 }
 
 template <int MODE, int ND, int K>
