@@ -163,12 +163,41 @@ struct Seq<N, N> {
   }
 };
 
+// Waits until at most n vector-memory operations of this wave are
+// outstanding (loads retire in issue order); the other counters are left
+// unconstrained.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | 0x70 | 0xF00 | ((N >> 4) << 14));
+}
+// 16 bytes per lane from global memory straight into LDS: lane l writes
+// dst + l (dst is wave-uniform).  Completion is counted by the vector-memory
+// counter.  Kept out of the kernel templates: clang emits no host launch
+// stub for a kernel template whose body names this builtin.
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+__device__ __forceinline__ void lds_copy16(const u32x4* src, lds_u32x4* dst) {
+  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+}
+// All of this wave's LDS reads have returned.
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+// Workgroup barrier with no memory fence: the waits it needs are explicit at
+// each use, so that loads in flight (gathers for later offsets) stay in
+// flight across it.  The empty asm statements keep the compiler from moving
+// memory operations across the barrier.
+__device__ __forceinline__ void bare_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 template <typename T, int MB, int KB, int G, int D>
 __global__ __launch_bounds__(256) void k_igemm(IgK a) {
   typedef typename Mfma<T>::frag Frag;
   constexpr int FR = MB * KB;                      // fragments per offset and block column
   constexpr int CHUNKS = FR * 64;                  // 16-byte chunks per weight slice
-  constexpr int CH = (CHUNKS + 255) / 256;         // per thread
+  constexpr int FW = (FR + 3) / 4;                 // fragments copied per wave (at most)
+  constexpr int GL = G * KB;                       // gather loads per wave and offset
   __shared__ u32x4 wl[2][CHUNKS];
   __shared__ uint64_t wunion[4];
 
@@ -205,6 +234,9 @@ __global__ __launch_bounds__(256) void k_igemm(IgK a) {
   if (lane == 0) wunion[wave] = u;
   __syncthreads();
   const uint64_t U = wunion[0] | wunion[1] | wunion[2] | wunion[3];
+  uint64_t mine = 0;
+#pragma unroll
+  for (int g = 0; g < G; ++g) mine |= m[g];
 
   f32x4 acc[G][MB];
 #pragma unroll
@@ -226,8 +258,8 @@ __global__ __launch_bounds__(256) void k_igemm(IgK a) {
   };
   // Gathers of offset o as buffer loads over the source matrix: a row that is
   // absent (or a tile without the offset) gets an out-of-range offset, which
-  // returns zeros without touching memory, so no select is needed at use and
-  // no cache access is spent on it.
+  // returns zeros without a memory access, so no select is needed at use and
+  // no cache access is spent on it.  Exactly GL loads, always issued.
   const __amdgpu_buffer_rsrc_t xr =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(src), 0, static_cast<int>(a.src_bytes), 0x00020000);
   auto gather = [&](int o, Frag (&x)[G][KB]) {
@@ -241,63 +273,56 @@ __global__ __launch_bounds__(256) void k_igemm(IgK a) {
         x[g][kb] = __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(xr, static_cast<int>(off + kb * 64), 0, 0));
     }
   };
-  // This thread's chunks of the packed slice of offset o.  Chunks of
-  // fragments past the packed column count read the slice start: they land in
-  // fragment rows of output channels that are never written out.
-  auto wload = [&](int o, u32x4 (&r)[CH]) {
-    const int64_t base = (static_cast<int64_t>(o) * a.mbt + mb0) * KB * 64;
-    const int64_t lim = (static_cast<int64_t>(o) * a.mbt + a.mbt) * KB * 64;
+  // Copy of the packed slice of offset o into LDS buffer `buf` by direct
+  // global-to-LDS loads: wave w moves fragments w, w+4, ... (1 KB each, lane
+  // l to chunk l) into buffer bb.  Fragments past the packed column count copy the slice
+  // start: they feed rows of output channels that are never written out.
+  // Wave-uniform; FW loads when the wave has FW fragments, fewer otherwise.
+  auto wcopy = [&](int o, int bb) {
+    const int64_t base = (static_cast<int64_t>(o) * a.mbt + mb0) * KB;
+    const int live = (a.mbt - mb0) * KB;           // fragments of this column inside the packing
 #pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int i = threadIdx.x + c * 256;
-      const int64_t idx = base + (i < CHUNKS ? i : 0);
-      r[c] = a.wp[idx < lim ? idx : base];
-    }
-  };
-  auto wstore = [&](const u32x4 (&r)[CH], u32x4* buf) {
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int i = threadIdx.x + c * 256;
-      if ((c + 1) * 256 <= CHUNKS || i < CHUNKS) buf[i] = r[c];
+    for (int j = 0; j < FW; ++j) {
+      const int f = wave + 4 * j;
+      if (FR % 4 != 0 && f >= FR) break;
+      const u32x4* srcf = a.wp + (base + (f < live ? f : 0)) * 64 + lane;
+      lds_copy16(srcf, (lds_u32x4*)&wl[bb][f * 64]);
     }
   };
 
   if (U) {
-    // Offsets u_0 < u_1 < ... of U; R = D + 1 register sets of gathers and of
-    // weights.  Step i: store W(u_{i+1}) (loaded at step i+1-D) into LDS
-    // buffer (i+1)%2, load W(u_{i+D}) and gather X(u_{i+D}) into set
-    // (i+D)%R, multiply X(u_i) (set i%R) by W(u_i) (buffer i%2), barrier.
-    // Past the last offset the prefetches repeat a valid offset (harmless
-    // loads).  Loads of one step are thus always D steps ahead of their use
-    // and never forced early by the in-order load counter.
+    // Offsets u_0 < u_1 < ... of U.  Weights: two LDS buffers, W(u_j) in
+    // buffer j % 2.  Gathers: R = D + 1 register sets, X(u_j) in set j % R,
+    // issued D steps ahead.  Step i:
+    //   wait for this wave's copy of W(u_i) (only the GL gathers issued after
+    //   it may stay in flight) and for its LDS reads of step i-1; barrier;
+    //   multiply X(u_i) by W(u_i); copy W(u_{i+1}) into buffer (i+1) % 2
+    //   (read at step i-1: every wave is past it); gather X(u_{i+D}).
+    // The copy goes after the fragment reads because the compiler makes any
+    // LDS read wait for every copy into LDS still in flight.  Issue order is
+    // the same in the prologue, so the wait count is the same constant at
+    // every step.  Past the last offset the gathers repeat a valid offset
+    // (harmless loads); no copy is issued past it.
     constexpr int R = D + 1;
     Frag xs[R][G][KB];
-    u32x4 wr[R][CH];
     int oc = __builtin_ctzll(U);  // u_i
-    int onx = oc;                 // u_{i+D} (repeats the last offset past the end)
-    int last = 63 - __builtin_clzll(U);
-    int ow = oc;                  // u_{i+1}
+    const int last = 63 - __builtin_clzll(U);
+    int onx = oc;                 // u_{i+D-1} before a step's gather, then u_{i+D}
 #pragma unroll
-    for (int j = 0; j < D; ++j) {
-      wload(onx, wr[j]);
+    for (int j = 0; j + 1 < D; ++j) {
       gather(onx, xs[j]);
-      if (j + 1 < D) onx = onx < last ? next_bit(U, onx) : onx;
+      onx = onx < last ? next_bit(U, onx) : onx;
     }
-    wstore(wr[0], wl[0]);
-    __syncthreads();
-    ow = oc < last ? next_bit(U, oc) : oc;
+    wcopy(oc, 0);
+    gather(onx, xs[D - 1]);
     auto step = [&](auto ic) -> bool {
       constexpr int i = decltype(ic)::v;
-      constexpr int cur = i % R, nxt = (i + 1) % R, fill = (i + D) % R, b = i % 2;
-      wstore(wr[nxt], wl[b ^ 1]);                 // W(u_{i+1})
-      onx = onx < last ? next_bit(U, onx) : onx;  // u_{i+D}
-      wload(onx, wr[fill]);
-      gather(onx, xs[fill]);
-      const u32x4* lw = wl[b];
-      uint64_t mine = 0;
-#pragma unroll
-      for (int g = 0; g < G; ++g) mine |= m[g];
+      constexpr int cur = i % R, fill = (i + D) % R, b = i % 2;
+      wait_vm<GL>();
+      wait_lds();
+      bare_barrier();
       if ((mine >> oc) & 1) {  // wave-uniform: no fragment reads for a wave without the offset
+        const u32x4* lw = wl[b];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
           Frag af[MB];
@@ -312,13 +337,16 @@ __global__ __launch_bounds__(256) void k_igemm(IgK a) {
         }
       }
       if (oc == last) return false;
-      __syncthreads();
-      oc = ow;
-      ow = ow < last ? next_bit(U, ow) : ow;
+      oc = next_bit(U, oc);
+      asm volatile("" ::: "memory");
+      wcopy(oc, b ^ 1);                           // W(u_{i+1})
+      onx = onx < last ? next_bit(U, onx) : onx;  // u_{i+D}
+      gather(onx, xs[fill]);
       return true;
     };
     while (Seq<0, 2 * R>::go(step)) {
     }
+    wait_vm<0>();  // no copy into LDS may still be in flight when the block ends
   }
 
   // write each destination row once
@@ -350,17 +378,18 @@ __global__ __launch_bounds__(256) void k_igemm(IgK a) {
   }
 }
 
-// Tiles per wave.  Default 1: more blocks in flight and a smaller offset
-// union per block beat sharing a weight slice across more tiles; the
-// environment variable TS_IGEMM_G (1 or 2) overrides it for tuning.
-static int tiles_per_wave(int mb) {
+// Tiles per wave.  Two when a weight slice is at least 32 fragments (e.g.
+// 128x128): each fragment read from LDS then feeds two MFMAs, which halves
+// the LDS reads per row and doubles the math per barrier.  For smaller slices
+// one, which keeps each block's offset union small.  TS_IGEMM_G (1 or 2)
+// overrides it for tuning.
+static int tiles_per_wave(int fr) {
   static const int forced = [] {
     const char* e = getenv("TS_IGEMM_G");
     return e ? atoi(e) : 0;
   }();
-  (void)mb;
   if (forced == 1 || forced == 2) return forced;
-  return 1;
+  return fr >= 32 ? 2 : 1;
 }
 
 // Workgroups are dealt to the 8 XCDs round-robin; numbering blocks so that
@@ -374,12 +403,12 @@ static int xcd_map_on() {
   return on;
 }
 
-// Prefetch depth in offsets: TS_IGEMM_D (2, 3 or 4) overrides the default 2.
+// Gather depth in offsets: TS_IGEMM_D (2 or 3) overrides the default 2.
 static int prefetch_depth() {
   static const int d = [] {
     const char* e = getenv("TS_IGEMM_D");
     const int v = e ? atoi(e) : 0;
-    return (v >= 2 && v <= 4) ? v : 2;
+    return v == 3 ? 3 : 2;
   }();
   return d;
 }
@@ -391,16 +420,15 @@ hipError_t launch_g(IgK k, hipStream_t s) {
   k.xcd_map = xcd_map_on();
   dim3 grid(static_cast<unsigned>(k.xcd_map ? k.nb8 * 8 : k.nblk), static_cast<unsigned>(ceil_div(k.c_dst / 16, MB)));
   switch (prefetch_depth()) {
-    case 2: k_igemm<T, MB, KB, G, 2><<<grid, 256, 0, s>>>(k); break;
-    case 4: k_igemm<T, MB, KB, G, 4><<<grid, 256, 0, s>>>(k); break;
-    default: k_igemm<T, MB, KB, G, 3><<<grid, 256, 0, s>>>(k); break;
+    case 3: k_igemm<T, MB, KB, G, 3><<<grid, 256, 0, s>>>(k); break;
+    default: k_igemm<T, MB, KB, G, 2><<<grid, 256, 0, s>>>(k); break;
   }
   return hipGetLastError();
 }
 
 template <typename T, int MB, int KB>
 hipError_t launch_mb_kb(const IgK& k, hipStream_t s) {
-  switch (tiles_per_wave(MB)) {
+  switch (tiles_per_wave(MB * KB)) {
     case 2: return launch_g<T, MB, KB, 2>(k, s);
     default: return launch_g<T, MB, KB, 1>(k, s);
   }
