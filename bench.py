@@ -142,16 +142,20 @@ class Step:
 
 
 # ---------------------------------------------------------------- workloads
-def setup_subm(ts, w, out_dtype=None) -> Step:
-    """Hash + kernel map (mask-grouped tiles) + SubmConv forward (implicit
-    GEMM when the channel counts allow it)."""
+def setup_subm(ts, w, out_dtype=None, kmap_flags=None) -> Step:
+    """Hash + kernel map + SubmConv forward (implicit GEMM when the channel
+    counts allow it).  The map serves one contraction, so its tiles keep rows
+    in index order (TS_KMAP_NATURAL) unless `kmap_flags` says otherwise: the
+    window sort by offset mask shortens the contraction by less than it costs
+    when the map is used once."""
+    kmap_flags = ts.TS_KMAP_NATURAL if kmap_flags is None else kmap_flags
     dev = torch.device("cuda")
     coords = torch.from_numpy(w.coords).to(dev)
     x, wt = w.x.to(dev), w.w.to(dev)
     n, nd, k = coords.shape[0], w.ndim, w.ksize
     flags = torch.zeros(1, dtype=torch.int32, device=dev)
     table = ts.HashTable(coords, 2.0, build=False)
-    kbuf = torch.empty(ts.ts_kmap_bytes(n, n, nd, k, 1, 0), dtype=torch.uint8, device=dev)
+    kbuf = torch.empty(ts.ts_kmap_bytes(n, n, nd, k, 1, kmap_flags), dtype=torch.uint8, device=dev)
     km = ts.TsKmap()
     y = torch.empty((n, w.cout), dtype=out_dtype or x.dtype, device=dev)
 
@@ -159,7 +163,7 @@ def setup_subm(ts, w, out_dtype=None) -> Step:
         ts.ts_hash_build(coords, table.buf, table.cap, flags)
 
     def kmap_build():
-        ts.ts_kmap_build(coords, table.buf, table.cap, None, n, None, None, 0, nd, k, 1, 0, kbuf, km)
+        ts.ts_kmap_build(coords, table.buf, table.cap, None, n, None, None, 0, nd, k, 1, kmap_flags, kbuf, km)
 
     hash_build()
     kmap_build()
@@ -175,8 +179,10 @@ def setup_subm(ts, w, out_dtype=None) -> Step:
                 kmap=kmap, x=x, w=wt, y=y, flags=flags, n=n, kvol=k ** nd)
 
 
-def setup_down(ts, w) -> Step:
-    """Strided Conv3d (support + kernel map + forward in one call)."""
+def setup_down(ts, w, kmap_flags=0) -> Step:
+    """Strided Conv3d (support + kernel map + forward in one call).  Tiles
+    are grouped by offset mask: with 8 offsets and 64 -> 128 channels the
+    shorter contraction repays the sort even for one use."""
     dev = torch.device("cuda")
     coords = torch.from_numpy(w.coords).to(dev)
     x, wt = w.x.to(dev), w.w.to(dev)
@@ -186,7 +192,7 @@ def setup_down(ts, w) -> Step:
     out = torch.empty_like(coords)
     n_out = torch.zeros(1, dtype=torch.int64, device=dev)
     flags = torch.zeros(1, dtype=torch.int32, device=dev)
-    kb = ts.ts_kmap_bytes(n, n, 3, 2, 2, 0)
+    kb = ts.ts_kmap_bytes(n, n, 3, 2, 2, kmap_flags)
     mbuf = torch.empty(kb + ts.ts_support_scratch_bytes(n), dtype=torch.uint8, device=dev)
     km = ts.TsKmap()
     y = torch.empty((n, w.cout), dtype=torch.float16, device=dev)
@@ -196,7 +202,7 @@ def setup_down(ts, w) -> Step:
         ts.ts_hash_build(coords, table.buf, table.cap, flags)
 
     def conv():
-        ts.ts_conv_fwd_strided(coords, table.buf, table.cap, 2, 2, 0, out, n_out, out_table.buf, out_table.cap, flags,
+        ts.ts_conv_fwd_strided(coords, table.buf, table.cap, 2, 2, kmap_flags, out, n_out, out_table.buf, out_table.cap, flags,
                                mbuf, km, x, wt, y, ts.TS_DATAFLOW_AUTO, ws)
 
     hash_build()
@@ -207,10 +213,12 @@ def setup_down(ts, w) -> Step:
                 out=out, n_out=n_out, kmap=kmap, x=x, w=wt, y=y, flags=flags, n=n, kvol=8)
 
 
-def setup_pixels(ts, w, dataflow=None) -> Step:
+def setup_pixels(ts, w, dataflow=None, kmap_flags=None) -> Step:
     """2-D tracks: hash + kernel map (with pair lists), then the 1 -> 8 and
-    8 -> 8 layers; layer 2 reads layer 1's fp16 output."""
+    8 -> 8 layers; layer 2 reads layer 1's fp16 output.  The direct kernels
+    work row by row, so tiles keep rows in index order by default."""
     dataflow = ts.TS_DATAFLOW_AUTO if dataflow is None else dataflow
+    kmap_flags = (ts.TS_KMAP_PAIRS | ts.TS_KMAP_NATURAL) if kmap_flags is None else kmap_flags
     dev = torch.device("cuda")
     coords = torch.from_numpy(w.coords).to(dev)
     x = w.x.to(dev)
@@ -218,7 +226,7 @@ def setup_pixels(ts, w, dataflow=None) -> Step:
     n = coords.shape[0]
     flags = torch.zeros(1, dtype=torch.int32, device=dev)
     table = ts.HashTable(coords, 2.0, build=False)
-    kbuf = torch.empty(ts.ts_kmap_bytes(n, n, 2, 3, 1, ts.TS_KMAP_PAIRS), dtype=torch.uint8, device=dev)
+    kbuf = torch.empty(ts.ts_kmap_bytes(n, n, 2, 3, 1, kmap_flags), dtype=torch.uint8, device=dev)
     km = ts.TsKmap()
     y1 = torch.empty((n, 8), dtype=torch.float16, device=dev)
     y2 = torch.empty((n, 8), dtype=torch.float16, device=dev)
@@ -228,7 +236,7 @@ def setup_pixels(ts, w, dataflow=None) -> Step:
         ts.ts_hash_build(coords, table.buf, table.cap, flags)
 
     def kmap_build():
-        ts.ts_kmap_build(coords, table.buf, table.cap, None, n, None, None, 0, 2, 3, 1, ts.TS_KMAP_PAIRS, kbuf, km)
+        ts.ts_kmap_build(coords, table.buf, table.cap, None, n, None, None, 0, 2, 3, 1, kmap_flags, kbuf, km)
 
     def layers():
         ts.ts_subm_conv_fwd(km, x, w1, y1, dataflow, ws)

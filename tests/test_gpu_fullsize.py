@@ -53,16 +53,25 @@ def ts_decode(km, kvol):
     return ts.decode_rel(km.rel_arrays("fwd"), kvol)
 
 
-def test_full_lidar_subm_f16(ts):
+@pytest.mark.parametrize("order", ["natural", "sorted"])
+def test_full_lidar_subm_f16(ts, order):
+    """Both tile orders: the benchmark's (rows in index order, the map
+    serving one contraction) and the window sort by offset mask."""
     w = synth.make("lidar")
-    s = bench.setup_subm(ts, w)
+    s = bench.setup_subm(ts, w, kmap_flags=ts.TS_KMAP_NATURAL if order == "natural" else 0)
     s.run_once()
     assert int(s.flags.item()) == 0
     check_hash(ts, s, w.coords, 11)
     tr = oracle.kmap(w.coords, w.coords, 3, 1)
     check_triples(s.kmap, tr, 27, "lidar")
     rel = s.kmap.rel_arrays("fwd")
-    check_window_sorted(rel["tile_rows"].cpu().numpy(), rel["row_mask"].cpu().numpy().view(np.uint64)[:w.n])
+    slots = rel["tile_rows"].cpu().numpy()
+    if order == "natural":
+        want = np.full(slots.shape[0], -1, np.int32)
+        want[:w.n] = np.arange(w.n, dtype=np.int32)
+        assert np.array_equal(slots, want)
+    else:
+        check_window_sorted(slots, rel["row_mask"].cpu().numpy().view(np.uint64)[:w.n])
     rows = sample_rows(w.n, 12)
     ref = oracle.conv_fwd(restrict(tr, rows, 1), w.x, w.w, w.n)[rows]
     assert_feature_close(s.y[torch.from_numpy(rows).cuda()], ref, torch.float16, "lidar fwd (fp16 out)")
@@ -120,6 +129,8 @@ def test_full_train_bf16(ts):
     check_hash(ts, s, w.coords, 41)
     tr = oracle.kmap(w.coords, w.coords, 3, 1)
     check_triples(s.kmap, tr, 27, "train")
+    rel = s.kmap.rel_arrays("fwd")
+    check_window_sorted(rel["tile_rows"].cpu().numpy(), rel["row_mask"].cpu().numpy().view(np.uint64)[:w.n])
     # the per-offset pair lists are the same relation
     ps, pin, pout = s.kmap.pairs()
     off = np.repeat(np.arange(27, dtype=np.int32), np.diff(ps))
