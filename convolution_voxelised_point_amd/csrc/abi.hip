@@ -270,6 +270,7 @@ ts_status ts_conv_fwd(const ts_kmap* map, const void* x, int cin, const void* w,
   const size_t need = conv_ws(map, cin, cout, in_dtype, out_dtype, dataflow, map->n_out_cap, map->n_in);
   if (need > 0 && (!ws || ws_bytes < need)) return TS_ERR_INVALID_ARG;
   ConvArgs a;
+  a.rows_in_order = (map->flags & TS_KMAP_NATURAL) != 0;
   a.rel = &map->fwd;
   a.kvol = map->kvol;
   a.src = x;
@@ -348,6 +349,7 @@ ts_status ts_conv_bwd_dgrad(const ts_kmap* map, const void* dy, int cout, const 
   const size_t need = conv_ws(map, cout, cin, in_dtype, out_dtype, dataflow, map->n_in, map->n_out_cap);
   if (need > 0 && (!ws || ws_bytes < need)) return TS_ERR_INVALID_ARG;
   ConvArgs a;
+  a.rows_in_order = (map->flags & TS_KMAP_NATURAL) != 0;
   a.kvol = map->kvol;
   a.src = dy;
   a.n_src = map->n_out_cap;

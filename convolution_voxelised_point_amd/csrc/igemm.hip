@@ -85,6 +85,7 @@ struct IgK {
   int64_t nblk;  // logical blocks
   int64_t nb8;   // ceil(nblk / 8)
   int xcd_map;   // number blocks so that each XCD walks a contiguous range
+  int in_order;  // tiles keep rows in index order (launch choice only)
 };
 
 // Packed chunk i = ((o * mbt + mb) * kbn + kb) * 64 + lane holds A_o[n][k..k+7]
@@ -380,16 +381,17 @@ __global__ __launch_bounds__(256) void k_igemm(IgK a) {
 
 // Tiles per wave.  Two when a weight slice is at least 32 fragments (e.g.
 // 128x128): each fragment read from LDS then feeds two MFMAs, which halves
-// the LDS reads per row and doubles the math per barrier.  For smaller slices
-// one, which keeps each block's offset union small.  TS_IGEMM_G (1 or 2)
-// overrides it for tuning.
-static int tiles_per_wave(int fr) {
+// the LDS reads per row and doubles the math per barrier.  Two as well when
+// tiles keep rows in index order: a block's offset union then covers nearly
+// every offset whatever its size.  Otherwise one, which keeps the union of a
+// mask-grouped block small.  TS_IGEMM_G (1 or 2) overrides it for tuning.
+static int tiles_per_wave(int fr, int in_order) {
   static const int forced = [] {
     const char* e = getenv("TS_IGEMM_G");
     return e ? atoi(e) : 0;
   }();
   if (forced == 1 || forced == 2) return forced;
-  return fr >= 32 ? 2 : 1;
+  return (fr >= 32 || in_order) ? 2 : 1;
 }
 
 // Workgroups are dealt to the 8 XCDs round-robin; numbering blocks so that
@@ -428,7 +430,7 @@ hipError_t launch_g(IgK k, hipStream_t s) {
 
 template <typename T, int MB, int KB>
 hipError_t launch_mb_kb(const IgK& k, hipStream_t s) {
-  switch (tiles_per_wave(MB * KB)) {
+  switch (tiles_per_wave(MB * KB, k.in_order)) {
     case 2: return launch_g<T, MB, KB, 2>(k, s);
     default: return launch_g<T, MB, KB, 1>(k, s);
   }
@@ -496,6 +498,7 @@ hipError_t launch_igemm(const ConvArgs& a, void* ws, hipStream_t s) {
   k.out_dtype = a.out_dtype;
   k.nblk = 0;
   k.nb8 = 0;
+  k.in_order = a.rows_in_order ? 1 : 0;
   const int64_t chunks = static_cast<int64_t>(a.kvol) * k.mbt * (a.c_src / 32) * 64;
   const unsigned pg = static_cast<unsigned>(ceil_div<int64_t>(chunks, 256));
   if (a.in_dtype == TS_F16) {

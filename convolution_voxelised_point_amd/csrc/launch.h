@@ -68,6 +68,7 @@ struct ConvArgs {
   int w_cin, w_cout;
   bool transpose;     // dgrad: contract over the layer's cout
   bool mirror;        // dgrad of a submanifold map: use W[kvol-1-o]
+  bool rows_in_order; // tiles keep rows in index order (no grouping by mask)
   ts_dtype in_dtype, out_dtype;
 };
 
