@@ -7,7 +7,8 @@
 // Build, in three launches:
 //   1. clear the block keys;
 //   2. each voxel claims the slot of its block (CAS on the block key, linear
-//      probing); the lane that claims a slot resets the block's 64 cells;
+//      probing), unless the previous lane holds a voxel of the same block;
+//      the lane that claims a slot resets the block's 64 cells;
 //   3. each voxel finds its block and atomicMin's its row into its cell, so a
 //      repeated coordinate keeps the lowest row (and raises TS_FLAG_DUP).
 // Cells are written only after every claim has reset its cells (a kernel
@@ -42,16 +43,31 @@ __device__ __forceinline__ int64_t block_claim(const Table& t, uint64_t bkey, ui
   return -1;
 }
 
+// True when the previous lane holds a valid key of the same block: that lane
+// claims (or finds) the block's slot, so this one need not touch it.  Rows in
+// index order are often neighbours in space, so runs of equal block keys are
+// common and most of a run's atomics are saved.  Every lane must call this.
+__device__ __forceinline__ bool same_block_as_prev_lane(uint64_t bkey, bool valid) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t lo = __shfl_up(static_cast<uint32_t>(bkey), 1, 64);
+  const uint32_t hi = __shfl_up(static_cast<uint32_t>(bkey >> 32), 1, 64);
+  const int pv = __shfl_up(valid ? 1 : 0, 1, 64);
+  return valid && lane > 0 && pv && ((static_cast<uint64_t>(hi) << 32) | lo) == bkey;
+}
+
 __global__ __launch_bounds__(256) void k_hash_claim(const int32_t* __restrict__ coords, int64_t n, Table t,
                                                     uint32_t* flags) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i >= n) return;
-  uint64_t key;
-  if (!row_key(coords, i, t.nd, &key)) {
-    if (flags) atomicOr(flags, TS_FLAG_RANGE);
+  uint64_t key = 0;
+  const bool in = i < n;
+  const bool valid = in && row_key(coords, i, t.nd, &key);
+  const uint64_t bkey = block_key(key, t.nd);
+  if (same_block_as_prev_lane(bkey, valid)) return;
+  if (!valid) {
+    if (in && flags) atomicOr(flags, TS_FLAG_RANGE);
     return;
   }
-  block_claim(t, block_key(key, t.nd), flags);
+  block_claim(t, bkey, flags);
 }
 
 __global__ __launch_bounds__(256) void k_hash_cells(const int32_t* __restrict__ coords, int64_t n, Table t,
@@ -118,11 +134,14 @@ __device__ __forceinline__ bool down_key(const int32_t* coords, int64_t i, int n
 __global__ __launch_bounds__(256) void k_down_claim(const int32_t* __restrict__ coords, int64_t n, int stride,
                                                     Table t, uint32_t* flags) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i >= n) return;
-  uint64_t key;
-  if (down_key(coords, i, t.nd, stride, &key)) {
-    block_claim(t, block_key(key, t.nd), flags);
-  } else if (flags) {
+  uint64_t key = 0;
+  const bool in = i < n;
+  const bool valid = in && down_key(coords, i, t.nd, stride, &key);
+  const uint64_t bkey = block_key(key, t.nd);
+  if (same_block_as_prev_lane(bkey, valid)) return;
+  if (valid) {
+    block_claim(t, bkey, flags);
+  } else if (in && flags) {
     atomicOr(flags, TS_FLAG_RANGE);
   }
 }
