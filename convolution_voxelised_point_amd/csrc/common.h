@@ -8,7 +8,7 @@
 
 namespace ts {
 
-constexpr uint64_t kEmptyKey = ~0ull;  // batch 65535 is outside the valid range, so no key equals it
+constexpr uint64_t kEmptyKey = ~0ull;  // key read from an empty slot; batch 65535 is out of range, so no key equals it
 constexpr int kTile = TS_TILE;
 constexpr int kWave = 64;
 
@@ -35,12 +35,18 @@ inline Offsets make_offsets(int ndim, int ksize) {
 // Two-level coordinate table.  Voxels are grouped in blocks (4x4x4 in 3-D,
 // 8x8 in 2-D, 64 cells either way).  An open-addressing table (linear
 // probing) maps a block key to a block slot; each slot owns a dense array of
-// 64 cells holding the row of each voxel of the block (kNoRow when absent).
+// 64 cells holding the row of each voxel of the block (encodings below).
 // The neighbourhood of a voxel then needs a few block lookups and direct
 // cell loads instead of one hashed probe per neighbour.
 //   buffer: keys [cap] u64 | (256-byte aligned) cells [cap][64] int32
 constexpr int kCells = 64;
-constexpr int32_t kNoRow = 0x7fffffff;
+// Stored encodings: a slot holds the bitwise NOT of its block key and a cell
+// the bitwise NOT of its row, so an all-zero buffer is an empty table (no
+// valid key is all ones: batch 65535 is out of range) and, with unsigned
+// atomicMax on cells, the lowest row wins.
+constexpr uint32_t kNoCell = 0;
+__device__ __forceinline__ uint32_t cell_enc(int64_t row) { return ~static_cast<uint32_t>(row); }
+__device__ __forceinline__ int32_t cell_row(uint32_t c) { return c == kNoCell ? -1 : static_cast<int32_t>(~c); }
 
 struct Table {
   uint64_t* keys;
@@ -114,7 +120,7 @@ __device__ __forceinline__ int cell_of(uint64_t key, int nd) {
 __device__ __forceinline__ int64_t block_find(const Table& t, uint64_t bkey) {
   uint64_t slot = hash64(bkey) & t.mask;
   for (uint64_t probe = 0; probe <= t.mask; ++probe) {
-    const uint64_t k = t.keys[slot];
+    const uint64_t k = ~t.keys[slot];
     if (k == bkey) return static_cast<int64_t>(slot);
     if (k == kEmptyKey) return -1;
     slot = (slot + 1) & t.mask;
@@ -126,8 +132,7 @@ __device__ __forceinline__ int64_t block_find(const Table& t, uint64_t bkey) {
 __device__ __forceinline__ int32_t table_find(const Table& t, uint64_t key) {
   const int64_t s = block_find(t, block_key(key, t.nd));
   if (s < 0) return -1;
-  const int32_t r = t.cells[s * kCells + cell_of(key, t.nd)];
-  return r == kNoRow ? -1 : r;
+  return cell_row(static_cast<uint32_t>(t.cells[s * kCells + cell_of(key, t.nd)]));
 }
 
 __device__ __forceinline__ int64_t floor_div(int64_t a, int64_t b) {

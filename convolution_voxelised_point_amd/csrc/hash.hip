@@ -4,39 +4,53 @@
 // "What remains familiar") and says a strided convolution creates a
 // downsampled support (section "Convolution mapping").
 //
-// Build, in three launches:
-//   1. clear the block keys;
-//   2. each voxel claims the slot of its block (CAS on the block key, linear
-//      probing), unless the previous lane holds a voxel of the same block;
-//      the lane that claims a slot resets the block's 64 cells;
-//   3. each voxel finds its block and atomicMin's its row into its cell, so a
-//      repeated coordinate keeps the lowest row (and raises TS_FLAG_DUP).
-// Cells are written only after every claim has reset its cells (a kernel
-// boundary apart), so no reset can overwrite a row.
+// Stored encodings (slots hold NOT key, cells NOT row) make an all-zero
+// buffer an empty table.  A table buffer starts zero-filled and every build
+// returns it to that state before filling it:
+//   1. clear: each slot the previous build occupied gets its 64 cells and its
+//      key zeroed (slots never occupied are zero already);
+//   2. insert: each voxel claims the slot of its block (CAS of the zero key,
+//      linear probing) unless the previous lane holds a voxel of the same
+//      block, in which case it takes that lane's slot; then it atomicMax's
+//      NOT row into its cell, so a repeated coordinate keeps the lowest row
+//      (and raises TS_FLAG_DUP).
+// Cells are zero before any insert starts (a kernel boundary apart), so a
+// claim needs no reset and no insert can be overwritten.
 #include "common.h"
 #include "launch.h"
 
 namespace ts {
 
-__global__ __launch_bounds__(256) void k_table_clear(uint64_t* __restrict__ keys, int64_t cap) {
+// One lane per slot; the wave then zeroes the cells of its occupied slots
+// together, 16 lanes per slot (16 bytes each), four slots per store.
+__global__ __launch_bounds__(256) void k_table_clear(Table t, int64_t cap) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i < cap) keys[i] = kEmptyKey;
+  const int lane = threadIdx.x & 63;
+  const bool occ = i < cap && t.keys[i] != 0;
+  if (occ) t.keys[i] = 0;
+  uint64_t pend = __ballot(occ);  // wave-uniform
+  const int64_t first = i - lane;
+  const int q = lane >> 4, c = lane & 15;
+  const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+  while (pend) {
+    int sl = -1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int b = pend ? __builtin_ctzll(pend) : -1;
+      pend &= pend - 1;
+      sl = (q == j) ? b : sl;
+    }
+    if (sl >= 0) reinterpret_cast<uint4*>(t.cells + (first + sl) * kCells)[c] = z;
+  }
 }
 
-// Slot of block `bkey`, claiming an empty one; the claimer resets the cells.
-// Returns -1 when the table is full.
+// Slot of block `bkey`, claiming an empty one.  Returns -1 when the table is
+// full.
 __device__ __forceinline__ int64_t block_claim(const Table& t, uint64_t bkey, uint32_t* flags) {
   uint64_t slot = hash64(bkey) & t.mask;
   for (uint64_t probe = 0; probe <= t.mask; ++probe) {
-    const uint64_t k = atomicCAS(reinterpret_cast<unsigned long long*>(t.keys + slot), kEmptyKey, bkey);
-    if (k == kEmptyKey) {
-      uint4* c = reinterpret_cast<uint4*>(t.cells + slot * kCells);
-      const uint4 none = make_uint4(kNoRow, kNoRow, kNoRow, kNoRow);
-#pragma unroll
-      for (int i = 0; i < kCells / 4; ++i) c[i] = none;
-      return static_cast<int64_t>(slot);
-    }
-    if (k == bkey) return static_cast<int64_t>(slot);
+    const uint64_t k = atomicCAS(reinterpret_cast<unsigned long long*>(t.keys + slot), 0ull, ~bkey);
+    if (k == 0 || ~k == bkey) return static_cast<int64_t>(slot);
     slot = (slot + 1) & t.mask;
   }
   if (flags) atomicOr(flags, TS_FLAG_FULL);
@@ -55,31 +69,32 @@ __device__ __forceinline__ bool same_block_as_prev_lane(uint64_t bkey, bool vali
   return valid && lane > 0 && pv && ((static_cast<uint64_t>(hi) << 32) | lo) == bkey;
 }
 
-__global__ __launch_bounds__(256) void k_hash_claim(const int32_t* __restrict__ coords, int64_t n, Table t,
-                                                    uint32_t* flags) {
+// Slot of this lane's block: the first lane of a run of equal block keys
+// claims it, the others take it from that lane.  Every lane must call this.
+__device__ __forceinline__ int32_t run_slot(const Table& t, uint64_t bkey, bool valid, uint32_t* flags) {
+  const int lane = threadIdx.x & 63;
+  const bool follow = same_block_as_prev_lane(bkey, valid);
+  const int64_t slot = (valid && !follow) ? block_claim(t, bkey, flags) : -1;
+  const uint64_t heads = __ballot(!follow) & ((2ull << lane) - 1);  // lanes <= this one that start a run
+  const int head = 63 - __builtin_clzll(heads);
+  return __shfl(static_cast<int32_t>(slot), head, 64);
+}
+
+__global__ __launch_bounds__(256) void k_hash_insert(const int32_t* __restrict__ coords, int64_t n, Table t,
+                                                     uint32_t* flags) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   uint64_t key = 0;
   const bool in = i < n;
   const bool valid = in && row_key(coords, i, t.nd, &key);
-  const uint64_t bkey = block_key(key, t.nd);
-  if (same_block_as_prev_lane(bkey, valid)) return;
+  const int32_t s = run_slot(t, block_key(key, t.nd), valid, flags);
   if (!valid) {
     if (in && flags) atomicOr(flags, TS_FLAG_RANGE);
     return;
   }
-  block_claim(t, bkey, flags);
-}
-
-__global__ __launch_bounds__(256) void k_hash_cells(const int32_t* __restrict__ coords, int64_t n, Table t,
-                                                    uint32_t* flags) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i >= n) return;
-  uint64_t key;
-  if (!row_key(coords, i, t.nd, &key)) return;
-  const int64_t s = block_find(t, block_key(key, t.nd));
   if (s < 0) return;  // only when the table was full
-  const int32_t old = atomicMin(t.cells + s * kCells + cell_of(key, t.nd), static_cast<int32_t>(i));
-  if (old != kNoRow && flags) atomicOr(flags, TS_FLAG_DUP);
+  unsigned* cell = reinterpret_cast<unsigned*>(t.cells) + static_cast<int64_t>(s) * kCells + cell_of(key, t.nd);
+  const unsigned old = atomicMax(cell, cell_enc(i));
+  if (old != kNoCell && flags) atomicOr(flags, TS_FLAG_DUP);
 }
 
 __global__ __launch_bounds__(256) void k_hash_query(Table t, const int32_t* __restrict__ q, int64_t m,
@@ -93,12 +108,8 @@ __global__ __launch_bounds__(256) void k_hash_query(Table t, const int32_t* __re
 hipError_t launch_hash_build(const int32_t* coords, int64_t n, int ndim, void* table, int64_t cap, uint32_t* flags,
                              hipStream_t s) {
   Table t = table_view(table, cap, ndim);
-  k_table_clear<<<static_cast<unsigned>(ceil_div<int64_t>(cap, 256)), 256, 0, s>>>(t.keys, cap);
-  if (n > 0) {
-    const unsigned g = static_cast<unsigned>(ceil_div<int64_t>(n, 256));
-    k_hash_claim<<<g, 256, 0, s>>>(coords, n, t, flags);
-    k_hash_cells<<<g, 256, 0, s>>>(coords, n, t, flags);
-  }
+  k_table_clear<<<static_cast<unsigned>(ceil_div<int64_t>(cap, 256)), 256, 0, s>>>(t, cap);
+  if (n > 0) k_hash_insert<<<static_cast<unsigned>(ceil_div<int64_t>(n, 256)), 256, 0, s>>>(coords, n, t, flags);
   return hipGetLastError();
 }
 
@@ -112,13 +123,15 @@ hipError_t launch_hash_query(const void* table, int64_t cap, int ndim, const int
 
 // ---------------------------------------------------------------------------
 // Strided support: unique(floor(c / s)) per batch, in first-occurrence order.
+//   0. the output table is cleared as in a build;
 //   1. every in-range input claims the block of its downsampled key;
-//   2. it atomicMin's its row into the key's cell (the cell keeps the lowest
+//   2. it atomicMax's NOT row into the key's cell (the cell keeps the lowest
 //      input row = the first occurrence) and remembers the cell;
 //   3. an input is "first" when its cell holds its own row;
 //   4. an exclusive scan over the first-flags numbers the outputs;
-//   5. each first input writes its output coordinate and stores its output
-//      row into the cell, so the table then maps coordinate -> output row.
+//   5. each first input writes its output coordinate and stores NOT its
+//      output row into the cell, so the table then maps coordinate -> output
+//      row.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ bool down_key(const int32_t* coords, int64_t i, int ndim, int stride, uint64_t* key) {
   const int32_t* c = coords + i * (ndim + 1);
@@ -156,7 +169,7 @@ __global__ __launch_bounds__(256) void k_down_cells(const int32_t* __restrict__ 
     const int64_t s = block_find(t, block_key(key, t.nd));
     if (s >= 0) {
       at = static_cast<int32_t>(s * kCells + cell_of(key, t.nd));
-      atomicMin(t.cells + at, static_cast<int32_t>(i));
+      atomicMax(reinterpret_cast<unsigned*>(t.cells) + at, cell_enc(i));
     }
   }
   cell_at[i] = at;
@@ -167,7 +180,7 @@ __global__ __launch_bounds__(256) void k_down_flag(const int32_t* __restrict__ c
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i >= n) return;
   const int32_t at = cell_at[i];
-  first[i] = (at >= 0 && t.cells[at] == static_cast<int32_t>(i)) ? 1 : 0;
+  first[i] = (at >= 0 && static_cast<uint32_t>(t.cells[at]) == cell_enc(i)) ? 1 : 0;
 }
 
 __global__ __launch_bounds__(256) void k_down_emit(const int32_t* __restrict__ coords, int64_t n, int ndim,
@@ -182,7 +195,7 @@ __global__ __launch_bounds__(256) void k_down_emit(const int32_t* __restrict__ c
   int32_t* o = out_coords + static_cast<int64_t>(j) * (ndim + 1);
   o[0] = c[0];
   for (int d = 0; d < ndim; ++d) o[1 + d] = static_cast<int32_t>(floor_div(c[1 + d], stride));
-  t.cells[cell_at[i]] = j;
+  t.cells[cell_at[i]] = static_cast<int32_t>(cell_enc(j));
 }
 
 size_t support_scratch_bytes(int64_t n) {
@@ -200,7 +213,7 @@ hipError_t launch_strided_support(const int32_t* coords, int64_t n, int ndim, in
   int32_t* first = reinterpret_cast<int32_t*>(p + a);
   int32_t* index = reinterpret_cast<int32_t*>(p + 2 * a);
   void* tmp = p + 3 * a;
-  k_table_clear<<<static_cast<unsigned>(ceil_div<int64_t>(out_cap, 256)), 256, 0, s>>>(t.keys, out_cap);
+  k_table_clear<<<static_cast<unsigned>(ceil_div<int64_t>(out_cap, 256)), 256, 0, s>>>(t, out_cap);
   if (n == 0) return fill_i64(n_out, 1, 0, s);
   const unsigned g = static_cast<unsigned>(ceil_div<int64_t>(n, 256));
   k_down_claim<<<g, 256, 0, s>>>(coords, n, stride, t, flags);

@@ -163,7 +163,7 @@ __device__ __forceinline__ void probe_fields(const Table& t, uint64_t base, cons
   for (uint64_t round = 0; round <= t.mask && __ballot(pend != 0); ++round) {
     uint64_t k[NC];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) k[c] = t.keys[((pend >> c) & 1) ? slot[c] : 0];
+    for (int c = 0; c < NC; ++c) k[c] = ~t.keys[((pend >> c) & 1) ? slot[c] : 0];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       if (!((pend >> c) & 1)) continue;
@@ -197,7 +197,7 @@ __device__ __forceinline__ void probe_fields(const Table& t, uint64_t base, cons
     r[o] = t.cells[valid ? static_cast<int64_t>(sl) * kCells + cell : 0];
   }
 #pragma unroll
-  for (int o = 0; o < KV; ++o) nb[o] = (ok[o] && r[o] != kNoRow) ? r[o] : -1;
+  for (int o = 0; o < KV; ++o) nb[o] = ok[o] ? cell_row(static_cast<uint32_t>(r[o])) : -1;
 }
 
 // Base fields of destination `row` for the submanifold (c) and downsampling

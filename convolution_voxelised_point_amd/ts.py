@@ -202,6 +202,10 @@ def _bytes(n: int, device) -> torch.Tensor:
     return torch.empty(max(int(n), 1), dtype=torch.uint8, device=device)
 
 
+def _zero_bytes(n: int, device) -> torch.Tensor:
+    return torch.zeros(max(int(n), 1), dtype=torch.uint8, device=device)
+
+
 class HashTable:
     """A coordinate table sized by the reserve ratio."""
 
@@ -209,7 +213,7 @@ class HashTable:
                  build: bool = True, stream=None):
         self.ndim = coords.shape[1] - 1
         self.cap = ts_hash_capacity(coords.shape[0], rsv_ratio)
-        self.buf = _bytes(ts_hash_table_bytes(self.cap), coords.device)
+        self.buf = _zero_bytes(ts_hash_table_bytes(self.cap), coords.device)  # a table starts zero-filled
         if build:
             ts_hash_build(coords, self.buf, self.cap, err_flags, stream)
 

@@ -106,13 +106,19 @@ const char* ts_version(void);
  * >= max(64, ceil(rsv * n)).  Returns -1 for n < 0 or rsv < 1. */
 int64_t ts_hash_capacity(int64_t n, double rsv_ratio);
 
-/* Bytes of a table of `cap` block slots (8 + 256 per slot). */
+/* Bytes of a table of `cap` block slots (8 + 256 per slot).  A table buffer
+ * must be zero-filled before its first build (an all-zero buffer is the
+ * empty table); every build and every strided support then leaves it in a
+ * state the next one clears itself, so one buffer can be rebuilt any number
+ * of times with the same cap.  A buffer holding anything else (or last built
+ * with a larger cap) gives wrong lookups: zero it again first. */
 size_t ts_hash_table_bytes(int64_t cap);
 
 /* Build the table of `n` coordinate rows coords[n][ndim+1] (device int32):
  * key(coords[i]) -> i, the lowest row winning for repeated keys.  `table`
- * (device, ts_hash_table_bytes(cap) bytes) is overwritten; cap must be a
- * power of two >= n.  err_flags (device uint32, may be NULL) receives
+ * (device, ts_hash_table_bytes(cap) bytes, see above) is rebuilt in place:
+ * the slots the previous build used are cleared first; cap must be a power
+ * of two >= n.  err_flags (device uint32, may be NULL) receives
  * TS_FLAG_DUP / TS_FLAG_RANGE / TS_FLAG_FULL. */
 ts_status ts_hash_build(const int32_t* coords, int64_t n, int ndim, void* table, int64_t cap,
                         uint32_t* err_flags, hipStream_t stream);
@@ -129,7 +135,8 @@ ts_status ts_hash_query(const void* table, int64_t cap, int ndim, const int32_t*
  * over the input rows (floor toward -inf), ordered by first occurrence in
  * input row order.  out_coords (device int32, capacity n_in rows) receives
  * them, *n_out (device int64) their count, and out_table (device,
- * ts_hash_table_bytes(out_cap), out_cap a power of two >= n_in) maps each
+ * ts_hash_table_bytes(out_cap), out_cap a power of two >= n_in, zero-filled
+ * before its first use like any table buffer) maps each
  * output coordinate to its output row -- it serves as the input table of a
  * following layer.  `scratch` (device) needs ts_support_scratch_bytes(n_in).
  * ---------------------------------------------------------------------- */

@@ -72,6 +72,29 @@ def test_hash_duplicates_range_and_empty(ts):
     np.testing.assert_array_equal(tab0.query(dev(c[:5])).cpu().numpy(), -np.ones(5, np.int32))
 
 
+def test_hash_rebuild_same_buffer(ts):
+    """A table buffer starts zero-filled and is rebuilt in place: each build
+    clears what the previous one stored, so no stale key or row survives a
+    rebuild with other coordinates, another dimension or a full table."""
+    a = synth.random_coords(21, 3000, 3, 2, 24, lo=-12)
+    b = synth.random_coords(22, 1200, 3, 3, 24, lo=-12)
+    p2 = synth.random_coords(23, 900, 2, 2, 40, lo=-20)
+    cap = ts.ts_hash_capacity(3000, 2.0)
+    buf = torch.zeros(ts.ts_hash_table_bytes(cap), dtype=torch.uint8, device="cuda")
+    flags = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for c in (a, b, p2, a, a[:700]):
+        flags.zero_()
+        ts.ts_hash_build(dev(c), buf, cap, flags)
+        nd = c.shape[1] - 1
+        others = [x for x in (a, b) if x.shape[1] == c.shape[1]] + ([p2] if nd == 2 else [])
+        q = np.concatenate([c] + others + [synth.random_coords(24, 300, nd, 4, 30, lo=-15)], axis=0)
+        got = torch.empty(q.shape[0], dtype=torch.int32, device="cuda")
+        ts.ts_hash_query(buf, cap, dev(q), got)
+        ref, rflags = oracle.hash_query(c, q)
+        np.testing.assert_array_equal(got.cpu().numpy(), ref)
+        assert int(flags.item()) == rflags
+
+
 def test_hash_small_reserve_ratio(ts):
     c = synth.random_coords(8, 2000, 3, 1, 30)
     flags = torch.zeros(1, dtype=torch.int32, device="cuda")
