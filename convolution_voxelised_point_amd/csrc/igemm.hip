@@ -192,15 +192,15 @@ __device__ __forceinline__ void bare_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <typename T, int MB, int KB, int G, int D>
-__global__ __launch_bounds__(256) void k_igemm(IgK a) {
+template <typename T, int MB, int KB, int G, int D, int NW>
+__global__ __launch_bounds__(NW * 64) void k_igemm(IgK a) {
   typedef typename Mfma<T>::frag Frag;
   constexpr int FR = MB * KB;                      // fragments per offset and block column
   constexpr int CHUNKS = FR * 64;                  // 16-byte chunks per weight slice
-  constexpr int FW = (FR + 3) / 4;                 // fragments copied per wave (at most)
+  constexpr int FW = (FR + NW - 1) / NW;           // fragments copied per wave (at most)
   constexpr int GL = G * KB;                       // gather loads per wave and offset
   __shared__ u32x4 wl[2][CHUNKS];
-  __shared__ uint64_t wunion[4];
+  __shared__ uint64_t wunion[NW];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -210,7 +210,7 @@ __global__ __launch_bounds__(256) void k_igemm(IgK a) {
   const int64_t lb = a.xcd_map ? (hb & 7) * a.nb8 + (hb >> 3) : hb;  // XCD-contiguous numbering
   if (lb >= a.nblk) return;                        // whole block, before any barrier
   const int mb0 = blockIdx.y * MB;
-  const int64_t t0 = (lb * 4 + wave) * G;
+  const int64_t t0 = (lb * NW + wave) * G;
   const int kvol = a.kvol;
 
   // masks, destination rows and their neighbours (first loads of the kernel)
@@ -234,7 +234,9 @@ __global__ __launch_bounds__(256) void k_igemm(IgK a) {
   }
   if (lane == 0) wunion[wave] = u;
   __syncthreads();
-  const uint64_t U = wunion[0] | wunion[1] | wunion[2] | wunion[3];
+  uint64_t U = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) U |= wunion[w];
   uint64_t mine = 0;
 #pragma unroll
   for (int g = 0; g < G; ++g) mine |= m[g];
@@ -275,7 +277,7 @@ __global__ __launch_bounds__(256) void k_igemm(IgK a) {
     }
   };
   // Copy of the packed slice of offset o into LDS buffer `buf` by direct
-  // global-to-LDS loads: wave w moves fragments w, w+4, ... (1 KB each, lane
+  // global-to-LDS loads: wave w moves fragments w, w+NW, ... (1 KB each, lane
   // l to chunk l) into buffer bb.  Fragments past the packed column count copy the slice
   // start: they feed rows of output channels that are never written out.
   // Wave-uniform; FW loads when the wave has FW fragments, fewer otherwise.
@@ -284,8 +286,8 @@ __global__ __launch_bounds__(256) void k_igemm(IgK a) {
     const int live = (a.mbt - mb0) * KB;           // fragments of this column inside the packing
 #pragma unroll
     for (int j = 0; j < FW; ++j) {
-      const int f = wave + 4 * j;
-      if (FR % 4 != 0 && f >= FR) break;
+      const int f = wave + NW * j;
+      if (FR % NW != 0 && f >= FR) break;
       const u32x4* srcf = a.wp + (base + (f < live ? f : 0)) * 64 + lane;
       lds_copy16(srcf, (lds_u32x4*)&wl[bb][f * 64]);
     }
@@ -405,27 +407,34 @@ static int xcd_map_on() {
   return on;
 }
 
-// Gather depth in offsets: TS_IGEMM_D (2 or 3) overrides the default 2.
-static int prefetch_depth() {
-  static const int d = [] {
-    const char* e = getenv("TS_IGEMM_D");
+// Waves per block: 4, or 8 when tiles keep rows in index order (every block
+// then walks nearly all offsets whatever its size, so a larger block only
+// shares each weight copy among more rows).  TS_IGEMM_NW (4 or 8) overrides
+// it for tuning.
+static int waves_per_block(int in_order) {
+  static const int forced = [] {
+    const char* e = getenv("TS_IGEMM_NW");
     const int v = e ? atoi(e) : 0;
-    return v == 3 ? 3 : 2;
+    return (v == 4 || v == 8) ? v : 0;
   }();
-  return d;
+  if (forced) return forced;
+  return in_order ? 8 : 4;
+}
+
+template <typename T, int MB, int KB, int G, int NW>
+hipError_t launch_gw(IgK k, hipStream_t s) {
+  k.nblk = ceil_div<int64_t>(k.n_tiles, NW * G);
+  k.nb8 = ceil_div<int64_t>(k.nblk, 8);
+  k.xcd_map = xcd_map_on();
+  dim3 grid(static_cast<unsigned>(k.xcd_map ? k.nb8 * 8 : k.nblk), static_cast<unsigned>(ceil_div(k.c_dst / 16, MB)));
+  k_igemm<T, MB, KB, G, 2, NW><<<grid, NW * 64, 0, s>>>(k);
+  return hipGetLastError();
 }
 
 template <typename T, int MB, int KB, int G>
 hipError_t launch_g(IgK k, hipStream_t s) {
-  k.nblk = ceil_div<int64_t>(k.n_tiles, 4 * G);
-  k.nb8 = ceil_div<int64_t>(k.nblk, 8);
-  k.xcd_map = xcd_map_on();
-  dim3 grid(static_cast<unsigned>(k.xcd_map ? k.nb8 * 8 : k.nblk), static_cast<unsigned>(ceil_div(k.c_dst / 16, MB)));
-  switch (prefetch_depth()) {
-    case 3: k_igemm<T, MB, KB, G, 3><<<grid, 256, 0, s>>>(k); break;
-    default: k_igemm<T, MB, KB, G, 2><<<grid, 256, 0, s>>>(k); break;
-  }
-  return hipGetLastError();
+  if (waves_per_block(k.in_order) == 8) return launch_gw<T, MB, KB, G, 8>(k, s);
+  return launch_gw<T, MB, KB, G, 4>(k, s);
 }
 
 template <typename T, int MB, int KB>
