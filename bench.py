@@ -214,11 +214,15 @@ def setup_down(ts, w, kmap_flags=0) -> Step:
 
 
 def setup_pixels(ts, w, dataflow=None, kmap_flags=None) -> Step:
-    """2-D tracks: hash + kernel map (with pair lists), then the 1 -> 8 and
-    8 -> 8 layers; layer 2 reads layer 1's fp16 output.  The direct kernels
-    work row by row, so tiles keep rows in index order by default."""
+    """2-D tracks: hash + kernel map, then the 1 -> 8 and 8 -> 8 layers;
+    layer 2 reads layer 1's fp16 output.  The direct kernels work row by row,
+    so tiles keep rows in index order by default; per-offset pair lists are
+    built only for the gather-scatter dataflow, the one that reads them."""
     dataflow = ts.TS_DATAFLOW_AUTO if dataflow is None else dataflow
-    kmap_flags = (ts.TS_KMAP_PAIRS | ts.TS_KMAP_NATURAL) if kmap_flags is None else kmap_flags
+    if kmap_flags is None:
+        kmap_flags = ts.TS_KMAP_NATURAL
+        if dataflow == ts.TS_DATAFLOW_GATHER_SCATTER:
+            kmap_flags |= ts.TS_KMAP_PAIRS
     dev = torch.device("cuda")
     coords = torch.from_numpy(w.coords).to(dev)
     x = w.x.to(dev)
