@@ -47,7 +47,7 @@ __global__ __launch_bounds__(256) void k_table_clear(Table t, int64_t cap) {
 // Slot of block `bkey`, claiming an empty one.  Returns -1 when the table is
 // full.
 __device__ __forceinline__ int64_t block_claim(const Table& t, uint64_t bkey, uint32_t* flags) {
-  uint64_t slot = hash64(bkey) & t.mask;
+  uint64_t slot = first_slot(t, bkey);
   for (uint64_t probe = 0; probe <= t.mask; ++probe) {
     const uint64_t k = atomicCAS(reinterpret_cast<unsigned long long*>(t.keys + slot), 0ull, ~bkey);
     if (k == 0 || ~k == bkey) return static_cast<int64_t>(slot);

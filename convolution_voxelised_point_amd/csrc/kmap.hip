@@ -157,23 +157,39 @@ __device__ __forceinline__ void probe_fields(const Table& t, uint64_t base, cons
     const uint64_t b1 = (c & 2) ? hi[1] : lo[1];
     const uint64_t b2 = ND == 3 ? static_cast<uint64_t>((c & 4) ? hi[2] : lo[2]) : static_cast<uint64_t>(f[2]);
     bk[c] = (b << 48) | (b0 << 32) | (b1 << 16) | b2;
-    slot[c] = static_cast<uint32_t>(hash64(bk[c]) & t.mask);
+    slot[c] = static_cast<uint32_t>(first_slot(t, bk[c]));
     found[c] = -1;
   }
+  // each round reads the aligned group of kSlotGroup slots at every pending
+  // corner's probe position and resolves the first slot that holds the key
+  // or is empty
   for (uint64_t round = 0; round <= t.mask && __ballot(pend != 0); ++round) {
-    uint64_t k[NC];
+    uint4 g[NC][2];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) k[c] = ~t.keys[((pend >> c) & 1) ? slot[c] : 0];
+    for (int c = 0; c < NC; ++c) {
+      const uint4* p = reinterpret_cast<const uint4*>(t.keys + (((pend >> c) & 1) ? slot[c] : 0));
+      g[c][0] = p[0];
+      g[c][1] = p[1];
+    }
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       if (!((pend >> c) & 1)) continue;
-      if (k[c] == bk[c]) {
-        found[c] = static_cast<int32_t>(slot[c]);
-        pend &= ~(1u << c);
-      } else if (k[c] == kEmptyKey) {
+      const uint64_t k4[4] = {~((static_cast<uint64_t>(g[c][0].y) << 32) | g[c][0].x),
+                              ~((static_cast<uint64_t>(g[c][0].w) << 32) | g[c][0].z),
+                              ~((static_cast<uint64_t>(g[c][1].y) << 32) | g[c][1].x),
+                              ~((static_cast<uint64_t>(g[c][1].w) << 32) | g[c][1].z)};
+      int hit = -1;
+      bool stop = false;
+#pragma unroll
+      for (int j = 3; j >= 0; --j) {  // first position that holds the key or is empty
+        if (k4[j] == bk[c]) { hit = j; stop = true; }
+        else if (k4[j] == kEmptyKey) { hit = -1; stop = true; }
+      }
+      if (stop) {
+        if (hit >= 0) found[c] = static_cast<int32_t>(slot[c] + hit);
         pend &= ~(1u << c);
       } else {
-        slot[c] = static_cast<uint32_t>((slot[c] + 1) & t.mask);
+        slot[c] = static_cast<uint32_t>((slot[c] + kSlotGroup) & t.mask);
       }
     }
   }
