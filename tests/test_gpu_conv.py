@@ -14,16 +14,19 @@ pytestmark = pytest.mark.gpu
 DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 
 
-def make_problem(coords, ksize, stride, cin, cout, dtype, seed):
-    """Device tensors, the GPU map and the oracle's triples for one layer."""
+def make_problem(coords, ksize, stride, cin, cout, dtype, seed, natural=False):
+    """Device tensors, the GPU map and the oracle's triples for one layer;
+    `natural` keeps tile rows in index order instead of grouping them by
+    offset mask."""
     from convolution_voxelised_point_amd import ts
     ndim = coords.shape[1] - 1
     kvol = ksize ** ndim
     cd = dev(coords)
     tab = ts.HashTable(cd, 2.0)
-    flags = ts.TS_KMAP_PAIRS | ts.TS_KMAP_BWD
+    order = ts.TS_KMAP_NATURAL if natural else 0
+    flags = ts.TS_KMAP_PAIRS | ts.TS_KMAP_BWD | order
     if stride == 1:
-        km = ts.build_kmap(cd, tab, ksize, 1, ts.TS_KMAP_PAIRS)
+        km = ts.build_kmap(cd, tab, ksize, 1, ts.TS_KMAP_PAIRS | order)
         oc = coords
     else:
         out, n_out, otab = ts.strided_support(cd, stride)
@@ -90,6 +93,25 @@ def test_wgrad(ts, case):
     dyd[:oc.shape[0]] = dev(dy)
     dw = ts.conv_wgrad(km, dev(x), dyd)
     assert_feature_close(dw, ref, DT[dt], f"{name} wgrad")
+
+
+IGEMM_CASES = [c for c in CONV_CASES if c[6] != "f32" and c[4] % 32 == 0 and c[5] % 16 == 0]
+
+
+@pytest.mark.parametrize("case", IGEMM_CASES, ids=[c[0] for c in IGEMM_CASES])
+def test_row_ordered_map(ts, case):
+    """Forward and dgrad on a map whose tiles keep rows in index order (the
+    implicit GEMM then takes more tiles per wavefront and per block)."""
+    name, c, k, s, cin, cout, dt = case
+    km, tr, oc, x, w, dy = make_problem(c, k, s, cin, cout, dt, 550, natural=True)
+    ref = oracle.conv_fwd(tr, x, w, oc.shape[0])
+    y = ts.conv_fwd(km, dev(x), dev(w), out_dtype=torch.float32)
+    assert_feature_close(y[:oc.shape[0]], ref, DT[dt], f"{name} fwd (row order)")
+    ref = oracle.conv_dgrad(tr, dy, w, c.shape[0])
+    dyd = torch.zeros((c.shape[0] if s == 1 else km.s.n_out_cap, cout), dtype=DT[dt], device="cuda")
+    dyd[:oc.shape[0]] = dev(dy)
+    dx = ts.conv_dgrad(km, dyd, dev(w), out_dtype=DT[dt])
+    assert_feature_close(dx, ref, DT[dt], f"{name} dgrad (row order)")
 
 
 def test_bitwise_repeatable(ts):
