@@ -480,32 +480,42 @@ __global__ __launch_bounds__(256) void k_pairs_count(const uint64_t* __restrict_
   }
 }
 
-__global__ void k_pairs_start(const int32_t* __restrict__ base, int kvol, int64_t nblk, const int64_t* total,
-                              int64_t* __restrict__ pair_start) {
-  const int o = threadIdx.x;
-  if (o < kvol) pair_start[o] = base[o * nblk];
-  if (o == kvol) pair_start[kvol] = *total;
-}
-
+// Writes the pairs of a block of 256 destination rows.  The write position
+// of each (wavefront, offset) -- the block's scanned base plus the counts of
+// the wavefronts before it -- is computed once into LDS.  Block 0 also
+// writes pair_start.
 __global__ __launch_bounds__(256) void k_pairs_fill(RelK a, int64_t nblk, const int32_t* __restrict__ base,
+                                                    const int64_t* total, int64_t* __restrict__ pair_start,
                                                     int32_t* __restrict__ pair_in, int32_t* __restrict__ pair_out) {
-  __shared__ int wave_cnt[4][TS_MAX_KVOL];
+  __shared__ int wave_pos[4][TS_MAX_KVOL];
   const int64_t n_dest = dest_count(a.n_dest, a.n_dest_cap);
   const int64_t row = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   const uint64_t mask = row < n_dest ? a.row_mask[row] : 0;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const uint64_t below = (1ull << lane) - 1;
+  if (blockIdx.x == 0 && threadIdx.x <= a.kvol)
+    pair_start[threadIdx.x] = threadIdx.x < a.kvol ? base[threadIdx.x * nblk] : *total;
   for (int o = 0; o < a.kvol; ++o) {
     const uint64_t bal = __ballot((mask >> o) & 1);
-    if (lane == 0) wave_cnt[wave][o] = __popcll(bal);
+    if (lane == 0) wave_pos[wave][o] = __popcll(bal);
+  }
+  __syncthreads();
+  if (threadIdx.x < a.kvol) {  // counts -> exclusive positions, per offset
+    const int o = threadIdx.x;
+    int p = base[o * nblk + blockIdx.x];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int c = wave_pos[w][o];
+      wave_pos[w][o] = p;
+      p += c;
+    }
   }
   __syncthreads();
   for (int o = 0; o < a.kvol; ++o) {
     const bool has = (mask >> o) & 1;
     const uint64_t bal = __ballot(has);  // every lane takes part
     if (!has) continue;
-    int pos = base[o * nblk + blockIdx.x] + __popcll(bal & below);
-    for (int w = 0; w < wave; ++w) pos += wave_cnt[w][o];
+    const int pos = wave_pos[wave][o] + __popcll(bal & below);
     pair_out[pos] = static_cast<int32_t>(row);
     pair_in[pos] = a.nbr[row * a.kvol + o];
   }
@@ -619,9 +629,9 @@ hipError_t launch_pairs_build(const RelBuild& bld, const ts_rel& rel, int64_t* p
                                                               nblk, cnt);
   hipError_t e = scan_exclusive_i32(cnt, cnt, n, pair_start + bld.kvol, tmp, s);
   if (e != hipSuccess) return e;
-  k_pairs_start<<<1, 128, 0, s>>>(cnt, bld.kvol, nblk, pair_start + bld.kvol, pair_start);
   RelK a = make_relk(bld, rel);
-  k_pairs_fill<<<static_cast<unsigned>(nblk), 256, 0, s>>>(a, nblk, cnt, pair_in, pair_out);
+  k_pairs_fill<<<static_cast<unsigned>(nblk), 256, 0, s>>>(a, nblk, cnt, pair_start + bld.kvol, pair_start, pair_in,
+                                                             pair_out);
   return hipGetLastError();
 }
 

@@ -1,7 +1,8 @@
 // Device-wide exclusive prefix sum of int32 counts and small fill kernels.
-// Blocks of 256 threads scan 2048 items each; a single block then scans the
-// per-block sums (any count, in chunks of 2048 with a running carry) and a
-// last pass adds each block's prefix.
+// Blocks of 256 threads scan 2048 items each.  Up to kMaxDirect blocks, a
+// second pass lets every block sum the block totals before it (one wave) and
+// add that prefix; beyond that a single block first scans the per-block sums
+// (in chunks of 2048 with a running carry).
 #include "common.h"
 #include "launch.h"
 
@@ -83,6 +84,30 @@ __global__ __launch_bounds__(kThreads) void k_scan_add(int32_t* out, int64_t n, 
     if (first + i < n) out[first + i] += add;
 }
 
+// Adds to block b's items the sum of the totals of blocks 0..b-1, summed by
+// the first wave; the last block also writes the grand total.
+constexpr int64_t kMaxDirect = 4096;
+__global__ __launch_bounds__(kThreads) void k_scan_add_direct(int32_t* out, int64_t n, const int32_t* sums,
+                                                              int64_t nb, int64_t* total) {
+  __shared__ int pre;
+  const int64_t b = blockIdx.x;
+  if (threadIdx.x < 64) {
+    int v = 0;
+    for (int64_t i = threadIdx.x; i < b; i += 64) v += sums[i];
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    if (threadIdx.x == 0) {
+      pre = v;
+      if (total && b == nb - 1) *total = static_cast<int64_t>(v) + sums[b];
+    }
+  }
+  __syncthreads();
+  const int add = pre;
+  const int64_t first = b * kPerBlock;
+  for (int i = threadIdx.x; i < kPerBlock; i += kThreads)
+    if (first + i < n) out[first + i] += add;
+}
+
 __global__ __launch_bounds__(256) void k_fill_i64(int64_t* p, int64_t n, int64_t v) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;
@@ -116,6 +141,10 @@ hipError_t scan_exclusive_i32(const int32_t* in, int32_t* out, int64_t n, int64_
   }
   int32_t* sums = static_cast<int32_t*>(tmp);
   k_scan_local<<<static_cast<unsigned>(nb), kThreads, 0, s>>>(in, out, n, sums, nullptr);
+  if (nb <= kMaxDirect) {
+    k_scan_add_direct<<<static_cast<unsigned>(nb), kThreads, 0, s>>>(out, n, sums, nb, total);
+    return hipGetLastError();
+  }
   k_scan_sums<<<1, kThreads, 0, s>>>(sums, nb, total);
   k_scan_add<<<static_cast<unsigned>(nb), kThreads, 0, s>>>(out, n, sums);
   return hipGetLastError();
