@@ -124,9 +124,11 @@ hipError_t launch_hash_query(const void* table, int64_t cap, int ndim, const int
 // ---------------------------------------------------------------------------
 // Strided support: unique(floor(c / s)) per batch, in first-occurrence order.
 //   0. the output table is cleared as in a build;
-//   1. every in-range input claims the block of its downsampled key;
+//   1. every in-range input claims (or shares) the block of its downsampled
+//      key;
 //   2. it atomicMax's NOT row into the key's cell (the cell keeps the lowest
-//      input row = the first occurrence) and remembers the cell;
+//      input row = the first occurrence) and remembers the cell (steps 1-2
+//      are one kernel);
 //   3. an input is "first" when its cell holds its own row;
 //   4. an exclusive scan over the first-flags numbers the outputs;
 //   5. each first input writes its output coordinate and stores NOT its
@@ -144,33 +146,24 @@ __device__ __forceinline__ bool down_key(const int32_t* coords, int64_t i, int n
   return make_key(ndim, c[0], q, key);
 }
 
-__global__ __launch_bounds__(256) void k_down_claim(const int32_t* __restrict__ coords, int64_t n, int stride,
-                                                    Table t, uint32_t* flags) {
+// Steps 1-2 in one pass (the table's cells are zero before it starts): the
+// first lane of a run of equal block keys claims the slot, the run shares
+// it, and each input atomicMax's NOT its row into its cell and remembers the
+// cell.
+__global__ __launch_bounds__(256) void k_down_insert(const int32_t* __restrict__ coords, int64_t n, int stride,
+                                                     Table t, uint32_t* flags, int32_t* __restrict__ cell_at) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   uint64_t key = 0;
   const bool in = i < n;
   const bool valid = in && down_key(coords, i, t.nd, stride, &key);
-  const uint64_t bkey = block_key(key, t.nd);
-  if (same_block_as_prev_lane(bkey, valid)) return;
-  if (valid) {
-    block_claim(t, bkey, flags);
-  } else if (in && flags) {
-    atomicOr(flags, TS_FLAG_RANGE);
-  }
-}
-
-__global__ __launch_bounds__(256) void k_down_cells(const int32_t* __restrict__ coords, int64_t n, int stride,
-                                                    Table t, int32_t* __restrict__ cell_at) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i >= n) return;
-  uint64_t key;
+  const int32_t sl = run_slot(t, block_key(key, t.nd), valid, flags);
+  if (!in) return;
   int32_t at = -1;
-  if (down_key(coords, i, t.nd, stride, &key)) {
-    const int64_t s = block_find(t, block_key(key, t.nd));
-    if (s >= 0) {
-      at = static_cast<int32_t>(s * kCells + cell_of(key, t.nd));
-      atomicMax(reinterpret_cast<unsigned*>(t.cells) + at, cell_enc(i));
-    }
+  if (!valid) {
+    if (flags) atomicOr(flags, TS_FLAG_RANGE);
+  } else if (sl >= 0) {
+    at = sl * kCells + cell_of(key, t.nd);
+    atomicMax(reinterpret_cast<unsigned*>(t.cells) + at, cell_enc(i));
   }
   cell_at[i] = at;
 }
@@ -216,8 +209,7 @@ hipError_t launch_strided_support(const int32_t* coords, int64_t n, int ndim, in
   k_table_clear<<<static_cast<unsigned>(ceil_div<int64_t>(out_cap, 256)), 256, 0, s>>>(t, out_cap);
   if (n == 0) return fill_i64(n_out, 1, 0, s);
   const unsigned g = static_cast<unsigned>(ceil_div<int64_t>(n, 256));
-  k_down_claim<<<g, 256, 0, s>>>(coords, n, stride, t, flags);
-  k_down_cells<<<g, 256, 0, s>>>(coords, n, stride, t, cell_at);
+  k_down_insert<<<g, 256, 0, s>>>(coords, n, stride, t, flags, cell_at);
   k_down_flag<<<g, 256, 0, s>>>(cell_at, n, t, first);
   hipError_t e = scan_exclusive_i32(first, index, n, n_out, tmp, s);
   if (e != hipSuccess) return e;
