@@ -89,7 +89,7 @@ struct WIc {
 };
 
 template <typename T, int TW>
-__global__ __launch_bounds__(256) void k_wgrad_mfma(const int32_t* __restrict__ chunk_base,
+__global__ __launch_bounds__(256, 2) void k_wgrad_mfma(const int32_t* __restrict__ chunk_base,
                                                     const int64_t* __restrict__ pair_start, int kvol,
                                                     const int32_t* __restrict__ pair_in,
                                                     const int32_t* __restrict__ pair_out, const T* __restrict__ x,
@@ -150,11 +150,10 @@ __global__ __launch_bounds__(256) void k_wgrad_mfma(const int32_t* __restrict__ 
     }
   };
   // 8 x 8 transpose of 16-bit values: out row e = channel ch+e over the 8 pairs
-  auto stage = [&](int st, const u32x4 (&v)[8], T* buf) {
+  auto stage = [&](int st, u32x4 (&in)[8], T* buf) {
     if (!stager) return;
-    u32x4 in[8];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) in[r] = valid(st, r) ? v[r] : u32x4{0u, 0u, 0u, 0u};
+    for (int r = 0; r < 8; ++r) in[r] = valid(st, r) ? in[r] : u32x4{0u, 0u, 0u, 0u};  // in place
     T* base = buf + (op ? TW * kWStride : 0);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -188,22 +187,24 @@ __global__ __launch_bounds__(256) void k_wgrad_mfma(const int32_t* __restrict__ 
     }
   };
 
-  // prologue: indices of steps 0..2, rows of steps 0..1, slab of step 0
-  int32_t id[4][8];
+  // prologue: indices of steps 0..2, rows of steps 0..1, slab of step 0.
+  // Index sets alternate: the set of step s+3 is loaded at step s into the
+  // one whose rows (step s+1) were issued at step s-1.
+  int32_t id[2][8];
   u32x4 rv[2][8];
   load_idx(0, id[0]);
   load_idx(1, id[1]);
-  load_idx(2, id[2]);
   load_rows(0, id[0], rv[0]);
   load_rows(1, id[1], rv[1]);
+  load_idx(2, id[0]);
   stage(0, rv[0], &slab[0][0][0]);
   __syncthreads();
   int s = 0;
   // step s: indices of s+3, rows of s+2, multiplies of s, staging of s+1
   auto step = [&](auto ic) -> bool {
     constexpr int i = decltype(ic)::v;
-    load_idx(s + 3, id[(i + 3) & 3]);
-    load_rows(s + 2, id[(i + 2) & 3], rv[i & 1]);
+    load_idx(s + 3, id[(i + 3) & 1]);
+    load_rows(s + 2, id[(i + 2) & 1], rv[i & 1]);
     mma(&slab[i & 1][0][0]);
     if (++s >= nsteps) return false;
     stage(s, rv[(i + 1) & 1], &slab[(i + 1) & 1][0][0]);
