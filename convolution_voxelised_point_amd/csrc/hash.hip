@@ -46,12 +46,28 @@ __global__ __launch_bounds__(256) void k_table_clear(Table t, int64_t cap) {
 
 // Slot of block `bkey`, claiming an empty one.  Returns -1 when the table is
 // full.
+// Each round reads the aligned group of kSlotGroup slots with a plain load
+// and takes the first slot that holds the key or is empty, with a CAS only
+// on an empty one; a CAS lost to another key moves on to the next slot.  So
+// a key still lands in the first empty slot of its probe order, and most
+// claims cost one atomic instead of one per occupied slot passed (keys that
+// share a group start there, so first-slot CASes collide often).
 __device__ __forceinline__ int64_t block_claim(const Table& t, uint64_t bkey, uint32_t* flags) {
-  uint64_t slot = first_slot(t, bkey);
-  for (uint64_t probe = 0; probe <= t.mask; ++probe) {
-    const uint64_t k = atomicCAS(reinterpret_cast<unsigned long long*>(t.keys + slot), 0ull, ~bkey);
-    if (k == 0 || ~k == bkey) return static_cast<int64_t>(slot);
-    slot = (slot + 1) & t.mask;
+  uint64_t group = first_slot(t, bkey);
+  for (uint64_t round = 0; round * kSlotGroup <= t.mask; ++round) {
+    const uint4* p = reinterpret_cast<const uint4*>(t.keys + group);
+    const uint4 a = p[0], b = p[1];
+    const uint64_t k4[4] = {(static_cast<uint64_t>(a.y) << 32) | a.x, (static_cast<uint64_t>(a.w) << 32) | a.z,
+                            (static_cast<uint64_t>(b.y) << 32) | b.x, (static_cast<uint64_t>(b.w) << 32) | b.z};
+    for (int j = 0; j < static_cast<int>(kSlotGroup); ++j) {
+      if (k4[j] != 0) {
+        if (~k4[j] == bkey) return static_cast<int64_t>(group + j);
+        continue;
+      }
+      const uint64_t k = atomicCAS(reinterpret_cast<unsigned long long*>(t.keys + group + j), 0ull, ~bkey);
+      if (k == 0 || ~k == bkey) return static_cast<int64_t>(group + j);
+    }
+    group = (group + kSlotGroup) & t.mask;
   }
   if (flags) atomicOr(flags, TS_FLAG_FULL);
   return -1;
