@@ -300,15 +300,19 @@ __device__ __forceinline__ void load_offsets(const RelK& a, int8_t* offs) {
 template <int MODE, int ND, int K>
 __global__ __launch_bounds__(256) void k_rel_probe(RelK a, int natural, int64_t* n_out_fill) {
   constexpr int KV = Geo<ND, K>::KV;
+  // The workgroup's 256 rows own one contiguous span of the neighbour table:
+  // lanes stage their rows in LDS, and the span is then written with
+  // coalesced 16-byte stores (a lane's own row is KV scattered words).
+  __shared__ __attribute__((aligned(16))) int32_t staged[256 * KV];
   const int64_t t = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / kTile;
   const int r = threadIdx.x & (kTile - 1);
   if (n_out_fill && blockIdx.x == 0 && threadIdx.x == 0) *n_out_fill = a.n_dest_cap;
-  if (t >= a.n_tiles) return;  // whole 16-lane groups leave together
+  const bool live = t < a.n_tiles;  // every lane stays for the barrier below
   const int64_t n_dest = dest_count(a.n_dest, a.n_dest_cap);
   const int64_t row = t * kTile + r;
   uint64_t base = 0;
   int64_t f[3] = {0, 0, 0};
-  const bool valid = row < n_dest && dest_fields<MODE, ND>(a, row, &base, f);
+  const bool valid = live && row < n_dest && dest_fields<MODE, ND>(a, row, &base, f);
   int32_t nb[KV];
   probe_fields<ND, K>(a.src, base, f, valid ? ~0ull : 0ull, nb);
   uint64_t mask = 0;
@@ -317,17 +321,25 @@ __global__ __launch_bounds__(256) void k_rel_probe(RelK a, int natural, int64_t*
     if (nb[o] >= 0) mask |= 1ull << o;
   // a submanifold output takes part only when it owns its coordinate
   if (MODE == kModeSubm && nb[(KV - 1) / 2] != static_cast<int32_t>(row)) mask = 0;
-  if (row < a.n_dest_cap) {
-    a.row_mask[row] = mask;
-    int32_t* out = a.nbr + row * KV;
+  if (live && row < a.n_dest_cap) a.row_mask[row] = mask;
 #pragma unroll
-    for (int o = 0; o < KV; ++o) out[o] = ((mask >> o) & 1) ? nb[o] : -1;
-  }
+  for (int o = 0; o < KV; ++o) staged[threadIdx.x * KV + o] = ((mask >> o) & 1) ? nb[o] : -1;
   if (natural) {
     const uint64_t tmask = group16_or(mask);
-    if (r == 0) a.tile_mask[t] = tmask;
-    a.tile_rows[t * kTile + r] = row < n_dest ? static_cast<int32_t>(row) : -1;
+    if (live && r == 0) a.tile_mask[t] = tmask;
+    if (live) a.tile_rows[t * kTile + r] = row < n_dest ? static_cast<int32_t>(row) : -1;
   }
+  __syncthreads();
+  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * 256;
+  const int64_t rows = a.n_dest_cap - row0 < 256 ? a.n_dest_cap - row0 : 256;
+  if (rows <= 0) return;
+  const int words = static_cast<int>(rows) * KV;  // span start row0 * KV * 4 bytes is 16-byte aligned
+  int32_t* dst = a.nbr + row0 * KV;
+  const uint4* s4 = reinterpret_cast<const uint4*>(staged);
+  uint4* d4 = reinterpret_cast<uint4*>(dst);
+  for (int i = threadIdx.x; i < words / 4; i += 256) d4[i] = s4[i];
+  const int tail = words & 3;
+  if (threadIdx.x < tail) dst[words - tail + threadIdx.x] = staged[words - tail + threadIdx.x];
 }
 
 // Runtime-kvol versions (neighbours kept in LDS), for kernel sizes without a
