@@ -13,24 +13,27 @@
 // chunks, fragment (o, mb, kb) = 64 consecutive chunks), so every later copy
 // of a slice is a straight coalesced 16-byte copy.
 //
-// Work split.  A block of 4 waves owns 4*G tiles of 16 destination rows (each
-// wave G tiles, the output channels of one block column).  The block walks
-// the union of its tiles' offset masks in ascending order.  Per offset:
-//   * the packed weight slice is copied into LDS once per block;
-//   * each wave gathers, for each of its tiles that has the offset, the 16
-//     source rows straight into B fragments (16 bytes per lane);
+// Work split.  A block of NW wavefronts owns NW*G tiles of 16 destination
+// rows (each wavefront G tiles, the output channels of one block column) and
+// walks the union of its tiles' offset masks in ascending order.  Per offset:
+//   * the packed weight slice is copied into one of two LDS buffers with
+//     direct global-to-LDS loads (no register staging);
+//   * each wavefront gathers, for each of its tiles that has the offset, the
+//     16 source rows straight into B fragments (16 bytes per lane);
 //   * v_mfma_f32_16x16x32 with D = A . X^T, so a lane ends holding 4
-//     consecutive output channels of one row.
+//     consecutive output channels of one row; with G = 2 each A fragment read
+//     from LDS feeds two MFMAs.
 // Latency: the neighbour rows of a tile's 16 rows (the source row of each
 // slot at each offset) are loaded once, up front, into registers and picked
 // per offset with a lane shuffle, so no load address waits on another load
-// inside the loop.  Gathers and weight loads run D offsets ahead (D+1
-// register sets of each, two LDS weight buffers, one barrier per offset), so
-// the in-order load counter never forces a load to land early.  Gathers are
-// buffer loads: an absent row reads out of range and returns zeros without a
-// memory access.  Every output
-// row is written once, no atomics.  Blocks are numbered so that each XCD walks
-// a contiguous range of tiles (its L2 keeps the gathered rows).
+// inside the loop.  Gathers run two offsets ahead in three register sets.
+// Each step waits on the vector-memory counter only for its own copy of the
+// slice and meets the other wavefronts at a barrier without a memory fence,
+// so gathers for later offsets stay in flight across it.  Gathers are buffer
+// loads: an absent row reads out of range and returns zeros without a
+// memory access.  Every output row is written once, no atomics.  Blocks are
+// numbered so that each XCD walks a contiguous range of tiles (its L2 keeps
+// the gathered rows).
 #include <stdlib.h>
 
 #include "common.h"
