@@ -402,7 +402,12 @@ __global__ __launch_bounds__(kSortThreads) void k_rel_sort(const uint64_t* __res
   constexpr int kSortWindow = kSortThreads * kItems;
   constexpr int kSortWaves = kSortThreads / 64;
   __shared__ uint2 buf[kSortWindow];
-  __shared__ int hist[kDigits * kItems * kSortWaves];  // [digit][item][wave] -> exclusive start
+  // [digit][item][wave] -> exclusive start, one pad word after every 64: the
+  // per-digit writes and reads stride by kItems * kSortWaves words, which
+  // unpadded would put a wavefront's lanes on one LDS bank
+  constexpr int kHist = kDigits * kItems * kSortWaves;
+  __shared__ int hist[kHist + kHist / 64];
+  auto hx = [](int l) { return l + (l >> 6); };
   __shared__ int wsum[kSortWaves];
   const int64_t base = static_cast<int64_t>(blockIdx.x) * kSortWindow;
   const int64_t n_dest = dest_count(n_dest_p, n_dest_cap);
@@ -428,11 +433,11 @@ __global__ __launch_bounds__(kSortThreads) void k_rel_sort(const uint64_t* __res
 #pragma unroll
       for (int b = 0; b < 4; ++b) bal[b] = __ballot((d[i] >> b) & 1);
       rank[i] = __popcll(digit_lanes(bal, d[i]) & lt);
-      if (lane < kDigits) hist[(lane * kItems + i) * kSortWaves + wave] = __popcll(digit_lanes(bal, lane));
+      if (lane < kDigits) hist[hx((lane * kItems + i) * kSortWaves + wave)] = __popcll(digit_lanes(bal, lane));
     }
     __syncthreads();
     // block-wide exclusive scan of the 1024 counts (one per thread)
-    const int v = hist[threadIdx.x];
+    const int v = hist[hx(threadIdx.x)];
     int x = v;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -444,11 +449,11 @@ __global__ __launch_bounds__(kSortThreads) void k_rel_sort(const uint64_t* __res
     int before = 0;
 #pragma unroll
     for (int w = 0; w < kSortWaves; ++w) before += w < wave ? wsum[w] : 0;
-    hist[threadIdx.x] = before + x - v;
+    hist[hx(threadIdx.x)] = before + x - v;
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < kItems; ++i) {
-      const int dest = hist[(d[i] * kItems + i) * kSortWaves + wave] + rank[i];
+      const int dest = hist[hx((d[i] * kItems + i) * kSortWaves + wave)] + rank[i];
       buf[dest] = make_uint2(key[i], static_cast<uint32_t>(row[i]));
     }
     __syncthreads();
