@@ -117,10 +117,11 @@ __device__ __forceinline__ int cell_of(uint64_t key, int nd) {
 }
 
 // Linear probing starts at the hashed slot rounded down to a multiple of
-// kSlotGroup, so a lookup may read a whole aligned group of slots (32 bytes)
-// per round and check kSlotGroup probe positions at once.  On the ring-scan
-// table (load 0.16) a wavefront's 8-corner lookups then finish in 1.4 rounds
-// on average (at most 3) instead of 3.8 (at most 11).
+// kSlotGroup, so a lookup may read several consecutive slots of an aligned
+// group per round and check those probe positions at once.  On the
+// ring-scan table (load 0.16), reading two slots per round, a wavefront's
+// 8-corner lookups finish in about 2.3 rounds on average (at most 6) instead
+// of 3.8 (at most 11); a claim reads the whole group of four.
 constexpr uint64_t kSlotGroup = 4;
 __device__ __forceinline__ uint64_t first_slot(const Table& t, uint64_t bkey) {
   return hash64(bkey) & t.mask & ~(kSlotGroup - 1);

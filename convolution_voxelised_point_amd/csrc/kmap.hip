@@ -160,36 +160,32 @@ __device__ __forceinline__ void probe_fields(const Table& t, uint64_t base, cons
     slot[c] = static_cast<uint32_t>(first_slot(t, bk[c]));
     found[c] = -1;
   }
-  // each round reads the aligned group of kSlotGroup slots at every pending
-  // corner's probe position and resolves the first slot that holds the key
-  // or is empty
+  // each round reads kProbeRead consecutive slots (16 bytes) at every pending
+  // corner's probe position -- half of an aligned group, which keeps the
+  // registers of 8 corners in flight low -- and resolves the first slot that
+  // holds the key or is empty
+  constexpr int kProbeRead = 2;
   for (uint64_t round = 0; round <= t.mask && __ballot(pend != 0); ++round) {
-    uint4 g[NC][2];
+    uint4 g[NC];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const uint4* p = reinterpret_cast<const uint4*>(t.keys + (((pend >> c) & 1) ? slot[c] : 0));
-      g[c][0] = p[0];
-      g[c][1] = p[1];
-    }
+    for (int c = 0; c < NC; ++c) g[c] = *reinterpret_cast<const uint4*>(t.keys + (((pend >> c) & 1) ? slot[c] : 0));
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       if (!((pend >> c) & 1)) continue;
-      const uint64_t k4[4] = {~((static_cast<uint64_t>(g[c][0].y) << 32) | g[c][0].x),
-                              ~((static_cast<uint64_t>(g[c][0].w) << 32) | g[c][0].z),
-                              ~((static_cast<uint64_t>(g[c][1].y) << 32) | g[c][1].x),
-                              ~((static_cast<uint64_t>(g[c][1].w) << 32) | g[c][1].z)};
+      const uint64_t k2[2] = {~((static_cast<uint64_t>(g[c].y) << 32) | g[c].x),
+                              ~((static_cast<uint64_t>(g[c].w) << 32) | g[c].z)};
       int hit = -1;
       bool stop = false;
 #pragma unroll
-      for (int j = 3; j >= 0; --j) {  // first position that holds the key or is empty
-        if (k4[j] == bk[c]) { hit = j; stop = true; }
-        else if (k4[j] == kEmptyKey) { hit = -1; stop = true; }
+      for (int j = kProbeRead - 1; j >= 0; --j) {  // first position that holds the key or is empty
+        if (k2[j] == bk[c]) { hit = j; stop = true; }
+        else if (k2[j] == kEmptyKey) { hit = -1; stop = true; }
       }
       if (stop) {
         if (hit >= 0) found[c] = static_cast<int32_t>(slot[c] + hit);
         pend &= ~(1u << c);
       } else {
-        slot[c] = static_cast<uint32_t>((slot[c] + kSlotGroup) & t.mask);
+        slot[c] = static_cast<uint32_t>((slot[c] + kProbeRead) & t.mask);
       }
     }
   }
