@@ -14,8 +14,13 @@ same way and reported under "secondary".
 The ``setup_*`` functions below fix each workload's launch configuration;
 the full-size parity tests run the same functions.
 
+Besides the K timed replays, the headline step is timed in five more runs of
+K replays (median and spread), and cold: eager steps, each after a 512 MiB
+write that evicts the caches.  A copy of the ring scan with its rows in
+random order is measured as a secondary workload.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
-                       [--only lidar|down|pixels|train] [--copy-calib MB]
+                       [--only lidar|lidar_shuffled|down|pixels|train] [--copy-calib MB]
 """
 from __future__ import annotations
 
@@ -38,6 +43,9 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_F16_PEAK_TFLOPS = 2500.0  # dense fp16/bf16 MFMA
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_igemm_ring_scan_c64_traffic.txt")
 IGEMM_SOURCE = os.path.join(ROOT, "convolution_voxelised_point_amd", "csrc", "igemm.hip")
+COLD_SCRATCH_MIB = 512         # written between cold steps: twice the last-level cache
+COLD_STEPS = 20
+TRIALS = 5
 
 
 def popcount_sum(masks: torch.Tensor, kvol: int) -> int:
@@ -127,6 +135,28 @@ def run_graph(g, steps, warmup):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     return (t1 - t0) * 1e3 / steps, e0.elapsed_time(e1) / steps
+
+
+def run_cold(fns, names, steps, scratch_mib=COLD_SCRATCH_MIB):
+    """Eager steps with a write of `scratch_mib` MiB between them (outside the
+    timed events), so that each step starts with the 4 MB L2s and the 256 MB
+    last-level cache holding other data: (ms per step, mean us per stage)."""
+    scratch = torch.empty(scratch_mib << 20, dtype=torch.uint8, device="cuda")
+    timer = Timer(names)
+    for i in range(steps):
+        scratch.fill_(i & 255)
+        timer.step(fns)
+    torch.cuda.synchronize()
+    timer.collect()
+    del scratch
+    st = timer.mean_us()
+    return sum(st.values()) / 1e3, st
+
+
+def trials(g, steps, n=TRIALS):
+    """`n` further timed runs of `steps` graph replays each (HIP events):
+    ms per step of every run, for the median and spread."""
+    return [run_graph(g, steps, 0)[1] for _ in range(n)]
 
 
 class Step:
@@ -305,7 +335,10 @@ def measure_lidar(ts, steps, warmup):
     w = synth.make("lidar")
     s = setup_subm(ts, w)
     ms_eager, st = run_steps(s.fns, s.names, steps, warmup)
-    ms, ms_events = run_graph(capture(s.fns), steps, warmup)
+    g = capture(s.fns)
+    ms, ms_events = run_graph(g, steps, warmup)
+    tr = trials(g, steps)
+    ms_cold, st_cold = run_cold(s.fns, s.names, COLD_STEPS)
     n, cap = s.n, s.table.cap
     P = popcount_sum(s.kmap.rel_arrays("fwd")["row_mask"][:n], 27)
     cin, cout, kvol, e = w.cin, w.cout, 27, 2
@@ -318,6 +351,8 @@ def measure_lidar(ts, steps, warmup):
         "n": n, "pairs": P, "flop_per_step": flop,
         "ms_per_step": ms, "ms_per_step_events": ms_events, "ms_per_step_eager": ms_eager,
         "stages_us": {k: round(v, 3) for k, v in st.items()},
+        "trials_ms_per_step": [round(t, 5) for t in tr],
+        "ms_per_step_cold": ms_cold, "stages_us_cold": {k: round(v, 3) for k, v in st_cold.items()},
         "fwd_tflops": flop / conv_s / 1e12,
         "fwd_mfma_frac": flop / conv_s / 1e12 / MFMA_F16_PEAK_TFLOPS,
         "fwd_alg_bytes": conv_bytes,
@@ -330,6 +365,24 @@ def measure_lidar(ts, steps, warmup):
         "err_flags": int(s.flags.item()),
     }
     return w, res
+
+
+def measure_lidar_shuffled(ts, steps, warmup):
+    """The ring scan with its rows in a seeded random order, with the map's
+    tiles in row order and sorted by offset mask."""
+    w = synth.shuffled(synth.make("lidar"))
+    out = {"workload": "lidar_shuffled", "n": w.n}
+    for order, flags in (("natural", ts.TS_KMAP_NATURAL), ("sorted", 0)):
+        s = setup_subm(ts, w, kmap_flags=flags)
+        _, st = run_steps(s.fns, s.names, steps, warmup)
+        ms, _ = run_graph(capture(s.fns), steps, warmup)
+        if order == "natural":
+            P = popcount_sum(s.kmap.rel_arrays("fwd")["row_mask"][:s.n], 27)
+            out["pairs"] = P
+        out[order] = {"ms_per_step": ms, "stages_us": {k: round(v, 3) for k, v in st.items()},
+                      "tflops_step": 2.0 * P * w.cin * w.cout / (ms * 1e-3) / 1e12}
+        del s
+    return out
 
 
 def measure_down(ts, steps, warmup):
@@ -395,8 +448,10 @@ def measured_traffic():
 
 # ---------------------------------------------------------------- CPU oracle
 def cpu_baseline(w, P, min_seconds=10.0):
-    """The oracle (hash, kernel map, forward; fp64, one thread) on the full
-    LiDAR workload, repeated until about min_seconds of CPU time."""
+    """The oracle (fp64, one thread) on the full ring-scan scene: hash +
+    kernel map and forward repeated until about `min_seconds` of CPU time
+    (the headline figure), then dgrad and wgrad once each with a seeded
+    upstream gradient, every stage reported on its own."""
     import oracle
     oracle.lib()
     t_kmap = t_fwd = 0.0
@@ -411,12 +466,30 @@ def cpu_baseline(w, P, min_seconds=10.0):
         t_kmap += t1 - t0
         t_fwd += t2 - t1
         passes += 1
+    dy = synth.normal(1000 * w.index + 903, (w.n, w.cout), 1.0, w.dtype)
+    t0 = time.perf_counter()
+    oracle.conv_dgrad(tr, dy, w.w, w.n)
+    t1 = time.perf_counter()
+    oracle.conv_wgrad(tr, w.x, dy, 27)
+    t2 = time.perf_counter()
+    t_dgrad, t_wgrad = t1 - t0, t2 - t1
     flop = 2.0 * P * w.cin * w.cout
     sec = (t_kmap + t_fwd) / passes
-    return {"value": flop / sec / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+
+    def stage(t, with_flop):
+        d = {"seconds": t, "mvox_s": w.n / t / 1e6}
+        if with_flop:
+            d["gflop_s"] = flop / t / 1e9
+        return d
+
+    return {"value": flop / sec / 1e12, "unit": "TFLOP/s", "cores": 1, "host_cpus": os.cpu_count(),
+            "kind": "oracle",
             "sample": f"full ring-scan scene ({w.coords.shape[0]} voxels, {P} pairs), {passes} passes of hash + "
-                      f"kernel map ({t_kmap / passes:.3f} s) and fp64 forward ({t_fwd / passes:.3f} s), one thread",
-            "seconds": t_kmap + t_fwd}
+                      f"kernel map ({t_kmap / passes:.3f} s) and fp64 forward ({t_fwd / passes:.3f} s), one thread; "
+                      f"value counts the forward's map-valid flops over hash + kernel map + forward",
+            "stages": {"hash_kmap": stage(t_kmap / passes, False), "fwd": stage(t_fwd / passes, True),
+                       "dgrad": stage(t_dgrad, True), "wgrad": stage(t_wgrad, True)},
+            "seconds": t_kmap + t_fwd + t_dgrad + t_wgrad}
 
 
 def copy_calibration(mb: int, steps: int):
@@ -436,7 +509,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
-    ap.add_argument("--only", default=None, help="measure one workload (lidar, down, pixels, train)")
+    ap.add_argument("--only", default=None,
+                    help="measure one workload (lidar, lidar_shuffled, down, pixels, train)")
     ap.add_argument("--copy-calib", type=int, default=0, help="run only a plain copy of this many MiB")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -450,13 +524,14 @@ def main():
 
     torch.cuda.synchronize()
     if args.only and args.only != "lidar":
-        fn = {"down": measure_down, "pixels": measure_pixels, "train": measure_train}[args.only]
+        fn = {"lidar_shuffled": measure_lidar_shuffled, "down": measure_down, "pixels": measure_pixels,
+              "train": measure_train}[args.only]
         print(json.dumps(fn(ts, args.steps, args.warmup)))
         return
     w, r = measure_lidar(ts, args.steps, args.warmup)
     secondary = []
     if args.only is None:
-        for fn in (measure_down, measure_pixels, measure_train):
+        for fn in (measure_lidar_shuffled, measure_down, measure_pixels, measure_train):
             secondary.append(fn(ts, args.steps, args.warmup))
     value = r["flop_per_step"] / (r["ms_per_step"] * 1e-3) / 1e12
     conv_s = r["stages_us"]["conv"] * 1e-6
@@ -470,6 +545,9 @@ def main():
         "ms_per_step": r["ms_per_step"],
         "ms_per_step_events": r["ms_per_step_events"],
         "ms_per_step_eager": r["ms_per_step_eager"],
+        "ms_per_step_median5": sorted(r["trials_ms_per_step"])[len(r["trials_ms_per_step"]) // 2],
+        "trials_ms_per_step": r["trials_ms_per_step"],
+        "ms_per_step_cold": r["ms_per_step_cold"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -483,6 +561,7 @@ def main():
         "kmap_with_hash_mvox_s": r["kmap_with_hash_mvox_s"],
         "kmap_hbm_frac": r["kmap_gbs"] / HBM_PEAK_GBS,
         "stages_us": r["stages_us"],
+        "stages_us_cold": r["stages_us_cold"],
         "roofline": {"bound": "hbm", "kernel": "SubmConv3d forward call (k_wpack + k_igemm)",
                      "achieved": r["fwd_alg_bytes"] / conv_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": r["fwd_alg_bytes"] / conv_s / 1e9 / HBM_PEAK_GBS, "traffic": measured_traffic(),

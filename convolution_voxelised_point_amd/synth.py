@@ -22,7 +22,7 @@ Workloads (all seeded with ``numpy.random.default_rng``):
 Seeds: the geometry of scene/image ``b`` of workload number ``c`` (1..5 in
 the order above) uses ``1000*c + b``; features ``1000*c + 900``; weights
 ``1000*c + 901`` (second pixel layer ``1000*c + 902``); upstream gradient
-``1000*c + 903``.  Low-precision values are drawn in fp32 and rounded to the
+``1000*c + 903``; the row permutation of a shuffled variant ``1000*c + 904``.  Low-precision values are drawn in fp32 and rounded to the
 storage type with round-to-nearest-even (torch's float conversion).
 
 Ring-scan scene (stands in for the autonomous-driving LiDAR benchmarks, whose
@@ -37,7 +37,7 @@ and rows are ordered lexicographically by (b, x, y, z).
 from __future__ import annotations
 
 import math
-from dataclasses import dataclass, field
+from dataclasses import dataclass, field, replace
 from typing import Dict, List, Optional
 
 import numpy as np
@@ -214,6 +214,17 @@ def make(name: str, scale: float = 1.0) -> Workload:
         dy = normal(1000 * c + 903, (coords.shape[0], 128), 1.0, "bf16")
         return Workload(name, c, coords, 3, 3, 1, 128, 128, "bf16", x, w, dy=dy)
     raise KeyError(name)
+
+
+def shuffled(w: Workload) -> Workload:
+    """The same workload with its rows in a seeded random order: coordinates,
+    features and upstream gradient permuted together (row i still owns
+    feature row i), so the scene is unchanged but neighbouring voxels no
+    longer sit in nearby rows."""
+    perm = np.random.default_rng(1000 * w.index + 904).permutation(w.n)
+    p = torch.from_numpy(perm)
+    return replace(w, name=w.name + "_shuffled", coords=np.ascontiguousarray(w.coords[perm]),
+                   x=w.x[p].contiguous(), dy=None if w.dy is None else w.dy[p].contiguous())
 
 
 def random_coords(seed: int, n: int, ndim: int, batch: int, extent: int,

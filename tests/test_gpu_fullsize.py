@@ -53,11 +53,15 @@ def ts_decode(km, kvol):
     return ts.decode_rel(km.rel_arrays("fwd"), kvol)
 
 
+@pytest.mark.parametrize("rows_shuffled", [False, True], ids=["lex_rows", "shuffled_rows"])
 @pytest.mark.parametrize("order", ["natural", "sorted"])
-def test_full_lidar_subm_f16(ts, order):
+def test_full_lidar_subm_f16(ts, order, rows_shuffled):
     """Both tile orders: the benchmark's (rows in index order, the map
-    serving one contraction) and the window sort by offset mask."""
+    serving one contraction) and the window sort by offset mask; on the
+    scene's lexicographic rows and on the seeded shuffle of them."""
     w = synth.make("lidar")
+    if rows_shuffled:
+        w = synth.shuffled(w)
     s = bench.setup_subm(ts, w, kmap_flags=ts.TS_KMAP_NATURAL if order == "natural" else 0)
     s.run_once()
     assert int(s.flags.item()) == 0
