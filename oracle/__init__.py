@@ -45,7 +45,9 @@ def lib():
         L.oracle_hash_query.restype = i64
         L.oracle_strided_support.argtypes = [p, i64, i32, i32, p]
         L.oracle_strided_support.restype = i64
-        L.oracle_kmap.argtypes = [p, i64, p, i64, i32, i32, i32, p, p, p, i64]
+        L.oracle_generative_support.argtypes = [p, i64, i32, i32, p, i64]
+        L.oracle_generative_support.restype = i64
+        L.oracle_kmap.argtypes = [p, i64, p, i64, i32, i32, i32, i32, p, p, p, i64]
         L.oracle_kmap.restype = i64
         L.oracle_conv_fwd.argtypes = [p, p, p, i64, p, i32, p, i32, p, i64]
         L.oracle_conv_fwd.restype = None
@@ -97,8 +99,23 @@ def strided_support(coords, stride: int) -> np.ndarray:
     return out[:n_out].copy()
 
 
-def kmap(in_coords, out_coords, ksize: int, stride: int = 1) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
-    """Kernel-map triples (in, out, offset), ordered by (out, offset)."""
+def generative_support(coords, ksize: int) -> np.ndarray:
+    """Output coordinates a stride-1 convolution generates: every site
+    c_i - delta_o, in first-occurrence order over (input row, offset)."""
+    c = _coords(coords)
+    ndim = c.shape[1] - 1
+    cap = max(1, c.shape[0] * ksize ** ndim)
+    out = np.empty((cap, ndim + 1), np.int32)
+    n_out = lib().oracle_generative_support(_ptr(c), c.shape[0], ndim, ksize, _ptr(out), cap)
+    assert n_out <= cap
+    return out[:n_out].copy()
+
+
+def kmap(in_coords, out_coords, ksize: int, stride: int = 1,
+         target: bool = False) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Kernel-map triples (in, out, offset), ordered by (out, offset).  With
+    `target` the output rows are caller coordinates (no ownership test at
+    stride 1)."""
     ci, co = _coords(in_coords), _coords(out_coords)
     ndim = ci.shape[1] - 1
     kvol = ksize ** ndim
@@ -106,7 +123,7 @@ def kmap(in_coords, out_coords, ksize: int, stride: int = 1) -> Tuple[np.ndarray
     t_in = np.empty(cap, np.int32)
     t_out = np.empty(cap, np.int32)
     t_off = np.empty(cap, np.int32)
-    n = lib().oracle_kmap(_ptr(ci), ci.shape[0], _ptr(co), co.shape[0], ndim, ksize, stride,
+    n = lib().oracle_kmap(_ptr(ci), ci.shape[0], _ptr(co), co.shape[0], ndim, ksize, stride, 1 if target else 0,
                           _ptr(t_in), _ptr(t_out), _ptr(t_off), cap)
     assert n <= cap
     return t_in[:n].copy(), t_out[:n].copy(), t_off[:n].copy()

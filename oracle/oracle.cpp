@@ -13,6 +13,11 @@
 //     dense feature row per coordinate row; the batch id lives in column 0;
 //   * SubmConv3d keeps the input coordinate set as the output set;
 //   * a strided Conv3d creates a downsampled output set;
+//   * a stride-1 Conv3d with a kernel wider than one cell generates its output
+//     set (section "What is intentionally different", row on convolution
+//     intent);
+//   * TargetConv3d computes at output coordinates the caller gives (same
+//     table, and the "Convolution mapping" table);
 //   * every dataflow must give the same result for a fixed relation
 //     (input row, output row, kernel offset) and weight tensor.
 //
@@ -30,6 +35,11 @@
 //   * submanifold: output row j reads input q_j + delta;
 //     strided: outputs are unique(floor(c/s)) in first-occurrence order and
 //     output j reads input s*q_j + delta;
+//     target: output row j (any caller coordinate, repeats allowed) reads
+//     input s*q_j + delta, s = 1 included, with no ownership condition;
+//     generative stride 1: outputs are every q = c_i - delta (the sites some
+//     input reaches), in first-occurrence order over (i, then offset), and
+//     are then used as targets;
 //   * cross-correlation (no kernel flip), W laid out [offset][cin][cout];
 //   * all arithmetic in fp64.
 //
@@ -154,12 +164,50 @@ int64_t oracle_strided_support(const int32_t* coords, int64_t n, int ndim, int s
   return n_out;
 }
 
+// Generated output set of a stride-1 convolution: for each input row i in
+// order that owns its coordinate, and each offset o in order, the site
+// q = c_i - delta_o (the output whose window holds c_i at offset o) is
+// appended when first seen; a site outside the coordinate range is skipped.
+// Writes up to `cap` rows and returns how many sites exist.
+int64_t oracle_generative_support(const int32_t* coords, int64_t n, int ndim, int ksize, int32_t* out_coords,
+                                  int64_t cap) {
+  Map owner = build_map(coords, n, ndim, nullptr);
+  Map seen;
+  const int kvol = ipow(ksize, ndim);
+  int64_t n_out = 0;
+  int64_t delta[3];
+  for (int64_t i = 0; i < n; ++i) {
+    const int32_t* row = coords + i * (ndim + 1);
+    if (!in_range(row, ndim) || lookup(owner, key_of(row, ndim)) != i) continue;
+    for (int o = 0; o < kvol; ++o) {
+      offset_delta(o, ndim, ksize, delta);
+      int32_t q[4] = {row[0], 0, 0, 0};
+      bool ok = true;
+      for (int d = 0; d < ndim; ++d) {
+        const int64_t v = static_cast<int64_t>(row[d + 1]) - delta[d];
+        if (v < -32768 || v > 32767) ok = false;
+        q[d + 1] = static_cast<int32_t>(v);
+      }
+      if (!ok) continue;
+      if (seen.emplace(key_of(q, ndim), n_out).second) {
+        if (n_out < cap)
+          for (int d = 0; d <= ndim; ++d) out_coords[n_out * (ndim + 1) + d] = q[d];
+        ++n_out;
+      }
+    }
+  }
+  return n_out;
+}
+
 // Kernel map: for every output row j (in order) and offset o (in order), the
-// input row i at s*q_j + delta_o (s = 1: q_j + delta_o) if it exists.  Writes
-// up to `cap` triples (in, out, offset) and returns how many exist.
+// input row i at s*q_j + delta_o (s = 1: q_j + delta_o) if it exists.  With
+// `target` == 0 and s = 1 the outputs are the inputs themselves (submanifold)
+// and a row takes part only if it owns its coordinate; with `target` != 0
+// every in-range output row takes part.  Writes up to `cap` triples
+// (in, out, offset) and returns how many exist.
 int64_t oracle_kmap(const int32_t* in_coords, int64_t n_in, const int32_t* out_coords, int64_t n_out,
-                    int ndim, int ksize, int stride, int32_t* t_in, int32_t* t_out, int32_t* t_off,
-                    int64_t cap) {
+                    int ndim, int ksize, int stride, int target, int32_t* t_in, int32_t* t_out,
+                    int32_t* t_off, int64_t cap) {
   Map map = build_map(in_coords, n_in, ndim, nullptr);
   const int kvol = ipow(ksize, ndim);
   int64_t count = 0;
@@ -169,7 +217,7 @@ int64_t oracle_kmap(const int32_t* in_coords, int64_t n_in, const int32_t* out_c
     if (!in_range(q, ndim)) continue;
     // submanifold outputs are the input rows: only the owner of a coordinate
     // takes part
-    if (stride == 1 && lookup(map, key_of(q, ndim)) != j) continue;
+    if (stride == 1 && !target && lookup(map, key_of(q, ndim)) != j) continue;
     for (int o = 0; o < kvol; ++o) {
       offset_delta(o, ndim, ksize, delta);
       Key p{0, 0, 0, 0};
