@@ -44,12 +44,16 @@ struct Carver {
   }
 };
 
-int64_t pair_capacity(int64_t n_in, int64_t n_out_cap, int ndim, int ksize, int stride) {
+// Pairs a map can hold: at most kvol per output row; with distinct outputs
+// (submanifold, or a support from ts_strided_support) also at most
+// ceil(k/s)^D per input row.  Caller targets may repeat a coordinate, so a
+// target map takes the first bound alone.
+int64_t pair_capacity(int64_t n_in, int64_t n_out_cap, int ndim, int ksize, int stride, bool target) {
   const int kvol = ipow(ksize, ndim);
   const int per_axis = (ksize + stride - 1) / stride;
   const int64_t a = n_out_cap * kvol;
   const int64_t b = n_in * ipow(per_axis, ndim);
-  return a < b ? a : b;
+  return (target || a < b) ? a : b;
 }
 
 void carve_rel(Carver& c, ts_rel* r, int64_t n_dest_cap, int kvol) {
@@ -72,22 +76,25 @@ size_t layout_kmap(char* base, ts_kmap* m, int64_t n_in, int64_t n_out_cap, int 
   m->stride = stride;
   m->kvol = ipow(ksize, ndim);
   m->flags = flags;
-  m->mirror_bwd = stride == 1 ? 1 : 0;
+  // a target map's outputs are not its inputs, so its transposed relation is
+  // a map of its own, as for a strided one
+  const bool own_bwd = stride > 1 || (flags & TS_KMAP_TARGET);
+  m->mirror_bwd = own_bwd ? 0 : 1;
   m->n_in = n_in;
   m->n_out_cap = n_out_cap;
   m->n_out = c.take<int64_t>(1);
   carve_rel(c, &m->fwd, n_out_cap, m->kvol);
-  if (stride > 1 && (flags & TS_KMAP_BWD)) carve_rel(c, &m->bwd, n_in, m->kvol);
+  if (own_bwd && (flags & TS_KMAP_BWD)) carve_rel(c, &m->bwd, n_in, m->kvol);
   size_t scratch = rel_scratch_bytes(n_out_cap, m->kvol);
   if (flags & TS_KMAP_PAIRS) {
-    m->pair_cap = pair_capacity(n_in, n_out_cap, ndim, ksize, stride);
+    m->pair_cap = pair_capacity(n_in, n_out_cap, ndim, ksize, stride, (flags & TS_KMAP_TARGET) != 0);
     m->pair_start = c.take<int64_t>(static_cast<size_t>(m->kvol) + 1);
     m->pair_in = c.take<int32_t>(static_cast<size_t>(m->pair_cap));
     m->pair_out = c.take<int32_t>(static_cast<size_t>(m->pair_cap));
     const size_t ps = pairs_scratch_bytes(n_out_cap, m->kvol);
     if (ps > scratch) scratch = ps;
   }
-  if (stride > 1 && (flags & TS_KMAP_BWD)) {
+  if (own_bwd && (flags & TS_KMAP_BWD)) {
     const size_t rs = rel_scratch_bytes(n_in, m->kvol);
     if (rs > scratch) scratch = rs;
   }
@@ -176,6 +183,26 @@ ts_status ts_strided_support(const int32_t* in_coords, int64_t n_in, int ndim, i
   return TS_OK;
 }
 
+size_t ts_generative_scratch_bytes(int64_t n_in, int ndim, int ksize) {
+  if (n_in < 0 || !shape_ok(ndim, ksize, 1)) return 0;
+  return generative_scratch_bytes(n_in * ipow(ksize, ndim));
+}
+
+ts_status ts_generative_support(const int32_t* in_coords, int64_t n_in, int ndim, int ksize, int32_t* out_coords,
+                                int64_t n_out_cap, int64_t* n_out, void* out_table, int64_t out_cap, void* scratch,
+                                size_t scratch_bytes, uint32_t* err_flags, hipStream_t stream) {
+  if (!shape_ok(ndim, ksize, 1)) return TS_ERR_INVALID_ARG;
+  if (n_in < 0 || n_in > kMaxRows || (n_in > 0 && !in_coords) || !n_out || !out_table) return TS_ERR_INVALID_ARG;
+  if (n_out_cap < 0 || n_out_cap > kMaxRows || (n_out_cap > 0 && !out_coords)) return TS_ERR_INVALID_ARG;
+  if (n_in * ipow(ksize, ndim) > kMaxRows) return TS_ERR_UNSUPPORTED;
+  if (!is_pow2(out_cap)) return TS_ERR_INVALID_ARG;
+  if (out_cap > kMaxCap) return TS_ERR_UNSUPPORTED;
+  if (!scratch || scratch_bytes < ts_generative_scratch_bytes(n_in, ndim, ksize)) return TS_ERR_INVALID_ARG;
+  TS_TRY(launch_generative_support(in_coords, n_in, ndim, ksize, out_coords, n_out_cap, n_out, out_table, out_cap,
+                                   scratch, err_flags, stream));
+  return TS_OK;
+}
+
 size_t ts_kmap_bytes(int64_t n_in, int64_t n_out_cap, int ndim, int ksize, int stride, uint32_t flags) {
   if (n_in < 0 || n_out_cap < 0 || !shape_ok(ndim, ksize, stride)) return 0;
   ts_kmap tmp;
@@ -193,9 +220,11 @@ ts_status ts_kmap_build(const int32_t* in_coords, int64_t n_in, const void* in_t
   }
   if (n_in < 0 || n_in > kMaxRows || (n_in > 0 && !in_coords) || !is_pow2(in_cap) || in_cap > kMaxCap)
     return TS_ERR_INVALID_ARG;
-  if (flags & ~(TS_KMAP_PAIRS | TS_KMAP_BWD | TS_KMAP_NATURAL)) return TS_ERR_INVALID_ARG;
+  if (flags & ~(TS_KMAP_PAIRS | TS_KMAP_BWD | TS_KMAP_NATURAL | TS_KMAP_TARGET)) return TS_ERR_INVALID_ARG;
   const int kvol = ipow(ksize, ndim);
-  if (stride == 1) {
+  const bool target = (flags & TS_KMAP_TARGET) != 0;
+  const bool subm = stride == 1 && !target;
+  if (subm) {
     if (ksize % 2 == 0) return TS_ERR_UNSUPPORTED;  // submanifold needs a centred kernel
     out_coords = in_coords;
     n_out_cap = n_in;
@@ -210,7 +239,9 @@ ts_status ts_kmap_build(const int32_t* in_coords, int64_t n_in, const void* in_t
   const bool natural = (flags & TS_KMAP_NATURAL) != 0;
 
   RelBuild f;
-  f.mode = stride == 1 ? kModeSubm : kModeDown;
+  // targets and strided outputs take the inputs at s*q + delta (s = 1 for a
+  // target map); only a submanifold output must also own its coordinate
+  f.mode = subm ? kModeSubm : kModeDown;
   f.dest_coords = out_coords;
   f.n_dest_cap = n_out_cap;
   f.ndim = ndim;
@@ -222,7 +253,7 @@ ts_status ts_kmap_build(const int32_t* in_coords, int64_t n_in, const void* in_t
   f.own_table = nullptr;
   f.own_cap = 0;
   int64_t* n_out_fill = nullptr;
-  if (stride == 1) {
+  if (subm) {
     n_out_fill = m.n_out;  // written by the map kernel: outputs = inputs
     f.n_dest = nullptr;
   } else {
@@ -232,7 +263,7 @@ ts_status ts_kmap_build(const int32_t* in_coords, int64_t n_in, const void* in_t
   m.fwd.n_dest = m.n_out;
   TS_TRY(launch_rel_build(f, m.fwd, natural, n_out_fill, stream));
 
-  if (stride > 1 && (flags & TS_KMAP_BWD)) {
+  if (!subm && (flags & TS_KMAP_BWD)) {
     RelBuild b = f;
     b.mode = kModeUp;
     b.dest_coords = in_coords;
@@ -244,7 +275,8 @@ ts_status ts_kmap_build(const int32_t* in_coords, int64_t n_in, const void* in_t
     b.own_cap = in_cap;
     TS_TRY(launch_rel_build(b, m.bwd, natural, nullptr, stream));
   }
-  if (flags & TS_KMAP_PAIRS) TS_TRY(launch_pairs_build(f, m.fwd, m.pair_start, m.pair_in, m.pair_out, m.scratch, stream));
+  if (flags & TS_KMAP_PAIRS)
+    TS_TRY(launch_pairs_build(f, m.fwd, m.pair_cap, m.pair_start, m.pair_in, m.pair_out, m.scratch, stream));
   *map = m;
   return TS_OK;
 }
@@ -299,7 +331,7 @@ ts_status ts_conv_fwd(const ts_kmap* map, const void* x, int cin, const void* w,
 ts_status ts_subm_conv_fwd(const ts_kmap* map, const void* x, int cin, const void* w, int cout, void* y,
                            ts_dtype in_dtype, ts_dtype out_dtype, ts_dataflow dataflow, void* ws, size_t ws_bytes,
                            hipStream_t stream) {
-  if (!map || map->stride != 1) return TS_ERR_INVALID_ARG;
+  if (!map || map->stride != 1 || (map->flags & TS_KMAP_TARGET)) return TS_ERR_INVALID_ARG;
   return ts_conv_fwd(map, x, cin, w, cout, y, in_dtype, out_dtype, dataflow, ws, ws_bytes, stream);
 }
 
@@ -335,6 +367,41 @@ ts_status ts_conv_fwd_strided(const int32_t* in_coords, int64_t n_in, int ndim, 
   if (st != TS_OK) return st;
   st = ts_kmap_build(in_coords, n_in, in_table, in_cap, out_coords, n_in, n_out, out_table, out_cap, ndim, ksize,
                      stride, kmap_flags, map_buf, kb, map, stream);
+  if (st != TS_OK) return st;
+  return ts_conv_fwd(map, x, cin, w, cout, y, in_dtype, out_dtype, dataflow, ws, ws_bytes, stream);
+}
+
+ts_status ts_conv_fwd_generative(const int32_t* in_coords, int64_t n_in, int ndim, const void* in_table,
+                                 int64_t in_cap, int ksize, uint32_t kmap_flags, int32_t* out_coords,
+                                 int64_t n_out_cap, int64_t* n_out, void* out_table, int64_t out_cap,
+                                 uint32_t* err_flags, void* map_buf, size_t map_bytes, ts_kmap* map, const void* x,
+                                 int cin, const void* w, int cout, void* y, ts_dtype in_dtype, ts_dtype out_dtype,
+                                 ts_dataflow dataflow, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!map_buf || !map) return TS_ERR_INVALID_ARG;
+  if (!shape_ok(ndim, ksize, 1)) return TS_ERR_INVALID_ARG;
+  if (n_in < 0 || n_in > kMaxRows || n_out_cap < 0 || n_out_cap > kMaxRows) return TS_ERR_INVALID_ARG;
+  const uint32_t flags = kmap_flags | TS_KMAP_TARGET;
+  const size_t kb = ts_kmap_bytes(n_in, n_out_cap, ndim, ksize, 1, flags);
+  const size_t sb = ts_generative_scratch_bytes(n_in, ndim, ksize);
+  if (kb == 0 || map_bytes < kb + sb) return TS_ERR_INVALID_ARG;
+  // validate the convolution arguments before launching anything
+  if (cin < 1 || cout < 1 || cin > kMaxChannels || cout > kMaxChannels || !w) return TS_ERR_INVALID_ARG;
+  if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return TS_ERR_INVALID_ARG;
+  if (out_dtype != TS_F32 && out_dtype != in_dtype) return TS_ERR_UNSUPPORTED;
+  if ((n_in > 0 && !x) || (n_out_cap > 0 && !y)) return TS_ERR_INVALID_ARG;
+  if (dataflow == TS_DATAFLOW_GATHER_SCATTER && !(flags & TS_KMAP_PAIRS)) return TS_ERR_INVALID_ARG;
+  {
+    ts_kmap probe;
+    layout_kmap(nullptr, &probe, n_in, n_out_cap, ndim, ksize, 1, flags);
+    const size_t need = conv_ws(&probe, cin, cout, in_dtype, out_dtype, dataflow, n_out_cap, n_in);
+    if (need > 0 && (!ws || ws_bytes < need)) return TS_ERR_INVALID_ARG;
+  }
+  void* scratch = static_cast<char*>(map_buf) + kb;
+  ts_status st = ts_generative_support(in_coords, n_in, ndim, ksize, out_coords, n_out_cap, n_out, out_table, out_cap,
+                                       scratch, sb, err_flags, stream);
+  if (st != TS_OK) return st;
+  st = ts_kmap_build(in_coords, n_in, in_table, in_cap, out_coords, n_out_cap, n_out, out_table, out_cap, ndim, ksize,
+                     1, flags, map_buf, kb, map, stream);
   if (st != TS_OK) return st;
   return ts_conv_fwd(map, x, cin, w, cout, y, in_dtype, out_dtype, dataflow, ws, ws_bytes, stream);
 }

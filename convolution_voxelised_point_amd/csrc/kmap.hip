@@ -326,8 +326,9 @@ __global__ __launch_bounds__(256) void k_rel_probe(RelK a, int natural, int64_t*
     if (live) a.tile_rows[t * kTile + r] = row < n_dest ? static_cast<int32_t>(row) : -1;
   }
   __syncthreads();
+  // rows at or past the device count are never read through the table
   const int64_t row0 = static_cast<int64_t>(blockIdx.x) * 256;
-  const int64_t rows = a.n_dest_cap - row0 < 256 ? a.n_dest_cap - row0 : 256;
+  const int64_t rows = n_dest - row0 < 256 ? n_dest - row0 : 256;
   if (rows <= 0) return;
   const int words = static_cast<int>(rows) * KV;  // span start row0 * KV * 4 bytes is 16-byte aligned
   int32_t* dst = a.nbr + row0 * KV;
@@ -360,10 +361,9 @@ __global__ __launch_bounds__(256) void k_rel_probe_any(RelK a, int natural) {
     if (n >= 0) mask |= 1ull << o;
   }
   if (MODE == kModeSubm && valid && my[a.centre] != static_cast<int32_t>(row)) mask = 0;
-  if (row < a.n_dest_cap) {
-    a.row_mask[row] = mask;
+  if (row < a.n_dest_cap) a.row_mask[row] = mask;
+  if (row < n_dest)
     for (int o = 0; o < a.kvol; ++o) a.nbr[row * a.kvol + o] = ((mask >> o) & 1) ? my[o] : -1;
-  }
   if (!natural) return;
   const uint64_t tmask = group16_or(mask);
   if (r == 0) a.tile_mask[t] = tmask;
@@ -498,16 +498,19 @@ __global__ __launch_bounds__(256) void k_pairs_count(const uint64_t* __restrict_
 // the wavefronts before it -- is computed once into LDS.  Block 0 also
 // writes pair_start.
 __global__ __launch_bounds__(256) void k_pairs_fill(RelK a, int64_t nblk, const int32_t* __restrict__ base,
-                                                    const int64_t* total, int64_t* __restrict__ pair_start,
-                                                    int32_t* __restrict__ pair_in, int32_t* __restrict__ pair_out) {
+                                                    const int64_t* total, int64_t pair_cap,
+                                                    int64_t* __restrict__ pair_start, int32_t* __restrict__ pair_in,
+                                                    int32_t* __restrict__ pair_out) {
   __shared__ int wave_pos[4][TS_MAX_KVOL];
   const int64_t n_dest = dest_count(a.n_dest, a.n_dest_cap);
   const int64_t row = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   const uint64_t mask = row < n_dest ? a.row_mask[row] : 0;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const uint64_t below = (1ull << lane) - 1;
-  if (blockIdx.x == 0 && threadIdx.x <= a.kvol)
-    pair_start[threadIdx.x] = threadIdx.x < a.kvol ? base[threadIdx.x * nblk] : *total;
+  if (blockIdx.x == 0 && threadIdx.x <= a.kvol) {  // clamped: lists never run past their capacity
+    const int64_t v = threadIdx.x < a.kvol ? base[threadIdx.x * nblk] : *total;
+    pair_start[threadIdx.x] = v < pair_cap ? v : pair_cap;
+  }
   for (int o = 0; o < a.kvol; ++o) {
     const uint64_t bal = __ballot((mask >> o) & 1);
     if (lane == 0) wave_pos[wave][o] = __popcll(bal);
@@ -529,6 +532,7 @@ __global__ __launch_bounds__(256) void k_pairs_fill(RelK a, int64_t nblk, const 
     const uint64_t bal = __ballot(has);  // every lane takes part
     if (!has) continue;
     const int pos = wave_pos[wave][o] + __popcll(bal & below);
+    if (pos >= pair_cap) continue;
     pair_out[pos] = static_cast<int32_t>(row);
     pair_in[pos] = a.nbr[row * a.kvol + o];
   }
@@ -631,8 +635,8 @@ size_t pairs_scratch_bytes(int64_t n_dest_cap, int kvol) {
   return align_up(static_cast<size_t>(n > 0 ? n : 1) * 4, 256) + scan_tmp_bytes(n);
 }
 
-hipError_t launch_pairs_build(const RelBuild& bld, const ts_rel& rel, int64_t* pair_start, int32_t* pair_in,
-                              int32_t* pair_out, void* scratch, hipStream_t s) {
+hipError_t launch_pairs_build(const RelBuild& bld, const ts_rel& rel, int64_t pair_cap, int64_t* pair_start,
+                              int32_t* pair_in, int32_t* pair_out, void* scratch, hipStream_t s) {
   const int64_t nblk = ceil_div<int64_t>(bld.n_dest_cap, 256);
   if (nblk == 0) return fill_i64(pair_start, bld.kvol + 1, 0, s);
   const int64_t n = nblk * bld.kvol;
@@ -643,8 +647,8 @@ hipError_t launch_pairs_build(const RelBuild& bld, const ts_rel& rel, int64_t* p
   hipError_t e = scan_exclusive_i32(cnt, cnt, n, pair_start + bld.kvol, tmp, s);
   if (e != hipSuccess) return e;
   RelK a = make_relk(bld, rel);
-  k_pairs_fill<<<static_cast<unsigned>(nblk), 256, 0, s>>>(a, nblk, cnt, pair_start + bld.kvol, pair_start, pair_in,
-                                                             pair_out);
+  k_pairs_fill<<<static_cast<unsigned>(nblk), 256, 0, s>>>(a, nblk, cnt, pair_start + bld.kvol, pair_cap, pair_start,
+                                                             pair_in, pair_out);
   return hipGetLastError();
 }
 

@@ -33,6 +33,11 @@ hipError_t launch_strided_support(const int32_t* coords, int64_t n, int ndim, in
                                   int64_t* n_out, void* out_table, int64_t out_cap, void* scratch, uint32_t* flags,
                                   hipStream_t s);
 
+size_t generative_scratch_bytes(int64_t n_cand);
+hipError_t launch_generative_support(const int32_t* coords, int64_t n, int ndim, int ksize, int32_t* out_coords,
+                                     int64_t n_out_cap, int64_t* n_out, void* out_table, int64_t out_cap,
+                                     void* scratch, uint32_t* flags, hipStream_t s);
+
 // kmap.hip
 enum RelMode { kModeSubm = 0, kModeDown = 1, kModeUp = 2 };
 
@@ -52,8 +57,10 @@ size_t rel_scratch_bytes(int64_t n_dest_cap, int kvol);
 // n_out_fill (device, may be NULL): receives n_dest_cap (the submanifold output count)
 hipError_t launch_rel_build(const RelBuild& b, const ts_rel& rel, bool natural, int64_t* n_out_fill, hipStream_t s);
 size_t pairs_scratch_bytes(int64_t n_dest_cap, int kvol);
-hipError_t launch_pairs_build(const RelBuild& b, const ts_rel& rel, int64_t* pair_start, int32_t* pair_in,
-                              int32_t* pair_out, void* scratch, hipStream_t s);
+// Pair lists of capacity pair_cap: entries past it are dropped and the
+// starts clamped to it, so a short capacity can never write out of bounds.
+hipError_t launch_pairs_build(const RelBuild& b, const ts_rel& rel, int64_t pair_cap, int64_t* pair_start,
+                              int32_t* pair_in, int32_t* pair_out, void* scratch, hipStream_t s);
 
 // conv.hip
 struct ConvArgs {

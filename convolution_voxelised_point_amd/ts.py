@@ -29,7 +29,7 @@ TS_OK, TS_ERR_INVALID_ARG, TS_ERR_UNSUPPORTED, TS_ERR_HIP = 0, 1, 2, 3
 TS_F32, TS_F16, TS_BF16 = 0, 1, 2
 TS_DATAFLOW_AUTO, TS_DATAFLOW_IMPLICIT_GEMM, TS_DATAFLOW_GATHER_SCATTER = 0, 1, 2
 TS_FLAG_DUP, TS_FLAG_RANGE, TS_FLAG_FULL = 1, 2, 4
-TS_KMAP_PAIRS, TS_KMAP_BWD, TS_KMAP_NATURAL = 1, 2, 4
+TS_KMAP_PAIRS, TS_KMAP_BWD, TS_KMAP_NATURAL, TS_KMAP_TARGET = 1, 2, 4, 8
 TS_OP_FWD, TS_OP_DGRAD, TS_OP_WGRAD = 0, 1, 2
 TS_TILE, TS_MAX_KVOL = 16, 64
 
@@ -67,6 +67,9 @@ _lib_hash_build = _sig("ts_hash_build", _i32, [_vp, _i64, _i32, _vp, _i64, _vp, 
 _lib_hash_query = _sig("ts_hash_query", _i32, [_vp, _i64, _i32, _vp, _i64, _vp, _vp])
 _lib_support_scratch_bytes = _sig("ts_support_scratch_bytes", _sz, [_i64])
 _lib_strided_support = _sig("ts_strided_support", _i32, [_vp, _i64, _i32, _i32, _vp, _vp, _vp, _i64, _vp, _sz, _vp, _vp])
+_lib_generative_scratch_bytes = _sig("ts_generative_scratch_bytes", _sz, [_i64, _i32, _i32])
+_lib_generative_support = _sig("ts_generative_support", _i32,
+                               [_vp, _i64, _i32, _i32, _vp, _i64, _vp, _vp, _i64, _vp, _sz, _vp, _vp])
 _lib_kmap_bytes = _sig("ts_kmap_bytes", _sz, [_i64, _i64, _i32, _i32, _i32, _u32])
 _lib_kmap_build = _sig("ts_kmap_build", _i32, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _i64, _i32, _i32, _i32, _u32,
                                                _vp, _sz, _P, _vp])
@@ -76,13 +79,17 @@ _lib_subm_conv_fwd = _sig("ts_subm_conv_fwd", _i32, [_P, _vp, _i32, _vp, _i32, _
 _lib_conv_fwd_strided = _sig("ts_conv_fwd_strided", _i32,
                              [_vp, _i64, _i32, _vp, _i64, _i32, _i32, _u32, _vp, _vp, _vp, _i64, _vp, _vp, _sz, _P,
                               _vp, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _vp, _sz, _vp])
+_lib_conv_fwd_generative = _sig("ts_conv_fwd_generative", _i32,
+                                [_vp, _i64, _i32, _vp, _i64, _i32, _u32, _vp, _i64, _vp, _vp, _i64, _vp, _vp, _sz, _P,
+                                 _vp, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _vp, _sz, _vp])
 _lib_conv_bwd_dgrad = _sig("ts_conv_bwd_dgrad", _i32, [_P, _vp, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _vp, _sz, _vp])
 _lib_conv_bwd_wgrad = _sig("ts_conv_bwd_wgrad", _i32, [_P, _vp, _i32, _vp, _i32, _i32, _vp, _vp, _sz, _vp])
 
 EXPORTED = ["ts_status_string", "ts_version", "ts_hash_capacity", "ts_hash_table_bytes", "ts_hash_build",
-            "ts_hash_query", "ts_support_scratch_bytes", "ts_strided_support", "ts_kmap_bytes", "ts_kmap_build",
-            "ts_conv_workspace_bytes", "ts_conv_fwd", "ts_subm_conv_fwd", "ts_conv_fwd_strided",
-            "ts_conv_bwd_dgrad", "ts_conv_bwd_wgrad"]
+            "ts_hash_query", "ts_support_scratch_bytes", "ts_strided_support", "ts_generative_scratch_bytes",
+            "ts_generative_support", "ts_kmap_bytes", "ts_kmap_build", "ts_conv_workspace_bytes", "ts_conv_fwd",
+            "ts_subm_conv_fwd", "ts_conv_fwd_strided", "ts_conv_fwd_generative", "ts_conv_bwd_dgrad",
+            "ts_conv_bwd_wgrad"]
 
 
 class TsError(RuntimeError):
@@ -152,6 +159,17 @@ def ts_strided_support(in_coords, stride, out_coords, n_out, out_table, out_cap,
                                 _stream(stream)), "ts_strided_support")
 
 
+def ts_generative_scratch_bytes(n_in: int, ndim: int, ksize: int) -> int:
+    return int(_lib_generative_scratch_bytes(n_in, ndim, ksize))
+
+
+def ts_generative_support(in_coords, ksize, out_coords, n_out, out_table, out_cap, scratch, err_flags=None,
+                          stream=None) -> None:
+    _check(_lib_generative_support(_p(in_coords), in_coords.shape[0], in_coords.shape[1] - 1, ksize, _p(out_coords),
+                                   out_coords.shape[0], _p(n_out), _p(out_table), out_cap, _p(scratch),
+                                   scratch.numel(), _p(err_flags), _stream(stream)), "ts_generative_support")
+
+
 def ts_kmap_bytes(n_in: int, n_out_cap: int, ndim: int, ksize: int, stride: int, flags: int) -> int:
     return int(_lib_kmap_bytes(n_in, n_out_cap, ndim, ksize, stride, flags))
 
@@ -184,6 +202,19 @@ def ts_conv_fwd_strided(in_coords, in_table, in_cap, ksize, stride, kmap_flags, 
                                  _p(err_flags), _p(map_buf), map_buf.numel(), ctypes.byref(kmap), _p(x), x.shape[1],
                                  _p(w), w.shape[2], _p(y), _dt(x), _dt(y), dataflow, _p(ws),
                                  0 if ws is None else ws.numel(), _stream(stream)), "ts_conv_fwd_strided")
+
+
+def ts_conv_fwd_generative(in_coords, in_table, in_cap, ksize, kmap_flags, out_coords, n_out, out_table, out_cap,
+                           err_flags, map_buf, kmap, x, w, y, dataflow=TS_DATAFLOW_AUTO, ws=None,
+                           stream=None) -> None:
+    """out_coords and y have the same row capacity (n_out_cap)."""
+    assert out_coords.shape[0] == y.shape[0]
+    _check(_lib_conv_fwd_generative(_p(in_coords), in_coords.shape[0], in_coords.shape[1] - 1, _p(in_table), in_cap,
+                                    ksize, kmap_flags, _p(out_coords), out_coords.shape[0], _p(n_out),
+                                    _p(out_table), out_cap, _p(err_flags), _p(map_buf), map_buf.numel(),
+                                    ctypes.byref(kmap), _p(x), x.shape[1], _p(w), w.shape[2], _p(y), _dt(x), _dt(y),
+                                    dataflow, _p(ws), 0 if ws is None else ws.numel(), _stream(stream)),
+           "ts_conv_fwd_generative")
 
 
 def ts_conv_bwd_dgrad(kmap, dy, w, dx, dataflow=TS_DATAFLOW_AUTO, ws=None, stream=None) -> None:
@@ -290,10 +321,11 @@ def decode_rel(arrs: dict, kvol: int, transposed: bool = False) -> Tuple[np.ndar
 def build_kmap(coords: torch.Tensor, table: HashTable, ksize: int, stride: int = 1, flags: int = 0,
                out_coords: Optional[torch.Tensor] = None, n_out: Optional[torch.Tensor] = None,
                out_table: Optional[HashTable] = None, stream=None) -> Kmap:
-    """Allocate and build a kernel map (submanifold when stride == 1)."""
+    """Allocate and build a kernel map (submanifold when stride == 1 and
+    TS_KMAP_TARGET is not set; otherwise over out_coords / n_out)."""
     ndim = coords.shape[1] - 1
     n_in = coords.shape[0]
-    n_out_cap = n_in if stride == 1 else out_coords.shape[0]
+    n_out_cap = n_in if (stride == 1 and not flags & TS_KMAP_TARGET) else out_coords.shape[0]
     nbytes = ts_kmap_bytes(n_in, n_out_cap, ndim, ksize, stride, flags)
     if nbytes == 0:
         raise TsError(TS_ERR_INVALID_ARG, "ts_kmap_bytes")
@@ -316,6 +348,25 @@ def strided_support(coords: torch.Tensor, stride: int, rsv_ratio: float = 2.0, e
     return out, n_out, table
 
 
+def generative_support(coords: torch.Tensor, ksize: int, n_out_cap: Optional[int] = None, out_cap: Optional[int] = None,
+                       err_flags=None, stream=None):
+    """(out_coords [capacity n_out_cap, default n_in * ksize^ndim], n_out
+    device scalar, out table of out_cap block slots, default as for n_out_cap
+    rows at the reserve ratio 2)."""
+    n, ndim = coords.shape[0], coords.shape[1] - 1
+    if n_out_cap is None:
+        n_out_cap = n * ksize ** ndim
+    out = torch.zeros((n_out_cap, ndim + 1), dtype=torch.int32, device=coords.device)
+    n_out = torch.zeros(1, dtype=torch.int64, device=coords.device)
+    table = HashTable(out, 2.0, build=False)
+    if out_cap is not None:
+        table.cap = out_cap
+        table.buf = _zero_bytes(ts_hash_table_bytes(out_cap), coords.device)
+    scratch = _bytes(ts_generative_scratch_bytes(n, ndim, ksize), coords.device)
+    ts_generative_support(coords, ksize, out, n_out, table.buf, table.cap, scratch, err_flags, stream)
+    return out, n_out, table
+
+
 def workspace(kmap: Kmap, cin: int, cout: int, op: int, dtype: torch.dtype, dataflow: int = TS_DATAFLOW_AUTO):
     n = ts_conv_workspace_bytes(kmap.s, cin, cout, op, _DT[dtype], dataflow)
     return _bytes(n, kmap.buf.device) if n > 0 else None
@@ -327,7 +378,7 @@ def conv_fwd(kmap: Kmap, x: torch.Tensor, w: torch.Tensor, out_dtype=None, dataf
     y = torch.empty((kmap.s.n_out_cap, w.shape[2]), dtype=out_dtype, device=x.device)
     if ws is None:
         ws = workspace(kmap, w.shape[1], w.shape[2], TS_OP_FWD, x.dtype, dataflow)
-    ts_conv_fwd(kmap.s, x, w, y, dataflow, ws, stream, subm=kmap.s.stride == 1)
+    ts_conv_fwd(kmap.s, x, w, y, dataflow, ws, stream, subm=kmap.s.stride == 1 and not kmap.s.flags & TS_KMAP_TARGET)
     return y
 
 

@@ -76,8 +76,9 @@ typedef enum ts_dataflow {
 
 /* kernel-map build options (bit set) */
 #define TS_KMAP_PAIRS 1u   /* also build per-offset (in, out) pair lists            */
-#define TS_KMAP_BWD 2u     /* strided: also build the transposed relation (dgrad)   */
+#define TS_KMAP_BWD 2u     /* strided/target: also build the transposed relation    */
 #define TS_KMAP_NATURAL 4u /* keep destination rows in index order inside tiles    */
+#define TS_KMAP_TARGET 8u  /* outputs are caller-given coordinates (TargetConv3d)  */
 
 #define TS_TILE 16     /* destination rows per tile */
 #define TS_MAX_KVOL 64 /* largest supported K^D     */
@@ -147,13 +148,41 @@ ts_status ts_strided_support(const int32_t* in_coords, int64_t n_in, int ndim, i
                              hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Generated support of a stride-1 convolution (torch-lattice migration page,
+ * table "What is intentionally different", row on convolution intent: a
+ * Conv3d generates its output support, unlike SubmConv3d).
+ *
+ * The outputs are every site q = c_i - delta_o that an input row i reaches
+ * through a kernel offset o -- the sites whose window holds at least one
+ * input -- each once, in order of first occurrence over (i ascending, then o
+ * ascending).  Rows repeating an earlier coordinate add nothing; an
+ * out-of-range input raises TS_FLAG_RANGE; sites outside the packable range
+ * are not generated.  out_coords (device int32, n_out_cap rows) receives the
+ * sites and *n_out (device int64) their count, clamped to n_out_cap: sites
+ * past the capacity are dropped and raise TS_FLAG_FULL (n_in * ksize^ndim
+ * rows always suffice).  out_table (out_cap a power of two, zero-filled
+ * before its first use like any table buffer; a full table raises
+ * TS_FLAG_FULL) maps each site to its output row.  `scratch` (device) needs
+ * ts_generative_scratch_bytes(n_in, ndim, ksize).  The map over these outputs
+ * is a TS_KMAP_TARGET map at stride 1, with out_table for its transposed
+ * relation.
+ * ---------------------------------------------------------------------- */
+size_t ts_generative_scratch_bytes(int64_t n_in, int ndim, int ksize);
+ts_status ts_generative_support(const int32_t* in_coords, int64_t n_in, int ndim, int ksize,
+                                int32_t* out_coords, int64_t n_out_cap, int64_t* n_out,
+                                void* out_table, int64_t out_cap, void* scratch, size_t scratch_bytes,
+                                uint32_t* err_flags, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Kernel map (the "kernel-map construction" of the page's section "Sparse
  * tensor expectations"): for every output row j and offset o, the input row
  * i at q_j + delta_o (stride 1) or s q_j + delta_o (stride s), as a relation
  * between destination rows and source rows:
  *
  *   nbr[d*kvol + o] is the source row of destination row d at offset o, or
- *   -1; row_mask[d] has bit o set exactly when nbr[d*kvol + o] >= 0.
+ *   -1; row_mask[d] has bit o set exactly when nbr[d*kvol + o] >= 0.  Both
+ *   cover the destination rows below the device count n_dest; past it,
+ *   row_mask is 0 and nbr is left unwritten.
  *   Destination rows are grouped in tiles of TS_TILE: tile_rows[t*TS_TILE + r]
  *   is the destination row in slot r of tile t (-1 for padding; every row
  *   appears once), and tile_mask[t] is the OR of its rows' masks, so the
@@ -181,7 +210,7 @@ typedef struct ts_kmap {
   int64_t n_out_cap;   /* output rows, upper bound                                 */
   int64_t* n_out;      /* device int64: output rows                                */
   ts_rel fwd;          /* destination = output rows, source = input rows           */
-  ts_rel bwd;          /* strided with TS_KMAP_BWD: destination = input rows       */
+  ts_rel bwd;          /* strided/target with TS_KMAP_BWD: destination = input rows */
   int64_t pair_cap;    /* capacity of the pair lists                               */
   int64_t* pair_start; /* device [kvol+1]: offset o owns pairs [start[o], start[o+1]) */
   int32_t* pair_in;    /* device [pair_cap] input row of each pair, output-row order */
@@ -196,10 +225,23 @@ size_t ts_kmap_bytes(int64_t n_in, int64_t n_out_cap, int ndim, int ksize, int s
 /* Build the kernel map into `buf` (device, ts_kmap_bytes(...) bytes) and fill
  * the host struct *map with pointers into it.
  *   stride == 1 (submanifold): ksize odd; the outputs are the inputs, so
- *     out_coords / n_out / out_table may be NULL and n_out_cap = n_in.
+ *     out_coords / n_out / out_table may be NULL and n_out_cap = n_in.  An
+ *     output row takes part only if it owns its coordinate in in_table.
  *   stride > 1: out_coords (device, n_out_cap rows), n_out (device int64)
  *     and, with TS_KMAP_BWD, out_table (out_cap slots) describe the output
- *     support, normally from ts_strided_support.
+ *     support, normally from ts_strided_support (distinct coordinates).
+ *   TS_KMAP_TARGET (convolution at caller-given output coordinates, the
+ *     TargetConv3d of the torch-lattice migration page, tables "What is
+ *     intentionally different" and "Convolution mapping"): out_coords /
+ *     n_out_cap / n_out are the caller's targets, which need not be inputs
+ *     and may repeat; output row j takes the input at s*q_j + delta_o (s = 1
+ *     included) for every offset o, with any ksize.  A target row whose
+ *     coordinate is outside the packable range takes no inputs.  Repeated
+ *     targets are fine for the forward pass and wgrad; dgrad needs distinct
+ *     targets (its scatter into input rows assumes each input meets an
+ *     offset once), and its transposed relation (TS_KMAP_BWD) needs
+ *     out_table = the ts_hash_build table of the targets (or the table
+ *     ts_generative_support leaves).
  * in_table / in_cap is the ts_hash_build table of the inputs. */
 ts_status ts_kmap_build(const int32_t* in_coords, int64_t n_in, const void* in_table, int64_t in_cap,
                         const int32_t* out_coords, int64_t n_out_cap, const int64_t* n_out,
@@ -228,7 +270,7 @@ ts_status ts_conv_fwd(const ts_kmap* map, const void* x, int cin, const void* w,
                       size_t ws_bytes, hipStream_t stream);
 
 /* Submanifold SubmConv3d / SubmConv2d forward: ts_conv_fwd on a stride-1 map
- * (output rows = input rows). */
+ * (output rows = input rows); a TS_KMAP_TARGET map is rejected. */
 ts_status ts_subm_conv_fwd(const ts_kmap* map, const void* x, int cin, const void* w, int cout, void* y,
                            ts_dtype in_dtype, ts_dtype out_dtype, ts_dataflow dataflow, void* ws,
                            size_t ws_bytes, hipStream_t stream);
@@ -245,6 +287,20 @@ ts_status ts_conv_fwd_strided(const int32_t* in_coords, int64_t n_in, int ndim, 
                               const void* x, int cin, const void* w, int cout, void* y,
                               ts_dtype in_dtype, ts_dtype out_dtype, ts_dataflow dataflow, void* ws,
                               size_t ws_bytes, hipStream_t stream);
+
+/* Generative stride-1 Conv3d / Conv2d forward, support generation included:
+ * runs ts_generative_support, ts_kmap_build (kmap_flags | TS_KMAP_TARGET,
+ * stride 1) and ts_conv_fwd in order.  `map_buf` holds
+ * ts_kmap_bytes(n_in, n_out_cap, ndim, ksize, 1, kmap_flags | TS_KMAP_TARGET)
+ * + ts_generative_scratch_bytes(n_in, ndim, ksize) bytes; *map is filled for
+ * the backward pass.  y has n_out_cap rows; rows >= *n_out are not written. */
+ts_status ts_conv_fwd_generative(const int32_t* in_coords, int64_t n_in, int ndim, const void* in_table,
+                                 int64_t in_cap, int ksize, uint32_t kmap_flags, int32_t* out_coords,
+                                 int64_t n_out_cap, int64_t* n_out, void* out_table, int64_t out_cap,
+                                 uint32_t* err_flags, void* map_buf, size_t map_bytes, ts_kmap* map,
+                                 const void* x, int cin, const void* w, int cout, void* y,
+                                 ts_dtype in_dtype, ts_dtype out_dtype, ts_dataflow dataflow, void* ws,
+                                 size_t ws_bytes, hipStream_t stream);
 
 /* dx[n_in][cin] = sum over triples (i, j, o) of dy[j] . W[o]^T.  Strided
  * maps need TS_KMAP_BWD (implicit GEMM) or TS_KMAP_PAIRS (gather-scatter). */
