@@ -8,8 +8,9 @@ JSON line reports map-valid TFLOP/s of that step (2 * pairs * Cin * Cout per
 replay time), the per-stage times of eager launches taken with HIP events on
 the launch stream, the roofline position of the dominant kernel, and the CPU
 oracle timed on this host.  The other workloads (strided 64 -> 128 downsampling,
-the 2-D pixel tracks, the bf16 128-channel training step) are measured the
-same way and reported under "secondary".
+the generative stride-1 convolution of the scene, the 2-D pixel tracks, the
+bf16 128-channel training step) are measured the same way and reported under
+"secondary".
 
 The ``setup_*`` functions below fix each workload's launch configuration;
 the full-size parity tests run the same functions.
@@ -20,7 +21,8 @@ write that evicts the caches.  A copy of the ring scan with its rows in
 random order is measured as a secondary workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
-                       [--only lidar|lidar_shuffled|down|pixels|train] [--copy-calib MB]
+                       [--only lidar|lidar_shuffled|down|generative|pixels|train]
+                       [--copy-calib MB]
 """
 from __future__ import annotations
 
@@ -285,6 +287,60 @@ def setup_pixels(ts, w, dataflow=None, kmap_flags=None) -> Step:
                 kmap=kmap, x=x, w1=w1, w2=w2, y1=y1, y2=y2, flags=flags, n=n, kvol=9)
 
 
+def setup_generative(ts, w, kmap_flags=None) -> Step:
+    """Generative stride-1 Conv3d k3 on the ring scan: hash of the inputs, the
+    generated support (every site some input reaches), the target map over
+    it and the forward.  The output row count is data-dependent; it is taken
+    from one generation at set-up and sizes the buffers (the timed steps then
+    regenerate it every time).  The target map is sorted by offset mask: the
+    rows of a generated support use 1.6 offsets each, but 16 consecutive
+    rows in row order touch 18 different ones."""
+    kmap_flags = 0 if kmap_flags is None else kmap_flags
+    kflags = kmap_flags | ts.TS_KMAP_TARGET
+    dev = torch.device("cuda")
+    coords = torch.from_numpy(w.coords).to(dev)
+    x, wt = w.x.to(dev), w.w.to(dev)
+    n, nd, k = coords.shape[0], w.ndim, w.ksize
+    flags = torch.zeros(1, dtype=torch.int32, device=dev)
+    table = ts.HashTable(coords, 2.0, build=False)
+    ts.ts_hash_build(coords, table.buf, table.cap, flags)
+    out0, n_out0, _ = ts.generative_support(coords, k, err_flags=flags)
+    m = int(n_out0.item())
+    del out0
+    out = torch.zeros((m, nd + 1), dtype=torch.int32, device=dev)
+    n_out = torch.zeros(1, dtype=torch.int64, device=dev)
+    out_table = ts.HashTable.with_capacity(nd, ts.generative_table_capacity(n), dev)
+    scratch = torch.empty(ts.ts_generative_scratch_bytes(n, nd, k), dtype=torch.uint8, device=dev)
+    kbuf = torch.empty(ts.ts_kmap_bytes(n, m, nd, k, 1, kflags), dtype=torch.uint8, device=dev)
+    km = ts.TsKmap()
+    y = torch.empty((m, w.cout), dtype=x.dtype, device=dev)
+
+    def hash_build():
+        ts.ts_hash_build(coords, table.buf, table.cap, flags)
+
+    def support():
+        ts.ts_generative_support(coords, k, out, n_out, out_table.buf, out_table.cap, scratch, flags)
+
+    def kmap_build():
+        ts.ts_kmap_build(coords, table.buf, table.cap, out, m, n_out, out_table.buf, out_table.cap, nd, k, 1, kflags,
+                         kbuf, km)
+
+    hash_build()
+    support()
+    kmap_build()
+    torch.cuda.synchronize()
+    wsb = ts.ts_conv_workspace_bytes(km, w.cin, w.cout, ts.TS_OP_FWD, ts._DT[x.dtype], ts.TS_DATAFLOW_AUTO)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+
+    def conv():
+        ts.ts_conv_fwd(km, x, wt, y, ts.TS_DATAFLOW_AUTO, ws)
+
+    kmap = ts.Kmap(km, kbuf, keep=(coords, table, out, n_out, out_table))
+    return Step(fns=[hash_build, support, kmap_build, conv], names=["hash", "support", "kmap", "conv"], coords=coords,
+                table=table, out=out, n_out=n_out, out_table=out_table, kmap=kmap, x=x, w=wt, y=y, flags=flags, n=n,
+                m=m, kvol=k ** nd)
+
+
 def setup_train(ts, w) -> Step:
     """bf16 128 -> 128 training step: hash, kernel map (+pairs), forward,
     dgrad (mirrored offsets), wgrad (fp32 dW)."""
@@ -383,6 +439,20 @@ def measure_lidar_shuffled(ts, steps, warmup):
                       "tflops_step": 2.0 * P * w.cin * w.cout / (ms * 1e-3) / 1e12}
         del s
     return out
+
+
+def measure_generative(ts, steps, warmup):
+    w = synth.make("lidar")
+    s = setup_generative(ts, w)
+    ms_eager, st = run_steps(s.fns, s.names, steps, warmup)
+    ms, _ = run_graph(capture(s.fns), steps, warmup)
+    P = popcount_sum(s.kmap.rel_arrays("fwd")["row_mask"][:s.m], 27)
+    flop = 2.0 * P * w.cin * w.cout
+    conv_bytes = s.n * w.cin * 2 + 27 * w.cin * w.cout * 2 + P * 4 + s.m * 4 + s.m * w.cout * 2
+    return {"workload": "generative", "n_in": s.n, "n_out": s.m, "pairs": P, "ms_per_step": ms,
+            "ms_per_step_eager": ms_eager, "stages_us": {k: round(v, 3) for k, v in st.items()},
+            "tflops_step": flop / (ms * 1e-3) / 1e12,
+            "conv_gbs": conv_bytes / (st["conv"] * 1e-6) / 1e9, "err_flags": int(s.flags.item())}
 
 
 def measure_down(ts, steps, warmup):
@@ -510,7 +580,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--only", default=None,
-                    help="measure one workload (lidar, lidar_shuffled, down, pixels, train)")
+                    help="measure one workload (lidar, lidar_shuffled, down, generative, pixels, train)")
     ap.add_argument("--copy-calib", type=int, default=0, help="run only a plain copy of this many MiB")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -524,14 +594,14 @@ def main():
 
     torch.cuda.synchronize()
     if args.only and args.only != "lidar":
-        fn = {"lidar_shuffled": measure_lidar_shuffled, "down": measure_down, "pixels": measure_pixels,
-              "train": measure_train}[args.only]
+        fn = {"lidar_shuffled": measure_lidar_shuffled, "down": measure_down, "generative": measure_generative,
+              "pixels": measure_pixels, "train": measure_train}[args.only]
         print(json.dumps(fn(ts, args.steps, args.warmup)))
         return
     w, r = measure_lidar(ts, args.steps, args.warmup)
     secondary = []
     if args.only is None:
-        for fn in (measure_lidar_shuffled, measure_down, measure_pixels, measure_train):
+        for fn in (measure_lidar_shuffled, measure_down, measure_generative, measure_pixels, measure_train):
             secondary.append(fn(ts, args.steps, args.warmup))
     value = r["flop_per_step"] / (r["ms_per_step"] * 1e-3) / 1e12
     conv_s = r["stages_us"]["conv"] * 1e-6

@@ -248,6 +248,14 @@ class HashTable:
         if build:
             ts_hash_build(coords, self.buf, self.cap, err_flags, stream)
 
+    @classmethod
+    def with_capacity(cls, ndim: int, cap: int, device) -> "HashTable":
+        """An empty (zero-filled) table of `cap` block slots."""
+        t = cls.__new__(cls)
+        t.ndim, t.cap = ndim, cap
+        t.buf = _zero_bytes(ts_hash_table_bytes(cap), device)
+        return t
+
     def query(self, q: torch.Tensor, stream=None) -> torch.Tensor:
         rows = torch.empty(q.shape[0], dtype=torch.int32, device=q.device)
         ts_hash_query(self.buf, self.cap, q, rows, stream)
@@ -348,20 +356,24 @@ def strided_support(coords: torch.Tensor, stride: int, rsv_ratio: float = 2.0, e
     return out, n_out, table
 
 
+def generative_table_capacity(n_in: int) -> int:
+    """Block slots for the table of a generated support: four per input row
+    (a site grid of surfaces spans about 1.3 blocks per input row for a 3^3
+    kernel); a support that needs more raises TS_FLAG_FULL."""
+    return ts_hash_capacity(n_in, 4.0)
+
+
 def generative_support(coords: torch.Tensor, ksize: int, n_out_cap: Optional[int] = None, out_cap: Optional[int] = None,
                        err_flags=None, stream=None):
     """(out_coords [capacity n_out_cap, default n_in * ksize^ndim], n_out
-    device scalar, out table of out_cap block slots, default as for n_out_cap
-    rows at the reserve ratio 2)."""
+    device scalar, out table of out_cap block slots, default
+    generative_table_capacity(n_in))."""
     n, ndim = coords.shape[0], coords.shape[1] - 1
     if n_out_cap is None:
         n_out_cap = n * ksize ** ndim
     out = torch.zeros((n_out_cap, ndim + 1), dtype=torch.int32, device=coords.device)
     n_out = torch.zeros(1, dtype=torch.int64, device=coords.device)
-    table = HashTable(out, 2.0, build=False)
-    if out_cap is not None:
-        table.cap = out_cap
-        table.buf = _zero_bytes(ts_hash_table_bytes(out_cap), coords.device)
+    table = HashTable.with_capacity(ndim, generative_table_capacity(n) if out_cap is None else out_cap, coords.device)
     scratch = _bytes(ts_generative_scratch_bytes(n, ndim, ksize), coords.device)
     ts_generative_support(coords, ksize, out, n_out, table.buf, table.cap, scratch, err_flags, stream)
     return out, n_out, table

@@ -108,6 +108,27 @@ def test_full_down_strided_f16(ts):
     assert_feature_close(s.y[torch.from_numpy(rows).cuda()], ref, torch.float16, "down fwd (fp16 out)")
 
 
+def test_full_generative_f16(ts):
+    """Generative stride-1 Conv3d k3 on the ring scan: the 1.77M generated
+    sites in first-occurrence order and the target map bit-exact, features on
+    sampled rows."""
+    w = synth.make("lidar")
+    s = bench.setup_generative(ts, w)
+    s.run_once()
+    assert int(s.flags.item()) == 0
+    oc = oracle.generative_support(w.coords, 3)
+    assert int(s.n_out.item()) == s.m == oc.shape[0]
+    assert np.array_equal(s.out.cpu().numpy(), oc)
+    rows = s.out_table.query(s.out).cpu().numpy()
+    assert np.array_equal(rows, np.arange(s.m, dtype=np.int32))
+    tr = oracle.kmap(w.coords, oc, 3, 1, target=True)
+    assert len(tr[0]) == 27 * w.n  # every input reaches a generated site through every offset
+    check_triples(s.kmap, tr, 27, "generative")
+    pick = sample_rows(s.m, 52)
+    ref = oracle.conv_fwd(restrict(tr, pick, 1), w.x, w.w, s.m)[pick]
+    assert_feature_close(s.y[torch.from_numpy(pick).cuda()], ref, torch.float16, "generative fwd (fp16 out)")
+
+
 @pytest.mark.parametrize("dataflow", ["auto", "gather_scatter"])
 def test_full_pixels_two_layers(ts, dataflow):
     w = synth.make("pixels")
