@@ -157,3 +157,79 @@ def test_workspace_sizes(ts):
     assert ts._lib_conv_workspace_bytes(ref, 16, 16, ts.TS_OP_FWD, ts.TS_F32, 0) == 0
     assert ts._lib_conv_workspace_bytes(ref, 64, 64, ts.TS_OP_FWD, ts.TS_F16, 2) >= 1000 * 64 * 4
     assert ts._lib_conv_workspace_bytes(ref, 64, 64, ts.TS_OP_WGRAD, ts.TS_F16, 0) >= 27 * 64 * 64 * 4
+
+
+def test_target_and_generative_sizes(ts):
+    T = ts.TS_KMAP_TARGET
+    base = ts.ts_kmap_bytes(100, 100, 3, 3, 1, 0)
+    assert ts.ts_kmap_bytes(100, 300, 3, 3, 1, T) > base                   # sized by the target count
+    assert ts.ts_kmap_bytes(100, 300, 3, 3, 1, T | ts.TS_KMAP_BWD) > ts.ts_kmap_bytes(100, 300, 3, 3, 1, T)
+    assert ts.ts_kmap_bytes(100, 100, 3, 3, 1, ts.TS_KMAP_BWD) == base     # a submanifold map has no own bwd
+    # a target map's pair lists hold kvol per target (targets may repeat)
+    p_t = ts.ts_kmap_bytes(100, 100, 3, 2, 2, T | ts.TS_KMAP_PAIRS) - ts.ts_kmap_bytes(100, 100, 3, 2, 2, T)
+    p_s = ts.ts_kmap_bytes(100, 100, 3, 2, 2, ts.TS_KMAP_PAIRS) - ts.ts_kmap_bytes(100, 100, 3, 2, 2, 0)
+    assert p_t >= p_s + (100 * 8 - 100) * 8
+    assert ts.ts_generative_scratch_bytes(100, 3, 3) >= 3 * 100 * 27 * 4
+    assert ts.ts_generative_scratch_bytes(-1, 3, 3) == 0
+    assert ts.ts_generative_scratch_bytes(10, 3, 5) == 0                   # 125 offsets
+    assert ts.ts_generative_scratch_bytes(10, 4, 3) == 0
+
+
+def test_target_map_rejects(ts):
+    L = ts._lib_kmap_build
+    km = ts.TsKmap()
+    T = ts.TS_KMAP_TARGET
+    need = ts.ts_kmap_bytes(100, 50, 3, 3, 1, T | ts.TS_KMAP_BWD)
+    # no target coordinates / count
+    assert L(FAKE, 100, FAKE, 256, None, 50, FAKE, None, 0, 3, 3, 1, T, FAKE, need, ctypes.byref(km), None) \
+        == ts.TS_ERR_INVALID_ARG
+    assert L(FAKE, 100, FAKE, 256, FAKE, 50, None, None, 0, 3, 3, 1, T, FAKE, need, ctypes.byref(km), None) \
+        == ts.TS_ERR_INVALID_ARG
+    # the transposed relation needs the targets' table
+    assert L(FAKE, 100, FAKE, 256, FAKE, 50, FAKE, None, 0, 3, 3, 1, T | ts.TS_KMAP_BWD, FAKE, need,
+             ctypes.byref(km), None) == ts.TS_ERR_INVALID_ARG
+    # a short buffer
+    assert L(FAKE, 100, FAKE, 256, FAKE, 50, FAKE, FAKE, 256, 3, 3, 1, T | ts.TS_KMAP_BWD, FAKE, need - 1,
+             ctypes.byref(km), None) == ts.TS_ERR_INVALID_ARG
+    # a target map is not a submanifold map
+    km.kvol, km.stride, km.flags = 27, 1, T
+    km.n_in = km.n_out_cap = 100
+    km.fwd.tile_mask, km.fwd.n_tiles = 0x2000, 7
+    assert ts._lib_subm_conv_fwd(ctypes.byref(km), FAKE, 16, FAKE, 16, FAKE, 0, 0, 0, None, 0, None) \
+        == ts.TS_ERR_INVALID_ARG
+
+
+def test_generative_rejects(ts):
+    G = ts._lib_generative_support
+    sb = ts.ts_generative_scratch_bytes(100, 3, 3)
+    ok = [FAKE, 100, 3, 3, FAKE, 2700, FAKE, FAKE, 1024, FAKE, sb, None, None]
+
+    def call(i, v):
+        a = list(ok)
+        a[i] = v
+        return G(*a)
+
+    assert call(6, None) == ts.TS_ERR_INVALID_ARG        # n_out
+    assert call(7, None) == ts.TS_ERR_INVALID_ARG        # out_table
+    assert call(8, 1000) == ts.TS_ERR_INVALID_ARG        # out_cap not a power of two
+    assert call(10, sb - 1) == ts.TS_ERR_INVALID_ARG     # short scratch
+    assert call(5, -1) == ts.TS_ERR_INVALID_ARG          # n_out_cap < 0
+    assert call(4, None) == ts.TS_ERR_INVALID_ARG        # no output coordinates
+    assert call(3, 5) == ts.TS_ERR_INVALID_ARG           # 125 offsets
+    assert call(0, None) == ts.TS_ERR_INVALID_ARG        # no input coordinates
+    C = ts._lib_conv_fwd_generative
+    kb = ts.ts_kmap_bytes(100, 2700, 3, 3, 1, ts.TS_KMAP_TARGET)
+    km = ts.TsKmap()
+    good = [FAKE, 100, 3, FAKE, 256, 3, 0, FAKE, 2700, FAKE, FAKE, 1024, None, FAKE, kb + sb, ctypes.byref(km),
+            FAKE, 64, FAKE, 64, FAKE, ts.TS_F16, ts.TS_F16, 0, FAKE, 1 << 30, None]
+
+    def conv(i, v):
+        a = list(good)
+        a[i] = v
+        return C(*a)
+
+    assert conv(14, kb + sb - 1) == ts.TS_ERR_INVALID_ARG    # short map buffer
+    assert conv(17, 0) == ts.TS_ERR_INVALID_ARG              # cin 0
+    assert conv(22, ts.TS_BF16) == ts.TS_ERR_UNSUPPORTED     # f16 in, bf16 out
+    assert conv(23, ts.TS_DATAFLOW_GATHER_SCATTER) == ts.TS_ERR_INVALID_ARG   # no pair lists
+    assert conv(20, None) == ts.TS_ERR_INVALID_ARG           # null y
