@@ -47,6 +47,10 @@ def lib():
         L.oracle_strided_support.restype = i64
         L.oracle_generative_support.argtypes = [p, i64, i32, i32, p, i64]
         L.oracle_generative_support.restype = i64
+        L.oracle_transposed_support.argtypes = [p, i64, i32, i32, i32, p, i64]
+        L.oracle_transposed_support.restype = i64
+        L.oracle_kmap_transposed.argtypes = [p, i64, p, i64, i32, i32, i32, p, p, p, i64]
+        L.oracle_kmap_transposed.restype = i64
         L.oracle_kmap.argtypes = [p, i64, p, i64, i32, i32, i32, i32, p, p, p, i64]
         L.oracle_kmap.restype = i64
         L.oracle_conv_fwd.argtypes = [p, p, p, i64, p, i32, p, i32, p, i64]
@@ -109,6 +113,43 @@ def generative_support(coords, ksize: int) -> np.ndarray:
     n_out = lib().oracle_generative_support(_ptr(c), c.shape[0], ndim, ksize, _ptr(out), cap)
     assert n_out <= cap
     return out[:n_out].copy()
+
+
+def transposed_support(coords, ksize: int, stride: int) -> np.ndarray:
+    """Output coordinates a transposed convolution of stride s generates:
+    every site s*c_j + delta_o, first-occurrence order over (input row,
+    offset)."""
+    c = _coords(coords)
+    ndim = c.shape[1] - 1
+    cap = max(1, c.shape[0] * ksize ** ndim)
+    out = np.empty((cap, ndim + 1), np.int32)
+    n_out = lib().oracle_transposed_support(_ptr(c), c.shape[0], ndim, ksize, stride, _ptr(out), cap)
+    assert n_out <= cap
+    return out[:n_out].copy()
+
+
+def kmap_transposed(in_coords, out_coords, ksize: int, stride: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Triples (coarse input row, fine output row, offset) of the transposed
+    relation: p_out = stride * q_in + delta_offset."""
+    ci, co = _coords(in_coords), _coords(out_coords)
+    ndim = ci.shape[1] - 1
+    cap = max(1, co.shape[0] * ksize ** ndim)
+    t_in = np.empty(cap, np.int32)
+    t_out = np.empty(cap, np.int32)
+    t_off = np.empty(cap, np.int32)
+    n = lib().oracle_kmap_transposed(_ptr(ci), ci.shape[0], _ptr(co), co.shape[0], ndim, ksize, stride,
+                                     _ptr(t_in), _ptr(t_out), _ptr(t_off), cap)
+    assert n <= cap
+    return t_in[:n].copy(), t_out[:n].copy(), t_off[:n].copy()
+
+
+def conv_transpose(triples, x, w, n_dest: int) -> np.ndarray:
+    """ConvTranspose over an existing relation (in, out, offset): the output
+    is indexed by the relation's input rows, y[in] = sum x[out] . w[offset]
+    with w[kvol][C of x][C of y] -- the forward formula over the relation read
+    the other way."""
+    t_in, t_out, t_off = triples
+    return conv_fwd((t_out, t_in, t_off), x, w, n_dest)
 
 
 def kmap(in_coords, out_coords, ksize: int, stride: int = 1,

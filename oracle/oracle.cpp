@@ -18,6 +18,9 @@
 //     intent);
 //   * TargetConv3d computes at output coordinates the caller gives (same
 //     table, and the "Convolution mapping" table);
+//   * a transposed convolution either reuses an existing relation
+//     (ConvTranspose3d) or generates its output support
+//     (GenerativeConvTranspose3d) ("Convolution mapping" table);
 //   * every dataflow must give the same result for a fixed relation
 //     (input row, output row, kernel offset) and weight tensor.
 //
@@ -40,6 +43,10 @@
 //     generative stride 1: outputs are every q = c_i - delta (the sites some
 //     input reaches), in first-occurrence order over (i, then offset), and
 //     are then used as targets;
+//     transposed: the relation of a stride-s convolution read the other way
+//     (fine output p takes coarse input q where p = s*q + delta); its
+//     generated support is every s*c_j + delta, first occurrence over
+//     (j, then offset); the contraction over it is the forward formula;
 //   * cross-correlation (no kernel flip), W laid out [offset][cin][cout];
 //   * all arithmetic in fp64.
 //
@@ -197,6 +204,81 @@ int64_t oracle_generative_support(const int32_t* coords, int64_t n, int ndim, in
     }
   }
   return n_out;
+}
+
+// Generated output set of a transposed convolution of stride s: for each input
+// row j in order that owns its coordinate, and each offset o in order, the
+// site s*c_j + delta_o is appended when first seen; a site outside the
+// coordinate range is skipped.  Writes up to `cap` rows and returns how many
+// sites exist.
+int64_t oracle_transposed_support(const int32_t* coords, int64_t n, int ndim, int ksize, int stride,
+                                  int32_t* out_coords, int64_t cap) {
+  Map owner = build_map(coords, n, ndim, nullptr);
+  Map seen;
+  const int kvol = ipow(ksize, ndim);
+  int64_t n_out = 0;
+  int64_t delta[3];
+  for (int64_t j = 0; j < n; ++j) {
+    const int32_t* row = coords + j * (ndim + 1);
+    if (!in_range(row, ndim) || lookup(owner, key_of(row, ndim)) != j) continue;
+    for (int o = 0; o < kvol; ++o) {
+      offset_delta(o, ndim, ksize, delta);
+      int32_t p[4] = {row[0], 0, 0, 0};
+      bool ok = true;
+      for (int d = 0; d < ndim; ++d) {
+        const int64_t v = static_cast<int64_t>(stride) * row[d + 1] + delta[d];
+        if (v < -32768 || v > 32767) ok = false;
+        p[d + 1] = static_cast<int32_t>(v);
+      }
+      if (!ok) continue;
+      if (seen.emplace(key_of(p, ndim), n_out).second) {
+        if (n_out < cap)
+          for (int d = 0; d <= ndim; ++d) out_coords[n_out * (ndim + 1) + d] = p[d];
+        ++n_out;
+      }
+    }
+  }
+  return n_out;
+}
+
+// Transposed kernel map: for every fine output row j (in order) that owns its
+// coordinate among the outputs, and every offset o (in order), the coarse
+// input row i with s*q_i + delta_o = p_j, when p_j - delta_o is divisible by
+// s on every axis and that coarse site exists.  Triples (in = coarse row,
+// out = fine row, offset); returns how many exist (writes up to `cap`).
+int64_t oracle_kmap_transposed(const int32_t* in_coords, int64_t n_in, const int32_t* out_coords, int64_t n_out,
+                               int ndim, int ksize, int stride, int32_t* t_in, int32_t* t_out, int32_t* t_off,
+                               int64_t cap) {
+  Map coarse = build_map(in_coords, n_in, ndim, nullptr);
+  Map fine = build_map(out_coords, n_out, ndim, nullptr);
+  const int kvol = ipow(ksize, ndim);
+  int64_t count = 0;
+  int64_t delta[3];
+  for (int64_t j = 0; j < n_out; ++j) {
+    const int32_t* p = out_coords + j * (ndim + 1);
+    if (!in_range(p, ndim) || lookup(fine, key_of(p, ndim)) != j) continue;
+    for (int o = 0; o < kvol; ++o) {
+      offset_delta(o, ndim, ksize, delta);
+      Key q{0, 0, 0, 0};
+      q[0] = p[0];
+      bool whole = true;
+      for (int d = 0; d < ndim; ++d) {
+        const int64_t t = static_cast<int64_t>(p[d + 1]) - delta[d];
+        if (t % stride != 0) whole = false;
+        q[d + 1] = floor_div(t, stride);
+      }
+      if (!whole) continue;
+      const int64_t i = lookup(coarse, q);
+      if (i < 0) continue;
+      if (count < cap) {
+        t_in[count] = static_cast<int32_t>(i);
+        t_out[count] = static_cast<int32_t>(j);
+        t_off[count] = o;
+      }
+      ++count;
+    }
+  }
+  return count;
 }
 
 // Kernel map: for every output row j (in order) and offset o (in order), the
