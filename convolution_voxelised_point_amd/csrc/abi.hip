@@ -44,16 +44,21 @@ struct Carver {
   }
 };
 
-// Pairs a map can hold: at most kvol per output row; with distinct outputs
-// (submanifold, or a support from ts_strided_support) also at most
-// ceil(k/s)^D per input row.  Caller targets may repeat a coordinate, so a
-// target map takes the first bound alone.
-int64_t pair_capacity(int64_t n_in, int64_t n_out_cap, int ndim, int ksize, int stride, bool target) {
+// Pairs a map can hold.  Forward maps: at most kvol per output row; with
+// distinct outputs (submanifold, or a support from ts_strided_support) also
+// at most ceil(k/s)^D per input row.  Caller targets may repeat a coordinate,
+// so a target map takes the first bound alone.  A transposed map swaps the
+// roles: at most ceil(k/s)^D per (fine) output row and kvol per input row.
+int64_t pair_capacity(int64_t n_in, int64_t n_out_cap, int ndim, int ksize, int stride, uint32_t flags) {
   const int kvol = ipow(ksize, ndim);
-  const int per_axis = (ksize + stride - 1) / stride;
+  const int64_t per_row = ipow((ksize + stride - 1) / stride, ndim);
+  if (flags & TS_KMAP_TRANSPOSED) {
+    const int64_t a = n_out_cap * per_row, b = n_in * kvol;
+    return a < b ? a : b;
+  }
   const int64_t a = n_out_cap * kvol;
-  const int64_t b = n_in * ipow(per_axis, ndim);
-  return (target || a < b) ? a : b;
+  const int64_t b = n_in * per_row;
+  return ((flags & TS_KMAP_TARGET) || a < b) ? a : b;
 }
 
 void carve_rel(Carver& c, ts_rel* r, int64_t n_dest_cap, int kvol) {
@@ -78,7 +83,7 @@ size_t layout_kmap(char* base, ts_kmap* m, int64_t n_in, int64_t n_out_cap, int 
   m->flags = flags;
   // a target map's outputs are not its inputs, so its transposed relation is
   // a map of its own, as for a strided one
-  const bool own_bwd = stride > 1 || (flags & TS_KMAP_TARGET);
+  const bool own_bwd = stride > 1 || (flags & (TS_KMAP_TARGET | TS_KMAP_TRANSPOSED));
   m->mirror_bwd = own_bwd ? 0 : 1;
   m->n_in = n_in;
   m->n_out_cap = n_out_cap;
@@ -87,7 +92,7 @@ size_t layout_kmap(char* base, ts_kmap* m, int64_t n_in, int64_t n_out_cap, int 
   if (own_bwd && (flags & TS_KMAP_BWD)) carve_rel(c, &m->bwd, n_in, m->kvol);
   size_t scratch = rel_scratch_bytes(n_out_cap, m->kvol);
   if (flags & TS_KMAP_PAIRS) {
-    m->pair_cap = pair_capacity(n_in, n_out_cap, ndim, ksize, stride, (flags & TS_KMAP_TARGET) != 0);
+    m->pair_cap = pair_capacity(n_in, n_out_cap, ndim, ksize, stride, flags);
     m->pair_start = c.take<int64_t>(static_cast<size_t>(m->kvol) + 1);
     m->pair_in = c.take<int32_t>(static_cast<size_t>(m->pair_cap));
     m->pair_out = c.take<int32_t>(static_cast<size_t>(m->pair_cap));
@@ -188,19 +193,40 @@ size_t ts_generative_scratch_bytes(int64_t n_in, int ndim, int ksize) {
   return generative_scratch_bytes(n_in * ipow(ksize, ndim));
 }
 
-ts_status ts_generative_support(const int32_t* in_coords, int64_t n_in, int ndim, int ksize, int32_t* out_coords,
-                                int64_t n_out_cap, int64_t* n_out, void* out_table, int64_t out_cap, void* scratch,
-                                size_t scratch_bytes, uint32_t* err_flags, hipStream_t stream) {
-  if (!shape_ok(ndim, ksize, 1)) return TS_ERR_INVALID_ARG;
+namespace {
+// Shared checks and launch of the two generated supports (site = scale * c +
+// sign * delta).
+ts_status generated_support(const int32_t* in_coords, int64_t n_in, int ndim, int ksize, int stride, int scale,
+                            int sign, int32_t* out_coords, int64_t n_out_cap, int64_t* n_out, void* out_table,
+                            int64_t out_cap, void* scratch, size_t scratch_bytes, uint32_t* err_flags,
+                            hipStream_t stream) {
+  if (!shape_ok(ndim, ksize, stride)) return TS_ERR_INVALID_ARG;
   if (n_in < 0 || n_in > kMaxRows || (n_in > 0 && !in_coords) || !n_out || !out_table) return TS_ERR_INVALID_ARG;
   if (n_out_cap < 0 || n_out_cap > kMaxRows || (n_out_cap > 0 && !out_coords)) return TS_ERR_INVALID_ARG;
   if (n_in * ipow(ksize, ndim) > kMaxRows) return TS_ERR_UNSUPPORTED;
   if (!is_pow2(out_cap)) return TS_ERR_INVALID_ARG;
   if (out_cap > kMaxCap) return TS_ERR_UNSUPPORTED;
   if (!scratch || scratch_bytes < ts_generative_scratch_bytes(n_in, ndim, ksize)) return TS_ERR_INVALID_ARG;
-  TS_TRY(launch_generative_support(in_coords, n_in, ndim, ksize, out_coords, n_out_cap, n_out, out_table, out_cap,
-                                   scratch, err_flags, stream));
+  TS_TRY(launch_generative_support(in_coords, n_in, ndim, ksize, scale, sign, out_coords, n_out_cap, n_out, out_table,
+                                   out_cap, scratch, err_flags, stream));
   return TS_OK;
+}
+}  // namespace
+
+ts_status ts_generative_support(const int32_t* in_coords, int64_t n_in, int ndim, int ksize, int32_t* out_coords,
+                                int64_t n_out_cap, int64_t* n_out, void* out_table, int64_t out_cap, void* scratch,
+                                size_t scratch_bytes, uint32_t* err_flags, hipStream_t stream) {
+  return generated_support(in_coords, n_in, ndim, ksize, 1, 1, -1, out_coords, n_out_cap, n_out, out_table, out_cap,
+                           scratch, scratch_bytes, err_flags, stream);
+}
+
+ts_status ts_transposed_support(const int32_t* in_coords, int64_t n_in, int ndim, int ksize, int stride,
+                                int32_t* out_coords, int64_t n_out_cap, int64_t* n_out, void* out_table,
+                                int64_t out_cap, void* scratch, size_t scratch_bytes, uint32_t* err_flags,
+                                hipStream_t stream) {
+  if (stride < 1) return TS_ERR_INVALID_ARG;
+  return generated_support(in_coords, n_in, ndim, ksize, stride, stride, 1, out_coords, n_out_cap, n_out, out_table,
+                           out_cap, scratch, scratch_bytes, err_flags, stream);
 }
 
 size_t ts_kmap_bytes(int64_t n_in, int64_t n_out_cap, int ndim, int ksize, int stride, uint32_t flags) {
@@ -220,17 +246,21 @@ ts_status ts_kmap_build(const int32_t* in_coords, int64_t n_in, const void* in_t
   }
   if (n_in < 0 || n_in > kMaxRows || (n_in > 0 && !in_coords) || !is_pow2(in_cap) || in_cap > kMaxCap)
     return TS_ERR_INVALID_ARG;
-  if (flags & ~(TS_KMAP_PAIRS | TS_KMAP_BWD | TS_KMAP_NATURAL | TS_KMAP_TARGET)) return TS_ERR_INVALID_ARG;
+  if (flags & ~(TS_KMAP_PAIRS | TS_KMAP_BWD | TS_KMAP_NATURAL | TS_KMAP_TARGET | TS_KMAP_TRANSPOSED))
+    return TS_ERR_INVALID_ARG;
   const int kvol = ipow(ksize, ndim);
   const bool target = (flags & TS_KMAP_TARGET) != 0;
-  const bool subm = stride == 1 && !target;
+  const bool transposed = (flags & TS_KMAP_TRANSPOSED) != 0;
+  if (target && transposed) return TS_ERR_INVALID_ARG;
+  const bool subm = stride == 1 && !target && !transposed;
   if (subm) {
     if (ksize % 2 == 0) return TS_ERR_UNSUPPORTED;  // submanifold needs a centred kernel
     out_coords = in_coords;
     n_out_cap = n_in;
   } else {
     if (n_out_cap < 0 || n_out_cap > kMaxRows || (n_out_cap > 0 && !out_coords) || !n_out) return TS_ERR_INVALID_ARG;
-    if ((flags & TS_KMAP_BWD) && (!out_table || !is_pow2(out_cap) || out_cap > kMaxCap)) return TS_ERR_INVALID_ARG;
+    if (((flags & TS_KMAP_BWD) || transposed) && (!out_table || !is_pow2(out_cap) || out_cap > kMaxCap))
+      return TS_ERR_INVALID_ARG;
   }
   if (n_out_cap * kvol > kMaxRows || n_in * kvol > kMaxRows) return TS_ERR_UNSUPPORTED;
   ts_kmap m;
@@ -240,8 +270,10 @@ ts_status ts_kmap_build(const int32_t* in_coords, int64_t n_in, const void* in_t
 
   RelBuild f;
   // targets and strided outputs take the inputs at s*q + delta (s = 1 for a
-  // target map); only a submanifold output must also own its coordinate
-  f.mode = subm ? kModeSubm : kModeDown;
+  // target map); only a submanifold output must also own its coordinate.  A
+  // transposed map reads the strided relation the other way: fine output p
+  // takes the coarse input at (p - delta)/s, and owns p in out_table.
+  f.mode = subm ? kModeSubm : (transposed ? kModeUp : kModeDown);
   f.dest_coords = out_coords;
   f.n_dest_cap = n_out_cap;
   f.ndim = ndim;
@@ -250,8 +282,8 @@ ts_status ts_kmap_build(const int32_t* in_coords, int64_t n_in, const void* in_t
   f.kvol = kvol;
   f.src_table = in_table;
   f.src_cap = in_cap;
-  f.own_table = nullptr;
-  f.own_cap = 0;
+  f.own_table = transposed ? out_table : nullptr;
+  f.own_cap = transposed ? out_cap : 0;
   int64_t* n_out_fill = nullptr;
   if (subm) {
     n_out_fill = m.n_out;  // written by the map kernel: outputs = inputs
@@ -265,14 +297,14 @@ ts_status ts_kmap_build(const int32_t* in_coords, int64_t n_in, const void* in_t
 
   if (!subm && (flags & TS_KMAP_BWD)) {
     RelBuild b = f;
-    b.mode = kModeUp;
+    b.mode = transposed ? kModeDown : kModeUp;
     b.dest_coords = in_coords;
     b.n_dest_cap = n_in;
     b.n_dest = nullptr;
     b.src_table = out_table;
     b.src_cap = out_cap;
-    b.own_table = in_table;
-    b.own_cap = in_cap;
+    b.own_table = transposed ? nullptr : in_table;
+    b.own_cap = transposed ? 0 : in_cap;
     TS_TRY(launch_rel_build(b, m.bwd, natural, nullptr, stream));
   }
   if (flags & TS_KMAP_PAIRS)
@@ -288,6 +320,7 @@ size_t ts_conv_workspace_bytes(const ts_kmap* map, int cin, int cout, int op, ts
     case TS_OP_FWD: return conv_ws(map, cin, cout, in_dtype, TS_BF16, dataflow, map->n_out_cap, map->n_in);
     case TS_OP_DGRAD: return conv_ws(map, cout, cin, in_dtype, TS_BF16, dataflow, map->n_in, map->n_out_cap);
     case TS_OP_WGRAD: return wgrad_workspace_bytes(map, cin, cout);
+    case TS_OP_TRANSPOSE: return conv_ws(map, cin, cout, in_dtype, TS_BF16, dataflow, map->n_in, map->n_out_cap);
   }
   return 0;
 }
@@ -445,6 +478,53 @@ ts_status ts_conv_bwd_dgrad(const ts_kmap* map, const void* dy, int cout, const 
     a.mirror = false;
   }
   if (use_igemm(dataflow, map->kvol, map->n_out_cap, cout, cin, in_dtype)) {
+    TS_TRY(launch_igemm(a, ws, stream));
+  } else {
+    TS_TRY(launch_direct(a, stream));
+  }
+  return TS_OK;
+}
+
+ts_status ts_conv_transpose_fwd(const ts_kmap* map, const void* x, int cin, const void* w, int cout, void* y,
+                                ts_dtype in_dtype, ts_dtype out_dtype, ts_dataflow dataflow, void* ws,
+                                size_t ws_bytes, hipStream_t stream) {
+  ts_status st = check_conv(map, cin, cout, in_dtype, out_dtype);
+  if (st != TS_OK) return st;
+  if (dataflow < TS_DATAFLOW_AUTO || dataflow > TS_DATAFLOW_GATHER_SCATTER) return TS_ERR_INVALID_ARG;
+  if (!w || (map->n_out_cap > 0 && !x) || (map->n_in > 0 && !y)) return TS_ERR_INVALID_ARG;
+  const size_t need = conv_ws(map, cin, cout, in_dtype, out_dtype, dataflow, map->n_in, map->n_out_cap);
+  if (need > 0 && (!ws || ws_bytes < need)) return TS_ERR_INVALID_ARG;
+  // the relation of dgrad, the weights as the forward reads them
+  ConvArgs a;
+  a.rows_in_order = (map->flags & TS_KMAP_NATURAL) != 0;
+  a.kvol = map->kvol;
+  a.src = x;
+  a.n_src = map->n_out_cap;
+  a.c_src = cin;
+  a.dst = y;
+  a.c_dst = cout;
+  a.w = w;
+  a.w_cin = cin;
+  a.w_cout = cout;
+  a.transpose = false;
+  a.in_dtype = in_dtype;
+  a.out_dtype = out_dtype;
+  if (dataflow == TS_DATAFLOW_GATHER_SCATTER) {
+    if (!(map->flags & TS_KMAP_PAIRS)) return TS_ERR_INVALID_ARG;
+    a.rel = &map->fwd;
+    a.mirror = false;
+    TS_TRY(launch_gather_scatter(map, a, true, map->n_in, ws, stream));
+    return TS_OK;
+  }
+  if (map->mirror_bwd) {
+    a.rel = &map->fwd;
+    a.mirror = true;
+  } else {
+    if (!(map->flags & TS_KMAP_BWD) || !map->bwd.tile_mask) return TS_ERR_INVALID_ARG;
+    a.rel = &map->bwd;
+    a.mirror = false;
+  }
+  if (use_igemm(dataflow, map->kvol, map->n_out_cap, cin, cout, in_dtype)) {
     TS_TRY(launch_igemm(a, ws, stream));
   } else {
     TS_TRY(launch_direct(a, stream));

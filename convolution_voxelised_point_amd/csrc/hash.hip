@@ -234,8 +234,10 @@ hipError_t launch_strided_support(const int32_t* coords, int64_t n, int ndim, in
 }
 
 // ---------------------------------------------------------------------------
-// Generated support of a stride-1 convolution: candidate m = i*kvol + o is the
-// site c_i - delta_o, the output whose window holds input i at offset o.  The
+// Generated supports.  Candidate m = i*kvol + o is the site scale*c_i +
+// sign*delta_o: c_i - delta_o for a stride-1 convolution (the output whose
+// window holds input i at offset o), s*c_i + delta_o for a transposed
+// convolution of stride s (the fine site input i reaches at offset o).  The
 // smallest candidate of each site owns it (cells keep NOT of the candidate,
 // raised with atomicMax), so the outputs come out in first-occurrence order
 // over (input row, offset) after the same flag / scan / emit steps as the
@@ -244,7 +246,7 @@ hipError_t launch_strided_support(const int32_t* coords, int64_t n, int ndim, in
 // cells emptied) and raise FULL.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ bool gen_key(const int32_t* coords, int64_t m, int ndim, int kvol, const Offsets& offs,
-                                        bool* input_ok, uint64_t* key) {
+                                        int scale, int sign, bool* input_ok, uint64_t* key) {
   const int64_t i = m / kvol;
   const int o = static_cast<int>(m - i * kvol);
   const int32_t* c = coords + i * (ndim + 1);
@@ -254,18 +256,18 @@ __device__ __forceinline__ bool gen_key(const int32_t* coords, int64_t m, int nd
   *input_ok = make_key(ndim, c[0], full, &k0);
   if (!*input_ok) return false;
   int64_t q[3] = {0, 0, 0};
-  for (int d = 0; d < ndim; ++d) q[d] = full[d] - offs.d[o][d];
+  for (int d = 0; d < ndim; ++d) q[d] = scale * full[d] + sign * offs.d[o][d];
   return make_key(ndim, c[0], q, key);
 }
 
 __global__ __launch_bounds__(256) void k_gen_insert(const int32_t* __restrict__ coords, int64_t n_cand, int kvol,
-                                                    Offsets offs, Table t, uint32_t* flags,
+                                                    Offsets offs, int scale, int sign, Table t, uint32_t* flags,
                                                     int32_t* __restrict__ cell_at) {
   const int64_t m = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   uint64_t key = 0;
   bool input_ok = true;
   const bool in = m < n_cand;
-  const bool valid = in && gen_key(coords, m, t.nd, kvol, offs, &input_ok, &key);
+  const bool valid = in && gen_key(coords, m, t.nd, kvol, offs, scale, sign, &input_ok, &key);
   const int32_t sl = run_slot(t, block_key(key, t.nd), valid, flags);
   if (!in) return;
   int32_t at = -1;
@@ -279,7 +281,8 @@ __global__ __launch_bounds__(256) void k_gen_insert(const int32_t* __restrict__ 
 }
 
 __global__ __launch_bounds__(256) void k_gen_emit(const int32_t* __restrict__ coords, int64_t n_cand, int ndim,
-                                                  int kvol, Offsets offs, const int32_t* __restrict__ cell_at,
+                                                  int kvol, Offsets offs, int scale, int sign,
+                                                  const int32_t* __restrict__ cell_at,
                                                   const int32_t* __restrict__ first,
                                                   const int32_t* __restrict__ index, int64_t n_out_cap,
                                                   int64_t* n_out, Table t, uint32_t* flags,
@@ -298,7 +301,7 @@ __global__ __launch_bounds__(256) void k_gen_emit(const int32_t* __restrict__ co
   const int32_t* c = coords + i * (ndim + 1);
   int32_t* q = out_coords + static_cast<int64_t>(j) * (ndim + 1);
   q[0] = c[0];
-  for (int d = 0; d < ndim; ++d) q[1 + d] = c[1 + d] - offs.d[o][d];
+  for (int d = 0; d < ndim; ++d) q[1 + d] = scale * c[1 + d] + sign * offs.d[o][d];
   t.cells[cell_at[m]] = static_cast<int32_t>(cell_enc(j));
 }
 
@@ -307,9 +310,9 @@ size_t generative_scratch_bytes(int64_t n_cand) {
   return 3 * a + scan_tmp_bytes(n_cand);
 }
 
-hipError_t launch_generative_support(const int32_t* coords, int64_t n, int ndim, int ksize, int32_t* out_coords,
-                                     int64_t n_out_cap, int64_t* n_out, void* out_table, int64_t out_cap,
-                                     void* scratch, uint32_t* flags, hipStream_t s) {
+hipError_t launch_generative_support(const int32_t* coords, int64_t n, int ndim, int ksize, int scale, int sign,
+                                     int32_t* out_coords, int64_t n_out_cap, int64_t* n_out, void* out_table,
+                                     int64_t out_cap, void* scratch, uint32_t* flags, hipStream_t s) {
   Table t = table_view(out_table, out_cap, ndim);
   const Offsets offs = make_offsets(ndim, ksize);
   int kvol = 1;
@@ -324,12 +327,12 @@ hipError_t launch_generative_support(const int32_t* coords, int64_t n, int ndim,
   k_table_clear<<<static_cast<unsigned>(ceil_div<int64_t>(out_cap, 256)), 256, 0, s>>>(t, out_cap);
   if (n_cand == 0) return fill_i64(n_out, 1, 0, s);
   const unsigned g = static_cast<unsigned>(ceil_div<int64_t>(n_cand, 256));
-  k_gen_insert<<<g, 256, 0, s>>>(coords, n_cand, kvol, offs, t, flags, cell_at);
+  k_gen_insert<<<g, 256, 0, s>>>(coords, n_cand, kvol, offs, scale, sign, t, flags, cell_at);
   k_down_flag<<<g, 256, 0, s>>>(cell_at, n_cand, t, first);
   hipError_t e = scan_exclusive_i32(first, index, n_cand, n_out, tmp, s);
   if (e != hipSuccess) return e;
-  k_gen_emit<<<g, 256, 0, s>>>(coords, n_cand, ndim, kvol, offs, cell_at, first, index, n_out_cap, n_out, t, flags,
-                               out_coords);
+  k_gen_emit<<<g, 256, 0, s>>>(coords, n_cand, ndim, kvol, offs, scale, sign, cell_at, first, index, n_out_cap, n_out,
+                               t, flags, out_coords);
   return hipGetLastError();
 }
 

@@ -110,13 +110,13 @@ __global__ __launch_bounds__(256) void k_wpack(const T* __restrict__ w, int kvol
   const int64_t slice = static_cast<int64_t>(c_src) * c_dst;
   u32x4 v = {0u, 0u, 0u, 0u};
   if (n < c_dst) {
+    const int os = mirror ? kvol - 1 - o : o;
     if (trans) {
-      const int os = mirror ? kvol - 1 - o : o;
       v = *reinterpret_cast<const u32x4*>(w + os * slice + static_cast<int64_t>(n) * c_src + k0);
     } else {
       unsigned short e[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) e[j] = __builtin_bit_cast(unsigned short, w[o * slice + static_cast<int64_t>(k0 + j) * c_dst + n]);
+      for (int j = 0; j < 8; ++j) e[j] = __builtin_bit_cast(unsigned short, w[os * slice + static_cast<int64_t>(k0 + j) * c_dst + n]);
 #pragma unroll
       for (int j = 0; j < 4; ++j) v[j] = static_cast<unsigned>(e[2 * j]) | (static_cast<unsigned>(e[2 * j + 1]) << 16);
     }

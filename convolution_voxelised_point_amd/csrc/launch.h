@@ -34,9 +34,10 @@ hipError_t launch_strided_support(const int32_t* coords, int64_t n, int ndim, in
                                   hipStream_t s);
 
 size_t generative_scratch_bytes(int64_t n_cand);
-hipError_t launch_generative_support(const int32_t* coords, int64_t n, int ndim, int ksize, int32_t* out_coords,
-                                     int64_t n_out_cap, int64_t* n_out, void* out_table, int64_t out_cap,
-                                     void* scratch, uint32_t* flags, hipStream_t s);
+// site of candidate (i, o) = scale * c_i + sign * delta_o
+hipError_t launch_generative_support(const int32_t* coords, int64_t n, int ndim, int ksize, int scale, int sign,
+                                     int32_t* out_coords, int64_t n_out_cap, int64_t* n_out, void* out_table,
+                                     int64_t out_cap, void* scratch, uint32_t* flags, hipStream_t s);
 
 // kmap.hip
 enum RelMode { kModeSubm = 0, kModeDown = 1, kModeUp = 2 };

@@ -29,8 +29,8 @@ TS_OK, TS_ERR_INVALID_ARG, TS_ERR_UNSUPPORTED, TS_ERR_HIP = 0, 1, 2, 3
 TS_F32, TS_F16, TS_BF16 = 0, 1, 2
 TS_DATAFLOW_AUTO, TS_DATAFLOW_IMPLICIT_GEMM, TS_DATAFLOW_GATHER_SCATTER = 0, 1, 2
 TS_FLAG_DUP, TS_FLAG_RANGE, TS_FLAG_FULL = 1, 2, 4
-TS_KMAP_PAIRS, TS_KMAP_BWD, TS_KMAP_NATURAL, TS_KMAP_TARGET = 1, 2, 4, 8
-TS_OP_FWD, TS_OP_DGRAD, TS_OP_WGRAD = 0, 1, 2
+TS_KMAP_PAIRS, TS_KMAP_BWD, TS_KMAP_NATURAL, TS_KMAP_TARGET, TS_KMAP_TRANSPOSED = 1, 2, 4, 8, 16
+TS_OP_FWD, TS_OP_DGRAD, TS_OP_WGRAD, TS_OP_TRANSPOSE = 0, 1, 2, 3
 TS_TILE, TS_MAX_KVOL = 16, 64
 
 _DT = {torch.float32: TS_F32, torch.float16: TS_F16, torch.bfloat16: TS_BF16}
@@ -70,6 +70,8 @@ _lib_strided_support = _sig("ts_strided_support", _i32, [_vp, _i64, _i32, _i32, 
 _lib_generative_scratch_bytes = _sig("ts_generative_scratch_bytes", _sz, [_i64, _i32, _i32])
 _lib_generative_support = _sig("ts_generative_support", _i32,
                                [_vp, _i64, _i32, _i32, _vp, _i64, _vp, _vp, _i64, _vp, _sz, _vp, _vp])
+_lib_transposed_support = _sig("ts_transposed_support", _i32,
+                               [_vp, _i64, _i32, _i32, _i32, _vp, _i64, _vp, _vp, _i64, _vp, _sz, _vp, _vp])
 _lib_kmap_bytes = _sig("ts_kmap_bytes", _sz, [_i64, _i64, _i32, _i32, _i32, _u32])
 _lib_kmap_build = _sig("ts_kmap_build", _i32, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _i64, _i32, _i32, _i32, _u32,
                                                _vp, _sz, _P, _vp])
@@ -82,14 +84,16 @@ _lib_conv_fwd_strided = _sig("ts_conv_fwd_strided", _i32,
 _lib_conv_fwd_generative = _sig("ts_conv_fwd_generative", _i32,
                                 [_vp, _i64, _i32, _vp, _i64, _i32, _u32, _vp, _i64, _vp, _vp, _i64, _vp, _vp, _sz, _P,
                                  _vp, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _vp, _sz, _vp])
+_lib_conv_transpose_fwd = _sig("ts_conv_transpose_fwd", _i32,
+                               [_P, _vp, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _vp, _sz, _vp])
 _lib_conv_bwd_dgrad = _sig("ts_conv_bwd_dgrad", _i32, [_P, _vp, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _vp, _sz, _vp])
 _lib_conv_bwd_wgrad = _sig("ts_conv_bwd_wgrad", _i32, [_P, _vp, _i32, _vp, _i32, _i32, _vp, _vp, _sz, _vp])
 
 EXPORTED = ["ts_status_string", "ts_version", "ts_hash_capacity", "ts_hash_table_bytes", "ts_hash_build",
             "ts_hash_query", "ts_support_scratch_bytes", "ts_strided_support", "ts_generative_scratch_bytes",
-            "ts_generative_support", "ts_kmap_bytes", "ts_kmap_build", "ts_conv_workspace_bytes", "ts_conv_fwd",
-            "ts_subm_conv_fwd", "ts_conv_fwd_strided", "ts_conv_fwd_generative", "ts_conv_bwd_dgrad",
-            "ts_conv_bwd_wgrad"]
+            "ts_generative_support", "ts_transposed_support", "ts_kmap_bytes", "ts_kmap_build",
+            "ts_conv_workspace_bytes", "ts_conv_fwd", "ts_subm_conv_fwd", "ts_conv_fwd_strided",
+            "ts_conv_fwd_generative", "ts_conv_transpose_fwd", "ts_conv_bwd_dgrad", "ts_conv_bwd_wgrad"]
 
 
 class TsError(RuntimeError):
@@ -170,6 +174,14 @@ def ts_generative_support(in_coords, ksize, out_coords, n_out, out_table, out_ca
                                    scratch.numel(), _p(err_flags), _stream(stream)), "ts_generative_support")
 
 
+def ts_transposed_support(in_coords, ksize, stride, out_coords, n_out, out_table, out_cap, scratch, err_flags=None,
+                          stream=None) -> None:
+    _check(_lib_transposed_support(_p(in_coords), in_coords.shape[0], in_coords.shape[1] - 1, ksize, stride,
+                                   _p(out_coords), out_coords.shape[0], _p(n_out), _p(out_table), out_cap,
+                                   _p(scratch), scratch.numel(), _p(err_flags), _stream(stream)),
+           "ts_transposed_support")
+
+
 def ts_kmap_bytes(n_in: int, n_out_cap: int, ndim: int, ksize: int, stride: int, flags: int) -> int:
     return int(_lib_kmap_bytes(n_in, n_out_cap, ndim, ksize, stride, flags))
 
@@ -215,6 +227,12 @@ def ts_conv_fwd_generative(in_coords, in_table, in_cap, ksize, kmap_flags, out_c
                                     ctypes.byref(kmap), _p(x), x.shape[1], _p(w), w.shape[2], _p(y), _dt(x), _dt(y),
                                     dataflow, _p(ws), 0 if ws is None else ws.numel(), _stream(stream)),
            "ts_conv_fwd_generative")
+
+
+def ts_conv_transpose_fwd(kmap, x, w, y, dataflow=TS_DATAFLOW_AUTO, ws=None, stream=None) -> None:
+    _check(_lib_conv_transpose_fwd(ctypes.byref(kmap), _p(x), x.shape[1], _p(w), w.shape[2], _p(y), _dt(x), _dt(y),
+                                   dataflow, _p(ws), 0 if ws is None else ws.numel(), _stream(stream)),
+           "ts_conv_transpose_fwd")
 
 
 def ts_conv_bwd_dgrad(kmap, dy, w, dx, dataflow=TS_DATAFLOW_AUTO, ws=None, stream=None) -> None:
@@ -330,10 +348,12 @@ def build_kmap(coords: torch.Tensor, table: HashTable, ksize: int, stride: int =
                out_coords: Optional[torch.Tensor] = None, n_out: Optional[torch.Tensor] = None,
                out_table: Optional[HashTable] = None, stream=None) -> Kmap:
     """Allocate and build a kernel map (submanifold when stride == 1 and
-    TS_KMAP_TARGET is not set; otherwise over out_coords / n_out)."""
+    neither TS_KMAP_TARGET nor TS_KMAP_TRANSPOSED is set; otherwise over
+    out_coords / n_out)."""
     ndim = coords.shape[1] - 1
     n_in = coords.shape[0]
-    n_out_cap = n_in if (stride == 1 and not flags & TS_KMAP_TARGET) else out_coords.shape[0]
+    own_outputs = flags & (TS_KMAP_TARGET | TS_KMAP_TRANSPOSED)
+    n_out_cap = n_in if (stride == 1 and not own_outputs) else out_coords.shape[0]
     nbytes = ts_kmap_bytes(n_in, n_out_cap, ndim, ksize, stride, flags)
     if nbytes == 0:
         raise TsError(TS_ERR_INVALID_ARG, "ts_kmap_bytes")
@@ -377,6 +397,35 @@ def generative_support(coords: torch.Tensor, ksize: int, n_out_cap: Optional[int
     scratch = _bytes(ts_generative_scratch_bytes(n, ndim, ksize), coords.device)
     ts_generative_support(coords, ksize, out, n_out, table.buf, table.cap, scratch, err_flags, stream)
     return out, n_out, table
+
+
+def transposed_support(coords: torch.Tensor, ksize: int, stride: int, n_out_cap: Optional[int] = None,
+                       out_cap: Optional[int] = None, err_flags=None, stream=None):
+    """(fine out_coords [capacity n_out_cap, default n_in * ksize^ndim], n_out
+    device scalar, their table of out_cap block slots, default
+    generative_table_capacity(n_in): the children of one input (k = s = 2)
+    share one fine block)."""
+    n, ndim = coords.shape[0], coords.shape[1] - 1
+    if n_out_cap is None:
+        n_out_cap = n * ksize ** ndim
+    out = torch.zeros((n_out_cap, ndim + 1), dtype=torch.int32, device=coords.device)
+    n_out = torch.zeros(1, dtype=torch.int64, device=coords.device)
+    cap = generative_table_capacity(n) if out_cap is None else out_cap
+    table = HashTable.with_capacity(ndim, cap, coords.device)
+    scratch = _bytes(ts_generative_scratch_bytes(n, ndim, ksize), coords.device)
+    ts_transposed_support(coords, ksize, stride, out, n_out, table.buf, table.cap, scratch, err_flags, stream)
+    return out, n_out, table
+
+
+def conv_transpose(kmap: Kmap, x: torch.Tensor, w: torch.Tensor, out_dtype=None, dataflow=TS_DATAFLOW_AUTO, ws=None,
+                   stream=None) -> torch.Tensor:
+    """ConvTranspose over the map's relation: y on the map's input rows."""
+    out_dtype = out_dtype or x.dtype
+    y = torch.empty((kmap.s.n_in, w.shape[2]), dtype=out_dtype, device=x.device)
+    if ws is None:
+        ws = workspace(kmap, w.shape[1], w.shape[2], TS_OP_TRANSPOSE, x.dtype, dataflow)
+    ts_conv_transpose_fwd(kmap.s, x, w, y, dataflow, ws, stream)
+    return y
 
 
 def workspace(kmap: Kmap, cin: int, cout: int, op: int, dtype: torch.dtype, dataflow: int = TS_DATAFLOW_AUTO):

@@ -79,6 +79,7 @@ typedef enum ts_dataflow {
 #define TS_KMAP_BWD 2u     /* strided/target: also build the transposed relation    */
 #define TS_KMAP_NATURAL 4u /* keep destination rows in index order inside tiles    */
 #define TS_KMAP_TARGET 8u  /* outputs are caller-given coordinates (TargetConv3d)  */
+#define TS_KMAP_TRANSPOSED 16u /* fine outputs of a transposed convolution      */
 
 #define TS_TILE 16     /* destination rows per tile */
 #define TS_MAX_KVOL 64 /* largest supported K^D     */
@@ -167,8 +168,24 @@ ts_status ts_strided_support(const int32_t* in_coords, int64_t n_in, int ndim, i
  * is a TS_KMAP_TARGET map at stride 1, with out_table for its transposed
  * relation.
  * ---------------------------------------------------------------------- */
+/* Scratch of ts_generative_support and ts_transposed_support (both hold
+ * three words per (input row, offset) candidate plus a scan). */
 size_t ts_generative_scratch_bytes(int64_t n_in, int ndim, int ksize);
 ts_status ts_generative_support(const int32_t* in_coords, int64_t n_in, int ndim, int ksize,
+                                int32_t* out_coords, int64_t n_out_cap, int64_t* n_out,
+                                void* out_table, int64_t out_cap, void* scratch, size_t scratch_bytes,
+                                uint32_t* err_flags, hipStream_t stream);
+
+/* Generated support of a transposed convolution of stride s (torch-lattice
+ * migration page, "Convolution mapping" table: GenerativeConvTranspose3d
+ * generates output support, where ConvTranspose3d reuses a relation).  The
+ * outputs are every fine site s*c_j + delta_o that a (coarse) input row j
+ * reaches through offset o, each once, in order of first occurrence over
+ * (j ascending, then o ascending); for k = s these are the s^D children of
+ * every input.  Repeats, range, capacity, table and scratch behave as in
+ * ts_generative_support.  The map over these outputs is a TS_KMAP_TRANSPOSED
+ * map with this out_table. */
+ts_status ts_transposed_support(const int32_t* in_coords, int64_t n_in, int ndim, int ksize, int stride,
                                 int32_t* out_coords, int64_t n_out_cap, int64_t* n_out,
                                 void* out_table, int64_t out_cap, void* scratch, size_t scratch_bytes,
                                 uint32_t* err_flags, hipStream_t stream);
@@ -242,6 +259,14 @@ size_t ts_kmap_bytes(int64_t n_in, int64_t n_out_cap, int ndim, int ksize, int s
  *     offset once), and its transposed relation (TS_KMAP_BWD) needs
  *     out_table = the ts_hash_build table of the targets (or the table
  *     ts_generative_support leaves).
+ *   TS_KMAP_TRANSPOSED (a transposed convolution onto generated or given fine
+ *     coordinates, e.g. from ts_transposed_support): out_coords / n_out_cap /
+ *     n_out are the fine outputs and out_table their table (required: an
+ *     output row takes part only if it owns its coordinate there); output
+ *     row j takes the coarse input at (p_j - delta_o)/s for every offset o
+ *     where that divides exactly -- the strided relation read the other way.
+ *     With TS_KMAP_BWD the transposed relation (coarse rows to fine rows, the
+ *     strided relation itself) is built too, for dgrad.
  * in_table / in_cap is the ts_hash_build table of the inputs. */
 ts_status ts_kmap_build(const int32_t* in_coords, int64_t n_in, const void* in_table, int64_t in_cap,
                         const int32_t* out_coords, int64_t n_out_cap, const int64_t* n_out,
@@ -258,6 +283,7 @@ ts_status ts_kmap_build(const int32_t* in_coords, int64_t n_in, const void* in_t
 #define TS_OP_FWD 0
 #define TS_OP_DGRAD 1
 #define TS_OP_WGRAD 2
+#define TS_OP_TRANSPOSE 3
 
 /* Workspace bytes for an op on this map (0 is a valid answer). */
 size_t ts_conv_workspace_bytes(const ts_kmap* map, int cin, int cout, int op, ts_dtype in_dtype,
@@ -301,6 +327,18 @@ ts_status ts_conv_fwd_generative(const int32_t* in_coords, int64_t n_in, int ndi
                                  const void* x, int cin, const void* w, int cout, void* y,
                                  ts_dtype in_dtype, ts_dtype out_dtype, ts_dataflow dataflow, void* ws,
                                  size_t ws_bytes, hipStream_t stream);
+
+/* ConvTranspose3d / ConvTranspose2d over an existing relation (torch-lattice
+ * migration page, "Convolution mapping": a transposed convolution that
+ * consumes an existing relation): y[n_in][cout] = sum over the map's triples
+ * (i, j, o) of x[j] . W[o], with x[n_out][cin] on the map's outputs and
+ * W[kvol][cin][cout] -- the relation of dgrad, the weights as the forward
+ * reads them.  Strided maps need TS_KMAP_BWD (implicit GEMM) or TS_KMAP_PAIRS
+ * (gather-scatter); a submanifold map uses its mirrored offsets.  Workspace:
+ * ts_conv_workspace_bytes(map, cin, cout, TS_OP_TRANSPOSE, ...). */
+ts_status ts_conv_transpose_fwd(const ts_kmap* map, const void* x, int cin, const void* w, int cout, void* y,
+                                ts_dtype in_dtype, ts_dtype out_dtype, ts_dataflow dataflow, void* ws,
+                                size_t ws_bytes, hipStream_t stream);
 
 /* dx[n_in][cin] = sum over triples (i, j, o) of dy[j] . W[o]^T.  Strided
  * maps need TS_KMAP_BWD (implicit GEMM) or TS_KMAP_PAIRS (gather-scatter). */
