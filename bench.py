@@ -8,8 +8,9 @@ JSON line reports map-valid TFLOP/s of that step (2 * pairs * Cin * Cout per
 replay time), the per-stage times of eager launches taken with HIP events on
 the launch stream, the roofline position of the dominant kernel, and the CPU
 oracle timed on this host.  The other workloads (strided 64 -> 128 downsampling,
-the generative stride-1 convolution of the scene, the 2-D pixel tracks, the
-bf16 128-channel training step) are measured the same way and reported under
+the transposed convolutions back up from it, the generative stride-1
+convolution of the scene, the 2-D pixel tracks, the bf16 128-channel
+training step) are measured the same way and reported under
 "secondary".
 
 The ``setup_*`` functions below fix each workload's launch configuration;
@@ -21,7 +22,7 @@ write that evicts the caches.  A copy of the ring scan with its rows in
 random order is measured as a secondary workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
-                       [--only lidar|lidar_shuffled|down|generative|pixels|train]
+                       [--only lidar|lidar_shuffled|down|up|generative|pixels|train]
                        [--copy-calib MB]
 """
 from __future__ import annotations
@@ -341,6 +342,68 @@ def setup_generative(ts, w, kmap_flags=None) -> Step:
                 m=m, kvol=k ** nd)
 
 
+def setup_up(ts, w) -> Step:
+    """Transposed convolutions on the two-scene workload's strided layer.
+    Set-up runs the strided support and its map (relation with its transpose
+    and pair lists), as the encoder layer would.  Timed:
+      * `transpose`: ConvTranspose3d k2 s2, 128 -> 64 channels fp16, over
+        that relation (coarse rows back onto the fine rows);
+      * `support`, `kmap`, `conv`: GenerativeConvTranspose3d k2 s2,
+        128 -> 64 fp16 from the coarse rows: generated fine support (8
+        children per coarse row), its transposed map, the forward."""
+    dev = torch.device("cuda")
+    coords = torch.from_numpy(w.coords).to(dev)
+    n = coords.shape[0]
+    table = ts.HashTable(coords, 2.0)
+    flags = torch.zeros(1, dtype=torch.int32, device=dev)
+    out, n_out, out_table = ts.strided_support(coords, 2, err_flags=flags)
+    enc = ts.build_kmap(coords, table, 2, 2, ts.TS_KMAP_BWD | ts.TS_KMAP_PAIRS, out_coords=out, n_out=n_out,
+                        out_table=out_table)
+    m = int(n_out.item())
+    coarse = out[:m].contiguous()
+    x = synth.normal(1000 * w.index + 905, (enc.s.n_out_cap, 128), 1.0, "f16").to(dev)
+    wt = synth.weight(1000 * w.index + 906, 8, 128, 64, "f16").to(dev)
+    y = torch.empty((n, 64), dtype=torch.float16, device=dev)
+    ws_t = ts.workspace(enc, 128, 64, ts.TS_OP_TRANSPOSE, torch.float16)
+
+    def transpose():
+        ts.ts_conv_transpose_fwd(enc.s, x, wt, y, ts.TS_DATAFLOW_AUTO, ws_t)
+
+    # generative: the coarse rows are the inputs (their own table)
+    ctab = ts.HashTable(coarse, 2.0)
+    fine_cap = 8 * m
+    fine = torch.zeros((fine_cap, 4), dtype=torch.int32, device=dev)
+    n_fine = torch.zeros(1, dtype=torch.int64, device=dev)
+    fine_table = ts.HashTable.with_capacity(3, ts.generative_table_capacity(m), dev)
+    scratch = torch.empty(ts.ts_generative_scratch_bytes(m, 3, 2), dtype=torch.uint8, device=dev)
+    kflags = ts.TS_KMAP_TRANSPOSED
+    kbuf = torch.empty(ts.ts_kmap_bytes(m, fine_cap, 3, 2, 2, kflags), dtype=torch.uint8, device=dev)
+    km = ts.TsKmap()
+    xc = x[:m].contiguous()
+    yg = torch.empty((fine_cap, 64), dtype=torch.float16, device=dev)
+
+    def support():
+        ts.ts_transposed_support(coarse, 2, 2, fine, n_fine, fine_table.buf, fine_table.cap, scratch, flags)
+
+    def kmap_build():
+        ts.ts_kmap_build(coarse, ctab.buf, ctab.cap, fine, fine_cap, n_fine, fine_table.buf, fine_table.cap, 3, 2, 2,
+                         kflags, kbuf, km)
+
+    support()
+    kmap_build()
+    torch.cuda.synchronize()
+    ws_g = torch.empty(max(ts.ts_conv_workspace_bytes(km, 128, 64, ts.TS_OP_FWD, ts.TS_F16, 0), 1),
+                       dtype=torch.uint8, device=dev)
+
+    def conv():
+        ts.ts_conv_fwd(km, xc, wt, yg, ts.TS_DATAFLOW_AUTO, ws_g)
+
+    gen = ts.Kmap(km, kbuf, keep=(coarse, ctab, fine, n_fine, fine_table))
+    return Step(fns=[transpose, support, kmap_build, conv], names=["transpose", "support", "kmap", "conv"],
+                coords=coords, enc=enc, coarse=coarse, m=m, x=x, w=wt, y=y, fine=fine, n_fine=n_fine,
+                fine_table=fine_table, gen=gen, yg=yg, flags=flags, n=n)
+
+
 def setup_train(ts, w) -> Step:
     """bf16 128 -> 128 training step: hash, kernel map (+pairs), forward,
     dgrad (mirrored offsets), wgrad (fp32 dW)."""
@@ -453,6 +516,22 @@ def measure_generative(ts, steps, warmup):
             "ms_per_step_eager": ms_eager, "stages_us": {k: round(v, 3) for k, v in st.items()},
             "tflops_step": flop / (ms * 1e-3) / 1e12,
             "conv_gbs": conv_bytes / (st["conv"] * 1e-6) / 1e9, "err_flags": int(s.flags.item())}
+
+
+def measure_up(ts, steps, warmup):
+    w = synth.make("down")
+    s = setup_up(ts, w)
+    ms_eager, st = run_steps(s.fns, s.names, steps, warmup)
+    ms_t, _ = run_graph(capture(s.fns[:1]), steps, warmup)
+    ms_g, _ = run_graph(capture(s.fns[1:]), steps, warmup)
+    pt = popcount_sum(s.enc.rel_arrays("fwd")["row_mask"][:s.m], 8)
+    n_fine = int(s.n_fine.item())
+    pg = popcount_sum(s.gen.rel_arrays("fwd")["row_mask"][:n_fine], 8)
+    return {"workload": "up", "n_fine": s.n, "n_coarse": s.m, "stages_us": {k: round(v, 3) for k, v in st.items()},
+            "conv_transpose": {"ms_per_step": ms_t, "pairs": pt, "tflops": 2.0 * pt * 128 * 64 / (ms_t * 1e-3) / 1e12},
+            "generative_transpose": {"ms_per_step": ms_g, "n_out": n_fine, "pairs": pg,
+                                     "tflops": 2.0 * pg * 128 * 64 / (ms_g * 1e-3) / 1e12},
+            "err_flags": int(s.flags.item())}
 
 
 def measure_down(ts, steps, warmup):
@@ -580,7 +659,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--only", default=None,
-                    help="measure one workload (lidar, lidar_shuffled, down, generative, pixels, train)")
+                    help="measure one workload (lidar, lidar_shuffled, down, up, generative, pixels, train)")
     ap.add_argument("--copy-calib", type=int, default=0, help="run only a plain copy of this many MiB")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -594,14 +673,15 @@ def main():
 
     torch.cuda.synchronize()
     if args.only and args.only != "lidar":
-        fn = {"lidar_shuffled": measure_lidar_shuffled, "down": measure_down, "generative": measure_generative,
-              "pixels": measure_pixels, "train": measure_train}[args.only]
+        fn = {"lidar_shuffled": measure_lidar_shuffled, "down": measure_down, "up": measure_up,
+              "generative": measure_generative, "pixels": measure_pixels, "train": measure_train}[args.only]
         print(json.dumps(fn(ts, args.steps, args.warmup)))
         return
     w, r = measure_lidar(ts, args.steps, args.warmup)
     secondary = []
     if args.only is None:
-        for fn in (measure_lidar_shuffled, measure_down, measure_generative, measure_pixels, measure_train):
+        for fn in (measure_lidar_shuffled, measure_down, measure_up, measure_generative, measure_pixels,
+                   measure_train):
             secondary.append(fn(ts, args.steps, args.warmup))
     value = r["flop_per_step"] / (r["ms_per_step"] * 1e-3) / 1e12
     conv_s = r["stages_us"]["conv"] * 1e-6

@@ -233,3 +233,40 @@ def test_generative_rejects(ts):
     assert conv(22, ts.TS_BF16) == ts.TS_ERR_UNSUPPORTED     # f16 in, bf16 out
     assert conv(23, ts.TS_DATAFLOW_GATHER_SCATTER) == ts.TS_ERR_INVALID_ARG   # no pair lists
     assert conv(20, None) == ts.TS_ERR_INVALID_ARG           # null y
+
+
+def test_transposed_rejects(ts):
+    T = ts._lib_transposed_support
+    sb = ts.ts_generative_scratch_bytes(100, 3, 2)
+    ok = [FAKE, 100, 3, 2, 2, FAKE, 800, FAKE, FAKE, 1024, FAKE, sb, None, None]
+
+    def call(i, v):
+        a = list(ok)
+        a[i] = v
+        return T(*a)
+
+    assert call(4, 0) == ts.TS_ERR_INVALID_ARG           # stride 0
+    assert call(7, None) == ts.TS_ERR_INVALID_ARG        # n_out
+    assert call(9, 100) == ts.TS_ERR_INVALID_ARG         # out_cap not a power of two
+    assert call(11, sb - 1) == ts.TS_ERR_INVALID_ARG     # short scratch
+    L = ts._lib_kmap_build
+    km = ts.TsKmap()
+    X = ts.TS_KMAP_TRANSPOSED
+    need = ts.ts_kmap_bytes(100, 800, 3, 2, 2, X | ts.TS_KMAP_BWD)
+    assert need > ts.ts_kmap_bytes(100, 800, 3, 2, 2, X)
+    # a transposed map needs the fine outputs' table, and is not also a target map
+    assert L(FAKE, 100, FAKE, 256, FAKE, 800, FAKE, None, 0, 3, 2, 2, X, FAKE, need, ctypes.byref(km), None) \
+        == ts.TS_ERR_INVALID_ARG
+    assert L(FAKE, 100, FAKE, 256, FAKE, 800, FAKE, FAKE, 1024, 3, 2, 2, X | ts.TS_KMAP_TARGET, FAKE, need,
+             ctypes.byref(km), None) == ts.TS_ERR_INVALID_ARG
+    # ConvTranspose over a strided map needs its transposed relation
+    km.kvol, km.stride, km.mirror_bwd = 8, 2, 0
+    km.n_in, km.n_out_cap = 100, 60
+    km.fwd.tile_mask, km.fwd.n_tiles = 0x2000, 4
+    assert ts._lib_conv_transpose_fwd(ctypes.byref(km), FAKE, 16, FAKE, 16, FAKE, 0, 0, 0, None, 0, None) \
+        == ts.TS_ERR_INVALID_ARG
+    assert ts._lib_conv_transpose_fwd(ctypes.byref(km), FAKE, 16, None, 16, FAKE, 0, 0, 0, None, 0, None) \
+        == ts.TS_ERR_INVALID_ARG
+    # workspace of the transposed op: the packed weights (kvol * Cout * Cin)
+    km.kvol = 8
+    assert ts._lib_conv_workspace_bytes(ctypes.byref(km), 128, 64, ts.TS_OP_TRANSPOSE, ts.TS_F16, 0) == 8 * 128 * 64 * 2

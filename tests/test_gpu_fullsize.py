@@ -129,6 +129,32 @@ def test_full_generative_f16(ts):
     assert_feature_close(s.y[torch.from_numpy(pick).cuda()], ref, torch.float16, "generative fwd (fp16 out)")
 
 
+def test_full_up_transposed_f16(ts):
+    """Transposed convolutions on the two-scene strided layer: ConvTranspose3d
+    over its relation and GenerativeConvTranspose3d from its coarse rows
+    (1.28M generated fine sites bit-exact, map bit-exact, features sampled)."""
+    w = synth.make("down")
+    s = bench.setup_up(ts, w)
+    s.run_once()
+    assert int(s.flags.item()) == 0
+    coarse = oracle.strided_support(w.coords, 2)
+    assert s.m == coarse.shape[0] and np.array_equal(s.coarse.cpu().numpy(), coarse)
+    x = s.x[:s.m].cpu()
+    tr = oracle.kmap(w.coords, coarse, 2, 2)
+    rows = sample_rows(s.n, 61)
+    ref = oracle.conv_transpose(restrict(tr, rows, 0), x, s.w.cpu(), s.n)[rows]
+    assert_feature_close(s.y[torch.from_numpy(rows).cuda()], ref, torch.float16, "ConvTranspose3d (fp16 out)")
+    fine = oracle.transposed_support(coarse, 2, 2)
+    n_f = int(s.n_fine.item())
+    assert n_f == fine.shape[0] == 8 * s.m
+    assert np.array_equal(s.fine[:n_f].cpu().numpy(), fine)
+    tg = oracle.kmap_transposed(coarse, fine, 2, 2)
+    check_triples(s.gen, tg, 8, "generative transposed")
+    pick = sample_rows(n_f, 62)
+    ref = oracle.conv_fwd(restrict(tg, pick, 1), x, s.w.cpu(), n_f)[pick]
+    assert_feature_close(s.yg[torch.from_numpy(pick).cuda()], ref, torch.float16, "GenerativeConvTranspose3d")
+
+
 @pytest.mark.parametrize("dataflow", ["auto", "gather_scatter"])
 def test_full_pixels_two_layers(ts, dataflow):
     w = synth.make("pixels")
