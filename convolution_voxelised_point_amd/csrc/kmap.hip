@@ -36,6 +36,7 @@ struct RelK {
   int64_t n_dest_cap;
   const int64_t* n_dest;
   int ndim, stride, kvol, centre;
+  int stride_shift;  // log2(stride) when stride is a power of two, else -1
   Offsets offs;
   Table src;
   Table own;
@@ -259,9 +260,16 @@ __device__ __forceinline__ bool probe_key(const RelK& a, const int8_t* offs, int
     } else if (MODE == kModeDown) {
       p[d] = static_cast<int64_t>(a.stride) * s[d] + dd;
     } else {
-      const int64_t t = s[d] - dd;
-      if (t % a.stride != 0) return false;
-      p[d] = t / a.stride;
+      // the transposed relation: (p - delta) / s where exact; coordinates
+      // fit in 32 bits, and a power-of-two stride needs no division
+      const int32_t t = static_cast<int32_t>(s[d] - dd);
+      if (a.stride_shift >= 0) {
+        if (t & ((1 << a.stride_shift) - 1)) return false;
+        p[d] = t >> a.stride_shift;  // exact: arithmetic shift of a multiple
+      } else {
+        if (t % a.stride != 0) return false;
+        p[d] = t / a.stride;
+      }
     }
   }
   return make_key(a.ndim, b, p, key);
@@ -339,8 +347,9 @@ __global__ __launch_bounds__(256) void k_rel_probe(RelK a, int natural, int64_t*
   if (threadIdx.x < tail) dst[words - tail + threadIdx.x] = staged[words - tail + threadIdx.x];
 }
 
-// Runtime-kvol versions (neighbours kept in LDS), for kernel sizes without a
-// compile-time instance.
+// Runtime-kvol versions, for kernel sizes and modes without a compile-time
+// instance: a lane per row probes every offset into its LDS row, and the
+// workgroup's 256 rows are then written as one coalesced span.
 template <int MODE>
 __global__ __launch_bounds__(256) void k_rel_probe_any(RelK a, int natural) {
   extern __shared__ int32_t nbr_lds[];  // [256][kvol]
@@ -348,11 +357,11 @@ __global__ __launch_bounds__(256) void k_rel_probe_any(RelK a, int natural) {
   load_offsets(a, offs);
   const int64_t t = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / kTile;
   const int r = threadIdx.x & (kTile - 1);
-  if (t >= a.n_tiles) return;
+  const bool live = t < a.n_tiles;  // every lane stays for the barrier below
   const int64_t n_dest = dest_count(a.n_dest, a.n_dest_cap);
   const int64_t row = t * kTile + r;
-  int64_t b, s[3];
-  const bool valid = row < n_dest && dest_load<MODE>(a, row, &b, s);
+  int64_t b = 0, s[3] = {0, 0, 0};
+  const bool valid = live && row < n_dest && dest_load<MODE>(a, row, &b, s);
   int32_t* my = nbr_lds + threadIdx.x * a.kvol;
   uint64_t mask = 0;
   for (int o = 0; o < a.kvol; ++o) {
@@ -360,14 +369,25 @@ __global__ __launch_bounds__(256) void k_rel_probe_any(RelK a, int natural) {
     my[o] = n;
     if (n >= 0) mask |= 1ull << o;
   }
-  if (MODE == kModeSubm && valid && my[a.centre] != static_cast<int32_t>(row)) mask = 0;
-  if (row < a.n_dest_cap) a.row_mask[row] = mask;
-  if (row < n_dest)
-    for (int o = 0; o < a.kvol; ++o) a.nbr[row * a.kvol + o] = ((mask >> o) & 1) ? my[o] : -1;
-  if (!natural) return;
-  const uint64_t tmask = group16_or(mask);
-  if (r == 0) a.tile_mask[t] = tmask;
-  a.tile_rows[t * kTile + r] = row < n_dest ? static_cast<int32_t>(row) : -1;
+  // a submanifold output takes part only when it owns its coordinate
+  if (MODE == kModeSubm && valid && my[a.centre] != static_cast<int32_t>(row)) {
+    mask = 0;
+    for (int o = 0; o < a.kvol; ++o) my[o] = -1;
+  }
+  if (live && row < a.n_dest_cap) a.row_mask[row] = mask;
+  const uint64_t tmask = group16_or(mask);  // a 16-lane group is live or not as a whole
+  if (natural && live) {
+    if (r == 0) a.tile_mask[t] = tmask;
+    a.tile_rows[t * kTile + r] = row < n_dest ? static_cast<int32_t>(row) : -1;
+  }
+  __syncthreads();
+  // rows at or past the device count are never read through the table
+  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * 256;
+  const int64_t rows = n_dest - row0 < 256 ? n_dest - row0 : 256;
+  if (rows <= 0) return;
+  const int words = static_cast<int>(rows) * a.kvol;
+  int32_t* dst = a.nbr + row0 * a.kvol;
+  for (int k = threadIdx.x; k < words; k += 256) dst[k] = nbr_lds[k];
 }
 
 // Pass 2: stable sort of each window's rows by offset mask: an LSD radix
@@ -545,6 +565,9 @@ RelK make_relk(const RelBuild& bld, const ts_rel& rel) {
   a.n_dest = bld.n_dest;
   a.ndim = bld.ndim;
   a.stride = bld.stride;
+  a.stride_shift = -1;
+  for (int k = 0; k < 17; ++k)
+    if (bld.stride == (1 << k)) a.stride_shift = k;
   a.kvol = bld.kvol;
   a.centre = (bld.kvol - 1) / 2;
   a.offs = make_offsets(bld.ndim, bld.ksize);
