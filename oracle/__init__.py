@@ -59,6 +59,8 @@ def lib():
         L.oracle_conv_dgrad.restype = None
         L.oracle_conv_wgrad.argtypes = [p, p, p, i64, p, i32, p, i32, p, i32]
         L.oracle_conv_wgrad.restype = None
+        L.oracle_pool.argtypes = [p, p, i64, p, i32, i32, p, i64]
+        L.oracle_pool.restype = None
         _lib = L
     return _lib
 
@@ -200,6 +202,17 @@ def conv_wgrad(triples, x, dy, kvol: int) -> np.ndarray:
     lib().oracle_conv_wgrad(_ptr(t_in), _ptr(t_out), _ptr(t_off), t_in.shape[0], _ptr(x), cin, _ptr(dy), cout,
                             _ptr(dw), kvol)
     return dw
+
+
+def pool(triples, x, n_out: int, mode: str) -> np.ndarray:
+    """Max ("max") or mean ("avg") of x over each output's present inputs;
+    0 for an output with none."""
+    t_in, t_out, _ = (np.ascontiguousarray(t, dtype=np.int32) for t in triples)
+    x = _f64(x)
+    c = x.shape[1]
+    y = np.empty((n_out, c), np.float64)
+    lib().oracle_pool(_ptr(t_in), _ptr(t_out), t_in.shape[0], _ptr(x), c, {"max": 0, "avg": 1}[mode], _ptr(y), n_out)
+    return y
 
 
 def subm_conv(coords, x, w, ksize: int):

@@ -21,6 +21,8 @@
 //   * a transposed convolution either reuses an existing relation
 //     (ConvTranspose3d) or generates its output support
 //     (GenerativeConvTranspose3d) ("Convolution mapping" table);
+//   * pooling runs over the same kernel maps as convolution (torch-lattice
+//     "What remains familiar": CUDA kernels cover pooling);
 //   * every dataflow must give the same result for a fixed relation
 //     (input row, output row, kernel offset) and weight tensor.
 //
@@ -342,6 +344,29 @@ void oracle_conv_dgrad(const int32_t* t_in, const int32_t* t_out, const int32_t*
     for (int ci = 0; ci < cin; ++ci)
       for (int co = 0; co < cout; ++co) d[ci] += g[co] * wo[ci * cout + co];
   }
+}
+
+// Pooling over a relation: y[j][c] = the maximum (mode 0) or the mean
+// (mode 1) of x[i][c] over the triples (i, j, o) of output row j -- over the
+// inputs present in its window, not over K^D -- and 0 for an output with
+// none.
+void oracle_pool(const int32_t* t_in, const int32_t* t_out, int64_t n_pairs, const double* x, int c, int mode,
+                 double* y, int64_t n_out) {
+  std::vector<int64_t> count(static_cast<size_t>(n_out), 0);
+  for (int64_t k = 0; k < n_out * c; ++k) y[k] = 0.0;
+  for (int64_t p = 0; p < n_pairs; ++p) {
+    const double* xi = x + static_cast<int64_t>(t_in[p]) * c;
+    double* yj = y + static_cast<int64_t>(t_out[p]) * c;
+    const bool first = count[t_out[p]]++ == 0;
+    for (int ch = 0; ch < c; ++ch) {
+      if (mode == 0) yj[ch] = first ? xi[ch] : (xi[ch] > yj[ch] ? xi[ch] : yj[ch]);
+      else yj[ch] += xi[ch];
+    }
+  }
+  if (mode == 1)
+    for (int64_t j = 0; j < n_out; ++j)
+      if (count[j] > 0)
+        for (int ch = 0; ch < c; ++ch) y[j * c + ch] /= static_cast<double>(count[j]);
 }
 
 // dw[o][ci][co] = sum over triples (i, j, o) of x[i][ci] * dy[j][co].
