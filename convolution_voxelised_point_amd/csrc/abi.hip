@@ -532,6 +532,17 @@ ts_status ts_conv_transpose_fwd(const ts_kmap* map, const void* x, int cin, cons
   return TS_OK;
 }
 
+ts_status ts_pool_fwd(const ts_kmap* map, const void* x, int c, void* y, ts_dtype in_dtype, ts_dtype out_dtype,
+                      int mode, hipStream_t stream) {
+  if (!map || map->kvol < 1 || map->kvol > TS_MAX_KVOL || !map->fwd.tile_mask) return TS_ERR_INVALID_ARG;
+  if (c < 1 || c > kMaxChannels || (mode != TS_POOL_MAX && mode != TS_POOL_AVG)) return TS_ERR_INVALID_ARG;
+  if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return TS_ERR_INVALID_ARG;
+  if (out_dtype != TS_F32 && out_dtype != in_dtype) return TS_ERR_UNSUPPORTED;
+  if ((map->n_in > 0 && !x) || (map->n_out_cap > 0 && !y)) return TS_ERR_INVALID_ARG;
+  TS_TRY(launch_pool(map->fwd, map->kvol, x, c, y, in_dtype, out_dtype, mode, stream));
+  return TS_OK;
+}
+
 ts_status ts_conv_bwd_wgrad(const ts_kmap* map, const void* x, int cin, const void* dy, int cout, ts_dtype in_dtype,
                             float* dw, void* ws, size_t ws_bytes, hipStream_t stream) {
   ts_status st = check_conv(map, cin, cout, in_dtype, TS_F32);

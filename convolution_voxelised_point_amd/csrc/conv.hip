@@ -235,6 +235,94 @@ hipError_t launch_direct(const ConvArgs& a, hipStream_t s) {
   }
 }
 
+// ---------------------------------------------------------------- pooling
+// Thread = (destination slot, 8-channel chunk).  It walks the row's offsets
+// in its mask and keeps the maximum, or the sum and the count, of the
+// neighbours' channels in fp32 (the maximum of stored values is exact in any
+// output type); an output with no neighbour gets 0.
+struct PoolK {
+  const int32_t* tile_rows;
+  const uint64_t* row_mask;
+  const int32_t* nbr;
+  int64_t slots;
+  int kvol, c, nchunk;
+  const void* src;
+  void* dst;
+};
+
+template <typename T, typename OT, int MODE>
+__global__ __launch_bounds__(256) void k_pool(PoolK a) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= a.slots * a.nchunk) return;
+  const int64_t slot = i / a.nchunk;
+  const int c0 = static_cast<int>(i - slot * a.nchunk) * 8;
+  const int32_t row = a.tile_rows[slot];
+  if (row < 0) return;
+  const T* src = static_cast<const T*>(a.src);
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = MODE == TS_POOL_MAX ? -__builtin_inff() : 0.f;
+  int count = 0;
+  for (uint64_t mm = a.row_mask[row]; mm; mm &= mm - 1) {
+    const int o = __builtin_ctzll(mm);
+    const int32_t nb = a.nbr[static_cast<int64_t>(row) * a.kvol + o];
+    if (nb < 0) continue;
+    const T* xs = src + static_cast<int64_t>(nb) * a.c + c0;
+    ++count;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if (c0 + e >= a.c) break;
+      const float v = to_f32(xs[e]);
+      acc[e] = MODE == TS_POOL_MAX ? fmaxf(acc[e], v) : acc[e] + v;
+    }
+  }
+  OT* out = static_cast<OT*>(a.dst) + static_cast<int64_t>(row) * a.c + c0;
+  const float inv = count > 0 ? 1.f / static_cast<float>(count) : 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    if (c0 + e >= a.c) break;
+    const float v = count == 0 ? 0.f : (MODE == TS_POOL_MAX ? acc[e] : acc[e] * inv);
+    out[e] = from_f32<OT>(v);
+  }
+}
+
+template <typename T, typename OT>
+static hipError_t pool_mode(const PoolK& k, int mode, hipStream_t s) {
+  const unsigned grid = static_cast<unsigned>(ceil_div<int64_t>(k.slots * k.nchunk, 256));
+  if (mode == TS_POOL_MAX) k_pool<T, OT, TS_POOL_MAX><<<grid, 256, 0, s>>>(k);
+  else k_pool<T, OT, TS_POOL_AVG><<<grid, 256, 0, s>>>(k);
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t pool_out(const PoolK& k, ts_dtype out, int mode, hipStream_t s) {
+  switch (out) {
+    case TS_F32: return pool_mode<T, float>(k, mode, s);
+    case TS_F16: return pool_mode<T, _Float16>(k, mode, s);
+    default: return pool_mode<T, __bf16>(k, mode, s);
+  }
+}
+
+hipError_t launch_pool(const ts_rel& rel, int kvol, const void* x, int c, void* y, ts_dtype in, ts_dtype out, int mode,
+                       hipStream_t s) {
+  if (rel.n_tiles == 0) return hipSuccess;
+  PoolK k;
+  k.tile_rows = rel.tile_rows;
+  k.row_mask = rel.row_mask;
+  k.nbr = rel.nbr;
+  k.slots = rel.n_tiles * kTile;
+  k.kvol = kvol;
+  k.c = c;
+  k.nchunk = (c + 7) / 8;
+  k.src = x;
+  k.dst = y;
+  switch (in) {
+    case TS_F32: return pool_out<float>(k, out, mode, s);
+    case TS_F16: return pool_out<_Float16>(k, out, mode, s);
+    default: return pool_out<__bf16>(k, out, mode, s);
+  }
+}
+
 size_t gs_workspace_bytes(int64_t n_dest_cap, int c_dst, ts_dtype out_dtype) {
   if (out_dtype == TS_F32) return 0;
   return align_up(static_cast<size_t>(n_dest_cap) * c_dst * 4, 256);

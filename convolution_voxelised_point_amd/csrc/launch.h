@@ -84,6 +84,8 @@ size_t igemm_workspace_bytes(int kvol, int c_src, int c_dst);
 bool igemm_supported(int kvol, int64_t n_src, int c_src, int c_dst, ts_dtype in_dtype);
 hipError_t launch_igemm(const ConvArgs& a, void* ws, hipStream_t s);
 hipError_t launch_direct(const ConvArgs& a, hipStream_t s);
+hipError_t launch_pool(const ts_rel& rel, int kvol, const void* x, int c, void* y, ts_dtype in, ts_dtype out, int mode,
+                       hipStream_t s);
 
 size_t gs_workspace_bytes(int64_t n_dest_cap, int c_dst, ts_dtype out_dtype);
 hipError_t launch_gather_scatter(const ts_kmap* map, const ConvArgs& a, bool backward, int64_t n_dest_cap,

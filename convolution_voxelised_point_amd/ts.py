@@ -31,6 +31,7 @@ TS_DATAFLOW_AUTO, TS_DATAFLOW_IMPLICIT_GEMM, TS_DATAFLOW_GATHER_SCATTER = 0, 1, 
 TS_FLAG_DUP, TS_FLAG_RANGE, TS_FLAG_FULL = 1, 2, 4
 TS_KMAP_PAIRS, TS_KMAP_BWD, TS_KMAP_NATURAL, TS_KMAP_TARGET, TS_KMAP_TRANSPOSED = 1, 2, 4, 8, 16
 TS_OP_FWD, TS_OP_DGRAD, TS_OP_WGRAD, TS_OP_TRANSPOSE = 0, 1, 2, 3
+TS_POOL_MAX, TS_POOL_AVG = 0, 1
 TS_TILE, TS_MAX_KVOL = 16, 64
 
 _DT = {torch.float32: TS_F32, torch.float16: TS_F16, torch.bfloat16: TS_BF16}
@@ -86,6 +87,7 @@ _lib_conv_fwd_generative = _sig("ts_conv_fwd_generative", _i32,
                                  _vp, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _vp, _sz, _vp])
 _lib_conv_transpose_fwd = _sig("ts_conv_transpose_fwd", _i32,
                                [_P, _vp, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _vp, _sz, _vp])
+_lib_pool_fwd = _sig("ts_pool_fwd", _i32, [_P, _vp, _i32, _vp, _i32, _i32, _i32, _vp])
 _lib_conv_bwd_dgrad = _sig("ts_conv_bwd_dgrad", _i32, [_P, _vp, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _vp, _sz, _vp])
 _lib_conv_bwd_wgrad = _sig("ts_conv_bwd_wgrad", _i32, [_P, _vp, _i32, _vp, _i32, _i32, _vp, _vp, _sz, _vp])
 
@@ -93,7 +95,8 @@ EXPORTED = ["ts_status_string", "ts_version", "ts_hash_capacity", "ts_hash_table
             "ts_hash_query", "ts_support_scratch_bytes", "ts_strided_support", "ts_generative_scratch_bytes",
             "ts_generative_support", "ts_transposed_support", "ts_kmap_bytes", "ts_kmap_build",
             "ts_conv_workspace_bytes", "ts_conv_fwd", "ts_subm_conv_fwd", "ts_conv_fwd_strided",
-            "ts_conv_fwd_generative", "ts_conv_transpose_fwd", "ts_conv_bwd_dgrad", "ts_conv_bwd_wgrad"]
+            "ts_conv_fwd_generative", "ts_conv_transpose_fwd", "ts_pool_fwd", "ts_conv_bwd_dgrad",
+            "ts_conv_bwd_wgrad"]
 
 
 class TsError(RuntimeError):
@@ -233,6 +236,11 @@ def ts_conv_transpose_fwd(kmap, x, w, y, dataflow=TS_DATAFLOW_AUTO, ws=None, str
     _check(_lib_conv_transpose_fwd(ctypes.byref(kmap), _p(x), x.shape[1], _p(w), w.shape[2], _p(y), _dt(x), _dt(y),
                                    dataflow, _p(ws), 0 if ws is None else ws.numel(), _stream(stream)),
            "ts_conv_transpose_fwd")
+
+
+def ts_pool_fwd(kmap, x, y, mode=TS_POOL_MAX, stream=None) -> None:
+    _check(_lib_pool_fwd(ctypes.byref(kmap), _p(x), x.shape[1], _p(y), _dt(x), _dt(y), mode, _stream(stream)),
+           "ts_pool_fwd")
 
 
 def ts_conv_bwd_dgrad(kmap, dy, w, dx, dataflow=TS_DATAFLOW_AUTO, ws=None, stream=None) -> None:
@@ -425,6 +433,13 @@ def conv_transpose(kmap: Kmap, x: torch.Tensor, w: torch.Tensor, out_dtype=None,
     if ws is None:
         ws = workspace(kmap, w.shape[1], w.shape[2], TS_OP_TRANSPOSE, x.dtype, dataflow)
     ts_conv_transpose_fwd(kmap.s, x, w, y, dataflow, ws, stream)
+    return y
+
+
+def pool(kmap: Kmap, x: torch.Tensor, mode: int = TS_POOL_MAX, out_dtype=None, stream=None) -> torch.Tensor:
+    """Max / average pooling over the map: y on the map's output rows."""
+    y = torch.empty((kmap.s.n_out_cap, x.shape[1]), dtype=out_dtype or x.dtype, device=x.device)
+    ts_pool_fwd(kmap.s, x, y, mode, stream)
     return y
 
 

@@ -340,6 +340,19 @@ ts_status ts_conv_transpose_fwd(const ts_kmap* map, const void* x, int cin, cons
                                 ts_dtype in_dtype, ts_dtype out_dtype, ts_dataflow dataflow, void* ws,
                                 size_t ws_bytes, hipStream_t stream);
 
+/* Sparse pooling over a kernel map (torch-lattice page, "What remains
+ * familiar": the CUDA kernels cover pooling, over the same maps as
+ * convolution): y[n_out][c] = the maximum (TS_POOL_MAX) or the mean
+ * (TS_POOL_AVG) of x[i] over the map's triples (i, j, o) of output row j --
+ * the inputs present in the window, not K^D -- and 0 for an output with
+ * none.  x is [n_in][c] (fp32/fp16/bf16), y fp32 or the input type; the
+ * maximum is exact in either, the mean is accumulated in fp32 and rounded to
+ * nearest even.  Rows of y at or past *n_out are not written. */
+#define TS_POOL_MAX 0
+#define TS_POOL_AVG 1
+ts_status ts_pool_fwd(const ts_kmap* map, const void* x, int c, void* y, ts_dtype in_dtype, ts_dtype out_dtype,
+                      int mode, hipStream_t stream);
+
 /* dx[n_in][cin] = sum over triples (i, j, o) of dy[j] . W[o]^T.  Strided
  * maps need TS_KMAP_BWD (implicit GEMM) or TS_KMAP_PAIRS (gather-scatter). */
 ts_status ts_conv_bwd_dgrad(const ts_kmap* map, const void* dy, int cout, const void* w, int cin, void* dx,
