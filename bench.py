@@ -8,7 +8,8 @@ JSON line reports map-valid TFLOP/s of that step (2 * pairs * Cin * Cout per
 replay time), the per-stage times of eager launches taken with HIP events on
 the launch stream, the roofline position of the dominant kernel, and the CPU
 oracle timed on this host.  The other workloads (strided 64 -> 128 downsampling,
-the transposed convolutions back up from it, the generative stride-1
+the transposed convolutions back up from it, max / average pooling over its
+map, the generative stride-1
 convolution of the scene, the 2-D pixel tracks, the bf16 128-channel
 training step) are measured the same way and reported under
 "secondary".
@@ -22,7 +23,7 @@ write that evicts the caches.  A copy of the ring scan with its rows in
 random order is measured as a secondary workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
-                       [--only lidar|lidar_shuffled|down|up|generative|pixels|train]
+                       [--only lidar|lidar_shuffled|down|up|pool|generative|pixels|train]
                        [--copy-calib MB]
 """
 from __future__ import annotations
@@ -534,6 +535,30 @@ def measure_up(ts, steps, warmup):
             "err_flags": int(s.flags.item())}
 
 
+def measure_pool(ts, steps, warmup):
+    """Max pooling k2 s2 of 64 fp16 channels over the two-scene strided map
+    (the map is built at set-up, as the layer that owns it would)."""
+    w = synth.make("down")
+    dev = torch.device("cuda")
+    coords = torch.from_numpy(w.coords).to(dev)
+    table = ts.HashTable(coords, 2.0)
+    out, n_out, out_table = ts.strided_support(coords, 2)
+    km = ts.build_kmap(coords, table, 2, 2, ts.TS_KMAP_NATURAL, out_coords=out, n_out=n_out, out_table=out_table)
+    x = w.x.to(dev)
+    y = torch.empty((km.s.n_out_cap, x.shape[1]), dtype=x.dtype, device=dev)
+    names = ["max", "avg"]
+    fns = [lambda: ts.ts_pool_fwd(km.s, x, y, ts.TS_POOL_MAX), lambda: ts.ts_pool_fwd(km.s, x, y, ts.TS_POOL_AVG)]
+    _, st = run_steps(fns, names, steps, warmup)
+    ms, _ = run_graph(capture(fns[:1]), steps, warmup)
+    n, m = coords.shape[0], int(n_out.item())
+    alg = n * 64 * 2 + m * 64 * 2 + m * (4 + 8 + 8 * 4)  # x read, y written, tile rows + masks + neighbours
+    # one kernel per step: a graph replay adds its own launch cost, so the
+    # bandwidth is taken from the event-timed stage
+    return {"workload": "pool", "n_in": n, "n_out": m, "stages_us": {k: round(v, 3) for k, v in st.items()},
+            "ms_per_step_max_graph": ms, "alg_bytes": alg, "max_gbs": alg / (st["max"] * 1e-6) / 1e9,
+            "avg_gbs": alg / (st["avg"] * 1e-6) / 1e9}
+
+
 def measure_down(ts, steps, warmup):
     w = synth.make("down")
     s = setup_down(ts, w)
@@ -659,7 +684,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--only", default=None,
-                    help="measure one workload (lidar, lidar_shuffled, down, up, generative, pixels, train)")
+                    help="measure one workload (lidar, lidar_shuffled, down, up, pool, generative, pixels, train)")
     ap.add_argument("--copy-calib", type=int, default=0, help="run only a plain copy of this many MiB")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -673,15 +698,15 @@ def main():
 
     torch.cuda.synchronize()
     if args.only and args.only != "lidar":
-        fn = {"lidar_shuffled": measure_lidar_shuffled, "down": measure_down, "up": measure_up,
+        fn = {"lidar_shuffled": measure_lidar_shuffled, "down": measure_down, "up": measure_up, "pool": measure_pool,
               "generative": measure_generative, "pixels": measure_pixels, "train": measure_train}[args.only]
         print(json.dumps(fn(ts, args.steps, args.warmup)))
         return
     w, r = measure_lidar(ts, args.steps, args.warmup)
     secondary = []
     if args.only is None:
-        for fn in (measure_lidar_shuffled, measure_down, measure_up, measure_generative, measure_pixels,
-                   measure_train):
+        for fn in (measure_lidar_shuffled, measure_down, measure_up, measure_pool, measure_generative,
+                   measure_pixels, measure_train):
             secondary.append(fn(ts, args.steps, args.warmup))
     value = r["flop_per_step"] / (r["ms_per_step"] * 1e-3) / 1e12
     conv_s = r["stages_us"]["conv"] * 1e-6

@@ -248,9 +248,17 @@ struct PoolK {
   int kvol, c, nchunk;
   const void* src;
   void* dst;
+  bool vec;  // channels a multiple of 8 and both buffers aligned to a whole vector
 };
 
-template <typename T, typename OT, int MODE>
+// Eight consecutive channels as one vector (16 bytes of fp16/bf16, 32 of
+// fp32), for rows whose channel count is a multiple of 8.
+template <typename T>
+struct Vec8 {
+  typedef T v __attribute__((ext_vector_type(8)));
+};
+
+template <typename T, typename OT, int MODE, bool VEC>
 __global__ __launch_bounds__(256) void k_pool(PoolK a) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (i >= a.slots * a.nchunk) return;
@@ -269,15 +277,31 @@ __global__ __launch_bounds__(256) void k_pool(PoolK a) {
     if (nb < 0) continue;
     const T* xs = src + static_cast<int64_t>(nb) * a.c + c0;
     ++count;
+    if (VEC) {
+      const typename Vec8<T>::v v8 = *reinterpret_cast<const typename Vec8<T>::v*>(xs);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      if (c0 + e >= a.c) break;
-      const float v = to_f32(xs[e]);
-      acc[e] = MODE == TS_POOL_MAX ? fmaxf(acc[e], v) : acc[e] + v;
+      for (int e = 0; e < 8; ++e) {
+        const float v = to_f32(v8[e]);
+        acc[e] = MODE == TS_POOL_MAX ? fmaxf(acc[e], v) : acc[e] + v;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (c0 + e >= a.c) break;
+        const float v = to_f32(xs[e]);
+        acc[e] = MODE == TS_POOL_MAX ? fmaxf(acc[e], v) : acc[e] + v;
+      }
     }
   }
   OT* out = static_cast<OT*>(a.dst) + static_cast<int64_t>(row) * a.c + c0;
   const float inv = count > 0 ? 1.f / static_cast<float>(count) : 0.f;
+  if (VEC) {
+    typename Vec8<OT>::v o8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o8[e] = from_f32<OT>(count == 0 ? 0.f : (MODE == TS_POOL_MAX ? acc[e] : acc[e] * inv));
+    *reinterpret_cast<typename Vec8<OT>::v*>(out) = o8;
+    return;
+  }
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     if (c0 + e >= a.c) break;
@@ -289,8 +313,13 @@ __global__ __launch_bounds__(256) void k_pool(PoolK a) {
 template <typename T, typename OT>
 static hipError_t pool_mode(const PoolK& k, int mode, hipStream_t s) {
   const unsigned grid = static_cast<unsigned>(ceil_div<int64_t>(k.slots * k.nchunk, 256));
-  if (mode == TS_POOL_MAX) k_pool<T, OT, TS_POOL_MAX><<<grid, 256, 0, s>>>(k);
-  else k_pool<T, OT, TS_POOL_AVG><<<grid, 256, 0, s>>>(k);
+  if (mode == TS_POOL_MAX) {
+    if (k.vec) k_pool<T, OT, TS_POOL_MAX, true><<<grid, 256, 0, s>>>(k);
+    else k_pool<T, OT, TS_POOL_MAX, false><<<grid, 256, 0, s>>>(k);
+  } else {
+    if (k.vec) k_pool<T, OT, TS_POOL_AVG, true><<<grid, 256, 0, s>>>(k);
+    else k_pool<T, OT, TS_POOL_AVG, false><<<grid, 256, 0, s>>>(k);
+  }
   return hipGetLastError();
 }
 
@@ -316,6 +345,8 @@ hipError_t launch_pool(const ts_rel& rel, int kvol, const void* x, int c, void* 
   k.nchunk = (c + 7) / 8;
   k.src = x;
   k.dst = y;
+  const uintptr_t in_vec = 8 * (in == TS_F32 ? 4 : 2), out_vec = 8 * (out == TS_F32 ? 4 : 2);
+  k.vec = c % 8 == 0 && reinterpret_cast<uintptr_t>(x) % in_vec == 0 && reinterpret_cast<uintptr_t>(y) % out_vec == 0;
   switch (in) {
     case TS_F32: return pool_out<float>(k, out, mode, s);
     case TS_F16: return pool_out<_Float16>(k, out, mode, s);

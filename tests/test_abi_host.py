@@ -270,3 +270,15 @@ def test_transposed_rejects(ts):
     # workspace of the transposed op: the packed weights (kvol * Cout * Cin)
     km.kvol = 8
     assert ts._lib_conv_workspace_bytes(ctypes.byref(km), 128, 64, ts.TS_OP_TRANSPOSE, ts.TS_F16, 0) == 8 * 128 * 64 * 2
+
+
+def test_pool_rejects_host(ts):
+    km = ts.TsKmap()
+    ref = ctypes.byref(km)
+    assert ts._lib_pool_fwd(ref, FAKE, 8, FAKE, 1, 1, 0, None) == ts.TS_ERR_INVALID_ARG   # unbuilt map
+    km.kvol, km.stride, km.n_in, km.n_out_cap = 8, 2, 100, 60
+    km.fwd.tile_mask, km.fwd.n_tiles = 0x2000, 4
+    assert ts._lib_pool_fwd(ref, FAKE, 0, FAKE, 1, 1, 0, None) == ts.TS_ERR_INVALID_ARG   # no channels
+    assert ts._lib_pool_fwd(ref, FAKE, 8, FAKE, 1, 1, 2, None) == ts.TS_ERR_INVALID_ARG   # mode
+    assert ts._lib_pool_fwd(ref, FAKE, 8, FAKE, 1, 2, 0, None) == ts.TS_ERR_UNSUPPORTED   # f16 -> bf16
+    assert ts._lib_pool_fwd(ref, None, 8, FAKE, 1, 1, 0, None) == ts.TS_ERR_INVALID_ARG   # no x
