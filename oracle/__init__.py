@@ -61,6 +61,8 @@ def lib():
         L.oracle_conv_wgrad.restype = None
         L.oracle_pool.argtypes = [p, p, i64, p, i32, i32, p, i64]
         L.oracle_pool.restype = None
+        L.oracle_voxelize.argtypes = [p, p, i64, i32, p, p, p, i32, p, p, p]
+        L.oracle_voxelize.restype = i64
         _lib = L
     return _lib
 
@@ -213,6 +215,25 @@ def pool(triples, x, n_out: int, mode: str) -> np.ndarray:
     y = np.empty((n_out, c), np.float64)
     lib().oracle_pool(_ptr(t_in), _ptr(t_out), t_in.shape[0], _ptr(x), c, {"max": 0, "avg": 1}[mode], _ptr(y), n_out)
     return y
+
+
+def voxelize(batch, pos, size, origin, feats):
+    """(voxel coords [M][D+1] int32 in first-occurrence order, voxel of each
+    point [N] (-1 when dropped), mean features [M][C] fp64).  Positions,
+    size and origin are float32; the voxel of a point is decided in float32."""
+    pos = np.ascontiguousarray(np.asarray(pos, dtype=np.float32))
+    n, ndim = pos.shape
+    b = None if batch is None else np.ascontiguousarray(np.asarray(batch, dtype=np.int32))
+    size = np.ascontiguousarray(np.asarray(size, dtype=np.float32))
+    origin = np.ascontiguousarray(np.asarray(origin, dtype=np.float32))
+    f = _f64(feats)
+    c = f.shape[1]
+    out = np.empty((max(n, 1), ndim + 1), np.int32)
+    vox_of = np.empty(max(n, 1), np.int32)
+    y = np.empty((max(n, 1), c), np.float64)
+    m = lib().oracle_voxelize(None if b is None else _ptr(b), _ptr(pos), n, ndim, _ptr(size), _ptr(origin), _ptr(f), c,
+                              _ptr(out), _ptr(vox_of), _ptr(y))
+    return out[:m].copy(), vox_of[:n].copy(), y[:m].copy()
 
 
 def subm_conv(coords, x, w, ksize: int):

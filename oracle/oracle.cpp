@@ -23,6 +23,8 @@
 //     (GenerativeConvTranspose3d) ("Convolution mapping" table);
 //   * pooling runs over the same kernel maps as convolution (torch-lattice
 //     "What remains familiar": CUDA kernels cover pooling);
+//   * voxelization turns points into a sparse tensor and devoxelization
+//     carries voxel features back to the points (same list);
 //   * every dataflow must give the same result for a fixed relation
 //     (input row, output row, kernel offset) and weight tensor.
 //
@@ -56,6 +58,7 @@
 // convolution (torch CPU, fp64), brute-force searches, closed forms and the
 // page's two-voxel example.
 #include <array>
+#include <cmath>
 #include <cstdint>
 #include <cstring>
 #include <unordered_map>
@@ -367,6 +370,48 @@ void oracle_pool(const int32_t* t_in, const int32_t* t_out, int64_t n_pairs, con
     for (int64_t j = 0; j < n_out; ++j)
       if (count[j] > 0)
         for (int ch = 0; ch < c; ++ch) y[j * c + ch] /= static_cast<double>(count[j]);
+}
+
+// Voxelization of points (batch b_i, position p_i in float32): voxel
+// coordinate v_i = floor((p_i - origin) / size) per axis, computed in float32
+// exactly as written (one rounded subtraction, one rounded division), then
+// floored.  Voxels are numbered in order of first occurrence over the points;
+// a point whose voxel leaves the coordinate range (or whose batch is out of
+// range) is dropped (voxel -1).  Voxel features are the mean of the features
+// of their points.  Writes out_coords (up to n rows), vox_of[n], feats
+// [n][c] (the first n_vox rows) and returns n_vox.
+int64_t oracle_voxelize(const int32_t* batch, const float* pos, int64_t n, int ndim, const float* size,
+                        const float* origin, const double* f, int c, int32_t* out_coords, int32_t* vox_of,
+                        double* feats) {
+  Map seen;
+  int64_t n_vox = 0;
+  std::vector<int64_t> count;
+  for (int64_t i = 0; i < n; ++i) {
+    int32_t q[4] = {batch ? batch[i] : 0, 0, 0, 0};
+    for (int d = 0; d < ndim; ++d) {
+      const float rel = pos[i * ndim + d] - origin[d];
+      const float v = std::floor(rel / size[d]);
+      q[d + 1] = (v >= -32768.0f && v <= 32767.0f) ? static_cast<int32_t>(v) : 40000;
+    }
+    if (!in_range(q, ndim)) {
+      vox_of[i] = -1;
+      continue;
+    }
+    auto ins = seen.emplace(key_of(q, ndim), n_vox);
+    if (ins.second) {
+      for (int d = 0; d <= ndim; ++d) out_coords[n_vox * (ndim + 1) + d] = q[d];
+      for (int ch = 0; ch < c; ++ch) feats[n_vox * c + ch] = 0.0;
+      count.push_back(0);
+      ++n_vox;
+    }
+    const int64_t j = ins.first->second;
+    vox_of[i] = static_cast<int32_t>(j);
+    ++count[j];
+    for (int ch = 0; ch < c; ++ch) feats[j * c + ch] += f[i * c + ch];
+  }
+  for (int64_t j = 0; j < n_vox; ++j)
+    for (int ch = 0; ch < c; ++ch) feats[j * c + ch] /= static_cast<double>(count[j]);
+  return n_vox;
 }
 
 // dw[o][ci][co] = sum over triples (i, j, o) of x[i][ci] * dy[j][co].
