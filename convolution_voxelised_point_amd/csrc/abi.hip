@@ -2,6 +2,8 @@
 // Every check that the host can make happens here, before any launch.
 #include <string.h>
 
+#include <cmath>
+
 #include "common.h"
 #include "launch.h"
 
@@ -227,6 +229,34 @@ ts_status ts_transposed_support(const int32_t* in_coords, int64_t n_in, int ndim
   if (stride < 1) return TS_ERR_INVALID_ARG;
   return generated_support(in_coords, n_in, ndim, ksize, stride, stride, 1, out_coords, n_out_cap, n_out, out_table,
                            out_cap, scratch, scratch_bytes, err_flags, stream);
+}
+
+size_t ts_voxelize_scratch_bytes(int64_t n_points) { return n_points < 0 ? 0 : voxelize_scratch_bytes(n_points); }
+
+ts_status ts_voxelize(const int32_t* batch, const float* pos, int64_t n, int ndim, const float* size,
+                      const float* origin, const float* feats, int c, int32_t* out_coords, int64_t* n_out,
+                      void* out_table, int64_t out_cap, int32_t* vox_of, float* out_feats, void* scratch,
+                      size_t scratch_bytes, uint32_t* err_flags, hipStream_t stream) {
+  if (ndim != 2 && ndim != 3) return TS_ERR_INVALID_ARG;
+  if (n < 0 || n > kMaxRows || !n_out || !out_table || !size || !origin) return TS_ERR_INVALID_ARG;
+  if (n > 0 && (!pos || !out_coords || !vox_of)) return TS_ERR_INVALID_ARG;
+  for (int d = 0; d < ndim; ++d)
+    if (!(size[d] > 0.f) || !std::isfinite(size[d]) || !std::isfinite(origin[d])) return TS_ERR_INVALID_ARG;
+  if (feats && (c < 1 || c > kMaxChannels || (n > 0 && !out_feats))) return TS_ERR_INVALID_ARG;
+  if (!is_pow2(out_cap)) return TS_ERR_INVALID_ARG;
+  if (out_cap > kMaxCap) return TS_ERR_UNSUPPORTED;
+  if (!scratch || scratch_bytes < voxelize_scratch_bytes(n)) return TS_ERR_INVALID_ARG;
+  TS_TRY(launch_voxelize(batch, pos, n, ndim, size, origin, feats, feats ? c : 0, out_coords, n_out, out_table,
+                         out_cap, vox_of, out_feats, scratch, err_flags, stream));
+  return TS_OK;
+}
+
+ts_status ts_devoxelize(const int32_t* vox_of, int64_t n, const void* vox_feats, int c, void* point_feats,
+                        ts_dtype dtype, hipStream_t stream) {
+  if (n < 0 || n > kMaxRows || c < 1 || c > kMaxChannels || !dtype_ok(dtype)) return TS_ERR_INVALID_ARG;
+  if (n > 0 && (!vox_of || !vox_feats || !point_feats)) return TS_ERR_INVALID_ARG;
+  TS_TRY(launch_devoxelize(vox_of, n, vox_feats, c, point_feats, dtype, stream));
+  return TS_OK;
 }
 
 size_t ts_kmap_bytes(int64_t n_in, int64_t n_out_cap, int ndim, int ksize, int stride, uint32_t flags) {

@@ -336,4 +336,164 @@ hipError_t launch_generative_support(const int32_t* coords, int64_t n, int ndim,
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Voxelization: point i goes to voxel floor((p_i - origin) / size) per axis,
+// decided in float32 (a rounded subtraction, a division rounded to nearest
+// even, a floor).  The smallest point index owns each voxel (NOT of it raised
+// with atomicMax in the voxel's cell), voxels are numbered in that order by
+// the flag / scan / emit steps of the strided support, and the table is left
+// mapping each voxel to its row.  Each point then reads its voxel row back,
+// and the features are summed per voxel with float atomics (the order of the
+// additions is not fixed) and divided by the point count.
+// ---------------------------------------------------------------------------
+struct VoxGeo {
+  float size[3];
+  float origin[3];
+};
+
+__device__ __forceinline__ bool vox_cell(const int32_t* batch, const float* pos, int64_t i, int ndim,
+                                         const VoxGeo& g, int64_t* b, int64_t* q) {
+  *b = batch ? batch[i] : 0;
+  q[0] = q[1] = q[2] = 0;
+  for (int d = 0; d < ndim; ++d) {
+    const float rel = pos[i * ndim + d] - g.origin[d];
+    const float v = floorf(__fdiv_rn(rel, g.size[d]));
+    if (!(v >= -32768.f && v <= 32767.f)) return false;  // NaN fails too
+    q[d] = static_cast<int64_t>(v);
+  }
+  return true;
+}
+
+__global__ __launch_bounds__(256) void k_vox_insert(const int32_t* __restrict__ batch, const float* __restrict__ pos,
+                                                    int64_t n, VoxGeo g, Table t, uint32_t* flags,
+                                                    int32_t* __restrict__ cell_at) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  uint64_t key = 0;
+  const bool in = i < n;
+  bool valid = false;
+  if (in) {
+    int64_t b, q[3];
+    valid = vox_cell(batch, pos, i, t.nd, g, &b, q) && make_key(t.nd, b, q, &key);
+  }
+  const int32_t sl = run_slot(t, block_key(key, t.nd), valid, flags);
+  if (!in) return;
+  int32_t at = -1;
+  if (!valid) {
+    if (flags) atomicOr(flags, TS_FLAG_RANGE);
+  } else if (sl >= 0) {
+    at = sl * kCells + cell_of(key, t.nd);
+    atomicMax(reinterpret_cast<unsigned*>(t.cells) + at, cell_enc(i));
+  }
+  cell_at[i] = at;
+}
+
+__global__ __launch_bounds__(256) void k_vox_emit(const int32_t* __restrict__ batch, const float* __restrict__ pos,
+                                                  int64_t n, int ndim, VoxGeo g, const int32_t* __restrict__ cell_at,
+                                                  const int32_t* __restrict__ first, const int32_t* __restrict__ index,
+                                                  Table t, int32_t* __restrict__ out_coords) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= n || !first[i]) return;
+  const int32_t j = index[i];
+  int64_t b, q[3];
+  vox_cell(batch, pos, i, ndim, g, &b, q);
+  int32_t* o = out_coords + static_cast<int64_t>(j) * (ndim + 1);
+  o[0] = static_cast<int32_t>(b);
+  for (int d = 0; d < ndim; ++d) o[1 + d] = static_cast<int32_t>(q[d]);
+  t.cells[cell_at[i]] = static_cast<int32_t>(cell_enc(j));
+}
+
+// Voxel row of every point (-1 when dropped); with features, their sum and
+// count per voxel (out_feats and counts start at zero).
+__global__ __launch_bounds__(256) void k_vox_assign(const int32_t* __restrict__ cell_at, int64_t n, Table t,
+                                                    int32_t* __restrict__ vox_of, const float* __restrict__ f,
+                                                    int c, float* __restrict__ out_feats, int32_t* __restrict__ counts) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int32_t at = cell_at[i];
+  const int32_t v = at >= 0 ? cell_row(static_cast<uint32_t>(t.cells[at])) : -1;
+  vox_of[i] = v;
+  if (v < 0 || !f) return;
+  atomicAdd(counts + v, 1);
+  for (int ch = 0; ch < c; ++ch) atomicAdd(out_feats + static_cast<int64_t>(v) * c + ch, f[i * c + ch]);
+}
+
+__global__ __launch_bounds__(256) void k_vox_mean(float* __restrict__ out_feats, const int32_t* __restrict__ counts,
+                                                  int64_t n_cap, const int64_t* n_out, int c) {
+  const int64_t k = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t n = *n_out < n_cap ? *n_out : n_cap;
+  if (k >= n * c) return;
+  const int32_t cnt = counts[k / c];
+  out_feats[k] = cnt > 0 ? out_feats[k] / static_cast<float>(cnt) : 0.f;
+}
+
+__global__ __launch_bounds__(256) void k_zero_f32(float* __restrict__ p, int64_t n) {
+  const int64_t k = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (k < n) p[k] = 0.f;
+}
+
+size_t voxelize_scratch_bytes(int64_t n) {
+  const size_t a = align_up(static_cast<size_t>(n) * 4, 256);
+  return 4 * a + scan_tmp_bytes(n);
+}
+
+hipError_t launch_voxelize(const int32_t* batch, const float* pos, int64_t n, int ndim, const float* size,
+                           const float* origin, const float* feats, int c, int32_t* out_coords, int64_t* n_out,
+                           void* out_table, int64_t out_cap, int32_t* vox_of, float* out_feats, void* scratch,
+                           uint32_t* flags, hipStream_t s) {
+  Table t = table_view(out_table, out_cap, ndim);
+  VoxGeo g{};
+  for (int d = 0; d < ndim; ++d) {
+    g.size[d] = size[d];
+    g.origin[d] = origin[d];
+  }
+  const size_t a = align_up(static_cast<size_t>(n) * 4, 256);
+  char* p = static_cast<char*>(scratch);
+  int32_t* cell_at = reinterpret_cast<int32_t*>(p);
+  int32_t* first = reinterpret_cast<int32_t*>(p + a);
+  int32_t* index = reinterpret_cast<int32_t*>(p + 2 * a);
+  int32_t* counts = reinterpret_cast<int32_t*>(p + 3 * a);
+  void* tmp = p + 4 * a;
+  k_table_clear<<<static_cast<unsigned>(ceil_div<int64_t>(out_cap, 256)), 256, 0, s>>>(t, out_cap);
+  if (n == 0) return fill_i64(n_out, 1, 0, s);
+  const unsigned g1 = static_cast<unsigned>(ceil_div<int64_t>(n, 256));
+  if (feats) {
+    k_zero_f32<<<static_cast<unsigned>(ceil_div<int64_t>(n * c, 256)), 256, 0, s>>>(out_feats, n * c);
+    k_zero_f32<<<g1, 256, 0, s>>>(reinterpret_cast<float*>(counts), n);  // zero bits: int 0
+  }
+  k_vox_insert<<<g1, 256, 0, s>>>(batch, pos, n, g, t, flags, cell_at);
+  k_down_flag<<<g1, 256, 0, s>>>(cell_at, n, t, first);
+  hipError_t e = scan_exclusive_i32(first, index, n, n_out, tmp, s);
+  if (e != hipSuccess) return e;
+  k_vox_emit<<<g1, 256, 0, s>>>(batch, pos, n, ndim, g, cell_at, first, index, t, out_coords);
+  k_vox_assign<<<g1, 256, 0, s>>>(cell_at, n, t, vox_of, feats, c, out_feats, counts);
+  if (feats)
+    k_vox_mean<<<static_cast<unsigned>(ceil_div<int64_t>(n * c, 256)), 256, 0, s>>>(out_feats, counts, n, n_out, c);
+  return hipGetLastError();
+}
+
+// Devoxelization: every point takes its voxel's features (0 when dropped).
+template <typename T>
+__global__ __launch_bounds__(256) void k_devox(const int32_t* __restrict__ vox_of, int64_t n, const T* __restrict__ vf,
+                                               int c, T* __restrict__ pf) {
+  const int64_t k = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (k >= n * c) return;
+  const int64_t i = k / c;
+  const int32_t v = vox_of[i];
+  pf[k] = v >= 0 ? vf[static_cast<int64_t>(v) * c + (k - i * c)] : T(0);
+}
+
+hipError_t launch_devoxelize(const int32_t* vox_of, int64_t n, const void* vf, int c, void* pf, ts_dtype dt,
+                             hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const unsigned g = static_cast<unsigned>(ceil_div<int64_t>(n * c, 256));
+  switch (dt) {
+    case TS_F32: k_devox<float><<<g, 256, 0, s>>>(vox_of, n, static_cast<const float*>(vf), c, static_cast<float*>(pf)); break;
+    case TS_F16:
+      k_devox<_Float16><<<g, 256, 0, s>>>(vox_of, n, static_cast<const _Float16*>(vf), c, static_cast<_Float16*>(pf));
+      break;
+    default: k_devox<__bf16><<<g, 256, 0, s>>>(vox_of, n, static_cast<const __bf16*>(vf), c, static_cast<__bf16*>(pf)); break;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace ts

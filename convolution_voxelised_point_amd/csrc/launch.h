@@ -39,6 +39,14 @@ hipError_t launch_generative_support(const int32_t* coords, int64_t n, int ndim,
                                      int32_t* out_coords, int64_t n_out_cap, int64_t* n_out, void* out_table,
                                      int64_t out_cap, void* scratch, uint32_t* flags, hipStream_t s);
 
+size_t voxelize_scratch_bytes(int64_t n);
+hipError_t launch_voxelize(const int32_t* batch, const float* pos, int64_t n, int ndim, const float* size,
+                           const float* origin, const float* feats, int c, int32_t* out_coords, int64_t* n_out,
+                           void* out_table, int64_t out_cap, int32_t* vox_of, float* out_feats, void* scratch,
+                           uint32_t* flags, hipStream_t s);
+hipError_t launch_devoxelize(const int32_t* vox_of, int64_t n, const void* vf, int c, void* pf, ts_dtype dt,
+                             hipStream_t s);
+
 // kmap.hip
 enum RelMode { kModeSubm = 0, kModeDown = 1, kModeUp = 2 };
 

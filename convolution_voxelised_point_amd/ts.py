@@ -73,6 +73,10 @@ _lib_generative_support = _sig("ts_generative_support", _i32,
                                [_vp, _i64, _i32, _i32, _vp, _i64, _vp, _vp, _i64, _vp, _sz, _vp, _vp])
 _lib_transposed_support = _sig("ts_transposed_support", _i32,
                                [_vp, _i64, _i32, _i32, _i32, _vp, _i64, _vp, _vp, _i64, _vp, _sz, _vp, _vp])
+_lib_voxelize_scratch_bytes = _sig("ts_voxelize_scratch_bytes", _sz, [_i64])
+_lib_voxelize = _sig("ts_voxelize", _i32, [_vp, _vp, _i64, _i32, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _i64, _vp, _vp, _vp,
+                                           _sz, _vp, _vp])
+_lib_devoxelize = _sig("ts_devoxelize", _i32, [_vp, _i64, _vp, _i32, _vp, _i32, _vp])
 _lib_kmap_bytes = _sig("ts_kmap_bytes", _sz, [_i64, _i64, _i32, _i32, _i32, _u32])
 _lib_kmap_build = _sig("ts_kmap_build", _i32, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _i64, _i32, _i32, _i32, _u32,
                                                _vp, _sz, _P, _vp])
@@ -93,7 +97,8 @@ _lib_conv_bwd_wgrad = _sig("ts_conv_bwd_wgrad", _i32, [_P, _vp, _i32, _vp, _i32,
 
 EXPORTED = ["ts_status_string", "ts_version", "ts_hash_capacity", "ts_hash_table_bytes", "ts_hash_build",
             "ts_hash_query", "ts_support_scratch_bytes", "ts_strided_support", "ts_generative_scratch_bytes",
-            "ts_generative_support", "ts_transposed_support", "ts_kmap_bytes", "ts_kmap_build",
+            "ts_generative_support", "ts_transposed_support", "ts_voxelize_scratch_bytes", "ts_voxelize",
+            "ts_devoxelize", "ts_kmap_bytes", "ts_kmap_build",
             "ts_conv_workspace_bytes", "ts_conv_fwd", "ts_subm_conv_fwd", "ts_conv_fwd_strided",
             "ts_conv_fwd_generative", "ts_conv_transpose_fwd", "ts_pool_fwd", "ts_conv_bwd_dgrad",
             "ts_conv_bwd_wgrad"]
@@ -183,6 +188,26 @@ def ts_transposed_support(in_coords, ksize, stride, out_coords, n_out, out_table
                                    _p(out_coords), out_coords.shape[0], _p(n_out), _p(out_table), out_cap,
                                    _p(scratch), scratch.numel(), _p(err_flags), _stream(stream)),
            "ts_transposed_support")
+
+
+def ts_voxelize_scratch_bytes(n: int) -> int:
+    return int(_lib_voxelize_scratch_bytes(n))
+
+
+def ts_voxelize(batch, pos, size, origin, feats, out_coords, n_out, out_table, out_cap, vox_of, out_feats, scratch,
+                err_flags=None, stream=None) -> None:
+    ndim = pos.shape[1]
+    sz = (ctypes.c_float * ndim)(*[float(v) for v in size])
+    og = (ctypes.c_float * ndim)(*[float(v) for v in origin])
+    c = 0 if feats is None else feats.shape[1]
+    _check(_lib_voxelize(_p(batch), _p(pos), pos.shape[0], ndim, sz, og, _p(feats), c, _p(out_coords), _p(n_out),
+                         _p(out_table), out_cap, _p(vox_of), _p(out_feats), _p(scratch), scratch.numel(), _p(err_flags),
+                         _stream(stream)), "ts_voxelize")
+
+
+def ts_devoxelize(vox_of, vox_feats, point_feats, stream=None) -> None:
+    _check(_lib_devoxelize(_p(vox_of), vox_of.shape[0], _p(vox_feats), vox_feats.shape[1], _p(point_feats),
+                           _dt(vox_feats), _stream(stream)), "ts_devoxelize")
 
 
 def ts_kmap_bytes(n_in: int, n_out_cap: int, ndim: int, ksize: int, stride: int, flags: int) -> int:
@@ -441,6 +466,22 @@ def pool(kmap: Kmap, x: torch.Tensor, mode: int = TS_POOL_MAX, out_dtype=None, s
     y = torch.empty((kmap.s.n_out_cap, x.shape[1]), dtype=out_dtype or x.dtype, device=x.device)
     ts_pool_fwd(kmap.s, x, y, mode, stream)
     return y
+
+
+def voxelize(pos: torch.Tensor, size, origin, feats: Optional[torch.Tensor] = None,
+             batch: Optional[torch.Tensor] = None, rsv_ratio: float = 2.0, err_flags=None, stream=None):
+    """(voxel coords [capacity n], n_out device scalar, voxel table, vox_of [n],
+    mean features [capacity n] or None)."""
+    n, ndim = pos.shape
+    out = torch.zeros((max(n, 1), ndim + 1), dtype=torch.int32, device=pos.device)
+    n_out = torch.zeros(1, dtype=torch.int64, device=pos.device)
+    table = HashTable.with_capacity(ndim, ts_hash_capacity(n, rsv_ratio), pos.device)
+    vox_of = torch.empty(max(n, 1), dtype=torch.int32, device=pos.device)
+    of = None if feats is None else torch.empty((max(n, 1), feats.shape[1]), dtype=torch.float32, device=pos.device)
+    scratch = _bytes(ts_voxelize_scratch_bytes(n), pos.device)
+    ts_voxelize(batch, pos, size, origin, feats, out, n_out, table.buf, table.cap, vox_of, of, scratch, err_flags,
+                stream)
+    return out, n_out, table, vox_of[:n], of
 
 
 def workspace(kmap: Kmap, cin: int, cout: int, op: int, dtype: torch.dtype, dataflow: int = TS_DATAFLOW_AUTO):

@@ -191,6 +191,37 @@ ts_status ts_transposed_support(const int32_t* in_coords, int64_t n_in, int ndim
                                 uint32_t* err_flags, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Voxelization and devoxelization (torch-lattice page, "What remains
+ * familiar": the CUDA kernels cover voxelization and devoxelization).
+ *
+ * Point i (batch[i], or 0 when batch is NULL; position pos[i][ndim], device
+ * float32) goes to voxel floor((pos - origin) / size) per axis, decided in
+ * float32: a rounded subtraction, a division rounded to nearest even and a
+ * floor (size and origin are host arrays of ndim floats; size > 0).  A point
+ * whose voxel or batch leaves the packable range is dropped (vox_of = -1)
+ * and raises TS_FLAG_RANGE.  Voxels are numbered in order of first
+ * occurrence over the points: out_coords (device int32, capacity n rows)
+ * receives them, *n_out (device int64) their count, vox_of[n] (device) each
+ * point's voxel row, and out_table (zero-filled before its first use, out_cap
+ * a power of two) maps each voxel to its row, so it serves as the input
+ * table of a kernel map without a hash build.  With feats (device
+ * [n][c] float32; may be NULL), out_feats (device [n][c] float32) receives
+ * the mean of each voxel's point features in its first *n_out rows; the sums
+ * use float atomics, so their order (and the last bits) may vary between
+ * runs.  scratch (device) needs ts_voxelize_scratch_bytes(n).
+ * ---------------------------------------------------------------------- */
+size_t ts_voxelize_scratch_bytes(int64_t n_points);
+ts_status ts_voxelize(const int32_t* batch, const float* pos, int64_t n, int ndim, const float* size,
+                      const float* origin, const float* feats, int c, int32_t* out_coords, int64_t* n_out,
+                      void* out_table, int64_t out_cap, int32_t* vox_of, float* out_feats, void* scratch,
+                      size_t scratch_bytes, uint32_t* err_flags, hipStream_t stream);
+
+/* Devoxelization: point_feats[i] = vox_feats[vox_of[i]] ([n][c], any feature
+ * type), or zeros for a dropped point (vox_of[i] = -1). */
+ts_status ts_devoxelize(const int32_t* vox_of, int64_t n, const void* vox_feats, int c, void* point_feats,
+                        ts_dtype dtype, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Kernel map (the "kernel-map construction" of the page's section "Sparse
  * tensor expectations"): for every output row j and offset o, the input row
  * i at q_j + delta_o (stride 1) or s q_j + delta_o (stride s), as a relation
