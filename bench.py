@@ -7,7 +7,8 @@ step's launches are captured once in a HIP graph and replayed; the printed
 JSON line reports map-valid TFLOP/s of that step (2 * pairs * Cin * Cout per
 replay time), the per-stage times of eager launches taken with HIP events on
 the launch stream, the roofline position of the dominant kernel, and the CPU
-oracle timed on this host.  The other workloads (strided 64 -> 128 downsampling,
+oracle timed on this host.  The other workloads (voxelization of the scene's
+points, strided 64 -> 128 downsampling,
 the transposed convolutions back up from it, max / average pooling over its
 map, the generative stride-1
 convolution of the scene, the 2-D pixel tracks, the bf16 128-channel
@@ -23,7 +24,7 @@ write that evicts the caches.  A copy of the ring scan with its rows in
 random order is measured as a secondary workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
-                       [--only lidar|lidar_shuffled|down|up|pool|generative|pixels|train]
+                       [--only lidar|lidar_shuffled|voxelize|down|up|pool|generative|pixels|train]
                        [--copy-calib MB]
 """
 from __future__ import annotations
@@ -559,6 +560,34 @@ def measure_pool(ts, steps, warmup):
             "avg_gbs": alg / (st["avg"] * 1e-6) / 1e9}
 
 
+def measure_voxelize(ts, steps, warmup):
+    """Voxelization of the lidar scene's raw points (64 rings x 1500 + 40
+    boxes x 500, float32) at 0.1 m with 4 float32 features per point: voxel
+    coordinates, each point's voxel, the voxel table and the mean features."""
+    w = synth.make("lidar")
+    dev = torch.device("cuda")
+    pos = torch.from_numpy(synth.ring_scan_points(1000 * w.index, 1500, 500).astype("float32")).to(dev)
+    feats = synth.normal(1000 * w.index + 907, (pos.shape[0], 4), 1.0, "f32").to(dev)
+    n = pos.shape[0]
+    out = torch.zeros((n, 4), dtype=torch.int32, device=dev)
+    n_out = torch.zeros(1, dtype=torch.int64, device=dev)
+    table = ts.HashTable.with_capacity(3, ts.ts_hash_capacity(n, 2.0), dev)
+    vox_of = torch.empty(n, dtype=torch.int32, device=dev)
+    of = torch.empty((n, 4), dtype=torch.float32, device=dev)
+    scratch = torch.empty(ts.ts_voxelize_scratch_bytes(n), dtype=torch.uint8, device=dev)
+    flags = torch.zeros(1, dtype=torch.int32, device=dev)
+    size, origin = [0.1, 0.1, 0.1], [-75.0, -75.0, -1.0]
+
+    def vox():
+        ts.ts_voxelize(None, pos, size, origin, feats, out, n_out, table.buf, table.cap, vox_of, of, scratch, flags)
+
+    ms_eager, st = run_steps([vox], ["voxelize"], steps, warmup)
+    ms, _ = run_graph(capture([vox]), steps, warmup)
+    return {"workload": "voxelize", "points": n, "voxels": int(n_out.item()), "ms_per_step": ms,
+            "stages_us": {k: round(v, 3) for k, v in st.items()}, "mpoints_s": n / (ms * 1e-3) / 1e6,
+            "err_flags": int(flags.item())}
+
+
 def measure_down(ts, steps, warmup):
     w = synth.make("down")
     s = setup_down(ts, w)
@@ -684,7 +713,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--only", default=None,
-                    help="measure one workload (lidar, lidar_shuffled, down, up, pool, generative, pixels, train)")
+                    help="measure one workload (lidar, lidar_shuffled, voxelize, down, up, pool, generative, "
+                         "pixels, train)")
     ap.add_argument("--copy-calib", type=int, default=0, help="run only a plain copy of this many MiB")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -698,15 +728,16 @@ def main():
 
     torch.cuda.synchronize()
     if args.only and args.only != "lidar":
-        fn = {"lidar_shuffled": measure_lidar_shuffled, "down": measure_down, "up": measure_up, "pool": measure_pool,
+        fn = {"lidar_shuffled": measure_lidar_shuffled, "voxelize": measure_voxelize, "down": measure_down,
+              "up": measure_up, "pool": measure_pool,
               "generative": measure_generative, "pixels": measure_pixels, "train": measure_train}[args.only]
         print(json.dumps(fn(ts, args.steps, args.warmup)))
         return
     w, r = measure_lidar(ts, args.steps, args.warmup)
     secondary = []
     if args.only is None:
-        for fn in (measure_lidar_shuffled, measure_down, measure_up, measure_pool, measure_generative,
-                   measure_pixels, measure_train):
+        for fn in (measure_lidar_shuffled, measure_voxelize, measure_down, measure_up, measure_pool,
+                   measure_generative, measure_pixels, measure_train):
             secondary.append(fn(ts, args.steps, args.warmup))
     value = r["flop_per_step"] / (r["ms_per_step"] * 1e-3) / 1e12
     conv_s = r["stages_us"]["conv"] * 1e-6

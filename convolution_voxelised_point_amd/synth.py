@@ -24,7 +24,7 @@ the order above) uses ``1000*c + b``; features ``1000*c + 900``; weights
 ``1000*c + 901`` (second pixel layer ``1000*c + 902``); upstream gradient
 ``1000*c + 903``; the row permutation of a shuffled variant ``1000*c + 904``;
 the coarse features and weights of a transposed layer ``1000*c + 905`` and
-``1000*c + 906``.  Low-precision values are drawn in fp32 and rounded to the
+``1000*c + 906``; the per-point features of a voxelization ``1000*c + 907``.  Low-precision values are drawn in fp32 and rounded to the
 storage type with round-to-nearest-even (torch's float conversion).
 
 Ring-scan scene (stands in for the autonomous-driving LiDAR benchmarks, whose

@@ -282,3 +282,32 @@ def test_pool_rejects_host(ts):
     assert ts._lib_pool_fwd(ref, FAKE, 8, FAKE, 1, 1, 2, None) == ts.TS_ERR_INVALID_ARG   # mode
     assert ts._lib_pool_fwd(ref, FAKE, 8, FAKE, 1, 2, 0, None) == ts.TS_ERR_UNSUPPORTED   # f16 -> bf16
     assert ts._lib_pool_fwd(ref, None, 8, FAKE, 1, 1, 0, None) == ts.TS_ERR_INVALID_ARG   # no x
+
+
+def test_voxelize_rejects(ts):
+    V = ts._lib_voxelize
+    sz = (ctypes.c_float * 3)(0.1, 0.1, 0.1)
+    og = (ctypes.c_float * 3)(0.0, 0.0, 0.0)
+    bad = (ctypes.c_float * 3)(0.1, 0.0, 0.1)
+    sb = ts.ts_voxelize_scratch_bytes(100)
+    assert sb >= 4 * 100 * 4
+    ok = [None, FAKE, 100, 3, sz, og, None, 0, FAKE, FAKE, FAKE, 256, FAKE, None, FAKE, sb, None, None]
+
+    def call(i, v):
+        a = list(ok)
+        a[i] = v
+        return V(*a)
+
+    assert call(3, 4) == ts.TS_ERR_INVALID_ARG          # ndim
+    assert call(4, bad) == ts.TS_ERR_INVALID_ARG        # a zero voxel size
+    assert call(1, None) == ts.TS_ERR_INVALID_ARG       # no positions
+    assert call(9, None) == ts.TS_ERR_INVALID_ARG       # n_out
+    assert call(11, 100) == ts.TS_ERR_INVALID_ARG       # table capacity not a power of two
+    assert call(15, sb - 1) == ts.TS_ERR_INVALID_ARG    # short scratch
+    a = list(ok)
+    a[6], a[7] = FAKE, 4                                # features but nowhere to put their means
+    assert V(*a) == ts.TS_ERR_INVALID_ARG
+    D = ts._lib_devoxelize
+    assert D(FAKE, 10, FAKE, 0, FAKE, ts.TS_F32, None) == ts.TS_ERR_INVALID_ARG     # no channels
+    assert D(None, 10, FAKE, 4, FAKE, ts.TS_F32, None) == ts.TS_ERR_INVALID_ARG     # no voxel index
+    assert D(FAKE, 10, FAKE, 4, FAKE, 9, None) == ts.TS_ERR_INVALID_ARG             # dtype
