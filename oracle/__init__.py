@@ -63,6 +63,8 @@ def lib():
         L.oracle_pool.restype = None
         L.oracle_voxelize.argtypes = [p, p, i64, i32, p, p, p, i32, p, p, p]
         L.oracle_voxelize.restype = i64
+        L.oracle_graph_conv.argtypes = [p, p, p, i64, p, i32, p, i32, p]
+        L.oracle_graph_conv.restype = None
         _lib = L
     return _lib
 
@@ -234,6 +236,20 @@ def voxelize(batch, pos, size, origin, feats):
     m = lib().oracle_voxelize(None if b is None else _ptr(b), _ptr(pos), n, ndim, _ptr(size), _ptr(origin), _ptr(f), c,
                               _ptr(out), _ptr(vox_of), _ptr(y))
     return out[:m].copy(), vox_of[:n].copy(), y[:m].copy()
+
+
+def graph_conv(indptr, src, rel, x, w) -> np.ndarray:
+    """Relational graph convolution over CSR edges (grouped by destination):
+    y[v] = sum over v's edges e of x[src[e]] . w[rel[e]]."""
+    indptr = np.ascontiguousarray(np.asarray(indptr, dtype=np.int64))
+    src = np.ascontiguousarray(np.asarray(src, dtype=np.int32))
+    rel = np.ascontiguousarray(np.asarray(rel, dtype=np.int32))
+    x, w = _f64(x), _f64(w)
+    n_dst = indptr.shape[0] - 1
+    cin, cout = w.shape[1], w.shape[2]
+    y = np.empty((max(n_dst, 1), cout), np.float64)
+    lib().oracle_graph_conv(_ptr(indptr), _ptr(src), _ptr(rel), n_dst, _ptr(x), cin, _ptr(w), cout, _ptr(y))
+    return y[:n_dst].copy()
 
 
 def subm_conv(coords, x, w, ksize: int):

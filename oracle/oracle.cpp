@@ -25,6 +25,9 @@
 //     "What remains familiar": CUDA kernels cover pooling);
 //   * voxelization turns points into a sparse tensor and devoxelization
 //     carries voxel features back to the points (same list);
+//   * graph convolution (TorchSparse++ abstract: the library also runs graph
+//     convolutions): a relational sum over incoming edges, of which sparse
+//     convolution is the case "edges = map triples, relations = offsets";
 //   * every dataflow must give the same result for a fixed relation
 //     (input row, output row, kernel offset) and weight tensor.
 //
@@ -412,6 +415,24 @@ int64_t oracle_voxelize(const int32_t* batch, const float* pos, int64_t n, int n
   for (int64_t j = 0; j < n_vox; ++j)
     for (int ch = 0; ch < c; ++ch) feats[j * c + ch] /= static_cast<double>(count[j]);
   return n_vox;
+}
+
+// Graph convolution over edges grouped by destination (CSR): for destination
+// v, edges e in [indptr[v], indptr[v+1]) carry source src[e] and relation
+// rel[e], and y[v][co] = sum over them of sum_ci x[src[e]][ci] *
+// w[rel[e]][ci][co] (no normalisation; 0 for a node without edges).
+void oracle_graph_conv(const int64_t* indptr, const int32_t* src, const int32_t* rel, int64_t n_dst,
+                       const double* x, int cin, const double* w, int cout, double* y) {
+  for (int64_t v = 0; v < n_dst; ++v) {
+    double* yv = y + v * cout;
+    for (int co = 0; co < cout; ++co) yv[co] = 0.0;
+    for (int64_t e = indptr[v]; e < indptr[v + 1]; ++e) {
+      const double* xs = x + static_cast<int64_t>(src[e]) * cin;
+      const double* wr = w + static_cast<int64_t>(rel[e]) * cin * cout;
+      for (int ci = 0; ci < cin; ++ci)
+        for (int co = 0; co < cout; ++co) yv[co] += xs[ci] * wr[ci * cout + co];
+    }
+  }
 }
 
 // dw[o][ci][co] = sum over triples (i, j, o) of x[i][ci] * dy[j][co].
