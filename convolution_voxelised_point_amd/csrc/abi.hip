@@ -573,6 +573,20 @@ ts_status ts_pool_fwd(const ts_kmap* map, const void* x, int c, void* y, ts_dtyp
   return TS_OK;
 }
 
+ts_status ts_graph_conv_fwd(const int64_t* indptr, const int32_t* src, const int32_t* rel, int64_t n_dst,
+                            int64_t n_src, int n_rel, const void* x, int cin, const void* w, int cout, void* y,
+                            ts_dtype in_dtype, ts_dtype out_dtype, uint32_t* err_flags, hipStream_t stream) {
+  if (n_dst < 0 || n_dst > kMaxRows || n_src < 0 || n_src > kMaxRows || n_rel < 1) return TS_ERR_INVALID_ARG;
+  if (cin < 1 || cout < 1 || cin > kMaxChannels || cout > kMaxChannels) return TS_ERR_INVALID_ARG;
+  if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return TS_ERR_INVALID_ARG;
+  if (out_dtype != TS_F32 && out_dtype != in_dtype) return TS_ERR_UNSUPPORTED;
+  if (n_dst > 0 && (!indptr || !src || !rel || !w || !y)) return TS_ERR_INVALID_ARG;
+  if (n_dst > 0 && n_src > 0 && !x) return TS_ERR_INVALID_ARG;
+  TS_TRY(launch_graph_conv(indptr, src, rel, n_dst, n_src, n_rel, x, cin, w, cout, y, in_dtype, out_dtype, err_flags,
+                           stream));
+  return TS_OK;
+}
+
 ts_status ts_conv_bwd_wgrad(const ts_kmap* map, const void* x, int cin, const void* dy, int cout, ts_dtype in_dtype,
                             float* dw, void* ws, size_t ws_bytes, hipStream_t stream) {
   ts_status st = check_conv(map, cin, cout, in_dtype, TS_F32);

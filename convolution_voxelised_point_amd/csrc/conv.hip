@@ -354,6 +354,82 @@ hipError_t launch_pool(const ts_rel& rel, int kvol, const void* x, int c, void* 
   }
 }
 
+// ---------------------------------------------------------------- graph convolution
+// Thread = (destination node, 8 output channels).  It walks the node's CSR
+// edges in order (so the sum order is fixed) and accumulates x[src] . W[rel]
+// in fp32.  An edge whose source or relation is out of range is skipped and
+// raises TS_FLAG_RANGE.
+struct GraphK {
+  const int64_t* indptr;
+  const int32_t* src;
+  const int32_t* rel;
+  int64_t n_dst, n_src;
+  int n_rel;
+  const void* x;
+  int cin;
+  const void* w;
+  int cout, nchunk;
+  void* y;
+  uint32_t* flags;
+};
+
+template <typename T, typename OT>
+__global__ __launch_bounds__(256) void k_graph(GraphK a) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= a.n_dst * a.nchunk) return;
+  const int64_t v = i / a.nchunk;
+  const int c0 = static_cast<int>(i - v * a.nchunk) * 8;
+  const T* x = static_cast<const T*>(a.x);
+  const T* w = static_cast<const T*>(a.w);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const int64_t e1 = a.indptr[v + 1];
+  bool bad = false;
+  for (int64_t e = a.indptr[v]; e < e1; ++e) {
+    const int32_t s = a.src[e], r = a.rel[e];
+    if (s < 0 || s >= a.n_src || r < 0 || r >= a.n_rel) {
+      bad = true;
+      continue;
+    }
+    const T* xs = x + static_cast<int64_t>(s) * a.cin;
+    const T* wr = w + static_cast<int64_t>(r) * a.cin * a.cout + c0;
+    for (int ci = 0; ci < a.cin; ++ci) {
+      const float xv = to_f32(xs[ci]);
+      const T* wc = wr + static_cast<int64_t>(ci) * a.cout;
+#pragma unroll
+      for (int e8 = 0; e8 < 8; ++e8)
+        if (c0 + e8 < a.cout) acc[e8] = fmaf(xv, to_f32(wc[e8]), acc[e8]);
+    }
+  }
+  if (bad && a.flags) atomicOr(a.flags, TS_FLAG_RANGE);
+  OT* out = static_cast<OT*>(a.y) + v * a.cout + c0;
+#pragma unroll
+  for (int e8 = 0; e8 < 8; ++e8)
+    if (c0 + e8 < a.cout) out[e8] = from_f32<OT>(acc[e8]);
+}
+
+template <typename T>
+static hipError_t graph_out(const GraphK& k, ts_dtype out, hipStream_t s) {
+  const unsigned grid = static_cast<unsigned>(ceil_div<int64_t>(k.n_dst * k.nchunk, 256));
+  switch (out) {
+    case TS_F32: k_graph<T, float><<<grid, 256, 0, s>>>(k); break;
+    case TS_F16: k_graph<T, _Float16><<<grid, 256, 0, s>>>(k); break;
+    default: k_graph<T, __bf16><<<grid, 256, 0, s>>>(k); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_graph_conv(const int64_t* indptr, const int32_t* src, const int32_t* rel, int64_t n_dst,
+                             int64_t n_src, int n_rel, const void* x, int cin, const void* w, int cout, void* y,
+                             ts_dtype in, ts_dtype out, uint32_t* flags, hipStream_t s) {
+  if (n_dst == 0) return hipSuccess;
+  GraphK k{indptr, src, rel, n_dst, n_src, n_rel, x, cin, w, cout, (cout + 7) / 8, y, flags};
+  switch (in) {
+    case TS_F32: return graph_out<float>(k, out, s);
+    case TS_F16: return graph_out<_Float16>(k, out, s);
+    default: return graph_out<__bf16>(k, out, s);
+  }
+}
+
 size_t gs_workspace_bytes(int64_t n_dest_cap, int c_dst, ts_dtype out_dtype) {
   if (out_dtype == TS_F32) return 0;
   return align_up(static_cast<size_t>(n_dest_cap) * c_dst * 4, 256);

@@ -92,6 +92,9 @@ size_t igemm_workspace_bytes(int kvol, int c_src, int c_dst);
 bool igemm_supported(int kvol, int64_t n_src, int c_src, int c_dst, ts_dtype in_dtype);
 hipError_t launch_igemm(const ConvArgs& a, void* ws, hipStream_t s);
 hipError_t launch_direct(const ConvArgs& a, hipStream_t s);
+hipError_t launch_graph_conv(const int64_t* indptr, const int32_t* src, const int32_t* rel, int64_t n_dst,
+                             int64_t n_src, int n_rel, const void* x, int cin, const void* w, int cout, void* y,
+                             ts_dtype in, ts_dtype out, uint32_t* flags, hipStream_t s);
 hipError_t launch_pool(const ts_rel& rel, int kvol, const void* x, int c, void* y, ts_dtype in, ts_dtype out, int mode,
                        hipStream_t s);
 

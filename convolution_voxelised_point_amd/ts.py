@@ -91,6 +91,8 @@ _lib_conv_fwd_generative = _sig("ts_conv_fwd_generative", _i32,
                                  _vp, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _vp, _sz, _vp])
 _lib_conv_transpose_fwd = _sig("ts_conv_transpose_fwd", _i32,
                                [_P, _vp, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _vp, _sz, _vp])
+_lib_graph_conv_fwd = _sig("ts_graph_conv_fwd", _i32, [_vp, _vp, _vp, _i64, _i64, _i32, _vp, _i32, _vp, _i32, _vp, _i32,
+                                                       _i32, _vp, _vp])
 _lib_pool_fwd = _sig("ts_pool_fwd", _i32, [_P, _vp, _i32, _vp, _i32, _i32, _i32, _vp])
 _lib_conv_bwd_dgrad = _sig("ts_conv_bwd_dgrad", _i32, [_P, _vp, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _vp, _sz, _vp])
 _lib_conv_bwd_wgrad = _sig("ts_conv_bwd_wgrad", _i32, [_P, _vp, _i32, _vp, _i32, _i32, _vp, _vp, _sz, _vp])
@@ -100,7 +102,7 @@ EXPORTED = ["ts_status_string", "ts_version", "ts_hash_capacity", "ts_hash_table
             "ts_generative_support", "ts_transposed_support", "ts_voxelize_scratch_bytes", "ts_voxelize",
             "ts_devoxelize", "ts_kmap_bytes", "ts_kmap_build",
             "ts_conv_workspace_bytes", "ts_conv_fwd", "ts_subm_conv_fwd", "ts_conv_fwd_strided",
-            "ts_conv_fwd_generative", "ts_conv_transpose_fwd", "ts_pool_fwd", "ts_conv_bwd_dgrad",
+            "ts_conv_fwd_generative", "ts_conv_transpose_fwd", "ts_pool_fwd", "ts_graph_conv_fwd", "ts_conv_bwd_dgrad",
             "ts_conv_bwd_wgrad"]
 
 
@@ -261,6 +263,12 @@ def ts_conv_transpose_fwd(kmap, x, w, y, dataflow=TS_DATAFLOW_AUTO, ws=None, str
     _check(_lib_conv_transpose_fwd(ctypes.byref(kmap), _p(x), x.shape[1], _p(w), w.shape[2], _p(y), _dt(x), _dt(y),
                                    dataflow, _p(ws), 0 if ws is None else ws.numel(), _stream(stream)),
            "ts_conv_transpose_fwd")
+
+
+def ts_graph_conv_fwd(indptr, src, rel, n_src, n_rel, x, w, y, err_flags=None, stream=None) -> None:
+    _check(_lib_graph_conv_fwd(_p(indptr), _p(src), _p(rel), indptr.shape[0] - 1, n_src, n_rel, _p(x), w.shape[1],
+                               _p(w), w.shape[2], _p(y), _dt(w), _dt(y), _p(err_flags), _stream(stream)),
+           "ts_graph_conv_fwd")
 
 
 def ts_pool_fwd(kmap, x, y, mode=TS_POOL_MAX, stream=None) -> None:

@@ -384,6 +384,20 @@ ts_status ts_conv_transpose_fwd(const ts_kmap* map, const void* x, int cin, cons
 ts_status ts_pool_fwd(const ts_kmap* map, const void* x, int c, void* y, ts_dtype in_dtype, ts_dtype out_dtype,
                       int mode, hipStream_t stream);
 
+/* Relational graph convolution (TorchSparse++ abstract: the library also runs
+ * graph convolutions; sparse convolution is the case "edges = kernel-map
+ * triples, relations = offsets").  Edges are grouped by destination (CSR):
+ * node v owns edges [indptr[v], indptr[v+1]) (device int64 [n_dst+1]), edge
+ * e runs from src[e] (device int32, < n_src) with relation rel[e] (device
+ * int32, < n_rel).  y[n_dst][cout] = sum over v's edges of x[src] . w[rel]
+ * with x [n_src][cin], w [n_rel][cin][cout] and fp32 accumulation in edge
+ * order (so the result does not vary between runs); no normalisation; 0 for
+ * a node without edges.  An edge with an out-of-range source or relation is
+ * skipped and raises TS_FLAG_RANGE.  y is fp32 or the input type. */
+ts_status ts_graph_conv_fwd(const int64_t* indptr, const int32_t* src, const int32_t* rel, int64_t n_dst,
+                            int64_t n_src, int n_rel, const void* x, int cin, const void* w, int cout, void* y,
+                            ts_dtype in_dtype, ts_dtype out_dtype, uint32_t* err_flags, hipStream_t stream);
+
 /* dx[n_in][cin] = sum over triples (i, j, o) of dy[j] . W[o]^T.  Strided
  * maps need TS_KMAP_BWD (implicit GEMM) or TS_KMAP_PAIRS (gather-scatter). */
 ts_status ts_conv_bwd_dgrad(const ts_kmap* map, const void* dy, int cout, const void* w, int cin, void* dx,
