@@ -89,6 +89,7 @@ struct IgK {
   int64_t nb8;   // ceil(nblk / 8)
   int xcd_map;   // number blocks so that each XCD walks a contiguous range
   int in_order;  // tiles keep rows in index order (launch choice only)
+  int ncol;      // weight-resident kernel: block columns
 };
 
 // Packed chunk i = ((o * mbt + mb) * kbn + kb) * 64 + lane holds A_o[n][k..k+7]
@@ -384,6 +385,226 @@ __global__ __launch_bounds__(NW * 64) void k_igemm(IgK a) {
   }
 }
 
+// Weight-resident variant, for layers whose weights (one block column of
+// output channels, every offset) fit in LDS: kvol * MB * KB fragments of
+// 1 KB, at most kResFrags.  The grid is one block per compute unit.  Each
+// block copies its column's weights into LDS once and then holds them; its
+// wavefronts walk tile groups independently, each over the union of its own
+// G tiles' masks only, with no barrier and no weight copy inside the loop,
+// so a step costs its fragment reads and MFMAs and waits only for the
+// gathers issued D steps earlier.
+//   * Block b serves XCD b % 8 (workgroups are dealt to XCDs round-robin) and
+//     column (b / 8) % ncol; XCD x walks the x-th eighth of the tile groups,
+//     each of its blocks a contiguous share, and the block's waves take the
+//     groups of that share from an LDS counter as they finish the last one.
+//     A single global counter per XCD was measured 2.6x slower: its atomics
+//     serialise.
+//   * The next group's masks, rows and neighbour rows load while the current
+//     group runs, so only a group's first gathers are exposed.
+//   * Every step issues its gathers, past the last offset out of range (no
+//     memory access), so all paths carry the same loads and the compiler's
+//     wait before a step covers that step's gathers only.
+constexpr int kResFrags = 144;
+
+template <typename T, int MB, int KB, int G, int D, int NW>
+__global__ __launch_bounds__(NW * 64) void k_igemm_res(IgK a) {
+  typedef typename Mfma<T>::frag Frag;
+  constexpr int FR = MB * KB;   // fragments per offset and block column
+  constexpr int GL = G * KB;    // gather loads per wave and offset
+  __shared__ u32x4 wl[kResFrags * 64];
+  __shared__ unsigned next_group;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 15;
+  const int kq = lane >> 4;
+  const int xcd = blockIdx.x & 7;
+  const int bi = blockIdx.x >> 3;
+  const int column = bi % a.ncol;
+  const int bj = bi / a.ncol;
+  const int mb0 = column * MB;
+  const int kvol = a.kvol;
+
+  // the column's weights, every offset: fragment f = o * FR + mb * KB + kb
+  {
+    const int live = (a.mbt - mb0) * KB;  // fragments of this column inside the packing
+    for (int f = wave; f < kvol * FR; f += NW) {
+      const int o = f / FR, r = f - o * FR;
+      const int64_t base = (static_cast<int64_t>(o) * a.mbt + mb0) * KB;
+      const u32x4* srcf = a.wp + (base + (r < live ? r : 0)) * 64 + lane;
+      lds_copy16(srcf, (lds_u32x4*)&wl[f * 64]);
+    }
+    if (threadIdx.x == 0) next_group = 0u;
+    wait_vm<0>();
+    __syncthreads();
+  }
+
+  const T* src = static_cast<const T*>(a.src);
+  const int c_src = a.c_src, c_dst = a.c_dst;
+  const __amdgpu_buffer_rsrc_t xr =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(src), 0, static_cast<int>(a.src_bytes), 0x00020000);
+  // XCD x walks the x-th eighth of the tile groups; each of its blocks of
+  // this column a contiguous share of that.
+  const int64_t ng = a.nblk;  // tile groups
+  const int64_t xlo = ng * xcd / 8, xn = ng * (xcd + 1) / 8 - xlo;
+  const int64_t lo = xlo + xn * bj / a.nb8, hi = xlo + xn * (bj + 1) / a.nb8;
+
+  // Tile metadata (masks, destination rows, then neighbour rows) of the
+  // wave's next group is loaded while the current group runs: the masks and
+  // rows after the current group's first gathers, the neighbour rows after
+  // its first D steps, so only the first gathers of a group wait.
+  uint64_t m[G];
+  int32_t drow[G], pr[G][kNbRegs];
+  auto load_meta = [&](int64_t g0, uint64_t (&mm)[G], int32_t (&dr)[G]) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {  // a tile past the end reads tile 0 and is masked off
+      const bool live = g0 >= 0 && g0 + g < a.n_tiles;
+      const int64_t tile = live ? g0 + g : 0;
+      const uint64_t v = a.tile_mask[tile];
+      mm[g] = live ? v : 0ull;
+      const int32_t r = a.tile_rows[tile * kTile + col];
+      dr[g] = live ? r : -1;
+    }
+  };
+  auto load_nbr = [&](const int32_t (&dr)[G], int32_t (&p)[G][kNbRegs]) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int32_t* nrow = a.nbr + static_cast<int64_t>(dr[g] >= 0 ? dr[g] : 0) * kvol;
+#pragma unroll
+      for (int j = 0; j < kNbRegs; ++j) {
+        const int o = kq * kNbRegs + j;
+        const int32_t v = nrow[o < kvol ? o : 0];
+        p[g][j] = dr[g] >= 0 ? v : -1;
+      }
+    }
+  };
+  // Groups of the block's share are dealt by an LDS ticket: a wave takes the
+  // next group when it starts one, so waves that drew short groups take more.
+  auto ticket = [&]() -> unsigned {  // issued by lane 0; the value is read later
+    unsigned v = 0u;
+    if (lane == 0) v = atomicAdd(&next_group, 1u);
+    return v;
+  };
+  int64_t gi = lo + static_cast<int64_t>(__builtin_amdgcn_readfirstlane(ticket()));
+  load_meta(gi < hi ? gi * G : -1, m, drow);
+  load_nbr(drow, pr);
+
+  while (gi < hi) {
+    const unsigned tk = ticket();
+    int64_t gn = hi, gnext = -1;
+    uint64_t mine = 0;
+#pragma unroll
+    for (int g = 0; g < G; ++g) mine |= m[g];
+    uint64_t nm[G];
+    int32_t ndrow[G], npr[G][kNbRegs];
+    bool nbr_issued = false;
+
+    f32x4 acc[G][MB];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) acc[g][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto pool_row = [&](int g, int o) -> int32_t {
+      const int q = o / kNbRegs, j = o - q * kNbRegs;
+      int32_t v = pr[g][0];
+#pragma unroll
+      for (int jj = 1; jj < kNbRegs; ++jj) v = (j == jj) ? pr[g][jj] : v;
+      return __shfl(v, col + 16 * q, 64);
+    };
+    // live = false (past the wave's last offset): out of range, no memory access
+    auto gather = [&](int o, bool live, Frag (&x)[G][KB]) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const int32_t nb = pool_row(g, o);
+        const bool ok = live && ((m[g] >> o) & 1) && nb >= 0;
+        const uint32_t off = ok ? static_cast<uint32_t>(nb * c_src + kq * 8) * 2u : 0x80000000u;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+          x[g][kb] = __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(xr, static_cast<int>(off + kb * 64), 0, 0));
+      }
+    };
+
+    if (mine) {
+      // Offsets u_0 < u_1 < ... < u_{n-1} of this wave's union; X(u_j) in
+      // register set j % R, gathered D steps ahead.  The walk runs a whole
+      // number of R-step rounds: steps past u_{n-1} do no math and gather
+      // out of range, so every path issues the same loads and no step has
+      // to wait for more than its own gathers.
+      constexpr int R = D + 1;
+      Frag xs[R][G][KB];
+      const int nst = __builtin_popcountll(mine);
+      int oc = __builtin_ctzll(mine);
+      int onx = oc;
+      int ng = 0;  // gathers issued
+#pragma unroll
+      for (int j = 0; j < D; ++j) {
+        gather(onx, ng < nst, xs[j]);
+        ++ng;
+        onx = next_bit(mine, onx);
+      }
+      gn = lo + static_cast<int64_t>(__builtin_amdgcn_readfirstlane(tk));
+      gnext = gn < hi ? gn * G : -1;
+      load_meta(gnext, nm, ndrow);
+      for (int st = 0; st < nst; st += R) {
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+          const int cur = i, fill = (i + D) % R;
+          if (st + i < nst) {  // wave-uniform
+            const u32x4* lw = wl + oc * FR * 64;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+              Frag af[MB];
+#pragma unroll
+              for (int mb = 0; mb < MB; ++mb) af[mb] = __builtin_bit_cast(Frag, lw[(mb * KB + kb) * 64 + lane]);
+#pragma unroll
+              for (int g = 0; g < G; ++g) {
+                if (!((m[g] >> oc) & 1)) continue;  // wave-uniform
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) acc[g][mb] = Mfma<T>::run(af[mb], xs[cur][g][kb], acc[g][mb]);
+              }
+            }
+            oc = next_bit(mine, oc);
+          }
+          gather(onx < 0 ? 0 : onx, ng < nst, xs[fill]);  // X(u_{st+i+D})
+          ++ng;
+          onx = next_bit(mine, onx);
+          if (st + i == D - 1) {  // wave-uniform
+            load_nbr(ndrow, npr);
+            nbr_issued = true;
+          }
+        }
+      }
+    } else {
+      gn = lo + static_cast<int64_t>(__builtin_amdgcn_readfirstlane(tk));
+      gnext = gn < hi ? gn * G : -1;
+      load_meta(gnext, nm, ndrow);
+    }
+    if (!nbr_issued) load_nbr(ndrow, npr);
+
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int32_t row = drow[g];  // -1 past the end or for an empty slot
+      if (row < 0) continue;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const int n = (mb0 + mb) * 16 + kq * 4;
+        if (n >= c_dst) continue;
+        store4(a.dst, a.out_dtype, static_cast<int64_t>(row) * c_dst + n, acc[g][mb]);
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      m[g] = nm[g];
+      drow[g] = ndrow[g];
+#pragma unroll
+      for (int j = 0; j < kNbRegs; ++j) pr[g][j] = npr[g][j];
+    }
+    gi = gn;
+  }
+  (void)GL;
+}
+
 // Tiles per wave.  Two when a weight slice is at least 32 fragments (e.g.
 // 128x128): each fragment read from LDS then feeds two MFMAs, which halves
 // the LDS reads per row and doubles the math per barrier.  Two as well when
@@ -469,6 +690,82 @@ static int max_mb() {
   return forced;
 }
 
+// Weight-resident launch.  Gathers in flight per wave: D offsets of G * KB
+// 16-byte loads.  Waves per block from the register need of acc, the gather
+// ring and the fragments (one block per compute unit: the weights take most
+// of the LDS).
+template <typename T, int MB, int KB>
+hipError_t launch_res_mk(IgK k, int ncu, hipStream_t s) {
+  constexpr int G = 2;
+  constexpr int D = KB >= 4 ? 2 : (KB == 1 ? 4 : 3);
+  constexpr int NW = MB * KB <= 2 ? 16 : (MB * KB <= 8 && MB < 8 ? 12 : 8);
+  k.nblk = ceil_div<int64_t>(k.n_tiles, G);
+  int64_t per = ncu / (8 * k.ncol);
+  if (per < 1) per = 1;
+  const int64_t need = ceil_div<int64_t>(ceil_div<int64_t>(k.nblk, 8), NW);  // blocks that have a group
+  k.nb8 = per < need ? per : need;
+  dim3 grid(static_cast<unsigned>(8 * k.ncol * k.nb8));
+  k_igemm_res<T, MB, KB, G, D, NW><<<grid, NW * 64, 0, s>>>(k);
+  return hipGetLastError();
+}
+
+template <typename T, int MB>
+hipError_t launch_res_m(const IgK& k, int ncu, hipStream_t s) {
+  switch (k.c_src / 32) {
+    case 1: return launch_res_mk<T, MB, 1>(k, ncu, s);
+    case 2: return launch_res_mk<T, MB, 2>(k, ncu, s);
+    case 3: return launch_res_mk<T, MB, 3>(k, ncu, s);
+    default: return launch_res_mk<T, MB, 4>(k, ncu, s);
+  }
+}
+
+// Fragments of 16 output channels per block for the weight-resident kernel
+// (all output channels in one block column), or 0 when those weights do not
+// fit in LDS.  Split into two columns (e.g. 27 offsets of 64 x 64), each
+// column would gather every source row and read the neighbour table again:
+// measured slower than the barrier-stepped kernel on the ring scan (50 vs
+// 42 us) and on its generated support (404 vs 340 us), so such layers stay on
+// that kernel.  TS_IGEMM_RES=0 switches the kernel off, TS_IGEMM_RES=2 allows
+// two columns (tuning).
+static int res_mb(int kvol, int c_src, int c_dst) {
+  static const int mode = [] {
+    const char* e = getenv("TS_IGEMM_RES");
+    return e ? atoi(e) : 1;
+  }();
+  if (mode <= 0) return 0;
+  const int mbt = ceil_div(c_dst, 16), kb = c_src / 32;
+  for (int ncol = 1; ncol <= (mode >= 2 ? 2 : 1); ++ncol) {
+    int mb = 1;
+    while (mb < ceil_div(mbt, ncol)) mb *= 2;
+    if (mb <= 8 && kvol * mb * kb <= kResFrags) return mb;
+  }
+  return 0;
+}
+
+static int cu_count() {
+  static int n[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (n[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    n[dev] = v;
+  }
+  return n[dev];
+}
+
+template <typename T>
+hipError_t launch_res(IgK k, int mb, hipStream_t s) {
+  k.ncol = ceil_div(k.mbt, mb);
+  const int ncu = cu_count();
+  switch (mb) {
+    case 1: return launch_res_m<T, 1>(k, ncu, s);
+    case 2: return launch_res_m<T, 2>(k, ncu, s);
+    case 4: return launch_res_m<T, 4>(k, ncu, s);
+    default: return launch_res_m<T, 8>(k, ncu, s);
+  }
+}
+
 template <typename T>
 hipError_t launch_t(const IgK& k, hipStream_t s) {
   int mbt = k.c_dst / 16;
@@ -511,16 +808,18 @@ hipError_t launch_igemm(const ConvArgs& a, void* ws, hipStream_t s) {
   k.nblk = 0;
   k.nb8 = 0;
   k.in_order = a.rows_in_order ? 1 : 0;
+  k.ncol = 1;
+  const int rmb = res_mb(a.kvol, a.c_src, a.c_dst);
   const int64_t chunks = static_cast<int64_t>(a.kvol) * k.mbt * (a.c_src / 32) * 64;
   const unsigned pg = static_cast<unsigned>(ceil_div<int64_t>(chunks, 256));
   if (a.in_dtype == TS_F16) {
     k_wpack<_Float16><<<pg, 256, 0, s>>>(static_cast<const _Float16*>(a.w), a.kvol, a.c_src, a.c_dst, k.mbt,
                                          a.transpose ? 1 : 0, a.mirror ? 1 : 0, static_cast<u32x4*>(ws));
-    return launch_t<_Float16>(k, s);
+    return rmb ? launch_res<_Float16>(k, rmb, s) : launch_t<_Float16>(k, s);
   }
   k_wpack<__bf16><<<pg, 256, 0, s>>>(static_cast<const __bf16*>(a.w), a.kvol, a.c_src, a.c_dst, k.mbt,
                                      a.transpose ? 1 : 0, a.mirror ? 1 : 0, static_cast<u32x4*>(ws));
-  return launch_t<__bf16>(k, s);
+  return rmb ? launch_res<__bf16>(k, rmb, s) : launch_t<__bf16>(k, s);
 }
 
 }  // namespace ts
