@@ -119,7 +119,15 @@ ts_status check_conv(const ts_kmap* map, int cin, int cout, ts_dtype in, ts_dtyp
 }
 
 bool use_igemm(ts_dataflow df, int kvol, int64_t n_src, int c_src, int c_dst, ts_dtype in) {
-  return (df == TS_DATAFLOW_AUTO || df == TS_DATAFLOW_IMPLICIT_GEMM) && igemm_supported(kvol, n_src, c_src, c_dst, in);
+  return (df == TS_DATAFLOW_AUTO || df == TS_DATAFLOW_IMPLICIT_GEMM || df == TS_DATAFLOW_IMPLICIT_GEMM_PACKED) &&
+         igemm_supported(kvol, n_src, c_src, c_dst, in);
+}
+
+// Dataflow in range; the weights are needed unless they come packed.
+ts_status check_dataflow(ts_dataflow df, const void* w) {
+  if (df < TS_DATAFLOW_AUTO || df > TS_DATAFLOW_IMPLICIT_GEMM_PACKED) return TS_ERR_INVALID_ARG;
+  if (!w && df != TS_DATAFLOW_IMPLICIT_GEMM_PACKED) return TS_ERR_INVALID_ARG;
+  return TS_OK;
 }
 
 size_t conv_ws(const ts_kmap* map, int c_src, int c_dst, ts_dtype in, ts_dtype out, ts_dataflow df, int64_t n_dest,
@@ -355,13 +363,44 @@ size_t ts_conv_workspace_bytes(const ts_kmap* map, int cin, int cout, int op, ts
   return 0;
 }
 
+ts_status ts_conv_pack_weights(const ts_kmap* map, const void* w, int cin, int cout, int op, ts_dtype in_dtype,
+                               void* ws, size_t ws_bytes, hipStream_t stream) {
+  ts_status st = check_conv(map, cin, cout, in_dtype, in_dtype);
+  if (st != TS_OK) return st;
+  if (!w || !ws) return TS_ERR_INVALID_ARG;
+  ConvArgs a;
+  a.kvol = map->kvol;
+  a.w = w;
+  a.w_cin = cin;
+  a.w_cout = cout;
+  a.in_dtype = a.out_dtype = in_dtype;
+  int64_t n_src = 0;
+  switch (op) {
+    case TS_OP_FWD:  // the forward contracts over cin, mirror-free
+      a.c_src = cin, a.c_dst = cout, a.transpose = false, a.mirror = false, n_src = map->n_in;
+      break;
+    case TS_OP_DGRAD:  // contracts over cout; mirrored offsets on a submanifold map
+      a.c_src = cout, a.c_dst = cin, a.transpose = true, a.mirror = map->mirror_bwd != 0, n_src = map->n_out_cap;
+      break;
+    case TS_OP_TRANSPOSE:  // the forward's weights over the dgrad relation
+      a.c_src = cin, a.c_dst = cout, a.transpose = false, a.mirror = map->mirror_bwd != 0, n_src = map->n_out_cap;
+      break;
+    default:
+      return TS_ERR_INVALID_ARG;
+  }
+  if (!igemm_supported(a.kvol, n_src, a.c_src, a.c_dst, in_dtype)) return TS_ERR_UNSUPPORTED;
+  if (ws_bytes < igemm_workspace_bytes(a.kvol, a.c_src, a.c_dst)) return TS_ERR_INVALID_ARG;
+  TS_TRY(launch_wpack(a, ws, stream));
+  return TS_OK;
+}
+
 ts_status ts_conv_fwd(const ts_kmap* map, const void* x, int cin, const void* w, int cout, void* y,
                       ts_dtype in_dtype, ts_dtype out_dtype, ts_dataflow dataflow, void* ws, size_t ws_bytes,
                       hipStream_t stream) {
   ts_status st = check_conv(map, cin, cout, in_dtype, out_dtype);
   if (st != TS_OK) return st;
-  if (dataflow < TS_DATAFLOW_AUTO || dataflow > TS_DATAFLOW_GATHER_SCATTER) return TS_ERR_INVALID_ARG;
-  if (!w || (map->n_in > 0 && !x) || (map->n_out_cap > 0 && !y)) return TS_ERR_INVALID_ARG;
+  if ((st = check_dataflow(dataflow, w)) != TS_OK) return st;
+  if ((map->n_in > 0 && !x) || (map->n_out_cap > 0 && !y)) return TS_ERR_INVALID_ARG;
   const size_t need = conv_ws(map, cin, cout, in_dtype, out_dtype, dataflow, map->n_out_cap, map->n_in);
   if (need > 0 && (!ws || ws_bytes < need)) return TS_ERR_INVALID_ARG;
   ConvArgs a;
@@ -380,6 +419,8 @@ ts_status ts_conv_fwd(const ts_kmap* map, const void* x, int cin, const void* w,
   a.mirror = false;
   a.in_dtype = in_dtype;
   a.out_dtype = out_dtype;
+  a.prepacked = dataflow == TS_DATAFLOW_IMPLICIT_GEMM_PACKED;
+  if (a.prepacked && !use_igemm(dataflow, map->kvol, map->n_in, cin, cout, in_dtype)) return TS_ERR_UNSUPPORTED;
   if (dataflow == TS_DATAFLOW_GATHER_SCATTER) {
     if (!(map->flags & TS_KMAP_PAIRS)) return TS_ERR_INVALID_ARG;
     TS_TRY(launch_gather_scatter(map, a, false, map->n_out_cap, ws, stream));
@@ -474,8 +515,8 @@ ts_status ts_conv_bwd_dgrad(const ts_kmap* map, const void* dy, int cout, const 
                             hipStream_t stream) {
   ts_status st = check_conv(map, cin, cout, in_dtype, out_dtype);
   if (st != TS_OK) return st;
-  if (dataflow < TS_DATAFLOW_AUTO || dataflow > TS_DATAFLOW_GATHER_SCATTER) return TS_ERR_INVALID_ARG;
-  if (!w || (map->n_out_cap > 0 && !dy) || (map->n_in > 0 && !dx)) return TS_ERR_INVALID_ARG;
+  if ((st = check_dataflow(dataflow, w)) != TS_OK) return st;
+  if ((map->n_out_cap > 0 && !dy) || (map->n_in > 0 && !dx)) return TS_ERR_INVALID_ARG;
   const size_t need = conv_ws(map, cout, cin, in_dtype, out_dtype, dataflow, map->n_in, map->n_out_cap);
   if (need > 0 && (!ws || ws_bytes < need)) return TS_ERR_INVALID_ARG;
   ConvArgs a;
@@ -492,6 +533,8 @@ ts_status ts_conv_bwd_dgrad(const ts_kmap* map, const void* dy, int cout, const 
   a.transpose = true;
   a.in_dtype = in_dtype;
   a.out_dtype = out_dtype;
+  a.prepacked = dataflow == TS_DATAFLOW_IMPLICIT_GEMM_PACKED;
+  if (a.prepacked && !use_igemm(dataflow, map->kvol, map->n_out_cap, cout, cin, in_dtype)) return TS_ERR_UNSUPPORTED;
   if (dataflow == TS_DATAFLOW_GATHER_SCATTER) {
     if (!(map->flags & TS_KMAP_PAIRS)) return TS_ERR_INVALID_ARG;
     a.rel = &map->fwd;
@@ -520,8 +563,8 @@ ts_status ts_conv_transpose_fwd(const ts_kmap* map, const void* x, int cin, cons
                                 size_t ws_bytes, hipStream_t stream) {
   ts_status st = check_conv(map, cin, cout, in_dtype, out_dtype);
   if (st != TS_OK) return st;
-  if (dataflow < TS_DATAFLOW_AUTO || dataflow > TS_DATAFLOW_GATHER_SCATTER) return TS_ERR_INVALID_ARG;
-  if (!w || (map->n_out_cap > 0 && !x) || (map->n_in > 0 && !y)) return TS_ERR_INVALID_ARG;
+  if ((st = check_dataflow(dataflow, w)) != TS_OK) return st;
+  if ((map->n_out_cap > 0 && !x) || (map->n_in > 0 && !y)) return TS_ERR_INVALID_ARG;
   const size_t need = conv_ws(map, cin, cout, in_dtype, out_dtype, dataflow, map->n_in, map->n_out_cap);
   if (need > 0 && (!ws || ws_bytes < need)) return TS_ERR_INVALID_ARG;
   // the relation of dgrad, the weights as the forward reads them
@@ -539,6 +582,8 @@ ts_status ts_conv_transpose_fwd(const ts_kmap* map, const void* x, int cin, cons
   a.transpose = false;
   a.in_dtype = in_dtype;
   a.out_dtype = out_dtype;
+  a.prepacked = dataflow == TS_DATAFLOW_IMPLICIT_GEMM_PACKED;
+  if (a.prepacked && !use_igemm(dataflow, map->kvol, map->n_out_cap, cin, cout, in_dtype)) return TS_ERR_UNSUPPORTED;
   if (dataflow == TS_DATAFLOW_GATHER_SCATTER) {
     if (!(map->flags & TS_KMAP_PAIRS)) return TS_ERR_INVALID_ARG;
     a.rel = &map->fwd;

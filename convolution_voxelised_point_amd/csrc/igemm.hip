@@ -788,8 +788,25 @@ size_t igemm_workspace_bytes(int kvol, int c_src, int c_dst) {
   return static_cast<size_t>(kvol) * ceil_div(c_dst, 16) * (c_src / 32) * 64 * 16;
 }
 
+hipError_t launch_wpack(const ConvArgs& a, void* ws, hipStream_t s) {
+  const int mbt = ceil_div(a.c_dst, 16);
+  const int64_t chunks = static_cast<int64_t>(a.kvol) * mbt * (a.c_src / 32) * 64;
+  const unsigned pg = static_cast<unsigned>(ceil_div<int64_t>(chunks, 256));
+  if (a.in_dtype == TS_F16)
+    k_wpack<_Float16><<<pg, 256, 0, s>>>(static_cast<const _Float16*>(a.w), a.kvol, a.c_src, a.c_dst, mbt,
+                                         a.transpose ? 1 : 0, a.mirror ? 1 : 0, static_cast<u32x4*>(ws));
+  else
+    k_wpack<__bf16><<<pg, 256, 0, s>>>(static_cast<const __bf16*>(a.w), a.kvol, a.c_src, a.c_dst, mbt,
+                                       a.transpose ? 1 : 0, a.mirror ? 1 : 0, static_cast<u32x4*>(ws));
+  return hipGetLastError();
+}
+
 hipError_t launch_igemm(const ConvArgs& a, void* ws, hipStream_t s) {
   const ts_rel& rel = *a.rel;
+  if (!a.prepacked) {
+    const hipError_t e = launch_wpack(a, ws, s);
+    if (e != hipSuccess) return e;
+  }
   if (rel.n_tiles == 0) return hipSuccess;
   IgK k;
   k.tile_mask = rel.tile_mask;
@@ -810,15 +827,7 @@ hipError_t launch_igemm(const ConvArgs& a, void* ws, hipStream_t s) {
   k.in_order = a.rows_in_order ? 1 : 0;
   k.ncol = 1;
   const int rmb = res_mb(a.kvol, a.c_src, a.c_dst);
-  const int64_t chunks = static_cast<int64_t>(a.kvol) * k.mbt * (a.c_src / 32) * 64;
-  const unsigned pg = static_cast<unsigned>(ceil_div<int64_t>(chunks, 256));
-  if (a.in_dtype == TS_F16) {
-    k_wpack<_Float16><<<pg, 256, 0, s>>>(static_cast<const _Float16*>(a.w), a.kvol, a.c_src, a.c_dst, k.mbt,
-                                         a.transpose ? 1 : 0, a.mirror ? 1 : 0, static_cast<u32x4*>(ws));
-    return rmb ? launch_res<_Float16>(k, rmb, s) : launch_t<_Float16>(k, s);
-  }
-  k_wpack<__bf16><<<pg, 256, 0, s>>>(static_cast<const __bf16*>(a.w), a.kvol, a.c_src, a.c_dst, k.mbt,
-                                     a.transpose ? 1 : 0, a.mirror ? 1 : 0, static_cast<u32x4*>(ws));
+  if (a.in_dtype == TS_F16) return rmb ? launch_res<_Float16>(k, rmb, s) : launch_t<_Float16>(k, s);
   return rmb ? launch_res<__bf16>(k, rmb, s) : launch_t<__bf16>(k, s);
 }
 

@@ -86,10 +86,12 @@ struct ConvArgs {
   bool mirror;        // dgrad of a submanifold map: use W[kvol-1-o]
   bool rows_in_order; // tiles keep rows in index order (no grouping by mask)
   ts_dtype in_dtype, out_dtype;
+  bool prepacked = false;  // implicit GEMM: ws already holds the packed weights
 };
 
 size_t igemm_workspace_bytes(int kvol, int c_src, int c_dst);
 bool igemm_supported(int kvol, int64_t n_src, int c_src, int c_dst, ts_dtype in_dtype);
+hipError_t launch_wpack(const ConvArgs& a, void* ws, hipStream_t s);
 hipError_t launch_igemm(const ConvArgs& a, void* ws, hipStream_t s);
 hipError_t launch_direct(const ConvArgs& a, hipStream_t s);
 hipError_t launch_graph_conv(const int64_t* indptr, const int32_t* src, const int32_t* rel, int64_t n_dst,

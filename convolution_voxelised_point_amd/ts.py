@@ -27,7 +27,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 TS_OK, TS_ERR_INVALID_ARG, TS_ERR_UNSUPPORTED, TS_ERR_HIP = 0, 1, 2, 3
 TS_F32, TS_F16, TS_BF16 = 0, 1, 2
-TS_DATAFLOW_AUTO, TS_DATAFLOW_IMPLICIT_GEMM, TS_DATAFLOW_GATHER_SCATTER = 0, 1, 2
+TS_DATAFLOW_AUTO, TS_DATAFLOW_IMPLICIT_GEMM, TS_DATAFLOW_GATHER_SCATTER, TS_DATAFLOW_IMPLICIT_GEMM_PACKED = 0, 1, 2, 3
 TS_FLAG_DUP, TS_FLAG_RANGE, TS_FLAG_FULL = 1, 2, 4
 TS_KMAP_PAIRS, TS_KMAP_BWD, TS_KMAP_NATURAL, TS_KMAP_TARGET, TS_KMAP_TRANSPOSED = 1, 2, 4, 8, 16
 TS_OP_FWD, TS_OP_DGRAD, TS_OP_WGRAD, TS_OP_TRANSPOSE = 0, 1, 2, 3
@@ -81,6 +81,7 @@ _lib_kmap_bytes = _sig("ts_kmap_bytes", _sz, [_i64, _i64, _i32, _i32, _i32, _u32
 _lib_kmap_build = _sig("ts_kmap_build", _i32, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _i64, _i32, _i32, _i32, _u32,
                                                _vp, _sz, _P, _vp])
 _lib_conv_workspace_bytes = _sig("ts_conv_workspace_bytes", _sz, [_P, _i32, _i32, _i32, _i32, _i32])
+_lib_conv_pack_weights = _sig("ts_conv_pack_weights", _i32, [_P, _vp, _i32, _i32, _i32, _i32, _vp, _sz, _vp])
 _lib_conv_fwd = _sig("ts_conv_fwd", _i32, [_P, _vp, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _vp, _sz, _vp])
 _lib_subm_conv_fwd = _sig("ts_subm_conv_fwd", _i32, [_P, _vp, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _vp, _sz, _vp])
 _lib_conv_fwd_strided = _sig("ts_conv_fwd_strided", _i32,
@@ -101,7 +102,7 @@ EXPORTED = ["ts_status_string", "ts_version", "ts_hash_capacity", "ts_hash_table
             "ts_hash_query", "ts_support_scratch_bytes", "ts_strided_support", "ts_generative_scratch_bytes",
             "ts_generative_support", "ts_transposed_support", "ts_voxelize_scratch_bytes", "ts_voxelize",
             "ts_devoxelize", "ts_kmap_bytes", "ts_kmap_build",
-            "ts_conv_workspace_bytes", "ts_conv_fwd", "ts_subm_conv_fwd", "ts_conv_fwd_strided",
+            "ts_conv_workspace_bytes", "ts_conv_pack_weights", "ts_conv_fwd", "ts_subm_conv_fwd", "ts_conv_fwd_strided",
             "ts_conv_fwd_generative", "ts_conv_transpose_fwd", "ts_pool_fwd", "ts_graph_conv_fwd", "ts_conv_bwd_dgrad",
             "ts_conv_bwd_wgrad"]
 
@@ -225,6 +226,13 @@ def ts_kmap_build(in_coords, in_table, in_cap, out_coords, n_out_cap, n_out, out
 
 def ts_conv_workspace_bytes(kmap: TsKmap, cin: int, cout: int, op: int, in_dtype: int, dataflow: int) -> int:
     return int(_lib_conv_workspace_bytes(ctypes.byref(kmap), cin, cout, op, in_dtype, dataflow))
+
+
+def ts_conv_pack_weights(kmap, w, op, ws, stream=None) -> None:
+    """Weights [kvol][cin][cout] packed into `ws` for a later call of `op`
+    with TS_DATAFLOW_IMPLICIT_GEMM_PACKED."""
+    _check(_lib_conv_pack_weights(ctypes.byref(kmap), _p(w), w.shape[1], w.shape[2], op, _dt(w), _p(ws),
+                                  0 if ws is None else ws.numel(), _stream(stream)), "ts_conv_pack_weights")
 
 
 def ts_conv_fwd(kmap, x, w, y, dataflow=TS_DATAFLOW_AUTO, ws=None, stream=None, subm=False) -> None:

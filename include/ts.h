@@ -66,7 +66,9 @@ typedef enum ts_dtype { TS_F32 = 0, TS_F16 = 1, TS_BF16 = 2 } ts_dtype;
 typedef enum ts_dataflow {
   TS_DATAFLOW_AUTO = 0,          /* per-shape choice                                   */
   TS_DATAFLOW_IMPLICIT_GEMM = 1, /* output-stationary tiles, MFMA for fp16/bf16        */
-  TS_DATAFLOW_GATHER_SCATTER = 2 /* per offset: gather, multiply, add into the outputs */
+  TS_DATAFLOW_GATHER_SCATTER = 2, /* per offset: gather, multiply, add into the outputs */
+  TS_DATAFLOW_IMPLICIT_GEMM_PACKED = 3 /* implicit GEMM on weights that ts_conv_pack_weights
+                                          already wrote into the workspace (w is ignored)  */
 } ts_dataflow;
 
 /* device-detected conditions, ORed into the caller's flag word */
@@ -319,6 +321,21 @@ ts_status ts_kmap_build(const int32_t* in_coords, int64_t n_in, const void* in_t
 /* Workspace bytes for an op on this map (0 is a valid answer). */
 size_t ts_conv_workspace_bytes(const ts_kmap* map, int cin, int cout, int op, ts_dtype in_dtype,
                                ts_dataflow dataflow);
+
+/* Packs w[kvol][cin][cout] (the layer's weights, fp16 or bf16, device) into
+ * ws in the fragment order the implicit GEMM of `op` reads (TS_OP_FWD,
+ * TS_OP_DGRAD or TS_OP_TRANSPOSE on this map: dgrad and the transposed
+ * convolution mirror the offsets on a submanifold map, dgrad also swaps the
+ * channel roles).  The implicit-GEMM calls do this themselves as their first
+ * launch; packing separately lets the caller run it on another stream (it
+ * needs only the weights, not the map's contents) and then call the op with
+ * TS_DATAFLOW_IMPLICIT_GEMM_PACKED and the same ws, cin, cout and dtype.
+ * ws_bytes must be at least ts_conv_workspace_bytes(map, cin, cout, op,
+ * in_dtype, TS_DATAFLOW_IMPLICIT_GEMM).  Errors: TS_ERR_INVALID_ARG (null,
+ * bad op or sizes, short ws), TS_ERR_UNSUPPORTED (the shape or dtype has no
+ * implicit GEMM: fp32, channels not multiples of 32 / 16, kvol > 28). */
+ts_status ts_conv_pack_weights(const ts_kmap* map, const void* w, int cin, int cout, int op, ts_dtype in_dtype,
+                               void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* y[n_out][cout] = sparse conv of x[n_in][cin] with w[kvol][cin][cout] over
  * map->fwd (any stride). */

@@ -145,6 +145,37 @@ def test_conv_rejects(ts):
     assert ts._lib_subm_conv_fwd(ref, FAKE, 16, FAKE, 16, FAKE, 9, 1, 0, None, 0, None) == ts.TS_ERR_INVALID_ARG
 
 
+def test_pack_weights_rejects(ts):
+    km = ts.TsKmap()
+    ref = ctypes.byref(km)
+    FAKE = ctypes.c_void_p(0x1000)
+    P = ts._lib_conv_pack_weights
+    assert P(ref, FAKE, 64, 64, ts.TS_OP_FWD, ts.TS_F16, FAKE, 1 << 30, None) == ts.TS_ERR_INVALID_ARG  # no map yet
+    km.kvol = 27
+    km.stride = 1
+    km.mirror_bwd = 1
+    km.n_in = km.n_out_cap = 100
+    km.fwd.tile_mask = 0x2000
+    need = ts._lib_conv_workspace_bytes(ref, 64, 64, ts.TS_OP_FWD, ts.TS_F16, ts.TS_DATAFLOW_IMPLICIT_GEMM)
+    assert need == 27 * 64 * 64 * 2
+    assert P(ref, None, 64, 64, ts.TS_OP_FWD, ts.TS_F16, FAKE, need, None) == ts.TS_ERR_INVALID_ARG       # null w
+    assert P(ref, FAKE, 64, 64, ts.TS_OP_FWD, ts.TS_F16, None, need, None) == ts.TS_ERR_INVALID_ARG       # null ws
+    assert P(ref, FAKE, 64, 64, ts.TS_OP_FWD, ts.TS_F16, FAKE, need - 1, None) == ts.TS_ERR_INVALID_ARG   # short ws
+    assert P(ref, FAKE, 64, 64, ts.TS_OP_WGRAD, ts.TS_F16, FAKE, need, None) == ts.TS_ERR_INVALID_ARG     # op
+    assert P(ref, FAKE, 64, 64, 7, ts.TS_F16, FAKE, need, None) == ts.TS_ERR_INVALID_ARG                  # op
+    assert P(ref, FAKE, 0, 64, ts.TS_OP_FWD, ts.TS_F16, FAKE, need, None) == ts.TS_ERR_INVALID_ARG        # cin
+    assert P(ref, FAKE, 64, 64, ts.TS_OP_FWD, ts.TS_F32, FAKE, need, None) == ts.TS_ERR_UNSUPPORTED       # fp32
+    assert P(ref, FAKE, 48, 64, ts.TS_OP_FWD, ts.TS_F16, FAKE, need, None) == ts.TS_ERR_UNSUPPORTED       # cin % 32
+    # the packed dataflow: unsupported shapes are refused, w may be null, the range ends at 3
+    F = ts._lib_conv_fwd
+    assert F(ref, FAKE, 16, None, 16, FAKE, 1, 1, 3, FAKE, 1 << 30, None) == ts.TS_ERR_UNSUPPORTED
+    assert F(ref, FAKE, 64, None, 64, FAKE, 1, 1, 1, FAKE, 1 << 30, None) == ts.TS_ERR_INVALID_ARG
+    assert F(ref, FAKE, 64, None, 64, FAKE, 1, 1, 4, FAKE, 1 << 30, None) == ts.TS_ERR_INVALID_ARG
+    assert F(ref, FAKE, 64, None, 64, FAKE, 1, 1, 3, FAKE, need - 1, None) == ts.TS_ERR_INVALID_ARG   # short ws
+    D = ts._lib_conv_bwd_dgrad
+    assert D(ref, FAKE, 16, None, 16, FAKE, 1, 1, 3, FAKE, 1 << 30, None) == ts.TS_ERR_UNSUPPORTED
+
+
 def test_workspace_sizes(ts):
     km = ts.TsKmap()
     km.kvol = 27

@@ -163,3 +163,43 @@ def test_isolated_rows_get_zero(ts):
     for i in range(3):
         np.testing.assert_allclose(y[i], xc[i] @ wc[13], rtol=1e-5, atol=1e-5)
     assert np.all(y[3] == 0)
+
+
+PACK_CASES = [c for c in CONV_CASES
+              if c[0] in ("lidar_f16_64", "lidar_bf16_128", "fuzz_f16_32x16", "down_f16_64x128", "down_bf16_k3s2")]
+
+
+@pytest.mark.parametrize("case", PACK_CASES, ids=[c[0] for c in PACK_CASES])
+def test_prepacked_weights(ts, case):
+    """Weights packed by ts_conv_pack_weights on a second stream, then the op
+    called with TS_DATAFLOW_IMPLICIT_GEMM_PACKED: bitwise the one-call
+    implicit GEMM, for the forward, dgrad and (strided maps) the transposed
+    convolution over the strided relation."""
+    name, c, k, s, cin, cout, dt = case
+    km, tr, oc, x, w, dy = make_problem(c, k, s, cin, cout, dt, 1200)
+    xd, wd = dev(x), dev(w)
+    rows_out = c.shape[0] if s == 1 else km.s.n_out_cap
+    dyd = torch.zeros((rows_out, cout), dtype=DT[dt], device="cuda")
+    dyd[:oc.shape[0]] = dev(dy)
+    ops = []  # (op, call, input, weights, rows the call defines)
+    if cin % 32 == 0:
+        ops.append((ts.TS_OP_FWD, ts.conv_fwd, xd, wd, oc.shape[0]))
+    if cout % 32 == 0:
+        ops.append((ts.TS_OP_DGRAD, ts.conv_dgrad, dyd, wd, c.shape[0]))
+    if s != 1 and cout % 32 == 0:  # ConvTranspose cout -> cin over the strided relation
+        wt = dev(synth.weight(1201, k ** (c.shape[1] - 1), cout, cin, dt))
+        ops.append((ts.TS_OP_TRANSPOSE, ts.conv_transpose, dyd, wt, c.shape[0]))
+    assert ops
+    side = torch.cuda.Stream()
+    for op, fn, inp, wgt, rows in ops:
+        ref = fn(km, inp, wgt, out_dtype=torch.float32, dataflow=ts.TS_DATAFLOW_IMPLICIT_GEMM)
+        ws = ts.workspace(km, wgt.shape[1], wgt.shape[2], op, DT[dt], ts.TS_DATAFLOW_IMPLICIT_GEMM)
+        assert ws is not None
+        ws.fill_(0xA5)  # stale contents must not leak through
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            ts.ts_conv_pack_weights(km.s, wgt, op, ws)
+        torch.cuda.current_stream().wait_stream(side)
+        got = fn(km, inp, wgt, out_dtype=torch.float32, dataflow=ts.TS_DATAFLOW_IMPLICIT_GEMM_PACKED, ws=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(got[:rows], ref[:rows]), f"{name} op {op}"
