@@ -34,6 +34,7 @@
 // memory access.  Every output row is written once, no atomics.  Blocks are
 // numbered so that each XCD walks a contiguous range of tiles (its L2 keeps
 // the gathered rows).
+#include <stdint.h>
 #include <stdlib.h>
 
 #include "common.h"
@@ -90,6 +91,9 @@ struct IgK {
   int xcd_map;   // number blocks so that each XCD walks a contiguous range
   int in_order;  // tiles keep rows in index order (launch choice only)
   int ncol;      // weight-resident kernel: block columns
+  const void* w;  // the layer's weights as stored (wmode 1)
+  int wmode;      // weight source: 0 packed fragments (wp), 1 forward rows of w
+  int mirror;     // wmode 1: offset o reads W[kvol-1-o]
 };
 
 // Packed chunk i = ((o * mbt + mb) * kbn + kb) * 64 + lane holds A_o[n][k..k+7]
@@ -196,8 +200,64 @@ __device__ __forceinline__ void bare_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <typename T, int MB, int KB, int G, int D, int NW>
+// Chunk swizzle of the row-by-row layout (WM 1): chunk cc of row ci sits at
+// cc ^ (2 * wswz<MB>(ci)) within its row (pairs of chunks, i.e. 16 output
+// channels, move together).  Chosen so that the 64 lanes of one transposing
+// read (16 rows, 2 chunks each) fall on every 16-byte bank group of a
+// 256-byte period exactly twice for MB = 2, 4 and 8; unswizzled rows of 128
+// or 256 bytes would put 8 or 16 of them on the same banks.
+template <int MB>
+__device__ __forceinline__ int wswz(int ci) {
+  return MB >= 8 ? ((ci & 7) + 2 * ((ci >> 3) & 3)) & 7 : ((ci >> 3) & 3) & (MB - 1);
+}
+
+// Source of the 16-byte weight chunk r * 64 + lane of offset o for the block
+// column whose first fragment row is mb0:
+//   WM 0: the packed fragments (fragment r of the column);
+//   WM 1: W[o] as the forward stores it, [c_src][c_dst]: the column's slice
+//         kept row by row (row ci = 2*MB chunks of 8 output channels, in the
+//         swizzled order of wswz), for the transposing fragment reads.
+// Output channels past c_dst read channel 0: they feed accumulators that are
+// never stored.
+template <typename T, int MB, int KB, int WM>
+__device__ __forceinline__ const u32x4* wchunk(const IgK& a, int o, int mb0, int r, int lane) {
+  if constexpr (WM == 0) {
+    const int live = (a.mbt - mb0) * KB;  // fragments of this column inside the packing
+    const int64_t base = (static_cast<int64_t>(o) * a.mbt + mb0) * KB;
+    return a.wp + (base + (r < live ? r : 0)) * 64 + lane;
+  } else {
+    const int os = a.mirror ? a.kvol - 1 - o : o;
+    const T* w = static_cast<const T*>(a.w);
+    const int c = r * 64 + lane;  // the LDS chunk this lane fills
+    const int ci = c / (2 * MB), cc = (c - ci * (2 * MB)) ^ (2 * wswz<MB>(ci));
+    int co = mb0 * 16 + cc * 8;
+    if (co >= a.c_dst) co = 0;
+    return reinterpret_cast<const u32x4*>(w + (static_cast<int64_t>(os) * a.c_src + ci) * a.c_dst + co);
+  }
+}
+
+// Transposing LDS reads (gfx950).  In each group of 16 lanes, lane q + 4m
+// (q, m < 4) names 4 consecutive 16-bit values and lane 4q + r receives value
+// r of the 4-value runs named by lanes q, q+4, q+8, q+12.  With W[o] held row
+// by row ([c_src][MB*16] 16-bit values) and lane (g, q + 4m) of group g naming
+// row 8g + m (+4 for the second read) at column 16*mb + 4q, lane (g, j) gets
+// rows 8g..8g+7 of column 16*mb + j: the A fragment of output channel j and
+// contracted channels 8g..8g+7.  `p0` and `p4` are that lane's byte
+// addresses in LDS for the first and the second four rows.  Kept out of the
+// kernel templates, like the global-to-LDS copy.
+typedef __attribute__((__vector_size__(4 * sizeof(__fp16)))) __fp16 h4tr;
+typedef __attribute__((address_space(3))) h4tr lds_h4tr;
+__device__ __forceinline__ u32x4 lds_tr_frag(const char* p0, const char* p4) {
+  const h4tr lo = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_h4tr*)p0);
+  const h4tr hi = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_h4tr*)p4);
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 l = __builtin_bit_cast(u32x2, lo), h = __builtin_bit_cast(u32x2, hi);
+  return u32x4{l[0], l[1], h[0], h[1]};
+}
+
+template <typename T, int MB, int KB, int G, int D, int NW, int WM>
 __global__ __launch_bounds__(NW * 64) void k_igemm(IgK a) {
+  constexpr bool TR = WM == 1;  // transposing fragment reads of the row-by-row layout
   typedef typename Mfma<T>::frag Frag;
   constexpr int FR = MB * KB;                      // fragments per offset and block column
   constexpr int CHUNKS = FR * 64;                  // 16-byte chunks per weight slice
@@ -286,16 +346,20 @@ __global__ __launch_bounds__(NW * 64) void k_igemm(IgK a) {
   // start: they feed rows of output channels that are never written out.
   // Wave-uniform; FW loads when the wave has FW fragments, fewer otherwise.
   auto wcopy = [&](int o, int bb) {
-    const int64_t base = (static_cast<int64_t>(o) * a.mbt + mb0) * KB;
-    const int live = (a.mbt - mb0) * KB;           // fragments of this column inside the packing
 #pragma unroll
     for (int j = 0; j < FW; ++j) {
       const int f = wave + NW * j;
       if (FR % NW != 0 && f >= FR) break;
-      const u32x4* srcf = a.wp + (base + (f < live ? f : 0)) * 64 + lane;
-      lds_copy16(srcf, (lds_u32x4*)&wl[bb][f * 64]);
+      lds_copy16(wchunk<T, MB, KB, WM>(a, o, mb0, f, lane), (lds_u32x4*)&wl[bb][f * 64]);
     }
   };
+  // transposing reads: this lane's byte offsets within a slice, for the
+  // first and the second four rows (row 8*kq + m (+4), column pair q >> 1,
+  // half q & 1), and the swizzle of those rows as a byte mask
+  const int trq = lane & 3, trm = (lane >> 2) & 3;
+  const int tr_b0 = (8 * kq + trm) * (MB * 32) + (trq >> 1) * 16 + (trq & 1) * 8;
+  const int tr_b4 = tr_b0 + 4 * MB * 32;
+  const int tr_x0 = 32 * wswz<MB>(8 * kq + trm), tr_x4 = 32 * wswz<MB>(8 * kq + 4 + trm);
 
   if (U) {
     // Offsets u_0 < u_1 < ... of U.  Weights: two LDS buffers, W(u_j) in
@@ -334,7 +398,15 @@ __global__ __launch_bounds__(NW * 64) void k_igemm(IgK a) {
         for (int kb = 0; kb < KB; ++kb) {
           Frag af[MB];
 #pragma unroll
-          for (int mb = 0; mb < MB; ++mb) af[mb] = __builtin_bit_cast(Frag, lw[(mb * KB + kb) * 64 + lane]);
+          for (int mb = 0; mb < MB; ++mb) {
+            if constexpr (TR) {
+              const char* sl = reinterpret_cast<const char*>(lw) + kb * 32 * MB * 32;
+              af[mb] = __builtin_bit_cast(Frag, lds_tr_frag(sl + tr_b0 + ((mb * 32) ^ tr_x0),
+                                                            sl + tr_b4 + ((mb * 32) ^ tr_x4)));
+            } else {
+              af[mb] = __builtin_bit_cast(Frag, lw[(mb * KB + kb) * 64 + lane]);
+            }
+          }
 #pragma unroll
           for (int g = 0; g < G; ++g) {
             if (!((m[g] >> oc) & 1)) continue;  // wave-uniform
@@ -406,8 +478,9 @@ __global__ __launch_bounds__(NW * 64) void k_igemm(IgK a) {
 //     wait before a step covers that step's gathers only.
 constexpr int kResFrags = 144;
 
-template <typename T, int MB, int KB, int G, int D, int NW>
+template <typename T, int MB, int KB, int G, int D, int NW, int WM>
 __global__ __launch_bounds__(NW * 64) void k_igemm_res(IgK a) {
+  constexpr bool TR = WM == 1;
   typedef typename Mfma<T>::frag Frag;
   constexpr int FR = MB * KB;   // fragments per offset and block column
   constexpr int GL = G * KB;    // gather loads per wave and offset
@@ -424,15 +497,17 @@ __global__ __launch_bounds__(NW * 64) void k_igemm_res(IgK a) {
   const int bj = bi / a.ncol;
   const int mb0 = column * MB;
   const int kvol = a.kvol;
+  // transposing reads: this lane's byte offsets within a slice (see k_igemm)
+  const int trq = lane & 3, trm = (lane >> 2) & 3;
+  const int tr_b0 = (8 * kq + trm) * (MB * 32) + (trq >> 1) * 16 + (trq & 1) * 8;
+  const int tr_b4 = tr_b0 + 4 * MB * 32;
+  const int tr_x0 = 32 * wswz<MB>(8 * kq + trm), tr_x4 = 32 * wswz<MB>(8 * kq + 4 + trm);
 
   // the column's weights, every offset: fragment f = o * FR + mb * KB + kb
   {
-    const int live = (a.mbt - mb0) * KB;  // fragments of this column inside the packing
     for (int f = wave; f < kvol * FR; f += NW) {
       const int o = f / FR, r = f - o * FR;
-      const int64_t base = (static_cast<int64_t>(o) * a.mbt + mb0) * KB;
-      const u32x4* srcf = a.wp + (base + (r < live ? r : 0)) * 64 + lane;
-      lds_copy16(srcf, (lds_u32x4*)&wl[f * 64]);
+      lds_copy16(wchunk<T, MB, KB, WM>(a, o, mb0, r, lane), (lds_u32x4*)&wl[f * 64]);
     }
     if (threadIdx.x == 0) next_group = 0u;
     wait_vm<0>();
@@ -556,7 +631,15 @@ __global__ __launch_bounds__(NW * 64) void k_igemm_res(IgK a) {
             for (int kb = 0; kb < KB; ++kb) {
               Frag af[MB];
 #pragma unroll
-              for (int mb = 0; mb < MB; ++mb) af[mb] = __builtin_bit_cast(Frag, lw[(mb * KB + kb) * 64 + lane]);
+              for (int mb = 0; mb < MB; ++mb) {
+                if constexpr (TR) {
+                  const char* sl = reinterpret_cast<const char*>(lw) + kb * 32 * MB * 32;
+                  af[mb] = __builtin_bit_cast(Frag, lds_tr_frag(sl + tr_b0 + ((mb * 32) ^ tr_x0),
+                                                                sl + tr_b4 + ((mb * 32) ^ tr_x4)));
+                } else {
+                  af[mb] = __builtin_bit_cast(Frag, lw[(mb * KB + kb) * 64 + lane]);
+                }
+              }
 #pragma unroll
               for (int g = 0; g < G; ++g) {
                 if (!((m[g] >> oc) & 1)) continue;  // wave-uniform
@@ -651,7 +734,10 @@ hipError_t launch_gw(IgK k, hipStream_t s) {
   k.nb8 = ceil_div<int64_t>(k.nblk, 8);
   k.xcd_map = xcd_map_on();
   dim3 grid(static_cast<unsigned>(k.xcd_map ? k.nb8 * 8 : k.nblk), static_cast<unsigned>(ceil_div(k.c_dst / 16, MB)));
-  k_igemm<T, MB, KB, G, 2, NW><<<grid, NW * 64, 0, s>>>(k);
+  if (k.wmode == 1)
+    k_igemm<T, MB, KB, G, 2, NW, 1><<<grid, NW * 64, 0, s>>>(k);
+  else
+    k_igemm<T, MB, KB, G, 2, NW, 0><<<grid, NW * 64, 0, s>>>(k);
   return hipGetLastError();
 }
 
@@ -705,7 +791,10 @@ hipError_t launch_res_mk(IgK k, int ncu, hipStream_t s) {
   const int64_t need = ceil_div<int64_t>(ceil_div<int64_t>(k.nblk, 8), NW);  // blocks that have a group
   k.nb8 = per < need ? per : need;
   dim3 grid(static_cast<unsigned>(8 * k.ncol * k.nb8));
-  k_igemm_res<T, MB, KB, G, D, NW><<<grid, NW * 64, 0, s>>>(k);
+  if (k.wmode == 1)
+    k_igemm_res<T, MB, KB, G, D, NW, 1><<<grid, NW * 64, 0, s>>>(k);
+  else
+    k_igemm_res<T, MB, KB, G, D, NW, 0><<<grid, NW * 64, 0, s>>>(k);
   return hipGetLastError();
 }
 
@@ -801,9 +890,28 @@ hipError_t launch_wpack(const ConvArgs& a, void* ws, hipStream_t s) {
   return hipGetLastError();
 }
 
+// TS_IGEMM_WDIRECT=0 makes every call pack its weights first (tuning).
+static int wdirect_on() {
+  static const int on = [] {
+    const char* e = getenv("TS_IGEMM_WDIRECT");
+    return e && e[0] == '0' ? 0 : 1;
+  }();
+  return on;
+}
+
 hipError_t launch_igemm(const ConvArgs& a, void* ws, hipStream_t s) {
   const ts_rel& rel = *a.rel;
-  if (!a.prepacked) {
+  // The kernels copy forward-layout weights straight from w (16-byte aligned)
+  // into a row-by-row LDS layout read with transposing loads, so no pack
+  // launch precedes them.  Measured faster for the weight-resident kernel
+  // and for block columns of up to 64 output channels; a 128-channel column
+  // of the barrier-stepped kernel reads its fragments faster packed (train
+  // forward 138.6 vs 141 us), as does dgrad, whose chunks would come from
+  // 16 rows apiece.  Weights packed ahead use the packed layout.
+  const int rmb = res_mb(a.kvol, a.c_src, a.c_dst);
+  const bool direct = !a.prepacked && !a.transpose && wdirect_on() &&
+                      (reinterpret_cast<uintptr_t>(a.w) & 15) == 0 && (rmb != 0 || ceil_div(a.c_dst, 16) <= 4);
+  if (!a.prepacked && !direct) {
     const hipError_t e = launch_wpack(a, ws, s);
     if (e != hipSuccess) return e;
   }
@@ -826,7 +934,9 @@ hipError_t launch_igemm(const ConvArgs& a, void* ws, hipStream_t s) {
   k.nb8 = 0;
   k.in_order = a.rows_in_order ? 1 : 0;
   k.ncol = 1;
-  const int rmb = res_mb(a.kvol, a.c_src, a.c_dst);
+  k.w = a.w;
+  k.wmode = direct ? 1 : 0;
+  k.mirror = a.mirror ? 1 : 0;
   if (a.in_dtype == TS_F16) return rmb ? launch_res<_Float16>(k, rmb, s) : launch_t<_Float16>(k, s);
   return rmb ? launch_res<__bf16>(k, rmb, s) : launch_t<__bf16>(k, s);
 }

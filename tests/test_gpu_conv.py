@@ -203,3 +203,23 @@ def test_prepacked_weights(ts, case):
         got = fn(km, inp, wgt, out_dtype=torch.float32, dataflow=ts.TS_DATAFLOW_IMPLICIT_GEMM_PACKED, ws=ws)
         torch.cuda.synchronize()
         assert torch.equal(got[:rows], ref[:rows]), f"{name} op {op}"
+
+
+@pytest.mark.parametrize("case", [c for c in CONV_CASES if c[0] in ("lidar_f16_64", "down_f16_64x128", "fuzz_f16_32x16")],
+                         ids=["lidar_f16_64", "down_f16_64x128", "fuzz_f16_32x16"])
+def test_unaligned_weights(ts, case):
+    """Weights whose address is not 16-byte aligned take the packed path
+    (the direct weight copies need aligned 16-byte chunks); the forward is
+    bitwise that of aligned weights."""
+    name, c, k, s, cin, cout, dt = case
+    km, tr, oc, x, w, dy = make_problem(c, k, s, cin, cout, dt, 1300)
+    xd, wd = dev(x), dev(w)
+    buf = torch.empty(wd.numel() + 8, dtype=wd.dtype, device="cuda")
+    wu = buf[1:1 + wd.numel()].view(wd.shape)
+    wu.copy_(wd)
+    assert wu.data_ptr() % 16 != 0
+    a = ts.conv_fwd(km, xd, wd, out_dtype=torch.float32)
+    b = ts.conv_fwd(km, xd, wu, out_dtype=torch.float32)
+    rows = oc.shape[0]
+    assert torch.equal(a[:rows], b[:rows]), name
+    assert_feature_close(b[:rows], oracle.conv_fwd(tr, x, w, rows), DT[dt], f"{name} unaligned weights")
