@@ -768,7 +768,7 @@ def main():
         "kmap_hbm_frac": r["kmap_gbs"] / HBM_PEAK_GBS,
         "stages_us": r["stages_us"],
         "stages_us_cold": r["stages_us_cold"],
-        "roofline": {"bound": "hbm", "kernel": "SubmConv3d forward call (k_wpack + k_igemm)",
+        "roofline": {"bound": "hbm", "kernel": "SubmConv3d forward call (k_igemm, weights read from w as stored)",
                      "achieved": r["fwd_alg_bytes"] / conv_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": r["fwd_alg_bytes"] / conv_s / 1e9 / HBM_PEAK_GBS, "traffic": measured_traffic(),
                      "alg_bytes_per_launch": r["fwd_alg_bytes"], "launch_us": r["stages_us"]["conv"]},
