@@ -326,10 +326,13 @@ size_t ts_conv_workspace_bytes(const ts_kmap* map, int cin, int cout, int op, ts
  * ws in the fragment order the implicit GEMM of `op` reads (TS_OP_FWD,
  * TS_OP_DGRAD or TS_OP_TRANSPOSE on this map: dgrad and the transposed
  * convolution mirror the offsets on a submanifold map, dgrad also swaps the
- * channel roles).  The implicit-GEMM calls do this themselves as their first
- * launch; packing separately lets the caller run it on another stream (it
- * needs only the weights, not the map's contents) and then call the op with
- * TS_DATAFLOW_IMPLICIT_GEMM_PACKED and the same ws, cin, cout and dtype.
+ * channel roles).  Without it the implicit-GEMM calls either read the
+ * weights as stored (forward-layout weights on 16-byte-aligned storage, for
+ * the shapes where that is faster) or pack them into ws as their first
+ * launch; packing separately lets a caller whose weights stay fixed pack once
+ * (on any stream: it needs only the weights, not the map's contents) and
+ * then call the op with TS_DATAFLOW_IMPLICIT_GEMM_PACKED and the same ws,
+ * cin, cout and dtype.
  * ws_bytes must be at least ts_conv_workspace_bytes(map, cin, cout, op,
  * in_dtype, TS_DATAFLOW_IMPLICIT_GEMM).  Errors: TS_ERR_INVALID_ARG (null,
  * bad op or sizes, short ws), TS_ERR_UNSUPPORTED (the shape or dtype has no
