@@ -9,9 +9,14 @@
 // with memory access) for its speed; the relation is the kernel map of the
 // torch-lattice page "Migrating from TorchSparse".
 //
-// First a small kernel packs the weights into MFMA fragment order (16-byte
-// chunks, fragment (o, mb, kb) = 64 consecutive chunks), so every later copy
-// of a slice is a straight coalesced 16-byte copy.
+// Weights reach LDS in one of two layouts.  Forward-layout weights on
+// 16-byte-aligned storage are copied as stored, row by row with a chunk
+// swizzle, and fragments are built with gfx950's transposing LDS reads (no
+// extra launch).  Otherwise (dgrad, 128-channel columns of the barrier-
+// stepped kernel, unaligned or pre-packed weights) a small kernel first packs
+// them into MFMA fragment order (16-byte chunks, fragment (o, mb, kb) = 64
+// consecutive chunks), so every copy of a slice is a straight coalesced
+// 16-byte copy.
 //
 // Work split.  A block of NW wavefronts owns NW*G tiles of 16 destination
 // rows (each wavefront G tiles, the output channels of one block column) and
