@@ -158,6 +158,22 @@ def run_cold(fns, names, steps, scratch_mib=COLD_SCRATCH_MIB):
     return sum(st.values()) / 1e3, st
 
 
+def back_to_back_us(fn, steps):
+    """One stage's launches repeated `steps` times back to back between two
+    HIP events on the launch stream: us per call, with only the gaps between
+    consecutive calls (not the wait behind the stage before it), which is what
+    a kernel trace's average duration is compared with."""
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / steps
+
+
 def trials(g, steps, n=TRIALS):
     """`n` further timed runs of `steps` graph replays each (HIP events):
     ms per step of every run, for the median and spread."""
@@ -460,6 +476,7 @@ def measure_lidar(ts, steps, warmup):
     ms, ms_events = run_graph(g, steps, warmup)
     tr = trials(g, steps)
     ms_cold, st_cold = run_cold(s.fns, s.names, COLD_STEPS)
+    conv_b2b = back_to_back_us(s.fns[-1], steps)
     n, cap = s.n, s.table.cap
     P = popcount_sum(s.kmap.rel_arrays("fwd")["row_mask"][:n], 27)
     cin, cout, kvol, e = w.cin, w.cout, 27, 2
@@ -474,6 +491,7 @@ def measure_lidar(ts, steps, warmup):
         "stages_us": {k: round(v, 3) for k, v in st.items()},
         "trials_ms_per_step": [round(t, 5) for t in tr],
         "ms_per_step_cold": ms_cold, "stages_us_cold": {k: round(v, 3) for k, v in st_cold.items()},
+        "conv_back_to_back_us": conv_b2b,
         "fwd_tflops": flop / conv_s / 1e12,
         "fwd_mfma_frac": flop / conv_s / 1e12 / MFMA_F16_PEAK_TFLOPS,
         "fwd_alg_bytes": conv_bytes,
@@ -771,7 +789,8 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "SubmConv3d forward call (k_igemm, weights read from w as stored)",
                      "achieved": r["fwd_alg_bytes"] / conv_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": r["fwd_alg_bytes"] / conv_s / 1e9 / HBM_PEAK_GBS, "traffic": measured_traffic(),
-                     "alg_bytes_per_launch": r["fwd_alg_bytes"], "launch_us": r["stages_us"]["conv"]},
+                     "alg_bytes_per_launch": r["fwd_alg_bytes"], "launch_us": r["stages_us"]["conv"],
+                     "launch_us_back_to_back": r["conv_back_to_back_us"]},
         "secondary": secondary,
     }
     if not args.no_cpu:
