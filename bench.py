@@ -230,7 +230,7 @@ def setup_subm(ts, w, out_dtype=None, kmap_flags=None) -> Step:
                 kmap=kmap, x=x, w=wt, y=y, flags=flags, n=n, kvol=k ** nd)
 
 
-def setup_down(ts, w, kmap_flags=0) -> Step:
+def setup_down(ts, w, kmap_flags=0, out_dtype=None) -> Step:
     """Strided Conv3d (support + kernel map + forward in one call).  Tiles
     are grouped by offset mask: with 8 offsets and 64 -> 128 channels the
     shorter contraction repays the sort even for one use."""
@@ -246,7 +246,7 @@ def setup_down(ts, w, kmap_flags=0) -> Step:
     kb = ts.ts_kmap_bytes(n, n, 3, 2, 2, kmap_flags)
     mbuf = torch.empty(kb + ts.ts_support_scratch_bytes(n), dtype=torch.uint8, device=dev)
     km = ts.TsKmap()
-    y = torch.empty((n, w.cout), dtype=torch.float16, device=dev)
+    y = torch.empty((n, w.cout), dtype=out_dtype or torch.float16, device=dev)
     ws = torch.empty(2 * 8 * w.cin * w.cout + 4096, dtype=torch.uint8, device=dev)
 
     def hash_build():
@@ -306,7 +306,7 @@ def setup_pixels(ts, w, dataflow=None, kmap_flags=None) -> Step:
                 kmap=kmap, x=x, w1=w1, w2=w2, y1=y1, y2=y2, flags=flags, n=n, kvol=9)
 
 
-def setup_generative(ts, w, kmap_flags=None) -> Step:
+def setup_generative(ts, w, kmap_flags=None, out_dtype=None) -> Step:
     """Generative stride-1 Conv3d k3 on the ring scan: hash of the inputs, the
     generated support (every site some input reaches), the target map over
     it and the forward.  The output row count is data-dependent; it is taken
@@ -332,7 +332,7 @@ def setup_generative(ts, w, kmap_flags=None) -> Step:
     scratch = torch.empty(ts.ts_generative_scratch_bytes(n, nd, k), dtype=torch.uint8, device=dev)
     kbuf = torch.empty(ts.ts_kmap_bytes(n, m, nd, k, 1, kflags), dtype=torch.uint8, device=dev)
     km = ts.TsKmap()
-    y = torch.empty((m, w.cout), dtype=x.dtype, device=dev)
+    y = torch.empty((m, w.cout), dtype=out_dtype or x.dtype, device=dev)
 
     def hash_build():
         ts.ts_hash_build(coords, table.buf, table.cap, flags)
@@ -360,7 +360,7 @@ def setup_generative(ts, w, kmap_flags=None) -> Step:
                 m=m, kvol=k ** nd)
 
 
-def setup_up(ts, w) -> Step:
+def setup_up(ts, w, out_dtype=None) -> Step:
     """Transposed convolutions on the two-scene workload's strided layer.
     Set-up runs the strided support and its map (relation with its transpose
     and pair lists), as the encoder layer would.  Timed:
@@ -381,7 +381,7 @@ def setup_up(ts, w) -> Step:
     coarse = out[:m].contiguous()
     x = synth.normal(1000 * w.index + 905, (enc.s.n_out_cap, 128), 1.0, "f16").to(dev)
     wt = synth.weight(1000 * w.index + 906, 8, 128, 64, "f16").to(dev)
-    y = torch.empty((n, 64), dtype=torch.float16, device=dev)
+    y = torch.empty((n, 64), dtype=out_dtype or torch.float16, device=dev)
     ws_t = ts.workspace(enc, 128, 64, ts.TS_OP_TRANSPOSE, torch.float16)
 
     def transpose():
@@ -398,7 +398,7 @@ def setup_up(ts, w) -> Step:
     kbuf = torch.empty(ts.ts_kmap_bytes(m, fine_cap, 3, 2, 2, kflags), dtype=torch.uint8, device=dev)
     km = ts.TsKmap()
     xc = x[:m].contiguous()
-    yg = torch.empty((fine_cap, 64), dtype=torch.float16, device=dev)
+    yg = torch.empty((fine_cap, 64), dtype=out_dtype or torch.float16, device=dev)
 
     def support():
         ts.ts_transposed_support(coarse, 2, 2, fine, n_fine, fine_table.buf, fine_table.cap, scratch, flags)
@@ -422,7 +422,7 @@ def setup_up(ts, w) -> Step:
                 fine_table=fine_table, gen=gen, yg=yg, flags=flags, n=n)
 
 
-def setup_train(ts, w) -> Step:
+def setup_train(ts, w, out_dtype=None) -> Step:
     """bf16 128 -> 128 training step: hash, kernel map (+pairs), forward,
     dgrad (mirrored offsets), wgrad (fp32 dW)."""
     dev = torch.device("cuda")
@@ -434,8 +434,8 @@ def setup_train(ts, w) -> Step:
     fk = ts.TS_KMAP_PAIRS
     kbuf = torch.empty(ts.ts_kmap_bytes(n, n, 3, 3, 1, fk), dtype=torch.uint8, device=dev)
     km = ts.TsKmap()
-    y = torch.empty((n, 128), dtype=torch.bfloat16, device=dev)
-    dx = torch.empty((n, 128), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((n, 128), dtype=out_dtype or torch.bfloat16, device=dev)
+    dx = torch.empty((n, 128), dtype=out_dtype or torch.bfloat16, device=dev)
     dw = torch.empty((27, 128, 128), dtype=torch.float32, device=dev)
 
     def hash_build():
@@ -503,6 +503,9 @@ def measure_lidar(ts, steps, warmup):
         "hash_gbs": hash_bytes / (st["hash"] * 1e-6) / 1e9,
         "err_flags": int(s.flags.item()),
     }
+    # the same forward with fp32 outputs, graded against the oracle in the
+    # CPU-baseline leg (which computes the oracle's forward anyway)
+    res["_y32"] = ts.conv_fwd(s.kmap, s.x, s.w, out_dtype=torch.float32).cpu()
     return w, res
 
 
@@ -668,11 +671,14 @@ def measured_traffic():
 
 
 # ---------------------------------------------------------------- CPU oracle
-def cpu_baseline(w, P, min_seconds=10.0):
+def cpu_baseline(w, P, y32=None, min_seconds=10.0):
     """The oracle (fp64, one thread) on the full ring-scan scene: hash +
     kernel map and forward repeated until about `min_seconds` of CPU time
     (the headline figure), then dgrad and wgrad once each with a seeded
-    upstream gradient, every stage reported on its own."""
+    upstream gradient, every stage reported on its own.  With `y32` (the GPU
+    forward of the same scene with fp32 outputs) the error distribution of
+    the GPU result against the oracle's forward is reported too."""
+    import numpy as np
     import oracle
     oracle.lib()
     t_kmap = t_fwd = 0.0
@@ -681,7 +687,7 @@ def cpu_baseline(w, P, min_seconds=10.0):
         t0 = time.perf_counter()
         tr = oracle.kmap(w.coords, w.coords, 3, 1)
         t1 = time.perf_counter()
-        oracle.conv_fwd(tr, w.x, w.w, w.coords.shape[0])
+        y_ref = oracle.conv_fwd(tr, w.x, w.w, w.coords.shape[0])
         t2 = time.perf_counter()
         assert len(tr[0]) == P, (len(tr[0]), P)
         t_kmap += t1 - t0
@@ -703,6 +709,13 @@ def cpu_baseline(w, P, min_seconds=10.0):
             d["gflop_s"] = flop / t / 1e9
         return d
 
+    parity = None
+    if y32 is not None:
+        e = np.abs(y32.double().numpy() - y_ref).ravel()
+        m = float(np.abs(y_ref).max())
+        parity = {"what": "GPU forward (fp32 outputs) vs fp64 oracle, every element", "elements": int(e.size),
+                  "max_ref": m, "err_p50": float(np.percentile(e, 50)), "err_p99": float(np.percentile(e, 99)),
+                  "err_max": float(e.max()), "max_err_over_max_ref": float(e.max()) / m, "bar": 2e-3}
     return {"value": flop / sec / 1e12, "unit": "TFLOP/s", "cores": 1, "host_cpus": os.cpu_count(),
             "kind": "oracle",
             "sample": f"full ring-scan scene ({w.coords.shape[0]} voxels, {P} pairs), {passes} passes of hash + "
@@ -710,7 +723,8 @@ def cpu_baseline(w, P, min_seconds=10.0):
                       f"value counts the forward's map-valid flops over hash + kernel map + forward",
             "stages": {"hash_kmap": stage(t_kmap / passes, False), "fwd": stage(t_fwd / passes, True),
                        "dgrad": stage(t_dgrad, True), "wgrad": stage(t_wgrad, True)},
-            "seconds": t_kmap + t_fwd + t_dgrad + t_wgrad}
+            "seconds": t_kmap + t_fwd + t_dgrad + t_wgrad,
+            "parity_vs_gpu": parity}
 
 
 def copy_calibration(mb: int, steps: int):
@@ -794,7 +808,7 @@ def main():
         "secondary": secondary,
     }
     if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(w, r["pairs"])
+        line["cpu_baseline"] = cpu_baseline(w, r["pairs"], r["_y32"])
     print(json.dumps(line))
 
 

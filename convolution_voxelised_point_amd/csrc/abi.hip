@@ -268,7 +268,9 @@ ts_status ts_devoxelize(const int32_t* vox_of, int64_t n, const void* vox_feats,
 }
 
 size_t ts_kmap_bytes(int64_t n_in, int64_t n_out_cap, int ndim, int ksize, int stride, uint32_t flags) {
-  if (n_in < 0 || n_out_cap < 0 || !shape_ok(ndim, ksize, stride)) return 0;
+  if (n_in < 0 || n_out_cap < 0 || n_in > kMaxRows || n_out_cap > kMaxRows || !shape_ok(ndim, ksize, stride)) return 0;
+  const int kvol = ipow(ksize, ndim);
+  if (n_out_cap * kvol > kMaxRows || n_in * kvol > kMaxRows) return 0;  // ts_kmap_build refuses these shapes
   ts_kmap tmp;
   return layout_kmap(nullptr, &tmp, n_in, n_out_cap, ndim, ksize, stride, flags);
 }
@@ -300,7 +302,12 @@ ts_status ts_kmap_build(const int32_t* in_coords, int64_t n_in, const void* in_t
     if (((flags & TS_KMAP_BWD) || transposed) && (!out_table || !is_pow2(out_cap) || out_cap > kMaxCap))
       return TS_ERR_INVALID_ARG;
   }
+  // Neighbour-table entries, pair-list positions and their scans are int32:
+  // a map with more than 2^31 - 1 (row, offset) slots on either side, or a
+  // pair capacity past that, is refused before anything is laid out.
   if (n_out_cap * kvol > kMaxRows || n_in * kvol > kMaxRows) return TS_ERR_UNSUPPORTED;
+  if ((flags & TS_KMAP_PAIRS) && pair_capacity(n_in, n_out_cap, ndim, ksize, stride, flags) > kMaxRows)
+    return TS_ERR_UNSUPPORTED;
   ts_kmap m;
   const size_t need = layout_kmap(static_cast<char*>(buf), &m, n_in, n_out_cap, ndim, ksize, stride, flags);
   if (buf_bytes < need) return TS_ERR_INVALID_ARG;
@@ -435,7 +442,7 @@ ts_status ts_conv_fwd(const ts_kmap* map, const void* x, int cin, const void* w,
 ts_status ts_subm_conv_fwd(const ts_kmap* map, const void* x, int cin, const void* w, int cout, void* y,
                            ts_dtype in_dtype, ts_dtype out_dtype, ts_dataflow dataflow, void* ws, size_t ws_bytes,
                            hipStream_t stream) {
-  if (!map || map->stride != 1 || (map->flags & TS_KMAP_TARGET)) return TS_ERR_INVALID_ARG;
+  if (!map || map->stride != 1 || (map->flags & (TS_KMAP_TARGET | TS_KMAP_TRANSPOSED))) return TS_ERR_INVALID_ARG;
   return ts_conv_fwd(map, x, cin, w, cout, y, in_dtype, out_dtype, dataflow, ws, ws_bytes, stream);
 }
 

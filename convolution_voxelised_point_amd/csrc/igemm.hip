@@ -40,7 +40,6 @@
 // numbered so that each XCD walks a contiguous range of tiles (its L2 keeps
 // the gathered rows).
 #include <stdint.h>
-#include <stdlib.h>
 
 #include "common.h"
 #include "launch.h"
@@ -105,7 +104,7 @@ struct IgK {
 // with n = mb*16 + lane%16, k = kb*32 + (lane/16)*8; zero for n >= c_dst.
 template <typename T>
 __global__ __launch_bounds__(256) void k_wpack(const T* __restrict__ w, int kvol, int c_src, int c_dst, int mbt,
-                                               int trans, int mirror, u32x4* __restrict__ out) {
+                                               int trans, int mirror, int vec, u32x4* __restrict__ out) {
   const int kbn = c_src / 32;
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (i >= static_cast<int64_t>(kvol) * mbt * kbn * 64) return;
@@ -121,8 +120,14 @@ __global__ __launch_bounds__(256) void k_wpack(const T* __restrict__ w, int kvol
   u32x4 v = {0u, 0u, 0u, 0u};
   if (n < c_dst) {
     const int os = mirror ? kvol - 1 - o : o;
-    if (trans) {
+    if (trans && vec) {  // 16-byte aligned weights: the 8 values are one aligned chunk
       v = *reinterpret_cast<const u32x4*>(w + os * slice + static_cast<int64_t>(n) * c_src + k0);
+    } else if (trans) {
+      unsigned short e[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) e[j] = __builtin_bit_cast(unsigned short, w[os * slice + static_cast<int64_t>(n) * c_src + k0 + j]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = static_cast<unsigned>(e[2 * j]) | (static_cast<unsigned>(e[2 * j + 1]) << 16);
     } else {
       unsigned short e[8];
 #pragma unroll
@@ -698,46 +703,23 @@ __global__ __launch_bounds__(NW * 64) void k_igemm_res(IgK a) {
 // the LDS reads per row and doubles the math per barrier.  Two as well when
 // tiles keep rows in index order: a block's offset union then covers nearly
 // every offset whatever its size.  Otherwise one, which keeps the union of a
-// mask-grouped block small.  TS_IGEMM_G (1 or 2) overrides it for tuning.
-static int tiles_per_wave(int fr, int in_order) {
-  static const int forced = [] {
-    const char* e = getenv("TS_IGEMM_G");
-    return e ? atoi(e) : 0;
-  }();
-  if (forced == 1 || forced == 2) return forced;
-  return (fr >= 32 || in_order) ? 2 : 1;
-}
+// mask-grouped block small.
+static int tiles_per_wave(int fr, int in_order) { return (fr >= 32 || in_order) ? 2 : 1; }
 
-// Workgroups are dealt to the 8 XCDs round-robin; numbering blocks so that
-// XCD x gets a contiguous range keeps each XCD's gathers in its own L2.
-// TS_IGEMM_XCD=0 switches the renumbering off (tuning).
-static int xcd_map_on() {
-  static const int on = [] {
-    const char* e = getenv("TS_IGEMM_XCD");
-    return e && e[0] == '0' ? 0 : 1;
-  }();
-  return on;
-}
+// Workgroups are dealt to the 8 XCDs round-robin; blocks are numbered so
+// that XCD x gets a contiguous range, which keeps each XCD's gathers in its
+// own L2.
 
 // Waves per block: 4, or 8 when tiles keep rows in index order (every block
 // then walks nearly all offsets whatever its size, so a larger block only
-// shares each weight copy among more rows).  TS_IGEMM_NW (4 or 8) overrides
-// it for tuning.
-static int waves_per_block(int in_order) {
-  static const int forced = [] {
-    const char* e = getenv("TS_IGEMM_NW");
-    const int v = e ? atoi(e) : 0;
-    return (v == 4 || v == 8) ? v : 0;
-  }();
-  if (forced) return forced;
-  return in_order ? 8 : 4;
-}
+// shares each weight copy among more rows).
+static int waves_per_block(int in_order) { return in_order ? 8 : 4; }
 
 template <typename T, int MB, int KB, int G, int NW>
 hipError_t launch_gw(IgK k, hipStream_t s) {
   k.nblk = ceil_div<int64_t>(k.n_tiles, NW * G);
   k.nb8 = ceil_div<int64_t>(k.nblk, 8);
-  k.xcd_map = xcd_map_on();
+  k.xcd_map = 1;
   dim3 grid(static_cast<unsigned>(k.xcd_map ? k.nb8 * 8 : k.nblk), static_cast<unsigned>(ceil_div(k.c_dst / 16, MB)));
   if (k.wmode == 1)
     k_igemm<T, MB, KB, G, 2, NW, 1><<<grid, NW * 64, 0, s>>>(k);
@@ -768,17 +750,6 @@ hipError_t launch_mb(const IgK& k, hipStream_t s) {
     case 3: return launch_mb_kb<T, MB, 3>(k, s);
     default: return launch_mb_kb<T, MB, 4>(k, s);
   }
-}
-
-// Output channels per block column: up to 128 (8 fragments) by default;
-// TS_IGEMM_MB (1, 2, 4 or 8 fragments of 16 channels) lowers it for tuning.
-static int max_mb() {
-  static const int forced = [] {
-    const char* e = getenv("TS_IGEMM_MB");
-    const int v = e ? atoi(e) : 0;
-    return (v == 1 || v == 2 || v == 4 || v == 8) ? v : 8;
-  }();
-  return forced;
 }
 
 // Weight-resident launch.  Gathers in flight per wave: D offsets of G * KB
@@ -819,21 +790,12 @@ hipError_t launch_res_m(const IgK& k, int ncu, hipStream_t s) {
 // column would gather every source row and read the neighbour table again:
 // measured slower than the barrier-stepped kernel on the ring scan (50 vs
 // 42 us) and on its generated support (404 vs 340 us), so such layers stay on
-// that kernel.  TS_IGEMM_RES=0 switches the kernel off, TS_IGEMM_RES=2 allows
-// two columns (tuning).
+// that kernel.
 static int res_mb(int kvol, int c_src, int c_dst) {
-  static const int mode = [] {
-    const char* e = getenv("TS_IGEMM_RES");
-    return e ? atoi(e) : 1;
-  }();
-  if (mode <= 0) return 0;
   const int mbt = ceil_div(c_dst, 16), kb = c_src / 32;
-  for (int ncol = 1; ncol <= (mode >= 2 ? 2 : 1); ++ncol) {
-    int mb = 1;
-    while (mb < ceil_div(mbt, ncol)) mb *= 2;
-    if (mb <= 8 && kvol * mb * kb <= kResFrags) return mb;
-  }
-  return 0;
+  int mb = 1;
+  while (mb < mbt) mb *= 2;
+  return (mb <= 8 && kvol * mb * kb <= kResFrags) ? mb : 0;
 }
 
 static int cu_count() {
@@ -862,8 +824,7 @@ hipError_t launch_res(IgK k, int mb, hipStream_t s) {
 
 template <typename T>
 hipError_t launch_t(const IgK& k, hipStream_t s) {
-  int mbt = k.c_dst / 16;
-  if (mbt > max_mb()) mbt = max_mb();
+  const int mbt = k.c_dst / 16;
   if (mbt > 4) return launch_mb<T, 8>(k, s);
   if (mbt > 2) return launch_mb<T, 4>(k, s);
   if (mbt > 1) return launch_mb<T, 2>(k, s);
@@ -886,22 +847,14 @@ hipError_t launch_wpack(const ConvArgs& a, void* ws, hipStream_t s) {
   const int mbt = ceil_div(a.c_dst, 16);
   const int64_t chunks = static_cast<int64_t>(a.kvol) * mbt * (a.c_src / 32) * 64;
   const unsigned pg = static_cast<unsigned>(ceil_div<int64_t>(chunks, 256));
+  const int vec = (reinterpret_cast<uintptr_t>(a.w) & 15) == 0 ? 1 : 0;
   if (a.in_dtype == TS_F16)
     k_wpack<_Float16><<<pg, 256, 0, s>>>(static_cast<const _Float16*>(a.w), a.kvol, a.c_src, a.c_dst, mbt,
-                                         a.transpose ? 1 : 0, a.mirror ? 1 : 0, static_cast<u32x4*>(ws));
+                                         a.transpose ? 1 : 0, a.mirror ? 1 : 0, vec, static_cast<u32x4*>(ws));
   else
     k_wpack<__bf16><<<pg, 256, 0, s>>>(static_cast<const __bf16*>(a.w), a.kvol, a.c_src, a.c_dst, mbt,
-                                       a.transpose ? 1 : 0, a.mirror ? 1 : 0, static_cast<u32x4*>(ws));
+                                       a.transpose ? 1 : 0, a.mirror ? 1 : 0, vec, static_cast<u32x4*>(ws));
   return hipGetLastError();
-}
-
-// TS_IGEMM_WDIRECT=0 makes every call pack its weights first (tuning).
-static int wdirect_on() {
-  static const int on = [] {
-    const char* e = getenv("TS_IGEMM_WDIRECT");
-    return e && e[0] == '0' ? 0 : 1;
-  }();
-  return on;
 }
 
 hipError_t launch_igemm(const ConvArgs& a, void* ws, hipStream_t s) {
@@ -914,7 +867,7 @@ hipError_t launch_igemm(const ConvArgs& a, void* ws, hipStream_t s) {
   // forward 138.6 vs 141 us), as does dgrad, whose chunks would come from
   // 16 rows apiece.  Weights packed ahead use the packed layout.
   const int rmb = res_mb(a.kvol, a.c_src, a.c_dst);
-  const bool direct = !a.prepacked && !a.transpose && wdirect_on() &&
+  const bool direct = !a.prepacked && !a.transpose &&
                       (reinterpret_cast<uintptr_t>(a.w) & 15) == 0 && (rmb != 0 || ceil_div(a.c_dst, 16) <= 4);
   if (!a.prepacked && !direct) {
     const hipError_t e = launch_wpack(a, ws, s);

@@ -20,8 +20,6 @@
 // default, sorted by offset mask inside windows of 4096 rows so that the 16
 // rows of a tile share most offsets and the contraction pads less.  The sort
 // is stable (ties keep row order), so the map is deterministic.
-#include <stdlib.h>
-
 #include "common.h"
 #include "launch.h"
 
@@ -581,33 +579,17 @@ RelK make_relk(const RelBuild& bld, const ts_rel& rel) {
   return a;
 }
 
-// Rows sorted together: kSortItems * threads.  TS_SORT_THREADS (256, 512 or
-// 1024) overrides the default for tuning.
-static int sort_threads() {
-  static const int v = [] {
-    const char* e = getenv("TS_SORT_THREADS");
-    const int t = e ? atoi(e) : 0;
-    return (t == 256 || t == 512 || t == 1024) ? t : 1024;
-  }();
-  return v;
-}
+// Rows sorted together: kSortItems * kSortThreads (one window per
+// workgroup).
+constexpr int kSortThreads = 1024;
 
 void launch_sort(const RelK& a, hipStream_t s) {
   const int64_t slots = a.n_tiles * kTile;
   const int nbits = a.kvol < 32 ? a.kvol : 32;
-  const int th = sort_threads();
-  const unsigned grid = static_cast<unsigned>(ceil_div<int64_t>(slots, static_cast<int64_t>(th) * kSortItems));
-  switch (th) {
-    case 256:
-      k_rel_sort<256><<<grid, 256, 0, s>>>(a.row_mask, a.n_dest_cap, a.n_dest, nbits, slots, a.tile_rows, a.tile_mask);
-      break;
-    case 512:
-      k_rel_sort<512><<<grid, 512, 0, s>>>(a.row_mask, a.n_dest_cap, a.n_dest, nbits, slots, a.tile_rows, a.tile_mask);
-      break;
-    default:
-      k_rel_sort<1024><<<grid, 1024, 0, s>>>(a.row_mask, a.n_dest_cap, a.n_dest, nbits, slots, a.tile_rows, a.tile_mask);
-      break;
-  }
+  const unsigned grid =
+      static_cast<unsigned>(ceil_div<int64_t>(slots, static_cast<int64_t>(kSortThreads) * kSortItems));
+  k_rel_sort<kSortThreads><<<grid, kSortThreads, 0, s>>>(a.row_mask, a.n_dest_cap, a.n_dest, nbits, slots,
+                                                         a.tile_rows, a.tile_mask);
 }
 
 template <int MODE, int ND, int K>

@@ -306,7 +306,11 @@ hipError_t launch_wgrad(const ts_kmap* map, const void* x, int cin, const void* 
   const int64_t elems = static_cast<int64_t>(cin) * cout;
   k_wgrad_chunks<<<1, 64, 0, s>>>(map->pair_start, map->kvol, chunk_base);
   const unsigned nch = static_cast<unsigned>(max_chunks(map));
-  const bool mfma = dt != TS_F32 && cin % 16 == 0 && cout % 16 == 0;
+  // The MFMA kernel stages rows with 16-byte loads: rows of 16-channel
+  // multiples are 16-byte aligned when the matrices are; otherwise the FMA
+  // kernel, which reads element by element, takes the layer.
+  const bool aligned = (reinterpret_cast<uintptr_t>(x) & 15) == 0 && (reinterpret_cast<uintptr_t>(dy) & 15) == 0;
+  const bool mfma = dt != TS_F32 && cin % 16 == 0 && cout % 16 == 0 && aligned;
   if (mfma) {
     if (cin >= 128 && cout >= 128)
       launch_wgrad_mfma<128>(grid_chunks(nch, cin, cout, 128), dt, map, x, cin, dy, cout, chunk_base, partial, s);

@@ -340,20 +340,43 @@ size_t ts_conv_workspace_bytes(const ts_kmap* map, int cin, int cout, int op, ts
 ts_status ts_conv_pack_weights(const ts_kmap* map, const void* w, int cin, int cout, int op, ts_dtype in_dtype,
                                void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* y[n_out][cout] = sparse conv of x[n_in][cin] with w[kvol][cin][cout] over
- * map->fwd (any stride). */
+/* Sparse convolution forward over a built map (torch-lattice migration page,
+ * section "Sparse tensor expectations": coordinate row i owns feature row i
+ * and the kernel map relates them; section "Backend and configuration
+ * differences": every dataflow computes the same result for a fixed relation
+ * and weight tensor, up to floating-point rounding; TorchSparse++ abstract:
+ * the gather-GEMM-scatter and implicit-GEMM dataflows).
+ *   y[j][co] = sum over the map's triples (i, j, o) of sum_ci x[i][ci] w[o][ci][co]
+ * x: device [map->n_in][cin] (row-major, in_dtype); w: device [kvol][cin][cout]
+ * (in_dtype); y: device [n_out_cap][cout] (out_dtype), every row below the
+ * device output count written once (zeros for rows without pairs), rows at or
+ * past it not written.  `dataflow` picks the kernel (AUTO: per shape); ws
+ * (device, may be NULL when ts_conv_workspace_bytes(map, cin, cout,
+ * TS_OP_FWD, in_dtype, dataflow) is 0) is scratch the caller owns.  Errors:
+ * TS_ERR_INVALID_ARG (null or short buffers, channel counts outside
+ * [1, 65536], a dataflow the map lacks the lists for), TS_ERR_UNSUPPORTED
+ * (an output type other than fp32 or in_dtype; packed weights for a shape
+ * without an implicit GEMM), TS_ERR_HIP (launch failure).  Any stride. */
 ts_status ts_conv_fwd(const ts_kmap* map, const void* x, int cin, const void* w, int cout, void* y,
                       ts_dtype in_dtype, ts_dtype out_dtype, ts_dataflow dataflow, void* ws,
                       size_t ws_bytes, hipStream_t stream);
 
-/* Submanifold SubmConv3d / SubmConv2d forward: ts_conv_fwd on a stride-1 map
- * (output rows = input rows); a TS_KMAP_TARGET map is rejected. */
+/* Submanifold SubmConv3d / SubmConv2d forward (torch-lattice migration page,
+ * "Convolution mapping" table: SubmConv3d preserves the input coordinate
+ * support; "What is intentionally different", convolution intent): the
+ * output rows are the input rows, y[n_in][cout].  Arguments, ownership and
+ * errors as ts_conv_fwd; a map that is not submanifold (stride > 1, a
+ * TS_KMAP_TARGET or TS_KMAP_TRANSPOSED map) returns TS_ERR_INVALID_ARG. */
 ts_status ts_subm_conv_fwd(const ts_kmap* map, const void* x, int cin, const void* w, int cout, void* y,
                            ts_dtype in_dtype, ts_dtype out_dtype, ts_dataflow dataflow, void* ws,
                            size_t ws_bytes, hipStream_t stream);
 
-/* Strided Conv3d / Conv2d forward, support generation included: runs
+/* Strided Conv3d / Conv2d forward, support generation included
+ * (torch-lattice migration page, "Convolution mapping" table: a strided
+ * forward convolution creates a downsampled support): runs
  * ts_strided_support, ts_kmap_build (kmap_flags) and ts_conv_fwd in order.
+ * Errors of any of the three are returned before the later ones launch;
+ * every argument is validated before the first launch.
  * `map_buf` holds ts_kmap_bytes(n_in, n_in, ndim, ksize, stride, kmap_flags)
  * + ts_support_scratch_bytes(n_in) bytes; *map is filled for the backward
  * pass.  y has capacity n_in rows; rows >= *n_out are not written. */
@@ -418,15 +441,28 @@ ts_status ts_graph_conv_fwd(const int64_t* indptr, const int32_t* src, const int
                             int64_t n_src, int n_rel, const void* x, int cin, const void* w, int cout, void* y,
                             ts_dtype in_dtype, ts_dtype out_dtype, uint32_t* err_flags, hipStream_t stream);
 
-/* dx[n_in][cin] = sum over triples (i, j, o) of dy[j] . W[o]^T.  Strided
- * maps need TS_KMAP_BWD (implicit GEMM) or TS_KMAP_PAIRS (gather-scatter). */
+/* Input gradient of the forward (the training workloads of the TorchSparse++
+ * abstract; the adjoint of ts_conv_fwd over the same relation):
+ *   dx[i][ci] = sum over triples (i, j, o) of sum_co dy[j][co] w[o][ci][co]
+ * dy: device [n_out_cap][cout]; w as in the forward; dx: device
+ * [n_in][cin] (out_dtype), every row written once.  A submanifold map uses
+ * its own offsets mirrored ((i, j, o) and (j, i, kvol-1-o) are the same
+ * pair); strided and target maps need TS_KMAP_BWD (implicit GEMM) or
+ * TS_KMAP_PAIRS (gather-scatter), else TS_ERR_INVALID_ARG.  Workspace and
+ * errors as ts_conv_fwd with TS_OP_DGRAD. */
 ts_status ts_conv_bwd_dgrad(const ts_kmap* map, const void* dy, int cout, const void* w, int cin, void* dx,
                             ts_dtype in_dtype, ts_dtype out_dtype, ts_dataflow dataflow, void* ws,
                             size_t ws_bytes, hipStream_t stream);
 
-/* dw[kvol][cin][cout] (device fp32, overwritten) = sum over triples (i, j, o)
- * of x[i]^T dy[j].  Needs TS_KMAP_PAIRS.  The per-offset reduction is split
- * over chunks of pairs and summed in a fixed order (deterministic). */
+/* Weight gradient of the forward (the training workloads of the TorchSparse++
+ * abstract; the adjoint of ts_conv_fwd in w):
+ *   dw[o][ci][co] = sum over triples (i, j, o) of x[i][ci] dy[j][co]
+ * x: device [n_in][cin], dy: device [n_out_cap][cout] (in_dtype); dw: device
+ * fp32 [kvol][cin][cout], overwritten.  Needs TS_KMAP_PAIRS (else
+ * TS_ERR_INVALID_ARG); ws (device) holds ts_conv_workspace_bytes(map, cin,
+ * cout, TS_OP_WGRAD, ...) bytes.  The per-offset reduction is split over
+ * chunks of pairs and summed in a fixed order, so the result is the same
+ * bits on every run. */
 ts_status ts_conv_bwd_wgrad(const ts_kmap* map, const void* x, int cin, const void* dy, int cout,
                             ts_dtype in_dtype, float* dw, void* ws, size_t ws_bytes, hipStream_t stream);
 

@@ -28,3 +28,17 @@ def ts():
         pytest.skip("no GPU visible")
     from convolution_voxelised_point_amd import ts as _ts
     return _ts
+
+
+def pytest_terminal_summary(terminalreporter):
+    """Error distribution of every feature comparison the session made."""
+    helpers = sys.modules.get("helpers")
+    log = getattr(helpers, "PARITY_LOG", None)
+    if not log:
+        return
+    tr = terminalreporter
+    tr.section("feature parity: |GPU - fp64 oracle| per comparison")
+    tr.write_line(f"{'comparison':58s} {'elements':>10s} {'max|ref|':>10s} {'p50':>10s} {'p99':>10s} "
+                  f"{'max':>10s} {'max/max|ref|':>12s}  bar")
+    for what, n, m, p50, p99, mx, rel, bar in log:
+        tr.write_line(f"{what[:58]:58s} {n:10d} {m:10.3e} {p50:10.3e} {p99:10.3e} {mx:10.3e} {rel:12.3e}  {bar}")

@@ -23,6 +23,12 @@ def err_stats(got: np.ndarray, ref: np.ndarray) -> str:
             f"max={e.max():.3e} rel(max)={e.max() / max(m, 1e-300):.3e}")
 
 
+# Error statistics of every feature comparison made in this session (what,
+# elements, max|ref|, p50, p99, max of |err|, max|err| / max|ref|, the bar);
+# tests/conftest.py prints them at the end of the run.
+PARITY_LOG: list = []
+
+
 def assert_feature_close(got: torch.Tensor, ref: np.ndarray, in_dtype: torch.dtype, what: str = "") -> None:
     """Parity bar: max|err| <= 1e-5 max|ref| (fp32 inputs) or 2e-3 max|ref|
     (fp16/bf16 inputs, fp32 accumulation), with max over the whole tensor; a
@@ -33,9 +39,14 @@ def assert_feature_close(got: torch.Tensor, ref: np.ndarray, in_dtype: torch.dty
     if ref.size == 0:
         return
     m = float(np.abs(ref).max())
-    base = (1e-5 if in_dtype == torch.float32 else 2e-3) * m
+    rel = 1e-5 if in_dtype == torch.float32 else 2e-3
+    base = rel * m
     tol = base + U_OUT[got.dtype] * np.abs(ref) * (1 + 1e-6) + 1e-30
     err = np.abs(g - ref)
+    e = err.ravel()
+    PARITY_LOG.append((what, int(e.size), m, float(np.percentile(e, 50)), float(np.percentile(e, 99)),
+                       float(e.max()), float(e.max()) / max(m, 1e-300),
+                       f"{rel:g}*max|ref|" + (f" + {U_OUT[got.dtype]:g}*|ref|" if U_OUT[got.dtype] else "")))
     bad = err > tol
     assert not bad.any(), f"{what}: {int(bad.sum())} elements over tolerance; {err_stats(g, ref)}"
 

@@ -109,6 +109,12 @@ def test_kmap_build_rejects(ts):
     assert call(in_table=None) == ts.TS_ERR_INVALID_ARG
     assert call(in_cap=100) == ts.TS_ERR_INVALID_ARG
     assert call(flags=64) == ts.TS_ERR_INVALID_ARG
+    # int32 neighbour tables and pair positions: more than 2^31 - 1 (row,
+    # offset) slots, e.g. 80M rows at 27 offsets, is refused up front
+    big = 80_000_000
+    assert call(n_in=big, in_cap=1 << 25, flags=ts.TS_KMAP_PAIRS) == ts.TS_ERR_UNSUPPORTED
+    assert call(n_in=big, in_cap=1 << 25) == ts.TS_ERR_UNSUPPORTED
+    assert ts.ts_kmap_bytes(big, big, 3, 3, 1, ts.TS_KMAP_PAIRS) == 0
     # strided maps need the output count and coordinates
     sneed = ts.ts_kmap_bytes(100, 100, 3, 2, 2, ts.TS_KMAP_BWD)
     assert call(stride=2, ksize=2, n_out_cap=100, buf_bytes=sneed) == ts.TS_ERR_INVALID_ARG
