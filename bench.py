@@ -193,13 +193,27 @@ class Step:
 
 
 # ---------------------------------------------------------------- workloads
+def fod_shape_ok(w) -> bool:
+    """Channel counts and type the fetch-on-demand MFMA kernel takes:
+    fp16/bf16, a multiple of 32 input channels up to 128, a multiple of 16
+    output channels."""
+    return w.dtype in ("f16", "bf16") and w.cin % 32 == 0 and w.cin <= 128 and w.cout % 16 == 0
+
+
+def subm_flags(ts, w) -> int:
+    """A single-use submanifold map: pair groups only where the
+    fetch-on-demand kernel takes the layer, else a table in row order."""
+    return (ts.TS_KMAP_GROUPS | ts.TS_KMAP_NO_TABLE) if fod_shape_ok(w) else ts.TS_KMAP_NATURAL
+
+
 def setup_subm(ts, w, out_dtype=None, kmap_flags=None) -> Step:
-    """Hash + kernel map + SubmConv forward (implicit GEMM when the channel
-    counts allow it).  The map serves one contraction, so its tiles keep rows
-    in index order (TS_KMAP_NATURAL) unless `kmap_flags` says otherwise: the
-    window sort by offset mask shortens the contraction by less than it costs
-    when the map is used once."""
-    kmap_flags = ts.TS_KMAP_NATURAL if kmap_flags is None else kmap_flags
+    """Hash + kernel map + SubmConv forward.  By default the map holds only
+    pair groups (TS_KMAP_GROUPS | TS_KMAP_NO_TABLE) and the forward runs the
+    fetch-on-demand dataflow over them; `kmap_flags` with a neighbour table
+    (e.g. TS_KMAP_NATURAL: tiles in row order, or 0: the window sort by
+    offset mask) runs the implicit GEMM where the channel counts allow it."""
+    if kmap_flags is None:
+        kmap_flags = subm_flags(ts, w)
     dev = torch.device("cuda")
     coords = torch.from_numpy(w.coords).to(dev)
     x, wt = w.x.to(dev), w.w.to(dev)
@@ -510,20 +524,29 @@ def measure_lidar(ts, steps, warmup):
 
 
 def measure_lidar_shuffled(ts, steps, warmup):
-    """The ring scan with its rows in a seeded random order, with the map's
-    tiles in row order and sorted by offset mask."""
-    w = synth.shuffled(synth.make("lidar"))
-    out = {"workload": "lidar_shuffled", "n": w.n}
-    for order, flags in (("natural", ts.TS_KMAP_NATURAL), ("sorted", 0)):
-        s = setup_subm(ts, w, kmap_flags=flags)
-        _, st = run_steps(s.fns, s.names, steps, warmup)
-        ms, _ = run_graph(capture(s.fns), steps, warmup)
-        if order == "natural":
+    """The ring scan in its lexicographic row order and with its rows in a
+    seeded random order, each with three maps: pair groups only (the
+    fetch-on-demand forward, as in the headline step), and a neighbour table
+    with tiles in row order or sorted by offset mask (the implicit GEMM)."""
+    out = {"workload": "lidar_dataflows"}
+    variants = (("fetch_on_demand", ts.TS_KMAP_GROUPS | ts.TS_KMAP_NO_TABLE),
+                ("implicit_gemm_natural", ts.TS_KMAP_NATURAL), ("implicit_gemm_sorted", 0))
+    for scene in ("lex", "shuffled"):
+        w = synth.make("lidar")
+        if scene == "shuffled":
+            w = synth.shuffled(w)
+        rec = {"n": w.n}
+        for name, flags in variants:
+            s = setup_subm(ts, w, kmap_flags=flags)
+            _, st = run_steps(s.fns, s.names, steps, warmup)
+            ms, _ = run_graph(capture(s.fns), steps, warmup)
             P = popcount_sum(s.kmap.rel_arrays("fwd")["row_mask"][:s.n], 27)
-            out["pairs"] = P
-        out[order] = {"ms_per_step": ms, "stages_us": {k: round(v, 3) for k, v in st.items()},
-                      "tflops_step": 2.0 * P * w.cin * w.cout / (ms * 1e-3) / 1e12}
-        del s
+            rec["pairs"] = P
+            rec[name] = {"ms_per_step": ms, "stages_us": {k: round(v, 3) for k, v in st.items()},
+                         "tflops_step": 2.0 * P * w.cin * w.cout / (ms * 1e-3) / 1e12,
+                         "conv_back_to_back_us": back_to_back_us(s.fns[-1], steps)}
+            del s
+        out[scene] = rec
     return out
 
 

@@ -63,14 +63,27 @@ int64_t pair_capacity(int64_t n_in, int64_t n_out_cap, int ndim, int ksize, int 
   return ((flags & TS_KMAP_TARGET) || a < b) ? a : b;
 }
 
-void carve_rel(Carver& c, ts_rel* r, int64_t n_dest_cap, int kvol) {
+// One relation: the neighbour table and tile lists (`table`), the row
+// masks, and the pair groups (`groups`).
+void carve_rel(Carver& c, ts_rel* r, int64_t n_dest_cap, int kvol, bool table, bool groups) {
   r->n_dest_cap = n_dest_cap;
   r->n_tiles = ceil_div<int64_t>(n_dest_cap, kTile);
-  r->tile_mask = c.take<uint64_t>(static_cast<size_t>(r->n_tiles));
-  r->tile_rows = c.take<int32_t>(static_cast<size_t>(r->n_tiles) * kTile);
-  r->nbr = c.take<int32_t>(static_cast<size_t>(n_dest_cap) * kvol);
+  r->tile_mask = table ? c.take<uint64_t>(static_cast<size_t>(r->n_tiles)) : nullptr;
+  r->tile_rows = table ? c.take<int32_t>(static_cast<size_t>(r->n_tiles) * kTile) : nullptr;
+  r->nbr = table ? c.take<int32_t>(static_cast<size_t>(n_dest_cap) * kvol) : nullptr;
   r->row_mask = c.take<uint64_t>(static_cast<size_t>(n_dest_cap));
   r->n_dest = nullptr;
+  r->n_gtiles = groups ? ceil_div<int64_t>(n_dest_cap, TS_GTILE) : 0;
+  const size_t entries = static_cast<size_t>(r->n_gtiles) * kvol * TS_GTILE;
+  r->gcount = groups ? c.take<int32_t>(static_cast<size_t>(r->n_gtiles) * kvol) : nullptr;
+  r->gsrc = groups ? c.take<int32_t>(entries) : nullptr;
+  r->gslot = groups ? c.take<uint8_t>(entries) : nullptr;
+}
+
+// Probe mode of a map's forward relation (see ts_kmap_build).
+int fwd_mode(int stride, uint32_t flags) {
+  if (flags & TS_KMAP_TRANSPOSED) return kModeUp;
+  return (stride == 1 && !(flags & TS_KMAP_TARGET)) ? kModeSubm : kModeDown;
 }
 
 // Lays out a map; with base == NULL only the size is computed.
@@ -90,8 +103,11 @@ size_t layout_kmap(char* base, ts_kmap* m, int64_t n_in, int64_t n_out_cap, int 
   m->n_in = n_in;
   m->n_out_cap = n_out_cap;
   m->n_out = c.take<int64_t>(1);
-  carve_rel(c, &m->fwd, n_out_cap, m->kvol);
-  if (own_bwd && (flags & TS_KMAP_BWD)) carve_rel(c, &m->bwd, n_in, m->kvol);
+  const bool groups = (flags & TS_KMAP_GROUPS) != 0;
+  const bool fwd_table =
+      !(groups && (flags & TS_KMAP_NO_TABLE) && rel_probe_emits_groups(fwd_mode(stride, flags), ndim, ksize));
+  carve_rel(c, &m->fwd, n_out_cap, m->kvol, fwd_table, groups);
+  if (own_bwd && (flags & TS_KMAP_BWD)) carve_rel(c, &m->bwd, n_in, m->kvol, true, groups);
   size_t scratch = rel_scratch_bytes(n_out_cap, m->kvol);
   if (flags & TS_KMAP_PAIRS) {
     m->pair_cap = pair_capacity(n_in, n_out_cap, ndim, ksize, stride, flags);
@@ -111,7 +127,8 @@ size_t layout_kmap(char* base, ts_kmap* m, int64_t n_in, int64_t n_out_cap, int 
 }
 
 ts_status check_conv(const ts_kmap* map, int cin, int cout, ts_dtype in, ts_dtype out) {
-  if (!map || map->kvol < 1 || map->kvol > TS_MAX_KVOL || !map->fwd.tile_mask) return TS_ERR_INVALID_ARG;
+  if (!map || map->kvol < 1 || map->kvol > TS_MAX_KVOL || !map->fwd.row_mask) return TS_ERR_INVALID_ARG;
+  if (!map->fwd.tile_mask && !map->fwd.gcount) return TS_ERR_INVALID_ARG;
   if (cin < 1 || cout < 1 || cin > kMaxChannels || cout > kMaxChannels) return TS_ERR_INVALID_ARG;
   if (!dtype_ok(in) || !dtype_ok(out)) return TS_ERR_INVALID_ARG;
   if (out != TS_F32 && out != in) return TS_ERR_UNSUPPORTED;
@@ -125,9 +142,46 @@ bool use_igemm(ts_dataflow df, int kvol, int64_t n_src, int c_src, int c_dst, ts
 
 // Dataflow in range; the weights are needed unless they come packed.
 ts_status check_dataflow(ts_dataflow df, const void* w) {
-  if (df < TS_DATAFLOW_AUTO || df > TS_DATAFLOW_IMPLICIT_GEMM_PACKED) return TS_ERR_INVALID_ARG;
+  if (df < TS_DATAFLOW_AUTO || df > TS_DATAFLOW_FETCH_ON_DEMAND) return TS_ERR_INVALID_ARG;
   if (!w && df != TS_DATAFLOW_IMPLICIT_GEMM_PACKED) return TS_ERR_INVALID_ARG;
   return TS_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+// Which kernel runs a contraction over relation `rel` (the forward's, dgrad's
+// or the transposed convolution's): the fetch-on-demand dataflow when asked
+// for, or by default when the relation has pair groups and the shape has a
+// kernel; the implicit GEMM or the direct kernel over the neighbour table
+// otherwise.  Returns TS_OK and sets *kind, or the error to report.
+enum Kind { kFod, kIgemm, kDirect };
+ts_status pick_kernel(ts_dataflow df, const ts_rel& rel, int kvol, int64_t n_src, int c_src, int c_dst,
+                      ts_dtype in, const void* src, Kind* kind) {
+  const bool fod_ok = rel.gcount && aligned16(src) && fod_supported(kvol, n_src, c_src, c_dst, in);
+  if (df == TS_DATAFLOW_FETCH_ON_DEMAND) {
+    if (!rel.gcount) return TS_ERR_INVALID_ARG;  // the map has no pair groups
+    if (!fod_ok) return TS_ERR_UNSUPPORTED;
+    *kind = kFod;
+    return TS_OK;
+  }
+  if (df == TS_DATAFLOW_AUTO && fod_ok) {
+    *kind = kFod;
+    return TS_OK;
+  }
+  if (!rel.tile_mask) return TS_ERR_INVALID_ARG;  // the other kernels walk the neighbour table
+  const bool ig = (df == TS_DATAFLOW_AUTO || df == TS_DATAFLOW_IMPLICIT_GEMM || df == TS_DATAFLOW_IMPLICIT_GEMM_PACKED) &&
+                  igemm_supported(kvol, n_src, c_src, c_dst, in) && aligned16(src);
+  if (df == TS_DATAFLOW_IMPLICIT_GEMM_PACKED && !ig) return TS_ERR_UNSUPPORTED;
+  *kind = ig ? kIgemm : kDirect;
+  return TS_OK;
+}
+
+hipError_t run_kernel(Kind kind, const ConvArgs& a, void* ws, hipStream_t s) {
+  switch (kind) {
+    case kFod: return launch_fod(a, s);
+    case kIgemm: return launch_igemm(a, ws, s);
+    default: return launch_direct(a, s);
+  }
 }
 
 size_t conv_ws(const ts_kmap* map, int c_src, int c_dst, ts_dtype in, ts_dtype out, ts_dataflow df, int64_t n_dest,
@@ -286,8 +340,10 @@ ts_status ts_kmap_build(const int32_t* in_coords, int64_t n_in, const void* in_t
   }
   if (n_in < 0 || n_in > kMaxRows || (n_in > 0 && !in_coords) || !is_pow2(in_cap) || in_cap > kMaxCap)
     return TS_ERR_INVALID_ARG;
-  if (flags & ~(TS_KMAP_PAIRS | TS_KMAP_BWD | TS_KMAP_NATURAL | TS_KMAP_TARGET | TS_KMAP_TRANSPOSED))
+  if (flags & ~(TS_KMAP_PAIRS | TS_KMAP_BWD | TS_KMAP_NATURAL | TS_KMAP_TARGET | TS_KMAP_TRANSPOSED | TS_KMAP_GROUPS |
+                TS_KMAP_NO_TABLE))
     return TS_ERR_INVALID_ARG;
+  if ((flags & TS_KMAP_NO_TABLE) && !(flags & TS_KMAP_GROUPS)) return TS_ERR_INVALID_ARG;
   const int kvol = ipow(ksize, ndim);
   const bool target = (flags & TS_KMAP_TARGET) != 0;
   const bool transposed = (flags & TS_KMAP_TRANSPOSED) != 0;
@@ -427,15 +483,14 @@ ts_status ts_conv_fwd(const ts_kmap* map, const void* x, int cin, const void* w,
   a.in_dtype = in_dtype;
   a.out_dtype = out_dtype;
   a.prepacked = dataflow == TS_DATAFLOW_IMPLICIT_GEMM_PACKED;
-  if (a.prepacked && !use_igemm(dataflow, map->kvol, map->n_in, cin, cout, in_dtype)) return TS_ERR_UNSUPPORTED;
   if (dataflow == TS_DATAFLOW_GATHER_SCATTER) {
     if (!(map->flags & TS_KMAP_PAIRS)) return TS_ERR_INVALID_ARG;
     TS_TRY(launch_gather_scatter(map, a, false, map->n_out_cap, ws, stream));
-  } else if (use_igemm(dataflow, map->kvol, map->n_in, cin, cout, in_dtype)) {
-    TS_TRY(launch_igemm(a, ws, stream));
-  } else {
-    TS_TRY(launch_direct(a, stream));
+    return TS_OK;
   }
+  Kind kind;
+  if ((st = pick_kernel(dataflow, map->fwd, map->kvol, map->n_in, cin, cout, in_dtype, x, &kind)) != TS_OK) return st;
+  TS_TRY(run_kernel(kind, a, ws, stream));
   return TS_OK;
 }
 
@@ -541,7 +596,6 @@ ts_status ts_conv_bwd_dgrad(const ts_kmap* map, const void* dy, int cout, const 
   a.in_dtype = in_dtype;
   a.out_dtype = out_dtype;
   a.prepacked = dataflow == TS_DATAFLOW_IMPLICIT_GEMM_PACKED;
-  if (a.prepacked && !use_igemm(dataflow, map->kvol, map->n_out_cap, cout, cin, in_dtype)) return TS_ERR_UNSUPPORTED;
   if (dataflow == TS_DATAFLOW_GATHER_SCATTER) {
     if (!(map->flags & TS_KMAP_PAIRS)) return TS_ERR_INVALID_ARG;
     a.rel = &map->fwd;
@@ -553,15 +607,13 @@ ts_status ts_conv_bwd_dgrad(const ts_kmap* map, const void* dy, int cout, const 
     a.rel = &map->fwd;
     a.mirror = true;
   } else {
-    if (!(map->flags & TS_KMAP_BWD) || !map->bwd.tile_mask) return TS_ERR_INVALID_ARG;
+    if (!(map->flags & TS_KMAP_BWD) || !map->bwd.row_mask) return TS_ERR_INVALID_ARG;
     a.rel = &map->bwd;
     a.mirror = false;
   }
-  if (use_igemm(dataflow, map->kvol, map->n_out_cap, cout, cin, in_dtype)) {
-    TS_TRY(launch_igemm(a, ws, stream));
-  } else {
-    TS_TRY(launch_direct(a, stream));
-  }
+  Kind kind;
+  if ((st = pick_kernel(dataflow, *a.rel, map->kvol, map->n_out_cap, cout, cin, in_dtype, dy, &kind)) != TS_OK) return st;
+  TS_TRY(run_kernel(kind, a, ws, stream));
   return TS_OK;
 }
 
@@ -590,7 +642,6 @@ ts_status ts_conv_transpose_fwd(const ts_kmap* map, const void* x, int cin, cons
   a.in_dtype = in_dtype;
   a.out_dtype = out_dtype;
   a.prepacked = dataflow == TS_DATAFLOW_IMPLICIT_GEMM_PACKED;
-  if (a.prepacked && !use_igemm(dataflow, map->kvol, map->n_out_cap, cin, cout, in_dtype)) return TS_ERR_UNSUPPORTED;
   if (dataflow == TS_DATAFLOW_GATHER_SCATTER) {
     if (!(map->flags & TS_KMAP_PAIRS)) return TS_ERR_INVALID_ARG;
     a.rel = &map->fwd;
@@ -602,15 +653,13 @@ ts_status ts_conv_transpose_fwd(const ts_kmap* map, const void* x, int cin, cons
     a.rel = &map->fwd;
     a.mirror = true;
   } else {
-    if (!(map->flags & TS_KMAP_BWD) || !map->bwd.tile_mask) return TS_ERR_INVALID_ARG;
+    if (!(map->flags & TS_KMAP_BWD) || !map->bwd.row_mask) return TS_ERR_INVALID_ARG;
     a.rel = &map->bwd;
     a.mirror = false;
   }
-  if (use_igemm(dataflow, map->kvol, map->n_out_cap, cin, cout, in_dtype)) {
-    TS_TRY(launch_igemm(a, ws, stream));
-  } else {
-    TS_TRY(launch_direct(a, stream));
-  }
+  Kind kind;
+  if ((st = pick_kernel(dataflow, *a.rel, map->kvol, map->n_out_cap, cin, cout, in_dtype, x, &kind)) != TS_OK) return st;
+  TS_TRY(run_kernel(kind, a, ws, stream));
   return TS_OK;
 }
 

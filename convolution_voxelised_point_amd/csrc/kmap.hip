@@ -43,6 +43,10 @@ struct RelK {
   int32_t* tile_rows;
   int32_t* nbr;
   uint64_t* row_mask;
+  int64_t n_gtiles;  // pair-group tiles (0: no groups)
+  int32_t* gcount;
+  int32_t* gsrc;
+  uint8_t* gslot;
 };
 
 __device__ __forceinline__ int64_t dest_count(const int64_t* n_dest, int64_t cap) {
@@ -296,10 +300,64 @@ __device__ __forceinline__ void load_offsets(const RelK& a, int8_t* offs) {
   __syncthreads();
 }
 
+// Pair groups of the two group tiles (TS_GTILE = 128 rows) of a workgroup of
+// 256 destination rows, one lane per row (thread i = slot i % 128 of tile
+// 2 * blockIdx.x + i / 128).  `nb(o)` is the lane's source row at offset o,
+// read only where bit o of `mask` is set.  Per offset, each wavefront counts
+// its rows by a ballot; the first wavefront of each tile turns the counts into
+// the offsets' padded runs (an exclusive scan over offsets of whole groups of
+// 16) and the tile's counts; every lane then writes its pairs at its run's
+// start plus its rank among the tile's rows with that offset, so each run
+// lists destination rows in order.  Every thread must call this (barriers).
+template <int KVMAX, typename NB>
+__device__ __forceinline__ void emit_groups(const RelK& a, int kvol, uint64_t mask, NB nb) {
+  __shared__ int gw[4][KVMAX];      // pairs per wavefront and offset
+  __shared__ int gstart[2][KVMAX];  // first entry of each offset's run, per tile
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const uint64_t lt = (1ull << lane) - 1;
+#pragma unroll
+  for (int o = 0; o < KVMAX; ++o) {
+    if (o >= kvol) break;
+    const uint64_t b = __ballot((mask >> o) & 1);
+    if (lane == 0) gw[wave][o] = __popcll(b);
+  }
+  __syncthreads();
+  const int h = threadIdx.x >> 7;
+  const int64_t gt = static_cast<int64_t>(blockIdx.x) * 2 + h;
+  if ((wave & 1) == 0) {  // wave-uniform: the first wavefront of each tile
+    const int c = lane < kvol ? gw[wave][lane] + gw[wave + 1][lane] : 0;
+    const int n16 = (c + 15) & ~15;
+    int incl = n16;
+#pragma unroll
+    for (int sh = 1; sh < 64; sh <<= 1) {
+      const int y = __shfl_up(incl, sh, 64);
+      incl += lane >= sh ? y : 0;
+    }
+    if (lane < kvol) {
+      gstart[h][lane] = incl - n16;
+      if (gt < a.n_gtiles) a.gcount[gt * kvol + lane] = c;
+    }
+  }
+  __syncthreads();
+  if (gt >= a.n_gtiles) return;
+  const int64_t ebase = gt * kvol * TS_GTILE;
+  const uint8_t slot = static_cast<uint8_t>(threadIdx.x & 127);
+#pragma unroll
+  for (int o = 0; o < KVMAX; ++o) {
+    if (o >= kvol) break;
+    const bool has = (mask >> o) & 1;
+    const uint64_t b = __ballot(has);
+    if (!has) continue;
+    const int pos = gstart[h][o] + ((wave & 1) ? gw[wave - 1][o] : 0) + __popcll(b & lt);
+    a.gsrc[ebase + pos] = nb(o);
+    a.gslot[ebase + pos] = slot;
+  }
+}
+
 // Pass 1: one lane per destination row in index order.  Writes the row's
-// neighbours and mask; with `natural` it also writes the tiles (rows stay in
-// index order).
-template <int MODE, int ND, int K>
+// mask and, with TB, its neighbours (and with `natural` the tiles: rows
+// stay in index order); with GR the pair groups.
+template <int MODE, int ND, int K, bool TB, bool GR>
 __global__ __launch_bounds__(256) void k_rel_probe(RelK a, int natural, int64_t* n_out_fill) {
   constexpr int KV = Geo<ND, K>::KV;
   // The workgroup's 256 rows own one contiguous span of the neighbour table:
@@ -324,6 +382,13 @@ __global__ __launch_bounds__(256) void k_rel_probe(RelK a, int natural, int64_t*
   // a submanifold output takes part only when it owns its coordinate
   if (MODE == kModeSubm && nb[(KV - 1) / 2] != static_cast<int32_t>(row)) mask = 0;
   if (live && row < a.n_dest_cap) a.row_mask[row] = mask;
+  if constexpr (GR) emit_groups<KV>(a, KV, mask, [&](int o) {
+      int32_t v = nb[0];
+#pragma unroll
+      for (int j = 1; j < KV; ++j) v = o == j ? nb[j] : v;
+      return v;
+    });
+  if constexpr (!TB) return;
 #pragma unroll
   for (int o = 0; o < KV; ++o) staged[threadIdx.x * KV + o] = ((mask >> o) & 1) ? nb[o] : -1;
   if (natural) {
@@ -386,6 +451,17 @@ __global__ __launch_bounds__(256) void k_rel_probe_any(RelK a, int natural) {
   const int words = static_cast<int>(rows) * a.kvol;
   int32_t* dst = a.nbr + row0 * a.kvol;
   for (int k = threadIdx.x; k < words; k += 256) dst[k] = nbr_lds[k];
+}
+
+// Pair groups of a relation that has its neighbour table (relations the
+// runtime-kvol probe builds): one lane per destination row, 256 rows (two
+// group tiles) per workgroup.
+__global__ __launch_bounds__(256) void k_groups_from_table(RelK a) {
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t n_dest = dest_count(a.n_dest, a.n_dest_cap);
+  const uint64_t mask = row < n_dest ? a.row_mask[row] : 0ull;
+  const int32_t* nr = a.nbr + (row < n_dest ? row : 0) * a.kvol;
+  emit_groups<TS_MAX_KVOL>(a, a.kvol, mask, [&](int o) { return nr[o]; });
 }
 
 // Pass 2: stable sort of each window's rows by offset mask: an LSD radix
@@ -556,6 +632,69 @@ __global__ __launch_bounds__(256) void k_pairs_fill(RelK a, int64_t nblk, const 
   }
 }
 
+// k_pairs_fill for a relation without its neighbour table: the source row
+// of a (row, offset) pair is read from the pair groups -- entry
+// (offset's run start) + (the row's rank among its tile's rows with the
+// offset), the rank from the same ballots that place the pair.
+__global__ __launch_bounds__(256) void k_pairs_fill_groups(RelK a, int64_t nblk, const int32_t* __restrict__ base,
+                                                           const int64_t* total, int64_t pair_cap,
+                                                           int64_t* __restrict__ pair_start,
+                                                           int32_t* __restrict__ pair_in,
+                                                           int32_t* __restrict__ pair_out) {
+  __shared__ int wave_pos[4][TS_MAX_KVOL];
+  __shared__ int wave_cnt[4][TS_MAX_KVOL];
+  __shared__ int run0[2][TS_MAX_KVOL];
+  const int64_t n_dest = dest_count(a.n_dest, a.n_dest_cap);
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const uint64_t mask = row < n_dest ? a.row_mask[row] : 0;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const uint64_t below = (1ull << lane) - 1;
+  const int h = threadIdx.x >> 7;
+  const int64_t gt = static_cast<int64_t>(blockIdx.x) * 2 + h;
+  if (blockIdx.x == 0 && threadIdx.x <= a.kvol) {  // clamped: lists never run past their capacity
+    const int64_t v = threadIdx.x < a.kvol ? base[threadIdx.x * nblk] : *total;
+    pair_start[threadIdx.x] = v < pair_cap ? v : pair_cap;
+  }
+  for (int o = 0; o < a.kvol; ++o) {
+    const uint64_t bal = __ballot((mask >> o) & 1);
+    if (lane == 0) wave_cnt[wave][o] = __popcll(bal);
+  }
+  if ((wave & 1) == 0) {  // the tile's run starts, from its group counts
+    const int c = lane < a.kvol && gt < a.n_gtiles ? a.gcount[gt * a.kvol + lane] : 0;
+    const int n16 = (c + 15) & ~15;
+    int incl = n16;
+#pragma unroll
+    for (int sh = 1; sh < 64; sh <<= 1) {
+      const int y = __shfl_up(incl, sh, 64);
+      incl += lane >= sh ? y : 0;
+    }
+    if (lane < a.kvol) run0[h][lane] = incl - n16;
+  }
+  __syncthreads();
+  if (threadIdx.x < a.kvol) {  // counts -> exclusive positions, per offset
+    const int o = threadIdx.x;
+    int p = base[o * nblk + blockIdx.x];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      wave_pos[w][o] = p;
+      p += wave_cnt[w][o];
+    }
+  }
+  __syncthreads();
+  const int64_t ebase = gt * a.kvol * TS_GTILE;
+  for (int o = 0; o < a.kvol; ++o) {
+    const bool has = (mask >> o) & 1;
+    const uint64_t bal = __ballot(has);  // every lane takes part
+    if (!has) continue;
+    const int rank = __popcll(bal & below);
+    const int pos = wave_pos[wave][o] + rank;
+    if (pos >= pair_cap) continue;
+    const int in_tile = run0[h][o] + ((wave & 1) ? wave_cnt[wave - 1][o] : 0) + rank;
+    pair_out[pos] = static_cast<int32_t>(row);
+    pair_in[pos] = a.gsrc[ebase + in_tile];
+  }
+}
+
 RelK make_relk(const RelBuild& bld, const ts_rel& rel) {
   RelK a;
   a.dc = bld.dest_coords;
@@ -576,6 +715,10 @@ RelK make_relk(const RelBuild& bld, const ts_rel& rel) {
   a.tile_rows = rel.tile_rows;
   a.nbr = rel.nbr;
   a.row_mask = rel.row_mask;
+  a.n_gtiles = rel.n_gtiles;
+  a.gcount = rel.gcount;
+  a.gsrc = rel.gsrc;
+  a.gslot = rel.gslot;
   return a;
 }
 
@@ -592,10 +735,19 @@ void launch_sort(const RelK& a, hipStream_t s) {
                                                          a.tile_rows, a.tile_mask);
 }
 
+// With a neighbour table (TB) the tiles are written in index order or
+// sorted; the pair groups come from the probe itself (GR).
 template <int MODE, int ND, int K>
 void launch_rel_geo(const RelK& a, bool natural, unsigned grid, int64_t* n_out_fill, hipStream_t s) {
-  k_rel_probe<MODE, ND, K><<<grid, 256, 0, s>>>(a, natural ? 1 : 0, n_out_fill);
-  if (!natural) launch_sort(a, s);
+  const bool tb = a.nbr != nullptr, gr = a.n_gtiles > 0;
+  const int nat = natural ? 1 : 0;
+  if (tb && gr)
+    k_rel_probe<MODE, ND, K, true, true><<<grid, 256, 0, s>>>(a, nat, n_out_fill);
+  else if (tb)
+    k_rel_probe<MODE, ND, K, true, false><<<grid, 256, 0, s>>>(a, nat, n_out_fill);
+  else
+    k_rel_probe<MODE, ND, K, false, true><<<grid, 256, 0, s>>>(a, nat, n_out_fill);
+  if (tb && !natural) launch_sort(a, s);
 }
 
 template <int MODE>
@@ -604,6 +756,12 @@ void launch_rel_any(const RelK& a, bool natural, unsigned grid, int64_t* n_out_f
   if (n_out_fill) (void)fill_i64(n_out_fill, 1, a.n_dest_cap, s);
   k_rel_probe_any<MODE><<<grid, 256, lds, s>>>(a, natural ? 1 : 0);
   if (!natural) launch_sort(a, s);
+  if (a.n_gtiles > 0) k_groups_from_table<<<grid, 256, 0, s>>>(a);
+}
+
+template <int ND, int K>
+constexpr bool geo_instanced() {
+  return (ND == 3 && (K == 1 || K == 2 || K == 3)) || (ND == 2 && (K == 2 || K == 3 || K == 5));
 }
 
 template <int MODE>
@@ -620,6 +778,11 @@ void launch_rel_mode(const RelK& a, int ksize, bool natural, unsigned grid, int6
 }  // namespace
 
 size_t rel_scratch_bytes(int64_t, int) { return 0; }
+
+bool rel_probe_emits_groups(int mode, int ndim, int ksize) {
+  if (mode != kModeSubm && mode != kModeDown) return false;
+  return (ndim == 3 && ksize >= 1 && ksize <= 3) || (ndim == 2 && (ksize == 2 || ksize == 3 || ksize == 5));
+}
 
 hipError_t launch_rel_build(const RelBuild& bld, const ts_rel& rel, bool natural, int64_t* n_out_fill,
                             hipStream_t s) {
@@ -652,8 +815,12 @@ hipError_t launch_pairs_build(const RelBuild& bld, const ts_rel& rel, int64_t pa
   hipError_t e = scan_exclusive_i32(cnt, cnt, n, pair_start + bld.kvol, tmp, s);
   if (e != hipSuccess) return e;
   RelK a = make_relk(bld, rel);
-  k_pairs_fill<<<static_cast<unsigned>(nblk), 256, 0, s>>>(a, nblk, cnt, pair_start + bld.kvol, pair_cap, pair_start,
-                                                             pair_in, pair_out);
+  if (rel.nbr)
+    k_pairs_fill<<<static_cast<unsigned>(nblk), 256, 0, s>>>(a, nblk, cnt, pair_start + bld.kvol, pair_cap,
+                                                               pair_start, pair_in, pair_out);
+  else
+    k_pairs_fill_groups<<<static_cast<unsigned>(nblk), 256, 0, s>>>(a, nblk, cnt, pair_start + bld.kvol, pair_cap,
+                                                                      pair_start, pair_in, pair_out);
   return hipGetLastError();
 }
 

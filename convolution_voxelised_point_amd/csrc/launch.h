@@ -63,6 +63,9 @@ struct RelBuild {
 };
 
 size_t rel_scratch_bytes(int64_t n_dest_cap, int kvol);
+// True when the probe of this relation writes its pair groups itself (so the
+// relation needs no neighbour table for them).
+bool rel_probe_emits_groups(int mode, int ndim, int ksize);
 // n_out_fill (device, may be NULL): receives n_dest_cap (the submanifold output count)
 hipError_t launch_rel_build(const RelBuild& b, const ts_rel& rel, bool natural, int64_t* n_out_fill, hipStream_t s);
 size_t pairs_scratch_bytes(int64_t n_dest_cap, int kvol);
@@ -99,6 +102,10 @@ hipError_t launch_graph_conv(const int64_t* indptr, const int32_t* src, const in
                              ts_dtype in, ts_dtype out, uint32_t* flags, hipStream_t s);
 hipError_t launch_pool(const ts_rel& rel, int kvol, const void* x, int c, void* y, ts_dtype in, ts_dtype out, int mode,
                        hipStream_t s);
+
+// fod.hip: the fetch-on-demand dataflow over a relation's pair groups
+bool fod_supported(int kvol, int64_t n_src, int c_src, int c_dst, ts_dtype in_dtype);
+hipError_t launch_fod(const ConvArgs& a, hipStream_t s);
 
 size_t gs_workspace_bytes(int64_t n_dest_cap, int c_dst, ts_dtype out_dtype);
 hipError_t launch_gather_scatter(const ts_kmap* map, const ConvArgs& a, bool backward, int64_t n_dest_cap,

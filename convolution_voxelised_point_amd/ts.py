@@ -28,11 +28,13 @@ _lib = ctypes.CDLL(LIB_PATH)
 TS_OK, TS_ERR_INVALID_ARG, TS_ERR_UNSUPPORTED, TS_ERR_HIP = 0, 1, 2, 3
 TS_F32, TS_F16, TS_BF16 = 0, 1, 2
 TS_DATAFLOW_AUTO, TS_DATAFLOW_IMPLICIT_GEMM, TS_DATAFLOW_GATHER_SCATTER, TS_DATAFLOW_IMPLICIT_GEMM_PACKED = 0, 1, 2, 3
+TS_DATAFLOW_FETCH_ON_DEMAND = 4
 TS_FLAG_DUP, TS_FLAG_RANGE, TS_FLAG_FULL = 1, 2, 4
 TS_KMAP_PAIRS, TS_KMAP_BWD, TS_KMAP_NATURAL, TS_KMAP_TARGET, TS_KMAP_TRANSPOSED = 1, 2, 4, 8, 16
+TS_KMAP_GROUPS, TS_KMAP_NO_TABLE = 32, 64
 TS_OP_FWD, TS_OP_DGRAD, TS_OP_WGRAD, TS_OP_TRANSPOSE = 0, 1, 2, 3
 TS_POOL_MAX, TS_POOL_AVG = 0, 1
-TS_TILE, TS_MAX_KVOL = 16, 64
+TS_TILE, TS_GTILE, TS_MAX_KVOL = 16, 128, 64
 
 _DT = {torch.float32: TS_F32, torch.float16: TS_F16, torch.bfloat16: TS_BF16}
 
@@ -41,7 +43,8 @@ _vp, _i64, _i32, _u32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctyp
 
 class TsRel(ctypes.Structure):
     _fields_ = [("n_dest_cap", _i64), ("n_tiles", _i64), ("n_dest", _vp), ("tile_mask", _vp),
-                ("tile_rows", _vp), ("nbr", _vp), ("row_mask", _vp)]
+                ("tile_rows", _vp), ("nbr", _vp), ("row_mask", _vp), ("n_gtiles", _i64), ("gcount", _vp),
+                ("gsrc", _vp), ("gslot", _vp)]
 
 
 class TsKmap(ctypes.Structure):
@@ -358,14 +361,19 @@ class Kmap:
         return self.buf[off:off + count * itemsize].view(dtype)
 
     def rel_arrays(self, which: str = "fwd") -> dict:
+        """Device views of a relation's arrays (those the map holds)."""
         r = getattr(self.s, which)
-        nt, kv = r.n_tiles, self.s.kvol
-        return {
-            "tile_mask": self._view(r.tile_mask, torch.int64, nt),
-            "tile_rows": self._view(r.tile_rows, torch.int32, nt * TS_TILE),
-            "nbr": self._view(r.nbr, torch.int32, r.n_dest_cap * kv),
-            "row_mask": self._view(r.row_mask, torch.int64, r.n_dest_cap),
-        }
+        nt, kv, ng = r.n_tiles, self.s.kvol, r.n_gtiles
+        out = {"row_mask": self._view(r.row_mask, torch.int64, r.n_dest_cap)}
+        if r.nbr:
+            out["tile_mask"] = self._view(r.tile_mask, torch.int64, nt)
+            out["tile_rows"] = self._view(r.tile_rows, torch.int32, nt * TS_TILE)
+            out["nbr"] = self._view(r.nbr, torch.int32, r.n_dest_cap * kv)
+        if ng:
+            out["gcount"] = self._view(r.gcount, torch.int32, ng * kv)
+            out["gsrc"] = self._view(r.gsrc, torch.int32, ng * kv * TS_GTILE)
+            out["gslot"] = self._view(r.gslot, torch.uint8, ng * kv * TS_GTILE)
+        return out
 
     def pairs(self):
         """(pair_start[kvol+1], pair_in[P], pair_out[P]) on the host."""
@@ -390,6 +398,30 @@ def decode_rel(arrs: dict, kvol: int, transposed: bool = False) -> Tuple[np.ndar
     a = sub[d, o].astype(np.int32)
     b = rows[d].astype(np.int32)
     c = o.astype(np.int32)
+    return (b, a, c) if transposed else (a, b, c)
+
+
+def decode_groups(arrs: dict, kvol: int, transposed: bool = False) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Host decode of a relation's pair groups into (in, out, offset)
+    triples (tile t, offset o: entries from 16 * sum of earlier offsets'
+    whole groups, gcount of them).  Used by tests."""
+    cnt = arrs["gcount"].cpu().numpy().reshape(-1, kvol).astype(np.int64)
+    nt = cnt.shape[0]
+    src = arrs["gsrc"].cpu().numpy().reshape(nt, kvol * TS_GTILE)
+    slot = arrs["gslot"].cpu().numpy().reshape(nt, kvol * TS_GTILE).astype(np.int64)
+    start = np.zeros_like(cnt)
+    start[:, 1:] = np.cumsum((cnt[:, :-1] + 15) // 16 * 16, axis=1)
+    t_idx, o_idx = np.nonzero(cnt > 0)
+    a, b, c = [], [], []
+    for t, o in zip(t_idx, o_idx):
+        e0, n = start[t, o], cnt[t, o]
+        a.append(src[t, e0:e0 + n])
+        b.append(t * TS_GTILE + slot[t, e0:e0 + n])
+        c.append(np.full(n, o, np.int64))
+    if not a:
+        z = np.zeros(0, np.int32)
+        return z, z, z
+    a, b, c = (np.concatenate(v).astype(np.int32) for v in (a, b, c))
     return (b, a, c) if transposed else (a, b, c)
 
 

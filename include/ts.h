@@ -67,8 +67,11 @@ typedef enum ts_dataflow {
   TS_DATAFLOW_AUTO = 0,          /* per-shape choice                                   */
   TS_DATAFLOW_IMPLICIT_GEMM = 1, /* output-stationary tiles, MFMA for fp16/bf16        */
   TS_DATAFLOW_GATHER_SCATTER = 2, /* per offset: gather, multiply, add into the outputs */
-  TS_DATAFLOW_IMPLICIT_GEMM_PACKED = 3 /* implicit GEMM on weights that ts_conv_pack_weights
-                                          already wrote into the workspace (w is ignored)  */
+  TS_DATAFLOW_IMPLICIT_GEMM_PACKED = 3, /* implicit GEMM on weights that ts_conv_pack_weights
+                                           already wrote into the workspace (w is ignored)  */
+  TS_DATAFLOW_FETCH_ON_DEMAND = 4 /* per-tile pair groups: each group of 16 pairs of one offset
+                                     fetches its source rows inside the MFMA loop and adds into
+                                     an on-chip accumulator tile (maps built with TS_KMAP_GROUPS) */
 } ts_dataflow;
 
 /* device-detected conditions, ORed into the caller's flag word */
@@ -82,9 +85,13 @@ typedef enum ts_dataflow {
 #define TS_KMAP_NATURAL 4u /* keep destination rows in index order inside tiles    */
 #define TS_KMAP_TARGET 8u  /* outputs are caller-given coordinates (TargetConv3d)  */
 #define TS_KMAP_TRANSPOSED 16u /* fine outputs of a transposed convolution      */
+#define TS_KMAP_GROUPS 32u   /* also build per-tile pair groups (fetch on demand)   */
+#define TS_KMAP_NO_TABLE 64u /* with TS_KMAP_GROUPS: no neighbour table or tile
+                                lists for the forward relation (see ts_kmap_build) */
 
-#define TS_TILE 16     /* destination rows per tile */
-#define TS_MAX_KVOL 64 /* largest supported K^D     */
+#define TS_TILE 16     /* destination rows per tile                  */
+#define TS_GTILE 128   /* destination rows per pair-group tile        */
+#define TS_MAX_KVOL 64 /* largest supported K^D                       */
 
 /* Human-readable name of a status code (static string). */
 const char* ts_status_string(ts_status s);
@@ -241,15 +248,29 @@ ts_status ts_devoxelize(const int32_t* vox_of, int64_t n, const void* vox_feats,
  * Which destination rows share a tile is a performance choice (rows with
  * similar masks are grouped unless TS_KMAP_NATURAL is set); the relation
  * itself -- the set of (in, out, offset) triples -- is fixed.
+ *
+ * Pair groups (TS_KMAP_GROUPS; the layout the fetch-on-demand dataflow
+ * reads): destination rows are cut into group tiles of TS_GTILE consecutive
+ * rows; tile t owns kvol * TS_GTILE entries of gsrc / gslot starting at
+ * t * kvol * TS_GTILE.  gcount[t*kvol + o] is the number of pairs of tile t
+ * at offset o.  Inside the tile, offset o's pairs are listed in destination
+ * order (gslot = destination row - t * TS_GTILE, gsrc = its source row),
+ * starting at entry 16 * sum_{o' < o} ceil(gcount[t*kvol + o'] / 16): each
+ * offset's run is padded to whole groups of 16 (padding entries are not
+ * written), so group g of the tile is entries [16g, 16g + 16).
  * ---------------------------------------------------------------------- */
 typedef struct ts_rel {
   int64_t n_dest_cap;    /* destination rows, upper bound (host)               */
   int64_t n_tiles;       /* ceil(n_dest_cap / TS_TILE)                         */
   const int64_t* n_dest; /* device int64: destination row count                */
-  uint64_t* tile_mask;   /* device [n_tiles]                                   */
-  int32_t* tile_rows;    /* device [n_tiles * TS_TILE]                         */
-  int32_t* nbr;          /* device [n_dest_cap * kvol]                         */
+  uint64_t* tile_mask;   /* device [n_tiles] (NULL without the table)          */
+  int32_t* tile_rows;    /* device [n_tiles * TS_TILE] (NULL without the table) */
+  int32_t* nbr;          /* device [n_dest_cap * kvol] (NULL without the table) */
   uint64_t* row_mask;    /* device [n_dest_cap]                                */
+  int64_t n_gtiles;      /* ceil(n_dest_cap / TS_GTILE), 0 without groups       */
+  int32_t* gcount;       /* device [n_gtiles * kvol]                           */
+  int32_t* gsrc;         /* device [n_gtiles * kvol * TS_GTILE]                */
+  uint8_t* gslot;        /* device [n_gtiles * kvol * TS_GTILE]                */
 } ts_rel;
 
 typedef struct ts_kmap {
@@ -300,7 +321,17 @@ size_t ts_kmap_bytes(int64_t n_in, int64_t n_out_cap, int ndim, int ksize, int s
  *     where that divides exactly -- the strided relation read the other way.
  *     With TS_KMAP_BWD the transposed relation (coarse rows to fine rows, the
  *     strided relation itself) is built too, for dgrad.
- * in_table / in_cap is the ts_hash_build table of the inputs. */
+ * in_table / in_cap is the ts_hash_build table of the inputs.
+ *   TS_KMAP_GROUPS builds the pair groups of every relation the map holds
+ *     (the forward one, and the transposed one with TS_KMAP_BWD);
+ *     TS_KMAP_NO_TABLE then leaves out the forward relation's neighbour
+ *     table, tile lists and tile masks (NULL in map->fwd) where its probe
+ *     emits the groups directly -- submanifold and strided maps of kernel
+ *     size 1, 2 or 3 in 3-D and 2, 3 or 5 in 2-D; other shapes keep the table.
+ *     A map without the table serves the fetch-on-demand and gather-scatter
+ *     dataflows and wgrad; the other dataflows and pooling need the table
+ *     and return TS_ERR_INVALID_ARG on it.  TS_KMAP_NO_TABLE without
+ *     TS_KMAP_GROUPS is TS_ERR_INVALID_ARG. */
 ts_status ts_kmap_build(const int32_t* in_coords, int64_t n_in, const void* in_table, int64_t in_cap,
                         const int32_t* out_coords, int64_t n_out_cap, const int64_t* n_out,
                         const void* out_table, int64_t out_cap, int ndim, int ksize, int stride,

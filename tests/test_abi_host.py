@@ -132,6 +132,7 @@ def test_conv_rejects(ts):
     km.stride = 1
     km.n_in = km.n_out_cap = 100
     km.fwd.tile_mask = 0x2000
+    km.fwd.row_mask = 0x3000
     km.fwd.n_tiles = 7
     assert ts._lib_conv_fwd(ref, FAKE, 0, FAKE, 16, FAKE, 1, 1, 0, None, 0, None) == ts.TS_ERR_INVALID_ARG   # cin 0
     assert ts._lib_conv_fwd(ref, FAKE, 16, FAKE, 16, FAKE, 7, 1, 0, None, 0, None) == ts.TS_ERR_INVALID_ARG  # dtype
@@ -141,6 +142,19 @@ def test_conv_rejects(ts):
     assert ts._lib_conv_fwd(ref, FAKE, 64, FAKE, 64, FAKE, 1, 1, 2, FAKE, 1 << 30, None) == ts.TS_ERR_INVALID_ARG  # GS w/o pairs
     assert ts._lib_conv_fwd(ref, FAKE, 16, None, 16, FAKE, 1, 1, 0, None, 0, None) == ts.TS_ERR_INVALID_ARG  # null w
     assert ts._lib_conv_fwd(ref, FAKE, 16, FAKE, 16, FAKE, 1, 1, 9, None, 0, None) == ts.TS_ERR_INVALID_ARG  # dataflow
+    # fetch on demand needs the pair groups; a map without groups or table is no map
+    FOD = ts.TS_DATAFLOW_FETCH_ON_DEMAND
+    assert ts._lib_conv_fwd(ref, FAKE, 64, FAKE, 64, FAKE, 1, 1, FOD, None, 0, None) == ts.TS_ERR_INVALID_ARG
+    km.fwd.tile_mask = None
+    assert ts._lib_conv_fwd(ref, FAKE, 64, FAKE, 64, FAKE, 1, 1, 0, None, 0, None) == ts.TS_ERR_INVALID_ARG
+    km.fwd.gcount = 0x4000
+    km.fwd.n_gtiles = 1
+    assert ts._lib_conv_fwd(ref, FAKE, 64, FAKE, 64, FAKE, 0, 0, FOD, None, 0, None) == ts.TS_ERR_UNSUPPORTED  # fp32
+    assert ts._lib_conv_fwd(ref, FAKE, 64, FAKE, 64, FAKE, 1, 1, 1, None, 0, None) == ts.TS_ERR_INVALID_ARG  # igemm, no table
+    assert ts._lib_pool_fwd(ref, FAKE, 16, FAKE, 1, 1, 0, None) == ts.TS_ERR_INVALID_ARG  # pooling needs the table
+    km.fwd.tile_mask = 0x2000
+    km.fwd.gcount = None
+    km.fwd.n_gtiles = 0
     # wgrad needs the pair lists
     assert ts._lib_conv_bwd_wgrad(ref, FAKE, 16, FAKE, 16, 1, FAKE, FAKE, 1 << 30, None) == ts.TS_ERR_INVALID_ARG
     # dgrad of a strided map needs the transposed relation
@@ -162,6 +176,7 @@ def test_pack_weights_rejects(ts):
     km.mirror_bwd = 1
     km.n_in = km.n_out_cap = 100
     km.fwd.tile_mask = 0x2000
+    km.fwd.row_mask = 0x3000
     need = ts._lib_conv_workspace_bytes(ref, 64, 64, ts.TS_OP_FWD, ts.TS_F16, ts.TS_DATAFLOW_IMPLICIT_GEMM)
     assert need == 27 * 64 * 64 * 2
     assert P(ref, None, 64, 64, ts.TS_OP_FWD, ts.TS_F16, FAKE, need, None) == ts.TS_ERR_INVALID_ARG       # null w

@@ -1,0 +1,264 @@
+"""Pair-group kernel maps and the fetch-on-demand dataflow on the GPU.
+
+The groups are checked bit-exactly against the oracle's triples (decoded
+tile by tile) and for their layout: each offset's run in destination order,
+padded to whole groups of 16.  The contraction over them is checked against
+the fp64 oracle (forward, dgrad, transposed convolution; fp32 and
+low-precision outputs), against the implicit GEMM and gather-scatter
+dataflows within the feature tolerance, and for bitwise repeatability."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from convolution_voxelised_point_amd import synth
+from helpers import assert_feature_close, canon, dev
+
+pytestmark = pytest.mark.gpu
+
+DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+def build(ts, coords, ksize, stride, flags, target=None):
+    cd = dev(coords)
+    tab = ts.HashTable(cd, 2.0)
+    if target is not None:
+        tc = dev(target)
+        n_out = torch.tensor([target.shape[0]], dtype=torch.int64, device="cuda")
+        ttab = ts.HashTable(tc, 2.0)
+        km = ts.build_kmap(cd, tab, ksize, stride, flags | ts.TS_KMAP_TARGET, out_coords=tc, n_out=n_out,
+                           out_table=ttab)
+        return km, target
+    if stride == 1:
+        return ts.build_kmap(cd, tab, ksize, 1, flags), coords
+    out, n_out, otab = ts.strided_support(cd, stride)
+    km = ts.build_kmap(cd, tab, ksize, stride, flags | ts.TS_KMAP_BWD, out_coords=out, n_out=n_out, out_table=otab)
+    return km, oracle.strided_support(coords, stride)
+
+
+def check_group_layout(arrs, kvol, n_dest):
+    """Runs in destination order, padded starts, counts summing to the rows'
+    mask bits."""
+    from convolution_voxelised_point_amd import ts
+    cnt = arrs["gcount"].cpu().numpy().reshape(-1, kvol).astype(np.int64)
+    slot = arrs["gslot"].cpu().numpy().reshape(cnt.shape[0], -1).astype(np.int64)
+    assert (cnt >= 0).all() and (cnt <= ts.TS_GTILE).all()
+    start = np.zeros_like(cnt)
+    start[:, 1:] = np.cumsum((cnt[:, :-1] + 15) // 16 * 16, axis=1)
+    assert (start[:, -1] + (cnt[:, -1] + 15) // 16 * 16 <= kvol * ts.TS_GTILE).all()
+    for t, o in zip(*np.nonzero(cnt > 0)):
+        s = slot[t, start[t, o]:start[t, o] + cnt[t, o]]
+        assert (np.diff(s) > 0).all(), "a run is not in destination order"
+        assert (t * ts.TS_GTILE + s < n_dest).all()
+    rm = arrs["row_mask"].cpu().numpy().view(np.uint64)[:n_dest]
+    bits = np.array([bin(int(m)).count("1") for m in rm], np.int64)
+    assert bits.sum() == cnt.sum()
+
+
+MAPS = [
+    # name, coords, ksize, stride
+    ("tiny_k3", synth.make("tiny").coords, 3, 1),
+    ("lidar_small_k3", synth.make("lidar", scale=0.04).coords, 3, 1),
+    ("fuzz_neg_k3", synth.random_coords(101, 1500, 3, 4, 16, lo=-8), 3, 1),
+    ("pixels_k3_2d", synth.make("pixels", scale=0.02).coords, 3, 1),
+    ("fuzz_k5_2d", synth.random_coords(14, 800, 2, 2, 40), 5, 1),
+    ("down_k2s2", synth.make("down", scale=0.03).coords, 2, 2),
+    ("fuzz_k3s2", synth.random_coords(15, 1500, 3, 2, 24, lo=-12), 3, 2),
+    ("k1", synth.random_coords(16, 700, 3, 2, 12), 1, 1),
+    ("k7_runtime_probe_2d", synth.random_coords(17, 600, 2, 2, 20), 7, 1),
+    ("one", np.array([[0, 3, 4, 5]], np.int32), 3, 1),
+]
+
+
+@pytest.mark.parametrize("no_table", [False, True], ids=["with_table", "no_table"])
+@pytest.mark.parametrize("case", MAPS, ids=[m[0] for m in MAPS])
+def test_groups_match_oracle(ts, case, no_table):
+    name, coords, k, s = case
+    if k % 2 == 0 and s == 1:
+        pytest.skip("submanifold maps need an odd kernel")
+    flags = ts.TS_KMAP_GROUPS | ts.TS_KMAP_PAIRS | (ts.TS_KMAP_NO_TABLE if no_table else 0)
+    km, oc = build(ts, coords, k, s, flags)
+    kvol = k ** (coords.shape[1] - 1)
+    tr = oracle.kmap(coords, oc, k, s)
+    arrs = km.rel_arrays("fwd")
+    assert np.array_equal(canon(ts.decode_groups(arrs, kvol)), canon(tr)), name
+    check_group_layout(arrs, kvol, oc.shape[0])
+    emits = (coords.shape[1] == 4 and k <= 3) or (coords.shape[1] == 3 and k in (2, 3, 5))
+    assert ("nbr" in arrs) == (not (no_table and emits))
+    if "nbr" in arrs:
+        assert np.array_equal(canon(ts.decode_rel(arrs, kvol)), canon(tr))
+    ps, pin, pout = km.pairs()
+    off = np.repeat(np.arange(kvol, dtype=np.int32), np.diff(ps))
+    assert np.array_equal(canon((pin, pout, off)), canon(tr))
+    for o in range(kvol):  # pair lists in output-row order within each offset
+        assert (np.diff(pout[ps[o]:ps[o + 1]]) > 0).all()
+    if s > 1:  # the transposed relation's groups (from its table)
+        barrs = km.rel_arrays("bwd")
+        assert np.array_equal(canon(ts.decode_groups(barrs, kvol, transposed=True)), canon(tr))
+        check_group_layout(barrs, kvol, coords.shape[0])
+
+
+CONV = [
+    # name, coords, ksize, stride, cin, cout, dtype
+    ("lidar_f16_64", synth.make("lidar", scale=0.04).coords, 3, 1, 64, 64, "f16"),
+    ("lidar_bf16_128", synth.make("lidar", scale=0.03).coords, 3, 1, 128, 128, "bf16"),
+    ("fuzz_f16_32x16", synth.random_coords(11, 1500, 3, 2, 14, lo=-7), 3, 1, 32, 16, "f16"),
+    ("fuzz_bf16_96x48", synth.random_coords(12, 900, 3, 3, 12, lo=-6), 3, 1, 96, 48, "bf16"),
+    ("fuzz_f16_64x80", synth.random_coords(18, 1100, 3, 2, 13, lo=-6), 3, 1, 64, 80, "f16"),
+    ("pixels_f16_32x32_2d", synth.make("pixels", scale=0.03).coords, 3, 1, 32, 32, "f16"),
+    ("k5_2d_bf16_64", synth.random_coords(14, 800, 2, 2, 40), 5, 1, 64, 64, "bf16"),
+    ("down_f16_64x128", synth.make("down", scale=0.03).coords, 2, 2, 64, 128, "f16"),
+    ("down_bf16_k3s2", synth.random_coords(15, 1500, 3, 2, 24, lo=-12), 3, 2, 32, 32, "bf16"),
+    ("k1_f16_64x32", synth.random_coords(16, 700, 3, 2, 12), 1, 1, 64, 32, "f16"),
+]
+
+
+@pytest.mark.parametrize("no_table", [False, True], ids=["with_table", "no_table"])
+@pytest.mark.parametrize("case", CONV, ids=[c[0] for c in CONV])
+def test_fod_parity(ts, case, no_table):
+    name, coords, k, s, cin, cout, dt = case
+    flags = ts.TS_KMAP_GROUPS | ts.TS_KMAP_PAIRS | (ts.TS_KMAP_NO_TABLE if no_table else 0)
+    km, oc = build(ts, coords, k, s, flags)
+    kvol = k ** (coords.shape[1] - 1)
+    tr = oracle.kmap(coords, oc, k, s)
+    n_in, n_out = coords.shape[0], oc.shape[0]
+    x = synth.normal(1400, (n_in, cin), 1.0, dt)
+    w = synth.weight(1401, kvol, cin, cout, dt)
+    dy = synth.normal(1402, (km.s.n_out_cap, cout), 1.0, dt)
+    xo = synth.normal(1403, (km.s.n_out_cap, cin), 1.0, dt)  # transposed conv input on the outputs
+    FOD = ts.TS_DATAFLOW_FETCH_ON_DEMAND
+    ref_y = oracle.conv_fwd(tr, x, w, n_out)
+    ref_dx = oracle.conv_dgrad(tr, dy[:n_out], w, n_in)
+    ref_t = oracle.conv_transpose(tr, xo[:n_out], w, n_in)
+    # the MFMA kernel contracts over multiples of 32 channels (up to 128)
+    # into multiples of 16: dgrad contracts over cout, into cin
+    fod_fwd = cin % 32 == 0 and cin <= 128 and cout % 16 == 0
+    fod_bwd = cout % 32 == 0 and cout <= 128 and cin % 16 == 0
+    assert fod_fwd
+    for out in (torch.float32, DT[dt]):
+        y = ts.conv_fwd(km, dev(x), dev(w), out_dtype=out, dataflow=FOD)
+        assert_feature_close(y[:n_out], ref_y, DT[dt], f"fod {name} fwd {out}")
+        yt = ts.conv_transpose(km, dev(xo), dev(w), out_dtype=out, dataflow=FOD)
+        assert_feature_close(yt, ref_t, DT[dt], f"fod {name} transpose {out}")
+        if fod_bwd:
+            dx = ts.conv_dgrad(km, dev(dy), dev(w), out_dtype=out, dataflow=FOD)
+            assert_feature_close(dx, ref_dx, DT[dt], f"fod {name} dgrad {out}")
+        else:
+            with pytest.raises(ts.TsError) as e:
+                ts.conv_dgrad(km, dev(dy), dev(w), out_dtype=out, dataflow=FOD)
+            assert e.value.status == ts.TS_ERR_UNSUPPORTED
+            if not no_table:  # AUTO falls back to the kernels that walk the table
+                dx = ts.conv_dgrad(km, dev(dy), dev(w), out_dtype=out)
+                assert_feature_close(dx, ref_dx, DT[dt], f"{name} dgrad (auto) {out}")
+    # the other dataflows agree within the feature tolerance; AUTO picks this one
+    y32 = ts.conv_fwd(km, dev(x), dev(w), out_dtype=torch.float32, dataflow=FOD)
+    auto = ts.conv_fwd(km, dev(x), dev(w), out_dtype=torch.float32)
+    assert torch.equal(auto[:n_out], y32[:n_out])
+    gs = ts.conv_fwd(km, dev(x), dev(w), out_dtype=torch.float32, dataflow=ts.TS_DATAFLOW_GATHER_SCATTER)
+    assert_feature_close(y32[:n_out], gs[:n_out].double().cpu().numpy(), DT[dt], f"fod vs gather-scatter {name}")
+    if not no_table:
+        ig = ts.conv_fwd(km, dev(x), dev(w), out_dtype=torch.float32, dataflow=ts.TS_DATAFLOW_IMPLICIT_GEMM)
+        assert_feature_close(y32[:n_out], ig[:n_out].double().cpu().numpy(), DT[dt], f"fod vs implicit GEMM {name}")
+    # bitwise repeatable
+    again = ts.conv_fwd(km, dev(x), dev(w), out_dtype=torch.float32, dataflow=FOD)
+    assert torch.equal(again[:n_out], y32[:n_out])
+
+
+def test_fod_target_and_generative(ts):
+    """Target maps (repeated targets, targets off the inputs) and a generated
+    support, through the pair groups."""
+    coords = synth.random_coords(21, 1200, 3, 2, 14, lo=-7)
+    rng = np.random.default_rng(22)
+    tgt = np.concatenate([coords[rng.choice(len(coords), 300)],
+                          synth.random_coords(23, 200, 3, 2, 16, lo=-8)]).astype(np.int32)
+    km, _ = build(ts, coords, 3, 1, ts.TS_KMAP_GROUPS, target=tgt)
+    tr = oracle.kmap(coords, tgt, 3, 1, target=True)
+    assert np.array_equal(canon(ts.decode_groups(km.rel_arrays("fwd"), 27)), canon(tr))
+    x = synth.normal(1410, (len(coords), 64), 1.0, "f16")
+    w = synth.weight(1411, 27, 64, 32, "f16")
+    y = ts.conv_fwd(km, dev(x), dev(w), out_dtype=torch.float32, dataflow=ts.TS_DATAFLOW_FETCH_ON_DEMAND)
+    assert_feature_close(y, oracle.conv_fwd(tr, x, w, len(tgt)), torch.float16, "fod target map")
+    # generated support
+    cd = dev(coords)
+    tab = ts.HashTable(cd, 2.0)
+    out, n_out, otab = ts.generative_support(cd, 3)
+    m = int(n_out.item())
+    km2 = ts.build_kmap(cd, tab, 3, 1, ts.TS_KMAP_TARGET | ts.TS_KMAP_GROUPS | ts.TS_KMAP_NO_TABLE,
+                        out_coords=out, n_out=n_out, out_table=otab)
+    oc = oracle.generative_support(coords, 3)
+    tr2 = oracle.kmap(coords, oc, 3, 1, target=True)
+    assert np.array_equal(canon(ts.decode_groups(km2.rel_arrays("fwd"), 27)), canon(tr2))
+    y2 = ts.conv_fwd(km2, dev(x), dev(w), out_dtype=torch.float32)
+    assert_feature_close(y2[:m], oracle.conv_fwd(tr2, x, w, m), torch.float16, "fod generative")
+
+
+@pytest.mark.parametrize("n", [0, 1, 127, 128, 129, 300])
+def test_fod_degenerate_sizes(ts, n):
+    coords = synth.random_coords(31, n, 3, 1, 10) if n else np.zeros((0, 4), np.int32)
+    n = coords.shape[0]
+    km, _ = build(ts, coords, 3, 1, ts.TS_KMAP_GROUPS | ts.TS_KMAP_NO_TABLE)
+    x = synth.normal(1420, (n, 64), 1.0, "f16")
+    w = synth.weight(1421, 27, 64, 64, "f16")
+    y = ts.conv_fwd(km, dev(x), dev(w), out_dtype=torch.float32, dataflow=ts.TS_DATAFLOW_FETCH_ON_DEMAND)
+    tr = oracle.kmap(coords, coords, 3, 1)
+    assert_feature_close(y, oracle.conv_fwd(tr, x, w, n), torch.float16, f"fod n={n}")
+
+
+def test_fod_duplicates_and_isolated_rows(ts):
+    """A repeated coordinate's higher row takes no part (zero output), an
+    isolated row gets only its centre term."""
+    c = synth.random_coords(41, 500, 3, 2, 12)
+    c = np.concatenate([c, c[[3, 10]], np.array([[1, 200, 200, 200]], np.int32)]).astype(np.int32)
+    km, _ = build(ts, c, 3, 1, ts.TS_KMAP_GROUPS | ts.TS_KMAP_NO_TABLE)
+    tr = oracle.kmap(c, c, 3, 1)
+    assert np.array_equal(canon(ts.decode_groups(km.rel_arrays("fwd"), 27)), canon(tr))
+    x = synth.normal(1430, (len(c), 32), 1.0, "bf16")
+    w = synth.weight(1431, 27, 32, 48, "bf16")
+    y = ts.conv_fwd(km, dev(x), dev(w), out_dtype=torch.float32)
+    ref = oracle.conv_fwd(tr, x, w, len(c))
+    assert_feature_close(y, ref, torch.bfloat16, "fod duplicates")
+    assert (y[-3:-1] == 0).all()
+
+
+def test_fod_unaligned_weights(ts):
+    coords = synth.make("lidar", scale=0.03).coords
+    km, _ = build(ts, coords, 3, 1, ts.TS_KMAP_GROUPS | ts.TS_KMAP_NO_TABLE)
+    x = dev(synth.normal(1440, (len(coords), 64), 1.0, "f16"))
+    w = dev(synth.weight(1441, 27, 64, 64, "f16"))
+    buf = torch.empty(w.numel() + 8, dtype=w.dtype, device="cuda")
+    wu = buf[1:1 + w.numel()].view(w.shape)
+    wu.copy_(w)
+    assert wu.data_ptr() % 16 != 0
+    a = ts.conv_fwd(km, x, w, out_dtype=torch.float32)
+    b = ts.conv_fwd(km, x, wu, out_dtype=torch.float32)
+    assert torch.equal(a, b)
+    dy = dev(synth.normal(1442, (len(coords), 64), 1.0, "f16"))
+    assert torch.equal(ts.conv_dgrad(km, dy, w, out_dtype=torch.float32),
+                       ts.conv_dgrad(km, dy, wu, out_dtype=torch.float32))
+
+
+def test_fod_rejections(ts):
+    coords = synth.random_coords(51, 400, 3, 1, 10)
+    cd = dev(coords)
+    tab = ts.HashTable(cd, 2.0)
+    plain = ts.build_kmap(cd, tab, 3, 1, 0)
+    notab = ts.build_kmap(cd, tab, 3, 1, ts.TS_KMAP_GROUPS | ts.TS_KMAP_NO_TABLE)
+    x = dev(synth.normal(1450, (len(coords), 64), 1.0, "f16"))
+    w = dev(synth.weight(1451, 27, 64, 64, "f16"))
+    y = torch.empty((len(coords), 64), dtype=torch.float16, device="cuda")
+    with pytest.raises(ts.TsError) as e:  # no pair groups in the map
+        ts.ts_conv_fwd(plain.s, x, w, y, ts.TS_DATAFLOW_FETCH_ON_DEMAND)
+    assert e.value.status == ts.TS_ERR_INVALID_ARG
+    with pytest.raises(ts.TsError) as e:  # the implicit GEMM needs the table
+        ts.ts_conv_fwd(notab.s, x, w, y, ts.TS_DATAFLOW_IMPLICIT_GEMM)
+    assert e.value.status == ts.TS_ERR_INVALID_ARG
+    with pytest.raises(ts.TsError) as e:  # pooling needs the table
+        ts.ts_pool_fwd(notab.s, x, y)
+    assert e.value.status == ts.TS_ERR_INVALID_ARG
+    x32 = x.float()
+    with pytest.raises(ts.TsError) as e:  # no MFMA kernel for fp32 inputs
+        ts.ts_conv_fwd(notab.s, x32, w.float(), y.float(), ts.TS_DATAFLOW_FETCH_ON_DEMAND)
+    assert e.value.status == ts.TS_ERR_UNSUPPORTED
+    with pytest.raises(ts.TsError) as e:  # NO_TABLE without GROUPS
+        ts.build_kmap(cd, tab, 3, 1, ts.TS_KMAP_NO_TABLE)
+    assert e.value.status == ts.TS_ERR_INVALID_ARG

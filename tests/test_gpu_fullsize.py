@@ -38,20 +38,27 @@ def check_triples(km, tr, kvol, what):
 
 
 def ts_decode(km, kvol):
+    """The map's forward relation as triples: from its neighbour table, or
+    from its pair groups when it has no table (both when it has both)."""
     from convolution_voxelised_point_amd import ts
-    return ts.decode_rel(km.rel_arrays("fwd"), kvol)
+    arrs = km.rel_arrays("fwd")
+    if "gcount" in arrs and "nbr" in arrs:
+        a, b = canon(ts.decode_rel(arrs, kvol)), canon(ts.decode_groups(arrs, kvol))
+        assert np.array_equal(a, b), "pair groups and neighbour table disagree"
+    return ts.decode_rel(arrs, kvol) if "nbr" in arrs else ts.decode_groups(arrs, kvol)
 
 
 @pytest.mark.parametrize("rows_shuffled", [False, True], ids=["lex_rows", "shuffled_rows"])
-@pytest.mark.parametrize("order", ["natural", "sorted"])
+@pytest.mark.parametrize("order", ["groups", "natural", "sorted"])
 def test_full_lidar_subm_f16(ts, order, rows_shuffled):
-    """Both tile orders: the benchmark's (rows in index order, the map
-    serving one contraction) and the window sort by offset mask; on the
+    """The three maps the benchmark measures: pair groups only (the
+    headline step: fetch-on-demand forward), and a neighbour table with
+    tiles in row order or sorted by offset mask (implicit GEMM); on the
     scene's lexicographic rows and on the seeded shuffle of them."""
     w = synth.make("lidar")
     if rows_shuffled:
         w = synth.shuffled(w)
-    flags = ts.TS_KMAP_NATURAL if order == "natural" else 0
+    flags = {"groups": ts.TS_KMAP_GROUPS | ts.TS_KMAP_NO_TABLE, "natural": ts.TS_KMAP_NATURAL, "sorted": 0}[order]
     s = bench.setup_subm(ts, w, kmap_flags=flags)
     s.run_once()
     assert int(s.flags.item()) == 0
@@ -59,13 +66,15 @@ def test_full_lidar_subm_f16(ts, order, rows_shuffled):
     tr = oracle.kmap(w.coords, w.coords, 3, 1)
     check_triples(s.kmap, tr, 27, "lidar")
     rel = s.kmap.rel_arrays("fwd")
-    slots = rel["tile_rows"].cpu().numpy()
-    if order == "natural":
+    if order == "groups":
+        assert "nbr" not in rel and "gcount" in rel
+    elif order == "natural":
+        slots = rel["tile_rows"].cpu().numpy()
         want = np.full(slots.shape[0], -1, np.int32)
         want[:w.n] = np.arange(w.n, dtype=np.int32)
         assert np.array_equal(slots, want)
     else:
-        check_window_sorted(slots, rel["row_mask"].cpu().numpy().view(np.uint64)[:w.n])
+        check_window_sorted(rel["tile_rows"].cpu().numpy(), rel["row_mask"].cpu().numpy().view(np.uint64)[:w.n])
     ref = oracle.conv_fwd(tr, w.x, w.w, w.n)
     tag = f"lidar {order} {'shuffled' if rows_shuffled else 'lex'}"
     assert_feature_close(s.y, ref, torch.float16, f"{tag} fwd fp16 out")
