@@ -35,6 +35,7 @@ TS_KMAP_GROUPS, TS_KMAP_NO_TABLE = 32, 64
 TS_OP_FWD, TS_OP_DGRAD, TS_OP_WGRAD, TS_OP_TRANSPOSE = 0, 1, 2, 3
 TS_POOL_MAX, TS_POOL_AVG = 0, 1
 TS_TILE, TS_GTILE, TS_MAX_KVOL = 16, 128, 64
+TS_NOALLOC_SCRATCH_BYTES = 4 << 20
 
 _DT = {torch.float32: TS_F32, torch.float16: TS_F16, torch.bfloat16: TS_BF16}
 
@@ -100,6 +101,7 @@ _lib_graph_conv_fwd = _sig("ts_graph_conv_fwd", _i32, [_vp, _vp, _vp, _i64, _i64
 _lib_pool_fwd = _sig("ts_pool_fwd", _i32, [_P, _vp, _i32, _vp, _i32, _i32, _i32, _vp])
 _lib_conv_bwd_dgrad = _sig("ts_conv_bwd_dgrad", _i32, [_P, _vp, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _vp, _sz, _vp])
 _lib_conv_bwd_wgrad = _sig("ts_conv_bwd_wgrad", _i32, [_P, _vp, _i32, _vp, _i32, _i32, _vp, _vp, _sz, _vp])
+_lib_conv_bwd_dgrad_noalloc = _sig("ts_conv_bwd_dgrad_noalloc", _i32, [_P, _vp, _i32, _vp, _i32, _vp, _i32, _i32, _vp])
 
 EXPORTED = ["ts_status_string", "ts_version", "ts_hash_capacity", "ts_hash_table_bytes", "ts_hash_build",
             "ts_hash_query", "ts_support_scratch_bytes", "ts_strided_support", "ts_generative_scratch_bytes",
@@ -107,7 +109,7 @@ EXPORTED = ["ts_status_string", "ts_version", "ts_hash_capacity", "ts_hash_table
             "ts_devoxelize", "ts_kmap_bytes", "ts_kmap_build",
             "ts_conv_workspace_bytes", "ts_conv_pack_weights", "ts_conv_fwd", "ts_subm_conv_fwd", "ts_conv_fwd_strided",
             "ts_conv_fwd_generative", "ts_conv_transpose_fwd", "ts_pool_fwd", "ts_graph_conv_fwd", "ts_conv_bwd_dgrad",
-            "ts_conv_bwd_wgrad"]
+            "ts_conv_bwd_wgrad", "ts_conv_bwd_dgrad_noalloc"]
 
 
 class TsError(RuntimeError):
@@ -291,6 +293,12 @@ def ts_conv_bwd_dgrad(kmap, dy, w, dx, dataflow=TS_DATAFLOW_AUTO, ws=None, strea
     _check(_lib_conv_bwd_dgrad(ctypes.byref(kmap), _p(dy), dy.shape[1], _p(w), dx.shape[1], _p(dx), _dt(dy), _dt(dx),
                                dataflow, _p(ws), 0 if ws is None else ws.numel(), _stream(stream)),
            "ts_conv_bwd_dgrad")
+
+
+def ts_conv_bwd_dgrad_noalloc(kmap, dy, w, dx, stream=None) -> None:
+    """dgrad with the library's static scratch instead of a workspace."""
+    _check(_lib_conv_bwd_dgrad_noalloc(ctypes.byref(kmap), _p(dy), dy.shape[1], _p(w), dx.shape[1], _p(dx), _dt(dy),
+                                       _dt(dx), _stream(stream)), "ts_conv_bwd_dgrad_noalloc")
 
 
 def ts_conv_bwd_wgrad(kmap, x, dy, dw, ws, stream=None) -> None:

@@ -497,6 +497,25 @@ ts_status ts_conv_bwd_dgrad(const ts_kmap* map, const void* dy, int cout, const 
 ts_status ts_conv_bwd_wgrad(const ts_kmap* map, const void* x, int cin, const void* dy, int cout,
                             ts_dtype in_dtype, float* dw, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation):
+ * ts_conv_bwd_dgrad with the implicit GEMM's packed weights in a static
+ * device array of the library instead of a caller workspace, so the call
+ * allocates nothing.  The array holds TS_NOALLOC_SCRATCH_BYTES; each GPU the
+ * library runs on keeps its own copy until the process ends.  Dataflow: the
+ * implicit GEMM where the shape has one (fp16/bf16, source channels a
+ * multiple of 32 up to 128, destination channels a multiple of 16), else the
+ * direct kernel, which needs no scratch; the gather-scatter dataflow is not
+ * offered (its accumulator grows with the rows).  Arguments, results and the
+ * other errors are those of ts_conv_bwd_dgrad; a shape whose packed weights
+ * exceed TS_NOALLOC_SCRATCH_BYTES returns TS_ERR_UNSUPPORTED, and a failed
+ * lookup of the array's device address TS_ERR_HIP.  Every call on one GPU
+ * shares that GPU's array: calls that overlap on one GPU (unordered streams,
+ * host threads) race and give wrong results; order them on one stream. */
+#define TS_NOALLOC_SCRATCH_BYTES (4u << 20)
+ts_status ts_conv_bwd_dgrad_noalloc(const ts_kmap* map, const void* dy, int cout, const void* w, int cin, void* dx,
+                                    ts_dtype in_dtype, ts_dtype out_dtype, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif
