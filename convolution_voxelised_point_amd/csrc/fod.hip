@@ -4,33 +4,42 @@
 // computation with memory access).  It walks a relation stored as per-tile
 // pair groups: the destination rows are cut into tiles of TS_GTILE rows, and
 // inside a tile the pairs of each offset are listed in destination order and
-// padded to whole groups of 16, so group g of a tile occupies entries
-// [16g, 16g + 16) of the tile's lists.  Every group is one 16-pair MFMA
-// product with a single offset's weights: only the source rows that exist are
-// fetched, straight from the source matrix into MFMA operands (no gather
-// buffer), and the products are added into the destination rows of an fp32
-// accumulator tile held in LDS, which is written out once per tile.  There
-// are no atomics: within a group the destination rows are distinct, and one
-// wave owns each accumulator tile and adds its groups in a fixed order, so
-// results are bitwise repeatable.
+// padded to whole groups of 16 (pads name no source row and the sink slot
+// TS_GTILE), so group g of a tile occupies entries [16g, 16g + 16).  Every
+// group is one 16-pair MFMA product with a single offset's weights: only the
+// source rows that exist are fetched, straight from the source matrix into
+// MFMA operands (no gather buffer), and the products are added into the
+// destination rows of an fp32 accumulator tile held in LDS, which is written
+// out once.  There are no atomics: within a group the destination rows are
+// distinct, and one wave owns each accumulator tile and adds its groups in
+// a fixed offset order, so results are bitwise repeatable.
 //
-// Work split.  A block owns one column of CB = 16 * MW output channels and
-// keeps that column's weights for every offset resident in LDS (loaded once
-// per block; the only barrier of the kernel follows that load).  Its waves
-// take tiles of the block's share from an LDS ticket; a wave's accumulator is
-// R x CB fp32 in its own LDS region.  Blocks are numbered so that each XCD
-// walks a contiguous eighth of the tiles for every column (the columns of a
-// tile then fetch the same source rows from the same L2).
+// Work split.  A block holds NT tiles, each owned by one or two compute waves
+// (two split a 64-channel column into halves of 32: smaller accumulators,
+// two waves per SIMD to overlap each other's waits), and one loader wave; a
+// block column covers up to 64 output channels.  The block steps through the
+// offsets in lockstep: barrier k means that step k's weights sit in LDS (a
+// ring of three slices, written by the loader wave from registers it fills
+// several steps ahead) and that every compute wave is done with the
+// steps before k.  Step k takes offset (k + rot) mod kvol, rot set by the
+// block, so that blocks running at once copy different weight slices.  A
+// compute wave passes the barriers of the steps its tile lacks without
+// work, and its gathers run ahead of the barriers (they do not depend on the
+// weights).  Blocks are numbered so that each XCD walks a contiguous range
+// of tiles (a tile's columns fetch the same source rows from the same L2).
 //
 // Weights reach LDS as stored: the forward layout W[o][c_src][c_dst] row by
 // row (fragments built with gfx950's transposing LDS reads), the dgrad
 // layout W[o][c_dst][c_src] row by row (fragments are plain 16-byte reads);
-// a mirrored map stores W[kvol-1-o] in slot o.
+// a mirrored map takes W[kvol-1-o] for offset o.
 //
-// Pipeline per wave (constant load pattern per group, so the compiler's
-// wait before a use covers only that use's loads): the source rows and
-// slots of group g + DM, the source-row fetches of group g + DB, then the
-// MFMAs of group g and the read-add-write of its accumulator rows.
+// Pipeline per compute wave (constant load pattern per group, so the
+// compiler's wait before a use covers only that use's loads): the source-row
+// fetches of group g + DB, the source rows and slots of group g + DM, then
+// the MFMAs of group g and the read-add-write of its accumulator rows.  The
+// loads are in flight for DB and DM groups: a gather from HBM takes
+// microseconds under load, so the depth, not the instruction count, sets the
+// time per group.
 #include "common.h"
 #include "launch.h"
 
@@ -60,12 +69,31 @@ struct FMfma<__bf16> {
   }
 };
 
-constexpr int kR = TS_GTILE;                     // destination rows per tile
-constexpr int kLdsChunks = (156 * 1024) / 16;    // 16-byte chunks of LDS per block
-constexpr int kRingM = 16;                       // register sets of (source row, slot), group mod 16
-constexpr int kRingB = 8;                        // register sets of fetched rows, group mod 8
-constexpr int kDM = 15;                          // groups the slot loads run ahead
-constexpr int kDB = 7;                           // groups the row fetches run ahead
+constexpr int kR = TS_GTILE;          // destination rows per tile (row kR of an accumulator: pad sink)
+constexpr int kSlots = 3;             // weight slices in LDS: offsets o, o + 1, o + 2
+constexpr int kLdsBytes = 160 * 1024; // LDS of one block
+// Pipeline depths (groups in flight per wave): the fetched source rows of
+// RB groups (4 when three waves share a SIMD's registers, else 8), the
+// entries of RM = 2 RB groups; a round is RM groups.
+constexpr int fod_rb(int waves) { return waves > 8 ? 4 : 8; }
+
+// Bytes of one offset's weight slice (c_src = 32 KB channels by 16 MW
+// output channels, 16-bit) and of one wave's accumulator (kR + 1 rows of
+// 16 MH fp32, MH the MFMA blocks of 16 output channels a wave owns).
+constexpr int fod_slice_bytes(int kb, int mw) { return 1024 * kb * mw; }
+constexpr int fod_acc_bytes(int mh) { return (kR + 1) * 64 * mh; }
+// Compute waves per block at most: 8 (with the loader, three waves on one
+// SIMD) for up to 64 contracted channels, else 6 (two per SIMD: their
+// fetched rows need the registers).
+constexpr int fod_max_nw(int kb) { return kb <= 2 ? 8 : 6; }
+// Tiles per block: as many tiles' accumulators (MW / MH waves each) as fit
+// beside the weight ring, within that wave count.
+constexpr int fod_tiles(int kb, int mw, int mh) {
+  return (kLdsBytes - kSlots * fod_slice_bytes(kb, mw)) / (fod_acc_bytes(mh) * (mw / mh)) * (mw / mh) >
+                 fod_max_nw(kb)
+             ? fod_max_nw(kb) / (mw / mh)
+             : (kLdsBytes - kSlots * fod_slice_bytes(kb, mw)) / (fod_acc_bytes(mh) * (mw / mh));
+}
 
 struct FodK {
   const int32_t* gcount;  // [n_gtiles][kvol]
@@ -76,17 +104,17 @@ struct FodK {
   int64_t n_dest_cap;
   int kvol;
   const void* src;
-  uint32_t src_bytes;     // < 2^31: an offset of 2^31 reads out of range
+  uint32_t src_bytes;     // < 2^31: an offset of 2^31 or more reads out of range
   int c_src;
   const void* w;
   int w_vec;              // w is 16-byte aligned
-  int mirror;             // slot o holds W[kvol - 1 - o]
+  int mirror;             // step o takes W[kvol - 1 - o]
   void* dst;
   int c_dst;
   int out_dtype;
   int ncol;               // output-channel columns
-  int nsub;               // blocks per (XCD, column)
-  int acc_base;           // first LDS chunk of the accumulators
+  int64_t nblk;           // blocks of NT tiles
+  int64_t nb8;            // ceil(nblk / 8)
 };
 
 // Swizzle of 16-byte chunk c in row r of a table whose rows hold nch chunks:
@@ -125,6 +153,17 @@ __device__ __forceinline__ u32x4 lds_tr_frag(const char* p0, const char* p4) {
   return u32x4{l[0], l[1], h[0], h[1]};
 }
 
+// All of this wave's LDS operations have completed.
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+// Workgroup barrier with no memory fence: each wave states the waits it
+// needs before it, so gathers in flight stay in flight across it.  The empty
+// asm statements keep the compiler from moving memory operations across.
+__device__ __forceinline__ void bare_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ void store4(void* dst, int out_dtype, int64_t off, f32x4 v) {
   if (out_dtype == TS_F32) {
     *reinterpret_cast<f32x4*>(static_cast<float*>(dst) + off) = v;
@@ -141,109 +180,168 @@ __device__ __forceinline__ void store4(void* dst, int out_dtype, int64_t off, f3
   }
 }
 
+// A wave-uniform address, stated as such (kept in scalar registers: a
+// buffer descriptor built from a vector register is used lane group by lane
+// group).
+__device__ __forceinline__ void* uniform_ptr(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
 template <int I>
 struct Fi {
   static constexpr int v = I;
 };
+// f(Fi<0>{}), ..., f(Fi<N-1>{}) in order, unrolled at compile time.
+template <int N, int I = 0>
+struct Unroll {
+  template <class F>
+  static __device__ __forceinline__ void run(F&& f) {
+    f(Fi<I>{});
+    Unroll<N, I + 1>::run(f);
+  }
+};
+template <int N>
+struct Unroll<N, N> {
+  template <class F>
+  static __device__ __forceinline__ void run(F&&) {}
+};
 
-// Waves per block at most: 12 (three per SIMD, up to 168 registers per
-// lane), or 8 for 96 and 128 contracted channels or 32-channel columns,
-// whose operand rings need more.
-constexpr int fod_max_waves(int kb, int mw) { return (kb >= 3 || mw >= 2) ? 8 : 12; }
-
-template <typename T, int KB, int MW, int WM>
-__global__ __launch_bounds__(64 * fod_max_waves(KB, MW)) void k_fod(FodK a) {
+template <typename T, int KB, int MW, int MH, int WM>
+__global__ __launch_bounds__(64 * (fod_tiles(KB, MW, MH) * (MW / MH) + 1)) void k_fod(FodK a) {
   typedef typename FMfma<T>::frag Frag;
+  constexpr int WPT = MW / MH;        // compute waves per tile (one per MH blocks of 16 channels)
+  constexpr int NT = fod_tiles(KB, MW, MH);  // tiles per block
+  constexpr int NW = NT * WPT;        // compute waves per block
   constexpr int CB = 16 * MW;         // output channels of the block column
-  constexpr int NCH = CB / 4;         // 16-byte fp32 chunks per accumulator row
+  constexpr int NCH = 4 * MH;         // 16-byte fp32 chunks per accumulator row
   constexpr int C_SRC = 32 * KB;      // contracted channels
   constexpr int WROW = WM == 0 ? CB * 2 : C_SRC * 2;  // bytes per stored weight row in LDS
-  constexpr int WROWS = WM == 0 ? C_SRC : CB;         // weight rows per offset
-  constexpr int WSLICE = WROW * WROWS;                // bytes per offset
-  __shared__ u32x4 lds[kLdsChunks];
-  __shared__ unsigned ticket;
+  constexpr int SLICE = fod_slice_bytes(KB, MW);      // bytes per offset
+  constexpr int COPIES = SLICE / 1024;                // 16-byte copies per lane and offset
+  constexpr int ACC = fod_acc_bytes(MH);
+  static_assert(kSlots * SLICE + NW * ACC <= kLdsBytes, "LDS budget");
+  __shared__ __attribute__((aligned(1024))) char lds[kSlots * SLICE + NW * ACC];
 
+  constexpr int RB = fod_rb(NW + 1);  // fetched-row register sets
+  constexpr int DB = RB - 1;          // groups the row fetches run ahead
+  constexpr int RM = 2 * RB;          // slot register sets, and groups per round
+  constexpr int DM = RM - 1;          // groups the entry loads run ahead
+  // source-row entries live DM - DB = RB groups (loaded DM, used DB groups
+  // ahead); every ring's length divides the round so positions repeat
+  constexpr int RS = RM;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int nwave = blockDim.x >> 6;
   const int col = lane & 15, kq = lane >> 4;
-  const int xcd = blockIdx.x & 7;
-  const int bk = blockIdx.x >> 3;
-  const int column = bk % a.ncol;
-  const int sub = bk / a.ncol;
+  const int hb = blockIdx.x;
+  const int k8 = hb >> 3;
+  const int column = k8 % a.ncol;
+  const int64_t tb = static_cast<int64_t>(hb & 7) * a.nb8 + k8 / a.ncol;
+  if (tb >= a.nblk) return;  // the whole block, before any barrier
   const int n0 = column * CB;
   const int kvol = a.kvol;
-  char* const ldsb = reinterpret_cast<char*>(lds);
+  // The block's steps k = 0 .. kvol-1 take offsets (k + rot) mod kvol:
+  // blocks that run at the same time start at different offsets, so their
+  // weight copies read different slices (one slice read by every block at
+  // once queues on the few L2 channels that hold it).
+  const int rot = static_cast<int>(tb % kvol);
 
-  // the column's weights for every offset, as stored, into LDS: each thread
-  // issues up to 8 chunk loads before it stores any (one memory round trip
-  // per 8 chunks); chunks outside the weights (channels past c_dst) load
-  // element 0 and store zeros
-  {
+  if (wave == NW) {
+    // Loader: step k's weights into slot k % 3 before barrier k, staged in
+    // registers LD steps ahead (the copy of a slice takes longer than a step).
+    // Chunk p of a slot (16 bytes): forward layout row ci = p / (CB/8) at
+    // swizzled column, dgrad layout row nl = p / (C_SRC/8) likewise; chunks
+    // of output channels past c_dst copy a valid chunk of the slice (they
+    // feed accumulator channels that are never written out).  Slot k % 3
+    // last held step k - 3, which every wave is past once barrier k - 1 is.
+    constexpr int LD = KB <= 2 && WM == 0 ? 4 : 2;
     const T* w = static_cast<const T*>(a.w);
-    const int per_slice = WSLICE / 16;
-    const int total = kvol * per_slice;
-    auto chunk_of = [&](int i, int64_t* g, int* lpos) {
-      const int o = i / per_slice, r = i - o * per_slice;
-      const int os = a.mirror ? kvol - 1 - o : o;
-      int lp;
-      if (WM == 0) {
-        const int ci = r / (CB / 8), part = r - ci * (CB / 8);
+    auto chunk_src = [&](int os, int p) -> int64_t {
+      if constexpr (WM == 0) {
+        const int ci = p / (CB / 8), sc = p - ci * (CB / 8);
+        const int part = sc ^ (2 * wswz<MW>(ci));
         const int co = n0 + 8 * part;
-        *g = co < a.c_dst ? (static_cast<int64_t>(os) * C_SRC + ci) * a.c_dst + co : -1;
-        lp = ci * WROW + 16 * (part ^ (2 * wswz<MW>(ci)));
+        return (static_cast<int64_t>(os) * C_SRC + ci) * a.c_dst + (co < a.c_dst ? co : 0);
       } else {
-        const int nl = r / (C_SRC / 8), part = r - nl * (C_SRC / 8);
+        const int nl = p / (C_SRC / 8), sc = p - nl * (C_SRC / 8);
+        const int part = chunk_swz(nl, sc, C_SRC / 8 < 16 ? C_SRC / 8 : 16);
         const int n = n0 + nl;
-        *g = n < a.c_dst ? (static_cast<int64_t>(os) * a.c_dst + n) * C_SRC + 8 * part : -1;
-        lp = nl * WROW + 16 * chunk_swz(nl, part, C_SRC / 8 < 16 ? C_SRC / 8 : 16);
+        return (static_cast<int64_t>(os) * a.c_dst + (n < a.c_dst ? n : 0)) * C_SRC + 8 * part;
       }
-      *lpos = o * WSLICE + lp;
     };
-    for (int i0 = threadIdx.x; i0 < total; i0 += 8 * blockDim.x) {
-      u32x4 v[8];
-      int lpos[8];
-      bool take[8];
+    u32x4 st[LD][COPIES];
+    auto fetch = [&](int k, u32x4 (&r)[COPIES]) {
+      const int o = k + rot < kvol ? k + rot : k + rot - kvol;
+      const int os = a.mirror ? kvol - 1 - o : o;
+      if (a.w_vec) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int i = i0 + u * static_cast<int>(blockDim.x);
-        int64_t g = -1;
-        lpos[u] = 0;
-        if (i < total) chunk_of(i, &g, &lpos[u]);
-        take[u] = i < total;
-        const int64_t gs = g >= 0 ? g : 0;
-        if (a.w_vec) {
-          v[u] = *reinterpret_cast<const u32x4*>(w + gs);
-        } else {
-          unsigned short e[8];
+        for (int j = 0; j < COPIES; ++j) r[j] = *reinterpret_cast<const u32x4*>(w + chunk_src(os, 64 * j + lane));
+      } else {  // unaligned weights: element by element
 #pragma unroll
-          for (int j = 0; j < 8; ++j) e[j] = __builtin_bit_cast(unsigned short, w[gs + j]);
+        for (int j = 0; j < COPIES; ++j) {
+          const T* g = w + chunk_src(os, 64 * j + lane);
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            v[u][j] = static_cast<unsigned>(e[2 * j]) | (static_cast<unsigned>(e[2 * j + 1]) << 16);
+          for (int q = 0; q < 4; ++q)
+            r[j][q] = static_cast<unsigned>(__builtin_bit_cast(unsigned short, g[2 * q])) |
+                      (static_cast<unsigned>(__builtin_bit_cast(unsigned short, g[2 * q + 1])) << 16);
         }
-        if (g < 0) v[u] = u32x4{0u, 0u, 0u, 0u};
       }
+    };
+    Unroll<LD>::run([&](auto jc) {
+      constexpr int j = decltype(jc)::v;
+      if (j < kvol) fetch(j, st[j]);
+    });
+    for (int k0 = 0; k0 < kvol; k0 += LD) {
+      Unroll<LD>::run([&](auto jc) {
+        constexpr int j = decltype(jc)::v;
+        const int k = k0 + j;
+        if (k < kvol) {  // wave-uniform
+          char* slot = lds + (k % kSlots) * SLICE;
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (take[u]) *reinterpret_cast<u32x4*>(ldsb + lpos[u]) = v[u];
+          for (int c = 0; c < COPIES; ++c) *reinterpret_cast<u32x4*>(slot + 1024 * c + 16 * lane) = st[j][c];
+          wait_lds();
+          bare_barrier();
+          if (k + LD < kvol) fetch(k + LD, st[j]);
+        }
+      });
     }
-    if (threadIdx.x == 0) ticket = 0u;
-    __syncthreads();
+    return;
   }
 
-  // this block's share of the tiles: XCD x walks the x-th eighth, its
-  // blocks of this column a contiguous part each
-  const int64_t nt = a.n_gtiles;
-  const int64_t xlo = nt * xcd / 8, xn = nt * (xcd + 1) / 8 - xlo;
-  const int64_t lo = xlo + xn * sub / a.nsub, hi = xlo + xn * (sub + 1) / a.nsub;
-  const int64_t n_dest = a.n_dest ? (*a.n_dest < a.n_dest_cap ? *a.n_dest : a.n_dest_cap) : a.n_dest_cap;
-  char* const accb = ldsb + static_cast<int64_t>(a.acc_base + wave * (kR * NCH)) * 16;
+  // compute wave: tile t, output channels n0 + 16 MH h .. + 16 MH
+  const int h = wave % WPT;
+  const int64_t t = tb * NT + wave / WPT;
+  const bool has_tile = t < a.n_gtiles;
+  const int nw0 = n0 + 16 * MH * h;
+  const int acc_off = kSlots * SLICE + wave * ACC;  // this wave's accumulator (row-size aligned)
+  char* const accb = lds + acc_off;
+#pragma unroll
+  for (int i = 0; i < kR * NCH / 64; ++i)
+    *reinterpret_cast<f32x4*>(accb + (i * 64 + lane) * 16) = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // groups of the tile in step order: lane k < kvol holds the group count of
+  // step k's offset and the end of its groups (inclusive prefix); group v
+  // of the steps is stored group (v + gbase) mod G, gbase the groups of the
+  // offsets before rot
+  const int lane_o = lane + rot < kvol ? lane + rot : lane + rot - kvol;
+  const int cnt = has_tile && lane < kvol ? a.gcount[t * kvol + lane_o] : 0;
+  const int ng = (cnt + 15) >> 4;
+  int incl = ng;
+#pragma unroll
+  for (int sh = 1; sh < 64; sh <<= 1) {
+    const int y = __shfl_up(incl, sh, 64);
+    incl += lane >= sh ? y : 0;
+  }
+  const int G = __builtin_amdgcn_readlane(incl, 63);
+  const uint64_t present = __ballot(lane < kvol && ng > 0);
+  const int gbase = rot == 0 ? 0 : G - __builtin_amdgcn_readlane(incl, kvol - rot - 1);
+  const int64_t ebase = t * static_cast<int64_t>(kvol) * kR;
+
   const T* src = static_cast<const T*>(a.src);
   const __amdgpu_buffer_rsrc_t xr =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(src), 0, static_cast<int>(a.src_bytes), 0x00020000);
-  const int c_src = a.c_src;
-  (void)nwave;
 
   // transposing-read addresses of this lane inside a forward-layout slice
   const int trq = lane & 3, trm = (lane >> 2) & 3;
@@ -251,250 +349,194 @@ __global__ __launch_bounds__(64 * fod_max_waves(KB, MW)) void k_fod(FodK a) {
   const int tr_b4 = tr_b0 + 4 * WROW;
   const int tr_x0 = 32 * wswz<MW>(8 * kq + trm), tr_x4 = 32 * wswz<MW>(8 * kq + 4 + trm);
 
-  for (;;) {
-    unsigned tk = 0u;
-    if (lane == 0) tk = atomicAdd(&ticket, 1u);
-    const int64_t t = lo + static_cast<int64_t>(__builtin_amdgcn_readfirstlane(tk));
-    if (t >= hi) break;
+  int k_cur = -1;  // step whose fragments are held (barriers 0..k_cur passed)
+  int e_cur = 0;   // end of its groups
 
-    // zero the accumulator tile
-#pragma unroll
-    for (int i = 0; i < kR * NCH / 64; ++i)
-      *reinterpret_cast<f32x4*>(accb + (i * 64 + lane) * 16) = f32x4{0.f, 0.f, 0.f, 0.f};
+  // Register rings indexed by group (compile-time positions): source row and
+  // slot of each lane (loaded DM groups ahead), the fetched source rows (DB
+  // groups ahead).  A slot is loaded as the aligned word that holds it (a
+  // group's entries start at a multiple of 16, so lane col's byte is byte
+  // col % 4 of its word) and taken out at its use: a ring of byte loads
+  // would be widened where the rounds loop back, which waits for them all.
+  // Entry loads go through buffer descriptors over the tile's entries, with
+  // the step's position as the instruction's constant offset; an entry past
+  // the tile reads as 0.  Source-row fetches are not masked: pads (-1) and
+  // entries past the tile's groups read out of range (zeros, no access) or
+  // a row that is never used.
+  int32_t msrc[RS];
+  uint32_t mslot[RM];
+  Frag xs[RB][KB];
+  Frag af[MH][KB];
+  const int slot_shift = 8 * (col & 3);
+  // (a wave without a tile builds them too and never uses them)
+  const __amdgpu_buffer_rsrc_t er_src =
+      __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(a.gsrc + ebase), 0, kvol * kR * 4, 0x00020000);
+  const __amdgpu_buffer_rsrc_t er_slot =
+      __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(a.gslot + ebase), 0, kvol * kR, 0x00020000);
+  // accumulator chunk swizzle: chunk c of row r sits at c ^ sw(r) (the
+  // chunk_swz layout), so the MH chunks of a lane's row are the address of
+  // chunk kq ^ sw(r) with bit 6 and up XORed by 64 mb (rows are 64 MH bytes,
+  // row-size aligned)
+  constexpr int SW_PER = NCH >= 16 ? 1 : 16 / NCH;
+  constexpr int SW_MASK = (NCH >= 16 ? 16 : NCH) - 1;
 
-    // groups of the tile: lane o < kvol holds its offset's pair count, the
-    // offset's first group (exclusive prefix of the group counts) and the
-    // end of its groups
-    const int cnt = lane < kvol ? a.gcount[t * kvol + lane] : 0;
-    const int ng = (cnt + 15) >> 4;
-    int incl = ng;
+  // one group position p of a round: the fetch of group v0 + p + DB's
+  // source rows, then the entry loads of group v0 + p + DM (groups past the
+  // tile's last read stored group 0), then, outside the first round, the
+  // MFMAs of group v0 + p.  The fetch reads its source-row entry before the
+  // entry load of the same step reuses that register.
+  auto step = [&](int v0, auto pc, auto firstc) {
+    constexpr int p = decltype(pc)::v;
+    constexpr bool FIRST = decltype(firstc)::v;
+    if constexpr (!FIRST || p + DB >= RM) {
+      const uint32_t off = static_cast<uint32_t>(msrc[(p + DB) % RS]) * (C_SRC * 2) + kq * 16;
 #pragma unroll
-    for (int sh = 1; sh < 64; sh <<= 1) {
-      const int y = __shfl_up(incl, sh, 64);
-      incl += lane >= sh ? y : 0;
+      for (int kb = 0; kb < KB; ++kb)
+        xs[(p + DB) % RB][kb] =
+            __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(xr, static_cast<int>(off + kb * 64), 0, 0));
     }
-    const int gfirst = incl - ng;
-    const int G = __builtin_amdgcn_readlane(incl, 63);
-    const int64_t ebase = t * static_cast<int64_t>(kvol) * kR;
-    // offset of group g (wave-uniform g < G): the offsets whose groups all
-    // come before g, counted
-    auto offset_of = [&](int g) -> int {
-      return __builtin_popcountll(__ballot(lane < kvol && incl <= g));
-    };
-    // valid lanes of group g: pairs left in its offset past 16 per earlier group
-    auto live_of = [&](int g, int o) -> int {
-      const int c = __builtin_amdgcn_readlane(cnt, o), f = __builtin_amdgcn_readlane(gfirst, o);
-      return c - 16 * (g - f);
-    };
-
-    // Register rings indexed by group mod 8 (compile-time positions):
-    // source row and slot of each lane (loaded DM groups ahead), the fetched
-    // source rows (DB groups ahead), and the group's offset and live lane
-    // count (decoded when its rows are fetched).
-    int32_t msrc[kRingM];
-    int32_t mslot[kRingM];
-    Frag xs[kRingB][KB];
-    int ro[kRingB], rl[kRingB];
-    Frag af[MW][KB];
-    int o_cur = -1;
-
-    auto step = [&](int v, auto pc) {
-      constexpr int p = decltype(pc)::v;
-      // slots and source rows of group v + DM
-      {
-        const int g = v + kDM;
-        const bool ok = g >= 0 && g < G;
-        const int64_t e = ebase + (ok ? 16 * g : 0) + col;
-        msrc[(p + kDM) % kRingM] = a.gsrc[e];
-        mslot[(p + kDM) % kRingM] = a.gslot[e];
-      }
-      // source rows of group v + DB, fetched into MFMA operands (absent rows
-      // read out of range: zeros, no memory access)
-      {
-        const int g = v + kDB;
-        int o = 0, live = 0;
-        if (g >= 0 && g < G) {  // wave-uniform
-          o = offset_of(g);
-          live = live_of(g, o);
-        }
-        ro[(p + kDB) % kRingB] = o;
-        rl[(p + kDB) % kRingB] = live;
-        const int32_t s = msrc[(p + kDB) % kRingM];
-        const uint32_t off = col < live ? static_cast<uint32_t>(s * c_src + kq * 8) * 2u : 0x80000000u;
+    if constexpr (!FIRST || p + DM >= RM) {
+      const int g = v0 + p + DM;
+      int sg = g + gbase;
+      sg = sg >= G ? sg - G : sg;
+      sg = g < G ? sg : 0;
+      msrc[(p + DM) % RS] = __builtin_bit_cast(int32_t, __builtin_amdgcn_raw_buffer_load_b32(er_src, 4 * col, 64 * sg, 0));
+      mslot[(p + DM) % RM] = __builtin_amdgcn_raw_buffer_load_b32(er_slot, col & ~3, 16 * sg, 0);
+    }
+    if constexpr (FIRST) return;
+    const int v = v0 + p;
+    if (v >= G) return;  // wave-uniform
+    if (v >= e_cur) {  // wave-uniform: the first group of the next step the tile has
+      const int k_new = __builtin_ctzll(present & (~0ull << (k_cur + 1)));
+      e_cur = __builtin_amdgcn_readlane(incl, k_new);
+      for (int k = k_cur + 1; k <= k_new; ++k) bare_barrier();
+      k_cur = k_new;
+      const char* sl = lds + (k_new % kSlots) * SLICE;
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-          xs[(p + kDB) % kRingB][kb] =
-              __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(xr, static_cast<int>(off + kb * 64), 0, 0));
-      }
-      if (v < 0 || v >= G) return;  // wave-uniform
-      const int o = ro[p % kRingB];
-      const bool live = col < rl[p % kRingB];
-      const int slot = mslot[p % kRingM];
-      // the accumulator rows of this group, read before the operands are
-      // needed: they enter the MFMAs as the C operand
-      f32x4 acc[MW];
-      char* arow = accb + slot * (NCH * 16);
+      for (int mb = 0; mb < MH; ++mb)
 #pragma unroll
-      for (int mb = 0; mb < MW; ++mb)
-        acc[mb] = live ? *reinterpret_cast<const f32x4*>(arow + chunk_swz(slot, 4 * mb + kq, NCH) * 16)
-                       : f32x4{0.f, 0.f, 0.f, 0.f};
-      if (o != o_cur) {  // wave-uniform: this offset's fragments from the resident weights
-        o_cur = o;
-        const char* sl = ldsb + o * WSLICE;
-#pragma unroll
-        for (int mb = 0; mb < MW; ++mb)
-#pragma unroll
-          for (int kb = 0; kb < KB; ++kb) {
-            if constexpr (WM == 0) {
-              const char* s2 = sl + kb * 32 * WROW;
-              af[mb][kb] = __builtin_bit_cast(Frag, lds_tr_frag(s2 + tr_b0 + ((mb * 32) ^ tr_x0),
-                                                                s2 + tr_b4 + ((mb * 32) ^ tr_x4)));
-            } else {
-              const int nl = 16 * mb + col;
-              const int c = chunk_swz(nl, 4 * kb + kq, C_SRC / 8 < 16 ? C_SRC / 8 : 16);
-              af[mb][kb] = __builtin_bit_cast(Frag, *reinterpret_cast<const u32x4*>(sl + nl * WROW + 16 * c));
-            }
+        for (int kb = 0; kb < KB; ++kb) {
+          const int mg = MH * h + mb;  // block of the slice
+          if constexpr (WM == 0) {
+            const char* s2 = sl + kb * 32 * WROW;
+            af[mb][kb] = __builtin_bit_cast(Frag, lds_tr_frag(s2 + tr_b0 + ((mg * 32) ^ tr_x0),
+                                                              s2 + tr_b4 + ((mg * 32) ^ tr_x4)));
+          } else {
+            const int nl = 16 * mg + col;
+            const int c = chunk_swz(nl, 4 * kb + kq, C_SRC / 8 < 16 ? C_SRC / 8 : 16);
+            af[mb][kb] = __builtin_bit_cast(Frag, *reinterpret_cast<const u32x4*>(sl + nl * WROW + 16 * c));
           }
-      }
-#pragma unroll
-      for (int mb = 0; mb < MW; ++mb) {
-        f32x4 d = acc[mb];
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) d = FMfma<T>::run(af[mb][kb], xs[p % kRingB][kb], d);
-        if (live) *reinterpret_cast<f32x4*>(arow + chunk_swz(slot, 4 * mb + kq, NCH) * 16) = d;
-      }
-    };
-
-    // virtual groups v = -16 .. G-1 in rounds of 16 (the ring positions are
-    // compile-time), the first round only issuing loads; a tile without
-    // pairs only writes zeros
-    if (G > 0) {
-      for (int v0 = -16; v0 < G; v0 += 16) {
-        step(v0 + 0, Fi<0>{});
-        step(v0 + 1, Fi<1>{});
-        step(v0 + 2, Fi<2>{});
-        step(v0 + 3, Fi<3>{});
-        step(v0 + 4, Fi<4>{});
-        step(v0 + 5, Fi<5>{});
-        step(v0 + 6, Fi<6>{});
-        step(v0 + 7, Fi<7>{});
-        step(v0 + 8, Fi<8>{});
-        step(v0 + 9, Fi<9>{});
-        step(v0 + 10, Fi<10>{});
-        step(v0 + 11, Fi<11>{});
-        step(v0 + 12, Fi<12>{});
-        step(v0 + 13, Fi<13>{});
-        step(v0 + 14, Fi<14>{});
-        step(v0 + 15, Fi<15>{});
-      }
+        }
     }
+    // the group's accumulator rows (the pad sink included) enter the MFMAs
+    // as the C operand and are written back
+    const uint32_t slot = (mslot[p % RM] >> slot_shift) & 0xffu;
+    const uint32_t abase = static_cast<uint32_t>(acc_off) + slot * (NCH * 16) +
+                           16u * (static_cast<uint32_t>(kq) ^ ((slot / SW_PER) & SW_MASK));
+    f32x4 acc[MH];
+#pragma unroll
+    for (int mb = 0; mb < MH; ++mb) acc[mb] = *reinterpret_cast<const f32x4*>(lds + (abase ^ (64u * mb)));
+#pragma unroll
+    for (int mb = 0; mb < MH; ++mb) {
+      f32x4 d = acc[mb];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) d = FMfma<T>::run(af[mb][kb], xs[p % RB][kb], d);
+      *reinterpret_cast<f32x4*>(lds + (abase ^ (64u * mb))) = d;
+    }
+  };
+  auto round = [&](int v0, auto firstc) { Unroll<RM>::run([&](auto pc) { step(v0, pc, firstc); }); };
 
-    // write the tile's rows once (rows at or past the device count are not
-    // written); lane l takes accumulator chunks l, l + 64, ...
-    for (int it = 0; it < kR * NCH / 64; ++it) {
-      const int i = it * 64 + lane;
+  // groups in rounds of RM (the ring positions are compile-time): a first
+  // round of loads only (entries of groups 0..DM-1, rows of groups
+  // 0..DB-1), then rounds that each compute RM groups
+  if (G > 0) {
+    round(-RM, Fi<1>{});
+    for (int v0 = 0; v0 < G; v0 += RM) round(v0, Fi<0>{});
+  }
+  // the barriers of the steps past the tile's last one
+  for (int k = k_cur + 1; k < kvol; ++k) bare_barrier();
+  if (!has_tile) return;
+
+  // write the tile's rows once (rows at or past the device count are not
+  // written); lane l takes accumulator chunks l, l + 64, ..., read eight at
+  // a time before they are stored
+  const int64_t n_dest = a.n_dest ? (*a.n_dest < a.n_dest_cap ? *a.n_dest : a.n_dest_cap) : a.n_dest_cap;
+  const int64_t left = n_dest - t * kR;
+  const int rows = static_cast<int>(left < kR ? (left > 0 ? left : 0) : kR);
+  constexpr int ITS = kR * NCH / 64;
+  constexpr int UN = ITS < 8 ? ITS : 8;
+  for (int it0 = 0; it0 < ITS; it0 += UN) {
+    f32x4 v[UN];
+#pragma unroll
+    for (int u = 0; u < UN; ++u) {
+      const int i = (it0 + u) * 64 + lane;
       const int r = i / NCH, c = i - r * NCH;
-      const int64_t row = t * kR + r;
-      const int n = n0 + 4 * c;
-      if (row < n_dest && n < a.c_dst) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(accb + (r * NCH + chunk_swz(r, c, NCH)) * 16);
-        store4(a.dst, a.out_dtype, row * a.c_dst + n, v);
-      }
+      v[u] = *reinterpret_cast<const f32x4*>(accb + (r * NCH + chunk_swz(r, c, NCH)) * 16);
+    }
+#pragma unroll
+    for (int u = 0; u < UN; ++u) {
+      const int i = (it0 + u) * 64 + lane;
+      const int r = i / NCH, c = i - r * NCH;
+      const int n = nw0 + 4 * c;
+      if (r < rows && n < a.c_dst) store4(a.dst, a.out_dtype, (t * kR + r) * a.c_dst + n, v[u]);
     }
   }
 }
 
-int fod_cu_count() {
-  static int n[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (n[dev] == 0) {
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
-    n[dev] = v;
-  }
-  return n[dev];
-}
-
-// LDS bytes of the resident weights of one column of 16 * mw channels.
-size_t fod_weight_bytes(int kvol, int c_src, int mw) { return static_cast<size_t>(kvol) * c_src * 16 * mw * 2; }
-
-// Column width (MFMA blocks of 16 channels per column) and waves per block:
-// the widest column whose weights leave room for at least eight waves'
-// accumulators, else the narrowest that leaves room for two; 0 when even
-// that does not fit.
-void fod_shape(int kvol, int c_src, int c_dst, int* mw_out, int* nw_out) {
-  *mw_out = 0;
-  *nw_out = 0;
-  const size_t lds = static_cast<size_t>(kLdsChunks) * 16;
-  for (int mw = 2; mw >= 1; mw >>= 1) {
-    if (mw == 2 && c_dst < 32) continue;
-    const int max_nw = fod_max_waves(c_src / 32, mw);
-    const size_t wb = fod_weight_bytes(kvol, c_src, mw);
-    if (wb >= lds) continue;
-    const size_t accw = static_cast<size_t>(kR) * 16 * mw * 4;
-    int nw = static_cast<int>((lds - wb) / accw);
-    if (nw > max_nw) nw = max_nw;
-    if (nw >= 6 || (mw == 1 && nw >= 2)) {
-      *mw_out = mw;
-      *nw_out = nw;
-      return;
-    }
-  }
-}
+// Column width in MFMA blocks of 16 output channels.
+int fod_mw(int c_dst) { return c_dst > 32 ? 4 : (c_dst > 16 ? 2 : 1); }
 
 template <typename T, int KB, int MW>
-hipError_t launch_kb_mw(FodK k, int wm, int nw, hipStream_t s) {
-  const int ncu = fod_cu_count();
+hipError_t launch_kb_mw(FodK k, int wm, hipStream_t s) {
+  constexpr int MH = MW >= 2 ? 2 : 1;  // two compute waves per tile for 64-channel columns
+  constexpr int NT = fod_tiles(KB, MW, MH);
+  constexpr int NW = NT * (MW / MH);
+  static_assert(NT >= 1, "a tile fits");
   k.ncol = ceil_div(k.c_dst, 16 * MW);
-  int nsub = ncu / (8 * k.ncol);
-  if (nsub < 1) nsub = 1;
-  const int64_t per_xcd = ceil_div<int64_t>(k.n_gtiles, 8);
-  if (nsub > per_xcd) nsub = static_cast<int>(per_xcd > 0 ? per_xcd : 1);
-  k.nsub = nsub;
-  k.acc_base = static_cast<int>(fod_weight_bytes(k.kvol, k.c_src, MW) / 16);
-  const dim3 grid(static_cast<unsigned>(8 * k.ncol * nsub));
+  k.nblk = ceil_div<int64_t>(k.n_gtiles, NT);
+  k.nb8 = ceil_div<int64_t>(k.nblk, 8);
+  const int64_t blocks = 8 * k.nb8 * k.ncol;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(blocks));
   if (wm == 0)
-    k_fod<T, KB, MW, 0><<<grid, nw * 64, 0, s>>>(k);
+    k_fod<T, KB, MW, MH, 0><<<grid, (NW + 1) * 64, 0, s>>>(k);
   else
-    k_fod<T, KB, MW, 1><<<grid, nw * 64, 0, s>>>(k);
+    k_fod<T, KB, MW, MH, 1><<<grid, (NW + 1) * 64, 0, s>>>(k);
   return hipGetLastError();
 }
 
 template <typename T, int KB>
-hipError_t launch_kb(const FodK& k, int mw, int wm, int nw, hipStream_t s) {
-  if (mw == 2) return launch_kb_mw<T, KB, 2>(k, wm, nw, s);
-  return launch_kb_mw<T, KB, 1>(k, wm, nw, s);
+hipError_t launch_kb(const FodK& k, int wm, hipStream_t s) {
+  switch (fod_mw(k.c_dst)) {
+    case 4: return launch_kb_mw<T, KB, 4>(k, wm, s);
+    case 2: return launch_kb_mw<T, KB, 2>(k, wm, s);
+    default: return launch_kb_mw<T, KB, 1>(k, wm, s);
+  }
 }
 
 template <typename T>
-hipError_t launch_t(const FodK& k, int mw, int wm, int nw, hipStream_t s) {
+hipError_t launch_t(const FodK& k, int wm, hipStream_t s) {
   switch (k.c_src / 32) {
-    case 1: return launch_kb<T, 1>(k, mw, wm, nw, s);
-    case 2: return launch_kb<T, 2>(k, mw, wm, nw, s);
-    case 3: return launch_kb<T, 3>(k, mw, wm, nw, s);
-    default: return launch_kb<T, 4>(k, mw, wm, nw, s);
+    case 1: return launch_kb<T, 1>(k, wm, s);
+    case 2: return launch_kb<T, 2>(k, wm, s);
+    case 3: return launch_kb<T, 3>(k, wm, s);
+    default: return launch_kb<T, 4>(k, wm, s);
   }
 }
 
 }  // namespace
 
 bool fod_supported(int kvol, int64_t n_src, int c_src, int c_dst, ts_dtype in_dtype) {
-  if (in_dtype == TS_F32 || kvol < 1 || c_src % 32 != 0 || c_src < 32 || c_src > 128 || c_dst % 16 != 0 ||
-      c_dst < 16)
+  if (in_dtype == TS_F32 || kvol < 1 || kvol > TS_MAX_KVOL || c_src % 32 != 0 || c_src < 32 || c_src > 128 ||
+      c_dst % 16 != 0 || c_dst < 16)
     return false;
-  if (n_src * c_src * 2 >= (int64_t{1} << 31)) return false;
-  int mw, nw;
-  fod_shape(kvol, c_src, c_dst, &mw, &nw);
-  return mw > 0;
+  return n_src * c_src * 2 < (int64_t{1} << 31);
 }
 
 hipError_t launch_fod(const ConvArgs& a, hipStream_t s) {
   const ts_rel& rel = *a.rel;
   if (rel.n_gtiles == 0) return hipSuccess;
-  int mw, nw;
-  fod_shape(a.kvol, a.c_src, a.c_dst, &mw, &nw);
-  if (mw == 0) return hipErrorInvalidValue;
+  if (!fod_supported(a.kvol, a.n_src, a.c_src, a.c_dst, a.in_dtype)) return hipErrorInvalidValue;
   FodK k;
   k.gcount = rel.gcount;
   k.gsrc = rel.gsrc;
@@ -513,11 +555,11 @@ hipError_t launch_fod(const ConvArgs& a, hipStream_t s) {
   k.c_dst = a.c_dst;
   k.out_dtype = a.out_dtype;
   k.ncol = 1;
-  k.nsub = 1;
-  k.acc_base = 0;
+  k.nblk = 0;
+  k.nb8 = 0;
   const int wm = a.transpose ? 1 : 0;
-  if (a.in_dtype == TS_F16) return launch_t<_Float16>(k, mw, wm, nw, s);
-  return launch_t<__bf16>(k, mw, wm, nw, s);
+  if (a.in_dtype == TS_F16) return launch_t<_Float16>(k, wm, s);
+  return launch_t<__bf16>(k, wm, s);
 }
 
 }  // namespace ts

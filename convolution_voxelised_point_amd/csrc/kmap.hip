@@ -352,6 +352,18 @@ __device__ __forceinline__ void emit_groups(const RelK& a, int kvol, uint64_t ma
     a.gsrc[ebase + pos] = nb(o);
     a.gslot[ebase + pos] = slot;
   }
+  // the pad entries that complete each offset's last group: no source row
+  // and the sink slot TS_GTILE
+  for (int idx = threadIdx.x & 127; idx < kvol * 16; idx += 128) {
+    const int o = idx >> 4, k = idx & 15;
+    const int c = gw[2 * h][o] + gw[2 * h + 1][o];
+    const int rem = c & 15;
+    if (rem != 0 && k >= rem) {
+      const int64_t e = ebase + gstart[h][o] + (c - rem) + k;
+      a.gsrc[e] = -1;
+      a.gslot[e] = static_cast<uint8_t>(TS_GTILE);
+    }
+  }
 }
 
 // Pass 1: one lane per destination row in index order.  Writes the row's

@@ -256,8 +256,9 @@ ts_status ts_devoxelize(const int32_t* vox_of, int64_t n, const void* vox_feats,
  * at offset o.  Inside the tile, offset o's pairs are listed in destination
  * order (gslot = destination row - t * TS_GTILE, gsrc = its source row),
  * starting at entry 16 * sum_{o' < o} ceil(gcount[t*kvol + o'] / 16): each
- * offset's run is padded to whole groups of 16 (padding entries are not
- * written), so group g of the tile is entries [16g, 16g + 16).
+ * offset's run is padded to whole groups of 16 (padding entries hold
+ * gsrc = -1 and gslot = TS_GTILE), so group g of the tile is entries
+ * [16g, 16g + 16).  Entries past a tile's last group are not written.
  * ---------------------------------------------------------------------- */
 typedef struct ts_rel {
   int64_t n_dest_cap;    /* destination rows, upper bound (host)               */

@@ -37,11 +37,12 @@ def build(ts, coords, ksize, stride, flags, target=None):
 
 
 def check_group_layout(arrs, kvol, n_dest):
-    """Runs in destination order, padded starts, counts summing to the rows'
-    mask bits."""
+    """Runs in destination order, padded starts, pads that name no source row
+    and the sink slot, counts summing to the rows' mask bits."""
     from convolution_voxelised_point_amd import ts
     cnt = arrs["gcount"].cpu().numpy().reshape(-1, kvol).astype(np.int64)
     slot = arrs["gslot"].cpu().numpy().reshape(cnt.shape[0], -1).astype(np.int64)
+    src = arrs["gsrc"].cpu().numpy().reshape(cnt.shape[0], -1)
     assert (cnt >= 0).all() and (cnt <= ts.TS_GTILE).all()
     start = np.zeros_like(cnt)
     start[:, 1:] = np.cumsum((cnt[:, :-1] + 15) // 16 * 16, axis=1)
@@ -50,6 +51,9 @@ def check_group_layout(arrs, kvol, n_dest):
         s = slot[t, start[t, o]:start[t, o] + cnt[t, o]]
         assert (np.diff(s) > 0).all(), "a run is not in destination order"
         assert (t * ts.TS_GTILE + s < n_dest).all()
+        end = start[t, o] + (cnt[t, o] + 15) // 16 * 16
+        assert (src[t, start[t, o] + cnt[t, o]:end] == -1).all(), "a pad names a source row"
+        assert (slot[t, start[t, o] + cnt[t, o]:end] == ts.TS_GTILE).all(), "a pad misses the sink slot"
     rm = arrs["row_mask"].cpu().numpy().view(np.uint64)[:n_dest]
     bits = np.array([bin(int(m)).count("1") for m in rm], np.int64)
     assert bits.sum() == cnt.sum()
