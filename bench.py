@@ -46,8 +46,8 @@ from convolution_voxelised_point_amd import synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_F16_PEAK_TFLOPS = 2500.0  # dense fp16/bf16 MFMA
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_igemm_ring_scan_c64_traffic.txt")
-IGEMM_SOURCE = os.path.join(ROOT, "convolution_voxelised_point_amd", "csrc", "igemm.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_fod_ring_scan_c64_traffic.txt")
+FOD_SOURCE = os.path.join(ROOT, "convolution_voxelised_point_amd", "csrc", "fod.hip")
 COLD_SCRATCH_MIB = 512         # written between cold steps: twice the last-level cache
 COLD_STEPS = 20
 TRIALS = 5
@@ -492,10 +492,14 @@ def measure_lidar(ts, steps, warmup):
     ms_cold, st_cold = run_cold(s.fns, s.names, COLD_STEPS)
     conv_b2b = back_to_back_us(s.fns[-1], steps)
     n, cap = s.n, s.table.cap
-    P = popcount_sum(s.kmap.rel_arrays("fwd")["row_mask"][:n], 27)
+    rel = s.kmap.rel_arrays("fwd")
+    P = popcount_sum(rel["row_mask"][:n], 27)
     cin, cout, kvol, e = w.cin, w.cout, 27, 2
     flop = 2.0 * P * cin * cout
-    conv_bytes = n * cin * e + kvol * cin * cout * e + P * 4 + n * 4 + n * cout * e
+    # fetch-on-demand forward: source rows, weights, the pairs' source rows
+    # and slots (4 + 1 bytes), the per-tile group counts, the output rows
+    n_gtiles = int(s.kmap.s.fwd.n_gtiles)
+    conv_bytes = n * cin * e + kvol * cin * cout * e + P * 5 + n_gtiles * kvol * 4 + n * cout * e
     kmap_bytes = n * 16 + cap * 12 + P * 8 + n * 8
     hash_bytes = n * 16 + cap * 12
     conv_s = st["conv"] * 1e-6
@@ -678,8 +682,9 @@ def measure_train(ts, steps, warmup):
 
 
 def measured_traffic():
-    """HBM bytes per implicit-GEMM launch from the committed rocprofv3 counter
-    runs, or None when the kernel source changed since they were taken."""
+    """HBM bytes per fetch-on-demand launch from the committed rocprofv3
+    counter runs, or None when the kernel source changed since they were
+    taken."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     rec = {}
@@ -687,7 +692,7 @@ def measured_traffic():
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             rec[k.strip()] = v.strip()
-    digest = hashlib.sha256(open(IGEMM_SOURCE, "rb").read()).hexdigest()[:16]
+    digest = hashlib.sha256(open(FOD_SOURCE, "rb").read()).hexdigest()[:16]
     if rec.get("source_sha256_16") != digest or "hbm_bytes_per_launch" not in rec:
         return None
     return float(rec["hbm_bytes_per_launch"])
@@ -823,7 +828,7 @@ def main():
         "kmap_hbm_frac": r["kmap_gbs"] / HBM_PEAK_GBS,
         "stages_us": r["stages_us"],
         "stages_us_cold": r["stages_us_cold"],
-        "roofline": {"bound": "hbm", "kernel": "SubmConv3d forward call (k_igemm, weights read from w as stored)",
+        "roofline": {"bound": "hbm", "kernel": "SubmConv3d forward call (k_fod: fetch-on-demand over pair groups)",
                      "achieved": r["fwd_alg_bytes"] / conv_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": r["fwd_alg_bytes"] / conv_s / 1e9 / HBM_PEAK_GBS, "traffic": measured_traffic(),
                      "alg_bytes_per_launch": r["fwd_alg_bytes"], "launch_us": r["stages_us"]["conv"],
