@@ -436,16 +436,19 @@ def setup_up(ts, w, out_dtype=None) -> Step:
                 fine_table=fine_table, gen=gen, yg=yg, flags=flags, n=n)
 
 
-def setup_train(ts, w, out_dtype=None) -> Step:
+def setup_train(ts, w, out_dtype=None, kmap_flags=None) -> Step:
     """bf16 128 -> 128 training step: hash, kernel map (+pairs), forward,
-    dgrad (mirrored offsets), wgrad (fp32 dW)."""
+    dgrad (mirrored offsets), wgrad (fp32 dW).  By default the map is a
+    neighbour table with tiles sorted by offset mask (the implicit GEMM: at
+    128 output channels it beats the fetch-on-demand kernel, which needs two
+    column passes); kmap_flags adds e.g. pair groups without the table."""
     dev = torch.device("cuda")
     coords = torch.from_numpy(w.coords).to(dev)
     x, wt, dy = w.x.to(dev), w.w.to(dev), w.dy.to(dev)
     n = coords.shape[0]
     flags = torch.zeros(1, dtype=torch.int32, device=dev)
     table = ts.HashTable(coords, 2.0, build=False)
-    fk = ts.TS_KMAP_PAIRS
+    fk = ts.TS_KMAP_PAIRS | (0 if kmap_flags is None else kmap_flags)
     kbuf = torch.empty(ts.ts_kmap_bytes(n, n, 3, 3, 1, fk), dtype=torch.uint8, device=dev)
     km = ts.TsKmap()
     y = torch.empty((n, 128), dtype=out_dtype or torch.bfloat16, device=dev)
@@ -667,18 +670,31 @@ def measure_pixels(ts, steps, warmup):
 
 
 def measure_train(ts, steps, warmup):
+    """The training step with its default map (a neighbour table sorted by
+    offset mask: the implicit GEMM) and, for comparison, with pair groups
+    only (the fetch-on-demand forward and dgrad)."""
     w = synth.make("train")
-    s = setup_train(ts, w)
-    ms_eager, st = run_steps(s.fns, s.names, steps, warmup)
-    ms, _ = run_graph(capture(s.fns), steps, warmup)
-    P = popcount_sum(s.kmap.rel_arrays("fwd")["row_mask"][:s.n], 27)
-    flop = 2.0 * P * 128 * 128
-    return {"workload": "train", "n": s.n, "pairs": P, "ms_per_step": ms, "ms_per_step_eager": ms_eager,
-            "stages_us": {k: round(v, 3) for k, v in st.items()},
-            "fwd_tflops": flop / (st["fwd"] * 1e-6) / 1e12,
-            "dgrad_tflops": flop / (st["dgrad"] * 1e-6) / 1e12,
-            "wgrad_tflops": flop / (st["wgrad"] * 1e-6) / 1e12,
-            "step_tflops": 3 * flop / (ms * 1e-3) / 1e12}
+    out = {"workload": "train"}
+    for name, flags in (("implicit_gemm_sorted", None),
+                        ("fetch_on_demand", ts.TS_KMAP_GROUPS | ts.TS_KMAP_NO_TABLE)):
+        s = setup_train(ts, w, kmap_flags=flags)
+        ms_eager, st = run_steps(s.fns, s.names, steps, warmup)
+        ms, _ = run_graph(capture(s.fns), steps, warmup)
+        P = popcount_sum(s.kmap.rel_arrays("fwd")["row_mask"][:s.n], 27)
+        flop = 2.0 * P * 128 * 128
+        rec = {"ms_per_step": ms, "ms_per_step_eager": ms_eager,
+               "stages_us": {k: round(v, 3) for k, v in st.items()},
+               "fwd_tflops": flop / (st["fwd"] * 1e-6) / 1e12,
+               "dgrad_tflops": flop / (st["dgrad"] * 1e-6) / 1e12,
+               "wgrad_tflops": flop / (st["wgrad"] * 1e-6) / 1e12,
+               "step_tflops": 3 * flop / (ms * 1e-3) / 1e12}
+        out["n"], out["pairs"] = s.n, P
+        if flags is None:
+            out.update(rec)
+        else:
+            out[name] = rec
+        del s
+    return out
 
 
 def measured_traffic():

@@ -19,8 +19,8 @@
 // two waves per SIMD to overlap each other's waits), and one loader wave; a
 // block column covers up to 64 output channels.  The block steps through the
 // offsets in lockstep: barrier k means that step k's weights sit in LDS (a
-// ring of three slices, written by the loader wave from registers it fills
-// several steps ahead) and that every compute wave is done with the
+// ring of three slices, loaded by the loader wave two steps ahead with
+// direct global-to-LDS copies) and that every compute wave is done with the
 // steps before k.  Step k takes offset (k + rot) mod kvol, rot set by the
 // block, so that blocks running at once copy different weight slices.  A
 // compute wave passes the barriers of the steps its tile lacks without
@@ -153,6 +153,21 @@ __device__ __forceinline__ u32x4 lds_tr_frag(const char* p0, const char* p4) {
   return u32x4{l[0], l[1], h[0], h[1]};
 }
 
+// 16 bytes per lane from global memory straight into LDS: lane l writes
+// dst + 16 l (dst is wave-uniform).  Completion is counted by the
+// vector-memory counter.  Not a template: clang emits no host launch stub for
+// a kernel template whose body names this builtin directly.
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+__device__ __forceinline__ void lds_copy16(const void* src, void* dst) {
+  __builtin_amdgcn_global_load_lds(static_cast<const u32x4*>(src), (lds_u32x4*)dst, 16, 0, 0);
+}
+// Waits until at most N vector-memory operations of this wave are
+// outstanding (they retire in issue order); other counters unconstrained.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | 0x70 | 0xF00 | ((N >> 4) << 14));
+}
 // All of this wave's LDS operations have completed.
 __device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 // Workgroup barrier with no memory fence: each wave states the waits it
@@ -249,14 +264,13 @@ __global__ __launch_bounds__(64 * (fod_tiles(KB, MW, MH) * (MW / MH) + 1)) void 
   const int rot = static_cast<int>(tb % kvol);
 
   if (wave == NW) {
-    // Loader: step k's weights into slot k % 3 before barrier k, staged in
-    // registers LD steps ahead (the copy of a slice takes longer than a step).
-    // Chunk p of a slot (16 bytes): forward layout row ci = p / (CB/8) at
-    // swizzled column, dgrad layout row nl = p / (C_SRC/8) likewise; chunks
-    // of output channels past c_dst copy a valid chunk of the slice (they
-    // feed accumulator channels that are never written out).  Slot k % 3
-    // last held step k - 3, which every wave is past once barrier k - 1 is.
-    constexpr int LD = KB <= 2 && WM == 0 ? 4 : 2;
+    // Loader: step k's weights into slot k % 3, two steps ahead of the
+    // compute waves, with direct global-to-LDS copies (element by element
+    // through registers when the weights are not 16-byte aligned).  Chunk p
+    // of a slot (16 bytes): forward layout row ci = p / (CB/8) at swizzled
+    // column, dgrad layout row nl = p / (C_SRC/8) likewise; chunks of output
+    // channels past c_dst copy a valid chunk of the slice (they feed
+    // accumulator channels that are never written out).
     const T* w = static_cast<const T*>(a.w);
     auto chunk_src = [&](int os, int p) -> int64_t {
       if constexpr (WM == 0) {
@@ -271,41 +285,40 @@ __global__ __launch_bounds__(64 * (fod_tiles(KB, MW, MH) * (MW / MH) + 1)) void 
         return (static_cast<int64_t>(os) * a.c_dst + (n < a.c_dst ? n : 0)) * C_SRC + 8 * part;
       }
     };
-    u32x4 st[LD][COPIES];
-    auto fetch = [&](int k, u32x4 (&r)[COPIES]) {
+    auto copy = [&](int k) {
       const int o = k + rot < kvol ? k + rot : k + rot - kvol;
       const int os = a.mirror ? kvol - 1 - o : o;
+      char* slot = lds + (k % kSlots) * SLICE;
       if (a.w_vec) {
 #pragma unroll
-        for (int j = 0; j < COPIES; ++j) r[j] = *reinterpret_cast<const u32x4*>(w + chunk_src(os, 64 * j + lane));
-      } else {  // unaligned weights: element by element
-#pragma unroll
+        for (int j = 0; j < COPIES; ++j) lds_copy16(w + chunk_src(os, 64 * j + lane), slot + 1024 * j);
+      } else {
         for (int j = 0; j < COPIES; ++j) {
           const T* g = w + chunk_src(os, 64 * j + lane);
+          u32x4 v;
 #pragma unroll
           for (int q = 0; q < 4; ++q)
-            r[j][q] = static_cast<unsigned>(__builtin_bit_cast(unsigned short, g[2 * q])) |
-                      (static_cast<unsigned>(__builtin_bit_cast(unsigned short, g[2 * q + 1])) << 16);
+            v[q] = static_cast<unsigned>(__builtin_bit_cast(unsigned short, g[2 * q])) |
+                   (static_cast<unsigned>(__builtin_bit_cast(unsigned short, g[2 * q + 1])) << 16);
+          *reinterpret_cast<u32x4*>(slot + 1024 * j + 16 * lane) = v;
         }
       }
     };
-    Unroll<LD>::run([&](auto jc) {
-      constexpr int j = decltype(jc)::v;
-      if (j < kvol) fetch(j, st[j]);
-    });
-    for (int k0 = 0; k0 < kvol; k0 += LD) {
-      Unroll<LD>::run([&](auto jc) {
-        constexpr int j = decltype(jc)::v;
-        const int k = k0 + j;
-        if (k < kvol) {  // wave-uniform
-          char* slot = lds + (k % kSlots) * SLICE;
-#pragma unroll
-          for (int c = 0; c < COPIES; ++c) *reinterpret_cast<u32x4*>(slot + 1024 * c + 16 * lane) = st[j][c];
-          wait_lds();
-          bare_barrier();
-          if (k + LD < kvol) fetch(k + LD, st[j]);
-        }
-      });
+    copy(0);
+    if (kvol > 1) copy(1);
+    for (int k = 0; k < kvol; ++k) {
+      // step k's weights have landed (only step k + 1's copies may still be
+      // in flight)
+      if (a.w_vec) {
+        if (k + 1 < kvol)
+          wait_vm<COPIES>();
+        else
+          wait_vm<0>();
+      } else {
+        wait_lds();
+      }
+      bare_barrier();
+      if (k + 2 < kvol) copy(k + 2);  // into the slot of step k - 1: every wave is past it
     }
     return;
   }

@@ -187,18 +187,25 @@ def test_full_pixels_two_layers(ts, dataflow):
     assert_feature_close(y2, ref2, torch.float16, f"pixels layer 2 ({dataflow}) fp32 out")
 
 
-def test_full_train_bf16(ts):
+@pytest.mark.parametrize("order", ["groups", "sorted"])
+def test_full_train_bf16(ts, order):
     """The 128-channel bf16 training step on four scenes: forward, dgrad and
-    all 27 offsets of wgrad over every element."""
+    all 27 offsets of wgrad over every element, with the default map (a
+    neighbour table sorted by offset mask: the implicit GEMM) and with pair
+    groups only (the fetch-on-demand kernels)."""
     w = synth.make("train")
-    s = bench.setup_train(ts, w)
+    flags = (ts.TS_KMAP_GROUPS | ts.TS_KMAP_NO_TABLE) if order == "groups" else None
+    s = bench.setup_train(ts, w, kmap_flags=flags)
     s.run_once()
     assert int(s.flags.item()) == 0
     check_hash(ts, s, w.coords, 41)
     tr = oracle.kmap(w.coords, w.coords, 3, 1)
     check_triples(s.kmap, tr, 27, "train")
     rel = s.kmap.rel_arrays("fwd")
-    check_window_sorted(rel["tile_rows"].cpu().numpy(), rel["row_mask"].cpu().numpy().view(np.uint64)[:w.n])
+    if order == "groups":
+        assert "nbr" not in rel and "gcount" in rel
+    else:
+        check_window_sorted(rel["tile_rows"].cpu().numpy(), rel["row_mask"].cpu().numpy().view(np.uint64)[:w.n])
     # the per-offset pair lists are the same relation
     ps, pin, pout = s.kmap.pairs()
     off = np.repeat(np.arange(27, dtype=np.int32), np.diff(ps))
@@ -206,13 +213,13 @@ def test_full_train_bf16(ts):
     ref_y = oracle.conv_fwd(tr, w.x, w.w, w.n)
     ref_dx = oracle.conv_dgrad(tr, w.dy, w.w, w.n)
     ref_dw = oracle.conv_wgrad(tr, w.x, w.dy, 27)
-    assert_feature_close(s.y, ref_y, torch.bfloat16, "train fwd bf16 out")
-    assert_feature_close(s.dx, ref_dx, torch.bfloat16, "train dgrad bf16 out")
-    assert_feature_close(s.dw, ref_dw, torch.bfloat16, "train wgrad (27 offsets, fp32 dW)")
+    assert_feature_close(s.y, ref_y, torch.bfloat16, f"train {order} fwd bf16 out")
+    assert_feature_close(s.dx, ref_dx, torch.bfloat16, f"train {order} dgrad bf16 out")
+    assert_feature_close(s.dw, ref_dw, torch.bfloat16, f"train {order} wgrad (27 offsets, fp32 dW)")
     dw0 = s.dw.clone()
     del s
-    s32 = bench.setup_train(ts, w, out_dtype=torch.float32)
+    s32 = bench.setup_train(ts, w, out_dtype=torch.float32, kmap_flags=flags)
     s32.run_once()
-    assert_feature_close(s32.y, ref_y, torch.bfloat16, "train fwd fp32 out")
-    assert_feature_close(s32.dx, ref_dx, torch.bfloat16, "train dgrad fp32 out")
+    assert_feature_close(s32.y, ref_y, torch.bfloat16, f"train {order} fwd fp32 out")
+    assert_feature_close(s32.dx, ref_dx, torch.bfloat16, f"train {order} dgrad fp32 out")
     assert torch.equal(s32.dw, dw0), "wgrad differs between two runs of the same step"
