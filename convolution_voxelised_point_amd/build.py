@@ -34,9 +34,16 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
+def cuid(src: str) -> str:
+    """Fixed compilation-unit id of a source: it names the object's embedded
+    GPU binary, so another host-side build of the same source (the sanitizer
+    build of the tests) can link against that binary."""
+    return "ts_" + os.path.splitext(os.path.basename(src))[0]
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *CFLAGS, f"-cuid={cuid(src)}", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

@@ -236,7 +236,9 @@ ts_status ts_hash_query(const void* table, int64_t cap, int ndim, const int32_t*
   return TS_OK;
 }
 
-size_t ts_support_scratch_bytes(int64_t n_in) { return n_in < 0 ? 0 : support_scratch_bytes(n_in); }
+size_t ts_support_scratch_bytes(int64_t n_in) {
+  return n_in < 0 || n_in > kMaxRows ? 0 : support_scratch_bytes(n_in);
+}
 
 ts_status ts_strided_support(const int32_t* in_coords, int64_t n_in, int ndim, int stride, int32_t* out_coords,
                              int64_t* n_out, void* out_table, int64_t out_cap, void* scratch, size_t scratch_bytes,
@@ -253,8 +255,9 @@ ts_status ts_strided_support(const int32_t* in_coords, int64_t n_in, int ndim, i
 }
 
 size_t ts_generative_scratch_bytes(int64_t n_in, int ndim, int ksize) {
-  if (n_in < 0 || !shape_ok(ndim, ksize, 1)) return 0;
-  return generative_scratch_bytes(n_in * ipow(ksize, ndim));
+  if (n_in < 0 || n_in > kMaxRows || !shape_ok(ndim, ksize, 1)) return 0;
+  const int64_t n_cand = n_in * ipow(ksize, ndim);  // kvol <= 64: no overflow
+  return n_cand > kMaxRows ? 0 : generative_scratch_bytes(n_cand);
 }
 
 namespace {
@@ -293,7 +296,9 @@ ts_status ts_transposed_support(const int32_t* in_coords, int64_t n_in, int ndim
                            out_cap, scratch, scratch_bytes, err_flags, stream);
 }
 
-size_t ts_voxelize_scratch_bytes(int64_t n_points) { return n_points < 0 ? 0 : voxelize_scratch_bytes(n_points); }
+size_t ts_voxelize_scratch_bytes(int64_t n_points) {
+  return n_points < 0 || n_points > kMaxRows ? 0 : voxelize_scratch_bytes(n_points);
+}
 
 ts_status ts_voxelize(const int32_t* batch, const float* pos, int64_t n, int ndim, const float* size,
                       const float* origin, const float* feats, int c, int32_t* out_coords, int64_t* n_out,

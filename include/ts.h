@@ -17,8 +17,10 @@
  * ----------------------------------------
  * - Memory: the caller allocates every device buffer; the library never
  *   allocates device memory.  Size queries (ts_hash_capacity,
- *   ts_hash_table_bytes, ts_kmap_bytes, ts_conv_workspace_bytes) say how
- *   much.  All pointers named "device" must be device memory of the current
+ *   ts_hash_table_bytes, ts_kmap_bytes, ts_conv_workspace_bytes and the
+ *   *_scratch_bytes functions) say how much; for arguments the matching call
+ *   refuses (negative counts, more than 2^31 - 1 rows or candidates,
+ *   unsupported shapes) the byte queries return 0.  All pointers named "device" must be device memory of the current
  *   HIP device; feature matrices are row-major and contiguous.
  * - Streams: every call is asynchronous and ordered on `stream`; there is no
  *   host synchronisation inside the library.  Counts that only the device
@@ -54,14 +56,22 @@
 extern "C" {
 #endif
 
+/* The *_RANGE_MIN_ / *_RANGE_MAX_ enumerators are no values of their own:
+ * they make every int a value of the enum type, so that an out-of-range
+ * value a C caller passes reaches the library's checks (and is refused with
+ * TS_ERR_INVALID_ARG) as a defined value. */
 typedef enum ts_status {
   TS_OK = 0,
   TS_ERR_INVALID_ARG = 1, /* null pointer, negative size, bad shape, short buffer */
   TS_ERR_UNSUPPORTED = 2, /* valid request this library does not implement      */
-  TS_ERR_HIP = 3          /* a HIP launch or runtime call failed                 */
+  TS_ERR_HIP = 3,         /* a HIP launch or runtime call failed                 */
+  TS_STATUS_RANGE_MIN_ = INT32_MIN, TS_STATUS_RANGE_MAX_ = INT32_MAX
 } ts_status;
 
-typedef enum ts_dtype { TS_F32 = 0, TS_F16 = 1, TS_BF16 = 2 } ts_dtype;
+typedef enum ts_dtype {
+  TS_F32 = 0, TS_F16 = 1, TS_BF16 = 2,
+  TS_DTYPE_RANGE_MIN_ = INT32_MIN, TS_DTYPE_RANGE_MAX_ = INT32_MAX
+} ts_dtype;
 
 typedef enum ts_dataflow {
   TS_DATAFLOW_AUTO = 0,          /* per-shape choice                                   */
@@ -69,9 +79,10 @@ typedef enum ts_dataflow {
   TS_DATAFLOW_GATHER_SCATTER = 2, /* per offset: gather, multiply, add into the outputs */
   TS_DATAFLOW_IMPLICIT_GEMM_PACKED = 3, /* implicit GEMM on weights that ts_conv_pack_weights
                                            already wrote into the workspace (w is ignored)  */
-  TS_DATAFLOW_FETCH_ON_DEMAND = 4 /* per-tile pair groups: each group of 16 pairs of one offset
+  TS_DATAFLOW_FETCH_ON_DEMAND = 4, /* per-tile pair groups: each group of 16 pairs of one offset
                                      fetches its source rows inside the MFMA loop and adds into
                                      an on-chip accumulator tile (maps built with TS_KMAP_GROUPS) */
+  TS_DATAFLOW_RANGE_MIN_ = INT32_MIN, TS_DATAFLOW_RANGE_MAX_ = INT32_MAX
 } ts_dataflow;
 
 /* device-detected conditions, ORed into the caller's flag word */

@@ -60,6 +60,7 @@
 // Parity pins: tests/test_oracle_*.py check every function here against dense
 // convolution (torch CPU, fp64), brute-force searches, closed forms and the
 // page's two-voxel example.
+#include <algorithm>
 #include <array>
 #include <cmath>
 #include <cstdint>
@@ -329,7 +330,7 @@ int64_t oracle_kmap(const int32_t* in_coords, int64_t n_in, const int32_t* out_c
 // y[j][co] = sum over triples (i, j, o) and ci of x[i][ci] * w[o][ci][co].
 void oracle_conv_fwd(const int32_t* t_in, const int32_t* t_out, const int32_t* t_off, int64_t n_pairs,
                      const double* x, int cin, const double* w, int cout, double* y, int64_t n_out) {
-  std::memset(y, 0, sizeof(double) * static_cast<size_t>(n_out) * cout);
+  std::fill_n(y, static_cast<size_t>(n_out) * cout, 0.0);
   for (int64_t p = 0; p < n_pairs; ++p) {
     const double* xi = x + static_cast<int64_t>(t_in[p]) * cin;
     const double* wo = w + static_cast<int64_t>(t_off[p]) * cin * cout;
@@ -342,7 +343,7 @@ void oracle_conv_fwd(const int32_t* t_in, const int32_t* t_out, const int32_t* t
 // dx[i][ci] = sum over triples (i, j, o) and co of dy[j][co] * w[o][ci][co].
 void oracle_conv_dgrad(const int32_t* t_in, const int32_t* t_out, const int32_t* t_off, int64_t n_pairs,
                        const double* dy, int cout, const double* w, int cin, double* dx, int64_t n_in) {
-  std::memset(dx, 0, sizeof(double) * static_cast<size_t>(n_in) * cin);
+  std::fill_n(dx, static_cast<size_t>(n_in) * cin, 0.0);
   for (int64_t p = 0; p < n_pairs; ++p) {
     const double* g = dy + static_cast<int64_t>(t_out[p]) * cout;
     const double* wo = w + static_cast<int64_t>(t_off[p]) * cin * cout;
@@ -438,7 +439,7 @@ void oracle_graph_conv(const int64_t* indptr, const int32_t* src, const int32_t*
 // dw[o][ci][co] = sum over triples (i, j, o) of x[i][ci] * dy[j][co].
 void oracle_conv_wgrad(const int32_t* t_in, const int32_t* t_out, const int32_t* t_off, int64_t n_pairs,
                        const double* x, int cin, const double* dy, int cout, double* dw, int kvol) {
-  std::memset(dw, 0, sizeof(double) * static_cast<size_t>(kvol) * cin * cout);
+  std::fill_n(dw, static_cast<size_t>(kvol) * cin * cout, 0.0);
   for (int64_t p = 0; p < n_pairs; ++p) {
     const double* xi = x + static_cast<int64_t>(t_in[p]) * cin;
     const double* g = dy + static_cast<int64_t>(t_out[p]) * cout;
