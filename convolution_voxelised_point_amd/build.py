@@ -1,8 +1,11 @@
-"""Compile the HIP sources under ``csrc/`` into ``libts.so`` (gfx950).
+"""Compile the HIP sources under ``csrc/`` into ``libts.so`` (gfx950) and
+the bounds-check variant ``libts_debug.so`` (the same sources compiled with
+TS_DEBUG_CHECKS).
 
 Usage: ``python -m convolution_voxelised_point_amd.build``.  hipcc
-cross-compiles without a GPU.  Objects go to ``_build/`` beside this file;
-the shared library lands next to this file so the binding finds it in-tree.
+cross-compiles without a GPU.  Objects go to ``_build/`` (``_build_debug/``)
+beside this file; the shared libraries land next to this file so the binding
+finds them in-tree.
 """
 from __future__ import annotations
 
@@ -18,6 +21,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libts.so")
+DEBUG_BUILD_DIR = os.path.join(HERE, "_build_debug")
+DEBUG_LIB = os.path.join(HERE, "libts_debug.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -41,9 +46,10 @@ def cuid(src: str) -> str:
     return "ts_" + os.path.splitext(os.path.basename(src))[0]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CFLAGS, f"-cuid={cuid(src)}", "-c", src, "-o", obj]
+def _compile(src: str, debug: bool = False) -> str:
+    obj = os.path.join(DEBUG_BUILD_DIR if debug else BUILD_DIR, os.path.basename(src) + ".o")
+    extra = ["-DTS_DEBUG_CHECKS"] if debug else []
+    cmd = [HIPCC, *CFLAGS, *extra, f"-cuid={cuid(src)}", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
@@ -54,16 +60,29 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int = 8) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, sources()))
-    tmp = LIB + ".tmp"
+def link(objs, lib: str) -> str:
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+    return lib
+
+
+def build(jobs: int = 8, debug: bool = True) -> str:
+    """Builds libts.so and, with `debug`, libts_debug.so; returns the path
+    of libts.so."""
+    variants = [False, True] if debug else [False]
+    for d in variants:
+        os.makedirs(DEBUG_BUILD_DIR if d else BUILD_DIR, exist_ok=True)
+    jobs_list = [(src, d) for d in variants for src in sources()]
+    # the slowest sources first, so the pool ends together
+    jobs_list.sort(key=lambda j: -os.path.getsize(j[0]))
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(lambda j: (j[1], _compile(*j)), jobs_list))
+    for d in variants:
+        link(sorted(o for dd, o in objs if dd == d), DEBUG_LIB if d else LIB)
     return LIB
 
 

@@ -201,11 +201,32 @@ const char* ts_status_string(ts_status s) {
     case TS_ERR_INVALID_ARG: return "invalid argument";
     case TS_ERR_UNSUPPORTED: return "unsupported";
     case TS_ERR_HIP: return "HIP error";
+    default: return "unknown status";
   }
-  return "unknown status";
 }
 
+#ifdef TS_DEBUG_CHECKS
+const char* ts_version(void) { return "ts 0.1.0 (gfx950, bounds checks)"; }
+#else
 const char* ts_version(void) { return "ts 0.1.0 (gfx950)"; }
+#endif
+
+ts_status ts_debug_violations(uint32_t* bits) {
+#ifdef TS_DEBUG_CHECKS
+  if (!bits) return TS_ERR_INVALID_ARG;
+  if (hipDeviceSynchronize() != hipSuccess) return TS_ERR_HIP;
+  hipError_t (*const take[])(uint32_t*) = {debug_take_conv, debug_take_igemm, debug_take_fod, debug_take_wgrad};
+  for (auto f : take) {
+    uint32_t v = 0;
+    if (f(&v) != hipSuccess) return TS_ERR_HIP;
+    *bits |= v;
+  }
+  return TS_OK;
+#else
+  (void)bits;
+  return TS_ERR_UNSUPPORTED;
+#endif
+}
 
 int64_t ts_hash_capacity(int64_t n, double rsv_ratio) {
   if (n < 0 || !(rsv_ratio >= 1.0)) return -1;
@@ -675,7 +696,7 @@ ts_status ts_pool_fwd(const ts_kmap* map, const void* x, int c, void* y, ts_dtyp
   if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return TS_ERR_INVALID_ARG;
   if (out_dtype != TS_F32 && out_dtype != in_dtype) return TS_ERR_UNSUPPORTED;
   if ((map->n_in > 0 && !x) || (map->n_out_cap > 0 && !y)) return TS_ERR_INVALID_ARG;
-  TS_TRY(launch_pool(map->fwd, map->kvol, x, c, y, in_dtype, out_dtype, mode, stream));
+  TS_TRY(launch_pool(map->fwd, map->kvol, x, map->n_in, c, y, in_dtype, out_dtype, mode, stream));
   return TS_OK;
 }
 

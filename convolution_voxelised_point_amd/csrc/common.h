@@ -157,4 +157,60 @@ __host__ __device__ __forceinline__ T ceil_div(T a, T b) {
   return (a + b - 1) / b;
 }
 
+// ---------------------------------------------------------------- bounds-check build
+// Compiled with TS_DEBUG_CHECKS (the separate bounds-check build of the
+// library), the contraction, pooling and weight-gradient kernels check every
+// row index they read from a map -- neighbour entries, tile rows, pairs,
+// group entries and slots -- against the matrix it indexes before using it.
+// An index out of range is replaced by one inside (an absent neighbour where
+// the kernel knows absence, else row 0), so no access leaves the buffers, and
+// ORs a TS_DEBUG_* bit into the violation word of its translation unit; the
+// results of such a call are then meaningless, and ts_debug_violations reports
+// the bits.  In the regular build the checks are the identity.
+#ifdef TS_DEBUG_CHECKS
+constexpr bool kDebugChecks = true;
+static __device__ uint32_t g_debug_word;
+#else
+constexpr bool kDebugChecks = false;
+#endif
+
+// An optional row index (-1 = absent): r for -1 <= r < n, else -1.
+__device__ __forceinline__ int32_t dbg_opt(int32_t r, int64_t n, uint32_t bit) {
+#ifdef TS_DEBUG_CHECKS
+  if (r < -1 || r >= n) {
+    atomicOr(&g_debug_word, bit);
+    return -1;
+  }
+#endif
+  return r;
+}
+
+// A required row index: r for 0 <= r < n, else 0.
+__device__ __forceinline__ int32_t dbg_req(int32_t r, int64_t n, uint32_t bit) {
+#ifdef TS_DEBUG_CHECKS
+  if (r < 0 || r >= n) {
+    atomicOr(&g_debug_word, bit);
+    return 0;
+  }
+#endif
+  return r;
+}
+
+#ifdef TS_DEBUG_CHECKS
+// This translation unit's violation word on the current device: read into
+// *v, then cleared (synchronous copies).
+static hipError_t debug_take_local(uint32_t* v) {
+  hipError_t e = hipMemcpyFromSymbol(v, HIP_SYMBOL(g_debug_word), sizeof(uint32_t), 0, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return e;
+  const uint32_t zero = 0;
+  return hipMemcpyToSymbol(HIP_SYMBOL(g_debug_word), &zero, sizeof zero, 0, hipMemcpyHostToDevice);
+}
+#define TS_DEBUG_TU(name) \
+  namespace ts {          \
+  hipError_t debug_take_##name(uint32_t* v) { return debug_take_local(v); } \
+  }
+#else
+#define TS_DEBUG_TU(name)
+#endif
+
 }  // namespace ts

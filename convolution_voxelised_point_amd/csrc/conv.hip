@@ -37,6 +37,8 @@ struct DirectK {
   int64_t n_tiles;
   int kvol;
   const void* src;
+  int64_t n_src;       // rows of src and of dst (bounds-check build)
+  int64_t n_dest;
   int c_src;
   const void* w;
   int w_cin, w_cout;
@@ -78,10 +80,10 @@ __global__ __launch_bounds__(256) void k_direct(DirectK a) {
   if (t >= a.n_tiles) return;
   const uint64_t tm = a.tile_mask[t];
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  const int32_t row = a.tile_rows[t * kTile + r];
+  const int32_t row = dbg_opt(a.tile_rows[t * kTile + r], a.n_dest, TS_DEBUG_DST_ROW);
   for (uint64_t mm = row >= 0 ? tm : 0ull; mm; mm &= mm - 1) {
     const int o = __builtin_ctzll(mm);
-    const int32_t nb = a.nbr[static_cast<int64_t>(row) * kvol + o];
+    const int32_t nb = dbg_opt(a.nbr[static_cast<int64_t>(row) * kvol + o], a.n_src, TS_DEBUG_SRC_ROW);
     if (nb < 0) continue;
     const T* xs = src + static_cast<int64_t>(nb) * c_src;
     if (STAGE) {
@@ -131,8 +133,9 @@ template <typename T, bool STAGE>
 __global__ __launch_bounds__(256) void k_gs_offset(const int64_t* __restrict__ pair_start, int o,
                                                    const int32_t* __restrict__ src_rows,
                                                    const int32_t* __restrict__ dst_rows, const T* __restrict__ src,
-                                                   int c_src, const T* __restrict__ w, int w_cin, int w_cout,
-                                                   bool transpose, float* __restrict__ acc, int c_dst) {
+                                                   int64_t n_src, int c_src, const T* __restrict__ w, int w_cin,
+                                                   int w_cout, bool transpose, float* __restrict__ acc,
+                                                   int64_t n_dest, int c_dst) {
   extern __shared__ __attribute__((aligned(16))) float wsh[];  // STAGE: c_src * c_dst floats
   const int nchunk = (c_dst + 7) / 8;
   const T* wo = w + static_cast<int64_t>(o) * w_cin * w_cout;
@@ -149,7 +152,7 @@ __global__ __launch_bounds__(256) void k_gs_offset(const int64_t* __restrict__ p
   const int64_t p = pair_start[o] + i / nchunk;
   if (p >= pair_start[o + 1]) return;
   const int c0 = static_cast<int>(i % nchunk) * 8;
-  const T* xs = src + static_cast<int64_t>(src_rows[p]) * c_src;
+  const T* xs = src + static_cast<int64_t>(dbg_req(src_rows[p], n_src, TS_DEBUG_SRC_ROW)) * c_src;
   float sum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int ci = 0; ci < c_src; ++ci) {
     const float xv = to_f32(xs[ci]);
@@ -164,7 +167,7 @@ __global__ __launch_bounds__(256) void k_gs_offset(const int64_t* __restrict__ p
       }
     }
   }
-  float* out = acc + static_cast<int64_t>(dst_rows[p]) * c_dst;
+  float* out = acc + static_cast<int64_t>(dbg_req(dst_rows[p], n_dest, TS_DEBUG_DST_ROW)) * c_dst;
 #pragma unroll
   for (int e = 0; e < 8; ++e)
     if (c0 + e < c_dst) out[c0 + e] += sum[e];
@@ -220,6 +223,8 @@ hipError_t launch_direct(const ConvArgs& a, hipStream_t s) {
   k.n_tiles = rel.n_tiles;
   k.kvol = a.kvol;
   k.src = a.src;
+  k.n_src = a.n_src;
+  k.n_dest = rel.n_dest_cap;
   k.c_src = a.c_src;
   k.w = a.w;
   k.w_cin = a.w_cin;
@@ -245,6 +250,7 @@ struct PoolK {
   const uint64_t* row_mask;
   const int32_t* nbr;
   int64_t slots;
+  int64_t n_src, n_dest;  // rows of src and of dst (bounds-check build)
   int kvol, c, nchunk;
   const void* src;
   void* dst;
@@ -264,7 +270,7 @@ __global__ __launch_bounds__(256) void k_pool(PoolK a) {
   if (i >= a.slots * a.nchunk) return;
   const int64_t slot = i / a.nchunk;
   const int c0 = static_cast<int>(i - slot * a.nchunk) * 8;
-  const int32_t row = a.tile_rows[slot];
+  const int32_t row = dbg_opt(a.tile_rows[slot], a.n_dest, TS_DEBUG_DST_ROW);
   if (row < 0) return;
   const T* src = static_cast<const T*>(a.src);
   float acc[8];
@@ -273,7 +279,7 @@ __global__ __launch_bounds__(256) void k_pool(PoolK a) {
   int count = 0;
   for (uint64_t mm = a.row_mask[row]; mm; mm &= mm - 1) {
     const int o = __builtin_ctzll(mm);
-    const int32_t nb = a.nbr[static_cast<int64_t>(row) * a.kvol + o];
+    const int32_t nb = dbg_opt(a.nbr[static_cast<int64_t>(row) * a.kvol + o], a.n_src, TS_DEBUG_SRC_ROW);
     if (nb < 0) continue;
     const T* xs = src + static_cast<int64_t>(nb) * a.c + c0;
     ++count;
@@ -332,14 +338,16 @@ static hipError_t pool_out(const PoolK& k, ts_dtype out, int mode, hipStream_t s
   }
 }
 
-hipError_t launch_pool(const ts_rel& rel, int kvol, const void* x, int c, void* y, ts_dtype in, ts_dtype out, int mode,
-                       hipStream_t s) {
+hipError_t launch_pool(const ts_rel& rel, int kvol, const void* x, int64_t n_src, int c, void* y, ts_dtype in,
+                       ts_dtype out, int mode, hipStream_t s) {
   if (rel.n_tiles == 0) return hipSuccess;
   PoolK k;
   k.tile_rows = rel.tile_rows;
   k.row_mask = rel.row_mask;
   k.nbr = rel.nbr;
   k.slots = rel.n_tiles * kTile;
+  k.n_src = n_src;
+  k.n_dest = rel.n_dest_cap;
   k.kvol = kvol;
   k.c = c;
   k.nchunk = (c + 7) / 8;
@@ -450,12 +458,12 @@ static hipError_t gs_offsets(const ts_kmap* map, const ConvArgs& a, bool backwar
   for (int o = 0; o < a.kvol; ++o) {
     if (stage)
       k_gs_offset<T, true><<<grid, 256, lds, s>>>(map->pair_start, o, src_rows, dst_rows, static_cast<const T*>(a.src),
-                                                  a.c_src, static_cast<const T*>(a.w), a.w_cin, a.w_cout, a.transpose,
-                                                  acc, a.c_dst);
+                                                  a.n_src, a.c_src, static_cast<const T*>(a.w), a.w_cin, a.w_cout,
+                                                  a.transpose, acc, n_dest_cap, a.c_dst);
     else
       k_gs_offset<T, false><<<grid, 256, 0, s>>>(map->pair_start, o, src_rows, dst_rows, static_cast<const T*>(a.src),
-                                                 a.c_src, static_cast<const T*>(a.w), a.w_cin, a.w_cout, a.transpose,
-                                                 acc, a.c_dst);
+                                                 a.n_src, a.c_src, static_cast<const T*>(a.w), a.w_cin, a.w_cout,
+                                                 a.transpose, acc, n_dest_cap, a.c_dst);
   }
   return hipGetLastError();
 }
@@ -480,3 +488,5 @@ hipError_t launch_gather_scatter(const ts_kmap* map, const ConvArgs& a, bool bac
 }
 
 }  // namespace ts
+
+TS_DEBUG_TU(conv)

@@ -105,6 +105,7 @@ struct FodK {
   int kvol;
   const void* src;
   uint32_t src_bytes;     // < 2^31: an offset of 2^31 or more reads out of range
+  int64_t n_src;          // source rows (bounds-check build)
   int c_src;
   const void* w;
   int w_vec;              // w is 16-byte aligned
@@ -339,7 +340,7 @@ __global__ __launch_bounds__(64 * (fod_tiles(KB, MW, MH) * (MW / MH) + 1)) void 
   // of the steps is stored group (v + gbase) mod G, gbase the groups of the
   // offsets before rot
   const int lane_o = lane + rot < kvol ? lane + rot : lane + rot - kvol;
-  const int cnt = has_tile && lane < kvol ? a.gcount[t * kvol + lane_o] : 0;
+  const int cnt = has_tile && lane < kvol ? dbg_req(a.gcount[t * kvol + lane_o], kR + 1, TS_DEBUG_DST_ROW) : 0;
   const int ng = (cnt + 15) >> 4;
   int incl = ng;
 #pragma unroll
@@ -402,7 +403,8 @@ __global__ __launch_bounds__(64 * (fod_tiles(KB, MW, MH) * (MW / MH) + 1)) void 
     constexpr int p = decltype(pc)::v;
     constexpr bool FIRST = decltype(firstc)::v;
     if constexpr (!FIRST || p + DB >= RM) {
-      const uint32_t off = static_cast<uint32_t>(msrc[(p + DB) % RS]) * (C_SRC * 2) + kq * 16;
+      const uint32_t off =
+          static_cast<uint32_t>(dbg_opt(msrc[(p + DB) % RS], a.n_src, TS_DEBUG_SRC_ROW)) * (C_SRC * 2) + kq * 16;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
         xs[(p + DB) % RB][kb] =
@@ -443,7 +445,8 @@ __global__ __launch_bounds__(64 * (fod_tiles(KB, MW, MH) * (MW / MH) + 1)) void 
     }
     // the group's accumulator rows (the pad sink included) enter the MFMAs
     // as the C operand and are written back
-    const uint32_t slot = (mslot[p % RM] >> slot_shift) & 0xffu;
+    uint32_t slot = (mslot[p % RM] >> slot_shift) & 0xffu;
+    if constexpr (kDebugChecks) slot = static_cast<uint32_t>(dbg_req(static_cast<int32_t>(slot), kR + 1, TS_DEBUG_DST_ROW));
     const uint32_t abase = static_cast<uint32_t>(acc_off) + slot * (NCH * 16) +
                            16u * (static_cast<uint32_t>(kq) ^ ((slot / SW_PER) & SW_MASK));
     f32x4 acc[MH];
@@ -560,6 +563,7 @@ hipError_t launch_fod(const ConvArgs& a, hipStream_t s) {
   k.kvol = a.kvol;
   k.src = a.src;
   k.src_bytes = static_cast<uint32_t>(a.n_src * a.c_src * 2);
+  k.n_src = a.n_src;
   k.c_src = a.c_src;
   k.w = a.w;
   k.w_vec = (reinterpret_cast<uintptr_t>(a.w) & 15) == 0 ? 1 : 0;
@@ -576,3 +580,5 @@ hipError_t launch_fod(const ConvArgs& a, hipStream_t s) {
 }
 
 }  // namespace ts
+
+TS_DEBUG_TU(fod)

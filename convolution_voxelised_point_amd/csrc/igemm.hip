@@ -84,6 +84,8 @@ struct IgK {
   int kvol;
   const void* src;
   uint32_t src_bytes;  // < 2^31: a buffer offset of 2^31 is out of range
+  int64_t n_src;       // rows of src and of dst (bounds-check build)
+  int64_t n_dest;
   int c_src;
   const u32x4* wp;  // packed fragments [kvol][mbt][c_src/32][64]
   int mbt;          // fragments of 16 output channels in the packed weights
@@ -297,12 +299,12 @@ __global__ __launch_bounds__(NW * 64) void k_igemm(IgK a) {
     const int64_t tile = live ? t0 + g : 0;
     m[g] = live ? a.tile_mask[tile] : 0ull;
     u |= m[g];
-    const int32_t drow = a.tile_rows[tile * kTile + col];
+    const int32_t drow = dbg_opt(a.tile_rows[tile * kTile + col], a.n_dest, TS_DEBUG_DST_ROW);
     const int32_t* nrow = a.nbr + static_cast<int64_t>(drow >= 0 ? drow : 0) * kvol;
 #pragma unroll
     for (int j = 0; j < kNbRegs; ++j) {
       const int o = kq * kNbRegs + j;
-      const int32_t v = nrow[o < kvol ? o : 0];
+      const int32_t v = dbg_opt(nrow[o < kvol ? o : 0], a.n_src, TS_DEBUG_SRC_ROW);
       pr[g][j] = drow >= 0 ? v : -1;
     }
   }
@@ -442,7 +444,7 @@ __global__ __launch_bounds__(NW * 64) void k_igemm(IgK a) {
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     if (t0 + g >= a.n_tiles) continue;
-    const int32_t row = a.tile_rows[(t0 + g) * kTile + col];
+    const int32_t row = dbg_opt(a.tile_rows[(t0 + g) * kTile + col], a.n_dest, TS_DEBUG_DST_ROW);
     if (row < 0) continue;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
@@ -547,7 +549,7 @@ __global__ __launch_bounds__(NW * 64) void k_igemm_res(IgK a) {
       const int64_t tile = live ? g0 + g : 0;
       const uint64_t v = a.tile_mask[tile];
       mm[g] = live ? v : 0ull;
-      const int32_t r = a.tile_rows[tile * kTile + col];
+      const int32_t r = dbg_opt(a.tile_rows[tile * kTile + col], a.n_dest, TS_DEBUG_DST_ROW);
       dr[g] = live ? r : -1;
     }
   };
@@ -558,7 +560,7 @@ __global__ __launch_bounds__(NW * 64) void k_igemm_res(IgK a) {
 #pragma unroll
       for (int j = 0; j < kNbRegs; ++j) {
         const int o = kq * kNbRegs + j;
-        const int32_t v = nrow[o < kvol ? o : 0];
+        const int32_t v = dbg_opt(nrow[o < kvol ? o : 0], a.n_src, TS_DEBUG_SRC_ROW);
         p[g][j] = dr[g] >= 0 ? v : -1;
       }
     }
@@ -882,6 +884,8 @@ hipError_t launch_igemm(const ConvArgs& a, void* ws, hipStream_t s) {
   k.kvol = a.kvol;
   k.src = a.src;
   k.src_bytes = static_cast<uint32_t>(a.n_src * a.c_src * 2);
+  k.n_src = a.n_src;
+  k.n_dest = rel.n_dest_cap;
   k.c_src = a.c_src;
   k.wp = static_cast<const u32x4*>(ws);
   k.mbt = ceil_div(a.c_dst, 16);
@@ -900,3 +904,5 @@ hipError_t launch_igemm(const ConvArgs& a, void* ws, hipStream_t s) {
 }
 
 }  // namespace ts
+
+TS_DEBUG_TU(igemm)

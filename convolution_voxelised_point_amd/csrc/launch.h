@@ -100,8 +100,8 @@ hipError_t launch_direct(const ConvArgs& a, hipStream_t s);
 hipError_t launch_graph_conv(const int64_t* indptr, const int32_t* src, const int32_t* rel, int64_t n_dst,
                              int64_t n_src, int n_rel, const void* x, int cin, const void* w, int cout, void* y,
                              ts_dtype in, ts_dtype out, uint32_t* flags, hipStream_t s);
-hipError_t launch_pool(const ts_rel& rel, int kvol, const void* x, int c, void* y, ts_dtype in, ts_dtype out, int mode,
-                       hipStream_t s);
+hipError_t launch_pool(const ts_rel& rel, int kvol, const void* x, int64_t n_src, int c, void* y, ts_dtype in,
+                       ts_dtype out, int mode, hipStream_t s);
 
 // fod.hip: the fetch-on-demand dataflow over a relation's pair groups
 bool fod_supported(int kvol, int64_t n_src, int c_src, int c_dst, ts_dtype in_dtype);
@@ -110,6 +110,13 @@ hipError_t launch_fod(const ConvArgs& a, hipStream_t s);
 size_t gs_workspace_bytes(int64_t n_dest_cap, int c_dst, ts_dtype out_dtype);
 hipError_t launch_gather_scatter(const ts_kmap* map, const ConvArgs& a, bool backward, int64_t n_dest_cap,
                                  void* ws, hipStream_t s);
+
+// bounds-check build: each checking translation unit's violation word
+// (read and cleared); defined only under TS_DEBUG_CHECKS
+hipError_t debug_take_conv(uint32_t* v);
+hipError_t debug_take_igemm(uint32_t* v);
+hipError_t debug_take_fod(uint32_t* v);
+hipError_t debug_take_wgrad(uint32_t* v);
 
 // wgrad.hip
 size_t wgrad_workspace_bytes(const ts_kmap* map, int cin, int cout);

@@ -94,7 +94,7 @@ __global__ __launch_bounds__(256, 2) void k_wgrad_mfma(const int32_t* __restrict
                                                     const int32_t* __restrict__ pair_in,
                                                     const int32_t* __restrict__ pair_out, const T* __restrict__ x,
                                                     int cin, const T* __restrict__ dy, int cout,
-                                                    float* __restrict__ partial) {
+                                                    float* __restrict__ partial, int64_t n_x, int64_t n_dy) {
   typedef typename WMfma<T>::frag Frag;
   constexpr int HT = TW / 2;   // channels per wave in each dim
   constexpr int NT = HT / 16;  // 16 x 16 MFMA tiles per wave in each dim
@@ -145,7 +145,7 @@ __global__ __launch_bounds__(256, 2) void k_wgrad_mfma(const int32_t* __restrict
   auto load_rows = [&](int st, const int32_t (&id)[8], u32x4 (&v)[8]) {
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
-      const int32_t row = valid(st, r) ? id[r] : 0;
+      const int32_t row = valid(st, r) ? dbg_req(id[r], op ? n_dy : n_x, op ? TS_DEBUG_DST_ROW : TS_DEBUG_SRC_ROW) : 0;
       v[r] = *reinterpret_cast<const u32x4*>(src + static_cast<int64_t>(row) * C + (cok ? ch : 0));
     }
   };
@@ -236,7 +236,7 @@ __global__ __launch_bounds__(256) void k_wgrad_fma(const int32_t* __restrict__ c
                                                    const int32_t* __restrict__ pair_in,
                                                    const int32_t* __restrict__ pair_out, const T* __restrict__ x,
                                                    int cin, const T* __restrict__ dy, int cout,
-                                                   float* __restrict__ partial) {
+                                                   float* __restrict__ partial, int64_t n_x, int64_t n_dy) {
   const int c = blockIdx.x;
   int o;
   int64_t p0, p1;
@@ -246,8 +246,9 @@ __global__ __launch_bounds__(256) void k_wgrad_fma(const int32_t* __restrict__ c
   const int ci = static_cast<int>(e / cout), co = static_cast<int>(e % cout);
   float acc = 0.f;
   for (int64_t p = p0; p < p1; ++p)
-    acc = fmaf(static_cast<float>(x[static_cast<int64_t>(pair_in[p]) * cin + ci]),
-               static_cast<float>(dy[static_cast<int64_t>(pair_out[p]) * cout + co]), acc);
+    acc = fmaf(static_cast<float>(x[static_cast<int64_t>(dbg_req(pair_in[p], n_x, TS_DEBUG_SRC_ROW)) * cin + ci]),
+               static_cast<float>(dy[static_cast<int64_t>(dbg_req(pair_out[p], n_dy, TS_DEBUG_DST_ROW)) * cout + co]),
+               acc);
   partial[static_cast<int64_t>(c) * cin * cout + e] = acc;
 }
 
@@ -285,11 +286,13 @@ void launch_wgrad_mfma(dim3 grid, ts_dtype dt, const ts_kmap* map, const void* x
   if (dt == TS_F16)
     k_wgrad_mfma<_Float16, TW><<<grid, 256, 0, s>>>(chunk_base, map->pair_start, map->kvol, map->pair_in,
                                                      map->pair_out, static_cast<const _Float16*>(x), cin,
-                                                     static_cast<const _Float16*>(dy), cout, partial);
+                                                     static_cast<const _Float16*>(dy), cout, partial, map->n_in,
+                                                     map->n_out_cap);
   else
     k_wgrad_mfma<__bf16, TW><<<grid, 256, 0, s>>>(chunk_base, map->pair_start, map->kvol, map->pair_in,
                                                    map->pair_out, static_cast<const __bf16*>(x), cin,
-                                                   static_cast<const __bf16*>(dy), cout, partial);
+                                                   static_cast<const __bf16*>(dy), cout, partial, map->n_in,
+                                                   map->n_out_cap);
 }
 
 }  // namespace
@@ -322,17 +325,18 @@ hipError_t launch_wgrad(const ts_kmap* map, const void* x, int cin, const void* 
       case TS_F32:
         k_wgrad_fma<float><<<grid, 256, 0, s>>>(chunk_base, map->pair_start, map->kvol, map->pair_in, map->pair_out,
                                                  static_cast<const float*>(x), cin, static_cast<const float*>(dy), cout,
-                                                 partial);
+                                                 partial, map->n_in, map->n_out_cap);
         break;
       case TS_F16:
         k_wgrad_fma<_Float16><<<grid, 256, 0, s>>>(chunk_base, map->pair_start, map->kvol, map->pair_in,
                                                     map->pair_out, static_cast<const _Float16*>(x), cin,
-                                                    static_cast<const _Float16*>(dy), cout, partial);
+                                                    static_cast<const _Float16*>(dy), cout, partial, map->n_in,
+                                                   map->n_out_cap);
         break;
       default:
         k_wgrad_fma<__bf16><<<grid, 256, 0, s>>>(chunk_base, map->pair_start, map->kvol, map->pair_in, map->pair_out,
                                                   static_cast<const __bf16*>(x), cin, static_cast<const __bf16*>(dy),
-                                                  cout, partial);
+                                                  cout, partial, map->n_in, map->n_out_cap);
         break;
     }
   }
@@ -343,3 +347,5 @@ hipError_t launch_wgrad(const ts_kmap* map, const void* x, int cin, const void* 
 }
 
 }  // namespace ts
+
+TS_DEBUG_TU(wgrad)

@@ -19,7 +19,9 @@ import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libts.so")
+DEBUG_LIB_PATH = os.path.join(_HERE, "libts_debug.so")
+# debug_binding() sets _LIB_OVERRIDE in a second instance of this module
+LIB_PATH = globals().get("_LIB_OVERRIDE") or os.path.join(_HERE, "libts.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -m convolution_voxelised_point_amd.build`")
@@ -36,6 +38,7 @@ TS_OP_FWD, TS_OP_DGRAD, TS_OP_WGRAD, TS_OP_TRANSPOSE = 0, 1, 2, 3
 TS_POOL_MAX, TS_POOL_AVG = 0, 1
 TS_TILE, TS_GTILE, TS_MAX_KVOL = 16, 128, 64
 TS_NOALLOC_SCRATCH_BYTES = 4 << 20
+TS_DEBUG_SRC_ROW, TS_DEBUG_DST_ROW = 1, 2
 
 _DT = {torch.float32: TS_F32, torch.float16: TS_F16, torch.bfloat16: TS_BF16}
 
@@ -102,6 +105,7 @@ _lib_pool_fwd = _sig("ts_pool_fwd", _i32, [_P, _vp, _i32, _vp, _i32, _i32, _i32,
 _lib_conv_bwd_dgrad = _sig("ts_conv_bwd_dgrad", _i32, [_P, _vp, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _vp, _sz, _vp])
 _lib_conv_bwd_wgrad = _sig("ts_conv_bwd_wgrad", _i32, [_P, _vp, _i32, _vp, _i32, _i32, _vp, _vp, _sz, _vp])
 _lib_conv_bwd_dgrad_noalloc = _sig("ts_conv_bwd_dgrad_noalloc", _i32, [_P, _vp, _i32, _vp, _i32, _vp, _i32, _i32, _vp])
+_lib_debug_violations = _sig("ts_debug_violations", _i32, [ctypes.POINTER(_u32)])
 
 EXPORTED = ["ts_status_string", "ts_version", "ts_hash_capacity", "ts_hash_table_bytes", "ts_hash_build",
             "ts_hash_query", "ts_support_scratch_bytes", "ts_strided_support", "ts_generative_scratch_bytes",
@@ -109,7 +113,7 @@ EXPORTED = ["ts_status_string", "ts_version", "ts_hash_capacity", "ts_hash_table
             "ts_devoxelize", "ts_kmap_bytes", "ts_kmap_build",
             "ts_conv_workspace_bytes", "ts_conv_pack_weights", "ts_conv_fwd", "ts_subm_conv_fwd", "ts_conv_fwd_strided",
             "ts_conv_fwd_generative", "ts_conv_transpose_fwd", "ts_pool_fwd", "ts_graph_conv_fwd", "ts_conv_bwd_dgrad",
-            "ts_conv_bwd_wgrad", "ts_conv_bwd_dgrad_noalloc"]
+            "ts_conv_bwd_wgrad", "ts_conv_bwd_dgrad_noalloc", "ts_debug_violations"]
 
 
 class TsError(RuntimeError):
@@ -142,6 +146,28 @@ def _dt(t: torch.Tensor) -> int:
 # ---------------------------------------------------------------- 1:1 wrappers
 def ts_status_string(st: int) -> str:
     return _lib_status_string(st).decode()
+
+
+def ts_debug_violations() -> int:
+    """Bits raised by the bounds checks on the current device since the last
+    call (the call waits for the device and clears them).  Only the
+    bounds-check build has checks; the regular library raises TsError
+    (unsupported)."""
+    bits = _u32(0)
+    _check(_lib_debug_violations(ctypes.byref(bits)), "ts_debug_violations")
+    return int(bits.value)
+
+
+def debug_binding():
+    """A second instance of this binding over the bounds-check build
+    ``libts_debug.so`` (the same entry points; every kernel checks the row
+    indexes it reads from a map).  Raises ImportError when it is not built."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(__name__ + "_debug", __file__)
+    mod = importlib.util.module_from_spec(spec)
+    mod._LIB_OVERRIDE = DEBUG_LIB_PATH
+    spec.loader.exec_module(mod)
+    return mod
 
 
 def ts_version() -> str:

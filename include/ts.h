@@ -528,6 +528,25 @@ ts_status ts_conv_bwd_wgrad(const ts_kmap* map, const void* x, int cin, const vo
 ts_status ts_conv_bwd_dgrad_noalloc(const ts_kmap* map, const void* dy, int cout, const void* w, int cin, void* dx,
                                     ts_dtype in_dtype, ts_dtype out_dtype, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Bounds-check build.  The library also builds as libts_debug.so, compiled
+ * with TS_DEBUG_CHECKS: there the contraction, pooling and weight-gradient
+ * kernels check every row index they read from a map (neighbour entries,
+ * tile rows, pair lists, pair-group entries and slots) against the matrix it
+ * indexes.  An index out of range is replaced by one inside, so no access
+ * leaves the caller's buffers, and raises a bit below; the results of that
+ * call are then meaningless.  Everything else is the regular library.
+ *
+ * ts_debug_violations waits for the current device (hipDeviceSynchronize),
+ * ORs the bits raised on it since the previous call into *bits (host) and
+ * clears them.  Errors: TS_ERR_INVALID_ARG (bits NULL), TS_ERR_HIP (the wait
+ * or a copy failed), TS_ERR_UNSUPPORTED in the regular build, which has no
+ * checks.
+ * ---------------------------------------------------------------------- */
+#define TS_DEBUG_SRC_ROW 1u /* a source row index outside the source matrix                 */
+#define TS_DEBUG_DST_ROW 2u /* a destination row, pair-group slot or group count out of range */
+ts_status ts_debug_violations(uint32_t* bits);
+
 #ifdef __cplusplus
 }
 #endif

@@ -51,6 +51,7 @@ static void sizes() {
   EXPECT(ts_status_string(static_cast<ts_status>(99)) != nullptr);
   EXPECT(ts_status_string(static_cast<ts_status>(-7)) != nullptr);
   EXPECT(strstr(ts_version(), "gfx950") != nullptr);
+  EXPECT(ts_debug_violations(nullptr) == TS_ERR_UNSUPPORTED);  // the regular build has no checks
 }
 
 static void hash() {

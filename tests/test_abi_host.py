@@ -363,3 +363,27 @@ def test_voxelize_rejects(ts):
     assert D(FAKE, 10, FAKE, 0, FAKE, ts.TS_F32, None) == ts.TS_ERR_INVALID_ARG     # no channels
     assert D(None, 10, FAKE, 4, FAKE, ts.TS_F32, None) == ts.TS_ERR_INVALID_ARG     # no voxel index
     assert D(FAKE, 10, FAKE, 4, FAKE, 9, None) == ts.TS_ERR_INVALID_ARG             # dtype
+
+
+DEBUG_LIB = os.path.join(ROOT, "convolution_voxelised_point_amd", "libts_debug.so")
+
+
+def test_debug_violations_needs_the_debug_build():
+    lib = ctypes.CDLL(LIB)
+    lib.ts_debug_violations.argtypes = [ctypes.c_void_p]
+    bits = ctypes.c_uint32(0)
+    assert lib.ts_debug_violations(ctypes.byref(bits)) == 2      # TS_ERR_UNSUPPORTED: no checks here
+
+
+@pytest.mark.skipif(not os.path.exists(DEBUG_LIB), reason="libts_debug.so not built")
+def test_debug_build_exports_and_identifies():
+    lib = ctypes.CDLL(DEBUG_LIB)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+    lib.ts_version.restype = ctypes.c_char_p
+    assert b"bounds checks" in lib.ts_version()
+    lib.ts_debug_violations.argtypes = [ctypes.c_void_p]
+    assert lib.ts_debug_violations(None) == 1                    # TS_ERR_INVALID_ARG, before touching the GPU
+    lib2 = ctypes.CDLL(LIB)
+    lib2.ts_version.restype = ctypes.c_char_p
+    assert b"bounds checks" not in lib2.ts_version()
