@@ -5,9 +5,10 @@
 // differences") requires every dataflow to give the same result for a fixed
 // relation and weight tensor.
 //
-// Dataflows here (the MFMA implicit GEMM lives in igemm.hip):
-//  * direct (k_direct): the implicit-GEMM walk over the tiles with FMA, for fp32
-//    and for channel counts the MFMA shapes do not fit.
+// Dataflows here (the fp16/bf16 MFMA implicit GEMM lives in igemm.hip):
+//  * direct: the implicit-GEMM walk over the tiles -- on the fp32 matrix
+//    cores (k_mfma_f32) for fp32 features with channels in multiples of 16,
+//    with FMA (k_direct) for the other shapes the MFMA kernels do not fit.
 //  * gather-scatter (k_gs_offset): offsets one after another in fixed order;
 //    per offset, gather the source rows of its pairs, multiply by W[o] and add
 //    into an fp32 accumulator at the destination rows.  Within one offset the
@@ -181,6 +182,60 @@ __global__ __launch_bounds__(256) void k_cast_rows(const float* __restrict__ acc
   if (i < n_elems && i < lim) out[i] = from_f32<OT>(acc[i]);
 }
 
+// ---------------------------------------------------------------- fp32 on the matrix cores
+// The same walk for fp32 features on v_mfma_f32_16x16x4_f32 (D[16][16] +=
+// A[16][4] B[4][16] in fp32).  A wave owns one tile of 16 destination rows
+// and one block of 16 destination channels:
+//   A[m][k] = W[o][ci][co0 + m]   (the weights; dgrad: W[o][co0 + m][ci]),
+//   B[k][n] = x[nbr(row n, o)][ci] (the gathered source rows, 0 if absent),
+//   D[m][n] = y[row n][co0 + m],
+// with lane l supplying A[l % 16][l / 16] and B[l / 16][l % 16] and holding
+// D[4 (l / 16) + r][l % 16], r < 4.  For a block of 16 source channels ci0,
+// lane l loads the 16 bytes x[nb][ci0 + 4 (l / 16) .. + 3] once; MFMA s of the
+// block then contracts channel ci0 + 4 (l / 16) + s on both operands.  Each
+// output row is written once, as 16-byte stores of 4 channels.
+// Needs c_src and c_dst multiples of 16 and 16-byte aligned src and dst.
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void k_mfma_f32(DirectK a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (t >= a.n_tiles) return;  // wave-uniform
+  const int n = lane & 15, g = lane >> 4;
+  const int co0 = blockIdx.y * 16;
+  const int kvol = a.kvol, c_src = a.c_src;
+  const float* src = static_cast<const float*>(a.src);
+  const float* w = static_cast<const float*>(a.w);
+  const int32_t row = dbg_opt(a.tile_rows[t * kTile + n], a.n_dest, TS_DEBUG_DST_ROW);
+  const uint64_t tm = a.tile_mask[t];
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  for (uint64_t mm = tm; mm; mm &= mm - 1) {  // wave-uniform
+    const int o = __builtin_ctzll(mm);
+    const int32_t nb = row >= 0 ? dbg_opt(a.nbr[static_cast<int64_t>(row) * kvol + o], a.n_src, TS_DEBUG_SRC_ROW) : -1;
+    const int os = a.mirror ? kvol - 1 - o : o;
+    const float* wo = w + static_cast<int64_t>(os) * a.w_cin * a.w_cout;
+    const float* xs = src + static_cast<int64_t>(nb) * c_src;
+    for (int ci0 = 0; ci0 < c_src; ci0 += 16) {
+      const int ci = ci0 + 4 * g;
+      f32x4_t xv = {0.f, 0.f, 0.f, 0.f};
+      if (nb >= 0) xv = *reinterpret_cast<const f32x4_t*>(xs + ci);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float av = a.transpose ? wo[static_cast<int64_t>(co0 + n) * a.w_cout + ci + q]
+                                     : wo[static_cast<int64_t>(ci + q) * a.w_cout + co0 + n];
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, xv[q], acc, 0, 0, 0);
+      }
+    }
+  }
+  if (row < 0) return;
+  *reinterpret_cast<f32x4_t*>(static_cast<float*>(a.dst) + static_cast<int64_t>(row) * a.c_dst + co0 + 4 * g) = acc;
+}
+
+bool mfma_f32_fits(const DirectK& k) {
+  const uintptr_t s = reinterpret_cast<uintptr_t>(k.src), d = reinterpret_cast<uintptr_t>(k.dst);
+  return k.c_src % 16 == 0 && k.c_dst % 16 == 0 && (s & 15) == 0 && (d & 15) == 0;
+}
+
 // ---------------------------------------------------------------- dispatch helpers
 template <typename T, typename OT>
 hipError_t direct_launch(const DirectK& k, hipStream_t s) {
@@ -233,6 +288,11 @@ hipError_t launch_direct(const ConvArgs& a, hipStream_t s) {
   k.mirror = a.mirror;
   k.dst = a.dst;
   k.c_dst = a.c_dst;
+  if (a.in_dtype == TS_F32 && mfma_f32_fits(k)) {  // fp32 in means fp32 out
+    const dim3 grid(static_cast<unsigned>(ceil_div<int64_t>(k.n_tiles, 4)), static_cast<unsigned>(k.c_dst / 16));
+    k_mfma_f32<<<grid, 256, 0, s>>>(k);
+    return hipGetLastError();
+  }
   switch (a.in_dtype) {
     case TS_F32: return direct_dispatch_out<float>(k, a.out_dtype, s);
     case TS_F16: return direct_dispatch_out<_Float16>(k, a.out_dtype, s);

@@ -54,6 +54,9 @@ CONV_CASES = [
     ("down_f16_64x128", synth.make("down", scale=0.03).coords, 2, 2, 64, 128, "f16"),
     ("down_bf16_k3s2", synth.random_coords(15, 1500, 3, 2, 24, lo=-12), 3, 2, 32, 32, "bf16"),
     ("down_f32_2d", synth.random_coords(16, 900, 2, 2, 50), 2, 2, 7, 9, "f32"),
+    # fp32 on the matrix cores: several 16-channel blocks on both sides
+    ("fuzz_f32_48x32", synth.random_coords(17, 1200, 3, 2, 14, lo=-7), 3, 1, 48, 32, "f32"),
+    ("down_f32_32x64", synth.random_coords(18, 1500, 3, 2, 24, lo=-12), 2, 2, 32, 64, "f32"),
 ]
 CONV_IDS = [c[0] for c in CONV_CASES]
 
@@ -223,3 +226,30 @@ def test_unaligned_weights(ts, case):
     rows = oc.shape[0]
     assert torch.equal(a[:rows], b[:rows]), name
     assert_feature_close(b[:rows], oracle.conv_fwd(tr, x, w, rows), DT[dt], f"{name} unaligned weights")
+
+
+@pytest.mark.parametrize("case", [c for c in CONV_CASES if c[6] == "f32" and c[4] % 16 == 0 and c[5] % 16 == 0],
+                         ids=lambda c: c[0])
+def test_fp32_matrix_cores_and_fma_agree(ts, case):
+    """fp32 features with channels in multiples of 16 run on the fp32 matrix
+    cores; a feature matrix that is not 16-byte aligned takes the FMA kernel.
+    Both match the oracle, forward and dgrad."""
+    name, c, k, s, cin, cout, dt = case
+    km, tr, oc, x, w, dy = make_problem(c, k, s, cin, cout, dt, 800)
+    wd = dev(w)
+    xa = dev(x)
+    xu = torch.empty(xa.numel() + 1, dtype=torch.float32, device="cuda")[1:].view_as(xa)  # 4 bytes off
+    xu.copy_(xa)
+    ref = oracle.conv_fwd(tr, x, w, oc.shape[0])
+    for tag, xx in (("aligned", xa), ("unaligned", xu)):
+        y = ts.conv_fwd(km, xx, wd)
+        assert_feature_close(y[:oc.shape[0]], ref, torch.float32, f"{name} fwd fp32 {tag}")
+    ref = oracle.conv_dgrad(tr, dy, w, c.shape[0])
+    n_dy = c.shape[0] if s == 1 else km.s.n_out_cap
+    dya = torch.zeros((n_dy, cout), dtype=torch.float32, device="cuda")
+    dya[:oc.shape[0]] = dev(dy)
+    dyu = torch.empty(dya.numel() + 1, dtype=torch.float32, device="cuda")[1:].view_as(dya)
+    dyu.copy_(dya)
+    for tag, g in (("aligned", dya), ("unaligned", dyu)):
+        dx = ts.conv_dgrad(km, g, wd)
+        assert_feature_close(dx, ref, torch.float32, f"{name} dgrad fp32 {tag}")
