@@ -26,7 +26,8 @@
 // compute wave passes the barriers of the steps its tile lacks without
 // work, and its gathers run ahead of the barriers (they do not depend on the
 // weights).  Blocks are numbered so that each XCD walks a contiguous range
-// of tiles (a tile's columns fetch the same source rows from the same L2).
+// of block indexes (a tile's columns fetch the same source rows from the
+// same L2); block b holds tiles b, b + nblk, ... (nblk blocks per column).
 //
 // Weights reach LDS as stored: the forward layout W[o][c_src][c_dst] row by
 // row (fragments built with gfx950's transposing LDS reads), the dgrad
@@ -324,9 +325,13 @@ __global__ __launch_bounds__(64 * (fod_tiles(KB, MW, MH) * (MW / MH) + 1)) void 
     return;
   }
 
-  // compute wave: tile t, output channels n0 + 16 MH h .. + 16 MH
+  // compute wave: tile t, output channels n0 + 16 MH h .. + 16 MH.  The
+  // block's tiles are tb, tb + nblk, tb + 2 nblk, ...: tiles from distant
+  // parts of the scene share a block, so that blocks whose lockstep steps
+  // wait on their densest tile carry similar loads (on the ring scan in row
+  // order, 26 against 28.5 us with NT consecutive tiles per block).
   const int h = wave % WPT;
-  const int64_t t = tb * NT + wave / WPT;
+  const int64_t t = tb + static_cast<int64_t>(wave / WPT) * a.nblk;
   const bool has_tile = t < a.n_gtiles;
   const int nw0 = n0 + 16 * MH * h;
   const int acc_off = kSlots * SLICE + wave * ACC;  // this wave's accumulator (row-size aligned)
