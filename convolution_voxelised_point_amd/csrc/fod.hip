@@ -504,8 +504,12 @@ __global__ __launch_bounds__(64 * (fod_tiles(KB, MW, MH) * (MW / MH) + 1)) void 
   }
 }
 
-// Column width in MFMA blocks of 16 output channels.
-int fod_mw(int c_dst) { return c_dst > 32 ? 4 : (c_dst > 16 ? 2 : 1); }
+// Column width in MFMA blocks of 16 output channels.  Layers of up to 64
+// output channels take columns of 32: a block then holds eight tiles (one
+// wave each) instead of four (two waves each), and the two columns fetch
+// every source row once each; on the ring scan (64 -> 64) that measured
+// 25.0 against 26.0 us.  Wider layers keep columns of 64.
+int fod_mw(int c_dst) { return c_dst > 64 ? 4 : (c_dst > 16 ? 2 : 1); }
 
 template <typename T, int KB, int MW>
 hipError_t launch_kb_mw(FodK k, int wm, hipStream_t s) {
