@@ -113,12 +113,18 @@ def test_full_down_strided_f16(ts):
     assert_feature_close(s32.y[:n_o], ref, torch.float16, "down fwd fp32 out")
 
 
-def test_full_generative_f16(ts):
+@pytest.mark.parametrize("order", ["groups", "sorted"])
+def test_full_generative_f16(ts, order):
     """Generative stride-1 Conv3d k3 on the ring scan: the 1.77M generated
     sites in first-occurrence order, the target map bit-exact, every output
-    row against the oracle."""
+    row against the oracle; with pair groups only (fetch-on-demand, as the
+    benchmark runs it) and with the neighbour table sorted by offset mask
+    (implicit GEMM)."""
     w = synth.make("lidar")
-    s = bench.setup_generative(ts, w)
+    flags = None if order == "groups" else 0
+    s = bench.setup_generative(ts, w, kmap_flags=flags)
+    if order == "groups":
+        assert "nbr" not in s.kmap.rel_arrays("fwd")
     s.run_once()
     assert int(s.flags.item()) == 0
     oc = oracle.generative_support(w.coords, 3)
@@ -132,7 +138,7 @@ def test_full_generative_f16(ts):
     ref = oracle.conv_fwd(tr, w.x, w.w, s.m)
     assert_feature_close(s.y, ref, torch.float16, "generative fwd fp16 out")
     del s
-    s32 = bench.setup_generative(ts, w, out_dtype=torch.float32)
+    s32 = bench.setup_generative(ts, w, kmap_flags=flags, out_dtype=torch.float32)
     s32.run_once()
     assert_feature_close(s32.y, ref, torch.float16, "generative fwd fp32 out")
 
