@@ -300,19 +300,26 @@ __device__ __forceinline__ void load_offsets(const RelK& a, int8_t* offs) {
   __syncthreads();
 }
 
-// Pair groups of the two group tiles (TS_GTILE = 128 rows) of a workgroup of
-// 256 destination rows, one lane per row (thread i = slot i % 128 of tile
-// 2 * blockIdx.x + i / 128).  `nb(o)` is the lane's source row at offset o,
-// read only where bit o of `mask` is set.  Per offset, each wavefront counts
-// its rows by a ballot; the first wavefront of each tile turns the counts into
-// the offsets' padded runs (an exclusive scan over offsets of whole groups of
-// 16) and the tile's counts; every lane then writes its pairs at its run's
-// start plus its rank among the tile's rows with that offset, so each run
-// lists destination rows in order.  Every thread must call this (barriers).
+// Group tiles of a 256-row workgroup: TS_GTILE rows are kWpt wavefronts,
+// and a workgroup covers kTpb tiles.
+constexpr int kWpt = TS_GTILE / 64;
+constexpr int kTpb = 256 / TS_GTILE;
+static_assert(TS_GTILE % 64 == 0 && 256 % TS_GTILE == 0, "group tiles of whole wavefronts within a workgroup");
+
+// Pair groups of the kTpb group tiles of a workgroup of 256 destination
+// rows, one lane per row (thread i = slot i % TS_GTILE of tile
+// kTpb * blockIdx.x + i / TS_GTILE).  `nb(o)` is the lane's source row at
+// offset o, read only where bit o of `mask` is set.  Per offset, each
+// wavefront counts its rows by a ballot; the first wavefront of each tile
+// turns the counts into the offsets' padded runs (an exclusive scan over
+// offsets of whole groups of 16) and the tile's counts; every lane then
+// writes its pairs at its run's start plus its rank among the tile's rows
+// with that offset, so each run lists destination rows in order.  Every
+// thread must call this (barriers).
 template <int KVMAX, typename NB>
 __device__ __forceinline__ void emit_groups(const RelK& a, int kvol, uint64_t mask, NB nb) {
-  __shared__ int gw[4][KVMAX];      // pairs per wavefront and offset
-  __shared__ int gstart[2][KVMAX];  // first entry of each offset's run, per tile
+  __shared__ int gw[4][KVMAX];         // pairs per wavefront and offset
+  __shared__ int gstart[kTpb][KVMAX];  // first entry of each offset's run, per tile
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const uint64_t lt = (1ull << lane) - 1;
 #pragma unroll
@@ -322,10 +329,12 @@ __device__ __forceinline__ void emit_groups(const RelK& a, int kvol, uint64_t ma
     if (lane == 0) gw[wave][o] = __popcll(b);
   }
   __syncthreads();
-  const int h = threadIdx.x >> 7;
-  const int64_t gt = static_cast<int64_t>(blockIdx.x) * 2 + h;
-  if ((wave & 1) == 0) {  // wave-uniform: the first wavefront of each tile
-    const int c = lane < kvol ? gw[wave][lane] + gw[wave + 1][lane] : 0;
+  const int h = wave / kWpt, wt = wave % kWpt;  // tile of the workgroup, wavefront of the tile
+  const int64_t gt = static_cast<int64_t>(blockIdx.x) * kTpb + h;
+  if (wt == 0) {  // wave-uniform: the first wavefront of each tile
+    int c = 0;
+#pragma unroll
+    for (int i = 0; i < kWpt; ++i) c += lane < kvol ? gw[wave + i][lane] : 0;
     const int n16 = (c + 15) & ~15;
     int incl = n16;
 #pragma unroll
@@ -341,22 +350,27 @@ __device__ __forceinline__ void emit_groups(const RelK& a, int kvol, uint64_t ma
   __syncthreads();
   if (gt >= a.n_gtiles) return;
   const int64_t ebase = gt * kvol * TS_GTILE;
-  const uint8_t slot = static_cast<uint8_t>(threadIdx.x & 127);
+  const uint8_t slot = static_cast<uint8_t>(threadIdx.x % TS_GTILE);
 #pragma unroll
   for (int o = 0; o < KVMAX; ++o) {
     if (o >= kvol) break;
     const bool has = (mask >> o) & 1;
     const uint64_t b = __ballot(has);
     if (!has) continue;
-    const int pos = gstart[h][o] + ((wave & 1) ? gw[wave - 1][o] : 0) + __popcll(b & lt);
+    int before = 0;  // the tile's rows with the offset in earlier wavefronts
+#pragma unroll
+    for (int i = 0; i < kWpt - 1; ++i) before += i < wt ? gw[wave - wt + i][o] : 0;
+    const int pos = gstart[h][o] + before + __popcll(b & lt);
     a.gsrc[ebase + pos] = nb(o);
     a.gslot[ebase + pos] = slot;
   }
   // the pad entries that complete each offset's last group: no source row
   // and the sink slot TS_GTILE
-  for (int idx = threadIdx.x & 127; idx < kvol * 16; idx += 128) {
+  for (int idx = threadIdx.x % TS_GTILE; idx < kvol * 16; idx += TS_GTILE) {
     const int o = idx >> 4, k = idx & 15;
-    const int c = gw[2 * h][o] + gw[2 * h + 1][o];
+    int c = 0;
+#pragma unroll
+    for (int i = 0; i < kWpt; ++i) c += gw[kWpt * h + i][o];
     const int rem = c & 15;
     if (rem != 0 && k >= rem) {
       const int64_t e = ebase + gstart[h][o] + (c - rem) + k;
@@ -466,7 +480,7 @@ __global__ __launch_bounds__(256) void k_rel_probe_any(RelK a, int natural) {
 }
 
 // Pair groups of a relation that has its neighbour table (relations the
-// runtime-kvol probe builds): one lane per destination row, 256 rows (two
+// runtime-kvol probe builds): one lane per destination row, 256 rows (kTpb
 // group tiles) per workgroup.
 __global__ __launch_bounds__(256) void k_groups_from_table(RelK a) {
   const int64_t row = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
@@ -655,14 +669,14 @@ __global__ __launch_bounds__(256) void k_pairs_fill_groups(RelK a, int64_t nblk,
                                                            int32_t* __restrict__ pair_out) {
   __shared__ int wave_pos[4][TS_MAX_KVOL];
   __shared__ int wave_cnt[4][TS_MAX_KVOL];
-  __shared__ int run0[2][TS_MAX_KVOL];
+  __shared__ int run0[kTpb][TS_MAX_KVOL];
   const int64_t n_dest = dest_count(a.n_dest, a.n_dest_cap);
   const int64_t row = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   const uint64_t mask = row < n_dest ? a.row_mask[row] : 0;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const uint64_t below = (1ull << lane) - 1;
-  const int h = threadIdx.x >> 7;
-  const int64_t gt = static_cast<int64_t>(blockIdx.x) * 2 + h;
+  const int h = wave / kWpt, wt = wave % kWpt;  // tile of the workgroup, wavefront of the tile
+  const int64_t gt = static_cast<int64_t>(blockIdx.x) * kTpb + h;
   if (blockIdx.x == 0 && threadIdx.x <= a.kvol) {  // clamped: lists never run past their capacity
     const int64_t v = threadIdx.x < a.kvol ? base[threadIdx.x * nblk] : *total;
     pair_start[threadIdx.x] = v < pair_cap ? v : pair_cap;
@@ -671,7 +685,7 @@ __global__ __launch_bounds__(256) void k_pairs_fill_groups(RelK a, int64_t nblk,
     const uint64_t bal = __ballot((mask >> o) & 1);
     if (lane == 0) wave_cnt[wave][o] = __popcll(bal);
   }
-  if ((wave & 1) == 0) {  // the tile's run starts, from its group counts
+  if (wt == 0) {  // the tile's run starts, from its group counts
     const int c = lane < a.kvol && gt < a.n_gtiles ? a.gcount[gt * a.kvol + lane] : 0;
     const int n16 = (c + 15) & ~15;
     int incl = n16;
@@ -701,7 +715,10 @@ __global__ __launch_bounds__(256) void k_pairs_fill_groups(RelK a, int64_t nblk,
     const int rank = __popcll(bal & below);
     const int pos = wave_pos[wave][o] + rank;
     if (pos >= pair_cap) continue;
-    const int in_tile = run0[h][o] + ((wave & 1) ? wave_cnt[wave - 1][o] : 0) + rank;
+    int before = 0;  // the tile's rows with the offset in earlier wavefronts
+#pragma unroll
+    for (int i = 0; i < kWpt - 1; ++i) before += i < wt ? wave_cnt[wave - wt + i][o] : 0;
+    const int in_tile = run0[h][o] + before + rank;
     pair_out[pos] = static_cast<int32_t>(row);
     pair_in[pos] = a.gsrc[ebase + in_tile];
   }
