@@ -682,8 +682,9 @@ def measure_pixels(ts, steps, warmup):
 
 def measure_train(ts, steps, warmup):
     """The training step with its default map (a neighbour table sorted by
-    offset mask: the implicit GEMM) and, for comparison, with pair groups
-    only (the fetch-on-demand forward and dgrad)."""
+    offset mask: the implicit GEMM), also cold (each step after a cache
+    eviction), and, for comparison, with pair groups only (the
+    fetch-on-demand forward and dgrad)."""
     w = synth.make("train")
     out = {"workload": "train"}
     for name, flags in (("implicit_gemm_sorted", None),
@@ -701,6 +702,10 @@ def measure_train(ts, steps, warmup):
                "step_tflops": 3 * flop / (ms * 1e-3) / 1e12}
         out["n"], out["pairs"] = s.n, P
         if flags is None:
+            # cold: eager steps, each after a 512 MiB write that evicts the caches
+            ms_cold, st_cold = run_cold(s.fns, s.names, COLD_STEPS)
+            rec["ms_per_step_cold"] = ms_cold
+            rec["stages_us_cold"] = {k: round(v, 3) for k, v in st_cold.items()}
             out.update(rec)
         else:
             out[name] = rec
