@@ -114,6 +114,8 @@ CONV = [
     ("down_f16_64x128", synth.make("down", scale=0.03).coords, 2, 2, 64, 128, "f16"),
     ("down_bf16_k3s2", synth.random_coords(15, 1500, 3, 2, 24, lo=-12), 3, 2, 32, 32, "bf16"),
     ("k1_f16_64x32", synth.random_coords(16, 700, 3, 2, 12), 1, 1, 64, 32, "f16"),
+    # 64 offsets, the most a map holds: every lane of a step walk is an offset
+    ("k4s2_kvol64_f16_64", synth.random_coords(19, 1500, 3, 2, 20, lo=-10), 4, 2, 64, 64, "f16"),
 ]
 
 
