@@ -14,10 +14,11 @@
 // distinct, and one wave owns each accumulator tile and adds its groups in
 // a fixed offset order, so results are bitwise repeatable.
 //
-// Work split.  A block holds NT tiles, each owned by one or two compute waves
-// (two split a 64-channel column into halves of 32: smaller accumulators,
-// two waves per SIMD to overlap each other's waits), and one loader wave; a
-// block column covers up to 64 output channels.  The block steps through the
+// Work split.  A block covers one column of output channels -- 32 for
+// layers of up to 64 outputs, else 64 -- for NT tiles, with one compute
+// wave per 32 channels of a tile (a 64-channel column is split into halves:
+// smaller accumulators, more waves to overlap each other's waits), and one
+// loader wave.  The block steps through the
 // offsets in lockstep: barrier k means that step k's weights sit in LDS (a
 // ring of three slices, loaded by the loader wave two steps ahead with
 // direct global-to-LDS copies) and that every compute wave is done with the
