@@ -187,12 +187,64 @@ static void supports() {
                      FAKE, vb - 1, nullptr, nullptr) == TS_ERR_INVALID_ARG);
 }
 
+static void fused_and_others() {
+  // strided forward with support generation: every argument is checked
+  // before the first launch
+  ts_kmap km;
+  memset(&km, 0, sizeof km);
+  const size_t kb = ts_kmap_bytes(100, 100, 3, 2, 2, 0) + ts_support_scratch_bytes(100);
+  auto strided = [&](int stride, size_t bytes, int cin, void* y, ts_dtype in, ts_dtype out, ts_dataflow df) {
+    return ts_conv_fwd_strided(FAKE_I, 100, 3, FAKE, 256, 2, stride, 0, reinterpret_cast<int32_t*>(FAKE),
+                               reinterpret_cast<int64_t*>(FAKE), FAKE, 256, nullptr, FAKE, bytes, &km, FAKE, cin, FAKE,
+                               64, y, in, out, df, FAKE, size_t{1} << 30, nullptr);
+  };
+  EXPECT(strided(1, kb, 64, FAKE, TS_F16, TS_F16, TS_DATAFLOW_AUTO) == TS_ERR_INVALID_ARG);      // stride 1
+  EXPECT(strided(2, kb - 1, 64, FAKE, TS_F16, TS_F16, TS_DATAFLOW_AUTO) == TS_ERR_INVALID_ARG);  // short map buffer
+  EXPECT(strided(2, kb, 0, FAKE, TS_F16, TS_F16, TS_DATAFLOW_AUTO) == TS_ERR_INVALID_ARG);       // no channels
+  EXPECT(strided(2, kb, 64, nullptr, TS_F16, TS_F16, TS_DATAFLOW_AUTO) == TS_ERR_INVALID_ARG);   // no output
+  EXPECT(strided(2, kb, 64, FAKE, TS_F16, TS_BF16, TS_DATAFLOW_AUTO) == TS_ERR_UNSUPPORTED);     // f16 -> bf16
+  EXPECT(strided(2, kb, 64, FAKE, TS_F16, TS_F16, TS_DATAFLOW_GATHER_SCATTER) == TS_ERR_INVALID_ARG);  // no pairs
+  // ConvTranspose over a strided relation needs its transposed relation
+  ts_kmap t;
+  memset(&t, 0, sizeof t);
+  t.kvol = 8;
+  t.stride = 2;
+  t.n_in = 100;
+  t.n_out_cap = 60;
+  t.fwd.n_dest_cap = 60;
+  t.fwd.tile_mask = reinterpret_cast<uint64_t*>(uintptr_t{0x2000});
+  t.fwd.row_mask = reinterpret_cast<uint64_t*>(uintptr_t{0x3000});
+  t.fwd.n_tiles = 4;
+  EXPECT(ts_conv_transpose_fwd(&t, FAKE, 16, FAKE, 16, FAKE, TS_F32, TS_F32, TS_DATAFLOW_AUTO, nullptr, 0, nullptr) ==
+         TS_ERR_INVALID_ARG);
+  // graph convolution
+  const int64_t* ip = reinterpret_cast<const int64_t*>(FAKE);
+  EXPECT(ts_graph_conv_fwd(ip, FAKE_I, FAKE_I, 10, 10, 0, FAKE, 8, FAKE, 8, FAKE, TS_F16, TS_F16, nullptr, nullptr) ==
+         TS_ERR_INVALID_ARG);  // no relations
+  EXPECT(ts_graph_conv_fwd(nullptr, FAKE_I, FAKE_I, 10, 10, 3, FAKE, 8, FAKE, 8, FAKE, TS_F16, TS_F16, nullptr,
+                           nullptr) == TS_ERR_INVALID_ARG);  // no CSR offsets
+  EXPECT(ts_graph_conv_fwd(ip, FAKE_I, FAKE_I, -1, 10, 3, FAKE, 8, FAKE, 8, FAKE, TS_F16, TS_F16, nullptr, nullptr) ==
+         TS_ERR_INVALID_ARG);
+  EXPECT(ts_graph_conv_fwd(ip, FAKE_I, FAKE_I, 10, 10, 3, FAKE, 8, FAKE, 8, FAKE, TS_BF16, TS_F16, nullptr, nullptr) ==
+         TS_ERR_UNSUPPORTED);
+  EXPECT(ts_graph_conv_fwd(ip, FAKE_I, FAKE_I, 10, 10, 3, FAKE, 8, FAKE, 8, FAKE, static_cast<ts_dtype>(5), TS_F16,
+                           nullptr, nullptr) == TS_ERR_INVALID_ARG);
+  // devoxelization and pooling
+  EXPECT(ts_devoxelize(FAKE_I, 10, FAKE, 0, FAKE, TS_F32, nullptr) == TS_ERR_INVALID_ARG);
+  EXPECT(ts_devoxelize(nullptr, 10, FAKE, 4, FAKE, TS_F32, nullptr) == TS_ERR_INVALID_ARG);
+  EXPECT(ts_devoxelize(FAKE_I, 10, FAKE, 4, FAKE, static_cast<ts_dtype>(-2), nullptr) == TS_ERR_INVALID_ARG);
+  EXPECT(ts_pool_fwd(&t, FAKE, 8, FAKE, TS_F16, TS_F16, 2, nullptr) == TS_ERR_INVALID_ARG);  // mode
+  EXPECT(ts_pool_fwd(&t, FAKE, 0, FAKE, TS_F16, TS_F16, TS_POOL_MAX, nullptr) == TS_ERR_INVALID_ARG);
+  EXPECT(ts_pool_fwd(&t, FAKE, 8, FAKE, TS_F16, TS_BF16, TS_POOL_MAX, nullptr) == TS_ERR_UNSUPPORTED);
+}
+
 int main() {
   sizes();
   hash();
   kmap_build();
   conv();
   supports();
+  fused_and_others();
   if (g_fail) fprintf(stderr, "%d expectation(s) failed\n", g_fail);
   else printf("abi host checks: all passed\n");
   return g_fail ? 1 : 0;
