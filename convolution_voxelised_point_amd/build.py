@@ -10,7 +10,9 @@ finds them in-tree.
 from __future__ import annotations
 
 import glob
+import json
 import os
+import re
 import subprocess
 import sys
 from concurrent.futures import ThreadPoolExecutor
@@ -46,15 +48,55 @@ def cuid(src: str) -> str:
     return "ts_" + os.path.splitext(os.path.basename(src))[0]
 
 
+_REMARK = "-Rpass-analysis=kernel-resource-usage"
+_FIELDS = {"VGPRs": "vgprs", "AGPRs": "agprs", "TotalSGPRs": "sgprs", "ScratchSize [bytes/lane]": "scratch_bytes",
+           "Occupancy [waves/SIMD]": "waves_per_simd", "SGPRs Spill": "sgpr_spill", "VGPRs Spill": "vgpr_spill",
+           "LDS Size [bytes/block]": "lds_bytes"}
+
+
+def parse_resource_remarks(text: str) -> dict:
+    """Per-kernel register, scratch and LDS use from the compiler's
+    kernel-resource-usage remarks: {mangled name: {field: int}}."""
+    out, cur = {}, None
+    for line in text.splitlines():
+        if "remark:" not in line:
+            continue
+        body = line.split("remark:", 1)[1].replace("[" + _REMARK + "]", "").strip()
+        if body.startswith("Function Name:"):
+            cur = out.setdefault(body.split(":", 1)[1].strip(), {})
+            continue
+        m = re.match(r"(.+?):\s*(-?\d+)$", body)
+        if cur is not None and m and m.group(1) in _FIELDS:
+            cur[_FIELDS[m.group(1)]] = int(m.group(2))
+    return out
+
+
+def resources_path(src: str) -> str:
+    return os.path.join(BUILD_DIR, os.path.basename(src) + ".resources.json")
+
+
 def _compile(src: str, debug: bool = False) -> str:
+    """Compiles one source; the regular build also writes the kernels'
+    resource use (registers, scratch, LDS) beside the object."""
     obj = os.path.join(DEBUG_BUILD_DIR if debug else BUILD_DIR, os.path.basename(src) + ".o")
-    extra = ["-DTS_DEBUG_CHECKS"] if debug else []
+    extra = ["-DTS_DEBUG_CHECKS"] if debug else [_REMARK]
     cmd = [HIPCC, *CFLAGS, *extra, f"-cuid={cuid(src)}", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
+    if not debug:
+        with open(resources_path(src), "w") as f:
+            json.dump(parse_resource_remarks(r.stderr), f, indent=0, sort_keys=True)
     noise = "is not a recognized feature for this target"
-    errs = "\n".join(l for l in r.stderr.splitlines() if noise not in l)
+    kept, in_remark = [], False
+    for line in r.stderr.splitlines():
+        if ": remark:" in line:
+            in_remark = True  # a remark and the source excerpt under it
+        elif ": warning:" in line or ": error:" in line or ": note:" in line:
+            in_remark = False
+        if not in_remark and noise not in line:
+            kept.append(line)
+    errs = "\n".join(kept)
     if errs.strip():
         sys.stderr.write(errs + "\n")
     return obj

@@ -72,7 +72,7 @@ struct FMfma<__bf16> {
 };
 
 constexpr int kR = TS_GTILE;          // destination rows per tile (row kR of an accumulator: pad sink)
-constexpr int kSlots = 3;             // weight slices in LDS: offsets o, o + 1, o + 2
+constexpr int kSlots = 3;             // weight slots in LDS: steps k, k + 1, k + 2
 constexpr int kLdsBytes = 160 * 1024; // LDS of one block
 // Pipeline depths (groups in flight per wave): the fetched source rows of
 // RB groups (4 when three waves share a SIMD's registers, else 8), the
@@ -89,13 +89,17 @@ constexpr int fod_acc_bytes(int mh) { return (kR + 1) * 64 * mh; }
 // fetched rows need the registers).
 constexpr int fod_max_nw(int kb) { return kb <= 2 ? 8 : 6; }
 // Tiles per block: as many tiles' accumulators (MW / MH waves each) as fit
-// beside the weight ring, within that wave count.
-constexpr int fod_tiles(int kb, int mw, int mh) {
-  return (kLdsBytes - kSlots * fod_slice_bytes(kb, mw)) / (fod_acc_bytes(mh) * (mw / mh)) * (mw / mh) >
+// beside the weight ring (slots of `ops` slices), within that wave count.
+constexpr int fod_tiles(int kb, int mw, int mh, int ops) {
+  return (kLdsBytes - kSlots * ops * fod_slice_bytes(kb, mw)) / (fod_acc_bytes(mh) * (mw / mh)) * (mw / mh) >
                  fod_max_nw(kb)
              ? fod_max_nw(kb) / (mw / mh)
-             : (kLdsBytes - kSlots * fod_slice_bytes(kb, mw)) / (fod_acc_bytes(mh) * (mw / mh));
+             : (kLdsBytes - kSlots * ops * fod_slice_bytes(kb, mw)) / (fod_acc_bytes(mh) * (mw / mh));
 }
+// Offsets per lockstep step: two when slots of two slices still leave room
+// for as many tiles as slots of one, else one.
+constexpr int fod_ops(int kb, int mw, int mh) { return fod_tiles(kb, mw, mh, 2) >= fod_tiles(kb, mw, mh, 1) ? 2 : 1; }
+#define FOD_OPS_OVERRIDE(x) (x)
 
 struct FodK {
   const int32_t* gcount;  // [n_gtiles][kvol]
@@ -227,11 +231,11 @@ struct Unroll<N, N> {
   static __device__ __forceinline__ void run(F&&) {}
 };
 
-template <typename T, int KB, int MW, int MH, int WM>
-__global__ __launch_bounds__(64 * (fod_tiles(KB, MW, MH) * (MW / MH) + 1)) void k_fod(FodK a) {
+template <typename T, int KB, int MW, int MH, int WM, int OPS>
+__global__ __launch_bounds__(64 * (fod_tiles(KB, MW, MH, OPS) * (MW / MH) + 1)) void k_fod(FodK a) {
   typedef typename FMfma<T>::frag Frag;
   constexpr int WPT = MW / MH;        // compute waves per tile (one per MH blocks of 16 channels)
-  constexpr int NT = fod_tiles(KB, MW, MH);  // tiles per block
+  constexpr int NT = fod_tiles(KB, MW, MH, OPS);  // tiles per block
   constexpr int NW = NT * WPT;        // compute waves per block
   constexpr int CB = 16 * MW;         // output channels of the block column
   constexpr int NCH = 4 * MH;         // 16-byte fp32 chunks per accumulator row
@@ -239,9 +243,10 @@ __global__ __launch_bounds__(64 * (fod_tiles(KB, MW, MH) * (MW / MH) + 1)) void 
   constexpr int WROW = WM == 0 ? CB * 2 : C_SRC * 2;  // bytes per stored weight row in LDS
   constexpr int SLICE = fod_slice_bytes(KB, MW);      // bytes per offset
   constexpr int COPIES = SLICE / 1024;                // 16-byte copies per lane and offset
+  constexpr int SLOT = OPS * SLICE;                   // bytes per step
   constexpr int ACC = fod_acc_bytes(MH);
-  static_assert(kSlots * SLICE + NW * ACC <= kLdsBytes, "LDS budget");
-  __shared__ __attribute__((aligned(1024))) char lds[kSlots * SLICE + NW * ACC];
+  static_assert(kSlots * SLOT + NW * ACC <= kLdsBytes, "LDS budget");
+  __shared__ __attribute__((aligned(1024))) char lds[kSlots * SLOT + NW * ACC];
 
   constexpr int RB = fod_rb(NW + 1);  // fetched-row register sets
   constexpr int DB = RB - 1;          // groups the row fetches run ahead
@@ -260,20 +265,25 @@ __global__ __launch_bounds__(64 * (fod_tiles(KB, MW, MH) * (MW / MH) + 1)) void 
   if (tb >= a.nblk) return;  // the whole block, before any barrier
   const int n0 = column * CB;
   const int kvol = a.kvol;
-  // The block's steps k = 0 .. kvol-1 take offsets (k + rot) mod kvol:
-  // blocks that run at the same time start at different offsets, so their
-  // weight copies read different slices (one slice read by every block at
-  // once queues on the few L2 channels that hold it).
+  // The block takes the offsets in the order k = 0 .. kvol-1, offset
+  // (k + rot) mod kvol, OPS of them per lockstep step (step k / OPS, slice
+  // k % OPS of its slot): blocks that run at the same time start at
+  // different offsets, so their weight copies read different slices (one
+  // slice read by every block at once queues on the few L2 channels that
+  // hold it).
   const int rot = static_cast<int>(tb % kvol);
+  const int nsteps = (kvol + OPS - 1) / OPS;
 
   if (wave == NW) {
-    // Loader: step k's weights into slot k % 3, two steps ahead of the
+    // Loader: step s's weights into slot s % 3, two steps ahead of the
     // compute waves, with direct global-to-LDS copies (element by element
     // through registers when the weights are not 16-byte aligned).  Chunk p
     // of a slot (16 bytes): forward layout row ci = p / (CB/8) at swizzled
     // column, dgrad layout row nl = p / (C_SRC/8) likewise; chunks of output
     // channels past c_dst copy a valid chunk of the slice (they feed
-    // accumulator channels that are never written out).
+    // accumulator channels that are never written out).  A last step with
+    // fewer than OPS offsets copies its first slice again into the unused
+    // ones, so every step issues the same number of copies.
     const T* w = static_cast<const T*>(a.w);
     auto chunk_src = [&](int os, int p) -> int64_t {
       if constexpr (WM == 0) {
@@ -288,10 +298,9 @@ __global__ __launch_bounds__(64 * (fod_tiles(KB, MW, MH) * (MW / MH) + 1)) void 
         return (static_cast<int64_t>(os) * a.c_dst + (n < a.c_dst ? n : 0)) * C_SRC + 8 * part;
       }
     };
-    auto copy = [&](int k) {
+    auto copy_slice = [&](int k, char* slot) __attribute__((always_inline)) {
       const int o = k + rot < kvol ? k + rot : k + rot - kvol;
       const int os = a.mirror ? kvol - 1 - o : o;
-      char* slot = lds + (k % kSlots) * SLICE;
       if (a.w_vec) {
 #pragma unroll
         for (int j = 0; j < COPIES; ++j) lds_copy16(w + chunk_src(os, 64 * j + lane), slot + 1024 * j);
@@ -307,21 +316,28 @@ __global__ __launch_bounds__(64 * (fod_tiles(KB, MW, MH) * (MW / MH) + 1)) void 
         }
       }
     };
+    auto copy = [&](int st) __attribute__((always_inline)) {
+#pragma unroll
+      for (int j = 0; j < OPS; ++j) {
+        const int k = st * OPS + j;
+        copy_slice(k < kvol ? k : st * OPS, lds + (st % kSlots) * SLOT + j * SLICE);
+      }
+    };
     copy(0);
-    if (kvol > 1) copy(1);
-    for (int k = 0; k < kvol; ++k) {
-      // step k's weights have landed (only step k + 1's copies may still be
-      // in flight)
+    if (nsteps > 1) copy(1);
+    for (int st = 0; st < nsteps; ++st) {
+      // step st's weights have landed (only step st + 1's copies may still
+      // be in flight)
       if (a.w_vec) {
-        if (k + 1 < kvol)
-          wait_vm<COPIES>();
+        if (st + 1 < nsteps)
+          wait_vm<OPS * COPIES>();
         else
           wait_vm<0>();
       } else {
         wait_lds();
       }
       bare_barrier();
-      if (k + 2 < kvol) copy(k + 2);  // into the slot of step k - 1: every wave is past it
+      if (st + 2 < nsteps) copy(st + 2);  // into the slot of step st - 1: every wave is past it
     }
     return;
   }
@@ -335,7 +351,7 @@ __global__ __launch_bounds__(64 * (fod_tiles(KB, MW, MH) * (MW / MH) + 1)) void 
   const int64_t t = tb + static_cast<int64_t>(wave / WPT) * a.nblk;
   const bool has_tile = t < a.n_gtiles;
   const int nw0 = n0 + 16 * MH * h;
-  const int acc_off = kSlots * SLICE + wave * ACC;  // this wave's accumulator (row-size aligned)
+  const int acc_off = kSlots * SLOT + wave * ACC;  // this wave's accumulator (row-size aligned)
   char* const accb = lds + acc_off;
 #pragma unroll
   for (int i = 0; i < kR * NCH / 64; ++i)
@@ -369,8 +385,9 @@ __global__ __launch_bounds__(64 * (fod_tiles(KB, MW, MH) * (MW / MH) + 1)) void 
   const int tr_b4 = tr_b0 + 4 * WROW;
   const int tr_x0 = 32 * wswz<MW>(8 * kq + trm), tr_x4 = 32 * wswz<MW>(8 * kq + 4 + trm);
 
-  int k_cur = -1;  // step whose fragments are held (barriers 0..k_cur passed)
-  int e_cur = 0;   // end of its groups
+  int k_cur = -1;  // offset (in the block's order) whose fragments are held
+  int s_cur = -1;  // barriers 0..s_cur passed
+  int e_cur = 0;   // end of offset k_cur's groups
 
   // Register rings indexed by group (compile-time positions): source row and
   // slot of each lane (loaded DM groups ahead), the fetched source rows (DB
@@ -378,11 +395,10 @@ __global__ __launch_bounds__(64 * (fod_tiles(KB, MW, MH) * (MW / MH) + 1)) void 
   // group's entries start at a multiple of 16, so lane col's byte is byte
   // col % 4 of its word) and taken out at its use: a ring of byte loads
   // would be widened where the rounds loop back, which waits for them all.
-  // Entry loads go through buffer descriptors over the tile's entries, with
-  // the step's position as the instruction's constant offset; an entry past
-  // the tile reads as 0.  Source-row fetches are not masked: pads (-1) and
-  // entries past the tile's groups read out of range (zeros, no access) or
-  // a row that is never used.
+  // Entry loads go through buffer descriptors over the tile's entries, the
+  // group's position in the scalar offset.  Source-row fetches are not
+  // masked: pads (-1) read out of range (zeros, no access), and groups past
+  // the tile's last fetch rows that are never used.
   int32_t msrc[RS];
   uint32_t mslot[RM];
   Frag xs[RB][KB];
@@ -427,12 +443,14 @@ __global__ __launch_bounds__(64 * (fod_tiles(KB, MW, MH) * (MW / MH) + 1)) void 
     if constexpr (FIRST) return;
     const int v = v0 + p;
     if (v >= G) return;  // wave-uniform
-    if (v >= e_cur) {  // wave-uniform: the first group of the next step the tile has
+    if (v >= e_cur) {  // wave-uniform: the first group of the next offset the tile has
       const int k_new = __builtin_ctzll(present & (~0ull << (k_cur + 1)));
       e_cur = __builtin_amdgcn_readlane(incl, k_new);
-      for (int k = k_cur + 1; k <= k_new; ++k) bare_barrier();
+      const int s_new = k_new / OPS;
+      for (int st = s_cur + 1; st <= s_new; ++st) bare_barrier();
+      s_cur = s_new;
       k_cur = k_new;
-      const char* sl = lds + (k_new % kSlots) * SLICE;
+      const char* sl = lds + (s_new % kSlots) * SLOT + (k_new - s_new * OPS) * SLICE;
 #pragma unroll
       for (int mb = 0; mb < MH; ++mb)
 #pragma unroll
@@ -476,7 +494,7 @@ __global__ __launch_bounds__(64 * (fod_tiles(KB, MW, MH) * (MW / MH) + 1)) void 
     for (int v0 = 0; v0 < G; v0 += RM) round(v0, Fi<0>{});
   }
   // the barriers of the steps past the tile's last one
-  for (int k = k_cur + 1; k < kvol; ++k) bare_barrier();
+  for (int st = s_cur + 1; st < nsteps; ++st) bare_barrier();
   if (!has_tile) return;
 
   // write the tile's rows once (rows at or past the device count are not
@@ -515,7 +533,8 @@ int fod_mw(int c_dst) { return c_dst > 64 ? 4 : (c_dst > 16 ? 2 : 1); }
 template <typename T, int KB, int MW>
 hipError_t launch_kb_mw(FodK k, int wm, hipStream_t s) {
   constexpr int MH = MW >= 2 ? 2 : 1;  // two compute waves per tile for 64-channel columns
-  constexpr int NT = fod_tiles(KB, MW, MH);
+  constexpr int OPS = FOD_OPS_OVERRIDE(fod_ops(KB, MW, MH));
+  constexpr int NT = fod_tiles(KB, MW, MH, OPS);
   constexpr int NW = NT * (MW / MH);
   static_assert(NT >= 1, "a tile fits");
   k.ncol = ceil_div(k.c_dst, 16 * MW);
@@ -525,9 +544,9 @@ hipError_t launch_kb_mw(FodK k, int wm, hipStream_t s) {
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(blocks));
   if (wm == 0)
-    k_fod<T, KB, MW, MH, 0><<<grid, (NW + 1) * 64, 0, s>>>(k);
+    k_fod<T, KB, MW, MH, 0, OPS><<<grid, (NW + 1) * 64, 0, s>>>(k);
   else
-    k_fod<T, KB, MW, MH, 1><<<grid, (NW + 1) * 64, 0, s>>>(k);
+    k_fod<T, KB, MW, MH, 1, OPS><<<grid, (NW + 1) * 64, 0, s>>>(k);
   return hipGetLastError();
 }
 

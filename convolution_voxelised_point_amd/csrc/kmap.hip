@@ -322,7 +322,10 @@ __device__ __forceinline__ void emit_groups(const RelK& a, int kvol, uint64_t ma
   __shared__ int gstart[kTpb][KVMAX];  // first entry of each offset's run, per tile
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const uint64_t lt = (1ull << lane) - 1;
-#pragma unroll
+  // unrolled for the compile-time kernel sizes (at most 27 offsets); the
+  // runtime-size instance (up to TS_MAX_KVOL) keeps its loops
+  constexpr int kUnroll = KVMAX <= 32 ? KVMAX : 1;
+#pragma unroll kUnroll
   for (int o = 0; o < KVMAX; ++o) {
     if (o >= kvol) break;
     const uint64_t b = __ballot((mask >> o) & 1);
@@ -351,7 +354,7 @@ __device__ __forceinline__ void emit_groups(const RelK& a, int kvol, uint64_t ma
   if (gt >= a.n_gtiles) return;
   const int64_t ebase = gt * kvol * TS_GTILE;
   const uint8_t slot = static_cast<uint8_t>(threadIdx.x % TS_GTILE);
-#pragma unroll
+#pragma unroll kUnroll
   for (int o = 0; o < KVMAX; ++o) {
     if (o >= kvol) break;
     const bool has = (mask >> o) & 1;
