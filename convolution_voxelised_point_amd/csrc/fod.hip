@@ -22,8 +22,7 @@
 // offsets in lockstep: barrier k means that step k's weights sit in LDS (a
 // ring of three slices, loaded by the loader wave two steps ahead with
 // direct global-to-LDS copies) and that every compute wave is done with the
-// steps before k.  Step k takes offset (k + rot) mod kvol, rot set by the
-// block, so that blocks running at once copy different weight slices.  A
+// steps before k.  A
 // compute wave passes the barriers of the steps its tile lacks without
 // work, and its gathers run ahead of the barriers (they do not depend on the
 // weights).  Blocks are numbered so that each XCD walks a contiguous range
@@ -265,13 +264,10 @@ __global__ __launch_bounds__(64 * (fod_tiles(KB, MW, MH, OPS) * (MW / MH) + 1)) 
   if (tb >= a.nblk) return;  // the whole block, before any barrier
   const int n0 = column * CB;
   const int kvol = a.kvol;
-  // The block takes the offsets in the order k = 0 .. kvol-1, offset
-  // (k + rot) mod kvol, OPS of them per lockstep step (step k / OPS, slice
-  // k % OPS of its slot): blocks that run at the same time start at
-  // different offsets, so their weight copies read different slices (one
-  // slice read by every block at once queues on the few L2 channels that
-  // hold it).
-  const int rot = static_cast<int>(tb % kvol);
+  // The block takes the offsets in order, OPS of them per lockstep step
+  // (offset k: step k / OPS, slice k % OPS of its slot).  Every block starts
+  // at offset 0: starting each block at its own offset, so that blocks
+  // running at once copy different slices, measured slower on the ring scan.
   const int nsteps = (kvol + OPS - 1) / OPS;
 
   if (wave == NW) {
@@ -298,8 +294,7 @@ __global__ __launch_bounds__(64 * (fod_tiles(KB, MW, MH, OPS) * (MW / MH) + 1)) 
         return (static_cast<int64_t>(os) * a.c_dst + (n < a.c_dst ? n : 0)) * C_SRC + 8 * part;
       }
     };
-    auto copy_slice = [&](int k, char* slot) __attribute__((always_inline)) {
-      const int o = k + rot < kvol ? k + rot : k + rot - kvol;
+    auto copy_slice = [&](int o, char* slot) __attribute__((always_inline)) {
       const int os = a.mirror ? kvol - 1 - o : o;
       if (a.w_vec) {
 #pragma unroll
@@ -357,12 +352,42 @@ __global__ __launch_bounds__(64 * (fod_tiles(KB, MW, MH, OPS) * (MW / MH) + 1)) 
   for (int i = 0; i < kR * NCH / 64; ++i)
     *reinterpret_cast<f32x4*>(accb + (i * 64 + lane) * 16) = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // groups of the tile in step order: lane k < kvol holds the group count of
-  // step k's offset and the end of its groups (inclusive prefix); group v
-  // of the steps is stored group (v + gbase) mod G, gbase the groups of the
-  // offsets before rot
-  const int lane_o = lane + rot < kvol ? lane + rot : lane + rot - kvol;
-  const int cnt = has_tile && lane < kvol ? dbg_req(a.gcount[t * kvol + lane_o], kR + 1, TS_DEBUG_DST_ROW) : 0;
+  const int64_t ebase = t * static_cast<int64_t>(kvol) * kR;
+  const T* src = static_cast<const T*>(a.src);
+  const __amdgpu_buffer_rsrc_t xr =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(src), 0, static_cast<int>(a.src_bytes), 0x00020000);
+
+  // Register rings indexed by group (compile-time positions): source row and
+  // slot of each lane (loaded DM groups ahead), the fetched source rows (DB
+  // groups ahead).  A slot is loaded as the aligned word that holds it (a
+  // group's entries start at a multiple of 16, so lane col's byte is byte
+  // col % 4 of its word) and taken out at its use: a ring of byte loads
+  // would be widened where the rounds loop back, which waits for them all.
+  // Entry loads go through buffer descriptors over the tile's entries, the
+  // group's position in the scalar offset (a wave without a tile gets empty
+  // descriptors: its loads read zeros and touch no memory).  Source-row
+  // fetches are not masked: pads (-1) read out of range (zeros, no access),
+  // and groups past the tile's last fetch rows that are never used.
+  int32_t msrc[RS];
+  uint32_t mslot[RM];
+  Frag xs[RB][KB];
+  Frag af[MH][KB];
+  const int slot_shift = 8 * (col & 3);
+  const __amdgpu_buffer_rsrc_t er_src =
+      __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(a.gsrc + ebase), 0, has_tile ? kvol * kR * 4 : 0, 0x00020000);
+  const __amdgpu_buffer_rsrc_t er_slot =
+      __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(a.gslot + ebase), 0, has_tile ? kvol * kR : 0, 0x00020000);
+  // the entries of groups 0 .. DM-1 (the first round's) go out before the
+  // group counts are read: they need no count (entries past the tile's
+  // groups feed no MFMA)
+  Unroll<DM>::run([&](auto ic) {
+    constexpr int i = decltype(ic)::v;
+    msrc[i % RS] = __builtin_bit_cast(int32_t, __builtin_amdgcn_raw_buffer_load_b32(er_src, 4 * col, 64 * i, 0));
+    mslot[i % RM] = __builtin_amdgcn_raw_buffer_load_b32(er_slot, col & ~3, 16 * i, 0);
+  });
+  // groups of the tile in offset order: lane k < kvol holds the group count
+  // of offset k and the end of its groups (inclusive prefix)
+  const int cnt = has_tile && lane < kvol ? dbg_req(a.gcount[t * kvol + lane], kR + 1, TS_DEBUG_DST_ROW) : 0;
   const int ng = (cnt + 15) >> 4;
   int incl = ng;
 #pragma unroll
@@ -372,12 +397,6 @@ __global__ __launch_bounds__(64 * (fod_tiles(KB, MW, MH, OPS) * (MW / MH) + 1)) 
   }
   const int G = __builtin_amdgcn_readlane(incl, 63);
   const uint64_t present = __ballot(lane < kvol && ng > 0);
-  const int gbase = rot == 0 ? 0 : G - __builtin_amdgcn_readlane(incl, kvol - rot - 1);
-  const int64_t ebase = t * static_cast<int64_t>(kvol) * kR;
-
-  const T* src = static_cast<const T*>(a.src);
-  const __amdgpu_buffer_rsrc_t xr =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(src), 0, static_cast<int>(a.src_bytes), 0x00020000);
 
   // transposing-read addresses of this lane inside a forward-layout slice
   const int trq = lane & 3, trm = (lane >> 2) & 3;
@@ -385,30 +404,10 @@ __global__ __launch_bounds__(64 * (fod_tiles(KB, MW, MH, OPS) * (MW / MH) + 1)) 
   const int tr_b4 = tr_b0 + 4 * WROW;
   const int tr_x0 = 32 * wswz<MW>(8 * kq + trm), tr_x4 = 32 * wswz<MW>(8 * kq + 4 + trm);
 
-  int k_cur = -1;  // offset (in the block's order) whose fragments are held
+  int k_cur = -1;  // offset whose fragments are held
   int s_cur = -1;  // barriers 0..s_cur passed
   int e_cur = 0;   // end of offset k_cur's groups
 
-  // Register rings indexed by group (compile-time positions): source row and
-  // slot of each lane (loaded DM groups ahead), the fetched source rows (DB
-  // groups ahead).  A slot is loaded as the aligned word that holds it (a
-  // group's entries start at a multiple of 16, so lane col's byte is byte
-  // col % 4 of its word) and taken out at its use: a ring of byte loads
-  // would be widened where the rounds loop back, which waits for them all.
-  // Entry loads go through buffer descriptors over the tile's entries, the
-  // group's position in the scalar offset.  Source-row fetches are not
-  // masked: pads (-1) read out of range (zeros, no access), and groups past
-  // the tile's last fetch rows that are never used.
-  int32_t msrc[RS];
-  uint32_t mslot[RM];
-  Frag xs[RB][KB];
-  Frag af[MH][KB];
-  const int slot_shift = 8 * (col & 3);
-  // (a wave without a tile builds them too and never uses them)
-  const __amdgpu_buffer_rsrc_t er_src =
-      __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(a.gsrc + ebase), 0, kvol * kR * 4, 0x00020000);
-  const __amdgpu_buffer_rsrc_t er_slot =
-      __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(a.gslot + ebase), 0, kvol * kR, 0x00020000);
   // accumulator chunk swizzle: chunk c of row r sits at c ^ sw(r) (the
   // chunk_swz layout), so the MH chunks of a lane's row are the address of
   // chunk kq ^ sw(r) with bit 6 and up XORed by 64 mb (rows are 64 MH bytes,
@@ -418,25 +417,27 @@ __global__ __launch_bounds__(64 * (fod_tiles(KB, MW, MH, OPS) * (MW / MH) + 1)) 
 
   // one group position p of a round: the fetch of group v0 + p + DB's
   // source rows, then the entry loads of group v0 + p + DM (groups past the
-  // tile's last read stored group 0), then, outside the first round, the
+  // tile's last read stored group 0; the first round's entries are loaded
+  // before the counts), then, outside the first round, the
   // MFMAs of group v0 + p.  The fetch reads its source-row entry before the
   // entry load of the same step reuses that register.
   auto step = [&](int v0, auto pc, auto firstc) {
     constexpr int p = decltype(pc)::v;
     constexpr bool FIRST = decltype(firstc)::v;
     if constexpr (!FIRST || p + DB >= RM) {
-      const uint32_t off =
-          static_cast<uint32_t>(dbg_opt(msrc[(p + DB) % RS], a.n_src, TS_DEBUG_SRC_ROW)) * (C_SRC * 2) + kq * 16;
+      int32_t ms = msrc[(p + DB) % RS];
+      // (the bounds-check build checks the entries of the tile's groups:
+      // the first round's may lie past them)
+      if constexpr (kDebugChecks) ms = v0 + p + DB < G ? dbg_opt(ms, a.n_src, TS_DEBUG_SRC_ROW) : ms;
+      const uint32_t off = static_cast<uint32_t>(ms) * (C_SRC * 2) + kq * 16;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
         xs[(p + DB) % RB][kb] =
             __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(xr, static_cast<int>(off + kb * 64), 0, 0));
     }
-    if constexpr (!FIRST || p + DM >= RM) {
+    if constexpr (!FIRST) {  // (the first round's entries are loaded above)
       const int g = v0 + p + DM;
-      int sg = g + gbase;
-      sg = sg >= G ? sg - G : sg;
-      sg = g < G ? sg : 0;
+      const int sg = g < G ? g : 0;
       msrc[(p + DM) % RS] = __builtin_bit_cast(int32_t, __builtin_amdgcn_raw_buffer_load_b32(er_src, 4 * col, 64 * sg, 0));
       mslot[(p + DM) % RM] = __builtin_amdgcn_raw_buffer_load_b32(er_slot, col & ~3, 16 * sg, 0);
     }
