@@ -95,6 +95,43 @@ def test_hash_rebuild_same_buffer(ts):
         assert int(flags.item()) == rflags
 
 
+def test_hash_many_rebuilds_and_supports_share_a_buffer(ts):
+    """Seventy builds into one buffer cycle through coordinate sets (a
+    superset, subsets, an empty set, repeated rows), with strided supports
+    written into the same buffer twice on the way; after each build every
+    query must answer as the oracle does and the flags must match, so no
+    build leaves anything a later one reads as its own."""
+    sets = [synth.random_coords(31 + k, n, 3, 2, 24, lo=-12) for k, n in enumerate((2500, 900, 3000, 40))]
+    sets.append(np.concatenate([sets[0][:500], sets[0][[3, 3, 9]]], axis=0))  # repeated rows: DUP
+    sets.append(np.zeros((0, 4), np.int32))
+    cap = ts.ts_hash_capacity(3000, 2.0)
+    buf = torch.zeros(ts.ts_hash_table_bytes(cap), dtype=torch.uint8, device="cuda")
+    flags = torch.zeros(1, dtype=torch.int32, device="cuda")
+    q = np.concatenate([s for s in sets if len(s)] + [synth.random_coords(39, 300, 3, 4, 30, lo=-15)], axis=0)
+    qd = dev(q)
+    got = torch.empty(q.shape[0], dtype=torch.int32, device="cuda")
+    out = torch.empty((3000, 4), dtype=torch.int32, device="cuda")
+    n_out = torch.zeros(1, dtype=torch.int64, device="cuda")
+    scratch = torch.empty(ts.ts_support_scratch_bytes(3000), dtype=torch.uint8, device="cuda")
+    for k in range(70):
+        c = sets[k % len(sets)]
+        if k in (20, 47):
+            flags.zero_()
+            src = sets[2]
+            ts.ts_strided_support(dev(src), 2, out, n_out, buf, cap, scratch, flags)
+            n = int(n_out.item())
+            ref_oc = oracle.strided_support(src, 2)
+            np.testing.assert_array_equal(out[:n].cpu().numpy(), ref_oc)
+            ts.ts_hash_query(buf, cap, qd, got)
+            np.testing.assert_array_equal(got.cpu().numpy(), oracle.hash_query(ref_oc, q)[0], err_msg=f"support {k}")
+        flags.zero_()
+        ts.ts_hash_build(dev(c), buf, cap, flags)
+        ts.ts_hash_query(buf, cap, qd, got)
+        ref, rflags = oracle.hash_query(c, q)
+        np.testing.assert_array_equal(got.cpu().numpy(), ref, err_msg=f"build {k}")
+        assert int(flags.item()) == rflags, f"build {k}"
+
+
 def test_hash_small_reserve_ratio(ts):
     c = synth.random_coords(8, 2000, 3, 1, 30)
     flags = torch.zeros(1, dtype=torch.int32, device="cuda")
