@@ -117,20 +117,25 @@ __device__ __forceinline__ bool offset_key(const Geo<ND, K>& g, uint64_t base, c
 // most 2^ND "corner" blocks:
 //   phase 1: the slots of the needed corner blocks, looked up together in
 //            rounds (every round issues the loads of all unresolved corners);
-//   phase 2: one cell load per wanted offset, all issued before any is used.
+//   phase 2: one cell load per offset, all issued before any is used.
 // No load sits under a branch (invalid ones read cell 0 and are masked), so
-// a row costs two memory round trips plus rare collision rounds.
+// a row costs two memory round trips plus rare collision rounds.  Whether an
+// offset's coordinate lies in the upper block, in range, and its cell bits
+// depend on each axis's displacement alone, so they are worked out per axis
+// and displacement (K values) and combined per offset: the corner slot of an
+// offset is picked by a tree of selects (x, then y, then z) shared between
+// offsets, rather than compared against all 2^ND corners.  `valid` false
+// probes nothing.
 template <int ND, int K>
-__device__ __forceinline__ void probe_fields(const Table& t, uint64_t base, const int64_t* f, uint64_t want,
+__device__ __forceinline__ void probe_fields(const Table& t, uint64_t base, const int64_t* f, bool valid,
                                              int32_t (&nb)[Geo<ND, K>::KV]) {
-  constexpr Geo<ND, K> g;
   constexpr int KV = Geo<ND, K>::KV;
   constexpr int LB = ND == 3 ? 2 : 3;  // log2 of the block side
   constexpr int NC = 1 << ND;
   constexpr int DMIN = -Geo<ND, K>::R, DMAX = K - 1 - Geo<ND, K>::R;
   const uint64_t b = base >> 48;
   int64_t lo[3] = {0, 0, 0}, hi[3] = {0, 0, 0};
-  bool live = want != 0;
+  bool live = valid;
 #pragma unroll
   for (int ax = 0; ax < ND; ++ax) {
     const int64_t vmin = f[ax] + DMIN, vmax = f[ax] + DMAX;
@@ -138,16 +143,30 @@ __device__ __forceinline__ void probe_fields(const Table& t, uint64_t base, cons
     lo[ax] = (vmin < 0 ? 0 : vmin) >> LB;
     hi[ax] = (vmax > 65535 ? 65535 : vmax) >> LB;
   }
-  // corner block of each wanted offset, and the corners needed
+  // per axis and displacement DMIN + i: upper block, in range, cell bits
+  bool up[3][K], inr[3][K];
+  uint32_t cb[3][K];
+  uint32_t seen[3] = {1u, 1u, 1u};  // block bits that occur on each axis (bit 0: lower, bit 1: upper)
+#pragma unroll
+  for (int ax = 0; ax < ND; ++ax) {
+    seen[ax] = 0;
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      const int64_t v = f[ax] + DMIN + i;
+      up[ax][i] = (v >> LB) != lo[ax];
+      inr[ax][i] = v >= 0 && v <= 65535;
+      cb[ax][i] = static_cast<uint32_t>(v) & ((1u << LB) - 1);
+      seen[ax] |= up[ax][i] ? 2u : 1u;
+    }
+  }
+  // the corners needed: every combination of the block bits that occur
   uint32_t need = 0;
-  uint8_t corner[KV];
 #pragma unroll
-  for (int o = 0; o < KV; ++o) {
-    int c = 0;
+  for (int c = 0; c < NC; ++c) {
+    bool use = live;
 #pragma unroll
-    for (int ax = 0; ax < ND; ++ax) c |= (((f[ax] + g.d[o][ax]) >> LB) != lo[ax] ? 1 : 0) << ax;
-    corner[o] = static_cast<uint8_t>(c);
-    if (live && ((want >> o) & 1)) need |= 1u << c;
+    for (int ax = 0; ax < ND; ++ax) use = use && ((seen[ax] >> ((c >> ax) & 1)) & 1);
+    need |= use ? 1u << c : 0u;
   }
   // phase 1: corner block slots
   uint64_t bk[NC];
@@ -192,24 +211,46 @@ __device__ __forceinline__ void probe_fields(const Table& t, uint64_t base, cons
       }
     }
   }
-  // phase 2: cells
+  // phase 2: the corner slot of each offset by selects along x, then y, then
+  // z; then its cell
   int32_t r[KV];
   bool ok[KV];
+  if constexpr (ND == 3) {
+    int32_t sx[K][4];  // by x displacement: the slots of the four (y, z) corners
 #pragma unroll
-  for (int o = 0; o < KV; ++o) {
-    int32_t sl = found[0];
+    for (int i0 = 0; i0 < K; ++i0)
 #pragma unroll
-    for (int c = 1; c < NC; ++c) sl = corner[o] == c ? found[c] : sl;
-    bool valid = live && ((want >> o) & 1) && sl >= 0;
-    int cell = 0;
+      for (int yz = 0; yz < 4; ++yz) sx[i0][yz] = up[0][i0] ? found[1 | (yz << 1)] : found[yz << 1];
 #pragma unroll
-    for (int ax = 0; ax < ND; ++ax) {
-      const int64_t v = f[ax] + g.d[o][ax];
-      valid = valid && v >= 0 && v <= 65535;
-      cell = ND == 3 ? (cell << 2) | static_cast<int>(v & 3) : (cell << 3) | static_cast<int>(v & 7);
+    for (int i0 = 0; i0 < K; ++i0)
+#pragma unroll
+      for (int i1 = 0; i1 < K; ++i1) {
+        const int32_t z0 = up[1][i1] ? sx[i0][1] : sx[i0][0];
+        const int32_t z1 = up[1][i1] ? sx[i0][3] : sx[i0][2];
+        const bool in01 = live && inr[0][i0] && inr[1][i1];
+        const uint32_t c01 = (cb[0][i0] << 4) | (cb[1][i1] << 2);
+#pragma unroll
+        for (int i2 = 0; i2 < K; ++i2) {
+          const int o = (i0 * K + i1) * K + i2;
+          const int32_t sl = up[2][i2] ? z1 : z0;
+          ok[o] = in01 && inr[2][i2] && sl >= 0;
+          r[o] = t.cells[ok[o] ? static_cast<int64_t>(static_cast<uint32_t>(sl) * kCells + (c01 | cb[2][i2])) : 0];
+        }
+      }
+  } else {
+#pragma unroll
+    for (int i0 = 0; i0 < K; ++i0) {
+      const int32_t y0 = up[0][i0] ? found[1] : found[0];
+      const int32_t y1 = up[0][i0] ? found[3] : found[2];
+#pragma unroll
+      for (int i1 = 0; i1 < K; ++i1) {
+        const int o = i0 * K + i1;
+        const int32_t sl = up[1][i1] ? y1 : y0;
+        ok[o] = live && inr[0][i0] && inr[1][i1] && sl >= 0;
+        r[o] = t.cells[ok[o] ? static_cast<int64_t>(static_cast<uint32_t>(sl) * kCells + ((cb[0][i0] << 3) | cb[1][i1]))
+                             : 0];
+      }
     }
-    ok[o] = valid;
-    r[o] = t.cells[valid ? static_cast<int64_t>(sl) * kCells + cell : 0];
   }
 #pragma unroll
   for (int o = 0; o < KV; ++o) nb[o] = ok[o] ? cell_row(static_cast<uint32_t>(r[o])) : -1;
@@ -403,7 +444,7 @@ __global__ __launch_bounds__(256) void k_rel_probe(RelK a, int natural, int64_t*
   int64_t f[3] = {0, 0, 0};
   const bool valid = live && row < n_dest && dest_fields<MODE, ND>(a, row, &base, f);
   int32_t nb[KV];
-  probe_fields<ND, K>(a.src, base, f, valid ? ~0ull : 0ull, nb);
+  probe_fields<ND, K>(a.src, base, f, valid, nb);
   uint64_t mask = 0;
 #pragma unroll
   for (int o = 0; o < KV; ++o)
