@@ -234,7 +234,8 @@ __device__ __forceinline__ void probe_fields(const Table& t, uint64_t base, cons
           const int o = (i0 * K + i1) * K + i2;
           const int32_t sl = up[2][i2] ? z1 : z0;
           ok[o] = in01 && inr[2][i2] && sl >= 0;
-          r[o] = t.cells[ok[o] ? static_cast<int64_t>(static_cast<uint32_t>(sl) * kCells + (c01 | cb[2][i2])) : 0];
+          const uint32_t ci = ok[o] ? static_cast<uint32_t>(sl) * kCells + (c01 | cb[2][i2]) : 0u;  // < 2^31
+          r[o] = t.cells[ci];
         }
       }
   } else {
@@ -247,8 +248,8 @@ __device__ __forceinline__ void probe_fields(const Table& t, uint64_t base, cons
         const int o = i0 * K + i1;
         const int32_t sl = up[1][i1] ? y1 : y0;
         ok[o] = live && inr[0][i0] && inr[1][i1] && sl >= 0;
-        r[o] = t.cells[ok[o] ? static_cast<int64_t>(static_cast<uint32_t>(sl) * kCells + ((cb[0][i0] << 3) | cb[1][i1]))
-                             : 0];
+        const uint32_t ci = ok[o] ? static_cast<uint32_t>(sl) * kCells + ((cb[0][i0] << 3) | cb[1][i1]) : 0u;
+        r[o] = t.cells[ci];
       }
     }
   }
@@ -341,6 +342,16 @@ __device__ __forceinline__ void load_offsets(const RelK& a, int8_t* offs) {
   __syncthreads();
 }
 
+// A wave-uniform address, stated as such (a buffer descriptor built from a
+// vector register would be used lane group by lane group).
+template <typename P>
+__device__ __forceinline__ P* wave_uniform(P* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<P*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
 // Group tiles of a 256-row workgroup: TS_GTILE rows are kWpt wavefronts,
 // and a workgroup covers kTpb tiles.
 constexpr int kWpt = TS_GTILE / 64;
@@ -395,18 +406,31 @@ __device__ __forceinline__ void emit_groups(const RelK& a, int kvol, uint64_t ma
   if (gt >= a.n_gtiles) return;
   const int64_t ebase = gt * kvol * TS_GTILE;
   const uint8_t slot = static_cast<uint8_t>(threadIdx.x % TS_GTILE);
+  // lane o < kvol holds where this wavefront's rows with offset o start in
+  // the tile's entries: the run start plus the tile's rows with o in earlier
+  // wavefronts (read per offset with a readlane)
+  int run_at = 0;
+  if (lane < kvol) {
+    int before = 0;
+#pragma unroll
+    for (int i = 0; i < kWpt - 1; ++i) before += i < wt ? gw[wave - wt + i][lane] : 0;
+    run_at = gstart[h][lane] + before;
+  }
+  // the tile's entries through buffer descriptors (32-bit offsets; the base
+  // is wave-uniform, stated as such)
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(wave_uniform(a.gsrc + ebase), 0, kvol * TS_GTILE * 4, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rq =
+      __builtin_amdgcn_make_buffer_rsrc(wave_uniform(a.gslot + ebase), 0, kvol * TS_GTILE, 0x00020000);
 #pragma unroll kUnroll
   for (int o = 0; o < KVMAX; ++o) {
     if (o >= kvol) break;
     const bool has = (mask >> o) & 1;
     const uint64_t b = __ballot(has);
     if (!has) continue;
-    int before = 0;  // the tile's rows with the offset in earlier wavefronts
-#pragma unroll
-    for (int i = 0; i < kWpt - 1; ++i) before += i < wt ? gw[wave - wt + i][o] : 0;
-    const int pos = gstart[h][o] + before + __popcll(b & lt);
-    a.gsrc[ebase + pos] = nb(o);
-    a.gslot[ebase + pos] = slot;
+    const int pos = __builtin_amdgcn_readlane(run_at, o) + __popcll(b & lt);
+    __builtin_amdgcn_raw_buffer_store_b32(nb(o), rs, 4 * pos, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b8(slot, rq, pos, 0, 0);
   }
   // the pad entries that complete each offset's last group: no source row
   // and the sink slot TS_GTILE
