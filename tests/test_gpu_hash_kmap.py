@@ -132,6 +132,26 @@ def test_hash_many_rebuilds_and_supports_share_a_buffer(ts):
         assert int(flags.item()) == rflags, f"build {k}"
 
 
+@pytest.mark.parametrize("cap", [1, 2, 4, 8, 64, 128, 512])
+def test_hash_tiny_capacities(ts, cap):
+    """Any power-of-two capacity >= n is a valid table, down to one slot:
+    builds, rebuilds (each clears what the last one stored) and queries."""
+    # rows inside one 4x4x4 block (one slot) so that even a one-slot table holds them
+    sets = [synth.random_coords(51, min(cap, 3), 3, 1, 4), synth.random_coords(52, min(cap, 2), 3, 1, 4),
+            synth.random_coords(53, 1, 3, 1, 4)]
+    buf = torch.zeros(ts.ts_hash_table_bytes(cap), dtype=torch.uint8, device="cuda")
+    flags = torch.zeros(1, dtype=torch.int32, device="cuda")
+    q = np.concatenate(sets + [synth.random_coords(54, 50, 3, 1, 8)], axis=0)
+    got = torch.empty(q.shape[0], dtype=torch.int32, device="cuda")
+    for c in sets + sets[::-1]:
+        flags.zero_()
+        ts.ts_hash_build(dev(c), buf, cap, flags)
+        ts.ts_hash_query(buf, cap, dev(q), got)
+        ref, rflags = oracle.hash_query(c, q)
+        np.testing.assert_array_equal(got.cpu().numpy(), ref)
+        assert int(flags.item()) == rflags
+
+
 def test_hash_small_reserve_ratio(ts):
     c = synth.random_coords(8, 2000, 3, 1, 30)
     flags = torch.zeros(1, dtype=torch.int32, device="cuda")
