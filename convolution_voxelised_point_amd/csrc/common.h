@@ -92,14 +92,18 @@ __device__ __forceinline__ bool row_key(const int32_t* coords, int64_t row, int 
   return make_key(ndim, c[0], s, key);
 }
 
-// 64-bit finaliser (xor-shift-multiply, constants of Stafford's "Mix13").
-__device__ __forceinline__ uint64_t hash64(uint64_t k) {
-  k ^= k >> 30;
-  k *= 0xbf58476d1ce4e5b9ull;
-  k ^= k >> 27;
-  k *= 0x94d049bb133111ebull;
-  k ^= k >> 31;
-  return k;
+// Slot hash of a block key: the two 32-bit halves folded with a golden-ratio
+// multiply, then the 32-bit finaliser of MurmurHash3 (xor-shift-multiply
+// with its published constants).  32-bit multiplies only: the probe hashes
+// up to eight corner blocks per row.
+__device__ __forceinline__ uint32_t hash_key(uint64_t k) {
+  uint32_t h = static_cast<uint32_t>(k) ^ (static_cast<uint32_t>(k >> 32) * 0x9e3779b1u);
+  h ^= h >> 16;
+  h *= 0x85ebca6bu;
+  h ^= h >> 13;
+  h *= 0xc2b2ae35u;
+  h ^= h >> 16;
+  return h;
 }
 
 // Key layout: [batch:16][f0:16][f1:16][f2:16] with f = value + 2^15 (a
@@ -124,7 +128,7 @@ __device__ __forceinline__ int cell_of(uint64_t key, int nd) {
 // of 3.8 (at most 11); a claim reads the whole group of four.
 constexpr uint64_t kSlotGroup = 4;
 __device__ __forceinline__ uint64_t first_slot(const Table& t, uint64_t bkey) {
-  return hash64(bkey) & t.mask & ~(kSlotGroup - 1);
+  return static_cast<uint64_t>(hash_key(bkey)) & t.mask & ~(kSlotGroup - 1);
 }
 
 // Slot of a block key or -1 (linear probing from its first slot).

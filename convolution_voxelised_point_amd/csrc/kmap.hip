@@ -373,7 +373,6 @@ __device__ __forceinline__ void emit_groups(const RelK& a, int kvol, uint64_t ma
   __shared__ int gw[4][KVMAX];         // pairs per wavefront and offset
   __shared__ int gstart[kTpb][KVMAX];  // first entry of each offset's run, per tile
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const uint64_t lt = (1ull << lane) - 1;
   // unrolled for the compile-time kernel sizes (at most 27 offsets); the
   // runtime-size instance (up to TS_MAX_KVOL) keeps its loops
   constexpr int kUnroll = KVMAX <= 32 ? KVMAX : 1;
@@ -428,7 +427,9 @@ __device__ __forceinline__ void emit_groups(const RelK& a, int kvol, uint64_t ma
     const bool has = (mask >> o) & 1;
     const uint64_t b = __ballot(has);
     if (!has) continue;
-    const int pos = __builtin_amdgcn_readlane(run_at, o) + __popcll(b & lt);
+    const int pos = __builtin_amdgcn_readlane(run_at, o) +
+                    static_cast<int>(__builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(b >> 32),
+                                                                __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(b), 0u)));
     __builtin_amdgcn_raw_buffer_store_b32(nb(o), rs, 4 * pos, 0, 0);
     __builtin_amdgcn_raw_buffer_store_b8(slot, rq, pos, 0, 0);
   }
