@@ -269,13 +269,25 @@ __global__ __launch_bounds__(256) void k_gen_insert(const int32_t* __restrict__ 
   const bool in = m < n_cand;
   const bool valid = in && gen_key(coords, m, t.nd, kvol, offs, scale, sign, &input_ok, &key);
   const int32_t sl = run_slot(t, block_key(key, t.nd), valid, flags);
+  // The candidate kvol + 1 lanes earlier is input i - 1 at offset o - 1: for
+  // a stride-1 generation and inputs that are neighbours along the last
+  // axis, the same site.  A candidate whose site an earlier lane also has
+  // cannot own it (the smallest candidate does), so it skips the atomic; the
+  // cell still ends up holding the owner, and first occurrences are read
+  // from the cells afterwards as before.
+  const int back = kvol + 1;
+  const uint32_t plo = __shfl_up(static_cast<uint32_t>(key), back, 64);
+  const uint32_t phi = __shfl_up(static_cast<uint32_t>(key >> 32), back, 64);
+  const int pvalid = __shfl_up(valid ? 1 : 0, back, 64);
+  const bool shadowed = scale == 1 && back < 64 && static_cast<int>(threadIdx.x & 63) >= back && pvalid &&
+                        ((static_cast<uint64_t>(phi) << 32) | plo) == key;
   if (!in) return;
   int32_t at = -1;
   if (!input_ok) {
     if (flags && m % kvol == 0) atomicOr(flags, TS_FLAG_RANGE);
   } else if (valid && sl >= 0) {
     at = sl * kCells + cell_of(key, t.nd);
-    atomicMax(reinterpret_cast<unsigned*>(t.cells) + at, cell_enc(m));
+    if (!shadowed) atomicMax(reinterpret_cast<unsigned*>(t.cells) + at, cell_enc(m));
   }
   cell_at[m] = at;
 }
